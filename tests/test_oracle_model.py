@@ -1,0 +1,166 @@
+"""Model-level pins of the oracle: a float64 shadow of the same weights (scale
+wiring), and the invariances the pages claim for the integer pipeline
+(batch composition, prefill vs token-by-token, split prefill)."""
+import numpy as np
+import pytest
+
+import detint_synth as S
+import oracle as O
+from tests import float_shadow as FS
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _cos(a, b):
+    a, b = a.ravel(), b.ravel()
+    return float(a @ b / np.linalg.norm(a) / np.linalg.norm(b))
+
+
+@pytest.fixture(scope="module")
+def layer256():
+    m = S.make_model("layer256", seed=1)
+    h0 = S.make_residual(64, 256, seed=2)
+    om = O.OracleModel(m, slots=1)
+    h1, dmp = om.layer(0, h0, [64], [0], [0], dump=True)
+    return m, h0, h1, dmp, om
+
+
+def test_layer_float_shadow(layer256):
+    m, h0, h1, dmp, _ = layer256
+    sh = m.shape
+    f0 = h0 / 2.0 ** sh.f_res
+    f1 = FS.layer(sh, m.layers[0], f0, np.arange(64))
+    d_int = (h1 - h0) / 2.0 ** sh.f_res
+    d_flt = f1 - f0
+    assert _cos(d_int, d_flt) > 0.99
+    assert _rel(d_int, d_flt) < 0.12
+
+
+def test_layer_stages_float_shadow(layer256):
+    """Every intermediate's dequantised value against the float quantity it
+    stands for, computed from the previous integer stage."""
+    m, h0, h1, dmp, om = layer256
+    sh, L = m.shape, m.layers[0]
+    d, nq, nkv, F = sh.head_dim, sh.n_q, sh.n_kv, sh.ffn
+    # attention RMSNorm
+    x1 = dmp["x1"] * (dmp["x1_m"] * 2.0 ** -dmp["x1_k"].astype(float))[:, None]
+    assert _rel(x1, FS.rmsnorm(h0.astype(float), L.attn_norm)) < 0.02
+    # QKV accumulators are exact
+    np.testing.assert_array_equal(dmp["qkv_acc"], dmp["x1"].astype(np.int64) @ L.wqkv.astype(np.int64).T)
+    # q after q-norm + RoPE, dequantised from q8 * 2^eq * 2^-f_n
+    qkv = dmp["x1"].astype(float) @ FS.wreal(L.wqkv, L.wqkv_m, sh.w_k).T
+    q = qkv[:, :nq * d].reshape(64, nq, d).transpose(1, 0, 2)
+    q = FS.rope(FS.rmsnorm(q, L.q_norm), np.arange(64), sh.rope_base)
+    q_int = (dmp["q8"] * 2.0 ** dmp["eq"][:, :, None]).transpose(1, 0, 2) / 2.0 ** sh.f_n
+    assert _rel(q_int, q) < 0.03
+    # attention output O against float softmax on the integer q8 / k8 / v8
+    kc, vc = om.kc[0, 0, :, :64], om.vc[0, 0, :, :64]
+    Ms, Ks = O.softmax_mult(L.kq_m, L.kq_k, d, sh.f_n)
+    att = dmp["attn"].reshape(64, nq, d)
+    for hh in range(nq):
+        kv = hh * nkv // nq
+        s = dmp["q8"][:, hh].astype(float) @ kc[kv].astype(float).T
+        x = s * 2.0 ** dmp["eq"][:, hh][:, None] * Ms * 2.0 ** -Ks / 2.0 ** 15     # log2 units
+        x = np.where(np.tril(np.ones((64, 64), bool)), x, -np.inf)
+        p = 2.0 ** (x - x.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        o = p @ vc[kv].astype(float) * 2 ** 15
+        assert _rel(att[:, hh], o) < 0.04
+    # the same scores in float from the real q/k (checks the softmax scale)
+    k = qkv[:, nq * d:(nq + nkv) * d].reshape(64, nkv, d).transpose(1, 0, 2)
+    k = FS.rope(FS.rmsnorm(k, L.k_norm), np.arange(64), sh.rope_base)
+    k_int = kc.astype(float) * 2.0 ** L.kq_k / L.kq_m / 2.0 ** sh.f_n
+    assert _rel(k_int, k) < 0.03
+    # FFN: gate/up in f_a fixed point, SwiGLU product dequantised
+    x2 = dmp["x2"] * (dmp["x2_m"] * 2.0 ** -dmp["x2_k"].astype(float))[:, None]
+    gu = x2 @ FS.wreal(L.wgu, L.wgu_m, sh.w_k).T
+    assert _rel(dmp["gu"] / 2.0 ** sh.f_a, gu) < 0.01
+    g_i, u_i = dmp["gu"][:, :F] / 4096.0, dmp["gu"][:, F:] / 4096.0
+    a = dmp["a8"] * (dmp["a_m"] * 2.0 ** -dmp["a_k"].astype(float))[:, None]
+    assert _rel(a, FS.silu(g_i) * u_i) < 0.05
+
+
+def test_layer_zero_projections_are_identity():
+    m = S.make_model("layer256", seed=3)
+    m.layers[0].wo[:] = 0
+    m.layers[0].wd[:] = 0
+    h0 = S.make_residual(20, 256, seed=4)
+    h1, _ = O.OracleModel(m).layer(0, h0, [20], [0], [0])
+    np.testing.assert_array_equal(h1, h0)
+
+
+def test_layer_batch_and_split_invariance():
+    m = S.make_model("layer256", seed=5)
+    a = S.make_residual(40, 256, seed=6)
+    b = S.make_residual(23, 256, seed=7)
+    ref = O.OracleModel(m, slots=1)
+    ha, _ = ref.layer(0, a, [40], [0], [0])
+    # a shares the batch with b (b first, a in slot 1)
+    both = O.OracleModel(m, slots=2)
+    hb, _ = both.layer(0, np.concatenate([b, a]), [23, 40], [0, 0], [0, 1])
+    np.testing.assert_array_equal(hb[23:], ha)
+    np.testing.assert_array_equal(both.kc[:, 1], ref.kc[:, 0])
+    np.testing.assert_array_equal(both.vc[:, 1], ref.vc[:, 0])
+    # split prefill 17 + 23, then token by token for the rest
+    sp = O.OracleModel(m, slots=1)
+    h1, _ = sp.layer(0, a[:17], [17], [0], [0])
+    h2, _ = sp.layer(0, a[17:30], [13], [17], [0])
+    rows = [h1, h2]
+    for t in range(30, 40):
+        r, _ = sp.layer(0, a[t:t + 1], [1], [t], [0])
+        rows.append(r)
+    np.testing.assert_array_equal(np.concatenate(rows), ha)
+
+
+def test_layer_residual_bound_raises():
+    m = S.make_model("layer256", seed=8)
+    h0 = S.make_residual(4, 256, seed=9)
+    h0[2, 5] = 1 << 25
+    with pytest.raises(O.OracleError):
+        O.OracleModel(m).layer(0, h0, [4], [0], [0])
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wide"])
+def test_forward_float_shadow_logits(name):
+    m = S.make_model(name, seed=10)
+    ids = S.make_prompt(m.shape.vocab, 48, seed=11)
+    om = O.OracleModel(m, slots=1)
+    logits, nxt = om.forward(ids, [48], [0], [0], all_rows=True)
+    ref = FS.forward_logits(m, ids)
+    got = logits / 2.0 ** m.shape.f_l
+    # without q/k-norm the scores are peakier and the integer softmax's error
+    # compounds more over two layers; a mis-wired scale or index gives cosine
+    # near 0 or a relative error near or above 1
+    assert _cos(got, ref) > (0.98 if m.shape.qk_norm else 0.96)
+    assert _rel(got, ref) < (0.2 if m.shape.qk_norm else 0.3)
+    np.testing.assert_array_equal(nxt, np.argmax(logits, 1))
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wide"])
+def test_forward_invariances(name):
+    m = S.make_model(name, seed=12)
+    V = m.shape.vocab
+    p0 = S.make_prompt(V, 33, seed=13)
+    others = S.make_prompts(V, 3, 5, 60, seed=14)
+    # prefill with logits at every position
+    a = O.OracleModel(m, slots=1)
+    all_logits, _ = a.forward(p0, [33], [0], [0], all_rows=True)
+    # token by token: every position's logits equal the prefill's
+    b = O.OracleModel(m, slots=1)
+    for t in range(33):
+        lg, _ = b.forward(p0[t:t + 1], [1], [t], [0])
+        np.testing.assert_array_equal(lg[0], all_logits[t])
+    # batch composition: generation of p0 alone vs inside a batch of 4
+    n_new = 12
+    solo = O.OracleModel(m, slots=1).generate([p0], n_new)
+    rows_solo, rows_batch = [], []
+    O.OracleModel(m, slots=1).generate([p0], n_new, on_step=lambda s, lg: rows_solo.append(lg[0].copy()))
+    batch = O.OracleModel(m, slots=4).generate([p0] + others, n_new,
+                                               on_step=lambda s, lg: rows_batch.append(lg[0].copy()))
+    np.testing.assert_array_equal(batch[0], solo[0])
+    np.testing.assert_array_equal(np.array(rows_batch), np.array(rows_solo))
+    # repeated runs are identical
+    again = O.OracleModel(m, slots=4).generate([p0] + others, n_new)
+    np.testing.assert_array_equal(again, batch)
