@@ -1,0 +1,282 @@
+/*
+ * detint.h - C ABI of libdetint, an integer-only transformer forward pass for
+ * AMD Instinct MI355X (gfx950). Every op from token ids to int32 logits is
+ * exact integer arithmetic, so results are bit-identical for any batch
+ * composition, prefill/decode split and summation order.
+ *
+ * Sources (page title, section):
+ *   DetLLM README ("DetLLM - Fully Deterministic LLM Inference"): intro and
+ *     "Layout" (integer primitives with frozen rounding, dyadic (data, m, k)
+ *     requant, the int8 GEMM as the one hardware-dispatched call, DI-Exp /
+ *     DI-Softmax / DI-RMSNorm / DI-SwiGLU / integer RoPE).
+ *   DetLLM blog (integer-arithmetic post), section "DetLLM": dyadic scales
+ *     m/2^k with one rounding rule, shift-based nonlinears, int16 sin/cos
+ *     tables, per-token activation quantisation, fixed-scale int8 KV cache,
+ *     lowest-id argmax; footnote 8: 15-bit attention probabilities and P.V
+ *     as two int8 GEMMs.
+ *   BitExact LLM blog, "Fix the arithmetic": 16-bit fixed-point weights as
+ *     integer limbs with wide accumulators; explicit rounding rules and
+ *     bounds.
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; arrays are
+ *     row-major and contiguous. int8 matrices that feed a GEMM need a 16-byte
+ *     aligned base and a row length that is a multiple of 16.
+ *   - Sizes are int64_t; no float type appears anywhere in this ABI.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls only enqueue work: no allocation, no synchronisation, no memset,
+ *     so every call may be captured into a hipGraph.
+ *   - Return value: DETINT_OK, or an error code (the call enqueued nothing);
+ *     detint_last_error() gives the message. Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Rounding rule used everywhere: R(x, s) = floor(x / 2^s + 1/2) for s >= 1
+ *     (round half up via an arithmetic shift), x for s = 0, x * 2^-s for s < 0.
+ *   - Per-token dynamic quantisation DQ(y) over a row: A = max |y_i|,
+ *     e = max(0, bitlen(A) - 7), q_i = clamp(R(y_i, e), -127, 127).
+ *   - Results are undefined (but memory-safe) where an input breaks a stated
+ *     bound; the CPU oracle of this project reports such inputs as errors.
+ */
+#ifndef DETINT_H
+#define DETINT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t detint_status;
+#define DETINT_OK 0
+#define DETINT_EINVAL 1        /* bad shape, null pointer, misalignment */
+#define DETINT_EUNSUPPORTED 2  /* shape or configuration this build does not handle */
+#define DETINT_EHIP 3          /* a HIP launch/runtime call failed */
+
+/* GEMM epilogue modes (DetLLM README "Layout": dyadic requant in dyadic.py). */
+#define DETINT_GEMM_RAW 0      /* out int32 = acc                                   */
+#define DETINT_GEMM_REQ_I8 1   /* out int8  = clamp8(R(acc*m_r*m_c, k_r + k_c))     */
+#define DETINT_GEMM_FIX 2      /* out int32 = R(acc*m_r*m_c, k_r + k_c - frac)      */
+#define DETINT_GEMM_RES_ADD 3  /* out int32 += R(acc*m_r*m_c, k_r + k_c - frac)     */
+
+const char *detint_version(void);
+/* Message of the last error returned on the calling thread ("" if none). */
+const char *detint_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* GEMM: acc[i][j] = sum_k A[i][k] * W[j][k], exact in int32 (DetLLM blog,
+ * "DetLLM": the int8 x int8 -> int32 matmul is the one hardware-dispatched
+ * function; integer accumulation is exact, so any tiling gives the same bits).
+ *   A      int8 [M, K] activations.          W      int8 [N, K] weights.
+ *   row_m  int32 [M], row_k int32 [M]: per-row dyadic scale (ignored in RAW).
+ *   col_m  int32 [N], col_k: per-column mantissas, one shift for the tensor.
+ *   frac   fractional bits of FIX / RES_ADD outputs.
+ *   out    [M, N] int32 (RAW, FIX, RES_ADD; read-modify-write for RES_ADD) or
+ *          int8 (REQ_I8).
+ * Bounds: K <= 131072 (|acc| < 2^31). M, N >= 0; M = 0 or N = 0 is a no-op. */
+detint_status detint_gemm_i8(const int8_t *A, const int8_t *W, int64_t M, int64_t N, int64_t K,
+                             const int32_t *row_m, const int32_t *row_k,
+                             const int32_t *col_m, int32_t col_k, int32_t frac,
+                             int32_t mode, void *out, void *stream);
+
+/* GEMM with 16-bit fixed-point weights W16 = 256 * hi + lo held as two int8
+ * planes: W_hi = W16 >> 8 (signed) and W_lo = (W16 & 255) - 128 (biased so
+ * both limbs feed the signed int8 matrix units). The int64 accumulator is
+ * 256 * (A.hi) + (A.lo') + 128 * rowsum(A) = A.W16 exactly (BitExact blog,
+ * "Fix the arithmetic": limb partial products combined in wide accumulators).
+ * Epilogue modes as above with a 128-bit product; RAW writes int64 [M, N].
+ * Bound: K <= 65536. */
+detint_status detint_gemm_w16(const int8_t *A, const int8_t *W_hi, const int8_t *W_lo,
+                              int64_t M, int64_t N, int64_t K,
+                              const int32_t *row_m, const int32_t *row_k,
+                              const int32_t *col_m, int32_t col_k, int32_t frac,
+                              int32_t mode, void *out, void *stream);
+
+/* Split int16 weights [n] into the two limb planes used by detint_gemm_w16. */
+detint_status detint_split_w16(const int16_t *W16, int64_t n, int8_t *W_hi, int8_t *W_lo,
+                               void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Row operations (DetLLM README "Layout", ops/). */
+
+/* Integer RMSNorm of R rows of n (DI-RMSNorm). For each row: S = sum h_i^2,
+ * c = max(0, floor((62 - bitlen(S)) / 2)), r = isqrt(floor(S * 4^c / n)),
+ * T = bitlen(r) + 14, m = RD(2^T, r) (m = 2^15 -> m = 2^14, T -= 1), where
+ * RD(a, b) = floor((2a + b) / 2b); (x8, e) = DQ(h_i * gain_i);
+ * row_m = m, row_k = T - c + 12 - e. So x8 * row_m * 2^-row_k approximates
+ * h * (gain * 2^-12) / rms(h). A zero row gives x8 = 0, scale (2^14, 26).
+ *   h int32 [R, n] with |h| < 2^25; gain int16 [n]; x8 int8 [R, n];
+ *   row_m, row_k int32 [R]. n <= 16384. */
+detint_status detint_rmsnorm(const int32_t *h, const int16_t *gain, int64_t R, int64_t n,
+                             int8_t *x8, int32_t *row_m, int32_t *row_k, void *stream);
+
+/* DQ of each row (per-token dynamic quantisation, DetLLM blog "DetLLM"):
+ *   y int32 [R, n] -> q int8 [R, n], row_e int32 [R] with y ~ q * 2^row_e. */
+detint_status detint_requant(const int32_t *y, int64_t R, int64_t n, int8_t *q, int32_t *row_e,
+                             void *stream);
+
+/* Integer RoPE in place on x int32 [R, heads, d] with Q1.14 tables
+ * cos_t/sin_t int16 [max_pos, d/2] (DetLLM blog "DetLLM": precomputed int16
+ * sin/cos tables). Pairs (i, i + d/2) at position pos[r]:
+ *   x_i' = R(x_i C - x_{i+d/2} S, 14), x_{i+d/2}' = R(x_{i+d/2} C + x_i S, 14).
+ * d even, d <= 256; 0 <= pos[r] < max_pos; |x| < 2^31 after rotation. */
+detint_status detint_rope(int32_t *x, const int32_t *pos, const int16_t *cos_t,
+                          const int16_t *sin_t, int64_t R, int64_t heads, int64_t d,
+                          int64_t max_pos, void *stream);
+
+/* DI-Softmax with 15-bit probabilities (DetLLM blog footnote 8). Row r has
+ * valid[r] (1 <= valid <= C) scores; mx = max of them;
+ * u_j = R((s_j - mx) * mult_m, mult_k - shift[r]) (base-2 exponent, Q15);
+ * E_j = DI-Exp(u_j): with v = -u_j, n = v >> 15, f = 2^15 - R(v & 32767, 1),
+ * E_j = R(f, n) (0 for n > 30); D = sum E_j; Rn = floor(2^46 / D);
+ * P_j = min(R(E_j * Rn, 31), 2^15 - 1); P_j = 0 for j >= valid[r].
+ *   s int32 [R, C], valid/shift int32 [R], P int16 [R, C]. C <= 65536. */
+detint_status detint_softmax(const int32_t *s, const int32_t *valid, const int32_t *shift,
+                             int64_t R, int64_t C, int32_t mult_m, int32_t mult_k, int16_t *P,
+                             void *stream);
+
+/* DI-SwiGLU of R rows. gu int32 [R, 2n]: gate in [:, :n], up in [:, n:], both
+ * with f_a fractional bits, |g|, |u| < 2^24. Integer sigmoid (Q15):
+ * E = DI-Exp(-R(|g| * Mg, Kg)) with (Mg, Kg) = detint_swiglu_mult(f_a),
+ * s+ = RD(2^30, 2^15 + E), s = s+ (g >= 0) or 2^15 - s+ (g < 0);
+ * silu = R(g * s, 15); p = silu * u; (a8, e) = DQ(p);
+ * row scale (row_m, row_k) = (2^14, 2 f_a - e + 14).
+ *   a8 int8 [R, n]; row_m, row_k int32 [R]. n <= 65536. */
+detint_status detint_swiglu(const int32_t *gu, int64_t R, int64_t n, int32_t f_a, int8_t *a8,
+                            int32_t *row_m, int32_t *row_k, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the int8 KV cache (DetLLM blog "DetLLM": K and V are
+ * quantised once at fixed offline scales, so prefill and decode see the same
+ * cached bits; footnote 8: 15-bit probabilities, P.V exact).
+ * Cache layout, K and V alike: int8 [n_slots][n_kv][max_pos][d] for ONE
+ * layer (pass the layer's base). Query head h reads KV head h * n_kv / n_q.
+ * Query row r at absolute position p attends positions 0..p of its slot
+ * (rows whose position or slot is out of range get zeros):
+ *   s_j = q8 . k8_j; P = DI-Softmax(s, mult, shift = e_q[r][h]);
+ *   out[r][h][t] = sum_j P_j * v8_j[t]   (int32, exact).
+ *   q8 int8 [rows, n_q, d]; e_q int32 [rows, n_q]; out int32 [rows, n_q, d].
+ * d in {64, 128}; n_q / n_kv in {1, 2, 4, 8}; max_pos <= 16384.          */
+
+/* Prefill: S packed sequences; sequence s owns rows cu_seqlens[s] ..
+ * cu_seqlens[s+1]-1 at positions start_pos[s] + i, cache slot slot[s]
+ * (chunked prefill: positions < start_pos[s] come from earlier calls).
+ * R = cu_seqlens[S] (host copy of the last entry). */
+detint_status detint_attn_prefill(const int8_t *q8, const int32_t *e_q, const int8_t *k_cache,
+                                  const int8_t *v_cache, int64_t n_slots, const int32_t *cu_seqlens,
+                                  const int32_t *start_pos, const int32_t *slot, int64_t S,
+                                  int64_t R, int64_t n_q, int64_t n_kv, int64_t d,
+                                  int64_t max_pos, int32_t mult_m, int32_t mult_k,
+                                  int32_t *out, void *stream);
+
+/* Decode: B rows, row b at position ctx_len[b] - 1 of slot slot[b]. */
+detint_status detint_attn_decode(const int8_t *q8, const int32_t *e_q, const int8_t *k_cache,
+                                 const int8_t *v_cache, int64_t n_slots, const int32_t *ctx_len,
+                                 const int32_t *slot, int64_t B, int64_t n_q, int64_t n_kv,
+                                 int64_t d, int64_t max_pos, int32_t mult_m, int32_t mult_k,
+                                 int32_t *out, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side set-up arithmetic (no device work; table/constant construction
+ * is offline work in the pages' design, outside the forward pass). */
+
+/* Q1.14 RoPE tables: C[p][i] = floor(2^14 cos(p * base^(-2i/d)) + 1/2), S
+ * likewise with sin, for p < P, i < d/2, evaluated in float64. Host arrays. */
+detint_status detint_rope_tables(int16_t *cos_t, int16_t *sin_t, int64_t P, int64_t d,
+                                 int64_t base);
+/* Softmax exponent multiplier (M, K): M * 2^-K ~ log2(e) / sqrt(d) * 2^15 *
+ * (2^kq_k / kq_m) * 2^(-2 f_n), M in [2^14, 2^15). */
+detint_status detint_softmax_mult(int32_t kq_m, int32_t kq_k, int64_t d, int32_t f_n,
+                                  int32_t *M, int32_t *K);
+/* SiLU exponent multiplier: M * 2^-K ~ log2(e) * 2^(15 - f_a). */
+detint_status detint_swiglu_mult(int32_t f_a, int32_t *M, int32_t *K);
+/* V-cache dequant scale (m, k), the dyadic inverse of the quant scale:
+ * m = RD(2^29, vq_m), k = 29 - vq_k (m = 2^15 -> (2^14, 28 - vq_k)). */
+detint_status detint_v_dequant(int32_t vq_m, int32_t vq_k, int32_t *m, int32_t *k);
+
+/* ------------------------------------------------------------------------ */
+/* Whole model (DetLLM README "Layout": the IntQwen3 runtime; "Usage": greedy
+ * generate). The handle only records caller-owned device pointers and
+ * integer constants; it copies no tensor and allocates no device memory. */
+
+typedef struct detint_layer_desc {
+  /* Linear weights [N, K]; for wide (16-bit) models w* is the high limb and
+   * w*_lo the biased low limb (see detint_gemm_w16), else w*_lo is NULL.
+   * wqkv rows: n_q*d query, n_kv*d key, n_kv*d value. wgu rows: ffn gate
+   * then ffn up. Each *_m is the per-output-channel mantissa [N]; the shift
+   * of every weight scale is the model's w_k. */
+  const int8_t *wqkv, *wqkv_lo; const int32_t *wqkv_m;
+  const int8_t *wo, *wo_lo;     const int32_t *wo_m;
+  const int8_t *wgu, *wgu_lo;   const int32_t *wgu_m;
+  const int8_t *wd, *wd_lo;     const int32_t *wd_m;
+  const int16_t *attn_norm, *ffn_norm;   /* [hidden] gains, value g * 2^-12 */
+  const int16_t *q_norm, *k_norm;        /* [d] gains (qk_norm models) or NULL */
+  int32_t kq_m, kq_k;                    /* K-cache quant scale: k8 = clamp8(R(k * kq_m, kq_k)) */
+  int32_t vq_m, vq_k;                    /* V-cache quant scale */
+} detint_layer_desc;
+
+typedef struct detint_model_desc {
+  int64_t n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab, max_pos;
+  int32_t qk_norm;   /* 1: per-head RMSNorm on q and k before RoPE (Qwen3) */
+  int32_t wide;      /* 1: 16-bit limbed linear weights and embedding        */
+  int32_t w_k;       /* shift of every weight / embedding scale              */
+  int32_t f_res;     /* fractional bits of the int32 residual stream         */
+  int32_t f_n;       /* fractional bits of q/k/v before quantisation         */
+  int32_t f_a;       /* fractional bits of SwiGLU gate/up                    */
+  int32_t f_l;       /* fractional bits of the int32 logits                  */
+  int32_t reserved;
+  const int8_t *emb, *emb_lo;   /* tied embedding / lm_head [vocab, hidden]; may be
+                                   NULL with vocab = 0 (layer-only models) */
+  const int32_t *emb_m;         /* [vocab] mantissas                          */
+  const int16_t *final_norm;    /* [hidden]                                   */
+  const int16_t *rope_cos, *rope_sin;  /* device [max_pos, d/2] Q1.14 tables  */
+  const detint_layer_desc *layers;     /* HOST array [n_layers], copied       */
+} detint_model_desc;
+
+typedef struct detint_model detint_model;
+
+detint_status detint_model_create(const detint_model_desc *desc, detint_model **out);
+void detint_model_destroy(detint_model *m);
+
+/* Bytes of device workspace detint_forward needs for up to max_rows packed
+ * rows in up to max_seqs sequences. */
+int64_t detint_workspace_size(const detint_model *m, int64_t max_rows, int64_t max_seqs);
+
+/* Forward pass: ids -> embedding -> n_layers decoder layers -> final RMSNorm
+ * -> tied lm_head -> int32 logits of the LAST row of each sequence, and the
+ * greedy next token (lowest id among the maxima; DetLLM blog "DetLLM").
+ *   k_cache, v_cache: int8 [n_layers][n_slots][n_kv][max_pos][d].
+ *   ids int32 [R]; cu_seqlens int32 [S+1]; start_pos, slot int32 [S]
+ *   (device); R and max_seqlen are host copies (rows in total, longest
+ *   sequence) used for launch sizes.
+ *   logits int32 [S, vocab]: written at row (logit_row_base ? *logit_row_base
+ *   : 0) + s, so a captured decode graph can append to a history buffer.
+ *   next_tok int32 [S] (may alias ids for decode).
+ *   flags: DETINT_FWD_ADVANCE - after the step, for every s: ids[s] =
+ *   next_tok[s], start_pos[s] += 1, and *logit_row_base += S (decode only:
+ *   requires R == S). Positions and lengths are read from device memory, so
+ *   one captured graph serves every decode step.
+ *   ws: device workspace of ws_bytes >= detint_workspace_size(m, R, S).     */
+#define DETINT_FWD_ADVANCE 1
+detint_status detint_forward(const detint_model *m, int8_t *k_cache, int8_t *v_cache,
+                             int64_t n_slots, int32_t *ids, int64_t R,
+                             const int32_t *cu_seqlens, int32_t *start_pos,
+                             const int32_t *slot, int64_t S, int64_t max_seqlen,
+                             int32_t *logits, int32_t *logit_row_base, int32_t *next_tok,
+                             int32_t flags, void *ws, int64_t ws_bytes, void *stream);
+
+/* One decoder layer in place on the int32 residual h [R, hidden] (|h| <
+ * 2^25), same sequence/cache arguments and workspace as detint_forward:
+ * RMSNorm -> QKV -> (q/k-norm) -> RoPE -> q DQ, K/V into the cache ->
+ * attention -> DQ -> O-proj + residual -> RMSNorm -> gate/up -> DI-SwiGLU ->
+ * down + residual (DetLLM README "Layout"; DetLLM blog "DetLLM"). Works on
+ * models without a vocabulary (vocab = 0). */
+detint_status detint_layer_forward(const detint_model *m, int64_t layer, int32_t *h,
+                                   int8_t *k_cache, int8_t *v_cache, int64_t n_slots, int64_t R,
+                                   const int32_t *cu_seqlens, const int32_t *start_pos,
+                                   const int32_t *slot, int64_t S, int64_t max_seqlen, void *ws,
+                                   int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETINT_H */

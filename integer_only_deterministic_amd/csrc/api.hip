@@ -1,0 +1,522 @@
+// C ABI of libdetint (declared in include/detint.h): argument checks, the
+// host-side set-up arithmetic, the model handle, and the forward pass as a
+// sequence of kernel launches on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/detint.h"
+#include "internal.h"
+
+using namespace detint;
+
+namespace {
+
+thread_local std::string g_err;
+
+detint_status fail(detint_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+detint_status ok() {
+  g_err.clear();
+  return DETINT_OK;
+}
+
+detint_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DETINT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+hipStream_t S_(void* s) { return (hipStream_t)s; }
+
+#define REQUIRE(cond, ...)                               \
+  do {                                                   \
+    if (!(cond)) return fail(DETINT_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+detint_status check_gemm(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
+                         const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
+                         int32_t mode, const void* out, int64_t kmax) {
+  REQUIRE(M >= 0 && N >= 0 && K > 0, "gemm: bad shape M=%lld N=%lld K=%lld", (long long)M,
+          (long long)N, (long long)K);
+  REQUIRE(K % 16 == 0, "gemm: K=%lld must be a multiple of 16", (long long)K);
+  REQUIRE(K <= kmax, "gemm: K=%lld exceeds %lld (int32 accumulator bound)", (long long)K,
+          (long long)kmax);
+  REQUIRE(M <= (int64_t)1 << 30 && N <= (int64_t)1 << 30, "gemm: M or N too large");
+  REQUIRE(mode >= DETINT_GEMM_RAW && mode <= DETINT_GEMM_RES_ADD, "gemm: bad mode %d", mode);
+  if (M == 0 || N == 0) return ok();
+  REQUIRE(A && W && out, "gemm: null pointer");
+  REQUIRE(aligned16(A) && aligned16(W), "gemm: A and W must be 16-byte aligned");
+  if (mode != DETINT_GEMM_RAW) REQUIRE(row_m && row_k && col_m, "gemm: null scale pointer");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* detint_version(void) { return "libdetint 0.1 gfx950"; }
+const char* detint_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------- GEMMs
+
+detint_status detint_gemm_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
+                             const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
+                             int32_t col_k, int32_t frac, int32_t mode, void* out, void* stream) {
+  detint_status s = check_gemm(A, W, M, N, K, row_m, row_k, col_m, mode, out, 131072);
+  if (s != DETINT_OK || M == 0 || N == 0) return s;
+  Epi e{row_m, row_k, col_m, col_k, frac, mode, nullptr};
+  return hip_status(launch_gemm(A, W, nullptr, M, N, K, e, out, S_(stream)), "gemm_i8 launch");
+}
+
+detint_status detint_gemm_w16(const int8_t* A, const int8_t* W_hi, const int8_t* W_lo, int64_t M,
+                              int64_t N, int64_t K, const int32_t* row_m, const int32_t* row_k,
+                              const int32_t* col_m, int32_t col_k, int32_t frac, int32_t mode,
+                              void* out, void* stream) {
+  detint_status s = check_gemm(A, W_hi, M, N, K, row_m, row_k, col_m, mode, out, 65536);
+  if (s != DETINT_OK || M == 0 || N == 0) return s;
+  REQUIRE(W_lo && aligned16(W_lo), "gemm_w16: W_lo null or misaligned");
+  Epi e{row_m, row_k, col_m, col_k, frac, mode, nullptr};
+  return hip_status(launch_gemm(A, W_hi, W_lo, M, N, K, e, out, S_(stream)), "gemm_w16 launch");
+}
+
+detint_status detint_split_w16(const int16_t* W16, int64_t n, int8_t* W_hi, int8_t* W_lo,
+                               void* stream) {
+  REQUIRE(n >= 0, "split_w16: n < 0");
+  if (n == 0) return ok();
+  REQUIRE(W16 && W_hi && W_lo, "split_w16: null pointer");
+  return hip_status(launch_split_w16(W16, n, W_hi, W_lo, S_(stream)), "split_w16 launch");
+}
+
+// ---------------------------------------------------------------- row ops
+
+detint_status detint_rmsnorm(const int32_t* h, const int16_t* gain, int64_t R, int64_t n,
+                             int8_t* x8, int32_t* row_m, int32_t* row_k, void* stream) {
+  REQUIRE(R >= 0 && n > 0 && n <= 16384, "rmsnorm: bad shape R=%lld n=%lld", (long long)R,
+          (long long)n);
+  if (R == 0) return ok();
+  REQUIRE(h && gain && x8 && row_m && row_k, "rmsnorm: null pointer");
+  return hip_status(launch_rmsnorm(h, nullptr, gain, R, n, x8, row_m, row_k, S_(stream)),
+                    "rmsnorm launch");
+}
+
+detint_status detint_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, int32_t* row_e,
+                             void* stream) {
+  REQUIRE(R >= 0 && n > 0 && n <= (int64_t)1 << 24, "requant: bad shape");
+  if (R == 0) return ok();
+  REQUIRE(y && q && row_e, "requant: null pointer");
+  return hip_status(launch_requant(y, R, n, q, row_e, nullptr, nullptr, 0, 0, S_(stream)),
+                    "requant launch");
+}
+
+detint_status detint_rope(int32_t* x, const int32_t* pos, const int16_t* cos_t,
+                          const int16_t* sin_t, int64_t R, int64_t heads, int64_t d,
+                          int64_t max_pos, void* stream) {
+  REQUIRE(R >= 0 && heads >= 0 && d > 0 && d % 2 == 0 && d <= 256 && max_pos > 0,
+          "rope: bad shape");
+  if (R == 0 || heads == 0) return ok();
+  REQUIRE(x && pos && cos_t && sin_t, "rope: null pointer");
+  return hip_status(launch_rope(x, pos, cos_t, sin_t, R, heads, d, max_pos, S_(stream)),
+                    "rope launch");
+}
+
+detint_status detint_softmax(const int32_t* s, const int32_t* valid, const int32_t* shift,
+                             int64_t R, int64_t C, int32_t mult_m, int32_t mult_k, int16_t* P,
+                             void* stream) {
+  REQUIRE(R >= 0 && C > 0 && C <= 65536, "softmax: bad shape");
+  if (R == 0) return ok();
+  REQUIRE(s && valid && shift && P, "softmax: null pointer");
+  REQUIRE(mult_m > 0 && mult_m < (1 << 16), "softmax: mult_m out of range");
+  return hip_status(launch_softmax(s, valid, shift, R, C, mult_m, mult_k, P, S_(stream)),
+                    "softmax launch");
+}
+
+detint_status detint_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int8_t* a8,
+                            int32_t* row_m, int32_t* row_k, void* stream) {
+  REQUIRE(R >= 0 && n > 0 && n <= 65536 && f_a >= 0 && f_a <= 24, "swiglu: bad shape");
+  if (R == 0) return ok();
+  REQUIRE(gu && a8 && row_m && row_k, "swiglu: null pointer");
+  int32_t Mg, Kg;
+  detint_swiglu_mult(f_a, &Mg, &Kg);
+  return hip_status(launch_swiglu(gu, R, n, f_a, Mg, Kg, a8, row_m, row_k, S_(stream)),
+                    "swiglu launch");
+}
+
+// -------------------------------------------------------------- attention
+
+static detint_status check_attn(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
+                                const int8_t* vc, int64_t nq, int64_t nkv, int64_t d,
+                                int64_t max_pos, const int32_t* out) {
+  REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0, "attention: n_q must be a multiple of n_kv");
+  REQUIRE(max_pos > 0 && max_pos <= 16384, "attention: max_pos out of range");
+  if (!attention_supported(d, nq / nkv, max_pos))
+    return fail(DETINT_EUNSUPPORTED, "attention: unsupported d=%lld group=%lld max_pos=%lld",
+                (long long)d, (long long)(nq / nkv), (long long)max_pos);
+  REQUIRE(q8 && e_q && kc && vc && out, "attention: null pointer");
+  REQUIRE(aligned16(q8) && aligned16(kc) && aligned16(vc), "attention: q8/cache misaligned");
+  return ok();
+}
+
+detint_status detint_attn_prefill(const int8_t* q8, const int32_t* e_q, const int8_t* k_cache,
+                                  const int8_t* v_cache, int64_t n_slots, const int32_t* cu_seqlens,
+                                  const int32_t* start_pos, const int32_t* slot, int64_t S,
+                                  int64_t R, int64_t n_q, int64_t n_kv, int64_t d,
+                                  int64_t max_pos, int32_t mult_m, int32_t mult_k, int32_t* out,
+                                  void* stream) {
+  REQUIRE(S >= 0 && R >= 0, "attn_prefill: bad sizes");
+  if (R == 0) return ok();
+  REQUIRE(S > 0 && cu_seqlens && start_pos && slot, "attn_prefill: null sequence arrays");
+  detint_status s = check_attn(q8, e_q, k_cache, v_cache, n_q, n_kv, d, max_pos, out);
+  if (s != DETINT_OK) return s;
+  REQUIRE(n_slots > 0, "attn_prefill: n_slots must be positive");
+  RowMap rows{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
+  return hip_status(launch_attention(q8, e_q, k_cache, v_cache, rows, R, n_q, n_kv, d, n_slots,
+                                     max_pos, mult_m, mult_k, out, S_(stream)),
+                    "attn_prefill launch");
+}
+
+detint_status detint_attn_decode(const int8_t* q8, const int32_t* e_q, const int8_t* k_cache,
+                                 const int8_t* v_cache, int64_t n_slots, const int32_t* ctx_len,
+                                 const int32_t* slot, int64_t B, int64_t n_q, int64_t n_kv,
+                                 int64_t d, int64_t max_pos, int32_t mult_m, int32_t mult_k,
+                                 int32_t* out, void* stream) {
+  REQUIRE(B >= 0, "attn_decode: bad sizes");
+  if (B == 0) return ok();
+  REQUIRE(ctx_len && slot, "attn_decode: null ctx_len/slot");
+  detint_status s = check_attn(q8, e_q, k_cache, v_cache, n_q, n_kv, d, max_pos, out);
+  if (s != DETINT_OK) return s;
+  REQUIRE(n_slots > 0, "attn_decode: n_slots must be positive");
+  RowMap rows{nullptr, nullptr, nullptr, 0, ctx_len, -1, slot};
+  return hip_status(launch_attention(q8, e_q, k_cache, v_cache, rows, B, n_q, n_kv, d, n_slots,
+                                     max_pos, mult_m, mult_k, out, S_(stream)),
+                    "attn_decode launch");
+}
+
+// ------------------------------------------------------ host set-up arithmetic
+
+detint_status detint_rope_tables(int16_t* cos_t, int16_t* sin_t, int64_t P, int64_t d,
+                                 int64_t base) {
+  REQUIRE(cos_t && sin_t && P > 0 && d > 0 && d % 2 == 0 && base > 1, "rope_tables: bad args");
+  const int64_t half = d / 2;
+  for (int64_t i = 0; i < half; ++i) {
+    const double theta = std::pow((double)base, -(double)(2 * i) / (double)d);
+    for (int64_t p = 0; p < P; ++p) {
+      const double a = (double)p * theta;
+      cos_t[p * half + i] = (int16_t)std::floor(16384.0 * std::cos(a) + 0.5);
+      sin_t[p * half + i] = (int16_t)std::floor(16384.0 * std::sin(a) + 0.5);
+    }
+  }
+  return ok();
+}
+
+// A positive real as (m, k) with m in [2^14, 2^15) and m * 2^-k nearest.
+static void to_dyadic(double x, int32_t* M, int32_t* K) {
+  int ex = 0;
+  const double f = std::frexp(x, &ex);  // x = f * 2^ex, f in [0.5, 1)
+  long long m = (long long)std::floor(std::ldexp(f, 15) + 0.5);
+  int k = 15 - ex;
+  if (m == 32768) {
+    m = 16384;
+    --k;
+  }
+  *M = (int32_t)m;
+  *K = k;
+}
+
+detint_status detint_softmax_mult(int32_t kq_m, int32_t kq_k, int64_t d, int32_t f_n,
+                                  int32_t* M, int32_t* K) {
+  REQUIRE(M && K && kq_m > 0 && d > 0, "softmax_mult: bad args");
+  const double log2e = 1.4426950408889634;
+  to_dyadic(std::ldexp(log2e, 15 + kq_k - 2 * f_n) / ((double)kq_m * std::sqrt((double)d)), M, K);
+  return ok();
+}
+
+detint_status detint_swiglu_mult(int32_t f_a, int32_t* M, int32_t* K) {
+  REQUIRE(M && K, "swiglu_mult: null");
+  to_dyadic(std::ldexp(1.4426950408889634, 15 - f_a), M, K);
+  return ok();
+}
+
+detint_status detint_v_dequant(int32_t vq_m, int32_t vq_k, int32_t* m, int32_t* k) {
+  REQUIRE(m && k && vq_m > 0, "v_dequant: bad args");
+  const long long a = 1LL << 29;
+  long long q = (2 * a + vq_m) / (2LL * vq_m);  // RD(2^29, vq_m)
+  int kk = 29 - vq_k;
+  if (q == 32768) {
+    q = 16384;
+    --kk;
+  }
+  *m = (int32_t)q;
+  *k = kk;
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ model
+
+struct detint_model {
+  detint_model_desc d;
+  std::vector<detint_layer_desc> layers;
+  std::vector<int32_t> sm_m, sm_k, vd_m, vd_k;
+  int32_t mg, kg;
+};
+
+namespace {
+
+constexpr int64_t kArgmaxParts = 64;
+
+int64_t al(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct WsLayout {
+  int64_t pos_of, slot_of, last_row, h, x8, rm, rk, qkv, q8, eq, att, gu, part, total;
+};
+
+WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
+  WsLayout w{};
+  const int64_t nqd = d.n_q * d.head_dim;
+  const int64_t nqkv = (d.n_q + 2 * d.n_kv) * d.head_dim;
+  int64_t kmax = d.hidden;
+  if (d.ffn > kmax) kmax = d.ffn;
+  if (nqd > kmax) kmax = nqd;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o += al(bytes);
+    return at;
+  };
+  const int64_t Rm = R > S ? R : S;
+  w.pos_of = take(4 * R);
+  w.slot_of = take(4 * R);
+  w.last_row = take(4 * S);
+  w.h = take(4 * R * d.hidden);
+  w.x8 = take(Rm * kmax);
+  w.rm = take(4 * Rm);
+  w.rk = take(4 * Rm);
+  w.qkv = take(4 * R * nqkv);
+  w.q8 = take(R * nqd);
+  w.eq = take(4 * R * d.n_q);
+  w.att = take(4 * R * nqd);
+  w.gu = take(4 * R * 2 * d.ffn);
+  w.part = take(8 * S * kArgmaxParts);
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+detint_status detint_model_create(const detint_model_desc* desc, detint_model** out) {
+  REQUIRE(desc && out, "model_create: null");
+  const detint_model_desc& d = *desc;
+  REQUIRE(d.n_layers > 0 && d.hidden > 0 && d.n_q > 0 && d.n_kv > 0 && d.head_dim > 0 &&
+              d.ffn > 0 && d.vocab >= 0 && d.max_pos > 0,
+          "model_create: bad dimensions");
+  REQUIRE(d.n_q % d.n_kv == 0, "model_create: n_q must be a multiple of n_kv");
+  REQUIRE(d.hidden % 16 == 0 && d.ffn % 16 == 0 && (d.n_q * d.head_dim) % 16 == 0,
+          "model_create: hidden, ffn and n_q*d must be multiples of 16");
+  REQUIRE(d.head_dim <= 128 && d.hidden <= 16384, "model_create: head_dim/hidden too large");
+  if (!attention_supported(d.head_dim, d.n_q / d.n_kv, d.max_pos))
+    return fail(DETINT_EUNSUPPORTED, "model_create: attention does not support d=%lld group=%lld max_pos=%lld",
+                (long long)d.head_dim, (long long)(d.n_q / d.n_kv), (long long)d.max_pos);
+  REQUIRE(d.layers && d.rope_cos && d.rope_sin, "model_create: null tensor pointer");
+  if (d.vocab > 0) {
+    REQUIRE(d.emb && d.emb_m && d.final_norm, "model_create: null embedding/final norm");
+    if (d.wide) REQUIRE(d.emb_lo, "model_create: wide model needs emb_lo");
+  }
+  for (int64_t l = 0; l < d.n_layers; ++l) {
+    const detint_layer_desc& L = d.layers[l];
+    REQUIRE(L.wqkv && L.wqkv_m && L.wo && L.wo_m && L.wgu && L.wgu_m && L.wd && L.wd_m &&
+                L.attn_norm && L.ffn_norm,
+            "model_create: layer %lld has a null pointer", (long long)l);
+    if (d.qk_norm) REQUIRE(L.q_norm && L.k_norm, "model_create: qk_norm needs q/k gains");
+    if (d.wide) REQUIRE(L.wqkv_lo && L.wo_lo && L.wgu_lo && L.wd_lo, "model_create: wide limbs");
+  }
+  REQUIRE(!(d.wide && d.qk_norm), "model_create: wide weights with q/k-norm not supported");
+  detint_model* m = new detint_model();
+  m->d = d;
+  m->layers.assign(d.layers, d.layers + d.n_layers);
+  m->d.layers = nullptr;
+  for (auto& L : m->layers) {
+    int32_t a, b;
+    detint_softmax_mult(L.kq_m, L.kq_k, d.head_dim, d.f_n, &a, &b);
+    m->sm_m.push_back(a);
+    m->sm_k.push_back(b);
+    detint_v_dequant(L.vq_m, L.vq_k, &a, &b);
+    m->vd_m.push_back(a);
+    m->vd_k.push_back(b);
+  }
+  detint_swiglu_mult(d.f_a, &m->mg, &m->kg);
+  *out = m;
+  return ok();
+}
+
+void detint_model_destroy(detint_model* m) { delete m; }
+
+int64_t detint_workspace_size(const detint_model* m, int64_t max_rows, int64_t max_seqs) {
+  if (!m || max_rows < 0 || max_seqs < 0) return -1;
+  return ws_layout(m->d, max_rows, max_seqs).total;
+}
+
+// One decoder layer in place on h [R, H] (workspace buffers from w).
+static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int8_t* k_cache,
+                               int8_t* v_cache, int64_t n_slots, int64_t R, char* base,
+                               const WsLayout& w, hipStream_t st) {
+  const detint_model_desc& d = m->d;
+  const detint_layer_desc& L = m->layers[l];
+  int32_t* pos_of = (int32_t*)(base + w.pos_of);
+  int32_t* slot_of = (int32_t*)(base + w.slot_of);
+  int8_t* x8 = (int8_t*)(base + w.x8);
+  int32_t* rm = (int32_t*)(base + w.rm);
+  int32_t* rk = (int32_t*)(base + w.rk);
+  int32_t* qkv = (int32_t*)(base + w.qkv);
+  int8_t* q8 = (int8_t*)(base + w.q8);
+  int32_t* eq = (int32_t*)(base + w.eq);
+  int32_t* att = (int32_t*)(base + w.att);
+  int32_t* gu = (int32_t*)(base + w.gu);
+  const int64_t H = d.hidden, nq = d.n_q, nkv = d.n_kv, hd = d.head_dim, F = d.ffn;
+  const int64_t nqd = nq * hd, nqkv = (nq + 2 * nkv) * hd;
+  const size_t layer_stride = (size_t)n_slots * nkv * d.max_pos * hd;
+  const int32_t wk = d.w_k;
+  int8_t* kc = k_cache + l * layer_stride;
+  int8_t* vc = v_cache + l * layer_stride;
+  const RowMap rows{nullptr, nullptr, nullptr, 0, pos_of, 0, slot_of};
+  hipError_t e;
+#define LAUNCH(x)                                  \
+  do {                                             \
+    e = (x);                                       \
+    if (e != hipSuccess) return hip_status(e, #x); \
+  } while (0)
+  // attention block: RMSNorm -> QKV -> q/k-norm, RoPE, q DQ, K/V cache ->
+  // attention -> DQ -> O-proj + residual
+  LAUNCH(launch_rmsnorm(h, nullptr, L.attn_norm, R, H, x8, rm, rk, st));
+  {
+    Epi ep{rm, rk, L.wqkv_m, wk, d.qk_norm ? 0 : d.f_n, d.qk_norm ? MODE_RAW : MODE_FIX, nullptr};
+    LAUNCH(launch_gemm(x8, L.wqkv, d.wide ? L.wqkv_lo : nullptr, R, nqkv, H, ep, qkv, st));
+  }
+  QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
+             L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
+  LAUNCH(launch_qkv_post(qkv, R, nq, nkv, hd, pos_of, slot_of, qp, q8, eq, kc, vc, n_slots,
+                         d.max_pos, st));
+  LAUNCH(launch_attention(q8, eq, kc, vc, rows, R, nq, nkv, hd, n_slots, d.max_pos, m->sm_m[l],
+                          m->sm_k[l], att, st));
+  LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
+  {
+    Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr};
+    LAUNCH(launch_gemm(x8, L.wo, d.wide ? L.wo_lo : nullptr, R, H, nqd, ep, h, st));
+  }
+  // FFN block: RMSNorm -> gate/up -> DI-SwiGLU -> down + residual
+  LAUNCH(launch_rmsnorm(h, nullptr, L.ffn_norm, R, H, x8, rm, rk, st));
+  {
+    Epi ep{rm, rk, L.wgu_m, wk, d.f_a, MODE_FIX, nullptr};
+    LAUNCH(launch_gemm(x8, L.wgu, d.wide ? L.wgu_lo : nullptr, R, 2 * F, H, ep, gu, st));
+  }
+  LAUNCH(launch_swiglu(gu, R, F, d.f_a, m->mg, m->kg, x8, rm, rk, st));
+  {
+    Epi ep{rm, rk, L.wd_m, wk, d.f_res, MODE_RES_ADD, nullptr};
+    LAUNCH(launch_gemm(x8, L.wd, d.wide ? L.wd_lo : nullptr, R, H, F, ep, h, st));
+  }
+#undef LAUNCH
+  return ok();
+}
+
+static detint_status check_run(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
+                               int64_t n_slots, int64_t R, const int32_t* cu_seqlens,
+                               const int32_t* start_pos, const int32_t* slot, int64_t S,
+                               int64_t max_seqlen, void* ws, int64_t ws_bytes) {
+  REQUIRE(m, "forward: null model");
+  REQUIRE(R >= 0 && S >= 0 && n_slots > 0, "forward: bad sizes");
+  REQUIRE(S > 0 && R >= S, "forward: need 1 <= S <= R (every sequence has a row)");
+  REQUIRE(k_cache && v_cache && cu_seqlens && start_pos && slot && ws, "forward: null pointer");
+  REQUIRE(aligned16(k_cache) && aligned16(v_cache) && aligned16(ws), "forward: misaligned buffer");
+  REQUIRE(max_seqlen >= 1 && max_seqlen <= R, "forward: bad max_seqlen");
+  const WsLayout w = ws_layout(m->d, R, S);
+  REQUIRE(ws_bytes >= w.total, "forward: workspace %lld < %lld bytes", (long long)ws_bytes,
+          (long long)w.total);
+  return ok();
+}
+
+detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t* h,
+                                   int8_t* k_cache, int8_t* v_cache, int64_t n_slots, int64_t R,
+                                   const int32_t* cu_seqlens, const int32_t* start_pos,
+                                   const int32_t* slot, int64_t S, int64_t max_seqlen, void* ws,
+                                   int64_t ws_bytes, void* stream) {
+  if (R == 0 && S == 0) return ok();
+  detint_status s = check_run(m, k_cache, v_cache, n_slots, R, cu_seqlens, start_pos, slot, S,
+                              max_seqlen, ws, ws_bytes);
+  if (s != DETINT_OK) return s;
+  REQUIRE(h && layer >= 0 && layer < m->d.n_layers, "layer_forward: bad layer or null h");
+  const WsLayout w = ws_layout(m->d, R, S);
+  char* base = (char*)ws;
+  hipStream_t st = S_(stream);
+  hipError_t e = launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
+                                  (int32_t*)(base + w.slot_of), (int32_t*)(base + w.last_row), st);
+  if (e != hipSuccess) return hip_status(e, "rows_meta");
+  return run_layer(m, layer, h, k_cache, v_cache, n_slots, R, base, w, st);
+}
+
+detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
+                             int64_t n_slots, int32_t* ids, int64_t R, const int32_t* cu_seqlens,
+                             int32_t* start_pos, const int32_t* slot, int64_t S,
+                             int64_t max_seqlen, int32_t* logits, int32_t* logit_row_base,
+                             int32_t* next_tok, int32_t flags, void* ws, int64_t ws_bytes,
+                             void* stream) {
+  if (R == 0 && S == 0) return ok();
+  detint_status s = check_run(m, k_cache, v_cache, n_slots, R, cu_seqlens, start_pos, slot, S,
+                              max_seqlen, ws, ws_bytes);
+  if (s != DETINT_OK) return s;
+  REQUIRE(ids && logits && next_tok, "forward: null ids/logits/next_tok");
+  REQUIRE(m->d.vocab > 0 && m->d.emb, "forward: model has no vocabulary");
+  if (flags & DETINT_FWD_ADVANCE) REQUIRE(R == S, "forward: ADVANCE needs one row per sequence");
+  const detint_model_desc& d = m->d;
+  const WsLayout w = ws_layout(d, R, S);
+  hipStream_t st = S_(stream);
+  char* base = (char*)ws;
+  int32_t* last_row = (int32_t*)(base + w.last_row);
+  int32_t* h = (int32_t*)(base + w.h);
+  int8_t* x8 = (int8_t*)(base + w.x8);
+  int32_t* rm = (int32_t*)(base + w.rm);
+  int32_t* rk = (int32_t*)(base + w.rk);
+  int64_t* part = (int64_t*)(base + w.part);
+  hipError_t e;
+#define LAUNCH(x)                                  \
+  do {                                             \
+    e = (x);                                       \
+    if (e != hipSuccess) return hip_status(e, #x); \
+  } while (0)
+  LAUNCH(launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
+                          (int32_t*)(base + w.slot_of), last_row, st));
+  LAUNCH(launch_embed(ids, R, d.emb, d.wide ? d.emb_lo : nullptr, d.emb_m, d.hidden, d.vocab,
+                      d.w_k - d.f_res, h, st));
+  for (int64_t l = 0; l < d.n_layers; ++l) {
+    s = run_layer(m, l, h, k_cache, v_cache, n_slots, R, base, w, st);
+    if (s != DETINT_OK) return s;
+  }
+  // final norm on each sequence's last row, tied lm_head, greedy token
+  LAUNCH(launch_rmsnorm(h, last_row, d.final_norm, S, d.hidden, x8, rm, rk, st));
+  {
+    Epi ep{rm, rk, d.emb_m, d.w_k, d.f_l, MODE_FIX, logit_row_base};
+    LAUNCH(launch_gemm(x8, d.emb, d.wide ? d.emb_lo : nullptr, S, d.vocab, d.hidden, ep, logits,
+                       st));
+  }
+  LAUNCH(launch_argmax(logits, logit_row_base, S, d.vocab, part, kArgmaxParts, next_tok, st));
+  if (flags & DETINT_FWD_ADVANCE)
+    LAUNCH(launch_advance(ids, next_tok, start_pos, logit_row_base, S, st));
+#undef LAUNCH
+  return ok();
+}
+
+}  // extern "C"

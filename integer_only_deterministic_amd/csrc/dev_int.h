@@ -1,0 +1,185 @@
+// Device integer primitives for gfx950 kernels of libdetint.
+//
+// Everything here is integer arithmetic. Division and square root are
+// bit-serial integer routines rather than the compiler's `/`, whose AMDGPU
+// lowering seeds its quotient with a float reciprocal; these run once per row
+// (or once per element on 16-bit quotients) and keep the ISA float-free.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace detint {
+
+constexpr int kWave = 64;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Round-half-up shift R(x, s): floor(x / 2^s + 1/2) for s >= 1, x for s = 0,
+// x * 2^-s for s < 0 (DetLLM blog "DetLLM": one fixed rounding rule for every
+// dyadic rescale). Shifts past 62 give 0 (inputs here stay below 2^61).
+__device__ __forceinline__ int64_t R(int64_t x, int s) {
+  if (s > 0) {
+    if (s > 62) return 0;
+    return (x + (int64_t(1) << (s - 1))) >> s;
+  }
+  return x * (int64_t(1) << (-s));
+}
+
+__device__ __forceinline__ int64_t R128(__int128 x, int s) {
+  if (s > 0) {
+    if (s > 126) return 0;
+    return (int64_t)((x + ((__int128)1 << (s - 1))) >> s);
+  }
+  return (int64_t)(x * ((__int128)1 << (-s)));
+}
+
+__device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __builtin_clzll(x) : 0; }
+
+__device__ __forceinline__ int8_t clamp8(int64_t x) {
+  return (int8_t)(x > 127 ? 127 : (x < -127 ? -127 : x));
+}
+
+__device__ __forceinline__ uint64_t uabs64(int64_t x) {
+  return x < 0 ? (uint64_t)0 - (uint64_t)x : (uint64_t)x;
+}
+
+// floor(n / d) for d > 0 by restoring binary long division.
+__device__ __forceinline__ uint64_t udiv64(uint64_t n, uint64_t d) {
+  uint64_t q = 0, r = 0;
+  for (int i = bitlen64(n) - 1; i >= 0; --i) {
+    r = (r << 1) | ((n >> i) & 1);
+    if (r >= d) {
+      r -= d;
+      q |= uint64_t(1) << i;
+    }
+  }
+  return q;
+}
+
+// RD(a, b) = floor((2a + b) / 2b), a >= 0, b > 0.
+__device__ __forceinline__ int64_t div_round(int64_t a, int64_t b) {
+  return (int64_t)udiv64(2 * (uint64_t)a + (uint64_t)b, 2 * (uint64_t)b);
+}
+
+// floor(sqrt(n)), digit-by-digit.
+__device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
+  uint64_t res = 0;
+  uint64_t bit = uint64_t(1) << 62;
+  while (bit > n) bit >>= 2;
+  while (bit) {
+    if (n >= res + bit) {
+      n -= res + bit;
+      res = (res >> 1) + bit;
+    } else {
+      res >>= 1;
+    }
+    bit >>= 2;
+  }
+  return res;
+}
+
+// Inverse RMS of n entries with sum of squares S > 0: 1/sqrt(S/n) ~ m * 2^-sh,
+// m in [2^14, 2^15) (DetLLM README "Layout": DI-RMSNorm).
+__device__ __forceinline__ void irms(int64_t S, int64_t n, int32_t& m, int32_t& sh) {
+  const int b = bitlen64((uint64_t)S);
+  const int c = b < 62 ? (62 - b) >> 1 : 0;
+  const uint64_t u = udiv64((uint64_t)S << (2 * c), (uint64_t)n);
+  const uint64_t r = isqrt64(u);
+  int T = bitlen64(r) + 14;
+  int64_t mm = div_round(int64_t(1) << T, (int64_t)r);
+  if (mm == (1 << 15)) {
+    mm = 1 << 14;
+    T -= 1;
+  }
+  m = (int32_t)mm;
+  sh = T - c;
+}
+
+// DI-Exp (DetLLM README "Layout"; shift-based exp as in I-ViT's Shiftmax):
+// u <= 0 is a base-2 exponent in Q15; returns E ~ 2^15 * 2^(u / 2^15), using
+// 2^(-r/2^15) ~ 1 - r/2^16 on the fractional part and a shift for the rest.
+__device__ __forceinline__ int32_t diexp(int64_t u) {
+  const int64_t v = -u;
+  const int64_t n = v >> 15;
+  const int64_t r = v & 32767;
+  const int64_t f = 32768 - ((r + 1) >> 1);
+  if (n > 30) return 0;
+  return (int32_t)R(f, (int)n);
+}
+
+// Integer sigmoid in Q15 of a gate g with f_a fractional bits, given the
+// exponent multiplier (Mg, Kg): E = DI-Exp(-R(|g| Mg, Kg)),
+// s+ = RD(2^30, 2^15 + E) computed by a 17-step restoring division (the
+// quotient is below 2^16), s = s+ or 2^15 - s+ by the sign of g.
+__device__ __forceinline__ int32_t sigmoid_q15(int64_t g, int32_t Mg, int32_t Kg) {
+  const int64_t ag = g < 0 ? -g : g;
+  const uint32_t E = (uint32_t)diexp(-R(ag * Mg, Kg));
+  const uint64_t b2 = 2u * (32768u + E);          // 2b in [2^16, 2^17]
+  uint64_t num = (1ull << 31) + (32768u + E);     // 2a + b with a = 2^30
+  uint32_t q = 0;
+#pragma unroll
+  for (int i = 15; i >= 0; --i) {
+    const uint64_t t = b2 << i;
+    if (num >= t) {
+      num -= t;
+      q |= 1u << i;
+    }
+  }
+  return (int32_t)(g >= 0 ? q : 32768 - q);
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int64_t wave_max(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    int64_t w = __shfl_xor(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = (uint64_t)__shfl_xor((long long)v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Block-wide reductions for blockDim.x a multiple of 64 (<= 1024); `red` is
+// shared scratch of >= 16 entries. All threads receive the result.
+__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+__device__ __forceinline__ int64_t block_max(int64_t v, int64_t* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int64_t t = red[0];
+  for (int i = 1; i < nw; ++i) t = red[i] > t ? red[i] : t;
+  return t;
+}
+
+// DQ exponent from the absolute maximum: e = max(0, bitlen(A) - 7).
+__device__ __forceinline__ int dq_exp(uint64_t A) {
+  const int b = bitlen64(A);
+  return b > 7 ? b - 7 : 0;
+}
+
+}  // namespace detint

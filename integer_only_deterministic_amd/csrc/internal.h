@@ -1,0 +1,102 @@
+// Internal launchers shared by the libdetint translation units (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace detint {
+
+enum { MODE_RAW = 0, MODE_REQ_I8 = 1, MODE_FIX = 2, MODE_RES_ADD = 3 };
+
+// Dyadic epilogue parameters of a GEMM (see detint.h, detint_gemm_i8).
+struct Epi {
+  const int32_t* row_m;
+  const int32_t* row_k;
+  const int32_t* col_m;
+  int32_t col_k;
+  int32_t frac;
+  int32_t mode;
+  const int32_t* out_row_base;  // nullable: output row i goes to row *base + i
+};
+
+// C = A[M,K] . W[N,K]^T with epilogue; W_lo != nullptr selects 16-bit limbs.
+hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
+                       int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st);
+hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
+                            hipStream_t st);
+
+// Row ops.
+hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int16_t* gain,
+                          int64_t R, int64_t n, int8_t* x8, int32_t* row_m, int32_t* row_k,
+                          hipStream_t st);
+// DQ of each row; optionally also a row scale (fold_m, fold_k - e) into
+// row_m / row_k (the attention output's scale folds the V dequant scale).
+hipError_t launch_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, int32_t* row_e,
+                          int32_t* row_m, int32_t* row_k, int32_t fold_m, int32_t fold_k,
+                          hipStream_t st);
+hipError_t launch_rope(int32_t* x, const int32_t* pos, const int16_t* cos_t,
+                       const int16_t* sin_t, int64_t R, int64_t heads, int64_t d, int64_t max_pos,
+                       hipStream_t st);
+hipError_t launch_softmax(const int32_t* s, const int32_t* valid, const int32_t* shift,
+                          int64_t R, int64_t C, int32_t M, int32_t K, int16_t* P,
+                          hipStream_t st);
+hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int32_t Mg,
+                         int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st);
+hipError_t launch_embed(const int32_t* ids, int64_t R, const int8_t* emb, const int8_t* emb_lo,
+                        const int32_t* emb_m, int64_t H, int64_t V, int32_t shift, int32_t* h,
+                        hipStream_t st);
+
+// Per-row metadata of packed sequences: pos_of/slot_of [R], last_row [S].
+hipError_t launch_rows_meta(const int32_t* cu, const int32_t* start, const int32_t* slot,
+                            int64_t S, int32_t* pos_of, int32_t* slot_of, int32_t* last_row,
+                            hipStream_t st);
+hipError_t launch_decode_meta(const int32_t* ctx_len, const int32_t* slot, int64_t B,
+                              int32_t* pos_of, int32_t* slot_of, hipStream_t st);
+
+// QKV post-processing: q/k-norm (or fixed-point input), RoPE, q DQ, K/V cache
+// writes. qkv int32 [R, (nq + 2 nkv) d].
+struct QkvPost {
+  int32_t qk_norm;            // 1: qkv holds raw accumulators; 0: f_n fixed point
+  const int32_t* row_m;       // row scale of the GEMM input (raw mode, V)
+  const int32_t* row_k;
+  const int32_t* col_m;       // column mantissas of Wqkv (raw mode)
+  int32_t col_k;
+  const int16_t* q_norm;
+  const int16_t* k_norm;
+  int32_t f_n;
+  int32_t kq_m, kq_k, vq_m, vq_k;
+  const int16_t* cos_t;
+  const int16_t* sin_t;
+};
+hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nkv, int64_t d,
+                           const int32_t* pos_of, const int32_t* slot_of, const QkvPost& p,
+                           int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
+                           int64_t max_pos, hipStream_t st);
+
+// Where a row sits: either packed sequences (cu != nullptr: row r belongs to
+// the sequence s with cu[s] <= r < cu[s+1], position start[s] + r - cu[s],
+// slot seq_slot[s]) or per-row arrays (position pos[r] + bias, slot slot[r]).
+struct RowMap {
+  const int32_t* cu;
+  const int32_t* start;
+  const int32_t* seq_slot;
+  int32_t S;
+  const int32_t* pos;
+  int32_t bias;
+  const int32_t* slot;
+};
+
+// Attention over the cache for R rows.
+hipError_t launch_attention(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
+                            const int8_t* vc, const RowMap& rows, int64_t R, int64_t nq,
+                            int64_t nkv, int64_t d, int64_t n_slots, int64_t max_pos, int32_t M,
+                            int32_t K, int32_t* out, hipStream_t st);
+// true when the attention kernel supports (d, n_q / n_kv, max_pos)
+bool attention_supported(int64_t d, int64_t group, int64_t max_pos);
+
+// Greedy argmax over rows of int32 logits (lowest index among maxima).
+hipError_t launch_argmax(const int32_t* logits, const int32_t* row_base, int64_t S, int64_t V,
+                         int64_t* part, int64_t nparts, int32_t* out, hipStream_t st);
+hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
+                          int32_t* row_base, int64_t S, hipStream_t st);
+
+}  // namespace detint

@@ -1,0 +1,412 @@
+// Row kernels of libdetint for gfx950: DI-RMSNorm, per-token DQ, integer
+// RoPE, DI-Softmax, DI-SwiGLU, embedding, QKV post-processing with the int8
+// KV-cache writes, greedy argmax. One workgroup (or wave) per row; row
+// statistics (sum of squares, absolute maximum, exponential sums) are exact
+// int64 reductions across lanes with shuffles and LDS, so their order cannot
+// matter (DetLLM README, "Why ...": integer sums are associative).
+#include "dev_int.h"
+#include "internal.h"
+
+namespace detint {
+namespace {
+
+constexpr int TPB = 256;
+
+// DI-RMSNorm (DetLLM README "Layout", ops/): x8 * m * 2^-k ~ h * g/2^12 / rms(h).
+__global__ __launch_bounds__(TPB) void rmsnorm_k(const int32_t* __restrict__ h,
+                                                 const int32_t* __restrict__ row_index,
+                                                 const int16_t* __restrict__ g, int n,
+                                                 int8_t* __restrict__ x8,
+                                                 int32_t* __restrict__ rm,
+                                                 int32_t* __restrict__ rk) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int src = row_index ? row_index[r] : r;
+  const int32_t* hr = h + (size_t)src * n;
+  int64_t S = 0, A = 0;
+  for (int i = threadIdx.x; i < n; i += TPB) {
+    const int64_t v = hr[i];
+    S += v * v;
+    const int64_t p = (int64_t)uabs64(v * g[i]);
+    A = p > A ? p : A;
+  }
+  S = block_sum(S, red);
+  A = block_max(A, red);
+  int8_t* xr = x8 + (size_t)r * n;
+  if (S == 0) {
+    for (int i = threadIdx.x; i < n; i += TPB) xr[i] = 0;
+    if (threadIdx.x == 0) {
+      rm[r] = 1 << 14;
+      rk[r] = 26;
+    }
+    return;
+  }
+  int32_t m, sh;
+  irms(S, n, m, sh);
+  const int e = dq_exp((uint64_t)A);
+  for (int i = threadIdx.x; i < n; i += TPB) xr[i] = clamp8(R((int64_t)hr[i] * g[i], e));
+  if (threadIdx.x == 0) {
+    rm[r] = m;
+    rk[r] = sh + 12 - e;
+  }
+}
+
+// Per-token DQ (DetLLM blog "DetLLM": a token's activations are quantised
+// from its own values): q = clamp8(R(y, e)), e from the row's |max|.
+__global__ __launch_bounds__(TPB) void requant_k(const int32_t* __restrict__ y, int n,
+                                                 int8_t* __restrict__ q, int32_t* row_e,
+                                                 int32_t* row_m, int32_t* row_k, int32_t fm,
+                                                 int32_t fk) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int32_t* yr = y + (size_t)r * n;
+  int64_t A = 0;
+  for (int i = threadIdx.x; i < n; i += TPB) {
+    const int64_t a = (int64_t)uabs64(yr[i]);
+    A = a > A ? a : A;
+  }
+  A = block_max(A, red);
+  const int e = dq_exp((uint64_t)A);
+  for (int i = threadIdx.x; i < n; i += TPB) q[(size_t)r * n + i] = clamp8(R(yr[i], e));
+  if (threadIdx.x == 0) {
+    if (row_e) row_e[r] = e;
+    if (row_m) {
+      row_m[r] = fm;
+      row_k[r] = fk - e;
+    }
+  }
+}
+
+// Integer RoPE on pairs (i, i + d/2) with Q1.14 tables.
+__global__ void rope_k(int32_t* __restrict__ x, const int32_t* __restrict__ pos,
+                       const int16_t* __restrict__ ct, const int16_t* __restrict__ stab,
+                       int heads, int d, int max_pos) {
+  const int r = blockIdx.x, hh = blockIdx.y, i = threadIdx.x;
+  const int half = d >> 1;
+  if (i >= half || pos[r] < 0 || pos[r] >= max_pos) return;  // out of table: untouched
+  int32_t* v = x + ((size_t)r * heads + hh) * d;
+  const int64_t a = v[i], b = v[i + half];
+  const int64_t c = ct[(size_t)pos[r] * half + i], s = stab[(size_t)pos[r] * half + i];
+  v[i] = (int32_t)R(a * c - b * s, 14);
+  v[i + half] = (int32_t)R(b * c + a * s, 14);
+}
+
+// DI-Softmax with 15-bit probabilities (DetLLM blog, footnote 8).
+__global__ __launch_bounds__(TPB) void softmax_k(const int32_t* __restrict__ s,
+                                                 const int32_t* __restrict__ valid,
+                                                 const int32_t* __restrict__ shift, int C,
+                                                 int32_t Mm, int32_t Kk, int16_t* __restrict__ P) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int32_t* sr = s + (size_t)r * C;
+  int v = valid[r];
+  v = v < 1 ? 1 : (v > C ? C : v);
+  const int sh = Kk - shift[r];
+  int64_t mx = INT64_MIN;
+  for (int j = threadIdx.x; j < v; j += TPB) mx = sr[j] > mx ? sr[j] : mx;
+  mx = block_max(mx, red);
+  int64_t D = 0;
+  for (int j = threadIdx.x; j < v; j += TPB) D += diexp(R((sr[j] - mx) * Mm, sh));
+  D = block_sum(D, red);
+  const int64_t Rn = (int64_t)udiv64(uint64_t(1) << 46, (uint64_t)D);
+  for (int j = threadIdx.x; j < C; j += TPB) {
+    int64_t p = 0;
+    if (j < v) {
+      p = R((int64_t)diexp(R((sr[j] - mx) * Mm, sh)) * Rn, 31);
+      p = p > 32767 ? 32767 : p;
+    }
+    P[(size_t)r * C + j] = (int16_t)p;
+  }
+}
+
+// DI-SwiGLU (DetLLM README "Layout"): a8 * 2^(e - 2 f_a) ~ silu(g) * u.
+__device__ __forceinline__ int64_t swiglu_p(int64_t g, int64_t u, int32_t Mg, int32_t Kg) {
+  return R(g * sigmoid_q15(g, Mg, Kg), 15) * u;
+}
+
+__global__ __launch_bounds__(TPB) void swiglu_k(const int32_t* __restrict__ gu, int n, int32_t f_a,
+                                                int32_t Mg, int32_t Kg, int8_t* __restrict__ a8,
+                                                int32_t* __restrict__ rm, int32_t* __restrict__ rk) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int32_t* g = gu + (size_t)r * 2 * n;
+  const int32_t* u = g + n;
+  int64_t A = 0;
+  for (int j = threadIdx.x; j < n; j += TPB) {
+    const int64_t p = (int64_t)uabs64(swiglu_p(g[j], u[j], Mg, Kg));
+    A = p > A ? p : A;
+  }
+  A = block_max(A, red);
+  const int e = dq_exp((uint64_t)A);
+  for (int j = threadIdx.x; j < n; j += TPB)
+    a8[(size_t)r * n + j] = clamp8(R(swiglu_p(g[j], u[j], Mg, Kg), e));
+  if (threadIdx.x == 0) {
+    rm[r] = 1 << 14;
+    rk[r] = 2 * f_a - e + 14;
+  }
+}
+
+// Embedding rounded once onto the residual grid (BitExact blog, "Three
+// execution paths"): h = R(E[id] * m_v[id], w_k - f_res).
+__global__ __launch_bounds__(TPB) void embed_k(const int32_t* __restrict__ ids,
+                                               const int8_t* __restrict__ emb,
+                                               const int8_t* __restrict__ emb_lo,
+                                               const int32_t* __restrict__ emb_m, int H, int V,
+                                               int shift, int32_t* __restrict__ h) {
+  const int r = blockIdx.x;
+  const int64_t id = ids[r];
+  if (id < 0 || id >= V) {  // out-of-vocabulary id: zero row
+    for (int i = threadIdx.x; i < H; i += TPB) h[(size_t)r * H + i] = 0;
+    return;
+  }
+  const int64_t m = emb_m[id];
+  for (int i = threadIdx.x; i < H; i += TPB) {
+    int64_t e = emb[id * H + i];
+    if (emb_lo) e = 256 * e + (int64_t)emb_lo[id * H + i] + 128;
+    h[(size_t)r * H + i] = (int32_t)R(e * m, shift);
+  }
+}
+
+__global__ void rows_meta_k(const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
+                            const int32_t* __restrict__ slot, int32_t* pos_of, int32_t* slot_of,
+                            int32_t* last_row) {
+  const int s = blockIdx.x;
+  const int b = cu[s], e = cu[s + 1];
+  for (int r = b + threadIdx.x; r < e; r += blockDim.x) {
+    pos_of[r] = start[s] + (r - b);
+    slot_of[r] = slot[s];
+  }
+  if (threadIdx.x == 0 && last_row) last_row[s] = e - 1;
+}
+
+__global__ void decode_meta_k(const int32_t* __restrict__ ctx, const int32_t* __restrict__ slot,
+                              int B, int32_t* pos_of, int32_t* slot_of) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    pos_of[b] = ctx[b] - 1;
+    slot_of[b] = slot[b];
+  }
+}
+
+// QKV post-processing, one wave per (row, head); lane i < d/2 owns the RoPE
+// pair (i, i + d/2). q/k: per-head RMSNorm (Qwen3 q/k-norm, before RoPE per
+// DetLLM blog footnote 8) or the f_n fixed point, then RoPE; q -> DQ per
+// head; k, v -> int8 at the fixed cache scales, written once into the cache
+// (DetLLM blog "DetLLM": prefill and decode read the same cached bits).
+__global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qkv, int nq, int nkv,
+                                                  int d, const int32_t* __restrict__ pos_of,
+                                                  const int32_t* __restrict__ slot_of, QkvPost p,
+                                                  int8_t* __restrict__ q8, int32_t* __restrict__ e_q,
+                                                  int8_t* __restrict__ kc, int8_t* __restrict__ vc,
+                                                  int n_slots, int max_pos) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = d >> 1;
+  const int nh = nq + 2 * nkv;
+  const int pos = pos_of[r], slot = slot_of[r];
+  const bool ok = pos >= 0 && pos < max_pos && slot >= 0 && slot < n_slots;
+  const bool act = lane < half;
+  const int j0 = lane, j1 = lane + half;
+  const int32_t* row = qkv + (size_t)r * nh * d;
+  for (int hh = wave; hh < nh; hh += TPB / 64) {
+    const int c0 = hh * d;
+    if (hh >= nq + nkv) {  // V
+      if (!act || !ok) continue;
+      const int kvh = hh - nq - nkv;
+      int8_t* dst = vc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = t ? j1 : j0;
+        int64_t vf = row[c0 + j];
+        if (p.qk_norm)
+          vf = R(vf * p.row_m[r] * p.col_m[c0 + j], p.row_k[r] + p.col_k - p.f_n);
+        dst[j] = clamp8(R(vf * p.vq_m, p.vq_k));
+      }
+      continue;
+    }
+    int64_t x0 = 0, x1 = 0;
+    if (act) {
+      x0 = row[c0 + j0];
+      x1 = row[c0 + j1];
+    }
+    if (p.qk_norm) {
+      const int16_t* gn = hh < nq ? p.q_norm : p.k_norm;
+      int64_t a0 = act ? x0 * p.col_m[c0 + j0] : 0, a1 = act ? x1 * p.col_m[c0 + j1] : 0;
+      const uint64_t u0 = uabs64(a0), u1 = uabs64(a1);
+      const int b = bitlen64(wave_max_u(u0 > u1 ? u0 : u1));
+      const int sh0 = b > 24 ? b - 24 : 0;
+      a0 = R(a0, sh0);
+      a1 = R(a1, sh0);
+      const int64_t S = wave_sum(a0 * a0 + a1 * a1);
+      if (S == 0) {
+        x0 = x1 = 0;
+      } else {
+        int32_t m, sh;
+        irms(S, d, m, sh);
+        if (act) {
+          x0 = R(a0 * gn[j0] * m, sh + 12 - p.f_n);
+          x1 = R(a1 * gn[j1] * m, sh + 12 - p.f_n);
+        }
+      }
+    }
+    int64_t y0 = 0, y1 = 0;
+    if (act && ok) {
+      const int64_t c = p.cos_t[(size_t)pos * half + lane], s = p.sin_t[(size_t)pos * half + lane];
+      y0 = R(x0 * c - x1 * s, 14);
+      y1 = R(x1 * c + x0 * s, 14);
+    }
+    if (hh < nq) {
+      const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
+      const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
+      int8_t* dst = q8 + ((size_t)r * nq + hh) * d;
+      if (act) {
+        dst[j0] = clamp8(R(y0, e));
+        dst[j1] = clamp8(R(y1, e));
+      }
+      if (lane == 0) e_q[(size_t)r * nq + hh] = e;
+    } else if (act && ok) {
+      const int kvh = hh - nq;
+      int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+      dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k));
+      dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k));
+    }
+  }
+}
+
+// Greedy argmax with the lowest index among maxima (DetLLM blog "DetLLM").
+// Key = value << 32 | (2^32 - 1 - index): the largest key is the largest
+// value at the smallest index, and max is order-free.
+__device__ __forceinline__ int64_t amax_key(int32_t v, int64_t j) {
+  return ((int64_t)v * 4294967296LL) | (int64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+__global__ __launch_bounds__(TPB) void argmax_part_k(const int32_t* __restrict__ logits,
+                                                     const int32_t* row_base, int V, int nparts,
+                                                     int chunk, int64_t* part) {
+  __shared__ int64_t red[16];
+  const int s = blockIdx.y, pi = blockIdx.x;
+  const int64_t base = row_base ? *row_base : 0;
+  const int32_t* L = logits + (base + s) * (int64_t)V;
+  const int lo = pi * chunk, hi = lo + chunk < V ? lo + chunk : V;
+  int64_t best = INT64_MIN;
+  for (int j = lo + threadIdx.x; j < hi; j += TPB) {
+    const int64_t k = amax_key(L[j], j);
+    best = k > best ? k : best;
+  }
+  best = block_max(best, red);
+  if (threadIdx.x == 0) part[(size_t)s * nparts + pi] = best;
+}
+
+__global__ void argmax_final_k(const int64_t* __restrict__ part, int nparts, int32_t* out) {
+  const int s = blockIdx.x;
+  int64_t best = INT64_MIN;
+  for (int i = threadIdx.x; i < nparts; i += 64) best = part[(size_t)s * nparts + i] > best ? part[(size_t)s * nparts + i] : best;
+  best = wave_max(best);
+  if (threadIdx.x == 0) out[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFLL));
+}
+
+__global__ void advance_k(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
+                          int32_t* row_base, int S) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < S) {
+    ids[s] = next_tok[s];
+    start_pos[s] += 1;
+  }
+  if (s == 0 && row_base) *row_base += S;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int16_t* gain,
+                          int64_t R, int64_t n, int8_t* x8, int32_t* row_m, int32_t* row_k,
+                          hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  rmsnorm_k<<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, int32_t* row_e,
+                          int32_t* row_m, int32_t* row_k, int32_t fold_m, int32_t fold_k,
+                          hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  requant_k<<<(unsigned)R, TPB, 0, st>>>(y, (int)n, q, row_e, row_m, row_k, fold_m, fold_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int32_t* x, const int32_t* pos, const int16_t* cos_t,
+                       const int16_t* sin_t, int64_t R, int64_t heads, int64_t d, int64_t max_pos,
+                       hipStream_t st) {
+  if (R == 0 || heads == 0) return hipSuccess;
+  const int thr = (int)((d / 2 + 63) / 64 * 64);
+  rope_k<<<dim3((unsigned)R, (unsigned)heads), thr, 0, st>>>(x, pos, cos_t, sin_t, (int)heads,
+                                                              (int)d, (int)max_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax(const int32_t* s, const int32_t* valid, const int32_t* shift,
+                          int64_t R, int64_t C, int32_t M, int32_t K, int16_t* P,
+                          hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  softmax_k<<<(unsigned)R, TPB, 0, st>>>(s, valid, shift, (int)C, M, K, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int32_t Mg,
+                         int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  swiglu_k<<<(unsigned)R, TPB, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* ids, int64_t R, const int8_t* emb, const int8_t* emb_lo,
+                        const int32_t* emb_m, int64_t H, int64_t V, int32_t shift, int32_t* h,
+                        hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  embed_k<<<(unsigned)R, TPB, 0, st>>>(ids, emb, emb_lo, emb_m, (int)H, (int)V, shift, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_meta(const int32_t* cu, const int32_t* start, const int32_t* slot,
+                            int64_t S, int32_t* pos_of, int32_t* slot_of, int32_t* last_row,
+                            hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  rows_meta_k<<<(unsigned)S, 256, 0, st>>>(cu, start, slot, pos_of, slot_of, last_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_meta(const int32_t* ctx_len, const int32_t* slot, int64_t B,
+                              int32_t* pos_of, int32_t* slot_of, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  decode_meta_k<<<(unsigned)((B + 255) / 256), 256, 0, st>>>(ctx_len, slot, (int)B, pos_of, slot_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nkv, int64_t d,
+                           const int32_t* pos_of, const int32_t* slot_of, const QkvPost& p,
+                           int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
+                           int64_t max_pos, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  qkv_post_k<<<(unsigned)R, TPB, 0, st>>>(qkv, (int)nq, (int)nkv, (int)d, pos_of, slot_of, p, q8,
+                                          e_q, kc, vc, (int)n_slots, (int)max_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const int32_t* logits, const int32_t* row_base, int64_t S, int64_t V,
+                         int64_t* part, int64_t nparts, int32_t* out, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  const int chunk = (int)((V + nparts - 1) / nparts);
+  argmax_part_k<<<dim3((unsigned)nparts, (unsigned)S), TPB, 0, st>>>(logits, row_base, (int)V,
+                                                                      (int)nparts, chunk, part);
+  argmax_final_k<<<(unsigned)S, 64, 0, st>>>(part, (int)nparts, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
+                          int32_t* row_base, int64_t S, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  advance_k<<<(unsigned)((S + 255) / 256), 256, 0, st>>>(ids, next_tok, start_pos, row_base, (int)S);
+  return hipGetLastError();
+}
+
+}  // namespace detint

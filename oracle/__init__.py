@@ -121,6 +121,8 @@ def _declare(L):
     L.orc_forward.argtypes = [C.POINTER(OrcModel), i32p, i64, i32p, i32p, i32p, i64,
                               i8p, i8p, i64, i32, i32p, vp]
     L.orc_argmax.argtypes = [i32p, i64, i64, i32p]
+    L.orc_attention.argtypes = [i8p, i32p, i8p, i8p, i32p, i32p, i64, i64, i64, i64, i64, i64,
+                                i32, i32, i32p]
 
 
 class OracleError(RuntimeError):
@@ -294,6 +296,18 @@ def swiglu(gu, f_a: int):
     k = np.zeros(R_, np.int32)
     lib().orc_swiglu(gu, R_, n, int(f_a), a8, m, k); _check()
     return a8, m, k
+
+
+def attention(q8, eq, kc, vc, pos, slot, M: int, K: int):
+    """q8 [R, nq, d], eq [R, nq]; kc/vc one layer [slots, nkv, max_pos, d]."""
+    q8 = _c(q8, np.int8)
+    R_, nq, d = q8.shape
+    slots, nkv, max_pos, _ = kc.shape
+    out = np.zeros((R_, nq, d), np.int32)
+    lib().orc_attention(q8, _c(eq, np.int32), _c(kc, np.int8), _c(vc, np.int8), _c(pos, np.int32),
+                        _c(slot, np.int32), R_, nq, nkv, d, slots, max_pos, int(M), int(K), out)
+    _check()
+    return out
 
 
 def argmax(logits):

@@ -533,6 +533,48 @@ static void linear(const orc_model *md, const int8_t *x8, int64_t R_, int64_t K,
   orc_gemm(x8, md->wide ? NULL : w8, md->wide ? w16 : NULL, R_, N, K, acc);
 }
 
+/* Attention of R query rows over one layer's int8 cache [slot][kv head]
+ * [position][d] (oracle layout). Row r sits at position pos[r] of slot slot[r]
+ * and attends positions 0..pos[r] (causal, keys already cached). Query head hh
+ * reads KV head hh * nkv / nq (grouped-query). Scores s_j = q8 . k8_j go
+ * through DI-Softmax with shift e_q[r][hh] (15-bit P, [BLOG] footnote 8) and
+ * out[r][hh][t] = sum_j P_j * v8_j[t], exactly. */
+int orc_attention(const int8_t *q8, const int32_t *eq, const int8_t *kc, const int8_t *vc,
+                  const int32_t *pos, const int32_t *slot, int64_t R_, int64_t nq, int64_t nkv,
+                  int64_t d, int64_t slots, int64_t max_pos, int32_t sm_M, int32_t sm_K,
+                  int32_t *att) {
+  for (int64_t r = 0; r < R_; r++)
+    CHECK(pos[r] >= 0 && pos[r] < max_pos && slot[r] >= 0 && slot[r] < slots, "attention row position/slot");
+  if (g_err) return g_err;
+#pragma omp parallel
+  {
+    int32_t *sc = malloc(4 * max_pos), *E = malloc(4 * max_pos);
+    int16_t *P = malloc(2 * max_pos);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+    for (int64_t r = 0; r < R_; r++)
+      for (int64_t hh = 0; hh < nq; hh++) {
+        const int64_t p = pos[r], kvh = hh * nkv / nq;
+        const int8_t *kb = kc + ((slot[r] * nkv + kvh) * max_pos) * d;
+        const int8_t *vb = vc + ((slot[r] * nkv + kvh) * max_pos) * d;
+        const int8_t *q = q8 + (r * nq + hh) * d;
+        for (int64_t j = 0; j <= p; j++) {
+          int64_t s = 0;
+          for (int64_t t = 0; t < d; t++) s += (int64_t)q[t] * kb[j * d + t];
+          sc[j] = (int32_t)s;
+        }
+        softmax_row(sc, p + 1, sm_M, sm_K, eq[r * nq + hh], E, P, p + 1);
+        for (int64_t t = 0; t < d; t++) {
+          int64_t o = 0;
+          for (int64_t j = 0; j <= p; j++) o += (int64_t)P[j] * vb[j * d + t];
+          CHECK(o < ((int64_t)1 << 31) && o > -((int64_t)1 << 31), "attention output exceeds int32");
+          att[(r * nq + hh) * d + t] = (int32_t)o;
+        }
+      }
+    free(sc); free(E); free(P);
+  }
+  return g_err;
+}
+
 /* Row index -> (sequence, absolute position). */
 static void row_positions(const int32_t *cu, const int32_t *start, int64_t S,
                           int64_t *seq_of, int64_t *pos_of) {
@@ -633,33 +675,13 @@ int orc_layer_forward(const orc_model *md, int64_t l, int32_t *h, int64_t R_,
   }
   if (dump && dump->q8) { memcpy(dump->q8, q8, R_ * nq * d); memcpy(dump->eq, eq, 4 * R_ * nq); }
 
-  /* 4. attention: causal over the cached keys 0..pos, grouped-query mapping
-   *    q head hh -> kv head hh * nkv / nq; DI-Softmax with 15-bit P; the
-   *    output O = sum_j P_j v8_j is exact. */
-#pragma omp parallel
+  /* 4. attention over the cache */
   {
-    int32_t *sc = malloc(4 * md->max_pos), *E = malloc(4 * md->max_pos);
-    int16_t *P = malloc(2 * md->max_pos);
-#pragma omp for schedule(dynamic, 1) collapse(2)
-    for (int64_t r = 0; r < R_; r++)
-      for (int64_t hh = 0; hh < nq; hh++) {
-        const int64_t p = pos_of[r], kvh = hh * nkv / nq, sl = slot[seq_of[r]];
-        const int8_t *q = q8 + (r * nq + hh) * d;
-        for (int64_t j = 0; j <= p; j++) {
-          const int8_t *k = kv_at(kc, md, slots, l, sl, kvh, j);
-          int64_t s = 0;
-          for (int64_t t = 0; t < d; t++) s += (int64_t)q[t] * k[t];
-          sc[j] = (int32_t)s;
-        }
-        softmax_row(sc, p + 1, sm_M, sm_K, eq[r * nq + hh], E, P, p + 1);
-        for (int64_t t = 0; t < d; t++) {
-          int64_t o = 0;
-          for (int64_t j = 0; j <= p; j++) o += (int64_t)P[j] * kv_at(vc, md, slots, l, sl, kvh, j)[t];
-          CHECK(o < ((int64_t)1 << 31) && o > -((int64_t)1 << 31), "attention output exceeds int32");
-          att[(r * nq + hh) * d + t] = (int32_t)o;
-        }
-      }
-    free(sc); free(E); free(P);
+    int32_t *po = malloc(4 * R_), *so = malloc(4 * R_);
+    for (int64_t r = 0; r < R_; r++) { po[r] = (int32_t)pos_of[r]; so[r] = slot[seq_of[r]]; }
+    orc_attention(q8, eq, kc + l * slots * nkv * md->max_pos * d, vc + l * slots * nkv * md->max_pos * d,
+                  po, so, R_, nq, nkv, d, slots, md->max_pos, sm_M, sm_K, att);
+    free(po); free(so);
   }
   if (dump && dump->attn) memcpy(dump->attn, att, 4 * R_ * nq * d);
 

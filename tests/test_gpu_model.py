@@ -1,0 +1,132 @@
+"""Whole-model GPU parity: logits of every generation step bit-identical to
+the CPU oracle, and the invariances the pages claim (batch composition,
+split prefill, token-by-token prompt feeding, graph vs eager, repeats).
+The Qwen3-0.6B-shaped runs compare against chained per-step logits hashes
+that tests/golden/make_golden.py wrote with the oracle alone."""
+import json
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import detint_synth as S
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+@pytest.fixture(scope="module")
+def D():
+    import torch
+    import integer_only_deterministic_amd as D
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    D.library()
+    return D
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wide"])
+@pytest.mark.parametrize("use_graph", [True, False])
+def test_tiny_generation_matches_oracle(D, name, use_graph):
+    m = S.make_model(name, seed=21)
+    V = m.shape.vocab
+    prompts = [S.make_prompt(V, 7, 1), S.make_prompt(V, 30, 2), S.make_prompt(V, 19, 3)]
+    n_new = 24
+    rows = []
+    toks = O.OracleModel(m, slots=3).generate(prompts, n_new, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=3)
+    hist = host(dm.generate(prompts, n_new, use_graph=use_graph))
+    want = np.stack(rows)                       # [n_new, B, V]
+    for s in range(n_new):
+        np.testing.assert_array_equal(hist[s], want[s], err_msg=f"{name} step {s}")
+    np.testing.assert_array_equal(hist.argmax(-1).T, toks)
+
+
+def test_tiny_kv_cache_matches_oracle(D):
+    m = S.make_model("tiny", seed=22)
+    prompts = [S.make_prompt(1000, 40, 4), S.make_prompt(1000, 9, 5)]
+    om = O.OracleModel(m, slots=2)
+    om.generate(prompts, 6)
+    dm = D.DetintModel(m, n_slots=2)
+    dm.generate(prompts, 6)
+    np.testing.assert_array_equal(host(dm.kc), om.kc)
+    np.testing.assert_array_equal(host(dm.vc), om.vc)
+
+
+# ----------------------------------------------------- Qwen3-0.6B shape
+
+@pytest.fixture(scope="module")
+def qwen(D):
+    g = json.loads((GOLDEN / "qwen3_b1.json").read_text())
+    m = S.make_model("qwen3_0.6b", seed=g["model_seed"])
+    assert S.model_digest(m) == g["model_digest"], "synthetic model drifted from the golden file"
+    return m, g
+
+
+def test_qwen3_b1_512_steps(D, qwen):
+    """64-token prompt + 512 greedy tokens at batch 1: every step's chained
+    logits hash and every token equal the oracle's."""
+    m, g = qwen
+    p0 = S.make_prompt(m.shape.vocab, 64, g["prompt_seed"])
+    dm = D.DetintModel(m, n_slots=1)
+    hist = host(dm.generate([p0], g["n_new"]))[:, 0]
+    chain = D.logits_chain(hist)
+    bad = [s for s in range(len(chain)) if chain[s] != g["logits_chain"][0][s]]
+    assert not bad, f"first mismatching step {bad[0]}"
+    np.testing.assert_array_equal(hist.argmax(-1), g["tokens"][0])
+
+
+def test_qwen3_b8_row0_hash(D, qwen):
+    """The same prompt sharing a batch of 8 with 7 random prompts of 16-256
+    tokens: row 0's 512-step hash equals batch 1's."""
+    m, g = qwen
+    V = m.shape.vocab
+    prompts = [S.make_prompt(V, 64, g["prompt_seed"])] + S.make_prompts(V, 7, 16, 256, 2)
+    dm = D.DetintModel(m, n_slots=8)
+    hist = host(dm.generate(prompts, g["n_new"]))
+    assert D.logits_chain(hist[:, 0])[-1] == g["logits_chain"][0][-1]
+    g8 = GOLDEN / "qwen3_b8.json"
+    if g8.exists():
+        gb = json.loads(g8.read_text())
+        for b in range(8):
+            assert D.logits_chain(hist[:, b])[-1] == gb["logits_chain"][b][-1], f"row {b}"
+
+
+@pytest.mark.parametrize("variant", ["two_halves", "half_then_tokens"])
+def test_qwen3_split_prefill(D, qwen, variant):
+    """Prefill in two halves (32 + 32), or 32 tokens then 32 one-by-one; then
+    greedy decode. The 512-step hash equals the single-prefill run."""
+    import torch
+    m, g = qwen
+    p0 = S.make_prompt(m.shape.vocab, 64, g["prompt_seed"])
+    n_new = g["n_new"]
+    dm = D.DetintModel(m, n_slots=1)
+    hist = torch.empty((n_new, 1, m.shape.vocab), dtype=torch.int32, device="cuda")
+    scratch = torch.empty((1, 1, m.shape.vocab), dtype=torch.int32, device="cuda")
+    if variant == "two_halves":
+        dm.prefill([p0[:32]], [0], [0], scratch, 0)
+        tok = dm.prefill([p0[32:]], [32], [0], hist, 0)
+    else:
+        dm.prefill([p0[:32]], [0], [0], scratch, 0)
+        for t in range(32, 64):
+            tok = dm.prefill([p0[t:t + 1]], [t], [0], hist if t == 63 else scratch, 0)
+    dm.decode(tok, [64], [0], n_new - 1, hist, 1)
+    chain = D.logits_chain(host(hist)[:, 0])
+    assert chain == g["logits_chain"][0]
+
+
+def test_qwen3_repeat_runs_identical(D, qwen):
+    m, g = qwen
+    p0 = S.make_prompt(m.shape.vocab, 64, g["prompt_seed"])
+    dm = D.DetintModel(m, n_slots=1)
+    a = host(dm.generate([p0], 64))
+    for _ in range(2):
+        dm.reset_cache()
+        np.testing.assert_array_equal(host(dm.generate([p0], 64)), a)
+    assert D.logits_chain(a[:, 0])[-1] == g["logits_chain"][0][63]

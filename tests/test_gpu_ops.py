@@ -1,0 +1,249 @@
+"""GPU parity of every libdetint op against the CPU oracle, bit for bit
+(tolerance 0: every result is an integer). Inputs are seeded synthetic data;
+sizes span several tiles plus ragged tails; the full-size GEMM sweep is
+checked on sampled rows the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import detint_synth as S
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def D():
+    import torch
+    import integer_only_deterministic_amd as D
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    D.library()
+    return D
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ GEMM
+
+@pytest.mark.parametrize("K,N", S.GEMM_SWEEP_KN)
+def test_gemm_sweep(D, K, N):
+    """The standalone sweep: M in {1, 8, 64, 512, 2048} x the five projection
+    shapes, RAW int32 and per-row x per-column requant to int8."""
+    for M in S.GEMM_SWEEP_M:
+        g = S.make_gemm_operands(M, N, K, seed=7)
+        A, W = dev(g["A"]), dev(g["W"])
+        rm, rk, cm = dev(g["row_m"]), dev(g["row_k"]), dev(g["col_m"])
+        raw = host(D.detint_gemm_i8(A, W))
+        q = host(D.detint_gemm_i8(A, W, rm, rk, cm, g["col_k"], 0, D.REQ_I8))
+        if M <= 64:
+            rows = np.arange(M)
+        else:
+            rng = np.random.default_rng(M + N + K)
+            rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], rng.integers(0, M, 12)]))
+        acc = O.gemm(g["A"][rows], g["W"])
+        np.testing.assert_array_equal(raw[rows], acc, err_msg=f"RAW M={M} N={N} K={K}")
+        want = O.epilogue(acc, g["row_m"][rows], g["row_k"][rows], g["col_m"], g["col_k"], 0, O.REQ_I8)
+        np.testing.assert_array_equal(q[rows], want, err_msg=f"REQ_I8 M={M} N={N} K={K}")
+        del A, W
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 77, 32), (17, 130, 64),
+                                   (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072)])
+def test_gemm_ragged_all_modes(D, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    A = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    W = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    A[0, :] = -128
+    W[0, :] = -128
+    rm = rng.integers(1 << 14, 1 << 15, M).astype(np.int32)
+    rk = rng.integers(14, 22, M).astype(np.int32)
+    cm = rng.integers(1 << 14, 1 << 15, N).astype(np.int32)
+    acc = O.gemm(A, W)
+    base = rng.integers(-(1 << 20), 1 << 20, (M, N)).astype(np.int32)
+    dA, dW, drm, drk, dcm = dev(A), dev(W), dev(rm), dev(rk), dev(cm)
+    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW)), acc)
+    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 0, D.REQ_I8)),
+                                  O.epilogue(acc, rm, rk, cm, 22, 0, O.REQ_I8))
+    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.FIX)),
+                                  O.epilogue(acc, rm, rk, cm, 22, 8, O.FIX))
+    out = dev(base)
+    D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.RES_ADD, out=out)
+    np.testing.assert_array_equal(host(out), O.epilogue(acc, rm, rk, cm, 22, 8, O.RES_ADD, out=base))
+
+
+def test_gemm_empty(D):
+    import torch
+    A = torch.zeros((0, 32), dtype=torch.int8, device="cuda")
+    W = torch.zeros((5, 32), dtype=torch.int8, device="cuda")
+    assert D.detint_gemm_i8(A, W).shape == (0, 5)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 100, 2048), (7, 300, 256), (16, 64, 8192), (33, 130, 512),
+                                   (300, 200, 1024)])
+def test_gemm_w16_limbs(D, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    A = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    W16 = rng.integers(-32767, 32768, (N, K)).astype(np.int16)
+    W16[0, :] = -32767
+    W16[1, :] = 32767
+    rm = rng.integers(1 << 14, 1 << 15, M).astype(np.int32)
+    rk = rng.integers(14, 22, M).astype(np.int32)
+    cm = rng.integers(1 << 14, 1 << 15, N).astype(np.int32)
+    hi, lo = D.detint_split_w16(dev(W16))
+    w = W16.astype(np.int64)
+    np.testing.assert_array_equal(host(hi), (w >> 8).astype(np.int8))
+    np.testing.assert_array_equal(host(lo), ((w & 255) - 128).astype(np.int8))
+    acc = O.gemm(A, W16)
+    dA, drm, drk, dcm = dev(A), dev(rm), dev(rk), dev(cm)
+    np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo)), acc)
+    np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 12, D.FIX)),
+                                  O.epilogue(acc, rm, rk, cm, 30, 12, O.FIX))
+    np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 0, D.REQ_I8)),
+                                  O.epilogue(acc, rm, rk, cm, 30, 0, O.REQ_I8))
+
+
+# -------------------------------------------------------------- row ops
+
+@pytest.mark.parametrize("R,n", [(1, 1024), (5, 256), (64, 768), (33, 2048), (3, 4096)])
+def test_rmsnorm(D, R, n):
+    rng = np.random.default_rng(R * n)
+    h = rng.integers(-(1 << 24), 1 << 24, (R, n)).astype(np.int32)
+    h[0, :] = 0
+    if R > 2:
+        h[1] //= 1 << 18
+        h[2, :] = -77
+    g = rng.integers(1 << 12, (1 << 13) + 1, n).astype(np.int16)
+    x8, m, k = D.detint_rmsnorm(dev(h), dev(g))
+    ox, om, ok = O.rmsnorm(h, g)
+    np.testing.assert_array_equal(host(x8), ox)
+    np.testing.assert_array_equal(host(m), om)
+    np.testing.assert_array_equal(host(k), ok)
+
+
+@pytest.mark.parametrize("R,n", [(1, 2048), (9, 512), (70, 4096)])
+def test_requant(D, R, n):
+    rng = np.random.default_rng(R + n)
+    y = rng.integers(-(1 << 22), 1 << 22, (R, n)).astype(np.int32)
+    y[0, :] = 0
+    y[-1, :] = rng.integers(-100, 100, n)
+    q, e = D.detint_requant(dev(y))
+    oq, oe = O.requant_rows(y)
+    np.testing.assert_array_equal(host(q), oq)
+    np.testing.assert_array_equal(host(e), oe)
+
+
+@pytest.mark.parametrize("d,base", [(64, 1_000_000), (128, 1_000_000), (64, 500_000)])
+def test_rope(D, d, base):
+    P = 600
+    cos_t, sin_t = D.detint_rope_tables(P, d, base)
+    rng = np.random.default_rng(d)
+    x = rng.integers(-(1 << 22), 1 << 22, (50, 3, d)).astype(np.int32)
+    pos = rng.integers(0, P, 50).astype(np.int32)
+    pos[0] = 0
+    pos[1] = P - 1
+    y = D.detint_rope(dev(x), dev(pos), dev(cos_t), dev(sin_t))
+    np.testing.assert_array_equal(host(y), O.rope(x, pos, cos_t, sin_t))
+
+
+def test_softmax(D):
+    rng = np.random.default_rng(3)
+    R, Cc = 40, 700
+    s = rng.integers(-200000, 200000, (R, Cc)).astype(np.int32)
+    s[5, :] = 1234
+    valid = rng.integers(1, Cc + 1, R).astype(np.int32)
+    valid[0], valid[1] = 1, Cc
+    shift = rng.integers(0, 12, R).astype(np.int32)
+    M, K = O.softmax_mult(28857, 23, 128, 12)
+    P = D.detint_softmax(dev(s), dev(valid), dev(shift), M, K)
+    np.testing.assert_array_equal(host(P), O.softmax(s, valid, shift, M, K))
+
+
+@pytest.mark.parametrize("R,n", [(1, 3072), (13, 768), (4, 8192)])
+def test_swiglu(D, R, n):
+    rng = np.random.default_rng(R * 3 + n)
+    gu = rng.normal(0, 8 * 4096, (R, 2 * n)).astype(np.int32)
+    gu[0, :n] = 0
+    gu[-1, 5] = (1 << 24) - 1
+    gu[-1, 6] = -(1 << 24) + 1
+    a8, m, k = D.detint_swiglu(dev(gu), 12)
+    oa, om, ok = O.swiglu(gu, 12)
+    np.testing.assert_array_equal(host(a8), oa)
+    np.testing.assert_array_equal(host(m), om)
+    np.testing.assert_array_equal(host(k), ok)
+
+
+# ------------------------------------------------------------- attention
+
+def _cache(rng, slots, nkv, max_pos, d):
+    k = rng.integers(-127, 128, (slots, nkv, max_pos, d)).astype(np.int8)
+    v = rng.integers(-127, 128, (slots, nkv, max_pos, d)).astype(np.int8)
+    return k, v
+
+
+@pytest.mark.parametrize("nq,nkv,d,max_pos", [(4, 2, 64, 256), (16, 8, 128, 1024), (32, 8, 64, 4096),
+                                              (8, 8, 128, 300)])
+def test_attention_prefill_and_decode(D, nq, nkv, d, max_pos):
+    rng = np.random.default_rng(nq * d + max_pos)
+    slots = 3
+    kc, vc = _cache(rng, slots, nkv, max_pos, d)
+    M, K = O.softmax_mult(20000, 22, d, 12)
+    # prefill: three packed sequences (chunked: positions start mid-way)
+    lens, starts, sl = [5, 40, 1], [0, 17, max_pos - 1], [2, 0, 1]
+    R = sum(lens)
+    q8 = rng.integers(-127, 128, (R, nq, d)).astype(np.int8)
+    eq = rng.integers(0, 12, (R, nq)).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pos = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, lens)]).astype(np.int32)
+    slot_r = np.repeat(sl, lens).astype(np.int32)
+    want = O.attention(q8, eq, kc, vc, pos, slot_r, M, K)
+    got = D.detint_attn_prefill(dev(q8), dev(eq), dev(kc), dev(vc), dev(cu), dev(np.int32(starts)),
+                                dev(np.int32(sl)), M, K)
+    np.testing.assert_array_equal(host(got), want)
+    # decode: one row per slot at various context lengths
+    ctx = np.array([1, max_pos // 2 + 3, max_pos], np.int32)
+    dsl = np.array([1, 2, 0], np.int32)
+    q8d, eqd = q8[:3], eq[:3]
+    want = O.attention(q8d, eqd, kc, vc, ctx - 1, dsl, M, K)
+    got = D.detint_attn_decode(dev(q8d), dev(eqd), dev(kc), dev(vc), dev(ctx), dev(dsl), M, K)
+    np.testing.assert_array_equal(host(got), want)
+
+
+# ---------------------------------------------------------------- layer
+
+@pytest.fixture(scope="module")
+def layer_case():
+    m = S.make_model("layer256", seed=1)
+    h0 = S.make_residual(64, 256, seed=2)
+    om = O.OracleModel(m, slots=1)
+    h1, _ = om.layer(0, h0, [64], [0], [0])
+    return m, h0, h1, om
+
+
+def test_layer256_prefill(D, layer_case):
+    """One Qwen3-style layer (hidden 256, 4/2 heads, d 64, FFN 768), 64
+    tokens, residual input uniform in [-2^15, 2^15): int32 residual out and
+    the KV cache equal the oracle's."""
+    m, h0, h1, om = layer_case
+    dm = D.DetintModel(m, n_slots=1)
+    got = dm.layer(0, h0, [64], [0], [0])
+    np.testing.assert_array_equal(got, h1)
+    np.testing.assert_array_equal(host(dm.kc), om.kc)
+    np.testing.assert_array_equal(host(dm.vc), om.vc)
+
+
+def test_layer256_split_and_token_by_token(D, layer_case):
+    m, h0, h1, om = layer_case
+    dm = D.DetintModel(m, n_slots=2)
+    a = dm.layer(0, h0[:20], [20], [0], [1])
+    b = dm.layer(0, h0[20:50], [30], [20], [1])
+    rows = [a, b] + [dm.layer(0, h0[t:t + 1], [1], [t], [1]) for t in range(50, 64)]
+    np.testing.assert_array_equal(np.concatenate(rows), h1)
+    np.testing.assert_array_equal(host(dm.kc)[:, 1], om.kc[:, 0])
