@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the integer-only forward pass on one MI355X.
+
+A step is one greedy decode step of the Qwen3-0.6B-shaped integer model
+(random init, seeded): embedding -> 28 layers (RMSNorm, QKV, q/k-norm,
+RoPE, int8 KV cache, DI-Softmax attention, O-proj, SwiGLU FFN) -> final
+RMSNorm -> tied lm_head -> int32 logits -> greedy token, captured once
+into a HIP graph and replayed. The headline value is decode tokens/s at
+batch 1 after a 64-token prompt; the same line reports batch-8 decode,
+prefill tokens/s, the int8 GEMM sweep at M = 2048 against the i8 MFMA peak,
+the roofline of the lm_head kernel, and the CPU oracle on this host.
+Every timed run's logits are hashed and compared with the oracle-written
+golden chain (tests/golden), so the timed run is also the verified run.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --roofline-only     # lm_head kernel + copy calibration (counter runs)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+I8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+PAGES_DECODE_B1 = 106.3      # the pages' A100 int8 decode tok/s at batch 1 (context only)
+PROMPT_LEN = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, n, torch):
+    """Average seconds per call of fn over n calls, HIP events on the current stream."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / n
+
+
+def lm_head_case(D, m, torch):
+    """The lm_head launch exactly as the decode step makes it (one row)."""
+    import numpy as np
+    sh = m.shape
+    rng = np.random.default_rng(5)
+    x8 = torch.from_numpy(rng.integers(-127, 128, (1, sh.hidden)).astype(np.int8)).cuda()
+    rm = torch.tensor([24000], dtype=torch.int32, device="cuda")
+    rk = torch.tensor([18], dtype=torch.int32, device="cuda")
+    emb = torch.from_numpy(m.emb).cuda()
+    emb_m = torch.from_numpy(m.emb_m).cuda()
+    logits, part = D.detint_lm_head(x8, emb, None, rm, rk, emb_m, sh.w_k, sh.f_l)
+    fn = lambda: D.detint_lm_head(x8, emb, None, rm, rk, emb_m, sh.w_k, sh.f_l, logits, part)
+    nbytes = sh.vocab * sh.hidden + sh.hidden + 4 * sh.vocab * 2 + 8 * part.numel() + 16
+    return fn, nbytes
+
+
+def traffic_from_profiles():
+    """HBM bytes per lm_head launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    f = ROOT / "profiles" / "lm_head_hbm_traffic.txt"
+    if not f.exists():
+        return None
+    vals = {}
+    for line in f.read_text().splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = (ROOT / "integer_only_deterministic_amd" / "csrc" / "gemm.hip").read_bytes()
+    if vals.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline_only(D, S, torch):
+    m = S.make_model("qwen3_0.6b", seed=0)
+    fn, nbytes = lm_head_case(D, m, torch)
+    for _ in range(5):
+        fn()
+    t = timed(fn, 50, torch)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"lm_head_us": t * 1e6, "lm_head_algorithmic_bytes": nbytes,
+                      "copy_bytes": src.numel(), "copy_launches": 5}))
+
+
+def decode_run(D, dm, prompts, warmup, steps, torch):
+    B = len(prompts)
+    V = dm.shape.vocab
+    hist = torch.empty((1 + warmup + steps, B, V), dtype=torch.int32, device="cuda")
+    dm.reset_cache()
+    tok = dm.prefill(prompts, [0] * B, list(range(B)), hist, 0)
+    step = dm.decode_step_fn(tok, [len(p) for p in prompts], list(range(B)), hist, B)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return hist, (t1 - t0), ev0.elapsed_time(ev1) / 1e3
+
+
+def cpu_baseline(m, p0, seconds: float, gpu_tokens):
+    import numpy as np
+    import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    om = O.OracleModel(m, slots=1)
+    t0 = time.perf_counter()
+    _, tok = om.forward(p0, [len(p0)], [0], [0])
+    t1 = time.perf_counter()
+    toks = [int(tok[0])]
+    pos = len(p0)
+    while time.perf_counter() - t1 < seconds and len(toks) < len(gpu_tokens):
+        _, tok = om.forward(np.array([toks[-1]], np.int32), [1], [pos], [0])
+        pos += 1
+        toks.append(int(tok[0]))
+    t2 = time.perf_counter()
+    n = len(toks) - 1
+    agree = toks == [int(t) for t in gpu_tokens[: len(toks)]]
+    return dict(value=round(n / (t2 - t1), 3) if n else None, unit="tok/s", cores=threads,
+                kind="oracle",
+                sample=f"batch-1 greedy decode of the same model: {len(p0)}-token prefill "
+                       f"({t1 - t0:.1f} s, untimed) then {n} decode steps in {t2 - t1:.1f} s; "
+                       f"tokens {'equal' if agree else 'DIFFER from'} the GPU run's")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py: this build runs on one GPU only (the integer forward pass is "
+            "data-parallel by sequence; see DESIGN.md for how it would shard). Use --gpus 1.")
+        sys.exit(2)
+    if args.warmup + args.steps > 511:
+        log("bench.py: warmup + steps must be <= 511 (64-token prompt + 512 steps fit the cache)")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import detint_synth as S
+    import integer_only_deterministic_amd as D
+
+    D.library()
+    torch.cuda.set_device(0)
+    if args.roofline_only:
+        roofline_only(D, S, torch)
+        return
+
+    gold = json.loads((ROOT / "tests" / "golden" / "qwen3_b1.json").read_text())
+    gold8 = json.loads((ROOT / "tests" / "golden" / "qwen3_b8.json").read_text())
+    log("building the seeded Qwen3-0.6B-shaped model ...")
+    m = S.make_model("qwen3_0.6b", seed=gold["model_seed"])
+    sh = m.shape
+    assert S.model_digest(m) == gold["model_digest"]
+    dm = D.DetintModel(m, n_slots=8)
+    p0 = S.make_prompt(sh.vocab, PROMPT_LEN, gold["prompt_seed"])
+    co = S.make_prompts(sh.vocab, 7, 16, 256, gold["coprompt_seed"])
+    W, K = args.warmup, args.steps
+
+    # ---- decode, batch 1 (headline) ----
+    log(f"decode b1: prefill {PROMPT_LEN}, {W} warmup + {K} timed graph replays")
+    hist, wall1, ev1 = decode_run(D, dm, [p0], W, K, torch)
+    h1 = hist.cpu().numpy()
+    chain1 = D.logits_chain(h1[:, 0])
+    exact_b1 = chain1 == gold["logits_chain"][0][: len(chain1)]
+    gpu_tokens = h1[:, 0].argmax(-1)
+    tps1 = K / wall1
+
+    # ---- decode, batch 8: the prompt among 7 random co-prompts ----
+    log("decode b8")
+    hist8, wall8, _ = decode_run(D, dm, [p0] + co, W, K, torch)
+    h8 = hist8.cpu().numpy()
+    exact_b8 = all(D.logits_chain(h8[:, b]) == gold8["logits_chain"][b][: h8.shape[0]] for b in range(8))
+    tps8 = 8 * K / wall8
+    del hist8, h8
+
+    # ---- prefill: the batch-8 ragged prompts in one call, and the 64-token prompt ----
+    log("prefill")
+    scratch = torch.empty((8, sh.vocab), dtype=torch.int32, device="cuda")
+    rag = [p0] + co
+    ntok = sum(len(p) for p in rag)
+    t_rag = timed(lambda: dm.prefill(rag, [0] * 8, list(range(8)), scratch, 0), 5, torch)
+    t_64 = timed(lambda: dm.prefill([p0], [0], [0], scratch, 0), 10, torch)
+
+    # ---- int8 GEMM sweep at M = 2048 (requant to int8) ----
+    log("GEMM sweep M=2048")
+    gemm = {}
+    for Kd, Nd in S.GEMM_SWEEP_KN:
+        g = S.make_gemm_operands(2048, Nd, Kd, seed=7)
+        A, Wt = torch.from_numpy(g["A"]).cuda(), torch.from_numpy(g["W"]).cuda()
+        rm, rk = torch.from_numpy(g["row_m"]).cuda(), torch.from_numpy(g["row_k"]).cuda()
+        cm = torch.from_numpy(g["col_m"]).cuda()
+        out = torch.empty((2048, Nd), dtype=torch.int8, device="cuda")
+        f = lambda: D.detint_gemm_i8(A, Wt, rm, rk, cm, 22, 0, D.REQ_I8, out)
+        for _ in range(3):
+            f()
+        t = timed(f, 20, torch)
+        gemm[f"{Kd}x{Nd}"] = round(2 * 2048 * Nd * Kd / t / 1e12, 1)
+        del A, Wt, out
+
+    # ---- roofline of the dominant single kernel: the lm_head GEMV ----
+    log("lm_head kernel")
+    fn, nbytes = lm_head_case(D, m, torch)
+    for _ in range(5):
+        fn()
+    t_lm = timed(fn, 100, torch)
+    achieved = nbytes / t_lm / 1e9
+    traffic = traffic_from_profiles()
+
+    cpu = None if args.no_cpu else cpu_baseline(m, p0, args.cpu_seconds, gpu_tokens)
+
+    weights = sum(L.wqkv.size + L.wo.size + L.wgu.size + L.wd.size for L in m.layers) + m.emb.size
+    ctx_avg = PROMPT_LEN + 1 + W + (K + 1) / 2
+    step_bytes = weights + 2 * sh.n_layers * sh.n_kv * sh.head_dim * ctx_avg
+    gemm_best = max(gemm.values())
+    line = {
+        "metric": "decode tok/s @bs1/8, prefill tok/s; i8 GEMM % MFMA peak; bit-exact logits",
+        "value": round(tps1, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(1e3 * wall1 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tps1 / PAGES_DECODE_B1, 2),
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-0.6B-shaped integer model (random init, seed 0), greedy "
+                               "decode at batch 1 after a 64-token prompt, one HIP-graph replay per token",
+                   "batch": 1, "prompt_len": PROMPT_LEN, "decode_steps_timed": K,
+                   "ctx_range": [PROMPT_LEN + 1 + W, PROMPT_LEN + W + K]},
+        "bit_exact": {"decode_b1_vs_oracle_chain": bool(exact_b1),
+                      "decode_b8_vs_oracle_chain": bool(exact_b8),
+                      "b1_logits_hash": chain1[-1][:12]},
+        "decode_b8_tok_s": round(tps8, 1),
+        "prefill_tok_s": {"ragged_8_prompts_%d_tokens" % ntok: round(ntok / t_rag, 1),
+                          "prompt_64": round(PROMPT_LEN / t_64, 1)},
+        "gemm_m2048_tops": gemm,
+        "gemm_m2048_best_frac_i8_mfma": round(gemm_best / I8_PEAK_TOPS, 4),
+        "decode_b1_hbm_frac": round(step_bytes * tps1 / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (gemv<1,false,true>)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(t_lm * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -263,6 +263,23 @@ detint_status detint_forward(const detint_model *m, int8_t *k_cache, int8_t *v_c
                              int32_t *logits, int32_t *logit_row_base, int32_t *next_tok,
                              int32_t flags, void *ws, int64_t ws_bytes, void *stream);
 
+/* Tied lm_head for up to 16 rows, as one kernel: logits int32 [S, V] =
+ * R(x8 . E^T * row_m * emb_m, row_k + w_k - f_l), plus for every row the
+ * partial greedy-argmax keys of each of the kernel's waves in
+ * part int64 [S, detint_lm_head_parts(V)] (key = logit * 2^32 + 2^32 - 1 - id:
+ * the largest key is the largest logit at the lowest id). x8 [S, H] int8;
+ * E = emb [V, H] int8, or 16-bit limbs emb/emb_lo as in detint_gemm_w16.
+ * DetLLM README intro: int32 logits; DetLLM blog "DetLLM": ties go to the
+ * smallest token id. */
+int64_t detint_lm_head_parts(int64_t V);
+detint_status detint_lm_head(const int8_t *x8, const int8_t *emb, const int8_t *emb_lo, int64_t S,
+                             int64_t V, int64_t H, const int32_t *row_m, const int32_t *row_k,
+                             const int32_t *emb_m, int32_t w_k, int32_t f_l, int32_t *logits,
+                             int64_t *part, void *stream);
+/* Greedy token of each row from detint_lm_head's partials: next_tok int32 [S]. */
+detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts,
+                                  int32_t *next_tok, void *stream);
+
 /* One decoder layer in place on the int32 residual h [R, hidden] (|h| <
  * 2^25), same sequence/cache arguments and workspace as detint_forward:
  * RMSNorm -> QKV -> (q/k-norm) -> RoPE -> q DQ, K/V into the cache ->

@@ -74,6 +74,9 @@ _SIGS = {
     "detint_workspace_size": (i64, [vp, i64, i64]),
     "detint_forward": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp,
                              i64, vp]),
+    "detint_lm_head_parts": (i64, [i64]),
+    "detint_lm_head": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp]),
+    "detint_argmax_parts": (i32, [vp, i64, i64, vp, vp]),
     "detint_layer_forward": (i32, [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, vp, i64,
                                    vp]),
 }
@@ -229,6 +232,29 @@ def detint_attn_decode(q8, e_q, k_cache, v_cache, ctx_len, slot, mult_m, mult_k)
     _call("detint_attn_decode", _p(q8, torch.int8), _p(e_q, torch.int32), _p(k_cache, torch.int8),
           _p(v_cache, torch.int8), n_slots, _p(ctx_len, torch.int32), _p(slot, torch.int32), B, nq,
           nkv, d, max_pos, int(mult_m), int(mult_k), _p(out), _stream())
+    return out
+
+
+def detint_lm_head(x8, emb, emb_lo, row_m, row_k, emb_m, w_k, f_l, logits=None, part=None):
+    """Logits [S, V] and greedy-argmax partials [S, detint_lm_head_parts(V)]."""
+    torch = _torch()
+    S_, H = x8.shape
+    V = emb.shape[0]
+    npart = library().detint_lm_head_parts(V)
+    if logits is None:
+        logits = torch.empty((S_, V), dtype=torch.int32, device=x8.device)
+    if part is None:
+        part = torch.empty((S_, npart), dtype=torch.int64, device=x8.device)
+    _call("detint_lm_head", _p(x8, torch.int8), _p(emb, torch.int8), _p(emb_lo), S_, V, H, _p(row_m),
+          _p(row_k), _p(emb_m), int(w_k), int(f_l), _p(logits), _p(part), _stream())
+    return logits, part
+
+
+def detint_argmax_parts(part):
+    torch = _torch()
+    S_, npart = part.shape
+    out = torch.empty(S_, dtype=torch.int32, device=part.device)
+    _call("detint_argmax_parts", _p(part, torch.int64), S_, npart, _p(out), _stream())
     return out
 
 
@@ -400,16 +426,15 @@ class DetintModel:
                          max(lens), hist, self._t([base_row]), tok)
         return tok
 
-    def decode(self, tok, pos, slots, n_steps: int, hist, base_row: int, use_graph: bool = True):
-        """n_steps greedy one-token steps for B rows starting from tokens `tok`
-        (device [B]) at positions `pos`. Each step is one detint_forward with
-        ADVANCE, so token, positions and the history row advance on the
-        device; with use_graph the step is captured once into a HIP graph and
-        replayed. Step i's logits go to hist rows base_row + i*B .. + B."""
+    def decode_step_fn(self, tok, pos, slots, hist, base_row: int, use_graph: bool = True):
+        """Return a callable that performs one greedy decode step for B rows
+        starting from tokens `tok` (device [B]) at positions `pos`: one
+        detint_forward with ADVANCE, so token, positions and the logits
+        history row (rows base_row + i*B .. + B for step i) advance on the
+        device. With use_graph the step is captured once into a HIP graph and
+        the callable replays it."""
         torch = self.torch
         B = len(pos)
-        if n_steps <= 0:
-            return
         dec = dict(cu=self._t(list(range(B + 1))), start=self._t(pos), slot=self._t(slots),
                    base=self._t([base_row]), tok=tok)
         self._dec = dec
@@ -419,19 +444,24 @@ class DetintModel:
             self.forward_raw(dec["tok"], B, dec["cu"], dec["start"], dec["slot"], B, 1, hist, dec["base"],
                              dec["tok"], FWD_ADVANCE)
 
-        if use_graph:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                step()
-            torch.cuda.current_stream().wait_stream(s)
-            for _ in range(n_steps):
-                g.replay()
-            self._graph = g
-        else:
-            for _ in range(n_steps):
-                step()
+        if not use_graph:
+            return step
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        self._graph = g
+        return g.replay
+
+    def decode(self, tok, pos, slots, n_steps: int, hist, base_row: int, use_graph: bool = True):
+        """n_steps greedy decode steps (see decode_step_fn)."""
+        if n_steps <= 0:
+            return
+        step = self.decode_step_fn(tok, pos, slots, hist, base_row, use_graph)
+        for _ in range(n_steps):
+            step()
 
     def generate(self, prompts, n_new: int, use_graph: bool = True, hist=None):
         """Greedy generation (slot i = prompt i): one prefill call over all

@@ -204,6 +204,34 @@ detint_status detint_attn_decode(const int8_t* q8, const int32_t* e_q, const int
                     "attn_decode launch");
 }
 
+// ------------------------------------------------------------- lm_head
+
+int64_t detint_lm_head_parts(int64_t V) { return V > 0 ? logits_argmax_parts(V) : 0; }
+
+detint_status detint_lm_head(const int8_t* x8, const int8_t* emb, const int8_t* emb_lo, int64_t S,
+                             int64_t V, int64_t H, const int32_t* row_m, const int32_t* row_k,
+                             const int32_t* emb_m, int32_t w_k, int32_t f_l, int32_t* logits,
+                             int64_t* part, void* stream) {
+  detint_status s = check_gemm(x8, emb, S, V, H, row_m, row_k, emb_m, DETINT_GEMM_FIX, logits,
+                               emb_lo ? 65536 : 131072);
+  if (s != DETINT_OK || S == 0 || V == 0) return s;
+  REQUIRE(S <= 16, "lm_head: at most 16 rows (S=%lld)", (long long)S);
+  REQUIRE(part, "lm_head: null partials");
+  if (emb_lo) REQUIRE(aligned16(emb_lo), "lm_head: emb_lo misaligned");
+  Epi e{row_m, row_k, emb_m, w_k, f_l, MODE_FIX, nullptr};
+  return hip_status(launch_logits_argmax(x8, emb, emb_lo, S, V, H, e, logits, part, S_(stream)),
+                    "lm_head launch");
+}
+
+detint_status detint_argmax_parts(const int64_t* part, int64_t S, int64_t nparts,
+                                  int32_t* next_tok, void* stream) {
+  REQUIRE(S >= 0 && nparts > 0, "argmax_parts: bad sizes");
+  if (S == 0) return ok();
+  REQUIRE(part && next_tok, "argmax_parts: null pointer");
+  return hip_status(launch_argmax_final(part, S, nparts, next_tok, S_(stream)),
+                    "argmax_parts launch");
+}
+
 // ------------------------------------------------------ host set-up arithmetic
 
 detint_status detint_rope_tables(int16_t* cos_t, int16_t* sin_t, int64_t P, int64_t d,
@@ -310,7 +338,8 @@ WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
   w.eq = take(4 * R * d.n_q);
   w.att = take(4 * R * nqd);
   w.gu = take(4 * R * 2 * d.ffn);
-  w.part = take(8 * S * kArgmaxParts);
+  const int64_t np = logits_argmax_parts(d.vocab > 0 ? d.vocab : 1);
+  w.part = take(8 * S * (np > kArgmaxParts ? np : kArgmaxParts));
   w.total = o;
   return w;
 }
@@ -509,10 +538,15 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
   LAUNCH(launch_rmsnorm(h, last_row, d.final_norm, S, d.hidden, x8, rm, rk, st));
   {
     Epi ep{rm, rk, d.emb_m, d.w_k, d.f_l, MODE_FIX, logit_row_base};
-    LAUNCH(launch_gemm(x8, d.emb, d.wide ? d.emb_lo : nullptr, S, d.vocab, d.hidden, ep, logits,
-                       st));
+    const int8_t* lo = d.wide ? d.emb_lo : nullptr;
+    if (S <= 16) {  // decode-sized: logits GEMV with fused argmax partials
+      LAUNCH(launch_logits_argmax(x8, d.emb, lo, S, d.vocab, d.hidden, ep, logits, part, st));
+      LAUNCH(launch_argmax_final(part, S, logits_argmax_parts(d.vocab), next_tok, st));
+    } else {
+      LAUNCH(launch_gemm(x8, d.emb, lo, S, d.vocab, d.hidden, ep, logits, st));
+      LAUNCH(launch_argmax(logits, logit_row_base, S, d.vocab, part, kArgmaxParts, next_tok, st));
+    }
   }
-  LAUNCH(launch_argmax(logits, logit_row_base, S, d.vocab, part, kArgmaxParts, next_tok, st));
   if (flags & DETINT_FWD_ADVANCE)
     LAUNCH(launch_advance(ids, next_tok, start_pos, logit_row_base, S, st));
 #undef LAUNCH

@@ -173,15 +173,28 @@ __global__ __launch_bounds__(256) void gemm_mfma(const int8_t* __restrict__ A,
 
 // ---------------------------------------------------------------- GEMV
 
-template <int MT, bool WIDE>
+// Key of a logit for the greedy argmax: larger value first, then the lower
+// index (DetLLM blog "DetLLM": ties go to the smallest token id); max over
+// keys is order-free.
+__device__ __forceinline__ int64_t amax_key(int64_t v, int64_t j) {
+  return (v * 4294967296LL) | (int64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+// ARGMAX: FIX-mode logits epilogue that also keeps, per row, the best key
+// over the columns this wave produced and writes it to part[m * nwaves + wave]
+// (the final reduction over waves is argmax_final in rowops.hip).
+template <int MT, bool WIDE, bool ARGMAX>
 __global__ __launch_bounds__(256) void gemv(const int8_t* __restrict__ A,
                                             const int8_t* __restrict__ W,
                                             const int8_t* __restrict__ Wlo, int M, int N, int K,
-                                            Epi e, void* out) {
+                                            Epi e, void* out, int64_t* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  int64_t best[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) best[m] = INT64_MIN;
   for (int j0 = wave * 2; j0 < N; j0 += nwaves * 2) {
     int acc[2][MT], accl[2][MT], rs[MT];
 #pragma unroll
@@ -221,25 +234,68 @@ __global__ __launch_bounds__(256) void gemv(const int8_t* __restrict__ A,
           s0 = 256 * s0 + wave_sum(accl[0][m]) + r;
           s1 = 256 * s1 + wave_sum(accl[1][m]) + r;
         }
-        if (lane == 0) {
+        if (ARGMAX) {
+          // logits: R(acc * m_r * m_c, k_r + k_c - frac), as epi_store's FIX
+          const int sh = e.row_k[m] + e.col_k - e.frac;
+          const int64_t y0 = WIDE ? R128((__int128)(s0 * e.row_m[m]) * e.col_m[j0], sh)
+                                  : R(s0 * e.row_m[m] * e.col_m[j0], sh);
+          int64_t k0 = amax_key(y0, j0);
+          const int64_t base = (e.out_row_base ? *e.out_row_base : 0) + m;
+          if (lane == 0) ((int32_t*)out)[base * N + j0] = (int32_t)y0;
+          if (two) {
+            const int64_t y1 = WIDE ? R128((__int128)(s1 * e.row_m[m]) * e.col_m[j0 + 1], sh)
+                                    : R(s1 * e.row_m[m] * e.col_m[j0 + 1], sh);
+            if (lane == 0) ((int32_t*)out)[base * N + j0 + 1] = (int32_t)y1;
+            const int64_t k1 = amax_key(y1, j0 + 1);
+            k0 = k1 > k0 ? k1 : k0;
+          }
+          best[m] = k0 > best[m] ? k0 : best[m];
+        } else if (lane == 0) {
           epi_store<WIDE>(s0, m, j0, N, e, out);
           if (two) epi_store<WIDE>(s1, m, j0 + 1, N, e, out);
         }
       }
     }
   }
+  if (ARGMAX && lane == 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M) part[(size_t)m * nwaves + wave] = best[m];
+  }
+}
+
+int gemv_blocks(int64_t N) {
+  const int64_t want = (N + 7) / 8;  // 8 columns per workgroup pass
+  return (int)(want < 4096 ? want : 4096);
 }
 
 template <int MT>
 hipError_t gemv_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
-                       const Epi& e, void* out, hipStream_t st) {
-  const int64_t want = ((int64_t)N + 7) / 8;  // 8 columns per workgroup pass
-  const int blocks = (int)(want < 4096 ? want : 4096);
-  if (Wlo)
-    gemv<MT, true><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out);
-  else
-    gemv<MT, false><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out);
+                       const Epi& e, void* out, int64_t* part, hipStream_t st) {
+  const int blocks = gemv_blocks(N);
+  if (part) {
+    if (Wlo)
+      gemv<MT, true, true><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out, part);
+    else
+      gemv<MT, false, true><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out, part);
+  } else {
+    if (Wlo)
+      gemv<MT, true, false><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out, nullptr);
+    else
+      gemv<MT, false, false><<<blocks, 256, 0, st>>>(A, W, Wlo, M, N, K, e, out, nullptr);
+  }
   return hipGetLastError();
+}
+
+hipError_t gemv_dispatch(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
+                         int64_t N, int64_t K, const Epi& e, void* out, int64_t* part,
+                         hipStream_t st) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (M <= 1) return gemv_launch<1>(A, W, W_lo, m, n, k, e, out, part, st);
+  if (M <= 2) return gemv_launch<2>(A, W, W_lo, m, n, k, e, out, part, st);
+  if (M <= 4) return gemv_launch<4>(A, W, W_lo, m, n, k, e, out, part, st);
+  if (M <= 8) return gemv_launch<8>(A, W, W_lo, m, n, k, e, out, part, st);
+  return gemv_launch<16>(A, W, W_lo, m, n, k, e, out, part, st);
 }
 
 __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __restrict__ hi,
@@ -257,20 +313,22 @@ __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __re
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (M <= 16) {
-    const int m = (int)M, n = (int)N, k = (int)K;
-    if (M <= 1) return gemv_launch<1>(A, W, W_lo, m, n, k, e, out, st);
-    if (M <= 2) return gemv_launch<2>(A, W, W_lo, m, n, k, e, out, st);
-    if (M <= 4) return gemv_launch<4>(A, W, W_lo, m, n, k, e, out, st);
-    if (M <= 8) return gemv_launch<8>(A, W, W_lo, m, n, k, e, out, st);
-    return gemv_launch<16>(A, W, W_lo, m, n, k, e, out, st);
-  }
+  if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   if (W_lo)
     gemm_mfma<true><<<grid, 256, 0, st>>>(A, W, W_lo, (int)M, (int)N, (int)K, e, out);
   else
     gemm_mfma<false><<<grid, 256, 0, st>>>(A, W, W_lo, (int)M, (int)N, (int)K, e, out);
   return hipGetLastError();
+}
+
+int64_t logits_argmax_parts(int64_t N) { return (int64_t)gemv_blocks(N) * 4; }
+
+hipError_t launch_logits_argmax(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
+                                int64_t N, int64_t K, const Epi& e, int32_t* logits,
+                                int64_t* part, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return gemv_dispatch(A, W, W_lo, M, N, K, e, logits, part, st);
 }
 
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,

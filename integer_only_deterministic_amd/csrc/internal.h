@@ -23,6 +23,14 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st);
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
                             hipStream_t st);
+// lm_head for M <= 16 rows: FIX-mode logits plus per-wave greedy-argmax
+// partials part[M][logits_argmax_parts(N)] (reduce with launch_argmax_final).
+int64_t logits_argmax_parts(int64_t N);
+hipError_t launch_logits_argmax(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
+                                int64_t N, int64_t K, const Epi& e, int32_t* logits,
+                                int64_t* part, hipStream_t st);
+hipError_t launch_argmax_final(const int64_t* part, int64_t S, int64_t nparts, int32_t* out,
+                               hipStream_t st);
 
 // Row ops.
 hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int16_t* gain,

@@ -402,6 +402,13 @@ hipError_t launch_argmax(const int32_t* logits, const int32_t* row_base, int64_t
   return hipGetLastError();
 }
 
+hipError_t launch_argmax_final(const int64_t* part, int64_t S, int64_t nparts, int32_t* out,
+                               hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  argmax_final_k<<<(unsigned)S, 64, 0, st>>>(part, (int)nparts, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
                           int32_t* row_base, int64_t S, hipStream_t st) {
   if (S == 0) return hipSuccess;

@@ -247,3 +247,39 @@ def test_layer256_split_and_token_by_token(D, layer_case):
     rows = [a, b] + [dm.layer(0, h0[t:t + 1], [1], [t], [1]) for t in range(50, 64)]
     np.testing.assert_array_equal(np.concatenate(rows), h1)
     np.testing.assert_array_equal(host(dm.kc)[:, 1], om.kc[:, 0])
+
+
+# -------------------------------------------------------------- lm_head
+
+@pytest.mark.parametrize("S_,V,H,wide", [(1, 151936, 1024, False), (8, 5000, 256, False),
+                                         (3, 4099, 512, True), (16, 1000, 256, False)])
+def test_lm_head_and_greedy_token(D, S_, V, H, wide):
+    rng = np.random.default_rng(S_ * V)
+    x8 = rng.integers(-127, 128, (S_, H)).astype(np.int8)
+    if wide:
+        E = rng.integers(-32767, 32768, (V, H)).astype(np.int16)
+    else:
+        E = rng.integers(-127, 128, (V, H)).astype(np.int8)
+    # duplicated rows make exact ties among the maxima: the lowest id must win
+    E[V - 1] = E[V // 2] = E[7]
+    rm = rng.integers(1 << 14, 1 << 15, S_).astype(np.int32)
+    rk = rng.integers(14, 20, S_).astype(np.int32)
+    em = rng.integers(1 << 14, 1 << 15, V).astype(np.int32)
+    em[V - 1] = em[V // 2] = em[7] = 1 << 15 - 1
+    wk, fl = (30, 16) if wide else (22, 16)
+    want = O.epilogue(O.gemm(x8, E), rm, rk, em, wk, fl, O.FIX)
+    if wide:
+        hi, lo = D.detint_split_w16(dev(E))
+    else:
+        hi, lo = dev(E), None
+    logits, part = D.detint_lm_head(dev(x8), hi, lo, dev(rm), dev(rk), dev(em), wk, fl)
+    np.testing.assert_array_equal(host(logits), want)
+    tok = host(D.detint_argmax_parts(part))
+    np.testing.assert_array_equal(tok, O.argmax(want))
+    # a row whose maximum is the tied triple picks id 7
+    x8b = np.zeros((1, H), np.int8)
+    x8b[0] = np.sign(E[7].astype(np.int64)).astype(np.int8) * 127
+    lg, pt = D.detint_lm_head(dev(x8b), hi, lo, dev(rm[:1]), dev(rk[:1]), dev(em), wk, fl)
+    lgh = host(lg)
+    assert lgh[0, 7] == lgh[0].max() == lgh[0, V // 2] == lgh[0, V - 1]
+    assert host(D.detint_argmax_parts(pt))[0] == 7
