@@ -139,7 +139,7 @@ detint_status detint_softmax(const int32_t *s, const int32_t *valid, const int32
  * s+ = RD(2^30, 2^15 + E), s = s+ (g >= 0) or 2^15 - s+ (g < 0);
  * silu = R(g * s, 15); p = silu * u; (a8, e) = DQ(p);
  * row scale (row_m, row_k) = (2^14, 2 f_a - e + 14).
- *   a8 int8 [R, n]; row_m, row_k int32 [R]. n <= 65536. */
+ *   a8 int8 [R, n]; row_m, row_k int32 [R]. n <= 8192. */
 detint_status detint_swiglu(const int32_t *gu, int64_t R, int64_t n, int32_t f_a, int8_t *a8,
                             int32_t *row_m, int32_t *row_k, void *stream);
 

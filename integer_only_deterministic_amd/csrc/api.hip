@@ -145,7 +145,7 @@ detint_status detint_softmax(const int32_t* s, const int32_t* valid, const int32
 
 detint_status detint_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int8_t* a8,
                             int32_t* row_m, int32_t* row_k, void* stream) {
-  REQUIRE(R >= 0 && n > 0 && n <= 65536 && f_a >= 0 && f_a <= 24, "swiglu: bad shape");
+  REQUIRE(R >= 0 && n > 0 && n <= 8192 && f_a >= 0 && f_a <= 24, "swiglu: bad shape (n <= 8192)");
   if (R == 0) return ok();
   REQUIRE(gu && a8 && row_m && row_k, "swiglu: null pointer");
   int32_t Mg, Kg;
@@ -357,7 +357,8 @@ detint_status detint_model_create(const detint_model_desc* desc, detint_model** 
   REQUIRE(d.n_q % d.n_kv == 0, "model_create: n_q must be a multiple of n_kv");
   REQUIRE(d.hidden % 16 == 0 && d.ffn % 16 == 0 && (d.n_q * d.head_dim) % 16 == 0,
           "model_create: hidden, ffn and n_q*d must be multiples of 16");
-  REQUIRE(d.head_dim <= 128 && d.hidden <= 16384, "model_create: head_dim/hidden too large");
+  REQUIRE(d.head_dim <= 128 && d.hidden <= 16384 && d.ffn <= 8192,
+          "model_create: head_dim/hidden/ffn too large");
   if (!attention_supported(d.head_dim, d.n_q / d.n_kv, d.max_pos))
     return fail(DETINT_EUNSUPPORTED, "model_create: attention does not support d=%lld group=%lld max_pos=%lld",
                 (long long)d.head_dim, (long long)(d.n_q / d.n_kv), (long long)d.max_pos);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     den[g] = block_sum(den[g], red);  // also orders pass-2 LDS writes before pass 4
-    rn[g] = (int64_t)udiv64(uint64_t(1) << 46, (uint64_t)den[g]);
+    rn[g] = (int64_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den[g]);  // D >= 2^15
   }
 
   // passes 3+4: probabilities and P.V

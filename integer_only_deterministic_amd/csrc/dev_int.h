@@ -57,16 +57,32 @@ __device__ __forceinline__ uint64_t udiv64(uint64_t n, uint64_t d) {
   return q;
 }
 
+// floor(n / d) when the quotient is known to be below 2^QB: QB restoring
+// steps on the shifted divisor (d << (QB - 1) must not overflow).
+template <int QB>
+__device__ __forceinline__ uint64_t udiv_q(uint64_t n, uint64_t d) {
+  uint64_t q = 0;
+#pragma unroll
+  for (int i = QB - 1; i >= 0; --i) {
+    const uint64_t t = d << i;
+    if (n >= t) {
+      n -= t;
+      q |= uint64_t(1) << i;
+    }
+  }
+  return q;
+}
+
 // RD(a, b) = floor((2a + b) / 2b), a >= 0, b > 0.
 __device__ __forceinline__ int64_t div_round(int64_t a, int64_t b) {
   return (int64_t)udiv64(2 * (uint64_t)a + (uint64_t)b, 2 * (uint64_t)b);
 }
 
-// floor(sqrt(n)), digit-by-digit.
+// floor(sqrt(n)), digit-by-digit from the highest even bit of n.
 __device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
+  if (n == 0) return 0;
   uint64_t res = 0;
-  uint64_t bit = uint64_t(1) << 62;
-  while (bit > n) bit >>= 2;
+  uint64_t bit = uint64_t(1) << ((bitlen64(n) - 1) & ~1);
   while (bit) {
     if (n >= res + bit) {
       n -= res + bit;
@@ -80,14 +96,17 @@ __device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
 }
 
 // Inverse RMS of n entries with sum of squares S > 0: 1/sqrt(S/n) ~ m * 2^-sh,
-// m in [2^14, 2^15) (DetLLM README "Layout": DI-RMSNorm).
+// m in [2^14, 2^15) (DetLLM README "Layout": DI-RMSNorm). The same integer
+// function as the definition in detint.h; the division by n is a shift when
+// n is a power of two, and RD(2^T, r) has a quotient <= 2^15.
 __device__ __forceinline__ void irms(int64_t S, int64_t n, int32_t& m, int32_t& sh) {
   const int b = bitlen64((uint64_t)S);
   const int c = b < 62 ? (62 - b) >> 1 : 0;
-  const uint64_t u = udiv64((uint64_t)S << (2 * c), (uint64_t)n);
+  const uint64_t num = (uint64_t)S << (2 * c);
+  const uint64_t u = (n & (n - 1)) == 0 ? num >> (__builtin_ctzll((uint64_t)n)) : udiv64(num, (uint64_t)n);
   const uint64_t r = isqrt64(u);
   int T = bitlen64(r) + 14;
-  int64_t mm = div_round(int64_t(1) << T, (int64_t)r);
+  int64_t mm = (int64_t)udiv_q<16>((uint64_t(1) << (T + 1)) + r, 2 * r);
   if (mm == (1 << 15)) {
     mm = 1 << 14;
     T -= 1;
@@ -110,20 +129,30 @@ __device__ __forceinline__ int32_t diexp(int64_t u) {
 
 // Integer sigmoid in Q15 of a gate g with f_a fractional bits, given the
 // exponent multiplier (Mg, Kg): E = DI-Exp(-R(|g| Mg, Kg)),
-// s+ = RD(2^30, 2^15 + E) computed by a 17-step restoring division (the
-// quotient is below 2^16), s = s+ or 2^15 - s+ by the sign of g.
+// s+ = RD(2^30, 2^15 + E) = floor((2^31 + b) / 2b) with b = 2^15 + E, a
+// quotient in [2^14, 2^15]: 15 restoring steps in 32 bits (b = 2^16 exactly,
+// i.e. E = 2^15, gives 2^14 directly), s = s+ or 2^15 - s+ by the sign of g.
 __device__ __forceinline__ int32_t sigmoid_q15(int64_t g, int32_t Mg, int32_t Kg) {
   const int64_t ag = g < 0 ? -g : g;
   const uint32_t E = (uint32_t)diexp(-R(ag * Mg, Kg));
-  const uint64_t b2 = 2u * (32768u + E);          // 2b in [2^16, 2^17]
-  uint64_t num = (1ull << 31) + (32768u + E);     // 2a + b with a = 2^30
-  uint32_t q = 0;
+  uint32_t q;
+  if (E >= 32768u) {
+    q = 16384u;
+  } else {
+    const uint32_t b2 = 2u * (32768u + E);        // 2b in [2^16, 2^17)
+    uint32_t num = (1u << 31) + (32768u + E);     // 2a + b
+    q = 0;
+    if (num >= (b2 << 15)) {                      // quotient bit 15 (b2 << 15 < 2^32)
+      num -= b2 << 15;
+      q = 1u << 15;
+    }
 #pragma unroll
-  for (int i = 15; i >= 0; --i) {
-    const uint64_t t = b2 << i;
-    if (num >= t) {
-      num -= t;
-      q |= 1u << i;
+    for (int i = 14; i >= 0; --i) {
+      const uint32_t t = b2 << i;
+      if (num >= t) {
+        num -= t;
+        q |= 1u << i;
+      }
     }
   }
   return (int32_t)(g >= 0 ? q : 32768 - q);

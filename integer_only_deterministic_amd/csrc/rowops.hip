@@ -108,7 +108,7 @@ __global__ __launch_bounds__(TPB) void softmax_k(const int32_t* __restrict__ s,
   int64_t D = 0;
   for (int j = threadIdx.x; j < v; j += TPB) D += diexp(R((sr[j] - mx) * Mm, sh));
   D = block_sum(D, red);
-  const int64_t Rn = (int64_t)udiv64(uint64_t(1) << 46, (uint64_t)D);
+  const int64_t Rn = (int64_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)D);  // D >= 2^15
   for (int j = threadIdx.x; j < C; j += TPB) {
     int64_t p = 0;
     if (j < v) {
@@ -124,22 +124,31 @@ __device__ __forceinline__ int64_t swiglu_p(int64_t g, int64_t u, int32_t Mg, in
   return R(g * sigmoid_q15(g, Mg, Kg), 15) * u;
 }
 
-__global__ __launch_bounds__(TPB) void swiglu_k(const int32_t* __restrict__ gu, int n, int32_t f_a,
+constexpr int SWT = 1024, SWPER = 8;  // n <= SWT * SWPER
+
+__global__ __launch_bounds__(SWT) void swiglu_k(const int32_t* __restrict__ gu, int n, int32_t f_a,
                                                 int32_t Mg, int32_t Kg, int8_t* __restrict__ a8,
                                                 int32_t* __restrict__ rm, int32_t* __restrict__ rk) {
   __shared__ int64_t red[16];
   const int r = blockIdx.x;
   const int32_t* g = gu + (size_t)r * 2 * n;
   const int32_t* u = g + n;
+  int64_t p[SWPER];
   int64_t A = 0;
-  for (int j = threadIdx.x; j < n; j += TPB) {
-    const int64_t p = (int64_t)uabs64(swiglu_p(g[j], u[j], Mg, Kg));
-    A = p > A ? p : A;
+#pragma unroll
+  for (int i = 0; i < SWPER; ++i) {
+    const int j = threadIdx.x + i * SWT;
+    p[i] = j < n ? swiglu_p(g[j], u[j], Mg, Kg) : 0;
+    const int64_t a = (int64_t)uabs64(p[i]);
+    A = a > A ? a : A;
   }
   A = block_max(A, red);
   const int e = dq_exp((uint64_t)A);
-  for (int j = threadIdx.x; j < n; j += TPB)
-    a8[(size_t)r * n + j] = clamp8(R(swiglu_p(g[j], u[j], Mg, Kg), e));
+#pragma unroll
+  for (int i = 0; i < SWPER; ++i) {
+    const int j = threadIdx.x + i * SWT;
+    if (j < n) a8[(size_t)r * n + j] = clamp8(R(p[i], e));
+  }
   if (threadIdx.x == 0) {
     rm[r] = 1 << 14;
     rk[r] = 2 * f_a - e + 14;
@@ -188,7 +197,8 @@ __global__ void decode_meta_k(const int32_t* __restrict__ ctx, const int32_t* __
   }
 }
 
-// QKV post-processing, one wave per (row, head); lane i < d/2 owns the RoPE
+// QKV post-processing, one wave per (row, head) - four heads per workgroup,
+// grid (rows, heads / 4); lane i < d/2 owns the RoPE
 // pair (i, i + d/2). q/k: per-head RMSNorm (Qwen3 q/k-norm, before RoPE per
 // DetLLM blog footnote 8) or the f_n fixed point, then RoPE; q -> DQ per
 // head; k, v -> int8 at the fixed cache scales, written once into the cache
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
                                                   int n_slots, int max_pos) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int half = d >> 1;
   const int nh = nq + 2 * nkv;
   const int pos = pos_of[r], slot = slot_of[r];
@@ -209,10 +219,10 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
   const bool act = lane < half;
   const int j0 = lane, j1 = lane + half;
   const int32_t* row = qkv + (size_t)r * nh * d;
-  for (int hh = wave; hh < nh; hh += TPB / 64) {
+  if (hh < nh) {
     const int c0 = hh * d;
     if (hh >= nq + nkv) {  // V
-      if (!act || !ok) continue;
+      if (!act || !ok) return;
       const int kvh = hh - nq - nkv;
       int8_t* dst = vc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
 #pragma unroll
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
           vf = R(vf * p.row_m[r] * p.col_m[c0 + j], p.row_k[r] + p.col_k - p.f_n);
         dst[j] = clamp8(R(vf * p.vq_m, p.vq_k));
       }
-      continue;
+      return;
     }
     int64_t x0 = 0, x1 = 0;
     if (act) {
@@ -298,11 +308,16 @@ __global__ __launch_bounds__(TPB) void argmax_part_k(const int32_t* __restrict__
   if (threadIdx.x == 0) part[(size_t)s * nparts + pi] = best;
 }
 
-__global__ void argmax_final_k(const int64_t* __restrict__ part, int nparts, int32_t* out) {
+__global__ __launch_bounds__(1024) void argmax_final_k(const int64_t* __restrict__ part, int nparts,
+                                                      int32_t* out) {
+  __shared__ int64_t red[16];
   const int s = blockIdx.x;
   int64_t best = INT64_MIN;
-  for (int i = threadIdx.x; i < nparts; i += 64) best = part[(size_t)s * nparts + i] > best ? part[(size_t)s * nparts + i] : best;
-  best = wave_max(best);
+  for (int i = threadIdx.x; i < nparts; i += 1024) {
+    const int64_t k = part[(size_t)s * nparts + i];
+    best = k > best ? k : best;
+  }
+  best = block_max(best, red);
   if (threadIdx.x == 0) out[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFLL));
 }
 
@@ -355,7 +370,8 @@ hipError_t launch_softmax(const int32_t* s, const int32_t* valid, const int32_t*
 hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int32_t Mg,
                          int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  swiglu_k<<<(unsigned)R, TPB, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+  if (n > SWT * SWPER) return hipErrorInvalidValue;
+  swiglu_k<<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
   return hipGetLastError();
 }
 
@@ -387,8 +403,9 @@ hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nk
                            int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
                            int64_t max_pos, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  qkv_post_k<<<(unsigned)R, TPB, 0, st>>>(qkv, (int)nq, (int)nkv, (int)d, pos_of, slot_of, p, q8,
-                                          e_q, kc, vc, (int)n_slots, (int)max_pos);
+  const unsigned hb = (unsigned)((nq + 2 * nkv + 3) / 4);  // 4 heads (waves) per workgroup
+  qkv_post_k<<<dim3((unsigned)R, hb), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, (int)d, pos_of, slot_of,
+                                                     p, q8, e_q, kc, vc, (int)n_slots, (int)max_pos);
   return hipGetLastError();
 }
 
@@ -398,14 +415,14 @@ hipError_t launch_argmax(const int32_t* logits, const int32_t* row_base, int64_t
   const int chunk = (int)((V + nparts - 1) / nparts);
   argmax_part_k<<<dim3((unsigned)nparts, (unsigned)S), TPB, 0, st>>>(logits, row_base, (int)V,
                                                                       (int)nparts, chunk, part);
-  argmax_final_k<<<(unsigned)S, 64, 0, st>>>(part, (int)nparts, out);
+  argmax_final_k<<<(unsigned)S, 1024, 0, st>>>(part, (int)nparts, out);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax_final(const int64_t* part, int64_t S, int64_t nparts, int32_t* out,
                                hipStream_t st) {
   if (S == 0) return hipSuccess;
-  argmax_final_k<<<(unsigned)S, 64, 0, st>>>(part, (int)nparts, out);
+  argmax_final_k<<<(unsigned)S, 1024, 0, st>>>(part, (int)nparts, out);
   return hipGetLastError();
 }
 
