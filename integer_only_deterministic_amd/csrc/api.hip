@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/detint.h"
+#include "detint.h"
 #include "internal.h"
 
 using namespace detint;
@@ -309,7 +309,7 @@ constexpr int64_t kArgmaxParts = 64;
 int64_t al(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct WsLayout {
-  int64_t pos_of, slot_of, last_row, h, x8, rm, rk, qkv, q8, eq, att, gu, part, total;
+  int64_t pos_of, slot_of, last_row, h, x8, rm, rk, qkv, q8, eq, att, gu, p64, part, total;
 };
 
 WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
@@ -338,7 +338,10 @@ WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
   w.eq = take(4 * R * d.n_q);
   w.att = take(4 * R * nqd);
   w.gu = take(4 * R * 2 * d.ffn);
-  const int64_t np = logits_argmax_parts(d.vocab > 0 ? d.vocab : 1);
+  w.p64 = take(8 * R * d.ffn);
+  int64_t np = logits_argmax_parts(d.vocab > 0 ? d.vocab : 1);
+  const int64_t npf = fused_decode_parts(d.vocab > 0 ? d.vocab : 1);
+  if (npf > np) np = npf;
   w.part = take(8 * S * (np > kArgmaxParts ? np : kArgmaxParts));
   w.total = o;
   return w;
@@ -463,6 +466,59 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   return ok();
 }
 
+// Decode-shaped forward (R == S rows, one per sequence at position
+// start_pos[s]): embedding, then per layer fused [RMSNorm + QKV],
+// [q/k-norm + RoPE + KV write + attention], [DQ + O-proj + residual],
+// [RMSNorm + gate/up + SwiGLU product], [DQ + down + residual]; then
+// [RMSNorm + lm_head + argmax partials] and [greedy token + advance].
+static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
+                                int64_t n_slots, int32_t* ids, int64_t R, int32_t* start_pos,
+                                const int32_t* slot, int32_t* logits, int32_t* row_base,
+                                int32_t* next_tok, bool advance, char* base, const WsLayout& w,
+                                hipStream_t st) {
+  const detint_model_desc& d = m->d;
+  int32_t* h = (int32_t*)(base + w.h);
+  int32_t* rm = (int32_t*)(base + w.rm);
+  int32_t* rk = (int32_t*)(base + w.rk);
+  int32_t* qkv = (int32_t*)(base + w.qkv);
+  int32_t* att = (int32_t*)(base + w.att);
+  int64_t* p64 = (int64_t*)(base + w.p64);
+  int64_t* part = (int64_t*)(base + w.part);
+  const int64_t H = d.hidden, nq = d.n_q, nkv = d.n_kv, hd = d.head_dim, F = d.ffn;
+  const int64_t nqd = nq * hd, nqkv = (nq + 2 * nkv) * hd;
+  const size_t layer_stride = (size_t)n_slots * nkv * d.max_pos * hd;
+  const int32_t wk = d.w_k;
+  hipError_t e;
+#define LAUNCH(x)                                  \
+  do {                                             \
+    e = (x);                                       \
+    if (e != hipSuccess) return hip_status(e, #x); \
+  } while (0)
+  LAUNCH(launch_embed(ids, R, d.emb, nullptr, d.emb_m, H, d.vocab, wk - d.f_res, h, st));
+  for (int64_t l = 0; l < d.n_layers; ++l) {
+    const detint_layer_desc& L = m->layers[l];
+    int8_t* kc = k_cache + l * layer_stride;
+    int8_t* vc = v_cache + l * layer_stride;
+    LAUNCH(launch_fused_qkv(h, L.attn_norm, L.wqkv, L.wqkv_m, wk, d.qk_norm ? 0 : d.f_n,
+                            d.qk_norm != 0, R, nqkv, H, qkv, rm, rk, st));
+    QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
+               L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
+    LAUNCH(launch_attention_decode_fused(qkv, qp, start_pos, slot, R, nq, nkv, hd, n_slots,
+                                         d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att, st));
+    LAUNCH(launch_fused_oproj(att, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, L.wo, L.wo_m, wk, d.f_res,
+                              R, H, nqd, h, st));
+    LAUNCH(launch_fused_gateup(h, L.ffn_norm, L.wgu, L.wgu_m, wk, d.f_a, m->mg, m->kg, R, F, H, p64,
+                               st));
+    LAUNCH(launch_fused_down(p64, d.f_a, L.wd, L.wd_m, wk, d.f_res, R, H, F, h, st));
+  }
+  LAUNCH(launch_fused_lm_head(h, nullptr, d.final_norm, d.emb, d.emb_m, wk, d.f_l, R, d.vocab, H,
+                              logits, row_base, part, st));
+  LAUNCH(launch_argmax_advance(part, R, fused_decode_parts(d.vocab), next_tok, ids, start_pos,
+                               row_base, advance, st));
+#undef LAUNCH
+  return ok();
+}
+
 static detint_status check_run(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
                                int64_t n_slots, int64_t R, const int32_t* cu_seqlens,
                                const int32_t* start_pos, const int32_t* slot, int64_t S,
@@ -527,6 +583,15 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
     e = (x);                                       \
     if (e != hipSuccess) return hip_status(e, #x); \
   } while (0)
+  int64_t kmax = d.hidden;
+  if (d.ffn > kmax) kmax = d.ffn;
+  if (d.n_q * d.head_dim > kmax) kmax = d.n_q * d.head_dim;
+  if (R == S && !d.wide && fused_decode_supported(R, kmax)) {
+    // decode-shaped call (one row per sequence): 5 fused kernels per layer
+    s = run_decode(m, k_cache, v_cache, n_slots, ids, R, start_pos, slot, logits, logit_row_base,
+                   next_tok, (flags & DETINT_FWD_ADVANCE) != 0, base, w, st);
+    return s;
+  }
   LAUNCH(launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
                           (int32_t*)(base + w.slot_of), last_row, st));
   LAUNCH(launch_embed(ids, R, d.emb, d.wide ? d.emb_lo : nullptr, d.emb_m, d.hidden, d.vocab,

@@ -1,0 +1,434 @@
+// Fused weight-streaming kernels for decode-sized batches (M <= 8 rows).
+//
+// A decode step is a chain of small GEMVs whose cost on this GPU is set by
+// the number of kernels and by memory latency, not by bytes: a graph node
+// costs ~1.6 us and a kernel with two dependent memory round trips a few us
+// more. Each kernel here therefore (1) issues its first weight loads before
+// touching activations (weights never depend on them), (2) recomputes the
+// row-wise prologue its input needs in every workgroup - RMSNorm of the
+// residual, or DQ of the attention output / SwiGLU product (DetLLM blog
+// "DetLLM": per-token quantisation from the token's own values) - into LDS,
+// and (3) fuses the dyadic epilogue: fixed point, residual add, the SwiGLU
+// product of a (gate j, up j) column pair, or int32 logits with greedy-argmax
+// partials. Every step is the same integer function as the unfused kernels.
+#include "dev_int.h"
+#include "internal.h"
+
+namespace detint {
+namespace {
+
+constexpr int TPB = 256;
+
+__device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
+  c = __builtin_amdgcn_sdot4(a.x, b.x, c, false);
+  c = __builtin_amdgcn_sdot4(a.y, b.y, c, false);
+  c = __builtin_amdgcn_sdot4(a.z, b.z, c, false);
+  c = __builtin_amdgcn_sdot4(a.w, b.w, c, false);
+  return c;
+}
+
+__device__ __forceinline__ int64_t amax_key(int64_t v, int64_t j) {
+  return (v * 4294967296LL) | (int64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+// Transposed wave reduction of NV (a power of two <= 64) int32 values per
+// lane: each halving step exchanges half of the values with the lane `O`
+// apart, so NV sums take NV - 1 + log2(64 / NV) shuffles instead of 6 NV.
+// Afterwards lane l holds the wave total of value index
+//   idx(l) = sum_s bit(l, 5 - s) * (NV >> (s + 1)),
+// identical in the 64 / NV lanes that differ only in their low bits. Sizes
+// and lane offsets are template constants, so every register index is static
+// and the exchanges compile to fixed-pattern lane swizzles.
+template <int N, int O>
+struct Halve {
+  __device__ __forceinline__ static int run(int* v, int lane) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const int keep = upper ? v[i + N / 2] : v[i];
+      const int give = upper ? v[i] : v[i + N / 2];
+      v[i] = keep + __shfl_xor(give, O);
+    }
+    return Halve<N / 2, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct Halve<1, O> {
+  __device__ __forceinline__ static int run(int* v, int) {
+    int t = v[0];
+#pragma unroll
+    for (int o = O; o > 0; o >>= 1) t += __shfl_xor(t, o);
+    return t;
+  }
+};
+
+template <int NV>
+__device__ __forceinline__ int wave_reduce_t(int (&v)[NV], int lane) {
+  return Halve<NV, 32>::run(v, lane);
+}
+
+// The same transposed reduction for int64 values with a sum or a max.
+template <int N, int O, bool MAX>
+struct Halve64 {
+  __device__ __forceinline__ static int64_t run(int64_t* v, int lane) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const int64_t keep = upper ? v[i + N / 2] : v[i];
+      const int64_t give = upper ? v[i] : v[i + N / 2];
+      const int64_t got = __shfl_xor(give, O);
+      v[i] = MAX ? (got > keep ? got : keep) : keep + got;
+    }
+    return Halve64<N / 2, O / 2, MAX>::run(v, lane);
+  }
+};
+template <int O, bool MAX>
+struct Halve64<1, O, MAX> {
+  __device__ __forceinline__ static int64_t run(int64_t* v, int) {
+    int64_t t = v[0];
+#pragma unroll
+    for (int o = O; o > 0; o >>= 1) {
+      const int64_t got = __shfl_xor(t, o);
+      t = MAX ? (got > t ? got : t) : t + got;
+    }
+    return t;
+  }
+};
+
+template <int NV>
+__device__ __forceinline__ int reduce_index(int lane) {
+  int idx = 0, h = NV >> 1, b = 5;
+#pragma unroll
+  for (int n = NV; n > 1; n >>= 1, h >>= 1, --b) idx += ((lane >> b) & 1) * h;
+  return idx;
+}
+
+enum { PRO_NORM = 1, PRO_DQ32 = 2, PRO_DQ64 = 3 };
+enum { EPI_RAW = 0, EPI_FIX = 1, EPI_RES = 2, EPI_SWIGLU = 3, EPI_LOGITS = 4 };
+
+struct FG {
+  const int32_t* h;          // PRO_NORM: residual rows [*, K]
+  const int16_t* gain;
+  const int32_t* row_index;  // PRO_NORM: input row of output row m (nullable)
+  const int32_t* in32;       // PRO_DQ32: [M, K]
+  int32_t fold_m, fold_k;    //   row scale (fold_m, fold_k - e)
+  const int64_t* in64;       // PRO_DQ64: [M, K]; row scale (2^14, 2 f_a - e + 14)
+  int32_t f_a;
+  const int8_t* W;           // [N, K] ([2N, K] for SWIGLU: gate rows then up rows)
+  const int32_t* col_m;
+  int32_t col_k, frac;
+  int32_t Mg, Kg;            // SWIGLU sigmoid multiplier
+  int32_t M, N, K;
+  void* out;
+  const int32_t* out_row_base;
+  int64_t* part;
+  int32_t* rm_out;           // nullable: row scales written by workgroup 0
+  int32_t* rk_out;
+};
+
+template <int MT, int CPW, int KC, int PRO, int EPI>
+__global__ __launch_bounds__(TPB) void fgemv(FG p) {
+  extern __shared__ __attribute__((aligned(16))) int8_t sx[];  // [MT][K] int8 input rows
+  __shared__ int64_t sred[TPB / 64][2 * MT];
+  __shared__ int32_t s_m[MT], s_k[MT], s_e[MT];
+  constexpr int NV = CPW * MT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gw = blockIdx.x * (TPB / 64) + wave, nw = gridDim.x * (TPB / 64);
+  const int M = p.M, N = p.N, K = p.K;
+  const int ngroups = EPI == EPI_SWIGLU ? N : (N + CPW - 1) / CPW;
+
+  // 1. weight loads for the first group are issued right after the
+  //    activation loads below (loads complete in order, so the activations
+  //    must go first to be usable while the weights are still in flight)
+  v4i w[CPW][KC];
+  auto load_w = [&](int g) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int row = EPI == EPI_SWIGLU ? (c == 0 ? g : N + g) : g * CPW + c;
+      const bool rv = EPI == EPI_SWIGLU ? true : row < N;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int k = kc * 1024 + lane * 16;
+        const v4i z = {0, 0, 0, 0};
+        w[c][kc] = (rv && k < K) ? *(const v4i*)(p.W + (size_t)row * K + k) : z;
+      }
+    }
+  };
+  int g = gw;
+
+  // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
+  //    elements kc * 1024 + 4 t .. + 3 of every row; all of its loads are
+  //    issued together and kept in registers for the quantisation pass.
+  typedef int64_t v4l __attribute__((ext_vector_type(4)));
+  constexpr bool WIDE_IN = PRO == PRO_DQ64;
+  int64_t xv[MT][KC][4];
+  int32_t gv[KC][4];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const int i = kc * 1024 + 4 * tid;
+    if (PRO == PRO_NORM) {
+      if (i < K) {
+        const int2 gg = *(const int2*)(p.gain + i);  // four int16 gains
+        gv[kc][0] = (int16_t)(gg.x & 0xFFFF);
+        gv[kc][1] = (int16_t)(gg.x >> 16);
+        gv[kc][2] = (int16_t)(gg.y & 0xFFFF);
+        gv[kc][3] = (int16_t)(gg.y >> 16);
+      } else {
+        gv[kc][0] = gv[kc][1] = gv[kc][2] = gv[kc][3] = 0;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M && i < K) {
+        if (PRO == PRO_NORM) {
+          const int src = p.row_index ? p.row_index[m] : m;
+          const v4i t4 = *(const v4i*)(p.h + (size_t)src * K + i);
+          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
+        } else if (!WIDE_IN) {
+          const v4i t4 = *(const v4i*)(p.in32 + (size_t)m * K + i);
+          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
+        } else {
+          const v4l t4 = *(const v4l*)(p.in64 + (size_t)m * K + i);
+          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
+        }
+      } else {
+        xv[m][kc][0] = xv[m][kc][1] = xv[m][kc][2] = xv[m][kc][3] = 0;
+      }
+    }
+  }
+  if (g < ngroups) load_w(g);  // weights in flight during the prologue arithmetic
+  int64_t Sv[MT], Av[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    int64_t S = 0, A = 0;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t v = xv[m][kc][e4];
+        if (PRO == PRO_NORM) S += v * v;
+        const int64_t a = (int64_t)uabs64(PRO == PRO_NORM ? v * gv[kc][e4] : v);
+        A = a > A ? a : A;
+      }
+    Sv[m] = S;
+    Av[m] = A;
+  }
+  {
+    // wave totals of every row at once: lane l ends with row idx(l)'s totals
+    const int64_t At = Halve64<MT, 32, true>::run(Av, lane);
+    const int64_t St = PRO == PRO_NORM ? Halve64<MT, 32, false>::run(Sv, lane) : 0;
+    const int r = reduce_index<MT>(lane);
+    if ((lane & (64 / MT - 1)) == 0) {
+      sred[wave][2 * r] = St;
+      sred[wave][2 * r + 1] = At;
+    }
+  }
+  __syncthreads();
+  // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole wave)
+  for (int r = wave; r < M; r += TPB / 64) {
+    int64_t St = 0, At = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < TPB / 64; ++w2) {
+      St += sred[w2][2 * r];
+      At = sred[w2][2 * r + 1] > At ? sred[w2][2 * r + 1] : At;
+    }
+    const int e = dq_exp((uint64_t)At);
+    int32_t sm, sk;
+    if (PRO == PRO_NORM) {
+      if (St == 0) {
+        sm = 1 << 14;
+        sk = 26;
+      } else {
+        int32_t mm, sh;
+        irms_wave(St, K, mm, sh);
+        sm = mm;
+        sk = sh + 12 - e;
+      }
+    } else if (PRO == PRO_DQ32) {
+      sm = p.fold_m;
+      sk = p.fold_k - e;
+    } else {
+      sm = 1 << 14;
+      sk = 2 * p.f_a - e + 14;
+    }
+    if (lane == 0) {
+      s_m[r] = sm;
+      s_k[r] = sk;
+      s_e[r] = (PRO == PRO_NORM && St == 0) ? 0 : e;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < M) {
+      const int e = s_e[m];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int i = kc * 1024 + 4 * tid;
+        if (i < K) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int64_t v = PRO == PRO_NORM ? xv[m][kc][e4] * gv[kc][e4] : xv[m][kc][e4];
+            // |R(v, e)| <= 128 by the choice of e, so the clamp can run in 32 bits
+            const int32_t q = (int32_t)R_nn(v, e);
+            packed |= (uint32_t)(uint8_t)(q > 127 ? 127 : (q < -127 ? -127 : q)) << (8 * e4);
+          }
+          *(uint32_t*)(sx + (size_t)m * K + i) = packed;
+        }
+      }
+    }
+  }
+  if (p.rm_out && blockIdx.x == 0 && tid < M) {
+    p.rm_out[tid] = s_m[tid];
+    p.rk_out[tid] = s_k[tid];
+  }
+  __syncthreads();
+
+  // 3. stream the weights: per group, dot products from LDS, reduce, epilogue
+  const int idx = reduce_index<NV>(lane);
+  const bool leader = (lane & (64 / NV - 1)) == 0;
+  const int cc = idx / MT, mm = idx % MT;  // the (column, row) this lane finishes
+  int64_t bestk = INT64_MIN;
+  const int64_t obase = EPI == EPI_LOGITS && p.out_row_base ? *p.out_row_base : 0;
+  for (; g < ngroups; g += nw) {
+    int v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = 0;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int k = kc * 1024 + lane * 16;
+      if (k < K) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const v4i x = *(const v4i*)(sx + (size_t)m * K + k);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c) v[c * MT + m] = dot16(x, w[c][kc], v[c * MT + m]);
+        }
+      }
+    }
+    const int gn = g + nw;
+    if (gn < ngroups) load_w(gn);  // next group's weights in flight during the epilogue
+    const int tot = wave_reduce_t<NV>(v, lane);
+    if (EPI == EPI_SWIGLU) {
+      const int up = __shfl_xor(tot, 32);  // column 1 (up) sits in the lane 32 apart
+      if (leader && cc == 0 && mm < M) {
+        const int j = g;
+        const int sh = s_k[mm] + p.col_k - p.f_a;
+        const int64_t gv = R((int64_t)tot * s_m[mm] * p.col_m[j], sh);
+        const int64_t uv = R((int64_t)up * s_m[mm] * p.col_m[N + j], sh);
+        ((int64_t*)p.out)[(size_t)mm * N + j] = R(gv * sigmoid_q15(gv, p.Mg, p.Kg), 15) * uv;
+      }
+    } else if (leader && mm < M) {
+      const int col = g * CPW + cc;
+      if (col < N) {
+        if (EPI == EPI_RAW) {
+          ((int32_t*)p.out)[(size_t)mm * N + col] = tot;
+        } else {
+          const int64_t y = R((int64_t)tot * s_m[mm] * p.col_m[col], s_k[mm] + p.col_k - p.frac);
+          if (EPI == EPI_FIX) {
+            ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)y;
+          } else if (EPI == EPI_RES) {
+            ((int32_t*)p.out)[(size_t)mm * N + col] += (int32_t)y;
+          } else {
+            ((int32_t*)p.out)[(size_t)(obase + mm) * N + col] = (int32_t)y;
+            const int64_t key = amax_key(y, col);
+            bestk = key > bestk ? key : bestk;
+          }
+        }
+      }
+    }
+  }
+  if (EPI == EPI_LOGITS) {
+    if (CPW == 2) {
+      const int64_t o2 = __shfl_xor(bestk, 32);
+      bestk = o2 > bestk ? o2 : bestk;
+    }
+    if (leader && cc == 0 && mm < M) p.part[(size_t)mm * nw + gw] = bestk;
+  }
+}
+
+int cap_blocks(int64_t groups) {
+  const int64_t b = (groups + 3) / 4;
+  return (int)(b < 2048 ? (b > 0 ? b : 1) : 2048);
+}
+
+template <int MT, int CPW, int PRO, int EPI>
+hipError_t launch_kc(const FG& p, hipStream_t st) {
+  const int64_t groups = EPI == EPI_SWIGLU ? p.N : (p.N + CPW - 1) / CPW;
+  const int blocks = cap_blocks(groups);
+  const size_t lds = (size_t)MT * p.K;
+  const int kc = (p.K + 1023) / 1024;
+#define DETINT_KC(KK)                                                         \
+  if (kc <= KK) {                                                             \
+    fgemv<MT, CPW, KK, PRO, EPI><<<blocks, TPB, lds, st>>>(p);                \
+    return hipGetLastError();                                                 \
+  }
+  DETINT_KC(1) DETINT_KC(2) DETINT_KC(3) DETINT_KC(8)
+#undef DETINT_KC
+  return hipErrorInvalidValue;
+}
+
+template <int CPW, int PRO, int EPI>
+hipError_t launch_mt(const FG& p, hipStream_t st) {
+  if (p.M <= 1) return launch_kc<1, CPW, PRO, EPI>(p, st);
+  if (p.M <= 4) return launch_kc<4, CPW, PRO, EPI>(p, st);
+  return launch_kc<8, CPW, PRO, EPI>(p, st);
+}
+
+}  // namespace
+
+int fused_decode_parts(int64_t V) { return cap_blocks((V + 1) / 2) * 4; }
+
+bool fused_decode_supported(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K <= 8192 && K % 16 == 0; }
+
+hipError_t launch_fused_qkv(const int32_t* h, const int16_t* gain, const int8_t* W,
+                            const int32_t* col_m, int32_t col_k, int32_t frac, bool raw, int64_t M,
+                            int64_t N, int64_t K, int32_t* out, int32_t* rm_out, int32_t* rk_out,
+                            hipStream_t st) {
+  FG p{};
+  p.h = h; p.gain = gain; p.W = W; p.col_m = col_m; p.col_k = col_k; p.frac = frac;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = out; p.rm_out = rm_out; p.rk_out = rk_out;
+  return raw ? launch_mt<2, PRO_NORM, EPI_RAW>(p, st) : launch_mt<2, PRO_NORM, EPI_FIX>(p, st);
+}
+
+hipError_t launch_fused_oproj(const int32_t* att, int32_t fold_m, int32_t fold_k, const int8_t* W,
+                              const int32_t* col_m, int32_t col_k, int32_t frac, int64_t M,
+                              int64_t N, int64_t K, int32_t* h, hipStream_t st) {
+  FG p{};
+  p.in32 = att; p.fold_m = fold_m; p.fold_k = fold_k; p.W = W; p.col_m = col_m; p.col_k = col_k;
+  p.frac = frac; p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h;
+  return launch_mt<1, PRO_DQ32, EPI_RES>(p, st);
+}
+
+hipError_t launch_fused_gateup(const int32_t* h, const int16_t* gain, const int8_t* W,
+                               const int32_t* col_m, int32_t col_k, int32_t f_a, int32_t Mg,
+                               int32_t Kg, int64_t M, int64_t F, int64_t K, int64_t* prod,
+                               hipStream_t st) {
+  FG p{};
+  p.h = h; p.gain = gain; p.W = W; p.col_m = col_m; p.col_k = col_k; p.f_a = f_a; p.Mg = Mg;
+  p.Kg = Kg; p.M = (int)M; p.N = (int)F; p.K = (int)K; p.out = prod;
+  return launch_mt<2, PRO_NORM, EPI_SWIGLU>(p, st);
+}
+
+hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, const int32_t* col_m,
+                             int32_t col_k, int32_t frac, int64_t M, int64_t N, int64_t K,
+                             int32_t* h, hipStream_t st) {
+  FG p{};
+  p.in64 = prod; p.f_a = f_a; p.W = W; p.col_m = col_m; p.col_k = col_k; p.frac = frac;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h;
+  return launch_mt<1, PRO_DQ64, EPI_RES>(p, st);
+}
+
+hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, const int16_t* gain,
+                                const int8_t* E, const int32_t* emb_m, int32_t w_k, int32_t f_l,
+                                int64_t M, int64_t V, int64_t K, int32_t* logits,
+                                const int32_t* row_base, int64_t* part, hipStream_t st) {
+  FG p{};
+  p.h = h; p.row_index = row_index; p.gain = gain; p.W = E; p.col_m = emb_m; p.col_k = w_k;
+  p.frac = f_l; p.M = (int)M; p.N = (int)V; p.K = (int)K; p.out = logits;
+  p.out_row_base = row_base; p.part = part;
+  return launch_mt<2, PRO_NORM, EPI_LOGITS>(p, st);
+}
+
+}  // namespace detint

@@ -36,6 +36,13 @@ __device__ __forceinline__ int64_t R128(__int128 x, int s) {
 
 __device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __builtin_clzll(x) : 0; }
 
+// R(x, e) for a shift e >= 0 known to be the same across the wave (a DQ
+// exponent): branch-free, the rounding half is 2^e >> 1 (0 for e = 0).
+__device__ __forceinline__ int64_t R_nn(int64_t x, int e) {
+  e = __builtin_amdgcn_readfirstlane(e);
+  return (x + ((int64_t(1) << e) >> 1)) >> e;
+}
+
 __device__ __forceinline__ int8_t clamp8(int64_t x) {
   return (int8_t)(x > 127 ? 127 : (x < -127 ? -127 : x));
 }
@@ -107,6 +114,60 @@ __device__ __forceinline__ void irms(int64_t S, int64_t n, int32_t& m, int32_t& 
   const uint64_t r = isqrt64(u);
   int T = bitlen64(r) + 14;
   int64_t mm = (int64_t)udiv_q<16>((uint64_t(1) << (T + 1)) + r, 2 * r);
+  if (mm == (1 << 15)) {
+    mm = 1 << 14;
+    T -= 1;
+  }
+  m = (int32_t)mm;
+  sh = T - c;
+}
+
+// ------------------------------------------------------ wave-parallel forms
+// Same integer functions as isqrt64 / udiv_q / irms, computed by a whole
+// wave (all 64 lanes active, uniform inputs): the result is found 6 bits at a
+// time, lane l testing the candidate with l in the current 6-bit digit; the
+// test is monotone in l, so the highest passing lane (ballot + clz) gives the
+// digit. About 6 rounds replace 31-47 dependent serial steps.
+
+// floor(sqrt(u)) for u < 2^64.
+__device__ __forceinline__ uint64_t isqrt_wave(uint64_t u) {
+  const uint64_t lane = threadIdx.x & 63;
+  const int nb = (bitlen64(u) + 1) >> 1;  // bits of the root
+  uint64_t r = 0;
+  for (int s = ((nb - 1) / 6) * 6; s >= 0; s -= 6) {
+    const uint64_t c = r | (lane << s);
+    const bool ok = c < (uint64_t(1) << 32) && c * c <= u;
+    const uint64_t mask = __ballot(ok);
+    r |= (uint64_t)(63 - __builtin_clzll(mask)) << s;
+  }
+  return r;
+}
+
+// floor(n / d), d > 0, when the quotient is known to be below 2^QB and
+// 2^QB * d < 2^64 (so every candidate product fits 64 bits).
+template <int QB>
+__device__ __forceinline__ uint64_t udiv_wave(uint64_t n, uint64_t d) {
+  const uint64_t lane = threadIdx.x & 63;
+  uint64_t q = 0;
+#pragma unroll
+  for (int s = ((QB - 1) / 6) * 6; s >= 0; s -= 6) {
+    const uint64_t c = q | (lane << s);
+    const bool ok = c < (uint64_t(1) << QB) && c * d <= n;
+    const uint64_t mask = __ballot(ok);
+    q |= (uint64_t)(63 - __builtin_clzll(mask)) << s;
+  }
+  return q;
+}
+
+// irms (see above) by a whole wave.
+__device__ __forceinline__ void irms_wave(int64_t S, int64_t n, int32_t& m, int32_t& sh) {
+  const int b = bitlen64((uint64_t)S);
+  const int c = b < 62 ? (62 - b) >> 1 : 0;
+  const uint64_t num = (uint64_t)S << (2 * c);
+  const uint64_t u = (n & (n - 1)) == 0 ? num >> (__builtin_ctzll((uint64_t)n)) : udiv64(num, (uint64_t)n);
+  const uint64_t r = isqrt_wave(u);
+  int T = bitlen64(r) + 14;
+  int64_t mm = (int64_t)udiv_wave<16>((uint64_t(1) << (T + 1)) + r, 2 * r);
   if (mm == (1 << 15)) {
     mm = 1 << 14;
     T -= 1;

@@ -98,6 +98,13 @@ hipError_t launch_attention(const int8_t* q8, const int32_t* e_q, const int8_t* 
                             const int8_t* vc, const RowMap& rows, int64_t R, int64_t nq,
                             int64_t nkv, int64_t d, int64_t n_slots, int64_t max_pos, int32_t M,
                             int32_t K, int32_t* out, hipStream_t st);
+// Decode (one row per sequence at position start_pos[b] of slot slot[b]):
+// QKV post-processing of each (row, KV head)'s own heads fused with attention.
+hipError_t launch_attention_decode_fused(const int32_t* qkv, const QkvPost& p,
+                                         const int32_t* start_pos, const int32_t* slot, int64_t B,
+                                         int64_t nq, int64_t nkv, int64_t d, int64_t n_slots,
+                                         int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M,
+                                         int32_t K, int32_t* out, hipStream_t st);
 // true when the attention kernel supports (d, n_q / n_kv, max_pos)
 bool attention_supported(int64_t d, int64_t group, int64_t max_pos);
 
@@ -106,5 +113,30 @@ hipError_t launch_argmax(const int32_t* logits, const int32_t* row_base, int64_t
                          int64_t* part, int64_t nparts, int32_t* out, hipStream_t st);
 hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
                           int32_t* row_base, int64_t S, hipStream_t st);
+hipError_t launch_argmax_advance(const int64_t* part, int64_t S, int64_t nparts, int32_t* next_tok,
+                                 int32_t* ids, int32_t* start_pos, int32_t* row_base, bool advance,
+                                 hipStream_t st);
+
+// Fused decode kernels (decode.hip), M <= 8 rows of 8-bit weights.
+bool fused_decode_supported(int64_t M, int64_t K);
+int fused_decode_parts(int64_t V);
+hipError_t launch_fused_qkv(const int32_t* h, const int16_t* gain, const int8_t* W,
+                            const int32_t* col_m, int32_t col_k, int32_t frac, bool raw, int64_t M,
+                            int64_t N, int64_t K, int32_t* out, int32_t* rm_out, int32_t* rk_out,
+                            hipStream_t st);
+hipError_t launch_fused_oproj(const int32_t* att, int32_t fold_m, int32_t fold_k, const int8_t* W,
+                              const int32_t* col_m, int32_t col_k, int32_t frac, int64_t M,
+                              int64_t N, int64_t K, int32_t* h, hipStream_t st);
+hipError_t launch_fused_gateup(const int32_t* h, const int16_t* gain, const int8_t* W,
+                               const int32_t* col_m, int32_t col_k, int32_t f_a, int32_t Mg,
+                               int32_t Kg, int64_t M, int64_t F, int64_t K, int64_t* prod,
+                               hipStream_t st);
+hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, const int32_t* col_m,
+                             int32_t col_k, int32_t frac, int64_t M, int64_t N, int64_t K,
+                             int32_t* h, hipStream_t st);
+hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, const int16_t* gain,
+                                const int8_t* E, const int32_t* emb_m, int32_t w_k, int32_t f_l,
+                                int64_t M, int64_t V, int64_t K, int32_t* logits,
+                                const int32_t* row_base, int64_t* part, hipStream_t st);
 
 }  // namespace detint

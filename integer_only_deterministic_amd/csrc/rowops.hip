@@ -6,6 +6,7 @@
 // matter (DetLLM README, "Why ...": integer sums are associative).
 #include "dev_int.h"
 #include "internal.h"
+#include "qkv_dev.h"
 
 namespace detint {
 namespace {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(TPB) void rmsnorm_k(const int32_t* __restrict__ h,
     return;
   }
   int32_t m, sh;
-  irms(S, n, m, sh);
+  irms_wave(S, n, m, sh);
   const int e = dq_exp((uint64_t)A);
   for (int i = threadIdx.x; i < n; i += TPB) xr[i] = clamp8(R((int64_t)hr[i] * g[i], e));
   if (threadIdx.x == 0) {
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(TPB) void softmax_k(const int32_t* __restrict__ s,
   int64_t D = 0;
   for (int j = threadIdx.x; j < v; j += TPB) D += diexp(R((sr[j] - mx) * Mm, sh));
   D = block_sum(D, red);
-  const int64_t Rn = (int64_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)D);  // D >= 2^15
+  const int64_t Rn = (int64_t)udiv_wave<32>(uint64_t(1) << 46, (uint64_t)D);  // D >= 2^15
   for (int j = threadIdx.x; j < C; j += TPB) {
     int64_t p = 0;
     if (j < v) {
@@ -198,11 +199,7 @@ __global__ void decode_meta_k(const int32_t* __restrict__ ctx, const int32_t* __
 }
 
 // QKV post-processing, one wave per (row, head) - four heads per workgroup,
-// grid (rows, heads / 4); lane i < d/2 owns the RoPE
-// pair (i, i + d/2). q/k: per-head RMSNorm (Qwen3 q/k-norm, before RoPE per
-// DetLLM blog footnote 8) or the f_n fixed point, then RoPE; q -> DQ per
-// head; k, v -> int8 at the fixed cache scales, written once into the cache
-// (DetLLM blog "DetLLM": prefill and decode read the same cached bits).
+// grid (rows, heads / 4); the per-head arithmetic is qkv_head (qkv_dev.h).
 __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qkv, int nq, int nkv,
                                                   int d, const int32_t* __restrict__ pos_of,
                                                   const int32_t* __restrict__ slot_of, QkvPost p,
@@ -210,78 +207,15 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
                                                   int8_t* __restrict__ kc, int8_t* __restrict__ vc,
                                                   int n_slots, int max_pos) {
   const int r = blockIdx.x;
-  const int lane = threadIdx.x & 63;
   const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int half = d >> 1;
   const int nh = nq + 2 * nkv;
+  if (hh >= nh) return;
   const int pos = pos_of[r], slot = slot_of[r];
   const bool ok = pos >= 0 && pos < max_pos && slot >= 0 && slot < n_slots;
-  const bool act = lane < half;
-  const int j0 = lane, j1 = lane + half;
-  const int32_t* row = qkv + (size_t)r * nh * d;
-  if (hh < nh) {
-    const int c0 = hh * d;
-    if (hh >= nq + nkv) {  // V
-      if (!act || !ok) return;
-      const int kvh = hh - nq - nkv;
-      int8_t* dst = vc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int j = t ? j1 : j0;
-        int64_t vf = row[c0 + j];
-        if (p.qk_norm)
-          vf = R(vf * p.row_m[r] * p.col_m[c0 + j], p.row_k[r] + p.col_k - p.f_n);
-        dst[j] = clamp8(R(vf * p.vq_m, p.vq_k));
-      }
-      return;
-    }
-    int64_t x0 = 0, x1 = 0;
-    if (act) {
-      x0 = row[c0 + j0];
-      x1 = row[c0 + j1];
-    }
-    if (p.qk_norm) {
-      const int16_t* gn = hh < nq ? p.q_norm : p.k_norm;
-      int64_t a0 = act ? x0 * p.col_m[c0 + j0] : 0, a1 = act ? x1 * p.col_m[c0 + j1] : 0;
-      const uint64_t u0 = uabs64(a0), u1 = uabs64(a1);
-      const int b = bitlen64(wave_max_u(u0 > u1 ? u0 : u1));
-      const int sh0 = b > 24 ? b - 24 : 0;
-      a0 = R(a0, sh0);
-      a1 = R(a1, sh0);
-      const int64_t S = wave_sum(a0 * a0 + a1 * a1);
-      if (S == 0) {
-        x0 = x1 = 0;
-      } else {
-        int32_t m, sh;
-        irms(S, d, m, sh);
-        if (act) {
-          x0 = R(a0 * gn[j0] * m, sh + 12 - p.f_n);
-          x1 = R(a1 * gn[j1] * m, sh + 12 - p.f_n);
-        }
-      }
-    }
-    int64_t y0 = 0, y1 = 0;
-    if (act && ok) {
-      const int64_t c = p.cos_t[(size_t)pos * half + lane], s = p.sin_t[(size_t)pos * half + lane];
-      y0 = R(x0 * c - x1 * s, 14);
-      y1 = R(x1 * c + x0 * s, 14);
-    }
-    if (hh < nq) {
-      const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
-      const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
-      int8_t* dst = q8 + ((size_t)r * nq + hh) * d;
-      if (act) {
-        dst[j0] = clamp8(R(y0, e));
-        dst[j1] = clamp8(R(y1, e));
-      }
-      if (lane == 0) e_q[(size_t)r * nq + hh] = e;
-    } else if (act && ok) {
-      const int kvh = hh - nq;
-      int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
-      dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k));
-      dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k));
-    }
-  }
+  const int32_t rm = p.qk_norm ? p.row_m[r] : 0, rk = p.qk_norm ? p.row_k[r] : 0;
+  qkv_head(qkv + (size_t)r * nh * d, hh, nq, nkv, d, pos, slot, ok, rm, rk, p,
+           q8 + ((size_t)r * nq + (hh < nq ? hh : 0)) * d, e_q + (size_t)r * nq + (hh < nq ? hh : 0),
+           kc, vc, max_pos);
 }
 
 // Greedy argmax with the lowest index among maxima (DetLLM blog "DetLLM").
@@ -319,6 +253,32 @@ __global__ __launch_bounds__(1024) void argmax_final_k(const int64_t* __restrict
   }
   best = block_max(best, red);
   if (threadIdx.x == 0) out[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFLL));
+}
+
+// Final greedy reduction of the lm_head partials fused with the decode-step
+// advance: next_tok[s]; with advance, ids[s] = next_tok[s], start_pos[s] += 1
+// and the logits history row base moves on by S.
+__global__ __launch_bounds__(1024) void argmax_advance_k(const int64_t* __restrict__ part, int nparts,
+                                                        int32_t* next_tok, int32_t* ids,
+                                                        int32_t* start_pos, int32_t* row_base, int S,
+                                                        int advance) {
+  __shared__ int64_t red[16];
+  const int s = blockIdx.x;
+  int64_t best = INT64_MIN;
+  for (int i = threadIdx.x; i < nparts; i += 1024) {
+    const int64_t k = part[(size_t)s * nparts + i];
+    best = k > best ? k : best;
+  }
+  best = block_max(best, red);
+  if (threadIdx.x == 0) {
+    const int32_t tok = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFLL));
+    next_tok[s] = tok;
+    if (advance) {
+      ids[s] = tok;
+      start_pos[s] += 1;
+      if (s == 0 && row_base) *row_base += S;
+    }
+  }
 }
 
 __global__ void advance_k(int32_t* ids, const int32_t* next_tok, int32_t* start_pos,
@@ -423,6 +383,15 @@ hipError_t launch_argmax_final(const int64_t* part, int64_t S, int64_t nparts, i
                                hipStream_t st) {
   if (S == 0) return hipSuccess;
   argmax_final_k<<<(unsigned)S, 1024, 0, st>>>(part, (int)nparts, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_advance(const int64_t* part, int64_t S, int64_t nparts, int32_t* next_tok,
+                                 int32_t* ids, int32_t* start_pos, int32_t* row_base, bool advance,
+                                 hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  argmax_advance_k<<<(unsigned)S, 1024, 0, st>>>(part, (int)nparts, next_tok, ids, start_pos,
+                                                 row_base, (int)S, advance ? 1 : 0);
   return hipGetLastError();
 }
 
