@@ -71,7 +71,9 @@ const char *detint_last_error(void);
  *   frac   fractional bits of FIX / RES_ADD outputs.
  *   out    [M, N] int32 (RAW, FIX, RES_ADD; read-modify-write for RES_ADD) or
  *          int8 (REQ_I8).
- * Bounds: K <= 131072 (|acc| < 2^31). M, N >= 0; M = 0 or N = 0 is a no-op. */
+ * Bounds: K <= 131072 (|acc| < 2^31); scaled modes |acc * m_r * m_c| < 2^62,
+ * and FIX / RES_ADD results within int32. M, N >= 0; M = 0 or N = 0 is a
+ * no-op. */
 detint_status detint_gemm_i8(const int8_t *A, const int8_t *W, int64_t M, int64_t N, int64_t K,
                              const int32_t *row_m, const int32_t *row_k,
                              const int32_t *col_m, int32_t col_k, int32_t frac,

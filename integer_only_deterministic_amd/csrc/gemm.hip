@@ -5,10 +5,19 @@
 // change a single bit (DetLLM blog, "DetLLM": the int8 matmul is the only
 // hardware-dispatched function and exactness makes it backend-independent).
 //
-//  * gemm_mfma: M > 16. 128x128 output tile per 256-thread workgroup, K in
-//    steps of 64 bytes staged through LDS (double buffered, rows padded to
-//    80 bytes so 16-byte fragment reads spread over the banks); each wave
-//    owns a 64x64 quadrant = 2x2 v_mfma_i32_32x32x32_i8 tiles.
+//  * gemm_pipe: M > 16 and K a multiple of 128. BMxBN output tile (256x256,
+//    128x256 or 128x128, chosen by how many tiles the shape gives) per
+//    256-thread workgroup; each wave owns a (BM/2)x(BN/2) quadrant of
+//    v_mfma_i32_32x32x32_i8 tiles with the accumulators in AGPRs. K advances
+//    128 bytes per tile through an ST-deep LDS ring filled by buffer loads
+//    that write LDS directly (no register staging; rows past M or N read as
+//    zero through the buffer bounds). 16-byte chunks are XOR-swizzled by row
+//    so that both the DMA writes and the MFMA fragment reads are free of
+//    bank conflicts on the 64-bank LDS. MFMA fragments are double-buffered
+//    in registers and the block barrier sits one k-step before the end of a
+//    tile, so the next tile's first fragments load under the last MFMAs.
+//  * gemm_mfma: other M > 16 shapes (K not a multiple of 128). 128x128 tile,
+//    K in steps of 64 bytes staged through registers into padded LDS rows.
 //  * gemv: M <= 16 (decode). Weight streaming: one wave per output column,
 //    16 bytes per lane per step (1 KiB contiguous per wave), v_dot4 on the
 //    activation rows, wave reduction, epilogue by lane 0.
@@ -39,6 +48,33 @@ __device__ __forceinline__ void epi_store(int64_t acc, int64_t i, int64_t j, int
     y = R128((__int128)(acc * e.row_m[i]) * e.col_m[j], s);
   else
     y = R(acc * e.row_m[i] * e.col_m[j], s);
+  if (e.mode == MODE_REQ_I8)
+    ((int8_t*)out)[o] = clamp8(y);
+  else if (e.mode == MODE_FIX)
+    ((int32_t*)out)[o] = (int32_t)y;
+  else
+    ((int32_t*)out)[o] += (int32_t)y;
+}
+
+// epi_store with the row and column scales already loaded and the flat
+// output index o. Without limbs |m_r * m_c| < 2^30, so acc * (m_r * m_c) is
+// one 32 x 32 -> 64-bit product; the value equals acc * m_r * m_c exactly.
+template <bool WIDE>
+__device__ __forceinline__ void epi_put(int64_t acc, int64_t o, int32_t rm, int32_t rk, int32_t cm,
+                                        const Epi& e, void* out) {
+  if (e.mode == MODE_RAW) {
+    if (WIDE)
+      ((int64_t*)out)[o] = acc;
+    else
+      ((int32_t*)out)[o] = (int32_t)acc;
+    return;
+  }
+  const int s = rk + e.col_k - (e.mode == MODE_REQ_I8 ? 0 : e.frac);
+  int64_t y;
+  if (WIDE)
+    y = R128((__int128)(acc * rm) * cm, s);
+  else
+    y = R((int64_t)(int32_t)acc * (int64_t)(rm * cm), s);
   if (e.mode == MODE_REQ_I8)
     ((int8_t*)out)[o] = clamp8(y);
   else if (e.mode == MODE_FIX)
@@ -169,6 +205,336 @@ __global__ __launch_bounds__(256) void gemm_mfma(const int8_t* __restrict__ A,
           epi_store<WIDE>(v, i, j, N, e, out);
         }
       }
+}
+
+// ------------------------------------------------------- pipelined MFMA GEMM
+
+#define DETINT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int PBK = 128;  // K bytes per pipeline tile
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (128-byte rows): two
+// rows share a 256-byte bank window, so 16 consecutive rows must land on 16
+// distinct chunk slots.
+__device__ __forceinline__ int pswz(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// buffer resource over [base, base + bytes): loads past the end return zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int BN, int ST, bool WIDE, int MODE>
+__global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
+                                                 const int8_t* __restrict__ W,
+                                                 const int8_t* __restrict__ Wlo, int M, int N,
+                                                 int K, Epi e, void* out) {
+  constexpr int NB = WIDE ? 2 : 1;             // weight planes
+  constexpr int CPR = PBK / 16;                // chunks per row
+  constexpr int SA = BM * PBK, SB = BN * PBK;  // bytes per stage and operand
+  constexpr int LA = SA / 4096, LB = SB / 4096;  // buffer loads per thread per stage
+  constexpr int LT = LA + NB * LB;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int NS = PBK / 32;                 // MFMA k-steps per tile
+  static_assert(NS % 2 == 0, "fragment double buffer assumes an even step count");
+  extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+  int8_t* sA = smem;
+  int8_t* sB = smem + ST * SA;  // [ST][NB][SB]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Tile order. Workgroups are dealt round-robin to the 8 XCDs: give each XCD
+  // a contiguous run of logical tiles, then sweep groups of 8 tile rows
+  // column by column, so an XCD's L2 holds the A rows and W columns it reuses.
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN, nb = nbm * nbn;
+  int b = blockIdx.x;
+  const int q8 = nb >> 3;
+  if (b < 8 * q8) b = (b & 7) * q8 + (b >> 3);
+  constexpr int G = 8;
+  const int grp = b / (G * nbn), first = grp * G, gm = min(nbm - first, G);
+  const int tm = first + (b % (G * nbn)) % gm, tn = (b % (G * nbn)) / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = K / PBK;
+
+  const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
+  const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
+  const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
+  // stage kt % ST <- tile kt. Load q of thread t moves chunk g = 256q + t of
+  // the stage: LDS bytes [16g, 16g + 16) = row g / 8, physical chunk g % 8.
+  auto issue = [&](int kt) {
+    const int st = kt % ST, k0 = kt * PBK;
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int g = q * 256 + tid, r = g / CPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, DETINT_LDS(sA + st * SA + (q * 256 + wave * 64) * 16), 16,
+          (m0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+#pragma unroll
+      for (int q = 0; q < LB; ++q) {
+        const int g = q * 256 + tid, r = g / CPR;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            p ? rl : rb, DETINT_LDS(sB + (st * NB + p) * SB + (q * 256 + wave * 64) * 16), 16,
+            (n0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
+      }
+  };
+
+  v16i acc[NB][TM][TN];
+#pragma unroll
+  for (int p = 0; p < NB; ++p)
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[p][a][t][r] = 0;
+  int rsum[TM];  // WIDE: partial row sums of A over this lane's fragment bytes
+#pragma unroll
+  for (int a = 0; a < TM; ++a) rsum[a] = 0;
+
+  v4i fa[2][TM], fb[2][NB][TN];
+  auto frag = [&](int kt, int s, int buf) {
+    const int8_t* a_s = sA + (kt % ST) * SA;
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int r = wm * WM + a * 32 + (lane & 31);
+      fa[buf][a] = *(const v4i*)(a_s + r * PBK + (pswz(c, r) << 4));
+    }
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * WN + t * 32 + (lane & 31);
+        fb[buf][p][t] = *(const v4i*)(sB + ((kt % ST) * NB + p) * SB + r * PBK + (pswz(c, r) << 4));
+      }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          acc[p][a][t] =
+              __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][a], fb[buf][p][t], acc[p][a][t], 0, 0, 0);
+    if (WIDE) {
+      const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+      for (int a = 0; a < TM; ++a) rsum[a] = dot16(fa[buf][a], ones, rsum[a]);
+    }
+  };
+
+  // every stage in flight, then wait for tile 0
+#pragma unroll
+  for (int s = 0; s < ST; ++s)
+    if (s < nk) issue(s);
+  if (ST - 1 < nk)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST - 1) * LT) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  frag(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < NS) {
+        frag(kt, s + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (kt + 1 < nk) {
+        // Tile kt+1 resident (own loads counted, others' by the barrier) and
+        // every wave's reads of tile kt issued and complete, so its stage can
+        // be refilled with tile kt+ST.
+        if (ST > 2 && kt + ST - 1 < nk)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((ST > 2 ? ST - 2 : 0) * LT) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + ST < nk) issue(kt + ST);
+        frag(kt + 1, 0, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mma(buf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue straight from the accumulators (fully unrolled so they stay
+  // statically indexed). Loads use clamped indices and are unconditional, so
+  // each tile's are issued together; only the stores are guarded. Accumulator
+  // layout of a 32x32 tile: lane l, register r -> row 8 * (r / 4) + 4 * (l / 32)
+  // + r % 4, column l % 32.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave done with the LDS ring
+  int32_t* srow = (int32_t*)smem;  // WIDE: row sums of the tile's A rows
+  int32_t* s_rm = srow + BM;       // row scales of the tile's rows
+  int32_t* s_rk = s_rm + BM;
+  if (WIDE && wn == 0) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int v = rsum[a] + __shfl_xor(rsum[a], 32);
+      if (lane < 32) srow[wm * WM + a * 32 + lane] = v;
+    }
+  }
+  // s_rk holds each row's total shift. The fast path needs every scale in
+  // [0, 2^15) and every shift in [1, 62] (int8 weights) or [32, 94] (limbs);
+  // anything else takes the general per-element path below.
+  const int csh = e.col_k - (MODE == MODE_REQ_I8 ? 0 : e.frac);
+  int slow = 0;
+  if (MODE != MODE_RAW) {
+    for (int t = tid; t < BM; t += 256) {
+      const int i = min(m0 + t, M - 1);
+      const int rm = e.row_m[i], sh = e.row_k[i] + csh;
+      s_rm[t] = rm;
+      s_rk[t] = sh;
+      slow |= (unsigned)rm >= 32768u || (WIDE ? sh < 32 || sh > 94 : sh < 1 || sh > 62);
+    }
+    for (int t = tid; t < BN; t += 256) slow |= (unsigned)e.col_m[min(n0 + t, N - 1)] >= 32768u;
+  }
+  const int64_t obase = e.out_row_base ? *e.out_row_base : 0;
+  slow = __syncthreads_or(slow);
+  if (MODE != MODE_RAW && !slow && m0 + BM <= M && n0 + BN <= N) {
+    // Interior tile, in-range scales: no bounds checks, branch-free rounding.
+    // int8 weights: |m_r * m_c| < 2^30, so acc * m_r * m_c is one 32 x 32 ->
+    // 64-bit product. Limbs: t = v * m_r fits int64; with t = th * 2^32 + tl
+    // (0 <= tl < 2^32) and the rounding term 2^(s-1) = ch * 2^32 + cl,
+    // R(t * m_c, s) = (th * m_c + ch + ((tl * m_c + cl) >> 32)) >> (s - 32)
+    // exactly, for 32 <= s <= 94.
+#pragma clang loop unroll(full)
+    for (int a = 0; a < TM; ++a)
+#pragma clang loop unroll(full)
+      for (int t = 0; t < TN; ++t) {
+        const int j = n0 + wn * WN + t * 32 + (lane & 31);
+        const int32_t cm = e.col_m[j];
+        const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
+        int32_t old[16];
+        if (MODE == MODE_RES_ADD) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            old[r] = ((const int32_t*)out)[(m0 + lb + 8 * (r >> 2) + (r & 3) + obase) * N + j];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int li = lb + 8 * (r >> 2) + (r & 3);
+          const int64_t o = (m0 + li + obase) * N + j;
+          const int sh = s_rk[li];
+          int64_t y;
+          if (WIDE) {
+            const int64_t v = 256 * (int64_t)acc[0][a][t][r] + (int64_t)acc[NB - 1][a][t][r] +
+                              128 * (int64_t)srow[li];
+            const int64_t tt = v * s_rm[li];
+            const int64_t th = tt >> 32;
+            const uint64_t tl = (uint32_t)tt;
+            const int64_t ch = sh >= 33 ? int64_t(1) << (sh - 33) : 0;
+            const uint64_t cl = sh == 32 ? uint64_t(1) << 31 : 0;
+            const uint64_t lo = tl * (uint64_t)(uint32_t)cm + cl;
+            y = (th * cm + ch + (int64_t)(lo >> 32)) >> (sh - 32);
+          } else {
+            const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)__mul24(s_rm[li], cm);
+            y = (pr + (int64_t(1) << (sh - 1))) >> sh;
+          }
+          if (MODE == MODE_REQ_I8)
+            ((int8_t*)out)[o] = clamp8(y);
+          else if (MODE == MODE_FIX)
+            ((int32_t*)out)[o] = (int32_t)y;
+          else
+            ((int32_t*)out)[o] = old[r] + (int32_t)y;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    return;
+  }
+#pragma clang loop unroll(full)
+  for (int a = 0; a < TM; ++a)
+#pragma clang loop unroll(full)
+    for (int t = 0; t < TN; ++t) {
+      const int j = n0 + wn * WN + t * 32 + (lane & 31), jc = min(j, N - 1);
+      const int32_t cm = MODE != MODE_RAW ? e.col_m[jc] : 0;
+      const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
+      int32_t old[16];
+      if (MODE == MODE_RES_ADD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = min(m0 + lb + 8 * (r >> 2) + (r & 3), M - 1);
+          old[r] = ((const int32_t*)out)[(i + obase) * N + jc];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int li = lb + 8 * (r >> 2) + (r & 3), i = m0 + li;
+        int64_t v = acc[0][a][t][r];
+        if (WIDE) v = 256 * v + (int64_t)acc[NB - 1][a][t][r] + 128 * (int64_t)srow[li];
+        const int64_t o = (i + obase) * N + j;
+        if (MODE == MODE_RAW) {
+          if (i < M && j < N) {
+            if (WIDE)
+              ((int64_t*)out)[o] = v;
+            else
+              ((int32_t*)out)[o] = (int32_t)v;
+          }
+          continue;
+        }
+        const int sh = s_rk[li];
+        const int64_t y = WIDE ? R128((__int128)(v * s_rm[li]) * cm, sh)
+                               : R((int64_t)(int32_t)v * s_rm[li] * cm, sh);
+        if (i < M && j < N) {
+          if (MODE == MODE_REQ_I8)
+            ((int8_t*)out)[o] = clamp8(y);
+          else if (MODE == MODE_FIX)
+            ((int32_t*)out)[o] = (int32_t)y;
+          else
+            ((int32_t*)out)[o] = old[r] + (int32_t)y;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep tiles' live ranges apart
+    }
+}
+
+template <int BM, int BN, int ST, bool WIDE, int MODE>
+hipError_t pipe_launch_m(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
+                         const Epi& e, void* out, hipStream_t st) {
+  constexpr int lds = ST * (BM + (WIDE ? 2 : 1) * BN) * PBK;
+  static_assert(lds <= 160 * 1024, "LDS ring exceeds the workgroup limit");
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t err = hipFuncSetAttribute((const void*)gemm_pipe<BM, BN, ST, WIDE, MODE>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr = true;
+  }
+  const int nb = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  gemm_pipe<BM, BN, ST, WIDE, MODE><<<nb, 256, lds, st>>>(A, W, Wlo, M, N, K, e, out);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int ST, bool WIDE>
+hipError_t pipe_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
+                       const Epi& e, void* out, hipStream_t st) {
+  switch (e.mode) {
+    case MODE_RAW: return pipe_launch_m<BM, BN, ST, WIDE, MODE_RAW>(A, W, Wlo, M, N, K, e, out, st);
+    case MODE_REQ_I8: return pipe_launch_m<BM, BN, ST, WIDE, MODE_REQ_I8>(A, W, Wlo, M, N, K, e, out, st);
+    case MODE_FIX: return pipe_launch_m<BM, BN, ST, WIDE, MODE_FIX>(A, W, Wlo, M, N, K, e, out, st);
+    default: return pipe_launch_m<BM, BN, ST, WIDE, MODE_RES_ADD>(A, W, Wlo, M, N, K, e, out, st);
+  }
+}
+
+// Largest tile that still gives the chip most of a wave of workgroups.
+template <bool WIDE>
+hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N,
+                         int K, const Epi& e, void* out, hipStream_t st) {
+  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  constexpr int64_t FILL = 192;  // 3/4 of the 256 CUs
+  if (WIDE) {
+    if (tiles(256, 128) >= FILL) return pipe_launch<256, 128, 2, true>(A, W, Wlo, M, N, K, e, out, st);
+    return pipe_launch<128, 128, 3, true>(A, W, Wlo, M, N, K, e, out, st);
+  }
+  if (tiles(256, 256) >= FILL) return pipe_launch<256, 256, 2, false>(A, W, Wlo, M, N, K, e, out, st);
+  if (tiles(128, 256) >= FILL) return pipe_launch<128, 256, 3, false>(A, W, Wlo, M, N, K, e, out, st);
+  return pipe_launch<128, 128, 4, false>(A, W, Wlo, M, N, K, e, out, st);
 }
 
 // ---------------------------------------------------------------- GEMV
@@ -314,6 +680,11 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
+  // buffer offsets are 32-bit
+  if (K % PBK == 0 && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31)) {
+    if (W_lo) return pipe_dispatch<true>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+    return pipe_dispatch<false>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+  }
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   if (W_lo)
     gemm_mfma<true><<<grid, 256, 0, st>>>(A, W, W_lo, (int)M, (int)N, (int)K, e, out);

@@ -55,8 +55,12 @@ def test_gemm_sweep(D, K, N):
         del A, W
 
 
+# K % 128 == 0 shapes take the pipelined kernel; the last three are sized so
+# that its 128x128, 128x256 and 256x256 tilings are each chosen, with ragged
+# M and N edges.
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 77, 32), (17, 130, 64),
-                                   (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072)])
+                                   (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072),
+                                   (200, 300, 256), (1000, 6100, 256), (2000, 6000, 128)])
 def test_gemm_ragged_all_modes(D, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
@@ -79,6 +83,36 @@ def test_gemm_ragged_all_modes(D, M, N, K):
     np.testing.assert_array_equal(host(out), O.epilogue(acc, rm, rk, cm, 22, 8, O.RES_ADD, out=base))
 
 
+@pytest.mark.parametrize("mode", ["REQ_I8", "FIX", "RES_ADD"])
+def test_gemm_general_scales(D, mode):
+    """All-interior 128x128 tiling with mantissas >= 2^15 and (for REQ_I8)
+    shifts from -3 to 70: the kernel's general epilogue, not its in-range
+    fast path."""
+    M, N, K = 512, 512, 256
+    rng = np.random.default_rng(99)
+    A = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    W = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    rm = rng.integers(1 << 14, 1 << 15, M).astype(np.int32)
+    rm[::7] = rng.integers(1 << 15, 1 << 20, len(rm[::7]))
+    cm = rng.integers(1 << 14, 1 << 15, N).astype(np.int32)
+    if mode == "REQ_I8":
+        rk = rng.integers(-25, 49, M).astype(np.int32)          # shift = rk + 22
+    else:
+        rk = rng.integers(40, 49, M).astype(np.int32)           # FIX/RES results stay in int32
+    acc = O.gemm(A, W)
+    dA, dW, drm, drk, dcm = dev(A), dev(W), dev(rm), dev(rk), dev(cm)
+    md = getattr(D, mode)
+    if mode == "RES_ADD":
+        base = rng.integers(-(1 << 20), 1 << 20, (M, N)).astype(np.int32)
+        out = dev(base)
+        D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, md, out=out)
+        want = O.epilogue(acc, rm, rk, cm, 22, 8, O.RES_ADD, out=base)
+        np.testing.assert_array_equal(host(out), want)
+    else:
+        got = host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, md))
+        np.testing.assert_array_equal(got, O.epilogue(acc, rm, rk, cm, 22, 8, getattr(O, mode)))
+
+
 def test_gemm_empty(D):
     import torch
     A = torch.zeros((0, 32), dtype=torch.int8, device="cuda")
@@ -86,8 +120,10 @@ def test_gemm_empty(D):
     assert D.detint_gemm_i8(A, W).shape == (0, 5)
 
 
+# (33, 130, 512) and (300, 200, 1024) take the pipelined kernel's 128x128
+# limb tiling, (1000, 6100, 128) its 256x128 one.
 @pytest.mark.parametrize("M,N,K", [(1, 100, 2048), (7, 300, 256), (16, 64, 8192), (33, 130, 512),
-                                   (300, 200, 1024)])
+                                   (300, 200, 1024), (1000, 6100, 128)])
 def test_gemm_w16_limbs(D, M, N, K):
     rng = np.random.default_rng(M + N + K)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
