@@ -16,6 +16,8 @@
 //    bank conflicts on the 64-bank LDS. MFMA fragments are double-buffered
 //    in registers and the block barrier sits one k-step before the end of a
 //    tile, so the next tile's first fragments load under the last MFMAs.
+//  * gemm_skinny: 16 < M <= 64 (32 with limbs), K a multiple of 512: weight
+//    streaming with MFMA; see the kernel.
 //  * gemm_mfma: other M > 16 shapes (K not a multiple of 128). 128x128 tile,
 //    K in steps of 64 bytes staged through registers into padded LDS rows.
 //  * gemv: M <= 16 (decode). Weight streaming: one wave per output column,
@@ -537,6 +539,142 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
   return pipe_launch<128, 128, 4, false>(A, W, Wlo, M, N, K, e, out, st);
 }
 
+// ------------------------------------------------------------- skinny GEMM
+
+// M <= 64 rows (batched decode, short prompts): weight streaming. A
+// 1024-thread workgroup owns 32 output columns for all rows; its 16 waves
+// split K into 16 chunks, each streaming its chunk of the weight rows from
+// HBM straight into MFMA fragments (buffer loads, two k-steps in flight per
+// wave) against A fragments that stay L2-resident. Per-wave partial sums
+// meet in LDS; integer sums are order-free, so the split changes no bit.
+// Limb planes are reduced separately in int32 (|sum| <= 2^14 K < 2^31) and
+// combined in int64 at the end.
+constexpr int SK_W = 16;   // waves per workgroup = K chunks
+constexpr int SK_G = 2;    // k-steps per load group
+
+template <bool WIDE, int MR>
+__global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A,
+                                                    const int8_t* __restrict__ W,
+                                                    const int8_t* __restrict__ Wlo, int M, int N,
+                                                    int K, Epi e, void* out) {
+  constexpr int NB = WIDE ? 2 : 1;
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  int32_t* part = (int32_t*)smem;                   // [SK_W][NB][MR][32 * 32]
+  int32_t* prs = part + SK_W * NB * MR * 1024;       // [SK_W][MR * 32] row sums
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 32;
+  const int kc = K / SK_W, nst = kc / 32;
+  const int kb = wave * kc + (lane >> 5) * 16;
+  const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
+  const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
+  const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
+  const int aoff = (lane & 31) * K + kb, woff = (n0 + (lane & 31)) * K + kb;
+
+  v16i acc[NB][MR];
+#pragma unroll
+  for (int p = 0; p < NB; ++p)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[p][m][r] = 0;
+  int rsum[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) rsum[m] = 0;
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+  v4i fa[2][SK_G][MR], fw[2][SK_G][NB];
+  auto load = [&](int g, int buf) {
+#pragma unroll
+    for (int s = 0; s < SK_G; ++s) {
+      const int k = (g * SK_G + s) * 32;
+      if (g * SK_G + s < nst) {
+#pragma unroll
+        for (int p = 0; p < NB; ++p)
+          fw[buf][s][p] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(p ? rl : rb, woff + k, 0, 0));
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+          fa[buf][s][m] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + m * 32 * K + k, 0, 0));
+      }
+    }
+  };
+  const int ng = (nst + SK_G - 1) / SK_G;
+  auto group = [&](int g, int buf) {  // buf is a constant at each call
+    if (g + 1 < ng) load(g + 1, buf ^ 1);
+#pragma unroll
+    for (int s = 0; s < SK_G; ++s) {
+      if (g * SK_G + s < nst) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+#pragma unroll
+          for (int p = 0; p < NB; ++p)
+            acc[p][m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][s][m], fw[buf][s][p],
+                                                              acc[p][m], 0, 0, 0);
+          if (WIDE) rsum[m] = dot16(fa[buf][s][m], ones, rsum[m]);
+        }
+      }
+    }
+  };
+  load(0, 0);
+  for (int g = 0; g < ng; g += 2) {
+    group(g, 0);
+    if (g + 1 < ng) group(g + 1, 1);
+  }
+  // partials to LDS (accumulator layout: lane l, register r -> row
+  // 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32)
+#pragma unroll
+  for (int p = 0; p < NB; ++p)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        part[((wave * NB + p) * MR + m) * 1024 + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 +
+             (lane & 31)] = acc[p][m][r];
+  if (WIDE) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int v = rsum[m] + __shfl_xor(rsum[m], 32);
+      if (lane < 32) prs[wave * MR * 32 + m * 32 + lane] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int row = m * 32 + (tid >> 5), i = row, j = n0 + (tid & 31);
+    int32_t hi = 0, lo = 0, rs = 0;
+#pragma unroll
+    for (int w = 0; w < SK_W; ++w) {
+      hi += part[((w * NB + 0) * MR + m) * 1024 + tid];
+      if (WIDE) {
+        lo += part[((w * NB + NB - 1) * MR + m) * 1024 + tid];
+        rs += prs[w * MR * 32 + row];
+      }
+    }
+    if (i < M && j < N) {
+      int64_t v = hi;
+      if (WIDE) v = 256 * v + (int64_t)lo + 128 * (int64_t)rs;
+      epi_store<WIDE>(v, i, j, N, e, out);
+    }
+  }
+}
+
+template <bool WIDE, int MR>
+hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
+                         const Epi& e, void* out, hipStream_t st) {
+  constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
+  static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t err = hipFuncSetAttribute((const void*)gemm_skinny<WIDE, MR>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr = true;
+  }
+  gemm_skinny<WIDE, MR><<<(N + 31) / 32, 1024, lds, st>>>(A, W, Wlo, M, N, K, e, out);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- GEMV
 
 // Key of a logit for the greedy argmax: larger value first, then the lower
@@ -681,7 +819,13 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
   if (M == 0 || N == 0) return hipSuccess;
   if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
   // buffer offsets are 32-bit
-  if (K % PBK == 0 && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31)) {
+  const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
+  if (off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !W_lo))) {
+    if (W_lo) return skinny_launch<true, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+    if (M <= 32) return skinny_launch<false, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+    return skinny_launch<false, 2>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+  }
+  if (K % PBK == 0 && off32) {
     if (W_lo) return pipe_dispatch<true>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
     return pipe_dispatch<false>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
   }
