@@ -182,8 +182,9 @@ detint_status detint_attn_prefill(const int8_t* q8, const int32_t* e_q, const in
   if (s != DETINT_OK) return s;
   REQUIRE(n_slots > 0, "attn_prefill: n_slots must be positive");
   RowMap rows{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
-  return hip_status(launch_attention(q8, e_q, k_cache, v_cache, rows, R, n_q, n_kv, d, n_slots,
-                                     max_pos, mult_m, mult_k, out, S_(stream)),
+  // R bounds the longest sequence
+  return hip_status(launch_attention_seqs(q8, e_q, k_cache, v_cache, rows, R, R, n_q, n_kv, d,
+                                          n_slots, max_pos, mult_m, mult_k, out, S_(stream)),
                     "attn_prefill launch");
 }
 
@@ -406,8 +407,8 @@ int64_t detint_workspace_size(const detint_model* m, int64_t max_rows, int64_t m
 
 // One decoder layer in place on h [R, H] (workspace buffers from w).
 static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int8_t* k_cache,
-                               int8_t* v_cache, int64_t n_slots, int64_t R, char* base,
-                               const WsLayout& w, hipStream_t st) {
+                               int8_t* v_cache, int64_t n_slots, int64_t R, const RowMap& seqs,
+                               int64_t max_seqlen, char* base, const WsLayout& w, hipStream_t st) {
   const detint_model_desc& d = m->d;
   const detint_layer_desc& L = m->layers[l];
   int32_t* pos_of = (int32_t*)(base + w.pos_of);
@@ -426,7 +427,6 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   const int32_t wk = d.w_k;
   int8_t* kc = k_cache + l * layer_stride;
   int8_t* vc = v_cache + l * layer_stride;
-  const RowMap rows{nullptr, nullptr, nullptr, 0, pos_of, 0, slot_of};
   hipError_t e;
 #define LAUNCH(x)                                  \
   do {                                             \
@@ -444,8 +444,8 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
              L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
   LAUNCH(launch_qkv_post(qkv, R, nq, nkv, hd, pos_of, slot_of, qp, q8, eq, kc, vc, n_slots,
                          d.max_pos, st));
-  LAUNCH(launch_attention(q8, eq, kc, vc, rows, R, nq, nkv, hd, n_slots, d.max_pos, m->sm_m[l],
-                          m->sm_k[l], att, st));
+  LAUNCH(launch_attention_seqs(q8, eq, kc, vc, seqs, R, max_seqlen, nq, nkv, hd, n_slots,
+                               d.max_pos, m->sm_m[l], m->sm_k[l], att, st));
   LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
   {
     Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr};
@@ -551,7 +551,8 @@ detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t
   hipError_t e = launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
                                   (int32_t*)(base + w.slot_of), (int32_t*)(base + w.last_row), st);
   if (e != hipSuccess) return hip_status(e, "rows_meta");
-  return run_layer(m, layer, h, k_cache, v_cache, n_slots, R, base, w, st);
+  const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
+  return run_layer(m, layer, h, k_cache, v_cache, n_slots, R, seqs, max_seqlen, base, w, st);
 }
 
 detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
@@ -596,8 +597,9 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
                           (int32_t*)(base + w.slot_of), last_row, st));
   LAUNCH(launch_embed(ids, R, d.emb, d.wide ? d.emb_lo : nullptr, d.emb_m, d.hidden, d.vocab,
                       d.w_k - d.f_res, h, st));
+  const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
   for (int64_t l = 0; l < d.n_layers; ++l) {
-    s = run_layer(m, l, h, k_cache, v_cache, n_slots, R, base, w, st);
+    s = run_layer(m, l, h, k_cache, v_cache, n_slots, R, seqs, max_seqlen, base, w, st);
     if (s != DETINT_OK) return s;
   }
   // final norm on each sequence's last row, tied lm_head, greedy token

@@ -22,6 +22,8 @@
 namespace detint {
 namespace {
 
+#define DETINT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 constexpr int TPB = 256;
 
 __device__ __forceinline__ int sbyte(int w, int b) { return (w << (24 - 8 * b)) >> 24; }
@@ -250,6 +252,322 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
                           sred);
 }
 
+// ------------------------------------------------------ prefill on MFMA
+//
+// Prefill rows of a sequence are consecutive positions, so a workgroup takes
+// a block of QP query positions of one sequence and the G query heads of one
+// KV head, and walks the causal key range in chunks of 32 keys three times:
+//   1. S^T = K . Q^T (v_mfma_i32_32x32x32_i8, exact int32): row maxima;
+//   2. recompute S^T; E = DI-Exp(...) as above; D = sum E;
+//   3. recompute S^T and E; P = min(R(E floor(2^46 / D), 31), 2^15 - 1);
+//      O^T += V^T . P^T on MFMA with P split into int8 limbs:
+//      P = 256 Ph + Pl + 128, Ph in [0, 127], Pl in [-128, 127]
+//      (DetLLM blog, footnote 8: 15-bit probabilities, P.V as two int8
+//      GEMMs), so O = 256 (Ph.V) + (Pl.V) + 128 colsum(V).
+// Computing S^T rather than S leaves each lane with 16 keys of one query in
+// its accumulator registers (lane l: query l % 32; register r: key
+// 8 (r / 4) + 4 (l / 32) + r % 4), which is exactly a 16-byte MFMA operand of
+// P^T once the contraction runs over keys in that order; V^T is staged in
+// LDS with its keys permuted the same way. Row statistics become per-lane
+// values plus one exchange between the two half-waves. Masked keys (past the
+// query's position, or past the chunk's end) get P = 0, i.e. Ph = 0,
+// Pl = -128, which the colsum term cancels exactly.
+template <int G>
+struct PfCfg {
+  static constexpr int PT = 4 / G;       // 32-position tiles per workgroup
+  static constexpr int QP = 32 * PT;     // query positions per workgroup
+};
+
+// position k' = 16 h + b of key 8 (b / 4) + 4 h + b % 4 in the P.V contraction
+__device__ __forceinline__ int key_slot(int key) {
+  return 16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3);
+}
+
+// E = DI-Exp(R((s - mx) M, sh)) for s <= mx, written for x = (mx - s) M >= 0:
+// R(-x, sh) = -((x + 2^(sh-1) - 1) >> sh) for sh >= 1, so DI-Exp's
+// magnitude is v = (x + 2^(sh-1) - 1) >> sh and E = R(2^15 - R(v mod 2^15, 1),
+// v >> 15), zero once v >> 15 > 30. Needs 1 <= sh <= 62 and M > 0; other
+// rows take diexp(R(...)) as written.
+__device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh) {
+  const uint64_t x = (uint64_t)delta * M;
+  const uint64_t v = (x + (uint64_t(1) << (sh - 1)) - 1) >> sh;
+  const uint32_t vv = (uint32_t)v, n = min(vv >> 15, 31u);
+  const uint32_t f = 32768u - (((vv & 32767u) + 1u) >> 1);
+  return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
+}
+
+template <int D, int G>
+struct PfLds {
+  static constexpr int BK = 256;           // keys per staged batch (8 chunks)
+  static constexpr int KB = BK * D;        // bytes of K (or V) per batch
+  static constexpr int VST = 48;           // V^T row stride (bytes; 16-byte aligned)
+  static constexpr int bytes = 4 * KB + 2 * D * VST + D * 4;
+};
+
+// K rows in LDS: 16-byte chunk c of key row r sits at chunk c ^ swz(r), so the
+// 16 rows one MFMA operand read touches per LDS cycle hit 16 distinct slots
+// of the 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_prefill_mfma(
+    const int8_t* __restrict__ q8, const int32_t* __restrict__ e_q, const int8_t* __restrict__ kc,
+    const int8_t* __restrict__ vc, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
+    const int32_t* __restrict__ seq_slot, int nq, int nkv, int n_slots, int max_pos, int nblk,
+    int32_t Ms, int32_t Ks, int32_t* __restrict__ out) {
+  constexpr int QP = PfCfg<G>::QP, KS = D / 32, CPR = D / 16;
+  using L = PfLds<D, G>;
+  constexpr int BK = L::BK, KB = L::KB, VST = L::VST;
+  constexpr int LPB = KB / 4096;  // DMA loads per thread per batch and operand
+  extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+  int8_t* sK = smem;                 // [2][KB]
+  int8_t* sV = smem + 2 * KB;        // [2][KB]
+  int8_t* vt = smem + 4 * KB;        // [2][D * VST]
+  int32_t* s_cs = (int32_t*)(vt + 2 * D * VST);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ql = lane & 31;
+  const int qb = nblk - 1 - (int)blockIdx.x, sq = blockIdx.y, kvh = blockIdx.z;
+  const int r0 = cu[sq], len = cu[sq + 1] - r0;
+  if (qb * QP >= len) return;
+  const int p0 = start[sq], slot = seq_slot[sq];
+  const int nrow = min(QP, len - qb * QP);
+  const int hq = kvh * G + wave % G, qi = (wave / G) * 32 + ql;
+  const int row = r0 + qb * QP + qi, pos = p0 + qb * QP + qi;
+  const bool rvalid = qi < nrow;
+  int32_t* orow = out + ((size_t)row * nq + hq) * D;
+  if (slot < 0 || slot >= n_slots) {
+    if (rvalid)
+      for (int d = hh; d < D; d += 2) orow[d] = 0;  // lanes l and l + 32 split the row
+    return;
+  }
+  const bool live = rvalid && pos >= 0 && pos < max_pos;
+  const int kend = min(p0 + qb * QP + nrow, max_pos);
+  const int nch = (kend + 31) >> 5, nbt = (kend + BK - 1) / BK;
+  const size_t base = ((size_t)slot * nkv + kvh) * max_pos * D;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0,
+                                                                      max_pos * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0,
+                                                                      max_pos * D, 0x00020000);
+  // batch bt of K (swizzled) and, for pass 3, V (natural) into buffer bt & 1:
+  // load q of thread t moves chunk g = 256 q + t, LDS bytes [16 g, 16 g + 16)
+  auto issue = [&](int bt, bool withv) {
+    const int buf = bt & 1;
+#pragma unroll
+    for (int q = 0; q < LPB; ++q) {
+      const int g = q * 256 + tid, r = g / CPR, ph = g % CPR;
+      const int goff = (bt * BK + r) * D;
+      // a template call written straight into the builtin's argument list
+      // leaves the kernel uninstantiated on the host side (no host stub)
+      const int koff = goff + ((ph ^ kswz<D>(r)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, DETINT_LDS(sK + buf * KB + (q * 256 + wave * 64) * 16),
+                                               16, koff, 0, 0, 0);
+      if (withv)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, DETINT_LDS(sV + buf * KB + (q * 256 + wave * 64) * 16),
+                                                 16, goff + (ph << 4), 0, 0, 0);
+    }
+  };
+
+  v4i qf[KS];
+  const v4i z4 = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = rvalid ? *(const v4i*)(q8 + ((size_t)row * nq + hq) * D + 32 * ks + 16 * hh) : z4;
+  const int sh = Ks - (rvalid ? e_q[(size_t)row * nq + hq] : 0);
+  const bool fast = sh >= 1 && sh <= 62 && Ms > 0;
+  const bool wfast = __all(fast);  // every lane of the wave on the fast form
+  // chunks below every query of this wave's tile need no causal mask
+  const int pmin = p0 + qb * QP + (wave / G) * 32;
+
+  // S^T of chunk c (keys 32 c ..) from the staged batch
+  auto scores = [&](int c) {
+    const int8_t* kb = sK + ((c / (BK / 32)) & 1) * KB;
+    const int r = (c * 32) % BK + ql;
+    v16i acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const v4i kf = *(const v4i*)(kb + r * D + (((2 * ks + hh) ^ kswz<D>(r)) << 4));
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ks], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  auto key_of = [&](int c, int r) { return c * 32 + 8 * (r >> 2) + 4 * hh + (r & 3); };
+  // Each pass walks the chunks with batches staged one ahead: at a batch's
+  // start, wait for it, then a barrier (which also retires every wave's
+  // reads of the buffer the next issue overwrites), then issue the next.
+  auto batch_begin = [&](int bt, bool withv) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (bt + 1 < nbt) issue(bt + 1, withv);
+  };
+  auto sweep_end = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  constexpr int CPB = BK / 32;  // chunks per batch
+
+  // pass 1: maxima
+  int mx = INT32_MIN;
+  issue(0, false);
+  for (int bt = 0; bt < nbt; ++bt) {
+    batch_begin(bt, false);
+    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
+      const v16i sacc = scores(c);
+      if (c * 32 + 31 <= pmin) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = max(mx, sacc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key_of(c, r) <= pos) mx = max(mx, sacc[r]);
+      }
+    }
+  }
+  sweep_end();
+  mx = max(mx, __shfl_xor(mx, 32));
+  if (!live) mx = 0;  // its values are never used; keep the arithmetic tame
+
+  // pass 2: sum of exponentials
+  int64_t den = 0;
+  issue(0, false);
+  for (int bt = 0; bt < nbt; ++bt) {
+    batch_begin(bt, false);
+    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
+      const v16i sacc = scores(c);
+      const int lim = pos - c * 32;  // key offsets <= lim are causal
+      int32_t part = 0;              // 16 terms of at most 2^15
+      if (wfast) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t E = exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh);
+          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t E = fast ? exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh)
+                                 : diexp(R(((int64_t)sacc[r] - mx) * Ms, sh));
+          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
+        }
+      }
+      den += part;
+    }
+  }
+  sweep_end();
+  den += __shfl_xor(den, 32);
+  if (!live) den = 0;
+  const int64_t rn = den > 0 ? (int64_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den) : 0;  // D >= 2^15
+
+  // pass 3: probabilities and P.V
+  v16i oh[KS], ol[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oh[t][r] = ol[t][r] = 0;
+  int cs = 0;  // thread d < D: colsum of V over the staged keys
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  // V^T of a chunk: thread t moves D/8 bytes of key t/8 (keys permuted)
+  const int vj = tid >> 3, vd = (tid & 7) * (D / 8), vslot = key_slot(vj);
+  issue(0, true);
+  for (int bt = 0; bt < nbt; ++bt) {
+   batch_begin(bt, true);
+   for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
+    int8_t* vb = vt + (c & 1) * D * VST;
+    {
+      const int8_t* src = sV + ((c / (BK / 32)) & 1) * KB + ((c * 32) % BK + vj) * D + vd;
+      uint32_t w[D / 32];
+      if constexpr (D == 64) {
+        const uint2 x = *(const uint2*)src;
+        w[0] = x.x;
+        w[1] = x.y;
+      } else {
+        const v4i x = *(const v4i*)src;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)x[i];
+      }
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) vb[(vd + i) * VST + vslot] = (int8_t)(w[i >> 2] >> (8 * (i & 3)));
+    }
+    __syncthreads();  // V^T of chunk c staged; the other V^T buffer is free
+    if (tid < D) {
+      cs = dot16(*(const v4i*)(vb + tid * VST), ones, cs);
+      cs = dot16(*(const v4i*)(vb + tid * VST + 16), ones, cs);
+    }
+    const v16i sacc = scores(c);
+    const int lim = live ? pos - c * 32 : -1;  // key offsets <= lim get P > 0
+    // P limbs, byte r of the fragment = register r. P = R(E rn, 31) capped
+    // at 2^15 - 1; E rn < 2^47.
+    uint32_t ph[4] = {0, 0, 0, 0}, pl[4] = {0, 0, 0, 0};
+    auto put = [&](int r, int32_t E) {
+      const uint32_t pp = (uint32_t)(((uint64_t)(uint32_t)E * (uint64_t)rn + (uint64_t(1) << 30)) >> 31);
+      uint32_t P = pp > 32767u ? 32767u : pp;
+      P = (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? P : 0u;
+      ph[r >> 2] |= (P >> 8) << (8 * (r & 3));
+      pl[r >> 2] |= ((P & 255u) ^ 128u) << (8 * (r & 3));  // (P & 255) - 128 as a byte
+    };
+    if (wfast) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put(r, exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        put(r, fast ? exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh)
+                    : diexp(R(((int64_t)sacc[r] - mx) * Ms, sh)));
+    }
+    const v4i fph = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3]};
+    const v4i fpl = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const v4i fv = *(const v4i*)(vb + (32 * t + ql) * VST + 16 * hh);
+      oh[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fph, oh[t], 0, 0, 0);
+      ol[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fpl, ol[t], 0, 0, 0);
+    }
+   }
+  }
+  sweep_end();
+  if (tid < D) s_cs[tid] = cs;
+  __syncthreads();
+  if (!rvalid) return;
+  // O^T layout: lane l holds query l % 32; register r of d-tile t is
+  // d = 32 t + 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * t + 8 * r4 + 4 * hh;
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * r4 + i;
+        o[i] = live ? (int)(256 * (int64_t)oh[t][r] + ol[t][r] + 128 * (int64_t)s_cs[d0 + i]) : 0;
+      }
+      *(v4i*)(orow + d0) = o;
+    }
+}
+
+template <int D, int G>
+hipError_t launch_pf(const int8_t* q8, const int32_t* e_q, const int8_t* kc, const int8_t* vc,
+                     const RowMap& seqs, int64_t max_seqlen, int64_t nq, int64_t nkv,
+                     int64_t n_slots, int64_t max_pos, int32_t M, int32_t K, int32_t* out,
+                     hipStream_t st) {
+  constexpr int lds = PfLds<D, G>::bytes;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t err = hipFuncSetAttribute((const void*)attn_prefill_mfma<D, G>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr = true;
+  }
+  const int nblk = (int)((max_seqlen + PfCfg<G>::QP - 1) / PfCfg<G>::QP);
+  attn_prefill_mfma<D, G><<<dim3((unsigned)nblk, (unsigned)seqs.S, (unsigned)nkv), 256, lds, st>>>(
+      q8, e_q, kc, vc, seqs.cu, seqs.start, seqs.seq_slot, (int)nq, (int)nkv, (int)n_slots,
+      (int)max_pos, nblk, M, K, out);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_t(const int8_t* q8, const int32_t* e_q, const int8_t* kc, const int8_t* vc,
                     const RowMap& rows, int64_t R, int64_t nq, int64_t nkv, int64_t n_slots,
@@ -300,6 +618,25 @@ hipError_t launch_attention_decode_fused(const int32_t* qkv, const QkvPost& p,
   DETINT_ATTF(128, 1) DETINT_ATTF(128, 2) DETINT_ATTF(128, 4) DETINT_ATTF(128, 8)
 #undef DETINT_ATTF
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_seqs(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
+                                 const int8_t* vc, const RowMap& seqs, int64_t R,
+                                 int64_t max_seqlen, int64_t nq, int64_t nkv, int64_t d,
+                                 int64_t n_slots, int64_t max_pos, int32_t M, int32_t K,
+                                 int32_t* out, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  const int64_t G = nq / nkv;
+  if (max_seqlen >= 16) {
+#define DETINT_PF(DD, GG)                                                                     \
+    if (d == DD && G == GG)                                                                   \
+      return launch_pf<DD, GG>(q8, e_q, kc, vc, seqs, max_seqlen, nq, nkv, n_slots, max_pos, M, \
+                               K, out, st);
+    DETINT_PF(64, 1) DETINT_PF(64, 2) DETINT_PF(64, 4)
+    DETINT_PF(128, 1) DETINT_PF(128, 2) DETINT_PF(128, 4)
+#undef DETINT_PF
+  }
+  return launch_attention(q8, e_q, kc, vc, seqs, R, nq, nkv, d, n_slots, max_pos, M, K, out, st);
 }
 
 bool attention_supported(int64_t d, int64_t group, int64_t max_pos) {

@@ -93,6 +93,15 @@ struct RowMap {
   const int32_t* slot;
 };
 
+// Attention for R rows packed as S sequences (seqs.cu / start / seq_slot):
+// the MFMA prefill kernel when the longest sequence has 16 or more rows and
+// the head shape allows, else the per-row kernel. Same results either way.
+hipError_t launch_attention_seqs(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
+                                 const int8_t* vc, const RowMap& seqs, int64_t R,
+                                 int64_t max_seqlen, int64_t nq, int64_t nkv, int64_t d,
+                                 int64_t n_slots, int64_t max_pos, int32_t M, int32_t K,
+                                 int32_t* out, hipStream_t st);
+
 // Attention over the cache for R rows.
 hipError_t launch_attention(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
                             const int8_t* vc, const RowMap& rows, int64_t R, int64_t nq,

@@ -256,6 +256,29 @@ def test_attention_prefill_and_decode(D, nq, nkv, d, max_pos):
     np.testing.assert_array_equal(host(got), want)
 
 
+@pytest.mark.parametrize("nq,nkv,d", [(32, 8, 64), (16, 8, 128), (8, 8, 128), (8, 4, 64)])
+def test_attention_prefill_long(D, nq, nkv, d):
+    """Sequences of several query blocks and key chunks (the MFMA prefill
+    path), one starting mid-cache, max_pos not a multiple of 32, and a slot
+    id out of range (its rows come back zero)."""
+    rng = np.random.default_rng(nq + d)
+    max_pos, slots = 500, 2
+    kc, vc = _cache(rng, slots, nkv, max_pos, d)
+    M, K = O.softmax_mult(20000, 22, d, 12)
+    lens, starts, sl = [300, 77, 20], [0, 400, 3], [1, 0, 5]
+    R = sum(lens)
+    q8 = rng.integers(-127, 128, (R, nq, d)).astype(np.int8)
+    eq = rng.integers(0, 12, (R, nq)).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    got = host(D.detint_attn_prefill(dev(q8), dev(eq), dev(kc), dev(vc), dev(cu),
+                                     dev(np.int32(starts)), dev(np.int32(sl)), M, K))
+    pos = np.concatenate([np.arange(s, s + n) for s, n in zip(starts[:2], lens[:2])]).astype(np.int32)
+    slot_r = np.repeat(sl[:2], lens[:2]).astype(np.int32)
+    want = O.attention(q8[:377], eq[:377], kc, vc, pos, slot_r, M, K)
+    np.testing.assert_array_equal(got[:377], want)
+    assert not got[377:].any()
+
+
 # ---------------------------------------------------------------- layer
 
 @pytest.fixture(scope="module")
