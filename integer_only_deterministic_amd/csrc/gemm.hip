@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   int8_t* sA = smem;
   int8_t* sB = smem + ST * SA;  // [ST][NB][SB]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS DMA bases in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
   // Tile order. Workgroups are dealt round-robin to the 8 XCDs: give each XCD
   // a contiguous run of logical tiles, then sweep groups of 8 tile rows
@@ -262,24 +263,25 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
   // stage kt % ST <- tile kt. Load q of thread t moves chunk g = 256q + t of
   // the stage: LDS bytes [16g, 16g + 16) = row g / 8, physical chunk g % 8.
-  auto issue = [&](int kt) {
+  // Loads 0 .. LA-1 fill A, the rest the weight plane(s).
+  auto issue_one = [&](int kt, int i) {
     const int st = kt % ST, k0 = kt * PBK;
-#pragma unroll
-    for (int q = 0; q < LA; ++q) {
+    if (i < LA) {
+      const int g = i * 256 + tid, r = g / CPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, DETINT_LDS(sA + st * SA + (i * 256 + wave * 64) * 16), 16,
+          (m0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
+    } else {
+      const int p = (i - LA) / LB, q = (i - LA) % LB;
       const int g = q * 256 + tid, r = g / CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, DETINT_LDS(sA + st * SA + (q * 256 + wave * 64) * 16), 16,
-          (m0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
+          p ? rl : rb, DETINT_LDS(sB + (st * NB + p) * SB + (q * 256 + wave * 64) * 16), 16,
+          (n0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
     }
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int p = 0; p < NB; ++p)
-#pragma unroll
-      for (int q = 0; q < LB; ++q) {
-        const int g = q * 256 + tid, r = g / CPR;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            p ? rl : rb, DETINT_LDS(sB + (st * NB + p) * SB + (q * 256 + wave * 64) * 16), 16,
-            (n0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
-      }
+    for (int i = 0; i < LT; ++i) issue_one(kt, i);
   };
 
   v16i acc[NB][TM][TN];
@@ -312,15 +314,23 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
         fb[buf][p][t] = *(const v4i*)(sB + ((kt % ST) * NB + p) * SB + r * PBK + (pswz(c, r) << 4));
       }
   };
-  auto mma = [&](int buf) {
+  // The MFMAs of one k-step; when kt_load >= 0 the LT loads of that tile go
+  // out one after each MFMA, so their issue overlaps matrix work.
+  auto mma = [&](int buf, int kt_load) {
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
+        for (int t = 0; t < TN; ++t) {
           acc[p][a][t] =
               __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][a], fb[buf][p][t], acc[p][a][t], 0, 0, 0);
+          const int i = (p * TM + a) * TN + t;
+          if (i < LT && kt_load >= 0) issue_one(kt_load, i);
+        }
+#pragma unroll
+    for (int i = NB * TM * TN; i < LT; ++i)
+      if (kt_load >= 0) issue_one(kt_load, i);
     if (WIDE) {
       const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
@@ -356,11 +366,10 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + ST < nk) issue(kt + ST);
         frag(kt + 1, 0, buf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      mma(buf);
+      mma(buf, (s + 1 == NS && kt + ST < nk) ? kt + ST : -1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
