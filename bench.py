@@ -6,14 +6,16 @@ A step is one greedy decode step of the Qwen3-0.6B-shaped integer model
 RoPE, int8 KV cache, DI-Softmax attention, O-proj, SwiGLU FFN) -> final
 RMSNorm -> tied lm_head -> int32 logits -> greedy token, captured once
 into a HIP graph and replayed. The headline value is decode tokens/s at
-batch 1 after a 64-token prompt; the same line reports batch-8 decode,
-prefill tokens/s, the int8 GEMM sweep at M = 2048 against the i8 MFMA peak,
-the roofline of the lm_head kernel, and the CPU oracle on this host.
-Every timed run's logits are hashed and compared with the oracle-written
-golden chain (tests/golden), so the timed run is also the verified run.
+batch 1 after a 64-token prompt. The same line reports batch-8 decode and
+prefill on that model, the Llama-3.2-1B-shaped 16-bit-limb model (prefill
+of 4 x 2048 tokens per call, batch-32 decode to a 4096-token context), the
+25-shape int8 GEMM sweep, the roofline of the decode step's fused final
+RMSNorm + lm_head kernel, and the CPU oracle on this host. The Qwen runs'
+logits are hashed and compared with the oracle-written golden chains
+(tests/golden), so the timed runs are also verified runs.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --roofline-only     # lm_head kernel + copy calibration (counter runs)
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-llama]
+    python bench.py --roofline-only     # final-head kernel + copy calibration (counter runs)
 """
 from __future__ import annotations
 
@@ -70,34 +72,38 @@ def timed_cold(fn, n, torch):
     return tot / n
 
 
-def lm_head_case(D, m, torch):
-    """The lm_head launch exactly as the decode step makes it (one row)."""
+def head_case(D, m, torch):
+    """detint_final_head for one row, logits only: the decode step's fused
+    final RMSNorm + tied lm_head streaming kernel, launched on its own."""
     import numpy as np
     sh = m.shape
     rng = np.random.default_rng(5)
-    x8 = torch.from_numpy(rng.integers(-127, 128, (1, sh.hidden)).astype(np.int8)).cuda()
-    rm = torch.tensor([24000], dtype=torch.int32, device="cuda")
-    rk = torch.tensor([18], dtype=torch.int32, device="cuda")
+    h = torch.from_numpy(rng.integers(-(1 << 20), 1 << 20, (1, sh.hidden)).astype(np.int32)).cuda()
+    g = torch.from_numpy(m.final_norm).cuda()
     emb = torch.from_numpy(m.emb).cuda()
     emb_m = torch.from_numpy(m.emb_m).cuda()
-    logits, part = D.detint_lm_head(x8, emb, None, rm, rk, emb_m, sh.w_k, sh.f_l)
-    fn = lambda: D.detint_lm_head(x8, emb, None, rm, rk, emb_m, sh.w_k, sh.f_l, logits, part)
-    nbytes = sh.vocab * sh.hidden + sh.hidden + 4 * sh.vocab * 2 + 8 * part.numel() + 16
+    ws = torch.empty(D.library().detint_final_head_workspace(1, sh.vocab, sh.hidden),
+                     dtype=torch.uint8, device="cuda")
+    logits, _ = D.detint_final_head(h, g, emb, None, emb_m, sh.w_k, sh.f_l, ws=ws, with_token=False)
+    fn = lambda: D.detint_final_head(h, g, emb, None, emb_m, sh.w_k, sh.f_l, logits, None, ws,
+                                     with_token=False)
+    # int8 table, its int32 mantissas, int32 logits out; the row and its gains
+    nbytes = sh.vocab * sh.hidden + 8 * sh.vocab + 6 * sh.hidden
     return fn, nbytes
 
 
 def kernel_source_sha() -> str:
-    """sha256 over the sources the lm_head kernel is compiled from."""
+    """sha256 over the sources the fused final-head kernel is compiled from."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "dev_int.h", "internal.h"):
+    for f in ("decode.hip", "dev_int.h", "internal.h"):
         h.update((ROOT / "integer_only_deterministic_amd" / "csrc" / f).read_bytes())
     return h.hexdigest()
 
 
 def traffic_from_profiles():
-    """HBM bytes per lm_head launch from the committed counter summary, or
+    """HBM bytes per final-head launch from the committed counter summary, or
     None when the kernel source changed since the counters were taken."""
-    f = ROOT / "profiles" / "lm_head_hbm_traffic.txt"
+    f = ROOT / "profiles" / "final_head_hbm_traffic.txt"
     if not f.exists():
         return None
     vals = {}
@@ -117,7 +123,7 @@ def roofline_only(D, S, torch):
     import dataclasses
     # the embedding / lm_head tensor is drawn independently of the layers
     m = S.make_model(dataclasses.replace(S.SHAPES["qwen3_0.6b"], n_layers=0), seed=0)
-    fn, nbytes = lm_head_case(D, m, torch)
+    fn, nbytes = head_case(D, m, torch)
     for _ in range(3):
         fn()
     t = timed_cold(fn, 20, torch)
@@ -126,7 +132,7 @@ def roofline_only(D, S, torch):
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"lm_head_us": t * 1e6, "lm_head_algorithmic_bytes": nbytes,
+    print(json.dumps({"final_head_us": t * 1e6, "final_head_algorithmic_bytes": nbytes,
                       "copy_bytes": src.numel(), "copy_launches": 5,
                       "kernel_source_sha256": kernel_source_sha()}))
 
@@ -150,6 +156,108 @@ def decode_run(D, dm, prompts, warmup, steps, torch):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return hist, (t1 - t0), ev0.elapsed_time(ev1) / 1e3
+
+
+def gemm_sweep(D, S, torch):
+    """The 25-shape int8 GEMM sweep, per-row x per-column requant to int8.
+    M >= 512: TOP/s against the i8 MFMA peak (back-to-back launches);
+    M <= 64: GB/s against HBM, each launch cache-cold."""
+    res = {}
+    for Kd, Nd in S.GEMM_SWEEP_KN:
+        g = S.make_gemm_operands(max(S.GEMM_SWEEP_M), Nd, Kd, seed=7)
+        A, Wt = torch.from_numpy(g["A"]).cuda(), torch.from_numpy(g["W"]).cuda()
+        rm, rk = torch.from_numpy(g["row_m"]).cuda(), torch.from_numpy(g["row_k"]).cuda()
+        cm = torch.from_numpy(g["col_m"]).cuda()
+        for M in S.GEMM_SWEEP_M:
+            out = torch.empty((M, Nd), dtype=torch.int8, device="cuda")
+            Am, rmm, rkm = A[:M], rm[:M], rk[:M]
+            f = lambda: D.detint_gemm_i8(Am, Wt, rmm, rkm, cm, g["col_k"], 0, D.REQ_I8, out)
+            for _ in range(3):
+                f()
+            key = f"M{M}_K{Kd}_N{Nd}"
+            if M >= 512:
+                t = timed(f, 20, torch)
+                tops = 2 * M * Nd * Kd / t / 1e12
+                res[key] = {"tops": round(tops, 1), "frac_i8_mfma": round(tops / I8_PEAK_TOPS, 4)}
+            else:
+                t = timed_cold(f, 10, torch)
+                gbs = (M * Kd + Nd * Kd + M * Nd + 8 * (M + Nd)) / t / 1e9
+                res[key] = {"gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "us": round(t * 1e6, 2)}
+            del out
+        del A, Wt
+    return res
+
+
+def llama_case(D, S, torch, dec_steps: int):
+    """Llama-3.2-1B-shaped model with 16-bit limbed weights: 32 seeded
+    2048-token prompts prefilled 4 per call, then batch-32 greedy decode
+    from position 2048 (HIP-graph segments of 256 steps)."""
+    import numpy as np
+    m = S.make_model("llama3.2_1b", seed=0)
+    sh = m.shape
+    B, P, SEG = 32, 2048, 256
+    prompts = S.make_prompts(sh.vocab, B, P, P, 5)
+    dm = D.DetintModel(m, n_slots=B)
+    scratch = torch.empty((B, sh.vocab), dtype=torch.int32, device="cuda")
+    toks, times = [], []
+    for c in range(B // 4):
+        sl = list(range(4 * c, 4 * c + 4))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks.append(dm.prefill([prompts[i] for i in sl], [0] * 4, sl, scratch, 4 * c))
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    t_pref = float(np.median(times[1:]))
+    L, H, F, nq, nkv, d = sh.n_layers, sh.hidden, sh.ffn, sh.n_q, sh.n_kv, sh.head_dim
+    lin_mac = L * H * ((nq + 2 * nkv) * d + nq * d + 2 * F) + L * F * H   # per token
+    att_mac = L * nq * d * 3 * 4 * (P * (P + 1) // 2)                     # QK^T + 2 P.V limbs, causal
+    ops = 2 * (2 * lin_mac * 4 * P + att_mac)                              # x2 limbs on the linears
+    tok = torch.cat(toks)
+    hist = torch.empty((SEG, B, sh.vocab), dtype=torch.int32, device="cuda")
+    done, t_dec, n_timed, pos = 0, 0.0, 0, P
+    first = None
+    while done < dec_steps:
+        n = min(SEG, dec_steps - done)
+        step = dm.decode_step_fn(tok, [pos] * B, list(range(B)), hist, 0)
+        step()                      # first replay of a fresh graph: untimed
+        torch.cuda.synchronize()
+        if first is None:
+            first = hist[0, 0].clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n - 1):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        t_dec += e0.elapsed_time(e1) / 1e3
+        n_timed += n - 1
+        done += n
+        pos += n
+    # batch invariance: prompt 0 alone, first decode step's logits equal row 0's
+    dm1 = dm
+    dm1.reset_cache()
+    t1 = dm1.prefill([prompts[0]], [0], [0], scratch, 0)
+    h1 = torch.empty((1, 1, sh.vocab), dtype=torch.int32, device="cuda")
+    dm1.decode_step_fn(t1, [P], [0], h1, 0, use_graph=False)()
+    torch.cuda.synchronize()
+    inv = bool(torch.equal(h1[0, 0], first))
+    w_bytes = 2 * (L * H * ((nq + 2 * nkv) * d + nq * d + 2 * F + F) + sh.vocab * H)
+    ctx_avg = P + 1 + (dec_steps - 1) / 2
+    step_bytes = w_bytes + 2 * L * nkv * d * B * ctx_avg
+    tps = B * n_timed / t_dec
+    return {
+        "workload": "Llama-3.2-1B-shaped integer model, 16-bit limbed weights (random init, seed 0)",
+        "prefill_4x2048_tok_s": round(4 * P / t_pref, 1),
+        "prefill_ms_per_call": round(1e3 * t_pref, 2),
+        "prefill_tops": round(ops / t_pref / 1e12, 1),
+        "prefill_frac_i8_mfma": round(ops / t_pref / 1e12 / I8_PEAK_TOPS, 4),
+        "decode_b32_tok_s": round(tps, 1),
+        "decode_b32_ms_per_step": round(1e3 * t_dec / n_timed, 3),
+        "decode_b32_hbm_frac": round(step_bytes * tps / B / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_ctx_range": [P + 1, P + dec_steps],
+        "batch_invariant_row0": inv,
+    }
 
 
 def cpu_baseline(m, p0, seconds: float, gpu_tokens):
@@ -184,6 +292,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--roofline-only", action="store_true")
+    ap.add_argument("--no-llama", action="store_true")
+    ap.add_argument("--llama-steps", type=int, default=2047)
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py: this build runs on one GPU only (the integer forward pass is "
@@ -241,37 +351,33 @@ def main():
     t_rag = timed(lambda: dm.prefill(rag, [0] * 8, list(range(8)), scratch, 0), 5, torch)
     t_64 = timed(lambda: dm.prefill([p0], [0], [0], scratch, 0), 10, torch)
 
-    # ---- int8 GEMM sweep at M = 2048 (requant to int8) ----
-    log("GEMM sweep M=2048")
-    gemm = {}
-    for Kd, Nd in S.GEMM_SWEEP_KN:
-        g = S.make_gemm_operands(2048, Nd, Kd, seed=7)
-        A, Wt = torch.from_numpy(g["A"]).cuda(), torch.from_numpy(g["W"]).cuda()
-        rm, rk = torch.from_numpy(g["row_m"]).cuda(), torch.from_numpy(g["row_k"]).cuda()
-        cm = torch.from_numpy(g["col_m"]).cuda()
-        out = torch.empty((2048, Nd), dtype=torch.int8, device="cuda")
-        f = lambda: D.detint_gemm_i8(A, Wt, rm, rk, cm, 22, 0, D.REQ_I8, out)
-        for _ in range(3):
-            f()
-        t = timed(f, 20, torch)
-        gemm[f"{Kd}x{Nd}"] = round(2 * 2048 * Nd * Kd / t / 1e12, 1)
-        del A, Wt, out
+    # ---- the 25-shape int8 GEMM sweep ----
+    log("GEMM sweep")
+    gemm = gemm_sweep(D, S, torch)
 
-    # ---- roofline of the dominant single kernel: the lm_head GEMV ----
-    log("lm_head kernel")
-    fn, nbytes = lm_head_case(D, m, torch)
+    # ---- roofline of the largest-traffic kernel of the step: the fused
+    # final RMSNorm + lm_head GEMV (one launch streams the 155.6 MB table) ----
+    log("final-head kernel")
+    fn, nbytes = head_case(D, m, torch)
     for _ in range(3):
         fn()
-    t_lm = timed_cold(fn, 30, torch)
-    achieved = nbytes / t_lm / 1e9
+    t_head = timed_cold(fn, 30, torch)
+    achieved = nbytes / t_head / 1e9
     traffic = traffic_from_profiles()
+
+    llama = None
+    if not args.no_llama:
+        del dm
+        torch.cuda.empty_cache()
+        log("Llama-3.2-1B-shaped model: prefill 4 x 2048 per call, batch-32 decode to 4096")
+        llama = llama_case(D, S, torch, args.llama_steps)
 
     cpu = None if args.no_cpu else cpu_baseline(m, p0, args.cpu_seconds, gpu_tokens)
 
     weights = sum(L.wqkv.size + L.wo.size + L.wgu.size + L.wd.size for L in m.layers) + m.emb.size
     ctx_avg = PROMPT_LEN + 1 + W + (K + 1) / 2
     step_bytes = weights + 2 * sh.n_layers * sh.n_kv * sh.head_dim * ctx_avg
-    gemm_best = max(gemm.values())
+    big = [v["frac_i8_mfma"] for v in gemm.values() if "frac_i8_mfma" in v]
     line = {
         "metric": "decode tok/s @bs1/8, prefill tok/s; i8 GEMM % MFMA peak; bit-exact logits",
         "value": round(tps1, 2),
@@ -295,14 +401,16 @@ def main():
         "decode_b8_tok_s": round(tps8, 1),
         "prefill_tok_s": {"ragged_8_prompts_%d_tokens" % ntok: round(ntok / t_rag, 1),
                           "prompt_64": round(PROMPT_LEN / t_64, 1)},
-        "gemm_m2048_tops": gemm,
-        "gemm_m2048_best_frac_i8_mfma": round(gemm_best / I8_PEAK_TOPS, 4),
         "decode_b1_hbm_frac": round(step_bytes * tps1 / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV (gemv<1,false,true>)",
+        "llama3.2_1b_limbs": llama,
+        "gemm_sweep_req_i8": gemm,
+        "gemm_best_frac_i8_mfma": round(max(big), 4),
+        "roofline": {"bound": "hbm",
+                     "kernel": "fused final RMSNorm + tied lm_head GEMV, 1 row (fgemv<1,2,1,1,4>)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": round(t_lm * 1e6, 2)},
+                     "avg_launch_us": round(t_head * 1e6, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

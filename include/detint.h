@@ -282,6 +282,24 @@ detint_status detint_lm_head(const int8_t *x8, const int8_t *emb, const int8_t *
 detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts,
                                   int32_t *next_tok, void *stream);
 
+/* The model's last step for S rows of the int32 residual h [S, H]: final
+ * RMSNorm with gain int16 [H] (scale 2^-12), tied lm_head logits int32
+ * [S, V] = R(x8 . E^T * m_r * emb_m, k_r + w_k - f_l), and the greedy token
+ * next_tok int32 [S] (lowest id among maxima). E is emb [V, H] int8, or
+ * 16-bit limbs emb/emb_lo as in detint_gemm_w16. For S <= 8 rows of int8
+ * weights (H <= 8192) it is the decode step's single streaming kernel (norm in
+ * its prologue, logits and per-wave argmax keys in its epilogue) plus one
+ * reduction; otherwise RMSNorm, lm_head and argmax run as separate launches.
+ * next_tok may be NULL: logits only (one launch on the fused path).
+ * ws: device scratch of detint_final_head_workspace(S, V, H) bytes.
+ * DetLLM README intro: int32 logits; DetLLM blog "DetLLM": DI-RMSNorm and
+ * the lowest-id tie rule. */
+int64_t detint_final_head_workspace(int64_t S, int64_t V, int64_t H);
+detint_status detint_final_head(const int32_t *h, int64_t S, int64_t H, const int16_t *gain,
+                                const int8_t *emb, const int8_t *emb_lo, const int32_t *emb_m,
+                                int64_t V, int32_t w_k, int32_t f_l, int32_t *logits,
+                                int32_t *next_tok, void *ws, int64_t ws_bytes, void *stream);
+
 /* One decoder layer in place on the int32 residual h [R, hidden] (|h| <
  * 2^25), same sequence/cache arguments and workspace as detint_forward:
  * RMSNorm -> QKV -> (q/k-norm) -> RoPE -> q DQ, K/V into the cache ->

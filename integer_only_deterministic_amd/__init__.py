@@ -77,6 +77,8 @@ _SIGS = {
     "detint_lm_head_parts": (i64, [i64]),
     "detint_lm_head": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp]),
     "detint_argmax_parts": (i32, [vp, i64, i64, vp, vp]),
+    "detint_final_head_workspace": (i64, [i64, i64, i64]),
+    "detint_final_head": (i32, [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, vp]),
     "detint_layer_forward": (i32, [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, vp, i64,
                                    vp]),
 }
@@ -248,6 +250,28 @@ def detint_lm_head(x8, emb, emb_lo, row_m, row_k, emb_m, w_k, f_l, logits=None, 
     _call("detint_lm_head", _p(x8, torch.int8), _p(emb, torch.int8), _p(emb_lo), S_, V, H, _p(row_m),
           _p(row_k), _p(emb_m), int(w_k), int(f_l), _p(logits), _p(part), _stream())
     return logits, part
+
+
+def detint_final_head(h, gain, emb, emb_lo, emb_m, w_k, f_l, logits=None, next_tok=None, ws=None,
+                      with_token=True):
+    """Final RMSNorm + tied lm_head + greedy token for the rows of h [S, H]:
+    returns (logits [S, V], next_tok [S] or None when with_token is False)."""
+    torch = _torch()
+    S_, H = h.shape
+    V = emb.shape[0]
+    if logits is None:
+        logits = torch.empty((S_, V), dtype=torch.int32, device=h.device)
+    if next_tok is None and with_token:
+        next_tok = torch.empty(S_, dtype=torch.int32, device=h.device)
+    nbytes = library().detint_final_head_workspace(S_, V, H)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device)
+    _call("detint_final_head", _p(h, torch.int32), S_, H, _p(gain, torch.int16), _p(emb, torch.int8),
+          _p(emb_lo, torch.int8) if emb_lo is not None else None, _p(emb_m, torch.int32), V,
+          int(w_k), int(f_l), _p(logits, torch.int32), _p(next_tok, torch.int32) if with_token else None,
+          _p(ws),
+          ws.numel() * ws.element_size(), _stream())
+    return logits, next_tok
 
 
 def detint_argmax_parts(part):

@@ -207,6 +207,8 @@ detint_status detint_attn_decode(const int8_t* q8, const int32_t* e_q, const int
 
 // ------------------------------------------------------------- lm_head
 
+constexpr int64_t kArgmaxParts = 64;
+
 int64_t detint_lm_head_parts(int64_t V) { return V > 0 ? logits_argmax_parts(V) : 0; }
 
 detint_status detint_lm_head(const int8_t* x8, const int8_t* emb, const int8_t* emb_lo, int64_t S,
@@ -222,6 +224,59 @@ detint_status detint_lm_head(const int8_t* x8, const int8_t* emb, const int8_t* 
   Epi e{row_m, row_k, emb_m, w_k, f_l, MODE_FIX, nullptr};
   return hip_status(launch_logits_argmax(x8, emb, emb_lo, S, V, H, e, logits, part, S_(stream)),
                     "lm_head launch");
+}
+
+static int64_t final_head_parts(int64_t S, int64_t V) {
+  int64_t np = logits_argmax_parts(V);
+  if (fused_decode_parts(V) > np) np = fused_decode_parts(V);
+  if (kArgmaxParts > np) np = kArgmaxParts;
+  return S * np;
+}
+
+int64_t detint_final_head_workspace(int64_t S, int64_t V, int64_t H) {
+  if (S < 0 || V < 0 || H < 0) return -1;
+  const int64_t a = 8 * final_head_parts(S, V > 0 ? V : 1);
+  const int64_t b = ((S * H + 255) / 256) * 256;
+  return a + b + 8 * S + 256;
+}
+
+detint_status detint_final_head(const int32_t* h, int64_t S, int64_t H, const int16_t* gain,
+                                const int8_t* emb, const int8_t* emb_lo, const int32_t* emb_m,
+                                int64_t V, int32_t w_k, int32_t f_l, int32_t* logits,
+                                int32_t* next_tok, void* ws, int64_t ws_bytes, void* stream) {
+  REQUIRE(S >= 0 && H > 0 && V >= 0, "final_head: bad sizes");
+  if (S == 0 || V == 0) return ok();
+  REQUIRE(h && gain && emb && emb_m && logits && ws, "final_head: null pointer");
+  REQUIRE(H % 16 == 0 && aligned16(emb) && (!emb_lo || aligned16(emb_lo)),
+          "final_head: hidden must be a multiple of 16 with 16-byte aligned tables");
+  REQUIRE(H <= (emb_lo ? 65536 : 131072), "final_head: hidden too large");
+  REQUIRE(ws_bytes >= detint_final_head_workspace(S, V, H), "final_head: workspace too small");
+  hipStream_t st = S_(stream);
+  int64_t* part = (int64_t*)ws;
+  int8_t* x8 = (int8_t*)ws + 8 * final_head_parts(S, V);
+  int32_t* rm = (int32_t*)(x8 + ((S * H + 255) / 256) * 256);
+  int32_t* rk = rm + S;
+  hipError_t e;
+  if (!emb_lo && fused_decode_supported(S, H)) {
+    // the decode step's kernel: RMSNorm prologue, logits, argmax partials
+    e = launch_fused_lm_head(h, nullptr, gain, emb, emb_m, w_k, f_l, S, V, H, logits, nullptr, part, st);
+    if (e != hipSuccess || !next_tok) return hip_status(e, "final_head fused launch");
+    return hip_status(launch_argmax_final(part, S, fused_decode_parts(V), next_tok, st),
+                      "final_head argmax");
+  }
+  e = launch_rmsnorm(h, nullptr, gain, S, H, x8, rm, rk, st);
+  if (e != hipSuccess) return hip_status(e, "final_head rmsnorm");
+  Epi ep{rm, rk, emb_m, w_k, f_l, MODE_FIX, nullptr};
+  if (S <= 16) {
+    e = launch_logits_argmax(x8, emb, emb_lo, S, V, H, ep, logits, part, st);
+    if (e != hipSuccess || !next_tok) return hip_status(e, "final_head lm_head");
+    return hip_status(launch_argmax_final(part, S, logits_argmax_parts(V), next_tok, st),
+                      "final_head argmax");
+  }
+  e = launch_gemm(x8, emb, emb_lo, S, V, H, ep, logits, st);
+  if (e != hipSuccess || !next_tok) return hip_status(e, "final_head lm_head");
+  return hip_status(launch_argmax(logits, nullptr, S, V, part, kArgmaxParts, next_tok, st),
+                    "final_head argmax");
 }
 
 detint_status detint_argmax_parts(const int64_t* part, int64_t S, int64_t nparts,
@@ -305,7 +360,6 @@ struct detint_model {
 
 namespace {
 
-constexpr int64_t kArgmaxParts = 64;
 
 int64_t al(int64_t x) { return (x + 255) & ~(int64_t)255; }
 

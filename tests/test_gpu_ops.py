@@ -314,6 +314,40 @@ def test_layer256_split_and_token_by_token(D, layer_case):
 
 # -------------------------------------------------------------- lm_head
 
+# S <= 8 int8 rows take the fused decode kernel; wide tables and S > 8 take
+# RMSNorm + lm_head (GEMV up to 16 rows, MFMA GEMM beyond) + argmax.
+@pytest.mark.parametrize("S_,V,H,wide", [(1, 151936, 1024, False), (8, 5000, 256, False),
+                                         (5, 4099, 2048, False), (12, 3000, 512, False),
+                                         (40, 2000, 256, False), (3, 4099, 512, True)])
+def test_final_head(D, S_, V, H, wide):
+    """Final RMSNorm + tied lm_head + greedy token from the residual rows,
+    with duplicated embedding rows forcing exact ties at the maximum."""
+    rng = np.random.default_rng(S_ + V + H)
+    h = rng.integers(-(1 << 20), 1 << 20, (S_, H)).astype(np.int32)
+    g = rng.integers(1 << 12, (1 << 13) + 1, H).astype(np.int16)
+    if wide:
+        E = rng.integers(-32767, 32768, (V, H)).astype(np.int16)
+    else:
+        E = rng.integers(-127, 128, (V, H)).astype(np.int8)
+    E[V - 1] = E[V // 2] = E[7]
+    em = rng.integers(1 << 14, 1 << 15, V).astype(np.int32)
+    em[V - 1] = em[V // 2] = em[7]
+    wk, fl = (30, 16) if wide else (22, 16)
+    x8, xm, xk = O.rmsnorm(h, g)
+    want = O.epilogue(O.gemm(x8, E), xm, xk, em, wk, fl, O.FIX)
+    if wide:
+        hi, lo = D.detint_split_w16(dev(E))
+    else:
+        hi, lo = dev(E), None
+    logits, tok = D.detint_final_head(dev(h), dev(g), hi, lo, dev(em), wk, fl)
+    np.testing.assert_array_equal(host(logits), want)
+    np.testing.assert_array_equal(host(tok), O.argmax(want))
+    lg2, none = D.detint_final_head(dev(h), dev(g), hi, lo, dev(em), wk, fl, with_token=False)
+    assert none is None
+    np.testing.assert_array_equal(host(lg2), want)
+
+
+
 @pytest.mark.parametrize("S_,V,H,wide", [(1, 151936, 1024, False), (8, 5000, 256, False),
                                          (3, 4099, 512, True), (16, 1000, 256, False)])
 def test_lm_head_and_greedy_token(D, S_, V, H, wide):
