@@ -16,6 +16,7 @@ logits are hashed and compared with the oracle-written golden chains
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-llama]
     python bench.py --roofline-only     # final-head kernel + copy calibration (counter runs)
+    python bench.py --llama-only --llama-steps 64   # the Llama-shaped runs alone (profiling)
 """
 from __future__ import annotations
 
@@ -293,6 +294,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--roofline-only", action="store_true")
     ap.add_argument("--no-llama", action="store_true")
+    ap.add_argument("--llama-only", action="store_true")
     ap.add_argument("--llama-steps", type=int, default=2047)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -313,6 +315,9 @@ def main():
     torch.cuda.set_device(0)
     if args.roofline_only:
         roofline_only(D, S, torch)
+        return
+    if args.llama_only:
+        print(json.dumps(llama_case(D, S, torch, args.llama_steps)), flush=True)
         return
 
     gold = json.loads((ROOT / "tests" / "golden" / "qwen3_b1.json").read_text())

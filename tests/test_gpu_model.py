@@ -130,3 +130,62 @@ def test_qwen3_repeat_runs_identical(D, qwen):
         dm.reset_cache()
         np.testing.assert_array_equal(host(dm.generate([p0], 64)), a)
     assert D.logits_chain(a[:, 0])[-1] == g["logits_chain"][0][63]
+
+
+# ------------------------------------------- Llama-3.2-1B shape, 16-bit limbs
+
+@pytest.fixture(scope="module")
+def llama():
+    return S.make_model("llama3.2_1b", seed=0)
+
+
+def test_llama_limbs_short_generation_matches_oracle(D, llama):
+    """Full Llama-3.2-1B shape (16 layers, hidden 2048, 32/8 heads, d 64,
+    FFN 8192, vocab 128256, 16-bit limbed weights): two prompts of 130 and 77
+    tokens in one prefill call (MFMA prefill attention, several query
+    blocks), then 4 batch-2 decode steps; every logits row equals the
+    oracle's."""
+    m = llama
+    V = m.shape.vocab
+    prompts = [S.make_prompt(V, 130, 11), S.make_prompt(V, 77, 12)]
+    n_new = 5
+    rows = []
+    toks = O.OracleModel(m, slots=2).generate(prompts, n_new, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=2)
+    hist = host(dm.generate(prompts, n_new))
+    for s in range(n_new):
+        np.testing.assert_array_equal(hist[s], rows[s], err_msg=f"step {s}")
+    np.testing.assert_array_equal(hist.argmax(-1).T, toks)
+
+
+def test_llama_limbs_invariances(D, llama):
+    """At the same shape with a 512-token prompt: its last-position logits,
+    and the logits of the decode step after it, are the same whether the
+    prompt is prefilled in one call, in two halves, or in one call together
+    with another prompt."""
+    import torch
+    m = llama
+    V = m.shape.vocab
+    p = S.make_prompt(V, 512, 21)
+    other = S.make_prompt(V, 300, 22)
+    got = {}
+    for mode in ("one", "halves", "batched"):
+        dm = D.DetintModel(m, n_slots=2)
+        rows = torch.zeros((4, V), dtype=torch.int32, device="cuda")   # prefill logits rows
+        step = torch.zeros((1, V), dtype=torch.int32, device="cuda")   # the decode step's row
+        if mode == "one":
+            tok = dm.prefill([p], [0], [0], rows, 0)
+            last = 0
+        elif mode == "halves":
+            dm.prefill([p[:256]], [0], [0], rows, 3)
+            tok = dm.prefill([p[256:]], [256], [0], rows, 0)
+            last = 0
+        else:
+            tok = dm.prefill([other, p], [0, 0], [1, 0], rows, 2)[1:]
+            last = 3
+        dm.decode(tok, [512], [0], 1, step, 0)
+        got[mode] = (host(rows[last]), host(step[0]))
+        del dm
+    for mode in ("halves", "batched"):
+        np.testing.assert_array_equal(got[mode][0], got["one"][0], err_msg=f"prefill logits, {mode}")
+        np.testing.assert_array_equal(got[mode][1], got["one"][1], err_msg=f"decode logits, {mode}")
