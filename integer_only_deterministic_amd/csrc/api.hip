@@ -364,8 +364,10 @@ namespace {
 int64_t al(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct WsLayout {
-  int64_t pos_of, slot_of, last_row, h, x8, rm, rk, qkv, q8, eq, att, gu, p64, part, total;
+  int64_t pos_of, slot_of, last_row, h, x8, rm, rk, qkv, q8, eq, att, gu, p64, part, sk_part,
+      sk_cnt, sk_tiles, total;
 };
+constexpr int64_t kSplitPairs = 1024;  // (tile, split) pairs of split-K partials
 
 WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
   WsLayout w{};
@@ -398,6 +400,13 @@ WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
   const int64_t npf = fused_decode_parts(d.vocab > 0 ? d.vocab : 1);
   if (npf > np) np = npf;
   w.part = take(8 * S * (np > kArgmaxParts ? np : kArgmaxParts));
+  // split-K partials and counters of the skinny (<= 64-row) GEMMs
+  int64_t nmax = nqkv > d.hidden ? nqkv : d.hidden;
+  if (2 * d.ffn > nmax) nmax = 2 * d.ffn;
+  w.sk_tiles = (nmax + 31) / 32;
+  w.sk_part = R <= 64 ? take(4 * kSplitPairs * kSplitTileInts) : 0;
+  w.sk_cnt = R <= 64 ? take(4 * w.sk_tiles) : 0;
+  if (R > 64) w.sk_tiles = 0;
   w.total = o;
   return w;
 }
@@ -479,6 +488,9 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   const int64_t nqd = nq * hd, nqkv = (nq + 2 * nkv) * hd;
   const size_t layer_stride = (size_t)n_slots * nkv * d.max_pos * hd;
   const int32_t wk = d.w_k;
+  const SplitWs spw{w.sk_tiles ? (int32_t*)(base + w.sk_part) : nullptr,
+                    w.sk_tiles ? (int32_t*)(base + w.sk_cnt) : nullptr, kSplitPairs, w.sk_tiles};
+  const SplitWs* sp = w.sk_tiles ? &spw : nullptr;
   int8_t* kc = k_cache + l * layer_stride;
   int8_t* vc = v_cache + l * layer_stride;
   hipError_t e;
@@ -492,7 +504,7 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   LAUNCH(launch_rmsnorm(h, nullptr, L.attn_norm, R, H, x8, rm, rk, st));
   {
     Epi ep{rm, rk, L.wqkv_m, wk, d.qk_norm ? 0 : d.f_n, d.qk_norm ? MODE_RAW : MODE_FIX, nullptr};
-    LAUNCH(launch_gemm(x8, L.wqkv, d.wide ? L.wqkv_lo : nullptr, R, nqkv, H, ep, qkv, st));
+    LAUNCH(launch_gemm(x8, L.wqkv, d.wide ? L.wqkv_lo : nullptr, R, nqkv, H, ep, qkv, st, sp));
   }
   QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
              L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
@@ -503,18 +515,18 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
   {
     Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr};
-    LAUNCH(launch_gemm(x8, L.wo, d.wide ? L.wo_lo : nullptr, R, H, nqd, ep, h, st));
+    LAUNCH(launch_gemm(x8, L.wo, d.wide ? L.wo_lo : nullptr, R, H, nqd, ep, h, st, sp));
   }
   // FFN block: RMSNorm -> gate/up -> DI-SwiGLU -> down + residual
   LAUNCH(launch_rmsnorm(h, nullptr, L.ffn_norm, R, H, x8, rm, rk, st));
   {
     Epi ep{rm, rk, L.wgu_m, wk, d.f_a, MODE_FIX, nullptr};
-    LAUNCH(launch_gemm(x8, L.wgu, d.wide ? L.wgu_lo : nullptr, R, 2 * F, H, ep, gu, st));
+    LAUNCH(launch_gemm(x8, L.wgu, d.wide ? L.wgu_lo : nullptr, R, 2 * F, H, ep, gu, st, sp));
   }
   LAUNCH(launch_swiglu(gu, R, F, d.f_a, m->mg, m->kg, x8, rm, rk, st));
   {
     Epi ep{rm, rk, L.wd_m, wk, d.f_res, MODE_RES_ADD, nullptr};
-    LAUNCH(launch_gemm(x8, L.wd, d.wide ? L.wd_lo : nullptr, R, H, F, ep, h, st));
+    LAUNCH(launch_gemm(x8, L.wd, d.wide ? L.wd_lo : nullptr, R, H, F, ep, h, st, sp));
   }
 #undef LAUNCH
   return ok();
@@ -603,7 +615,8 @@ detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t
   char* base = (char*)ws;
   hipStream_t st = S_(stream);
   hipError_t e = launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
-                                  (int32_t*)(base + w.slot_of), (int32_t*)(base + w.last_row), st);
+                                  (int32_t*)(base + w.slot_of), (int32_t*)(base + w.last_row), st,
+                                  w.sk_tiles ? (int32_t*)(base + w.sk_cnt) : nullptr, w.sk_tiles);
   if (e != hipSuccess) return hip_status(e, "rows_meta");
   const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
   return run_layer(m, layer, h, k_cache, v_cache, n_slots, R, seqs, max_seqlen, base, w, st);
@@ -648,7 +661,8 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
     return s;
   }
   LAUNCH(launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
-                          (int32_t*)(base + w.slot_of), last_row, st));
+                          (int32_t*)(base + w.slot_of), last_row, st,
+                          w.sk_tiles ? (int32_t*)(base + w.sk_cnt) : nullptr, w.sk_tiles));
   LAUNCH(launch_embed(ids, R, d.emb, d.wide ? d.emb_lo : nullptr, d.emb_m, d.hidden, d.vocab,
                       d.w_k - d.f_res, h, st));
   const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};

@@ -57,7 +57,8 @@ __device__ __forceinline__ void row_info(const RowMap& m, int r, int& pos, int& 
 // Attention of one query row for the G query heads sharing one KV head.
 // sq: the G q8 vectors (LDS, 16-byte chunks); eqv: their DQ exponents;
 // K, V: the (slot, KV head) cache block; keys 0..ctx-1; sc: LDS [G][ld].
-template <int D, int G, int NT = TPB>
+// KU key rows and VU value rows are in flight per thread in passes 1 and 4.
+template <int D, int G, int NT = TPB, int KU = 4, int VU = 8>
 __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const int8_t* __restrict__ K,
                                        const int8_t* __restrict__ V, int ctx, int ld, int32_t Ms,
                                        int32_t Ks, int32_t* __restrict__ orow, int32_t* sc,
@@ -86,17 +87,16 @@ __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const 
     }
   };
   int j1 = tid;
-  for (; j1 + NT < ctx; j1 += 2 * NT) {  // two key rows in flight
-    v4i ka[CH], kb[CH];
+  for (; j1 + (KU - 1) * NT < ctx; j1 += KU * NT) {  // KU key rows in flight
+    v4i kk[KU][CH];
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      ka[cc] = ((const v4i*)(K + (size_t)j1 * D))[cc];
-      kb[cc] = ((const v4i*)(K + (size_t)(j1 + NT) * D))[cc];
-    }
-    score(ka, j1);
-    score(kb, j1 + NT);
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) kk[u][cc] = ((const v4i*)(K + (size_t)(j1 + u * NT) * D))[cc];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) score(kk[u], j1 + u * NT);
   }
-  if (j1 < ctx) {
+  for (; j1 < ctx; j1 += NT) {
     v4i ka[CH];
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) ka[cc] = ((const v4i*)(K + (size_t)j1 * D))[cc];
@@ -149,15 +149,12 @@ __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const 
     }
   };
   int j = rg;
-  for (; j + 3 * RG < ctx; j += 4 * RG) {  // four independent row loads in flight
-    const v4i v0 = *(const v4i*)(V + (size_t)j * D + c * 16);
-    const v4i v1 = *(const v4i*)(V + (size_t)(j + RG) * D + c * 16);
-    const v4i v2 = *(const v4i*)(V + (size_t)(j + 2 * RG) * D + c * 16);
-    const v4i v3 = *(const v4i*)(V + (size_t)(j + 3 * RG) * D + c * 16);
-    pv(v0, j);
-    pv(v1, j + RG);
-    pv(v2, j + 2 * RG);
-    pv(v3, j + 3 * RG);
+  for (; j + (VU - 1) * RG < ctx; j += VU * RG) {  // VU independent row loads in flight
+    v4i vv[VU];
+#pragma unroll
+    for (int u = 0; u < VU; ++u) vv[u] = *(const v4i*)(V + (size_t)(j + u * RG) * D + c * 16);
+#pragma unroll
+    for (int u = 0; u < VU; ++u) pv(vv[u], j + u * RG);
   }
   for (; j < ctx; j += RG) pv(*(const v4i*)(V + (size_t)j * D + c * 16), j);
   // reduce over the lanes of a wave that share chunk c

@@ -561,19 +561,26 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
 constexpr int SK_W = 16;   // waves per workgroup = K chunks
 constexpr int SK_G = 2;    // k-steps per load group
 
+// Split-K across workgroups (grid.y = ks > 1, given a workspace): split s
+// covers K range [s K / ks, (s + 1) K / ks); each split writes its partial
+// sums for the tile to sp.part, and the last split to arrive (counted in
+// sp.cnt[tile], which it resets to 0) adds the ks partials - an exact integer
+// sum, so the split changes no bit - and runs the epilogue.
 template <bool WIDE, int MR>
 __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A,
                                                     const int8_t* __restrict__ W,
                                                     const int8_t* __restrict__ Wlo, int M, int N,
-                                                    int K, Epi e, void* out) {
+                                                    int K, Epi e, void* out, SplitWs sp) {
   constexpr int NB = WIDE ? 2 : 1;
+  constexpr int TE = NB * MR * 1024 + MR * 32;       // partial ints per (tile, split)
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   int32_t* part = (int32_t*)smem;                   // [SK_W][NB][MR][32 * 32]
   int32_t* prs = part + SK_W * NB * MR * 1024;       // [SK_W][MR * 32] row sums
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 32;
-  const int kc = K / SK_W, nst = kc / 32;
-  const int kb = wave * kc + (lane >> 5) * 16;
+  const int n0 = blockIdx.x * 32, ks = gridDim.y, split = blockIdx.y;
+  const int kc = K / ks / SK_W, nst = kc / 32;
+  const int kb = split * (K / ks) + wave * kc + (lane >> 5) * 16;
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
@@ -648,18 +655,61 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     }
   }
   __syncthreads();
+  int32_t hs[MR], ls[MR], rss[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int row = m * 32 + (tid >> 5);
+    hs[m] = ls[m] = rss[m] = 0;
+#pragma unroll
+    for (int w = 0; w < SK_W; ++w) {
+      hs[m] += part[((w * NB + 0) * MR + m) * 1024 + tid];
+      if (WIDE) {
+        ls[m] += part[((w * NB + NB - 1) * MR + m) * 1024 + tid];
+        rss[m] += prs[w * MR * 32 + row];
+      }
+    }
+  }
+  if (ks > 1) {
+    // Partials go out as agent-scope stores (coherent across the XCDs' L2
+    // caches without a full L2 write-back), complete before the barrier; the
+    // arrival count is a device-scope atomic; the last split reads them back
+    // with agent-scope loads.
+    auto put = [](int32_t* p, int32_t v) {
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto get = [](const int32_t* p) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    int32_t* mine = sp.part + ((size_t)blockIdx.x * ks + split) * TE;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      put(&mine[m * 1024 + tid], hs[m]);
+      if (WIDE) put(&mine[(MR + m) * 1024 + tid], ls[m]);
+      if (WIDE && (tid & 31) == 0) put(&mine[NB * MR * 1024 + m * 32 + (tid >> 5)], rss[m]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&sp.cnt[blockIdx.x], 1) == ks - 1;
+    __syncthreads();
+    if (!s_last) return;
+    const int32_t* all = sp.part + (size_t)blockIdx.x * ks * TE;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      hs[m] = ls[m] = rss[m] = 0;
+      for (int t = 0; t < ks; ++t) {
+        hs[m] += get(&all[t * TE + m * 1024 + tid]);
+        if (WIDE) {
+          ls[m] += get(&all[t * TE + (MR + m) * 1024 + tid]);
+          rss[m] += get(&all[t * TE + NB * MR * 1024 + m * 32 + (tid >> 5)]);
+        }
+      }
+    }
+    if (tid == 0) put(&sp.cnt[blockIdx.x], 0);  // ready for the next call
+  }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     const int row = m * 32 + (tid >> 5), i = row, j = n0 + (tid & 31);
-    int32_t hi = 0, lo = 0, rs = 0;
-#pragma unroll
-    for (int w = 0; w < SK_W; ++w) {
-      hi += part[((w * NB + 0) * MR + m) * 1024 + tid];
-      if (WIDE) {
-        lo += part[((w * NB + NB - 1) * MR + m) * 1024 + tid];
-        rs += prs[w * MR * 32 + row];
-      }
-    }
+    const int32_t hi = hs[m], lo = ls[m], rs = rss[m];
     if (i < M && j < N) {
       int64_t v = hi;
       if (WIDE) v = 256 * v + (int64_t)lo + 128 * (int64_t)rs;
@@ -668,9 +718,25 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
   }
 }
 
+// K splits for a skinny GEMM: enough workgroups to cover the chip (about
+// 256), each split a multiple of 512 bytes of K, within the workspace.
+int skinny_splits(int64_t N, int64_t K, const SplitWs* sp) {
+  if (!sp || !sp->part) return 1;
+  const int64_t tiles = (N + 31) / 32;
+  if (tiles >= 256) return 1;  // already a workgroup per CU
+  int ks = 1;
+  for (int c = 2; c <= 16; ++c) {
+    if (K % (c * 512) != 0) continue;
+    if (tiles * c > sp->max_tile_splits || tiles > sp->max_tiles) break;
+    ks = c;
+    if (tiles * c >= 256) break;
+  }
+  return ks;
+}
+
 template <bool WIDE, int MR>
 hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
-                         const Epi& e, void* out, hipStream_t st) {
+                         const Epi& e, void* out, const SplitWs* sp, hipStream_t st) {
   constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
   static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
   static bool attr = false;
@@ -680,7 +746,10 @@ hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
     if (err != hipSuccess) return err;
     attr = true;
   }
-  gemm_skinny<WIDE, MR><<<(N + 31) / 32, 1024, lds, st>>>(A, W, Wlo, M, N, K, e, out);
+  const int ks = skinny_splits(N, K, sp);
+  const SplitWs none{};
+  gemm_skinny<WIDE, MR><<<dim3((unsigned)((N + 31) / 32), (unsigned)ks), 1024, lds, st>>>(
+      A, W, Wlo, M, N, K, e, out, ks > 1 ? *sp : none);
   return hipGetLastError();
 }
 
@@ -824,15 +893,16 @@ __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __re
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
-                       int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st) {
+                       int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
+                       const SplitWs* sp) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
   // buffer offsets are 32-bit
   const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
   if (off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !W_lo))) {
-    if (W_lo) return skinny_launch<true, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
-    if (M <= 32) return skinny_launch<false, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
-    return skinny_launch<false, 2>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
+    if (W_lo) return skinny_launch<true, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
+    if (M <= 32) return skinny_launch<false, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
+    return skinny_launch<false, 2>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
   }
   if (K % PBK == 0 && off32) {
     if (W_lo) return pipe_dispatch<true>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);

@@ -19,8 +19,21 @@ struct Epi {
 };
 
 // C = A[M,K] . W[N,K]^T with epilogue; W_lo != nullptr selects 16-bit limbs.
+// Workspace for split-K skinny GEMMs: int32 partials for up to
+// max_tile_splits (tile, split) pairs of up to 2 x 64 x 32 values each plus
+// row sums, and one arrival counter per 32-column tile (max_tiles), which must
+// be zero before the first use (every use leaves them zero).
+struct SplitWs {
+  int32_t* part;
+  int32_t* cnt;
+  int64_t max_tile_splits;
+  int64_t max_tiles;
+};
+constexpr int64_t kSplitTileInts = 2 * 2 * 1024 + 2 * 32;
+
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
-                       int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st);
+                       int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
+                       const SplitWs* sp = nullptr);
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
                             hipStream_t st);
 // lm_head for M <= 16 rows: FIX-mode logits plus per-wave greedy-argmax
@@ -53,10 +66,11 @@ hipError_t launch_embed(const int32_t* ids, int64_t R, const int8_t* emb, const 
                         const int32_t* emb_m, int64_t H, int64_t V, int32_t shift, int32_t* h,
                         hipStream_t st);
 
-// Per-row metadata of packed sequences: pos_of/slot_of [R], last_row [S].
+// Per-row metadata of packed sequences: pos_of/slot_of [R], last_row [S];
+// also zeroes zero[0 .. nzero) (the split-K arrival counters).
 hipError_t launch_rows_meta(const int32_t* cu, const int32_t* start, const int32_t* slot,
                             int64_t S, int32_t* pos_of, int32_t* slot_of, int32_t* last_row,
-                            hipStream_t st);
+                            hipStream_t st, int32_t* zero = nullptr, int64_t nzero = 0);
 hipError_t launch_decode_meta(const int32_t* ctx_len, const int32_t* slot, int64_t B,
                               int32_t* pos_of, int32_t* slot_of, hipStream_t st);
 

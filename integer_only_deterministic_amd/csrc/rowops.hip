@@ -179,8 +179,10 @@ __global__ __launch_bounds__(TPB) void embed_k(const int32_t* __restrict__ ids,
 
 __global__ void rows_meta_k(const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
                             const int32_t* __restrict__ slot, int32_t* pos_of, int32_t* slot_of,
-                            int32_t* last_row) {
+                            int32_t* last_row, int32_t* zero, int nzero) {
   const int s = blockIdx.x;
+  if (s == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   const int b = cu[s], e = cu[s + 1];
   for (int r = b + threadIdx.x; r < e; r += blockDim.x) {
     pos_of[r] = start[s] + (r - b);
@@ -345,9 +347,10 @@ hipError_t launch_embed(const int32_t* ids, int64_t R, const int8_t* emb, const 
 
 hipError_t launch_rows_meta(const int32_t* cu, const int32_t* start, const int32_t* slot,
                             int64_t S, int32_t* pos_of, int32_t* slot_of, int32_t* last_row,
-                            hipStream_t st) {
+                            hipStream_t st, int32_t* zero, int64_t nzero) {
   if (S == 0) return hipSuccess;
-  rows_meta_k<<<(unsigned)S, 256, 0, st>>>(cu, start, slot, pos_of, slot_of, last_row);
+  rows_meta_k<<<(unsigned)S, 256, 0, st>>>(cu, start, slot, pos_of, slot_of, last_row, zero,
+                                           (int)nzero);
   return hipGetLastError();
 }
 

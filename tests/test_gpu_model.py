@@ -189,3 +189,36 @@ def test_llama_limbs_invariances(D, llama):
     for mode in ("halves", "batched"):
         np.testing.assert_array_equal(got[mode][0], got["one"][0], err_msg=f"prefill logits, {mode}")
         np.testing.assert_array_equal(got[mode][1], got["one"][1], err_msg=f"decode logits, {mode}")
+
+
+def test_qwen3_batch40_split_k_rows_match(D, qwen):
+    """40 decode rows take the skinny split-K GEMMs (17-64 rows); row 0 is the
+    golden prompt, whose first decode logits must continue the oracle-written
+    hash chain, and row 39 must equal the same prompt decoded alone."""
+    import torch
+    m, g = qwen
+    V = m.shape.vocab
+    p0 = S.make_prompt(V, 64, g["prompt_seed"])
+    prompts = [p0] + S.make_prompts(V, 39, 16, 64, 7)
+    dm = D.DetintModel(m, n_slots=40)
+    hist = host(dm.generate(prompts, 3))            # [3, 40, V]
+    chain = D.logits_chain(hist[:, 0])
+    assert chain == g["logits_chain"][0][:3]
+    dm1 = D.DetintModel(m, n_slots=1)
+    alone = host(dm1.generate([prompts[39]], 3))
+    np.testing.assert_array_equal(hist[:, 39], alone[:, 0])
+
+
+def test_llama_limbs_batch24_split_k_rows_match(D, llama):
+    """24 decode rows of the 16-bit-limb model (skinny split-K limb GEMMs):
+    rows 0 and 23 equal the same prompts decoded alone."""
+    m = llama
+    V = m.shape.vocab
+    prompts = S.make_prompts(V, 24, 16, 40, 9)
+    dm = D.DetintModel(m, n_slots=24)
+    hist = host(dm.generate(prompts, 3))
+    for r in (0, 23):
+        dm1 = D.DetintModel(m, n_slots=1)
+        alone = host(dm1.generate([prompts[r]], 3))
+        np.testing.assert_array_equal(hist[:, r], alone[:, 0], err_msg=f"row {r}")
+        del dm1
