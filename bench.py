@@ -55,21 +55,23 @@ def timed(fn, n, torch):
 
 def timed_cold(fn, n, torch):
     """Average seconds of one fn launch with the caches flushed before it:
-    a 2 x 512 MiB copy evicts the 256 MB Infinity Cache, and each launch is
-    bracketed by its own HIP events, so the figure is HBM streaming, not
-    cache hits on the previous launch's data."""
-    a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
+    reading a 1 GiB buffer evicts the 256 MB Infinity Cache and the L2s with
+    clean lines (a write flush would leave dirty lines whose write-back
+    during the timed launch halves the read bandwidth it sees; a decode
+    step's caches hold clean weight lines), and each launch is bracketed by
+    its own HIP events, so the figure is HBM streaming, not cache hits on
+    the previous launch's data."""
+    a = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     tot = 0.0
     for _ in range(n):
-        b.copy_(a)
+        a.sum()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         fn()
         e.record()
         torch.cuda.synchronize()
         tot += s.elapsed_time(e) / 1e3
-    del a, b
+    del a
     return tot / n
 
 

@@ -140,17 +140,21 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
   // 1. weight loads for the first group are issued right after the
   //    activation loads below (loads complete in order, so the activations
   //    must go first to be usable while the weights are still in flight)
-  v4i w[CPW][KC];
-  auto load_w = [&](int g) {
+  //    Two groups are kept in flight (a register ring of two buffers),
+  //    with their column mantissas.
+  v4i w[2][CPW][KC];
+  int32_t cmv[2][CPW];
+  auto load_w = [&](int g, int b) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int row = EPI == EPI_SWIGLU ? (c == 0 ? g : N + g) : g * CPW + c;
       const bool rv = EPI == EPI_SWIGLU ? true : row < N;
+      if (EPI != EPI_RAW) cmv[b][c] = rv ? p.col_m[row] : 0;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const int k = kc * 1024 + lane * 16;
         const v4i z = {0, 0, 0, 0};
-        w[c][kc] = (rv && k < K) ? *(const v4i*)(p.W + (size_t)row * K + k) : z;
+        w[b][c][kc] = (rv && k < K) ? *(const v4i*)(p.W + (size_t)row * K + k) : z;
       }
     }
   };
@@ -196,7 +200,9 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
       }
     }
   }
-  if (g < ngroups) load_w(g);  // weights in flight during the prologue arithmetic
+  // weights in flight during the prologue arithmetic
+  if (g < ngroups) load_w(g, 0);
+  if (g + nw < ngroups) load_w(g + nw, 1);
   int64_t Sv[MT], Av[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -291,7 +297,10 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
   const int cc = idx / MT, mm = idx % MT;  // the (column, row) this lane finishes
   int64_t bestk = INT64_MIN;
   const int64_t obase = EPI == EPI_LOGITS && p.out_row_base ? *p.out_row_base : 0;
-  for (; g < ngroups; g += nw) {
+  auto group = [&](int g, int b) {  // b is a constant at each call
+    int32_t cm[CPW];  // this group's mantissas, before buffer b is refilled
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) cm[c] = cmv[b][c];
     int v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = 0;
@@ -303,20 +312,20 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
         for (int m = 0; m < MT; ++m) {
           const v4i x = *(const v4i*)(sx + (size_t)m * K + k);
 #pragma unroll
-          for (int c = 0; c < CPW; ++c) v[c * MT + m] = dot16(x, w[c][kc], v[c * MT + m]);
+          for (int c = 0; c < CPW; ++c) v[c * MT + m] = dot16(x, w[b][c][kc], v[c * MT + m]);
         }
       }
     }
-    const int gn = g + nw;
-    if (gn < ngroups) load_w(gn);  // next group's weights in flight during the epilogue
+    const int gn = g + 2 * nw;
+    if (gn < ngroups) load_w(gn, b);  // two groups ahead, into the buffer just consumed
     const int tot = wave_reduce_t<NV>(v, lane);
     if (EPI == EPI_SWIGLU) {
       const int up = __shfl_xor(tot, 32);  // column 1 (up) sits in the lane 32 apart
       if (leader && cc == 0 && mm < M) {
         const int j = g;
         const int sh = s_k[mm] + p.col_k - p.f_a;
-        const int64_t gv = R((int64_t)tot * s_m[mm] * p.col_m[j], sh);
-        const int64_t uv = R((int64_t)up * s_m[mm] * p.col_m[N + j], sh);
+        const int64_t gv = R((int64_t)tot * s_m[mm] * cm[0], sh);
+        const int64_t uv = R((int64_t)up * s_m[mm] * cm[1], sh);
         ((int64_t*)p.out)[(size_t)mm * N + j] = R(gv * sigmoid_q15(gv, p.Mg, p.Kg), 15) * uv;
       }
     } else if (leader && mm < M) {
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
         if (EPI == EPI_RAW) {
           ((int32_t*)p.out)[(size_t)mm * N + col] = tot;
         } else {
-          const int64_t y = R((int64_t)tot * s_m[mm] * p.col_m[col], s_k[mm] + p.col_k - p.frac);
+          const int64_t y = R((int64_t)tot * s_m[mm] * cm[cc], s_k[mm] + p.col_k - p.frac);
           if (EPI == EPI_FIX) {
             ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)y;
           } else if (EPI == EPI_RES) {
@@ -338,6 +347,10 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
         }
       }
     }
+  };
+  for (; g < ngroups; g += 2 * nw) {
+    group(g, 0);
+    if (g + nw < ngroups) group(g + nw, 1);
   }
   if (EPI == EPI_LOGITS) {
     if (CPW == 2) {
