@@ -136,73 +136,109 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
   const int gw = blockIdx.x * (TPB / 64) + wave, nw = gridDim.x * (TPB / 64);
   const int M = p.M, N = p.N, K = p.K;
   const int ngroups = EPI == EPI_SWIGLU ? N : (N + CPW - 1) / CPW;
+  const int64_t obase = EPI == EPI_LOGITS && p.out_row_base ? *p.out_row_base : 0;
 
-  // 1. weight loads for the first group are issued right after the
-  //    activation loads below (loads complete in order, so the activations
-  //    must go first to be usable while the weights are still in flight)
-  //    Two groups are kept in flight (a register ring of two buffers),
-  //    with their column mantissas.
+  // 1. Loads. Every load below uses a clamped, always-valid address and
+  //    its register is left untouched until all of them are in flight:
+  //    activations first, then the weights of the wave's first two groups
+  //    (a register ring of two buffers, with their column mantissas). Loads
+  //    complete in order, so the prologue arithmetic waits for the
+  //    activations only, and the LDS-only barriers below do not drain the
+  //    weights. Out-of-range elements are zeroed after the loads (inputs) or
+  //    multiply the zero padding of the LDS rows / land in discarded columns
+  //    (weights).
   v4i w[2][CPW][KC];
   int32_t cmv[2][CPW];
+  // weights and mantissas through buffer resources: a group past the end
+  // (and lanes past K) get out-of-range offsets, which read zeros without
+  // touching memory, so no load sits behind a branch
+  const int wrows = EPI == EPI_SWIGLU ? 2 * N : N;
+  const int wbytes = wrows * K;  // < 2^31 and (rows + 2^16) K < 2^32 (checked at launch)
+  const __amdgpu_buffer_rsrc_t wsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.W, (short)0, wbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t csrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.col_m, (short)0, wrows * 4, 0x00020000);
   auto load_w = [&](int g, int b) {
+    // rows of a group past the end fall past the buffer (for SWIGLU the
+    // group index is moved there), lanes past K read a clamped chunk whose
+    // products with the zero padding of the LDS rows vanish; all offsets are
+    // formed before the first load is issued
+    const uint32_t gg = EPI == EPI_SWIGLU && g >= ngroups ? 2u * N : (uint32_t)g;
+    uint32_t roff[CPW], koff[KC];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      roff[c] = EPI == EPI_SWIGLU ? (c == 0 ? gg : N + gg) : gg * CPW + c;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) koff[kc] = (uint32_t)min(kc * 1024 + lane * 16, K - 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int row = EPI == EPI_SWIGLU ? (c == 0 ? g : N + g) : g * CPW + c;
-      const bool rv = EPI == EPI_SWIGLU ? true : row < N;
-      if (EPI != EPI_RAW) cmv[b][c] = rv ? p.col_m[row] : 0;
+      if (EPI != EPI_RAW)
+        cmv[b][c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(csrc, (int)(roff[c] * 4u), 0, 0);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int k = kc * 1024 + lane * 16;
-        const v4i z = {0, 0, 0, 0};
-        w[b][c][kc] = (rv && k < K) ? *(const v4i*)(p.W + (size_t)row * K + k) : z;
-      }
+      for (int kc = 0; kc < KC; ++kc)
+        w[b][c][kc] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)(roff[c] * (uint32_t)K + koff[kc]), 0, 0));
     }
   };
   int g = gw;
 
-  // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
-  //    elements kc * 1024 + 4 t .. + 3 of every row; all of its loads are
-  //    issued together and kept in registers for the quantisation pass.
   typedef int64_t v4l __attribute__((ext_vector_type(4)));
   constexpr bool WIDE_IN = PRO == PRO_DQ64;
+  v4i xr[MT][KC];        // int32 inputs as loaded
+  v4l xw[WIDE_IN ? MT : 1][KC];  // int64 inputs as loaded
+  int2 graw[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const int i = min(kc * 1024 + 4 * tid, K - 4);
+    if (PRO == PRO_NORM) graw[kc] = *(const int2*)(p.gain + i);  // four int16 gains
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mc = m < M ? m : M - 1;
+      if (PRO == PRO_NORM) {
+        const int src = p.row_index ? p.row_index[mc] : mc;
+        xr[m][kc] = *(const v4i*)(p.h + (size_t)src * K + i);
+      } else if (!WIDE_IN) {
+        xr[m][kc] = *(const v4i*)(p.in32 + (size_t)mc * K + i);
+      } else {
+        xw[m][kc] = *(const v4l*)(p.in64 + (size_t)mc * K + i);
+      }
+    }
+  }
+  load_w(g, 0);
+  load_w(g + nw, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
+  //    elements kc * 1024 + 4 t .. + 3 of every row (zero past K, and rows
+  //    past M are zero).
   int64_t xv[MT][KC][4];
   int32_t gv[KC][4];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    const int i = kc * 1024 + 4 * tid;
+    const bool iv = kc * 1024 + 4 * tid < K;
     if (PRO == PRO_NORM) {
-      if (i < K) {
-        const int2 gg = *(const int2*)(p.gain + i);  // four int16 gains
-        gv[kc][0] = (int16_t)(gg.x & 0xFFFF);
-        gv[kc][1] = (int16_t)(gg.x >> 16);
-        gv[kc][2] = (int16_t)(gg.y & 0xFFFF);
-        gv[kc][3] = (int16_t)(gg.y >> 16);
-      } else {
-        gv[kc][0] = gv[kc][1] = gv[kc][2] = gv[kc][3] = 0;
-      }
+      gv[kc][0] = iv ? (int16_t)(graw[kc].x & 0xFFFF) : 0;
+      gv[kc][1] = iv ? (int16_t)(graw[kc].x >> 16) : 0;
+      gv[kc][2] = iv ? (int16_t)(graw[kc].y & 0xFFFF) : 0;
+      gv[kc][3] = iv ? (int16_t)(graw[kc].y >> 16) : 0;
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      if (m < M && i < K) {
-        if (PRO == PRO_NORM) {
-          const int src = p.row_index ? p.row_index[m] : m;
-          const v4i t4 = *(const v4i*)(p.h + (size_t)src * K + i);
-          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
-        } else if (!WIDE_IN) {
-          const v4i t4 = *(const v4i*)(p.in32 + (size_t)m * K + i);
-          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
-        } else {
-          const v4l t4 = *(const v4l*)(p.in64 + (size_t)m * K + i);
-          xv[m][kc][0] = t4.x; xv[m][kc][1] = t4.y; xv[m][kc][2] = t4.z; xv[m][kc][3] = t4.w;
-        }
+      const bool ok = iv && m < M;
+      if (!WIDE_IN) {
+        xv[m][kc][0] = ok ? xr[m][kc].x : 0;
+        xv[m][kc][1] = ok ? xr[m][kc].y : 0;
+        xv[m][kc][2] = ok ? xr[m][kc].z : 0;
+        xv[m][kc][3] = ok ? xr[m][kc].w : 0;
       } else {
-        xv[m][kc][0] = xv[m][kc][1] = xv[m][kc][2] = xv[m][kc][3] = 0;
+        xv[m][kc][0] = ok ? xw[m][kc].x : 0;
+        xv[m][kc][1] = ok ? xw[m][kc].y : 0;
+        xv[m][kc][2] = ok ? xw[m][kc].z : 0;
+        xv[m][kc][3] = ok ? xw[m][kc].w : 0;
       }
     }
   }
-  // weights in flight during the prologue arithmetic
-  if (g < ngroups) load_w(g, 0);
-  if (g + nw < ngroups) load_w(g + nw, 1);
   int64_t Sv[MT], Av[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -229,7 +265,7 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
       sred[wave][2 * r + 1] = At;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole wave)
   for (int r = wave; r < M; r += TPB / 64) {
     int64_t St = 0, At = 0;
@@ -263,65 +299,70 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
       s_e[r] = (PRO == PRO_NORM && St == 0) ? 0 : e;
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // quantised rows, zero-padded to KC * 1024 bytes (the weight loads of
+  // lanes past K read clamped addresses; their products with the padding
+  // are zero)
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if (m < M) {
-      const int e = s_e[m];
+    const int e = s_e[m < M ? m : 0];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int i = kc * 1024 + 4 * tid;
-        if (i < K) {
-          uint32_t packed = 0;
+    for (int kc = 0; kc < KC; ++kc) {
+      const int i = kc * 1024 + 4 * tid;
+      uint32_t packed = 0;
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int64_t v = PRO == PRO_NORM ? xv[m][kc][e4] * gv[kc][e4] : xv[m][kc][e4];
-            // |R(v, e)| <= 128 by the choice of e, so the clamp can run in 32 bits
-            const int32_t q = (int32_t)R_nn(v, e);
-            packed |= (uint32_t)(uint8_t)(q > 127 ? 127 : (q < -127 ? -127 : q)) << (8 * e4);
-          }
-          *(uint32_t*)(sx + (size_t)m * K + i) = packed;
-        }
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t v = PRO == PRO_NORM ? xv[m][kc][e4] * gv[kc][e4] : xv[m][kc][e4];
+        // |R(v, e)| <= 128 by the choice of e, so the clamp can run in 32 bits
+        const int32_t q = (int32_t)R_nn(v, e);
+        packed |= (uint32_t)(uint8_t)(q > 127 ? 127 : (q < -127 ? -127 : q)) << (8 * e4);
       }
+      *(uint32_t*)(sx + (size_t)m * (KC * 1024) + i) = packed;
     }
   }
   if (p.rm_out && blockIdx.x == 0 && tid < M) {
     p.rm_out[tid] = s_m[tid];
     p.rk_out[tid] = s_k[tid];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3. stream the weights: per group, dot products from LDS, reduce, epilogue
   const int idx = reduce_index<NV>(lane);
   const bool leader = (lane & (64 / NV - 1)) == 0;
   const int cc = idx / MT, mm = idx % MT;  // the (column, row) this lane finishes
   int64_t bestk = INT64_MIN;
-  const int64_t obase = EPI == EPI_LOGITS && p.out_row_base ? *p.out_row_base : 0;
-  auto group = [&](int g, int b) {  // b is a constant at each call
+  auto group = [&](int g, int b) {  // b is a constant at each call; g may be past the end
     int32_t cm[CPW];  // this group's mantissas, before buffer b is refilled
 #pragma unroll
     for (int c = 0; c < CPW; ++c) cm[c] = cmv[b][c];
+    // residual value to add to, loaded before the refill below so that
+    // waiting for it does not wait for the refill (clamped address)
+    int32_t old = 0;
+    if (EPI == EPI_RES)
+      old = ((const int32_t*)p.out)[(size_t)(mm < M ? mm : M - 1) * N + min(g * CPW + cc, N - 1)];
     int v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = 0;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const int k = kc * 1024 + lane * 16;
-      if (k < K) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const v4i x = *(const v4i*)(sx + (size_t)m * K + k);
+      for (int m = 0; m < MT; ++m) {
+        const v4i x = *(const v4i*)(sx + (size_t)m * (KC * 1024) + k);
 #pragma unroll
-          for (int c = 0; c < CPW; ++c) v[c * MT + m] = dot16(x, w[b][c][kc], v[c * MT + m]);
-        }
+        for (int c = 0; c < CPW; ++c) v[c * MT + m] = dot16(x, w[b][c][kc], v[c * MT + m]);
       }
     }
-    const int gn = g + 2 * nw;
-    if (gn < ngroups) load_w(gn, b);  // two groups ahead, into the buffer just consumed
+    // two groups ahead, into the buffer just consumed (kept apart from the
+    // dot products so the loads reuse its registers: a copy would have to
+    // wait for them)
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(g + 2 * nw, b);
+    __builtin_amdgcn_sched_barrier(0);
     const int tot = wave_reduce_t<NV>(v, lane);
     if (EPI == EPI_SWIGLU) {
       const int up = __shfl_xor(tot, 32);  // column 1 (up) sits in the lane 32 apart
-      if (leader && cc == 0 && mm < M) {
+      if (leader && cc == 0 && mm < M && g < ngroups) {
         const int j = g;
         const int sh = s_k[mm] + p.col_k - p.f_a;
         const int64_t gv = R((int64_t)tot * s_m[mm] * cm[0], sh);
@@ -338,7 +379,7 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
           if (EPI == EPI_FIX) {
             ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)y;
           } else if (EPI == EPI_RES) {
-            ((int32_t*)p.out)[(size_t)mm * N + col] += (int32_t)y;
+            ((int32_t*)p.out)[(size_t)mm * N + col] = old + (int32_t)y;
           } else {
             ((int32_t*)p.out)[(size_t)(obase + mm) * N + col] = (int32_t)y;
             const int64_t key = amax_key(y, col);
@@ -348,9 +389,12 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
       }
     }
   };
+  // both calls unconditional (the second group may be past the end: its
+  // loads read zeros and its results are dropped), so the loop body is
+  // straight-line code and the wait for a buffer counts only older loads
   for (; g < ngroups; g += 2 * nw) {
     group(g, 0);
-    if (g + nw < ngroups) group(g + nw, 1);
+    group(g + nw, 1);
   }
   if (EPI == EPI_LOGITS) {
     if (CPW == 2) {
@@ -370,10 +414,14 @@ template <int MT, int CPW, int PRO, int EPI>
 hipError_t launch_kc(const FG& p, hipStream_t st) {
   const int64_t groups = EPI == EPI_SWIGLU ? p.N : (p.N + CPW - 1) / CPW;
   const int blocks = cap_blocks(groups);
-  const size_t lds = (size_t)MT * p.K;
+  // weight offsets are 32-bit buffer offsets; those of groups up to two
+  // rounds past the end (at most 2^16 rows) must not wrap
+  if ((int64_t)(EPI == EPI_SWIGLU ? 2 : 1) * p.N * p.K >= (int64_t(1) << 31) || p.K > 8192)
+    return hipErrorInvalidValue;
   const int kc = (p.K + 1023) / 1024;
 #define DETINT_KC(KK)                                                         \
   if (kc <= KK) {                                                             \
+    const size_t lds = (size_t)MT * KK * 1024;                                \
     fgemv<MT, CPW, KK, PRO, EPI><<<blocks, TPB, lds, st>>>(p);                \
     return hipGetLastError();                                                 \
   }

@@ -266,6 +266,17 @@ __device__ __forceinline__ int64_t block_max(int64_t v, int64_t* red) {
   return t;
 }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads also drains
+// every outstanding global load of the wave (vmcnt(0)); this one waits for
+// the wave's LDS (and scalar) operations alone, so global loads issued before
+// it - weights streamed ahead of their use - stay in flight across it. The
+// compiler still waits for those loads before their registers are used.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // DQ exponent from the absolute maximum: e = max(0, bitlen(A) - 7).
 __device__ __forceinline__ int dq_exp(uint64_t A) {
   const int b = bitlen64(A);
