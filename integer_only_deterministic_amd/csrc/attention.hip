@@ -36,6 +36,28 @@ __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
   return c;
 }
 
+// Transposed partial reduction of N int32 values per lane over the lane
+// offsets O, O/2, ..., OMIN: each step keeps half of the values and adds the
+// partner's copy of them, so N - N / 2^steps exchanges replace
+// N * steps. Afterwards lane l holds, in v[0 .. N / (64 / OMIN)), the totals
+// (over the lanes that differ from l in those offset bits) of value indices
+// base(l) + i, base(l) = sum over steps of bit(l, O_s) * N / 2^(s+1).
+template <int N, int O, int OMIN>
+struct HalveTo {
+  __device__ __forceinline__ static void run(int* v, int lane) {
+    if constexpr (O >= OMIN && N > 1) {
+      const bool upper = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const int keep = upper ? v[i + N / 2] : v[i];
+        const int give = upper ? v[i] : v[i + N / 2];
+        v[i] = keep + __shfl_xor(give, O);
+      }
+      HalveTo<N / 2, O / 2, OMIN>::run(v, lane);
+    }
+  }
+};
+
 __device__ __forceinline__ void row_info(const RowMap& m, int r, int& pos, int& slot) {
   if (m.cu) {
     int lo = 0, hi = m.S - 1;  // last s with cu[s] <= r
@@ -209,44 +231,313 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
   attend<D, G>(sq, seq, kc + base, vc + base, pos + 1, max_pos, Ms, Ks, orow, sc, red, sred);
 }
 
-// Decode: one row per sequence. The workgroup of (row, KV head) first does
-// the QKV post-processing of its own heads (G query heads -> q8 in LDS, the
-// key and value -> int8 into the cache at the row's position), then attends
-// over positions 0..pos, which include the key it just wrote.
-template <int D, int G>
+// Decode: one row per sequence. The workgroup of (row, KV head) does the QKV
+// post-processing of its own heads (G query heads -> q8 in LDS, the new key
+// and value -> int8 into the cache at the row's position and into LDS), then
+// attends over positions 0..pos. The row position is the only input the
+// cached rows 0..pos-1 depend on, so their first PRE keys and values are
+// loaded into registers before the post-processing (its own loads go first:
+// loads complete in order) and arrive while it computes; the new row at pos
+// is taken from LDS. Later cached rows, if any, are streamed as in `attend`.
+// Same passes and the same integer results as `attend`.
+// (qkv is not __restrict__: loads through a restrict-qualified read-only
+// pointer may be sunk to their first use, past the cache loads)
+template <int D, int G, bool QKN>
 __global__ __launch_bounds__(TPB) void attn_decode_fused(
-    const int32_t* __restrict__ qkv, QkvPost p, const int32_t* __restrict__ start_pos,
+    const int32_t* qkv, QkvPost p, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ slot_arr, int nq, int nkv, int n_slots, int max_pos,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, int32_t Ms, int32_t Ks,
     int32_t* __restrict__ out) {
-  constexpr int CH = D / 16;
-  extern __shared__ int32_t sc[];
+  constexpr int CH = D / 16;              // 16-byte chunks per row
+  constexpr int NW = TPB / 64;
+  constexpr int PRE = G <= 2 ? 768 : 512; // cached rows loaded up front
+  constexpr int KU = PRE / TPB;           // key rows per thread (one row each)
+  constexpr int RG = TPB / CH;            // value rows per pass-4 step
+  constexpr int VU = PRE / RG;            // value chunks per thread
+  constexpr int NH = G + 2;               // heads post-processed here
+  constexpr int HR = (NH + NW - 1) / NW;  // rounds of NW waves
+  constexpr int half = D / 2;
+  extern __shared__ int32_t sc[];         // [G][max_pos]: scores -> E
   __shared__ v4i sq[G * CH];
+  __shared__ v4i snew[2 * CH];            // new key row, new value row (int8)
   __shared__ int32_t seq[G];
-  __shared__ int64_t red[16];
-  constexpr int DEC_NT = TPB;
-  __shared__ int32_t sred[DEC_NT / 64][G * D];
-  const int r = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+  __shared__ int64_t rmax[NW][G], rsum[NW][G], rnv[G];
+  __shared__ int32_t sred[NW][G * D];
+  const int r = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
+            wave = tid >> 6;
   const int h0 = kvh * G;
+
+  // 1. loads of the post-processing, which do not depend on the row's
+  //    position: per head this wave handles, lane i < d/2 holds elements i
+  //    and i + d/2 (addresses clamped, lanes past d/2 idle)
+  const int nh = nq + 2 * nkv;
+  const int32_t* row = qkv + (size_t)r * nh * D;
+  const bool act = lane < half;
+  const int jl = act ? lane : 0;
+  int32_t hx0[HR], hx1[HR], hm0[HR], hm1[HR], hg0[HR], hg1[HR];
+#pragma unroll
+  for (int u = 0; u < HR; ++u) {
+    const int t = min(wave + NW * u, NH - 1);
+    const int hh = t < G ? h0 + t : (t == G ? nq + kvh : nq + nkv + kvh);
+    const int c0 = hh * D;
+    hx0[u] = row[c0 + jl];
+    hx1[u] = row[c0 + jl + half];
+    if (QKN) {
+      hm0[u] = p.col_m[c0 + jl];
+      hm1[u] = p.col_m[c0 + jl + half];
+      const int16_t* gn = t < G ? p.q_norm : p.k_norm;
+      hg0[u] = gn[jl];
+      hg1[u] = gn[jl + half];
+    }
+  }
+  const int32_t rm = QKN ? p.row_m[r] : 0, rk = QKN ? p.row_k[r] : 0;
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ones below
   const int pos = start_pos[r], slot = slot_arr[r];
   int32_t* orow = out + ((size_t)r * nq + h0) * D;
   if (pos < 0 || pos >= max_pos || slot < 0 || slot >= n_slots) {
-    for (int t = tid; t < G * D; t += DEC_NT) orow[t] = 0;
+    for (int t = tid; t < G * D; t += TPB) orow[t] = 0;
     return;
   }
-  const int nh = nq + 2 * nkv;
-  const int32_t* row = qkv + (size_t)r * nh * D;
-  const int32_t rm = p.qk_norm ? p.row_m[r] : 0, rk = p.qk_norm ? p.row_k[r] : 0;
-  for (int t = wave; t < G + 2; t += DEC_NT / 64) {
-    const int hh = t < G ? h0 + t : (t == G ? nq + kvh : nq + nkv + kvh);
-    int8_t* qd = (int8_t*)sq + (t < G ? t : 0) * D;
-    qkv_head(row, hh, nq, nkv, D, pos, slot, true, rm, rk, p, qd, &seq[t < G ? t : 0], kc, vc,
-             max_pos);
-  }
-  __syncthreads();
+  const int nold = pos, ctx = pos + 1, ld = max_pos;
+  const int64_t cs = p.cos_t[(size_t)pos * half + jl], sn = p.sin_t[(size_t)pos * half + jl];
+  asm volatile("" ::: "memory");
+
+  // 2. cached keys and values 0..min(pos, PRE)-1 into registers; rows past
+  //    them read zeros without touching memory (out-of-range offsets)
   const size_t base = ((size_t)slot * nkv + kvh) * max_pos * D;
-  attend<D, G, DEC_NT>(sq, seq, kc + base, vc + base, pos + 1, max_pos, Ms, Ks, orow, sc, red,
-                          sred);
+  const int cbytes = max_pos * D;
+  const __amdgpu_buffer_rsrc_t rsk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, cbytes, 0x00020000);
+  const int c = tid % CH, rg = tid / CH;
+  v4i kpre[KU][CH], vpre[VU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int j = tid + u * TPB;
+    const int off = j < nold ? j * D : cbytes;
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc)
+      kpre[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int j = rg + u * RG;
+    vpre[u] = __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. post-processing (the integer steps of qkv_head): q -> q8, e_q (LDS);
+  //    k, v -> int8 at the cache scales, into the cache and LDS
+  int8_t* snk = (int8_t*)snew;
+  int8_t* snv = (int8_t*)snew + D;
+#pragma unroll
+  for (int u = 0; u < HR; ++u) {
+    const int t = wave + NW * u;
+    if (t >= NH) break;
+    const int j0 = lane, j1 = lane + half;
+    if (t == G + 1) {  // value head
+      const int c0 = (nq + nkv + kvh) * D;
+      int8_t* dst = vc + base + (size_t)pos * D;
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        int64_t vf = e2 ? hx1[u] : hx0[u];
+        if (QKN) vf = R(vf * rm * (e2 ? hm1[u] : hm0[u]), rk + p.col_k - p.f_n);
+        const int8_t v8 = clamp8(R(vf * p.vq_m, p.vq_k));
+        if (act) {
+          dst[e2 ? j1 : j0] = v8;
+          snv[e2 ? j1 : j0] = v8;
+        }
+      }
+      (void)c0;
+      continue;
+    }
+    int64_t x0 = act ? hx0[u] : 0, x1 = act ? hx1[u] : 0;
+    if (QKN) {
+      int64_t a0 = act ? x0 * hm0[u] : 0, a1 = act ? x1 * hm1[u] : 0;
+      const uint64_t u0 = uabs64(a0), u1 = uabs64(a1);
+      const int b = bitlen64(wave_max_u(u0 > u1 ? u0 : u1));
+      const int sh0 = b > 24 ? b - 24 : 0;
+      a0 = R(a0, sh0);
+      a1 = R(a1, sh0);
+      const int64_t S = wave_sum(a0 * a0 + a1 * a1);
+      if (S == 0) {
+        x0 = x1 = 0;
+      } else {
+        int32_t m, sh;
+        irms_wave(S, D, m, sh);
+        x0 = R(a0 * hg0[u] * m, sh + 12 - p.f_n);
+        x1 = R(a1 * hg1[u] * m, sh + 12 - p.f_n);
+      }
+    }
+    const int64_t y0 = act ? R(x0 * cs - x1 * sn, 14) : 0;
+    const int64_t y1 = act ? R(x1 * cs + x0 * sn, 14) : 0;
+    if (t < G) {
+      const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
+      const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
+      int8_t* qd = (int8_t*)sq + t * D;
+      if (act) {
+        qd[j0] = clamp8(R(y0, e));
+        qd[j1] = clamp8(R(y1, e));
+      }
+      if (lane == 0) seq[t] = e;
+    } else if (act) {  // key head
+      int8_t* dst = kc + base + (size_t)pos * D;
+      const int8_t k0 = clamp8(R(y0 * p.kq_m, p.kq_k)), k1 = clamp8(R(y1 * p.kq_m, p.kq_k));
+      dst[j0] = k0;
+      dst[j1] = k1;
+      snk[j0] = k0;
+      snk[j1] = k1;
+    }
+  }
+  lds_barrier();
+
+  // 4. pass 1: scores into LDS, per-head maxima
+  int64_t mx[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) mx[g] = INT64_MIN;
+  auto score = [&](const v4i (&kv)[CH], int j) {
+    int s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = 0;
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = dot16(sq[g * CH + cc], kv[cc], s[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      sc[g * ld + j] = s[g];
+      mx[g] = s[g] > mx[g] ? s[g] : mx[g];
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < KU; ++u)
+    if (tid + u * TPB < nold) score(kpre[u], tid + u * TPB);
+  {
+    int j1 = tid + PRE;
+    for (; j1 + 3 * TPB < nold; j1 += 4 * TPB) {  // four cached rows in flight
+      v4i kk[4][CH];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc) kk[u][cc] = ((const v4i*)(kc + base + (size_t)(j1 + u * TPB) * D))[cc];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) score(kk[u], j1 + u * TPB);
+    }
+    for (; j1 < nold; j1 += TPB) {
+      v4i ka[CH];
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) ka[cc] = ((const v4i*)(kc + base + (size_t)j1 * D))[cc];
+      score(ka, j1);
+    }
+  }
+  if (tid == TPB - 1) {  // the new key
+    v4i kn[CH];
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) kn[cc] = snew[cc];
+    score(kn, pos);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t m = wave_max(mx[g]);
+    if (lane == 0) rmax[wave][g] = m;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    int64_t m = rmax[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = rmax[w][g] > m ? rmax[w][g] : m;
+    mx[g] = m;
+  }
+
+  // 5. pass 2: exponentials in place and their sums; 2^46 / D per head
+  int64_t den[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) den[g] = 0;
+  for (int j = tid; j < ctx; j += TPB) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int32_t E = diexp(R(((int64_t)sc[g * ld + j] - mx[g]) * Ms, Ks - seq[g]));
+      sc[g * ld + j] = E;
+      den[g] += E;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t d = wave_sum(den[g]);
+    if (lane == 0) rsum[wave][g] = d;
+  }
+  lds_barrier();
+  for (int g = wave; g < G; g += NW) {  // one head per wave, in parallel
+    int64_t d = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) d += rsum[w][g];
+    const int64_t q = (int64_t)udiv_wave<32>(uint64_t(1) << 46, (uint64_t)d);  // D >= 2^15
+    if (lane == 0) rnv[g] = q;
+  }
+  lds_barrier();
+  int64_t rn[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) rn[g] = rnv[g];
+
+  // 6. passes 3+4: P = min(R(E rn, 31), 2^15 - 1) and P.V; lane owns a
+  //    16-byte chunk c of value rows rg, rg + RG, ...
+  int acc[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int b = 0; b < 16; ++b) acc[g][b] = 0;
+  auto pv = [&](const v4i& v, int j) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t pp = R((int64_t)sc[g * ld + j] * rn[g], 31);
+      const int P = (int)(pp > 32767 ? 32767 : pp);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[g][b] += P * sbyte(v.x, b);
+        acc[g][4 + b] += P * sbyte(v.y, b);
+        acc[g][8 + b] += P * sbyte(v.z, b);
+        acc[g][12 + b] += P * sbyte(v.w, b);
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < VU; ++u)
+    if (rg + u * RG < nold) pv(vpre[u], rg + u * RG);
+  {
+    constexpr int SU = 8;
+    int j = rg + PRE;
+    for (; j + (SU - 1) * RG < nold; j += SU * RG) {  // SU value rows in flight
+      v4i vv[SU];
+#pragma unroll
+      for (int u = 0; u < SU; ++u) vv[u] = *(const v4i*)(vc + base + (size_t)(j + u * RG) * D + c * 16);
+#pragma unroll
+      for (int u = 0; u < SU; ++u) pv(vv[u], j + u * RG);
+    }
+    for (; j < nold; j += RG) pv(*(const v4i*)(vc + base + (size_t)j * D + c * 16), j);
+  }
+  if (rg == RG - 1) pv(snew[CH + c], pos);  // the new value row
+  // reduce over the 64 / CH lanes of a wave that share chunk c, transposed:
+  // each halving step sends half of the values to the partner lane, so lane
+  // l ends with NV / (64 / CH) totals, value indices (l / CH) NV CH / 64 + i;
+  // then over waves through LDS
+  constexpr int NV = 16 * G, NL = NV * CH / 64;
+  int* av = &acc[0][0];
+  HalveTo<NV, 32, CH>::run(av, lane);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int vi = (lane / CH) * NL + i, g = vi / 16, b = vi % 16;
+    sred[wave][g * D + c * 16 + b] = av[i];
+  }
+  lds_barrier();
+  for (int t = tid; t < G * D; t += TPB) {
+    int s2 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s2 += sred[w][t];
+    orow[t] = s2;
+  }
 }
 
 // ------------------------------------------------------ prefill on MFMA
@@ -589,12 +880,18 @@ hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* s
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_decode_fused<D, G>,
+    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, true>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr_set = true;
   }
-  attn_decode_fused<D, G><<<dim3((unsigned)B, (unsigned)nkv), TPB, lds, st>>>(
-      qkv, p, start_pos, slot, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, kc, vc, M, K, out);
+  if (p.qk_norm)
+    attn_decode_fused<D, G, true><<<dim3((unsigned)B, (unsigned)nkv), TPB, lds, st>>>(
+        qkv, p, start_pos, slot, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, kc, vc, M, K, out);
+  else
+    attn_decode_fused<D, G, false><<<dim3((unsigned)B, (unsigned)nkv), TPB, lds, st>>>(
+        qkv, p, start_pos, slot, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, kc, vc, M, K, out);
   return hipGetLastError();
 }
 

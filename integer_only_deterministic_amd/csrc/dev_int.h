@@ -129,38 +129,50 @@ __device__ __forceinline__ void irms(int64_t S, int64_t n, int32_t& m, int32_t& 
 // test is monotone in l, so the highest passing lane (ballot + clz) gives the
 // digit. About 6 rounds replace 31-47 dependent serial steps.
 
-// floor(sqrt(u)) for u < 2^64.
+// A wave-uniform 64-bit value moved to scalar registers, so that the
+// bookkeeping below runs on the scalar unit.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// floor(sqrt(u)) for u < 2^64: six rounds at fixed digit positions 30, 24,
+// ..., 0 (a round above the root's top bit finds digit 0), branch-free. In
+// the first round only candidates below 2^32 (lanes 0..3) take part.
 __device__ __forceinline__ uint64_t isqrt_wave(uint64_t u) {
-  const uint64_t lane = threadIdx.x & 63;
-  const int nb = (bitlen64(u) + 1) >> 1;  // bits of the root
-  uint64_t r = 0;
-  for (int s = ((nb - 1) / 6) * 6; s >= 0; s -= 6) {
-    const uint64_t c = r | (lane << s);
-    const bool ok = c < (uint64_t(1) << 32) && c * c <= u;
-    const uint64_t mask = __ballot(ok);
-    r |= (uint64_t)(63 - __builtin_clzll(mask)) << s;
+  const uint32_t lane = threadIdx.x & 63;
+  u = uniform64(u);
+  uint32_t r = 0;
+#pragma unroll
+  for (int s = 30; s >= 0; s -= 6) {
+    const uint32_t c = r | (lane << s);  // exact for the lanes that take part
+    const bool ok = (s < 30 || lane < 4) & ((uint64_t)c * c <= u);
+    r |= (uint32_t)(63 - __builtin_clzll(__ballot(ok))) << s;
   }
   return r;
 }
 
 // floor(n / d), d > 0, when the quotient is known to be below 2^QB and
-// 2^QB * d < 2^64 (so every candidate product fits 64 bits).
+// 2^QB * d < 2^64 (so every candidate product fits 64 bits); branch-free.
 template <int QB>
 __device__ __forceinline__ uint64_t udiv_wave(uint64_t n, uint64_t d) {
   const uint64_t lane = threadIdx.x & 63;
+  n = uniform64(n);
+  d = uniform64(d);
   uint64_t q = 0;
 #pragma unroll
   for (int s = ((QB - 1) / 6) * 6; s >= 0; s -= 6) {
     const uint64_t c = q | (lane << s);
-    const bool ok = c < (uint64_t(1) << QB) && c * d <= n;
-    const uint64_t mask = __ballot(ok);
-    q |= (uint64_t)(63 - __builtin_clzll(mask)) << s;
+    const bool ok = (QB - s >= 6 || lane < (uint64_t(1) << (QB - s))) & (c * d <= n);
+    q |= (uint64_t)(63 - __builtin_clzll(__ballot(ok))) << s;
   }
   return q;
 }
 
 // irms (see above) by a whole wave.
 __device__ __forceinline__ void irms_wave(int64_t S, int64_t n, int32_t& m, int32_t& sh) {
+  S = (int64_t)uniform64((uint64_t)S);
   const int b = bitlen64((uint64_t)S);
   const int c = b < 62 ? (62 - b) >> 1 : 0;
   const uint64_t num = (uint64_t)S << (2 * c);

@@ -168,6 +168,27 @@ def test_rmsnorm(D, R, n):
     np.testing.assert_array_equal(host(k), ok)
 
 
+@pytest.mark.parametrize("n", [64, 128, 768, 1024, 2048])
+def test_rmsnorm_magnitudes(D, n):
+    """The integer square root and divisions of irms over the whole range of
+    row magnitudes: row i is scaled to about 2^(i % 26), some rows hold a
+    single nonzero element, some sit at the +-2^25 residual bound."""
+    R = 416
+    rng = np.random.default_rng(n + 7)
+    h = rng.integers(-(1 << 25) + 1, 1 << 25, (R, n)).astype(np.int64)
+    for i in range(R):
+        h[i] >>= 25 - (i % 26)
+    h[::7, 1:] = 0                                   # one nonzero element
+    h[3::11] = rng.choice([-(1 << 25) + 1, (1 << 25) - 1], (len(h[3::11]), n))
+    h = h.astype(np.int32)
+    g = rng.integers(1 << 12, (1 << 13) + 1, n).astype(np.int16)
+    x8, m, k = D.detint_rmsnorm(dev(h), dev(g))
+    ox, om, ok = O.rmsnorm(h, g)
+    np.testing.assert_array_equal(host(m), om)
+    np.testing.assert_array_equal(host(k), ok)
+    np.testing.assert_array_equal(host(x8), ox)
+
+
 @pytest.mark.parametrize("R,n", [(1, 2048), (9, 512), (70, 4096)])
 def test_requant(D, R, n):
     rng = np.random.default_rng(R + n)
