@@ -239,7 +239,10 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
 // loaded into registers before the post-processing (its own loads go first:
 // loads complete in order) and arrive while it computes; the new row at pos
 // is taken from LDS. Later cached rows, if any, are streamed as in `attend`.
-// Same passes and the same integer results as `attend`.
+// Same passes and the same integer results as `attend`. A workgroup takes G
+// of the gq query heads that share a KV head (G = gq, or G = 1 to spread a
+// small batch over more CUs; the key and value rows are then written by
+// each of the gq workgroups, with identical bytes).
 // (qkv is not __restrict__: loads through a restrict-qualified read-only
 // pointer may be sunk to their first use, past the cache loads)
 template <int D, int G, bool QKN>
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
     const int32_t* qkv, QkvPost p, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ slot_arr, int nq, int nkv, int n_slots, int max_pos,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, int32_t Ms, int32_t Ks,
-    int32_t* __restrict__ out) {
+    int32_t* __restrict__ out, int gq) {
   constexpr int CH = D / 16;              // 16-byte chunks per row
   constexpr int NW = TPB / 64;
   constexpr int PRE = G <= 2 ? 768 : 512; // cached rows loaded up front
@@ -263,9 +266,8 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   __shared__ int32_t seq[G];
   __shared__ int64_t rmax[NW][G], rsum[NW][G], rnv[G];
   __shared__ int32_t sred[NW][G * D];
-  const int r = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
-            wave = tid >> 6;
-  const int h0 = kvh * G;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h0 = blockIdx.y * G, kvh = h0 / gq;
 
   // 1. loads of the post-processing, which do not depend on the row's
   //    position: per head this wave handles, lane i < d/2 holds elements i
@@ -873,7 +875,7 @@ hipError_t launch_t(const int8_t* q8, const int32_t* e_q, const int8_t* kc, cons
 }
 
 template <int D, int G>
-hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
+hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
                           const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
                           hipStream_t st) {
@@ -886,13 +888,33 @@ hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* s
                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr_set = true;
   }
+  const dim3 grid((unsigned)B, (unsigned)(nq / G));
+  const int gq = (int)(nq / nkv);
   if (p.qk_norm)
-    attn_decode_fused<D, G, true><<<dim3((unsigned)B, (unsigned)nkv), TPB, lds, st>>>(
-        qkv, p, start_pos, slot, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, kc, vc, M, K, out);
+    attn_decode_fused<D, G, true><<<grid, TPB, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
+                                                         (int)n_slots, (int)max_pos, kc, vc, M, K,
+                                                         out, gq);
   else
-    attn_decode_fused<D, G, false><<<dim3((unsigned)B, (unsigned)nkv), TPB, lds, st>>>(
-        qkv, p, start_pos, slot, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, kc, vc, M, K, out);
+    attn_decode_fused<D, G, false><<<grid, TPB, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
+                                                          (int)n_slots, (int)max_pos, kc, vc, M, K,
+                                                          out, gq);
   return hipGetLastError();
+}
+
+// A workgroup per (row, KV head) when that fills the GPU reasonably, else
+// one per (row, query head): a batch-1 step has only n_kv workgroups'
+// worth of work and is latency-bound, so halving or quartering each
+// workgroup's arithmetic matters more than reading the cache rows once.
+template <int D, int G>
+hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
+                          const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
+                          int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
+                          hipStream_t st) {
+  if (G > 1 && B * nkv < 64)
+    return launch_fused_g<D, 1>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M, K,
+                                out, st);
+  return launch_fused_g<D, G>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M, K,
+                              out, st);
 }
 
 }  // namespace

@@ -360,7 +360,19 @@ __global__ __launch_bounds__(TPB) void fgemv(FG p) {
     load_w(g + 2 * nw, b);
     __builtin_amdgcn_sched_barrier(0);
     const int tot = wave_reduce_t<NV>(v, lane);
-    if (EPI == EPI_SWIGLU) {
+    if (EPI == EPI_SWIGLU && MT == 1) {
+      // one row: the gate total sits in lanes 0..31, the up total in lanes
+      // 32..63; the whole wave computes the (uniform) epilogue
+      const int gt = __builtin_amdgcn_readfirstlane(tot);
+      const int ut = __builtin_amdgcn_readlane(tot, 32);
+      if (g < ngroups) {
+        const int sh = s_k[0] + p.col_k - p.f_a;
+        const int64_t gv = R((int64_t)gt * s_m[0] * cm[0], sh);
+        const int64_t uv = R((int64_t)ut * s_m[0] * cm[1], sh);
+        const int64_t res = R(gv * sigmoid_q15_wave(gv, p.Mg, p.Kg), 15) * uv;
+        if (lane == 0) ((int64_t*)p.out)[g] = res;
+      }
+    } else if (EPI == EPI_SWIGLU) {
       const int up = __shfl_xor(tot, 32);  // column 1 (up) sits in the lane 32 apart
       if (leader && cc == 0 && mm < M && g < ngroups) {
         const int j = g;
