@@ -508,10 +508,19 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   }
   QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
              L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
-  LAUNCH(launch_qkv_post(qkv, R, nq, nkv, hd, pos_of, slot_of, qp, q8, eq, kc, vc, n_slots,
-                         d.max_pos, st));
-  LAUNCH(launch_attention_seqs(q8, eq, kc, vc, seqs, R, max_seqlen, nq, nkv, hd, n_slots,
-                               d.max_pos, m->sm_m[l], m->sm_k[l], att, st));
+  if (max_seqlen == 1 && seqs.cu && (int64_t)seqs.S == R) {
+    // one row per sequence (decode rows): post-processing fused into the
+    // attention kernel, which reads row r's position and slot from
+    // start[r] and seq_slot[r]
+    LAUNCH(launch_attention_decode_fused(qkv, qp, seqs.start, seqs.seq_slot, R, nq, nkv, hd,
+                                         n_slots, d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att,
+                                         st));
+  } else {
+    LAUNCH(launch_qkv_post(qkv, R, nq, nkv, hd, pos_of, slot_of, qp, q8, eq, kc, vc, n_slots,
+                           d.max_pos, st));
+    LAUNCH(launch_attention_seqs(q8, eq, kc, vc, seqs, R, max_seqlen, nq, nkv, hd, n_slots,
+                                 d.max_pos, m->sm_m[l], m->sm_k[l], att, st));
+  }
   LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
   {
     Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr};

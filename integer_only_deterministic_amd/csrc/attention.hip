@@ -416,22 +416,33 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
 #pragma unroll
   for (int u = 0; u < KU; ++u)
     if (tid + u * TPB < nold) score(kpre[u], tid + u * TPB);
-  {
-    int j1 = tid + PRE;
-    for (; j1 + 3 * TPB < nold; j1 += 4 * TPB) {  // four cached rows in flight
-      v4i kk[4][CH];
+  if (PRE < nold) {
+    // later cached keys in batches of SK rows per thread, two batches in
+    // flight (rows past pos read zeros and are skipped); the loop body is
+    // straight-line so each wait counts only the older batch
+    constexpr int SK = D == 64 ? 4 : 2;
+    v4i ka[SK][CH], kb[SK][CH];
+    auto kload = [&](v4i (&kr)[SK][CH], int b0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < SK; ++u) {
+        const int j = b0 + tid + u * TPB;
+        const int off = j < nold ? j * D : cbytes;
 #pragma unroll
-        for (int cc = 0; cc < CH; ++cc) kk[u][cc] = ((const v4i*)(kc + base + (size_t)(j1 + u * TPB) * D))[cc];
+        for (int cc = 0; cc < CH; ++cc)
+          kr[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
+      }
+    };
+    auto kuse = [&](v4i (&kr)[SK][CH], int b0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) score(kk[u], j1 + u * TPB);
-    }
-    for (; j1 < nold; j1 += TPB) {
-      v4i ka[CH];
-#pragma unroll
-      for (int cc = 0; cc < CH; ++cc) ka[cc] = ((const v4i*)(kc + base + (size_t)j1 * D))[cc];
-      score(ka, j1);
+      for (int u = 0; u < SK; ++u)
+        if (b0 + tid + u * TPB < nold) score(kr[u], b0 + tid + u * TPB);
+    };
+    kload(ka, PRE);
+    for (int b0 = PRE; b0 < nold; b0 += 2 * SK * TPB) {
+      kload(kb, b0 + SK * TPB);
+      kuse(ka, b0);
+      kload(ka, b0 + 2 * SK * TPB);
+      kuse(kb, b0 + SK * TPB);
     }
   }
   if (tid == TPB - 1) {  // the new key
@@ -508,17 +519,29 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
 #pragma unroll
   for (int u = 0; u < VU; ++u)
     if (rg + u * RG < nold) pv(vpre[u], rg + u * RG);
-  {
+  if (PRE < nold) {  // later cached values, as the keys: SU rows per batch, two in flight
     constexpr int SU = 8;
-    int j = rg + PRE;
-    for (; j + (SU - 1) * RG < nold; j += SU * RG) {  // SU value rows in flight
-      v4i vv[SU];
+    v4i va[SU], vb[SU];
+    auto vload = [&](v4i (&vr)[SU], int b0) {
 #pragma unroll
-      for (int u = 0; u < SU; ++u) vv[u] = *(const v4i*)(vc + base + (size_t)(j + u * RG) * D + c * 16);
+      for (int u = 0; u < SU; ++u) {
+        const int j = b0 + rg + u * RG;
+        vr[u] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
+      }
+    };
+    auto vuse = [&](v4i (&vr)[SU], int b0) {
 #pragma unroll
-      for (int u = 0; u < SU; ++u) pv(vv[u], j + u * RG);
+      for (int u = 0; u < SU; ++u)
+        if (b0 + rg + u * RG < nold) pv(vr[u], b0 + rg + u * RG);
+    };
+    vload(va, PRE);
+    for (int b0 = PRE; b0 < nold; b0 += 2 * SU * RG) {
+      vload(vb, b0 + SU * RG);
+      vuse(va, b0);
+      vload(va, b0 + 2 * SU * RG);
+      vuse(vb, b0 + SU * RG);
     }
-    for (; j < nold; j += RG) pv(*(const v4i*)(vc + base + (size_t)j * D + c * 16), j);
   }
   if (rg == RG - 1) pv(snew[CH + c], pos);  // the new value row
   // reduce over the 64 / CH lanes of a wave that share chunk c, transposed:

@@ -29,6 +29,7 @@
 // acc64 = 256 * (A.hi) + (A.lo') + 128 * rowsum(A).
 #include "dev_int.h"
 #include "internal.h"
+#include <type_traits>
 
 namespace detint {
 namespace {
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   // [0, 2^15) and every shift in [1, 62] (int8 weights) or [32, 94] (limbs);
   // anything else takes the general per-element path below.
   const int csh = e.col_k - (MODE == MODE_REQ_I8 ? 0 : e.frac);
-  int slow = 0;
+  int slow = 0, narrow = 0;
   if (MODE != MODE_RAW) {
     for (int t = tid; t < BM; t += 256) {
       const int i = min(m0 + t, M - 1);
@@ -403,11 +404,16 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
       s_rm[t] = rm;
       s_rk[t] = sh;
       slow |= (unsigned)rm >= 32768u || (WIDE ? sh < 32 || sh > 94 : sh < 1 || sh > 62);
+      narrow |= sh < 33;
     }
     for (int t = tid; t < BN; t += 256) slow |= (unsigned)e.col_m[min(n0 + t, N - 1)] >= 32768u;
   }
   const int64_t obase = e.out_row_base ? *e.out_row_base : 0;
   slow = __syncthreads_or(slow);
+  // int8 weights with every shift >= 33: R(p, s) = (hi(p) + 2^(s-33)) >> (s-32)
+  // exactly, hi(p) the upper 32 bits of the 64-bit product p (the low word
+  // cannot carry into the floor), so the product needs one mul_hi
+  const bool hi_only = !WIDE && !__syncthreads_or(narrow);
   if (MODE != MODE_RAW && !slow && m0 + BM <= M && n0 + BN <= N) {
     // Interior tile, in-range scales: no bounds checks, branch-free rounding.
     // int8 weights: |m_r * m_c| < 2^30, so acc * m_r * m_c is one 32 x 32 ->
@@ -415,48 +421,63 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
     // (0 <= tl < 2^32) and the rounding term 2^(s-1) = ch * 2^32 + cl,
     // R(t * m_c, s) = (th * m_c + ch + ((tl * m_c + cl) >> 32)) >> (s - 32)
     // exactly, for 32 <= s <= 94.
+    auto tiles = [&](auto hi) {  // hi: every shift >= 33 (compile-time flag)
+      constexpr bool HI = decltype(hi)::value;
 #pragma clang loop unroll(full)
-    for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
-      for (int t = 0; t < TN; ++t) {
-        const int j = n0 + wn * WN + t * 32 + (lane & 31);
-        const int32_t cm = e.col_m[j];
-        const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
-        int32_t old[16];
-        if (MODE == MODE_RES_ADD) {
+        for (int t = 0; t < TN; ++t) {
+          const int j = n0 + wn * WN + t * 32 + (lane & 31);
+          const int32_t cm = e.col_m[j];
+          const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
+          int32_t old[16];
+          if (MODE == MODE_RES_ADD) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            old[r] = ((const int32_t*)out)[(m0 + lb + 8 * (r >> 2) + (r & 3) + obase) * N + j];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int li = lb + 8 * (r >> 2) + (r & 3);
-          const int64_t o = (m0 + li + obase) * N + j;
-          const int sh = s_rk[li];
-          int64_t y;
-          if (WIDE) {
-            const int64_t v = 256 * (int64_t)acc[0][a][t][r] + (int64_t)acc[NB - 1][a][t][r] +
-                              128 * (int64_t)srow[li];
-            const int64_t tt = v * s_rm[li];
-            const int64_t th = tt >> 32;
-            const uint64_t tl = (uint32_t)tt;
-            const int64_t ch = sh >= 33 ? int64_t(1) << (sh - 33) : 0;
-            const uint64_t cl = sh == 32 ? uint64_t(1) << 31 : 0;
-            const uint64_t lo = tl * (uint64_t)(uint32_t)cm + cl;
-            y = (th * cm + ch + (int64_t)(lo >> 32)) >> (sh - 32);
-          } else {
-            const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)__mul24(s_rm[li], cm);
-            y = (pr + (int64_t(1) << (sh - 1))) >> sh;
+            for (int r = 0; r < 16; ++r)
+              old[r] = ((const int32_t*)out)[(m0 + lb + 8 * (r >> 2) + (r & 3) + obase) * N + j];
           }
-          if (MODE == MODE_REQ_I8)
-            ((int8_t*)out)[o] = clamp8(y);
-          else if (MODE == MODE_FIX)
-            ((int32_t*)out)[o] = (int32_t)y;
-          else
-            ((int32_t*)out)[o] = old[r] + (int32_t)y;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int li = lb + 8 * (r >> 2) + (r & 3);
+            const int64_t o = (m0 + li + obase) * N + j;
+            const int sh = s_rk[li];
+            int64_t y;
+            if (WIDE) {
+              const int64_t v = 256 * (int64_t)acc[0][a][t][r] + (int64_t)acc[NB - 1][a][t][r] +
+                                128 * (int64_t)srow[li];
+              const int64_t tt = v * s_rm[li];
+              const int64_t th = tt >> 32;
+              const uint64_t tl = (uint32_t)tt;
+              const int64_t ch = sh >= 33 ? int64_t(1) << (sh - 33) : 0;
+              const uint64_t cl = sh == 32 ? uint64_t(1) << 31 : 0;
+              const uint64_t lo = tl * (uint64_t)(uint32_t)cm + cl;
+              y = (th * cm + ch + (int64_t)(lo >> 32)) >> (sh - 32);
+            } else if (HI) {
+              const int32_t ph = __mulhi(acc[0][a][t][r], __mul24(s_rm[li], cm));
+              y = (ph + (1 << (sh - 33))) >> (sh - 32);
+            } else {
+              const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)__mul24(s_rm[li], cm);
+              y = (pr + (int64_t(1) << (sh - 1))) >> sh;
+            }
+            if (MODE == MODE_REQ_I8)
+              ((int8_t*)out)[o] = clamp8(y);
+            else if (MODE == MODE_FIX)
+              ((int32_t*)out)[o] = (int32_t)y;
+            else
+              ((int32_t*)out)[o] = old[r] + (int32_t)y;
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // one copy of the unrolled tile loop per case (a per-element branch
+    // would interleave both and double the code the loop runs through)
+    if constexpr (!WIDE) {
+      if (hi_only) {
+        tiles(std::true_type{});
+        return;
       }
+    }
+    tiles(std::false_type{});
     return;
   }
 #pragma clang loop unroll(full)
