@@ -245,17 +245,17 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
 // each of the gq workgroups, with identical bytes).
 // (qkv is not __restrict__: loads through a restrict-qualified read-only
 // pointer may be sunk to their first use, past the cache loads)
-template <int D, int G, bool QKN>
-__global__ __launch_bounds__(TPB) void attn_decode_fused(
+template <int D, int G, bool QKN, int NT>
+__global__ __launch_bounds__(NT) void attn_decode_fused(
     const int32_t* qkv, QkvPost p, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ slot_arr, int nq, int nkv, int n_slots, int max_pos,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, int32_t Ms, int32_t Ks,
     int32_t* __restrict__ out, int gq) {
   constexpr int CH = D / 16;              // 16-byte chunks per row
-  constexpr int NW = TPB / 64;
-  constexpr int PRE = G <= 2 ? 768 : 512; // cached rows loaded up front
-  constexpr int KU = PRE / TPB;           // key rows per thread (one row each)
-  constexpr int RG = TPB / CH;            // value rows per pass-4 step
+  constexpr int NW = NT / 64;
+  constexpr int PRE = G <= 2 && NT == 256 ? 768 : 512;  // cached rows loaded up front
+  constexpr int KU = PRE / NT;           // key rows per thread (one row each)
+  constexpr int RG = NT / CH;            // value rows per pass-4 step
   constexpr int VU = PRE / RG;            // value chunks per thread
   constexpr int NH = G + 2;               // heads post-processed here
   constexpr int HR = (NH + NW - 1) / NW;  // rounds of NW waves
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   const int pos = start_pos[r], slot = slot_arr[r];
   int32_t* orow = out + ((size_t)r * nq + h0) * D;
   if (pos < 0 || pos >= max_pos || slot < 0 || slot >= n_slots) {
-    for (int t = tid; t < G * D; t += TPB) orow[t] = 0;
+    for (int t = tid; t < G * D; t += NT) orow[t] = 0;
     return;
   }
   const int nold = pos, ctx = pos + 1, ld = max_pos;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   v4i kpre[KU][CH], vpre[VU];
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const int j = tid + u * TPB;
+    const int j = tid + u * NT;
     const int off = j < nold ? j * D : cbytes;
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc)
@@ -415,17 +415,17 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   };
 #pragma unroll
   for (int u = 0; u < KU; ++u)
-    if (tid + u * TPB < nold) score(kpre[u], tid + u * TPB);
+    if (tid + u * NT < nold) score(kpre[u], tid + u * NT);
   if (PRE < nold) {
     // later cached keys in batches of SK rows per thread, two batches in
     // flight (rows past pos read zeros and are skipped); the loop body is
     // straight-line so each wait counts only the older batch
-    constexpr int SK = D == 64 ? 4 : 2;
+    constexpr int SK = D == 64 && NT == 256 ? 4 : 2;
     v4i ka[SK][CH], kb[SK][CH];
     auto kload = [&](v4i (&kr)[SK][CH], int b0) {
 #pragma unroll
       for (int u = 0; u < SK; ++u) {
-        const int j = b0 + tid + u * TPB;
+        const int j = b0 + tid + u * NT;
         const int off = j < nold ? j * D : cbytes;
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc)
@@ -435,17 +435,17 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
     auto kuse = [&](v4i (&kr)[SK][CH], int b0) {
 #pragma unroll
       for (int u = 0; u < SK; ++u)
-        if (b0 + tid + u * TPB < nold) score(kr[u], b0 + tid + u * TPB);
+        if (b0 + tid + u * NT < nold) score(kr[u], b0 + tid + u * NT);
     };
     kload(ka, PRE);
-    for (int b0 = PRE; b0 < nold; b0 += 2 * SK * TPB) {
-      kload(kb, b0 + SK * TPB);
+    for (int b0 = PRE; b0 < nold; b0 += 2 * SK * NT) {
+      kload(kb, b0 + SK * NT);
       kuse(ka, b0);
-      kload(ka, b0 + 2 * SK * TPB);
-      kuse(kb, b0 + SK * TPB);
+      kload(ka, b0 + 2 * SK * NT);
+      kuse(kb, b0 + SK * NT);
     }
   }
-  if (tid == TPB - 1) {  // the new key
+  if (tid == NT - 1) {  // the new key
     v4i kn[CH];
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) kn[cc] = snew[cc];
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   int64_t den[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) den[g] = 0;
-  for (int j = tid; j < ctx; j += TPB) {
+  for (int j = tid; j < ctx; j += NT) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int32_t E = diexp(R(((int64_t)sc[g * ld + j] - mx[g]) * Ms, Ks - seq[g]));
@@ -491,12 +491,22 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
     if (lane == 0) rnv[g] = q;
   }
   lds_barrier();
-  int64_t rn[G];
+  {
+    // 6a. P = min(R(E rn, 31), 2^15 - 1) in place, once per (head, key)
+    int64_t rn[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) rn[g] = rnv[g];
+    for (int g = 0; g < G; ++g) rn[g] = rnv[g];
+    for (int j = tid; j < ctx; j += NT) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t pp = R((int64_t)sc[g * ld + j] * rn[g], 31);
+        sc[g * ld + j] = (int32_t)(pp > 32767 ? 32767 : pp);
+      }
+    }
+  }
+  lds_barrier();
 
-  // 6. passes 3+4: P = min(R(E rn, 31), 2^15 - 1) and P.V; lane owns a
-  //    16-byte chunk c of value rows rg, rg + RG, ...
+  // 6b. P.V; a lane owns a 16-byte chunk c of value rows rg, rg + RG, ...
   int acc[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -505,8 +515,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   auto pv = [&](const v4i& v, int j) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t pp = R((int64_t)sc[g * ld + j] * rn[g], 31);
-      const int P = (int)(pp > 32767 ? 32767 : pp);
+      const int P = sc[g * ld + j];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         acc[g][b] += P * sbyte(v.x, b);
@@ -520,7 +529,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
   for (int u = 0; u < VU; ++u)
     if (rg + u * RG < nold) pv(vpre[u], rg + u * RG);
   if (PRE < nold) {  // later cached values, as the keys: SU rows per batch, two in flight
-    constexpr int SU = 8;
+    constexpr int SU = NT == 256 ? 8 : 4;
     v4i va[SU], vb[SU];
     auto vload = [&](v4i (&vr)[SU], int b0) {
 #pragma unroll
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(TPB) void attn_decode_fused(
     sred[wave][g * D + c * 16 + b] = av[i];
   }
   lds_barrier();
-  for (int t = tid; t < G * D; t += TPB) {
+  for (int t = tid; t < G * D; t += NT) {
     int s2 = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) s2 += sred[w][t];
@@ -897,7 +906,7 @@ hipError_t launch_t(const int8_t* q8, const int32_t* e_q, const int8_t* kc, cons
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, int NT>
 hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
                           const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
@@ -905,20 +914,20 @@ hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* s
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, true>,
+    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, true, NT>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, false>,
+    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, false, NT>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr_set = true;
   }
   const dim3 grid((unsigned)B, (unsigned)(nq / G));
   const int gq = (int)(nq / nkv);
   if (p.qk_norm)
-    attn_decode_fused<D, G, true><<<grid, TPB, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
+    attn_decode_fused<D, G, true, NT><<<grid, NT, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
                                                          (int)n_slots, (int)max_pos, kc, vc, M, K,
                                                          out, gq);
   else
-    attn_decode_fused<D, G, false><<<grid, TPB, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
+    attn_decode_fused<D, G, false, NT><<<grid, NT, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
                                                           (int)n_slots, (int)max_pos, kc, vc, M, K,
                                                           out, gq);
   return hipGetLastError();
@@ -934,10 +943,13 @@ hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* s
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
                           hipStream_t st) {
   if (G > 1 && B * nkv < 64)
-    return launch_fused_g<D, 1>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M, K,
-                                out, st);
-  return launch_fused_g<D, G>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M, K,
-                              out, st);
+    return launch_fused_g<D, 1, 256>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc,
+                                     M, K, out, st);
+  // four heads per workgroup with 64-wide heads: the passes are
+  // VALU-bound, so two waves per SIMD instead of one
+  constexpr int NT = D == 64 && G == 4 ? 512 : 256;
+  return launch_fused_g<D, G, NT>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M,
+                                  K, out, st);
 }
 
 }  // namespace
