@@ -36,6 +36,19 @@ __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
   return c;
 }
 
+// E = DI-Exp(R((s - mx) M, sh)) for s <= mx, written for x = (mx - s) M >= 0:
+// R(-x, sh) = -((x + 2^(sh-1) - 1) >> sh) for sh >= 1, so DI-Exp's
+// magnitude is v = (x + 2^(sh-1) - 1) >> sh and E = R(2^15 - R(v mod 2^15, 1),
+// v >> 15), zero once v >> 15 > 30. Needs 1 <= sh <= 62 and M > 0; other
+// rows take diexp(R(...)) as written.
+__device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh) {
+  const uint64_t x = (uint64_t)delta * M;
+  const uint64_t v = (x + (uint64_t(1) << (sh - 1)) - 1) >> sh;
+  const uint32_t vv = (uint32_t)v, n = min(vv >> 15, 31u);
+  const uint32_t f = 32768u - (((vv & 32767u) + 1u) >> 1);
+  return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
+}
+
 // Transposed partial reduction of N int32 values per lane over the lane
 // offsets O, O/2, ..., OMIN: each step keeps half of the values and adds the
 // partner's copy of them, so N - N / 2^steps exchanges replace
@@ -328,6 +341,21 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     vpre[u] = __builtin_bit_cast(
         v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
   }
+  // the first batch of later cached keys too (long contexts; out-of-range
+  // rows read zeros without touching memory)
+  constexpr int SK = D == 64 && NT == 256 ? 4 : 2;
+  v4i ka[SK][CH], kb[SK][CH];
+  auto kload = [&](v4i (&kr)[SK][CH], int b0) {
+#pragma unroll
+    for (int u = 0; u < SK; ++u) {
+      const int j = b0 + tid + u * NT;
+      const int off = j < nold ? j * D : cbytes;
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc)
+        kr[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
+    }
+  };
+  kload(ka, PRE);
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. post-processing (the integer steps of qkv_head): q -> q8, e_q (LDS);
@@ -417,27 +445,15 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   for (int u = 0; u < KU; ++u)
     if (tid + u * NT < nold) score(kpre[u], tid + u * NT);
   if (PRE < nold) {
-    // later cached keys in batches of SK rows per thread, two batches in
-    // flight (rows past pos read zeros and are skipped); the loop body is
-    // straight-line so each wait counts only the older batch
-    constexpr int SK = D == 64 && NT == 256 ? 4 : 2;
-    v4i ka[SK][CH], kb[SK][CH];
-    auto kload = [&](v4i (&kr)[SK][CH], int b0) {
-#pragma unroll
-      for (int u = 0; u < SK; ++u) {
-        const int j = b0 + tid + u * NT;
-        const int off = j < nold ? j * D : cbytes;
-#pragma unroll
-        for (int cc = 0; cc < CH; ++cc)
-          kr[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
-      }
-    };
+    // later cached keys in batches of SK rows per thread (the first one is
+    // already in flight), two batches in flight (rows past pos read zeros
+    // and are skipped); the loop body is straight-line so each wait counts
+    // only the older batch
     auto kuse = [&](v4i (&kr)[SK][CH], int b0) {
 #pragma unroll
       for (int u = 0; u < SK; ++u)
         if (b0 + tid + u * NT < nold) score(kr[u], b0 + tid + u * NT);
     };
-    kload(ka, PRE);
     for (int b0 = PRE; b0 < nold; b0 += 2 * SK * NT) {
       kload(kb, b0 + SK * NT);
       kuse(ka, b0);
@@ -465,16 +481,49 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     mx[g] = m;
   }
 
+  // the first batch of later cached values, in flight during passes 2-3
+  constexpr int SU = NT == 256 ? 8 : 4;
+  v4i va[SU], vb[SU];
+  auto vload = [&](v4i (&vr)[SU], int b0) {
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int j = b0 + rg + u * RG;
+      vr[u] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
+    }
+  };
+  if (PRE < nold) vload(va, PRE);
+
   // 5. pass 2: exponentials in place and their sums; 2^46 / D per head
   int64_t den[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) den[g] = 0;
-  for (int j = tid; j < ctx; j += NT) {
+  {
+    int shg[G];
+    bool fast = Ms > 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int32_t E = diexp(R(((int64_t)sc[g * ld + j] - mx[g]) * Ms, Ks - seq[g]));
-      sc[g * ld + j] = E;
-      den[g] += E;
+      shg[g] = __builtin_amdgcn_readfirstlane(Ks - seq[g]);
+      fast = fast && shg[g] >= 1 && shg[g] <= 62;
+    }
+    if (fast) {  // uniform: the branch-free form of DI-Exp (exp_delta)
+      for (int j = tid; j < ctx; j += NT) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int32_t E = exp_delta((uint32_t)(mx[g] - sc[g * ld + j]), (uint32_t)Ms, shg[g]);
+          sc[g * ld + j] = E;
+          den[g] += E;
+        }
+      }
+    } else {
+      for (int j = tid; j < ctx; j += NT) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int32_t E = diexp(R(((int64_t)sc[g * ld + j] - mx[g]) * Ms, shg[g]));
+          sc[g * ld + j] = E;
+          den[g] += E;
+        }
+      }
     }
   }
 #pragma unroll
@@ -529,22 +578,11 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   for (int u = 0; u < VU; ++u)
     if (rg + u * RG < nold) pv(vpre[u], rg + u * RG);
   if (PRE < nold) {  // later cached values, as the keys: SU rows per batch, two in flight
-    constexpr int SU = NT == 256 ? 8 : 4;
-    v4i va[SU], vb[SU];
-    auto vload = [&](v4i (&vr)[SU], int b0) {
-#pragma unroll
-      for (int u = 0; u < SU; ++u) {
-        const int j = b0 + rg + u * RG;
-        vr[u] = __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
-      }
-    };
     auto vuse = [&](v4i (&vr)[SU], int b0) {
 #pragma unroll
       for (int u = 0; u < SU; ++u)
         if (b0 + rg + u * RG < nold) pv(vr[u], b0 + rg + u * RG);
     };
-    vload(va, PRE);
     for (int b0 = PRE; b0 < nold; b0 += 2 * SU * RG) {
       vload(vb, b0 + SU * RG);
       vuse(va, b0);
@@ -603,19 +641,6 @@ struct PfCfg {
 // position k' = 16 h + b of key 8 (b / 4) + 4 h + b % 4 in the P.V contraction
 __device__ __forceinline__ int key_slot(int key) {
   return 16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3);
-}
-
-// E = DI-Exp(R((s - mx) M, sh)) for s <= mx, written for x = (mx - s) M >= 0:
-// R(-x, sh) = -((x + 2^(sh-1) - 1) >> sh) for sh >= 1, so DI-Exp's
-// magnitude is v = (x + 2^(sh-1) - 1) >> sh and E = R(2^15 - R(v mod 2^15, 1),
-// v >> 15), zero once v >> 15 > 30. Needs 1 <= sh <= 62 and M > 0; other
-// rows take diexp(R(...)) as written.
-__device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh) {
-  const uint64_t x = (uint64_t)delta * M;
-  const uint64_t v = (x + (uint64_t(1) << (sh - 1)) - 1) >> sh;
-  const uint32_t vv = (uint32_t)v, n = min(vv >> 15, 31u);
-  const uint32_t f = 32768u - (((vv & 32767u) + 1u) >> 1);
-  return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
 }
 
 template <int D, int G>
