@@ -127,7 +127,7 @@ struct FG {
 };
 
 template <int MT, int CPW, int KC, int PRO, int EPI>
-__global__ __launch_bounds__(TPB) void fgemv(FG p) {
+__global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 : 1)) void fgemv(FG p) {
   extern __shared__ __attribute__((aligned(16))) int8_t sx[];  // [MT][K] int8 input rows
   __shared__ int64_t sred[TPB / 64][2 * MT];
   __shared__ int32_t s_m[MT], s_k[MT], s_e[MT];
