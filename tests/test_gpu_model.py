@@ -222,3 +222,45 @@ def test_llama_limbs_batch24_split_k_rows_match(D, llama):
         alone = host(dm1.generate([prompts[r]], 3))
         np.testing.assert_array_equal(hist[:, r], alone[:, 0], err_msg=f"row {r}")
         del dm1
+
+
+@pytest.mark.parametrize("nq,nkv,d,qkn", [(8, 2, 64, False), (4, 2, 128, True)])
+def test_decode_attention_long_context_matches_prefill(D, nq, nkv, d, qkn):
+    """Decode rows whose context runs past the cached rows the fused decode
+    attention loads up front (512-768), so its double-buffered streaming
+    loops run, in its launch shapes: 32 rows (a workgroup per KV head; 512
+    threads for four 64-wide heads) and one row (a workgroup per query head).
+    Each decode step's logits must equal the last-position logits of
+    prefilling the prompt plus the decoded token in one call (the MFMA
+    prefill attention, itself checked against the oracle)."""
+    import torch
+    shape = S.ModelShape("long_ctx", 1, 256, nq, nkv, d, 512, 1000, qkn, False,
+                         1_000_000, 2048, 22)
+    m = S.make_model(shape, seed=5)
+    V, B = shape.vocab, 32
+    prompts = S.make_prompts(V, B, 900, 1700, 31)
+    dm = D.DetintModel(m, n_slots=B)
+    first = torch.zeros((B, V), dtype=torch.int32, device="cuda")
+    tok = dm.prefill(prompts, [0] * B, list(range(B)), first, 0)
+    toks = host(tok).copy()
+    step = torch.zeros((B, V), dtype=torch.int32, device="cuda")
+    dm.decode(tok, [len(p) for p in prompts], list(range(B)), 1, step, 0, use_graph=False)
+    got = host(step)
+    del dm
+
+    def reference(r):
+        dm1 = D.DetintModel(m, n_slots=1)
+        ref = torch.zeros((1, V), dtype=torch.int32, device="cuda")
+        dm1.prefill([np.append(prompts[r], toks[r]).astype(np.int32)], [0], [0], ref, 0)
+        return host(ref)[0]
+
+    for r in (0, 13, 31):
+        np.testing.assert_array_equal(got[r], reference(r), err_msg=f"batch-32 row {r}")
+    # one row alone
+    r = 7
+    dm1 = D.DetintModel(m, n_slots=1)
+    one = torch.zeros((1, V), dtype=torch.int32, device="cuda")
+    t1 = dm1.prefill([prompts[r]], [0], [0], one, 0)
+    assert int(host(t1)[0]) == int(toks[r])
+    dm1.decode(t1, [len(prompts[r])], [0], 1, one, 0, use_graph=False)
+    np.testing.assert_array_equal(host(one)[0], reference(r), err_msg="batch-1 row")
