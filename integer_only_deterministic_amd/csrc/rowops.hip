@@ -52,6 +52,117 @@ __global__ __launch_bounds__(TPB) void rmsnorm_k(const int32_t* __restrict__ h,
   }
 }
 
+// Row-in-registers forms of the row kernels (n % 4 == 0, n <= 4 NT U, 16-byte
+// aligned rows): thread t owns elements u 4 NT + 4 t .. + 3 for u < U. Every
+// load is issued before any is used (clamped addresses, so none sits behind
+// a branch; elements past n are zeroed afterwards) and the second pass works
+// on the registers instead of re-reading the row. Same integer results as
+// the loop forms above and below.
+template <int NT, int U>
+struct RowRegs {
+  __device__ __forceinline__ static int first(int u) { return u * 4 * NT + 4 * (int)threadIdx.x; }
+  __device__ __forceinline__ static int at(int u, int n) { return min(first(u), n - 4); }
+};
+
+__device__ __forceinline__ uint32_t pack4(int64_t a, int64_t b, int64_t c, int64_t d) {
+  return (uint32_t)(uint8_t)clamp8(a) | (uint32_t)(uint8_t)clamp8(b) << 8 |
+         (uint32_t)(uint8_t)clamp8(c) << 16 | (uint32_t)(uint8_t)clamp8(d) << 24;
+}
+
+template <int U>
+__global__ __launch_bounds__(TPB) void rmsnorm_rk(const int32_t* __restrict__ h,
+                                                  const int32_t* __restrict__ row_index,
+                                                  const int16_t* __restrict__ g, int n,
+                                                  int8_t* __restrict__ x8,
+                                                  int32_t* __restrict__ rm,
+                                                  int32_t* __restrict__ rk) {
+  using RR = RowRegs<TPB, U>;
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int src = row_index ? row_index[r] : r;
+  const int32_t* hr = h + (size_t)src * n;
+  v4i hv[U];
+  int2 gw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    hv[u] = *(const v4i*)(hr + RR::at(u, n));
+    gw[u] = *(const int2*)(g + RR::at(u, n));
+  }
+  int64_t v[U][4], gv[U][4], S = 0, A = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = RR::first(u) < n;
+    v[u][0] = ok ? hv[u].x : 0; v[u][1] = ok ? hv[u].y : 0;
+    v[u][2] = ok ? hv[u].z : 0; v[u][3] = ok ? hv[u].w : 0;
+    gv[u][0] = (int16_t)(gw[u].x & 0xFFFF); gv[u][1] = (int16_t)(gw[u].x >> 16);
+    gv[u][2] = (int16_t)(gw[u].y & 0xFFFF); gv[u][3] = (int16_t)(gw[u].y >> 16);
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      S += v[u][e4] * v[u][e4];
+      const int64_t a = (int64_t)uabs64(v[u][e4] * gv[u][e4]);
+      A = a > A ? a : A;
+    }
+  }
+  S = block_sum(S, red);
+  A = block_max(A, red);
+  int8_t* xr = x8 + (size_t)r * n;
+  int32_t m = 1 << 14, sh = 26;
+  int e = 0;
+  if (S != 0) {
+    irms_wave(S, n, m, sh);
+    e = dq_exp((uint64_t)A);
+    sh = sh + 12 - e;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (RR::first(u) < n)  // an all-zero row quantises to zeros with e = 0
+      *(uint32_t*)(xr + RR::first(u)) =
+          pack4(R_nn(v[u][0] * gv[u][0], e), R_nn(v[u][1] * gv[u][1], e),
+                R_nn(v[u][2] * gv[u][2], e), R_nn(v[u][3] * gv[u][3], e));
+  if (threadIdx.x == 0) {
+    rm[r] = m;
+    rk[r] = sh;
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(TPB) void requant_rk(const int32_t* __restrict__ y, int n,
+                                                  int8_t* __restrict__ q, int32_t* row_e,
+                                                  int32_t* row_m, int32_t* row_k, int32_t fm,
+                                                  int32_t fk) {
+  using RR = RowRegs<TPB, U>;
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int32_t* yr = y + (size_t)r * n;
+  v4i yv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) yv[u] = *(const v4i*)(yr + RR::at(u, n));
+  int64_t A = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = RR::first(u) < n;
+    if (!ok) yv[u] = v4i{0, 0, 0, 0};
+    const uint64_t a = uabs64(yv[u].x) > uabs64(yv[u].y) ? uabs64(yv[u].x) : uabs64(yv[u].y);
+    const uint64_t b = uabs64(yv[u].z) > uabs64(yv[u].w) ? uabs64(yv[u].z) : uabs64(yv[u].w);
+    const int64_t c = (int64_t)(a > b ? a : b);
+    A = c > A ? c : A;
+  }
+  A = block_max(A, red);
+  const int e = dq_exp((uint64_t)A);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (RR::first(u) < n)
+      *(uint32_t*)(q + (size_t)r * n + RR::first(u)) =
+          pack4(R_nn(yv[u].x, e), R_nn(yv[u].y, e), R_nn(yv[u].z, e), R_nn(yv[u].w, e));
+  if (threadIdx.x == 0) {
+    if (row_e) row_e[r] = e;
+    if (row_m) {
+      row_m[r] = fm;
+      row_k[r] = fk - e;
+    }
+  }
+}
+
 // Per-token DQ (DetLLM blog "DetLLM": a token's activations are quantised
 // from its own values): q = clamp8(R(y, e)), e from the row's |max|.
 __global__ __launch_bounds__(TPB) void requant_k(const int32_t* __restrict__ y, int n,
@@ -150,6 +261,45 @@ __global__ __launch_bounds__(SWT) void swiglu_k(const int32_t* __restrict__ gu, 
     const int j = threadIdx.x + i * SWT;
     if (j < n) a8[(size_t)r * n + j] = clamp8(R(p[i], e));
   }
+  if (threadIdx.x == 0) {
+    rm[r] = 1 << 14;
+    rk[r] = 2 * f_a - e + 14;
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(SWT) void swiglu_rk(const int32_t* __restrict__ gu, int n, int32_t f_a,
+                                                 int32_t Mg, int32_t Kg, int8_t* __restrict__ a8,
+                                                 int32_t* __restrict__ rm, int32_t* __restrict__ rk) {
+  using RR = RowRegs<SWT, U>;
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int32_t* g = gu + (size_t)r * 2 * n;
+  const int32_t* up = g + n;
+  v4i gv[U], uv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    gv[u] = *(const v4i*)(g + RR::at(u, n));
+    uv[u] = *(const v4i*)(up + RR::at(u, n));
+  }
+  int64_t p[U][4], A = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = RR::first(u) < n;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      p[u][e4] = ok ? swiglu_p(gv[u][e4], uv[u][e4], Mg, Kg) : 0;
+      const int64_t a = (int64_t)uabs64(p[u][e4]);
+      A = a > A ? a : A;
+    }
+  }
+  A = block_max(A, red);
+  const int e = dq_exp((uint64_t)A);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (RR::first(u) < n)
+      *(uint32_t*)(a8 + (size_t)r * n + RR::first(u)) =
+          pack4(R_nn(p[u][0], e), R_nn(p[u][1], e), R_nn(p[u][2], e), R_nn(p[u][3], e));
   if (threadIdx.x == 0) {
     rm[r] = 1 << 14;
     rk[r] = 2 * f_a - e + 14;
@@ -293,12 +443,27 @@ __global__ void advance_k(int32_t* ids, const int32_t* next_tok, int32_t* start_
   if (s == 0 && row_base) *row_base += S;
 }
 
+bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int16_t* gain,
                           int64_t R, int64_t n, int8_t* x8, int32_t* row_m, int32_t* row_k,
                           hipStream_t st) {
   if (R == 0) return hipSuccess;
+  if (n % 4 == 0 && n >= 4 && n <= 32 * TPB && aligned_to(h, 16) && aligned_to(gain, 8) &&
+      aligned_to(x8, 4)) {
+    const int u = (int)((n + 4 * TPB - 1) / (4 * TPB));
+    if (u <= 1)
+      rmsnorm_rk<1><<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
+    else if (u <= 2)
+      rmsnorm_rk<2><<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
+    else if (u <= 4)
+      rmsnorm_rk<4><<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
+    else
+      rmsnorm_rk<8><<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
+    return hipGetLastError();
+  }
   rmsnorm_k<<<(unsigned)R, TPB, 0, st>>>(h, row_index, gain, (int)n, x8, row_m, row_k);
   return hipGetLastError();
 }
@@ -307,6 +472,21 @@ hipError_t launch_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, int
                           int32_t* row_m, int32_t* row_k, int32_t fold_m, int32_t fold_k,
                           hipStream_t st) {
   if (R == 0) return hipSuccess;
+  if (n % 4 == 0 && n >= 4 && n <= 32 * TPB && aligned_to(y, 16) && aligned_to(q, 4)) {
+    const int u = (int)((n + 4 * TPB - 1) / (4 * TPB));
+#define DETINT_RQ(UU) \
+  requant_rk<UU><<<(unsigned)R, TPB, 0, st>>>(y, (int)n, q, row_e, row_m, row_k, fold_m, fold_k)
+    if (u <= 1)
+      DETINT_RQ(1);
+    else if (u <= 2)
+      DETINT_RQ(2);
+    else if (u <= 4)
+      DETINT_RQ(4);
+    else
+      DETINT_RQ(8);
+#undef DETINT_RQ
+    return hipGetLastError();
+  }
   requant_k<<<(unsigned)R, TPB, 0, st>>>(y, (int)n, q, row_e, row_m, row_k, fold_m, fold_k);
   return hipGetLastError();
 }
@@ -333,6 +513,13 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
                          int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st) {
   if (R == 0) return hipSuccess;
   if (n > SWT * SWPER) return hipErrorInvalidValue;
+  if (n % 4 == 0 && n >= 4 && aligned_to(gu, 16) && aligned_to(a8, 4)) {
+    if (n <= 4 * SWT)
+      swiglu_rk<1><<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+    else
+      swiglu_rk<2><<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+    return hipGetLastError();
+  }
   swiglu_k<<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
   return hipGetLastError();
 }

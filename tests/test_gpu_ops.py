@@ -152,7 +152,8 @@ def test_gemm_w16_limbs(D, M, N, K):
 
 # -------------------------------------------------------------- row ops
 
-@pytest.mark.parametrize("R,n", [(1, 1024), (5, 256), (64, 768), (33, 2048), (3, 4096)])
+@pytest.mark.parametrize("R,n", [(1, 1024), (5, 256), (64, 768), (33, 2048), (3, 4096),
+                                 (6, 8192), (7, 1022)])
 def test_rmsnorm(D, R, n):
     rng = np.random.default_rng(R * n)
     h = rng.integers(-(1 << 24), 1 << 24, (R, n)).astype(np.int32)
@@ -189,7 +190,7 @@ def test_rmsnorm_magnitudes(D, n):
     np.testing.assert_array_equal(host(x8), ox)
 
 
-@pytest.mark.parametrize("R,n", [(1, 2048), (9, 512), (70, 4096)])
+@pytest.mark.parametrize("R,n", [(1, 2048), (9, 512), (70, 4096), (5, 8192), (4, 1030)])
 def test_requant(D, R, n):
     rng = np.random.default_rng(R + n)
     y = rng.integers(-(1 << 22), 1 << 22, (R, n)).astype(np.int32)
@@ -227,7 +228,7 @@ def test_softmax(D):
     np.testing.assert_array_equal(host(P), O.softmax(s, valid, shift, M, K))
 
 
-@pytest.mark.parametrize("R,n", [(1, 3072), (13, 768), (4, 8192)])
+@pytest.mark.parametrize("R,n", [(1, 3072), (13, 768), (4, 8192), (3, 998), (2, 4100)])
 def test_swiglu(D, R, n):
     rng = np.random.default_rng(R * 3 + n)
     gu = rng.normal(0, 8 * 4096, (R, 2 * n)).astype(np.int32)
