@@ -103,8 +103,8 @@ __device__ __forceinline__ int reduce_index(int lane) {
   return idx;
 }
 
-enum { PRO_NORM = 1, PRO_DQ32 = 2, PRO_DQ64 = 3 };
-enum { EPI_RAW = 0, EPI_FIX = 1, EPI_RES = 2, EPI_SWIGLU = 3, EPI_LOGITS = 4 };
+enum { PRO_NORM = 1, PRO_DQ32 = 2, PRO_DQ64 = 3, PRO_I8 = 4 };
+enum { EPI_RAW = 0, EPI_FIX = 1, EPI_RES = 2, EPI_SWIGLU = 3, EPI_LOGITS = 4, EPI_REQ = 5 };
 
 struct FG {
   const int32_t* h;          // PRO_NORM: residual rows [*, K]
@@ -114,6 +114,9 @@ struct FG {
   int32_t fold_m, fold_k;    //   row scale (fold_m, fold_k - e)
   const int64_t* in64;       // PRO_DQ64: [M, K]; row scale (2^14, 2 f_a - e + 14)
   int32_t f_a;
+  const int8_t* a8;          // PRO_I8: int8 rows [M, K] with scales rm_in / rk_in (nullable: RAW)
+  const int32_t* rm_in;
+  const int32_t* rk_in;
   const int8_t* W;           // [N, K] ([2N, K] for SWIGLU: gate rows then up rows)
   const int32_t* col_m;
   int32_t col_k, frac;
@@ -183,148 +186,176 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
   };
   int g = gw;
 
-  typedef int64_t v4l __attribute__((ext_vector_type(4)));
-  constexpr bool WIDE_IN = PRO == PRO_DQ64;
-  v4i xr[MT][KC];        // int32 inputs as loaded
-  v4l xw[WIDE_IN ? MT : 1][KC];  // int64 inputs as loaded
-  int2 graw[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int i = min(kc * 1024 + 4 * tid, K - 4);
-    if (PRO == PRO_NORM) graw[kc] = *(const int2*)(p.gain + i);  // four int16 gains
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int mc = m < M ? m : M - 1;
-      if (PRO == PRO_NORM) {
-        const int src = p.row_index ? p.row_index[mc] : mc;
-        xr[m][kc] = *(const v4i*)(p.h + (size_t)src * K + i);
-      } else if (!WIDE_IN) {
-        xr[m][kc] = *(const v4i*)(p.in32 + (size_t)mc * K + i);
-      } else {
-        xw[m][kc] = *(const v4l*)(p.in64 + (size_t)mc * K + i);
-      }
-    }
-  }
-  load_w(g, 0);
-  load_w(g + nw, 1);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
-  //    elements kc * 1024 + 4 t .. + 3 of every row (zero past K, and rows
-  //    past M are zero).
-  int64_t xv[MT][KC][4];
-  int32_t gv[KC][4];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const bool iv = kc * 1024 + 4 * tid < K;
-    if (PRO == PRO_NORM) {
-      gv[kc][0] = iv ? (int16_t)(graw[kc].x & 0xFFFF) : 0;
-      gv[kc][1] = iv ? (int16_t)(graw[kc].x >> 16) : 0;
-      gv[kc][2] = iv ? (int16_t)(graw[kc].y & 0xFFFF) : 0;
-      gv[kc][3] = iv ? (int16_t)(graw[kc].y >> 16) : 0;
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const bool ok = iv && m < M;
-      if (!WIDE_IN) {
-        xv[m][kc][0] = ok ? xr[m][kc].x : 0;
-        xv[m][kc][1] = ok ? xr[m][kc].y : 0;
-        xv[m][kc][2] = ok ? xr[m][kc].z : 0;
-        xv[m][kc][3] = ok ? xr[m][kc].w : 0;
-      } else {
-        xv[m][kc][0] = ok ? xw[m][kc].x : 0;
-        xv[m][kc][1] = ok ? xw[m][kc].y : 0;
-        xv[m][kc][2] = ok ? xw[m][kc].z : 0;
-        xv[m][kc][3] = ok ? xw[m][kc].w : 0;
-      }
-    }
-  }
-  int64_t Sv[MT], Av[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    int64_t S = 0, A = 0;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t v = xv[m][kc][e4];
-        if (PRO == PRO_NORM) S += v * v;
-        const int64_t a = (int64_t)uabs64(PRO == PRO_NORM ? v * gv[kc][e4] : v);
-        A = a > A ? a : A;
-      }
-    Sv[m] = S;
-    Av[m] = A;
-  }
-  {
-    // wave totals of every row at once: lane l ends with row idx(l)'s totals
-    const int64_t At = Halve64<MT, 32, true>::run(Av, lane);
-    const int64_t St = PRO == PRO_NORM ? Halve64<MT, 32, false>::run(Sv, lane) : 0;
-    const int r = reduce_index<MT>(lane);
-    if ((lane & (64 / MT - 1)) == 0) {
-      sred[wave][2 * r] = St;
-      sred[wave][2 * r + 1] = At;
-    }
-  }
-  lds_barrier();
-  // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole wave)
-  for (int r = wave; r < M; r += TPB / 64) {
-    int64_t St = 0, At = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < TPB / 64; ++w2) {
-      St += sred[w2][2 * r];
-      At = sred[w2][2 * r + 1] > At ? sred[w2][2 * r + 1] : At;
-    }
-    const int e = dq_exp((uint64_t)At);
-    int32_t sm, sk;
-    if (PRO == PRO_NORM) {
-      if (St == 0) {
-        sm = 1 << 14;
-        sk = 26;
-      } else {
-        int32_t mm, sh;
-        irms_wave(St, K, mm, sh);
-        sm = mm;
-        sk = sh + 12 - e;
-      }
-    } else if (PRO == PRO_DQ32) {
-      sm = p.fold_m;
-      sk = p.fold_k - e;
-    } else {
-      sm = 1 << 14;
-      sk = 2 * p.f_a - e + 14;
-    }
-    if (lane == 0) {
-      s_m[r] = sm;
-      s_k[r] = sk;
-      s_e[r] = (PRO == PRO_NORM && St == 0) ? 0 : e;
-    }
-  }
-  lds_barrier();
-  // quantised rows, zero-padded to KC * 1024 bytes (the weight loads of
-  // lanes past K read clamped addresses; their products with the padding
-  // are zero)
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int e = s_e[m < M ? m : 0];
+  if constexpr (PRO == PRO_I8) {
+    // int8 rows given (a standalone GEMM): rows and their scales into LDS
+    uint32_t ar[MT][KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const int i = kc * 1024 + 4 * tid;
-      uint32_t packed = 0;
+      const int i = min(kc * 1024 + 4 * tid, K - 4);
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t v = PRO == PRO_NORM ? xv[m][kc][e4] * gv[kc][e4] : xv[m][kc][e4];
-        // |R(v, e)| <= 128 by the choice of e, so the clamp can run in 32 bits
-        const int32_t q = (int32_t)R_nn(v, e);
-        packed |= (uint32_t)(uint8_t)(q > 127 ? 127 : (q < -127 ? -127 : q)) << (8 * e4);
-      }
-      *(uint32_t*)(sx + (size_t)m * (KC * 1024) + i) = packed;
+      for (int m = 0; m < MT; ++m)
+        ar[m][kc] = *(const uint32_t*)(p.a8 + (size_t)(m < M ? m : M - 1) * K + i);
     }
+    load_w(g, 0);
+    load_w(g + nw, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < MT) {
+      const int mc = tid < M ? tid : M - 1;
+      s_m[tid] = p.rm_in ? p.rm_in[mc] : 0;
+      s_k[tid] = p.rk_in ? p.rk_in[mc] : 0;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bool ok = m < M && kc * 1024 + 4 * tid < K;
+        *(uint32_t*)(sx + (size_t)m * (KC * 1024) + kc * 1024 + 4 * tid) = ok ? ar[m][kc] : 0u;
+      }
+    lds_barrier();
+  } else {
+    typedef int64_t v4l __attribute__((ext_vector_type(4)));
+    constexpr bool WIDE_IN = PRO == PRO_DQ64;
+    v4i xr[MT][KC];        // int32 inputs as loaded
+    v4l xw[WIDE_IN ? MT : 1][KC];  // int64 inputs as loaded
+    int2 graw[KC];
+  #pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int i = min(kc * 1024 + 4 * tid, K - 4);
+      if (PRO == PRO_NORM) graw[kc] = *(const int2*)(p.gain + i);  // four int16 gains
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int mc = m < M ? m : M - 1;
+        if (PRO == PRO_NORM) {
+          const int src = p.row_index ? p.row_index[mc] : mc;
+          xr[m][kc] = *(const v4i*)(p.h + (size_t)src * K + i);
+        } else if (!WIDE_IN) {
+          xr[m][kc] = *(const v4i*)(p.in32 + (size_t)mc * K + i);
+        } else {
+          xw[m][kc] = *(const v4l*)(p.in64 + (size_t)mc * K + i);
+        }
+      }
+    }
+    load_w(g, 0);
+    load_w(g + nw, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
+    //    elements kc * 1024 + 4 t .. + 3 of every row (zero past K, and rows
+    //    past M are zero).
+    int64_t xv[MT][KC][4];
+    int32_t gv[KC][4];
+  #pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const bool iv = kc * 1024 + 4 * tid < K;
+      if (PRO == PRO_NORM) {
+        gv[kc][0] = iv ? (int16_t)(graw[kc].x & 0xFFFF) : 0;
+        gv[kc][1] = iv ? (int16_t)(graw[kc].x >> 16) : 0;
+        gv[kc][2] = iv ? (int16_t)(graw[kc].y & 0xFFFF) : 0;
+        gv[kc][3] = iv ? (int16_t)(graw[kc].y >> 16) : 0;
+      }
+  #pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bool ok = iv && m < M;
+        if (!WIDE_IN) {
+          xv[m][kc][0] = ok ? xr[m][kc].x : 0;
+          xv[m][kc][1] = ok ? xr[m][kc].y : 0;
+          xv[m][kc][2] = ok ? xr[m][kc].z : 0;
+          xv[m][kc][3] = ok ? xr[m][kc].w : 0;
+        } else {
+          xv[m][kc][0] = ok ? xw[m][kc].x : 0;
+          xv[m][kc][1] = ok ? xw[m][kc].y : 0;
+          xv[m][kc][2] = ok ? xw[m][kc].z : 0;
+          xv[m][kc][3] = ok ? xw[m][kc].w : 0;
+        }
+      }
+    }
+    int64_t Sv[MT], Av[MT];
+  #pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      int64_t S = 0, A = 0;
+  #pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+  #pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int64_t v = xv[m][kc][e4];
+          if (PRO == PRO_NORM) S += v * v;
+          const int64_t a = (int64_t)uabs64(PRO == PRO_NORM ? v * gv[kc][e4] : v);
+          A = a > A ? a : A;
+        }
+      Sv[m] = S;
+      Av[m] = A;
+    }
+    {
+      // wave totals of every row at once: lane l ends with row idx(l)'s totals
+      const int64_t At = Halve64<MT, 32, true>::run(Av, lane);
+      const int64_t St = PRO == PRO_NORM ? Halve64<MT, 32, false>::run(Sv, lane) : 0;
+      const int r = reduce_index<MT>(lane);
+      if ((lane & (64 / MT - 1)) == 0) {
+        sred[wave][2 * r] = St;
+        sred[wave][2 * r + 1] = At;
+      }
+    }
+    lds_barrier();
+    // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole wave)
+    for (int r = wave; r < M; r += TPB / 64) {
+      int64_t St = 0, At = 0;
+  #pragma unroll
+      for (int w2 = 0; w2 < TPB / 64; ++w2) {
+        St += sred[w2][2 * r];
+        At = sred[w2][2 * r + 1] > At ? sred[w2][2 * r + 1] : At;
+      }
+      const int e = dq_exp((uint64_t)At);
+      int32_t sm, sk;
+      if (PRO == PRO_NORM) {
+        if (St == 0) {
+          sm = 1 << 14;
+          sk = 26;
+        } else {
+          int32_t mm, sh;
+          irms_wave(St, K, mm, sh);
+          sm = mm;
+          sk = sh + 12 - e;
+        }
+      } else if (PRO == PRO_DQ32) {
+        sm = p.fold_m;
+        sk = p.fold_k - e;
+      } else {
+        sm = 1 << 14;
+        sk = 2 * p.f_a - e + 14;
+      }
+      if (lane == 0) {
+        s_m[r] = sm;
+        s_k[r] = sk;
+        s_e[r] = (PRO == PRO_NORM && St == 0) ? 0 : e;
+      }
+    }
+    lds_barrier();
+    // quantised rows, zero-padded to KC * 1024 bytes (the weight loads of
+    // lanes past K read clamped addresses; their products with the padding
+    // are zero)
+  #pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int e = s_e[m < M ? m : 0];
+  #pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int i = kc * 1024 + 4 * tid;
+        uint32_t packed = 0;
+  #pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int64_t v = PRO == PRO_NORM ? xv[m][kc][e4] * gv[kc][e4] : xv[m][kc][e4];
+          // |R(v, e)| <= 128 by the choice of e, so the clamp can run in 32 bits
+          const int32_t q = (int32_t)R_nn(v, e);
+          packed |= (uint32_t)(uint8_t)(q > 127 ? 127 : (q < -127 ? -127 : q)) << (8 * e4);
+        }
+        *(uint32_t*)(sx + (size_t)m * (KC * 1024) + i) = packed;
+      }
+    }
+    if (p.rm_out && blockIdx.x == 0 && tid < M) {
+      p.rm_out[tid] = s_m[tid];
+      p.rk_out[tid] = s_k[tid];
+    }
+    lds_barrier();
   }
-  if (p.rm_out && blockIdx.x == 0 && tid < M) {
-    p.rm_out[tid] = s_m[tid];
-    p.rk_out[tid] = s_k[tid];
-  }
-  lds_barrier();
 
   // 3. stream the weights: per group, dot products from LDS, reduce, epilogue
   const int idx = reduce_index<NV>(lane);
@@ -390,6 +421,8 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
           const int64_t y = R((int64_t)tot * s_m[mm] * cm[cc], s_k[mm] + p.col_k - p.frac);
           if (EPI == EPI_FIX) {
             ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)y;
+          } else if (EPI == EPI_REQ) {
+            ((int8_t*)p.out)[(size_t)mm * N + col] = clamp8(y);
           } else if (EPI == EPI_RES) {
             ((int32_t*)p.out)[(size_t)mm * N + col] = old + (int32_t)y;
           } else {
@@ -491,6 +524,21 @@ hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, 
   p.in64 = prod; p.f_a = f_a; p.W = W; p.col_m = col_m; p.col_k = col_k; p.frac = frac;
   p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h;
   return launch_mt<1, PRO_DQ64, EPI_RES>(p, st);
+}
+
+hipError_t launch_fgemv_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
+                           const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
+                           int32_t col_k, int32_t frac, int mode, void* out, hipStream_t st) {
+  FG p{};
+  p.a8 = A; p.rm_in = row_m; p.rk_in = row_k; p.W = W; p.col_m = col_m; p.col_k = col_k;
+  p.frac = mode == MODE_REQ_I8 ? 0 : frac;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = out;
+  switch (mode) {
+    case MODE_RAW: return launch_mt<2, PRO_I8, EPI_RAW>(p, st);
+    case MODE_REQ_I8: return launch_mt<2, PRO_I8, EPI_REQ>(p, st);
+    case MODE_FIX: return launch_mt<2, PRO_I8, EPI_FIX>(p, st);
+    default: return launch_mt<2, PRO_I8, EPI_RES>(p, st);
+  }
 }
 
 hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, const int16_t* gain,

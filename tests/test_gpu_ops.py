@@ -63,7 +63,8 @@ def test_gemm_sweep(D, K, N):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 77, 32), (17, 130, 64),
                                    (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072),
                                    (200, 300, 256), (1000, 6100, 256), (2000, 6000, 128),
-                                   (32, 1000, 2048), (20, 100, 512), (50, 77, 1024)])
+                                   (32, 1000, 2048), (20, 100, 512), (50, 77, 1024),
+                                   (5, 300, 1040), (8, 333, 2064)])
 def test_gemm_ragged_all_modes(D, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
@@ -87,11 +88,12 @@ def test_gemm_ragged_all_modes(D, M, N, K):
 
 
 @pytest.mark.parametrize("mode", ["REQ_I8", "FIX", "RES_ADD"])
-def test_gemm_general_scales(D, mode):
-    """All-interior 128x128 tiling with mantissas >= 2^15 and (for REQ_I8)
-    shifts from -3 to 70: the kernel's general epilogue, not its in-range
-    fast path."""
-    M, N, K = 512, 512, 256
+@pytest.mark.parametrize("M", [512, 6])
+def test_gemm_general_scales(D, mode, M):
+    """Mantissas >= 2^15 and (for REQ_I8) shifts from -3 to 70: at M = 512 an
+    all-interior 128x128 tiling takes the pipelined kernel's general
+    epilogue, not its in-range fast path; at M = 6 the GEMV's epilogue."""
+    N, K = 512, 256
     rng = np.random.default_rng(99)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
     W = rng.integers(-128, 128, (N, K)).astype(np.int8)
