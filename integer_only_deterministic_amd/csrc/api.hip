@@ -228,7 +228,7 @@ detint_status detint_lm_head(const int8_t* x8, const int8_t* emb, const int8_t* 
 
 static int64_t final_head_parts(int64_t S, int64_t V) {
   int64_t np = logits_argmax_parts(V);
-  if (fused_decode_parts(V) > np) np = fused_decode_parts(V);
+  if (fused_decode_parts(V, S) > np) np = fused_decode_parts(V, S);
   if (kArgmaxParts > np) np = kArgmaxParts;
   return S * np;
 }
@@ -261,7 +261,7 @@ detint_status detint_final_head(const int32_t* h, int64_t S, int64_t H, const in
     // the decode step's kernel: RMSNorm prologue, logits, argmax partials
     e = launch_fused_lm_head(h, nullptr, gain, emb, emb_m, w_k, f_l, S, V, H, logits, nullptr, part, st);
     if (e != hipSuccess || !next_tok) return hip_status(e, "final_head fused launch");
-    return hip_status(launch_argmax_final(part, S, fused_decode_parts(V), next_tok, st),
+    return hip_status(launch_argmax_final(part, S, fused_decode_parts(V, S), next_tok, st),
                       "final_head argmax");
   }
   e = launch_rmsnorm(h, nullptr, gain, S, H, x8, rm, rk, st);
@@ -397,8 +397,10 @@ WsLayout ws_layout(const detint_model_desc& d, int64_t R, int64_t S) {
   w.gu = take(4 * R * 2 * d.ffn);
   w.p64 = take(8 * R * d.ffn);
   int64_t np = logits_argmax_parts(d.vocab > 0 ? d.vocab : 1);
-  const int64_t npf = fused_decode_parts(d.vocab > 0 ? d.vocab : 1);
-  if (npf > np) np = npf;
+  for (int64_t mrows : {int64_t(1), int64_t(8)}) {  // the fused lm_head's partials for any R <= 8
+    const int64_t npf = fused_decode_parts(d.vocab > 0 ? d.vocab : 1, mrows);
+    if (npf > np) np = npf;
+  }
   w.part = take(8 * S * (np > kArgmaxParts ? np : kArgmaxParts));
   // split-K partials and counters of the skinny (<= 64-row) GEMMs
   int64_t nmax = nqkv > d.hidden ? nqkv : d.hidden;
@@ -588,7 +590,7 @@ static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* 
   }
   LAUNCH(launch_fused_lm_head(h, nullptr, d.final_norm, d.emb, d.emb_m, wk, d.f_l, R, d.vocab, H,
                               logits, row_base, part, st));
-  LAUNCH(launch_argmax_advance(part, R, fused_decode_parts(d.vocab), next_tok, ids, start_pos,
+  LAUNCH(launch_argmax_advance(part, R, fused_decode_parts(d.vocab, R), next_tok, ids, start_pos,
                                row_base, advance, st));
 #undef LAUNCH
   return ok();

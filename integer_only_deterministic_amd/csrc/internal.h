@@ -142,7 +142,9 @@ hipError_t launch_argmax_advance(const int64_t* part, int64_t S, int64_t nparts,
 
 // Fused decode kernels (decode.hip), M <= 8 rows of 8-bit weights.
 bool fused_decode_supported(int64_t M, int64_t K);
-int fused_decode_parts(int64_t V);
+// argmax partials per row of the fused lm_head for M rows (at most
+// fused_decode_parts(V, 8) for any M <= 8)
+int fused_decode_parts(int64_t V, int64_t M);
 hipError_t launch_fused_qkv(const int32_t* h, const int16_t* gain, const int8_t* W,
                             const int32_t* col_m, int32_t col_k, int32_t frac, bool raw, int64_t M,
                             int64_t N, int64_t K, int32_t* out, int32_t* rm_out, int32_t* rk_out,
