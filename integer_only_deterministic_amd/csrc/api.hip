@@ -530,11 +530,18 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   }
   // FFN block: RMSNorm -> gate/up -> DI-SwiGLU -> down + residual
   LAUNCH(launch_rmsnorm(h, nullptr, L.ffn_norm, R, H, x8, rm, rk, st));
-  {
+  if (gemm_takes_skinny(R, 2 * F, H, d.wide) && F % 16 == 0 && F % 4 == 0 && F <= 8192) {
+    // decode-sized batches: the SwiGLU product in the gate/up GEMM's
+    // epilogue (spread over all its workgroups), then only the row DQ
+    int64_t* p64 = (int64_t*)(base + w.p64);
+    Epi ep{rm, rk, L.wgu_m, wk, d.f_a, MODE_SWIGLU, nullptr, m->mg, m->kg};
+    LAUNCH(launch_gemm(x8, L.wgu, d.wide ? L.wgu_lo : nullptr, R, 2 * F, H, ep, p64, st, sp));
+    LAUNCH(launch_dq64(p64, R, F, d.f_a, x8, rm, rk, st));
+  } else {
     Epi ep{rm, rk, L.wgu_m, wk, d.f_a, MODE_FIX, nullptr};
     LAUNCH(launch_gemm(x8, L.wgu, d.wide ? L.wgu_lo : nullptr, R, 2 * F, H, ep, gu, st, sp));
+    LAUNCH(launch_swiglu(gu, R, F, d.f_a, m->mg, m->kg, x8, rm, rk, st));
   }
-  LAUNCH(launch_swiglu(gu, R, F, d.f_a, m->mg, m->kg, x8, rm, rk, st));
   {
     Epi ep{rm, rk, L.wd_m, wk, d.f_res, MODE_RES_ADD, nullptr};
     LAUNCH(launch_gemm(x8, L.wd, d.wide ? L.wd_lo : nullptr, R, H, F, ep, h, st, sp));

@@ -605,7 +605,13 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
-  const int aoff = (lane & 31) * K + kb, woff = (n0 + (lane & 31)) * K + kb;
+  // weight row of this lane's output column; in SWIGLU mode a tile's 32
+  // columns are gate columns j0 .. j0 + 15 then up columns j0 .. j0 + 15
+  // (j0 = n0 / 2), so each gate/up pair meets in one workgroup
+  const bool swg = e.mode == MODE_SWIGLU;
+  const int cl = lane & 31;
+  const int wrow = swg ? (cl < 16 ? (n0 >> 1) + cl : (N >> 1) + (n0 >> 1) + cl - 16) : n0 + cl;
+  const int aoff = (lane & 31) * K + kb, woff = wrow * K + kb;
 
   v16i acc[NB][MR];
 #pragma unroll
@@ -726,6 +732,26 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
       }
     }
     if (tid == 0) put(&sp.cnt[blockIdx.x], 0);  // ready for the next call
+  }
+  if (swg) {
+    // FIX value of this thread's gate or up column, then the gate thread
+    // (column c < 16) takes its up partner's from the lane 16 apart
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int i = m * 32 + (tid >> 5), ic = i < M ? i : M - 1, c = tid & 31;
+      const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
+      const int wrc = wr < N ? wr : N - 1;
+      int64_t v = hs[m];
+      if (WIDE) v = 256 * v + (int64_t)ls[m] + 128 * (int64_t)rss[m];
+      const int s = e.row_k[ic] + e.col_k - e.frac;
+      const int64_t y = WIDE ? R128((__int128)(v * e.row_m[ic]) * e.col_m[wrc], s)
+                             : R(v * e.row_m[ic] * e.col_m[wrc], s);
+      const int64_t u = __shfl_xor(y, 16);
+      const int j = (n0 >> 1) + c;
+      if (c < 16 && i < M && j < (N >> 1))
+        ((int64_t*)out)[(size_t)i * (N >> 1) + j] = R(y * sigmoid_q15(y, e.sw_mg, e.sw_kg), 15) * u;
+    }
+    return;
   }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -913,10 +939,17 @@ __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __re
 
 }  // namespace
 
+bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs) {
+  const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
+  return M > 16 && off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !limbs));
+}
+
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
                        const SplitWs* sp) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (e.mode == MODE_SWIGLU && (!gemm_takes_skinny(M, N, K, W_lo != nullptr) || N % 32 != 0))
+    return hipErrorInvalidValue;
   if (M <= 8 && K >= 16 && !W_lo && !e.out_row_base && fused_decode_supported(M, K) &&
       N * K < (int64_t(1) << 31) && ((uintptr_t)A & 3) == 0)
     return launch_fgemv_i8(A, W, M, N, K, e.row_m, e.row_k, e.col_m, e.col_k, e.frac, e.mode, out,

@@ -5,7 +5,7 @@
 
 namespace detint {
 
-enum { MODE_RAW = 0, MODE_REQ_I8 = 1, MODE_FIX = 2, MODE_RES_ADD = 3 };
+enum { MODE_RAW = 0, MODE_REQ_I8 = 1, MODE_FIX = 2, MODE_RES_ADD = 3, MODE_SWIGLU = 4 };
 
 // Dyadic epilogue parameters of a GEMM (see detint.h, detint_gemm_i8).
 struct Epi {
@@ -16,6 +16,11 @@ struct Epi {
   int32_t frac;
   int32_t mode;
   const int32_t* out_row_base;  // nullable: output row i goes to row *base + i
+  // MODE_SWIGLU (skinny GEMMs only): W holds F gate rows then F up rows
+  // (N = 2F, F % 16 == 0); gate and up go through the FIX epilogue (frac =
+  // f_a) and the int64 DI-SwiGLU product R(g sigmoid(g), 15) u is stored to
+  // out [M, F]. Sigmoid multiplier (sw_mg, sw_kg).
+  int32_t sw_mg, sw_kg;
 };
 
 // C = A[M,K] . W[N,K]^T with epilogue; W_lo != nullptr selects 16-bit limbs.
@@ -34,6 +39,9 @@ constexpr int64_t kSplitTileInts = 2 * 2 * 1024 + 2 * 32;
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
                        const SplitWs* sp = nullptr);
+// true when launch_gemm runs this shape on the skinny kernel (the only one
+// with MODE_SWIGLU)
+bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs);
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
                             hipStream_t st);
 // lm_head for M <= 16 rows: FIX-mode logits plus per-wave greedy-argmax
@@ -62,6 +70,9 @@ hipError_t launch_softmax(const int32_t* s, const int32_t* valid, const int32_t*
                           hipStream_t st);
 hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int32_t Mg,
                          int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st);
+// DQ of int64 SwiGLU products [R, n] -> int8, row scale (2^14, 2 f_a - e + 14)
+hipError_t launch_dq64(const int64_t* p, int64_t R, int64_t n, int32_t f_a, int8_t* a8,
+                       int32_t* row_m, int32_t* row_k, hipStream_t st);
 hipError_t launch_embed(const int32_t* ids, int64_t R, const int8_t* emb, const int8_t* emb_lo,
                         const int32_t* emb_m, int64_t H, int64_t V, int32_t shift, int32_t* h,
                         hipStream_t st);

@@ -306,6 +306,45 @@ __global__ __launch_bounds__(SWT) void swiglu_rk(const int32_t* __restrict__ gu,
   }
 }
 
+// The DQ half of DI-SwiGLU for products already formed (by a GEMM
+// epilogue): int64 rows -> int8, row scale (2^14, 2 f_a - e + 14).
+template <int U>
+__global__ __launch_bounds__(TPB) void dq64_rk(const int64_t* __restrict__ p, int n, int32_t f_a,
+                                               int8_t* __restrict__ a8, int32_t* __restrict__ rm,
+                                               int32_t* __restrict__ rk) {
+  using RR = RowRegs<TPB, U>;
+  typedef int64_t v2l __attribute__((ext_vector_type(2)));
+  __shared__ int64_t red[16];
+  const int r = blockIdx.x;
+  const int64_t* pr = p + (size_t)r * n;
+  v2l lo[U], hi[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    lo[u] = *(const v2l*)(pr + RR::at(u, n));
+    hi[u] = *(const v2l*)(pr + RR::at(u, n) + 2);
+  }
+  int64_t A = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (RR::first(u) >= n) lo[u] = hi[u] = v2l{0, 0};
+    const uint64_t a = uabs64(lo[u].x) > uabs64(lo[u].y) ? uabs64(lo[u].x) : uabs64(lo[u].y);
+    const uint64_t b = uabs64(hi[u].x) > uabs64(hi[u].y) ? uabs64(hi[u].x) : uabs64(hi[u].y);
+    const int64_t c = (int64_t)(a > b ? a : b);
+    A = c > A ? c : A;
+  }
+  A = block_max(A, red);
+  const int e = dq_exp((uint64_t)A);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (RR::first(u) < n)
+      *(uint32_t*)(a8 + (size_t)r * n + RR::first(u)) =
+          pack4(R_nn(lo[u].x, e), R_nn(lo[u].y, e), R_nn(hi[u].x, e), R_nn(hi[u].y, e));
+  if (threadIdx.x == 0) {
+    rm[r] = 1 << 14;
+    rk[r] = 2 * f_a - e + 14;
+  }
+}
+
 // Embedding rounded once onto the residual grid (BitExact blog, "Three
 // execution paths"): h = R(E[id] * m_v[id], w_k - f_res).
 __global__ __launch_bounds__(TPB) void embed_k(const int32_t* __restrict__ ids,
@@ -521,6 +560,25 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
     return hipGetLastError();
   }
   swiglu_k<<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq64(const int64_t* p, int64_t R, int64_t n, int32_t f_a, int8_t* a8,
+                       int32_t* row_m, int32_t* row_k, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (n % 4 != 0 || n < 4 || n > 32 * TPB || !aligned_to(p, 16) || !aligned_to(a8, 4))
+    return hipErrorInvalidValue;
+  const int u = (int)((n + 4 * TPB - 1) / (4 * TPB));
+#define DETINT_DQ(UU) dq64_rk<UU><<<(unsigned)R, TPB, 0, st>>>(p, (int)n, f_a, a8, row_m, row_k)
+  if (u <= 1)
+    DETINT_DQ(1);
+  else if (u <= 2)
+    DETINT_DQ(2);
+  else if (u <= 4)
+    DETINT_DQ(4);
+  else
+    DETINT_DQ(8);
+#undef DETINT_DQ
   return hipGetLastError();
 }
 
