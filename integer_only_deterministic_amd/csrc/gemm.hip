@@ -765,18 +765,20 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
   }
 }
 
-// K splits for a skinny GEMM: enough workgroups to cover the chip (about
-// 256), each split a multiple of 512 bytes of K, within the workspace.
+// K splits for a skinny GEMM: the most workgroups that still run as one
+// round (one 1024-thread workgroup per CU, 256 CUs: a second round would
+// repeat the whole load / reduce / epilogue latency), each split a multiple
+// of 512 bytes of K, within the workspace.
 int skinny_splits(int64_t N, int64_t K, const SplitWs* sp) {
   if (!sp || !sp->part) return 1;
   const int64_t tiles = (N + 31) / 32;
   if (tiles >= 256) return 1;  // already a workgroup per CU
   int ks = 1;
   for (int c = 2; c <= 16; ++c) {
+    if (tiles * c > 256) break;
     if (K % (c * 512) != 0) continue;
     if (tiles * c > sp->max_tile_splits || tiles > sp->max_tiles) break;
     ks = c;
-    if (tiles * c >= 256) break;
   }
   return ks;
 }
