@@ -226,6 +226,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, int64_
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
+// Epilogue helper: hands one 32x32 sub-tile's accumulators (both limb planes)
+// to the epilogue where it is used. The empty volatile asm is a point the
+// compiler cannot move their reads or their widening to 64 bits across, so it
+// no longer converts every accumulator of the tile at the end of the K loop
+// (256 values that do not fit the register file and went to scratch).
+template <int NB, typename Acc>
+__device__ __forceinline__ void pin_acc(Acc& acc, int a, int t) {
+  asm volatile("" : "+v"(acc[0][a][t]));
+  if (NB > 1) asm volatile("" : "+v"(acc[NB - 1][a][t]));
+}
+
 template <int BM, int BN, int ST, bool WIDE, int MODE>
 __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
                                                  const int8_t* __restrict__ W,
@@ -427,6 +438,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
       for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
         for (int t = 0; t < TN; ++t) {
+          if constexpr (WIDE) pin_acc<NB>(acc, a, t);
           const int j = n0 + wn * WN + t * 32 + (lane & 31);
           const int32_t cm = e.col_m[j];
           const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
@@ -484,6 +496,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
     for (int t = 0; t < TN; ++t) {
+      if constexpr (WIDE) pin_acc<NB>(acc, a, t);
       const int j = n0 + wn * WN + t * 32 + (lane & 31), jc = min(j, N - 1);
       const int32_t cm = MODE != MODE_RAW ? e.col_m[jc] : 0;
       const int lb = wm * WM + a * 32 + 4 * (lane >> 5);

@@ -150,6 +150,10 @@ def test_gemm_w16_limbs(D, M, N, K):
                                   O.epilogue(acc, rm, rk, cm, 30, 12, O.FIX))
     np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 0, D.REQ_I8)),
                                   O.epilogue(acc, rm, rk, cm, 30, 0, O.REQ_I8))
+    base = rng.integers(-(1 << 20), 1 << 20, (M, N)).astype(np.int32)
+    out = dev(base)
+    D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 12, D.RES_ADD, out=out)
+    np.testing.assert_array_equal(host(out), O.epilogue(acc, rm, rk, cm, 30, 12, O.RES_ADD, out=base))
 
 
 # -------------------------------------------------------------- row ops
