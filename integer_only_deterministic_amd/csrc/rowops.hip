@@ -306,6 +306,92 @@ __global__ __launch_bounds__(SWT) void swiglu_rk(const int32_t* __restrict__ gu,
   }
 }
 
+// Quotients of the integer sigmoid, q(E) = RD(2^30, 2^15 + E) for every
+// DI-Exp output E in [0, 2^15] (the same rounded division sigmoid_q15 runs
+// bit-serially), evaluated by the compiler as exact integer constant
+// expressions. 32769 entries, padded to a whole number of 16-byte chunks.
+constexpr int kSigEntries = 32769, kSigPad = 32776;
+struct alignas(16) SigTable {
+  uint16_t q[kSigPad];
+};
+constexpr SigTable make_sig_table() {
+  SigTable t{};
+  for (uint32_t E = 0; E < (uint32_t)kSigEntries; ++E) {
+    const uint64_t b = 32768u + E;
+    t.q[E] = (uint16_t)(((uint64_t(1) << 31) + b) / (2 * b));
+  }
+  return t;
+}
+__device__ const SigTable kSigTable = make_sig_table();
+constexpr size_t kSigLds = sizeof(SigTable);  // 65552 bytes
+
+// DI-SwiGLU for many rows (prefill): a persistent grid whose workgroups copy
+// the sigmoid quotients into LDS once and then take rows w, w + G, ...; the
+// sigmoid's division becomes one LDS lookup. Each row's inputs for the next
+// row are loaded while the current one is computed. Same integer function
+// as swiglu_rk, row for row.
+template <int U>
+__global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__ gu, int rows, int n,
+                                                     int32_t f_a, int32_t Mg, int32_t Kg,
+                                                     int8_t* __restrict__ a8,
+                                                     int32_t* __restrict__ rm,
+                                                     int32_t* __restrict__ rk) {
+  using RR = RowRegs<SWT, U>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t tab[];  // kSigPad entries
+  __shared__ int64_t red[16];
+  for (int i = threadIdx.x; i < kSigPad / 8; i += SWT)
+    ((v4i*)tab)[i] = ((const v4i*)kSigTable.q)[i];
+  const int G = (int)gridDim.x;
+  int r = blockIdx.x;
+  v4i gv[U], uv[U];
+  auto load = [&](int row, v4i (&gg)[U], v4i (&uu)[U]) {
+    const int32_t* g = gu + (size_t)row * 2 * n;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      gg[u] = *(const v4i*)(g + RR::at(u, n));
+      uu[u] = *(const v4i*)(g + n + RR::at(u, n));
+    }
+  };
+  load(r, gv, uv);
+  __syncthreads();  // table resident
+  for (; r < rows; r += G) {
+    v4i gn[U], un[U];
+    load(min(r + G, rows - 1), gn, un);  // next row (clamped: the last row reloads itself)
+    int64_t p[U][4], A = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = RR::first(u) < n;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t g = gv[u][e4];
+        const int64_t ag = g < 0 ? -g : g;
+        const int E = min(diexp(-R(ag * Mg, Kg)), kSigEntries - 1);
+        const int32_t q = tab[E];
+        const int32_t sig = g >= 0 ? q : 32768 - q;
+        p[u][e4] = ok ? R(g * sig, 15) * (int64_t)uv[u][e4] : 0;
+        const int64_t a = (int64_t)uabs64(p[u][e4]);
+        A = a > A ? a : A;
+      }
+    }
+    A = block_max(A, red);
+    const int e = dq_exp((uint64_t)A);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (RR::first(u) < n)
+        *(uint32_t*)(a8 + (size_t)r * n + RR::first(u)) =
+            pack4(R_nn(p[u][0], e), R_nn(p[u][1], e), R_nn(p[u][2], e), R_nn(p[u][3], e));
+    if (threadIdx.x == 0) {
+      rm[r] = 1 << 14;
+      rk[r] = 2 * f_a - e + 14;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      gv[u] = gn[u];
+      uv[u] = un[u];
+    }
+  }
+}
+
 // The DQ half of DI-SwiGLU for products already formed (by a GEMM
 // epilogue): int64 rows -> int8, row scale (2^14, 2 f_a - e + 14).
 template <int U>
@@ -553,6 +639,25 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
   if (R == 0) return hipSuccess;
   if (n > SWT * SWPER) return hipErrorInvalidValue;
   if (n % 4 == 0 && n >= 4 && aligned_to(gu, 16) && aligned_to(a8, 4)) {
+    if (R > 64) {
+      // persistent, two workgroups per CU (the table takes 64 KiB of LDS)
+      static bool attr = false;
+      if (!attr) {
+        hipError_t err = hipFuncSetAttribute((const void*)swiglu_tab_rk<1>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kSigLds);
+        if (err == hipSuccess)
+          err = hipFuncSetAttribute((const void*)swiglu_tab_rk<2>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kSigLds);
+        if (err != hipSuccess) return err;
+        attr = true;
+      }
+      const unsigned grid = (unsigned)(R < 512 ? R : 512);
+      if (n <= 4 * SWT)
+        swiglu_tab_rk<1><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+      else
+        swiglu_tab_rk<2><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+      return hipGetLastError();
+    }
     if (n <= 4 * SWT)
       swiglu_rk<1><<<(unsigned)R, SWT, 0, st>>>(gu, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
     else

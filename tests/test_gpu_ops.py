@@ -234,13 +234,31 @@ def test_softmax(D):
     np.testing.assert_array_equal(host(P), O.softmax(s, valid, shift, M, K))
 
 
-@pytest.mark.parametrize("R,n", [(1, 3072), (13, 768), (4, 8192), (3, 998), (2, 4100)])
+# More than 64 rows take the persistent kernel with the sigmoid quotients in
+# LDS (ragged against its 512-workgroup grid at 700 rows).
+@pytest.mark.parametrize("R,n", [(1, 3072), (13, 768), (4, 8192), (3, 998), (2, 4100), (65, 3072),
+                                 (700, 8192), (130, 4100)])
 def test_swiglu(D, R, n):
     rng = np.random.default_rng(R * 3 + n)
     gu = rng.normal(0, 8 * 4096, (R, 2 * n)).astype(np.int32)
     gu[0, :n] = 0
     gu[-1, 5] = (1 << 24) - 1
     gu[-1, 6] = -(1 << 24) + 1
+    a8, m, k = D.detint_swiglu(dev(gu), 12)
+    oa, om, ok = O.swiglu(gu, 12)
+    np.testing.assert_array_equal(host(a8), oa)
+    np.testing.assert_array_equal(host(m), om)
+    np.testing.assert_array_equal(host(k), ok)
+
+
+def test_swiglu_every_gate(D):
+    """Every gate value in [-2^17, 2^17) exactly once (256 shuffled rows of
+    1024, so the table-driven kernel runs): with f_a = 12 larger gates all give
+    DI-Exp output 0, so this reaches every sigmoid quotient a gate can select."""
+    rng = np.random.default_rng(17)
+    g = rng.permutation(np.arange(-(1 << 17), 1 << 17, dtype=np.int64)).astype(np.int32)
+    u = rng.integers(-(1 << 16), 1 << 16, g.size).astype(np.int32)
+    gu = np.concatenate([g.reshape(256, 1024), u.reshape(256, 1024)], axis=1)
     a8, m, k = D.detint_swiglu(dev(gu), 12)
     oa, om, ok = O.swiglu(gu, 12)
     np.testing.assert_array_equal(host(a8), oa)
