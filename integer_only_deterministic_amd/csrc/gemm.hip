@@ -7,8 +7,9 @@
 //
 //  * gemm_pipe: M > 16 and K a multiple of 128. BMxBN output tile (256x256,
 //    128x256 or 128x128, chosen by how many tiles the shape gives) per
-//    256-thread workgroup; each wave owns a (BM/2)x(BN/2) quadrant of
-//    v_mfma_i32_32x32x32_i8 tiles with the accumulators in AGPRs. K advances
+//    workgroup of a WGM x WGN grid of waves (2 x 2, or 2 x 4 for the 256x256
+//    int8 tiling); each wave owns a (BM/WGM)x(BN/WGN) block of
+//    v_mfma_i32_32x32x32_i8 tiles with the accumulators in registers. K advances
 //    128 bytes per tile through an ST-deep LDS ring filled by buffer loads
 //    that write LDS directly (no register staging; rows past M or N read as
 //    zero through the buffer bounds). 16-byte chunks are XOR-swizzled by row
@@ -237,17 +238,19 @@ __device__ __forceinline__ void pin_acc(Acc& acc, int a, int t) {
   if (NB > 1) asm volatile("" : "+v"(acc[NB - 1][a][t]));
 }
 
-template <int BM, int BN, int ST, bool WIDE, int MODE>
-__global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
+template <int BM, int BN, int ST, bool WIDE, int MODE, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __restrict__ A,
                                                  const int8_t* __restrict__ W,
                                                  const int8_t* __restrict__ Wlo, int M, int N,
                                                  int K, Epi e, void* out) {
   constexpr int NB = WIDE ? 2 : 1;             // weight planes
   constexpr int CPR = PBK / 16;                // chunks per row
   constexpr int SA = BM * PBK, SB = BN * PBK;  // bytes per stage and operand
-  constexpr int LA = SA / 4096, LB = SB / 4096;  // buffer loads per thread per stage
+  constexpr int NT = 64 * WGM * WGN;           // threads: a WGM x WGN grid of waves
+  constexpr int LA = SA / (16 * NT), LB = SB / (16 * NT);  // buffer loads per thread per stage
   constexpr int LT = LA + NB * LB;
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  static_assert(LA * 16 * NT == SA && LB * 16 * NT == SB, "stage must split evenly over the threads");
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   constexpr int NS = PBK / 32;                 // MFMA k-steps per tile
   static_assert(NS % 2 == 0, "fragment double buffer assumes an even step count");
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS DMA bases in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   // Tile order. Workgroups are dealt round-robin to the 8 XCDs: give each XCD
   // a contiguous run of logical tiles, then sweep groups of 8 tile rows
   // column by column, so an XCD's L2 holds the A rows and W columns it reuses.
@@ -273,21 +276,21 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
-  // stage kt % ST <- tile kt. Load q of thread t moves chunk g = 256q + t of
+  // stage kt % ST <- tile kt. Load q of thread t moves chunk g = NT q + t of
   // the stage: LDS bytes [16g, 16g + 16) = row g / 8, physical chunk g % 8.
   // Loads 0 .. LA-1 fill A, the rest the weight plane(s).
   auto issue_one = [&](int kt, int i) {
     const int st = kt % ST, k0 = kt * PBK;
     if (i < LA) {
-      const int g = i * 256 + tid, r = g / CPR;
+      const int g = i * NT + tid, r = g / CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, DETINT_LDS(sA + st * SA + (i * 256 + wave * 64) * 16), 16,
+          ra, DETINT_LDS(sA + st * SA + (i * NT + wave * 64) * 16), 16,
           (m0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
     } else {
       const int p = (i - LA) / LB, q = (i - LA) % LB;
-      const int g = q * 256 + tid, r = g / CPR;
+      const int g = q * NT + tid, r = g / CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          p ? rl : rb, DETINT_LDS(sB + (st * NB + p) * SB + (q * 256 + wave * 64) * 16), 16,
+          p ? rl : rb, DETINT_LDS(sB + (st * NB + p) * SB + (q * NT + wave * 64) * 16), 16,
           (n0 + r) * K + k0 + pswz(g % CPR, r) * 16, 0, 0, 0);
     }
   };
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
   const int csh = e.col_k - (MODE == MODE_REQ_I8 ? 0 : e.frac);
   int slow = 0, narrow = 0;
   if (MODE != MODE_RAW) {
-    for (int t = tid; t < BM; t += 256) {
+    for (int t = tid; t < BM; t += NT) {
       const int i = min(m0 + t, M - 1);
       const int rm = e.row_m[i], sh = e.row_k[i] + csh;
       s_rm[t] = rm;
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
       slow |= (unsigned)rm >= 32768u || (WIDE ? sh < 32 || sh > 94 : sh < 1 || sh > 62);
       narrow |= sh < 33;
     }
-    for (int t = tid; t < BN; t += 256) slow |= (unsigned)e.col_m[min(n0 + t, N - 1)] >= 32768u;
+    for (int t = tid; t < BN; t += NT) slow |= (unsigned)e.col_m[min(n0 + t, N - 1)] >= 32768u;
   }
   const int64_t obase = e.out_row_base ? *e.out_row_base : 0;
   slow = __syncthreads_or(slow);
@@ -539,35 +542,43 @@ __global__ __launch_bounds__(256) void gemm_pipe(const int8_t* __restrict__ A,
     }
 }
 
-template <int BM, int BN, int ST, bool WIDE, int MODE>
+template <int BM, int BN, int ST, bool WIDE, int MODE, int WGM, int WGN>
 hipError_t pipe_launch_m(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                          const Epi& e, void* out, hipStream_t st) {
   constexpr int lds = ST * (BM + (WIDE ? 2 : 1) * BN) * PBK;
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the workgroup limit");
   static bool attr = false;
   if (!attr) {
-    const hipError_t err = hipFuncSetAttribute((const void*)gemm_pipe<BM, BN, ST, WIDE, MODE>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const hipError_t err =
+        hipFuncSetAttribute((const void*)gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
     attr = true;
   }
   const int nb = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  gemm_pipe<BM, BN, ST, WIDE, MODE><<<nb, 256, lds, st>>>(A, W, Wlo, M, N, K, e, out);
+  gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN><<<nb, 64 * WGM * WGN, lds, st>>>(A, W, Wlo, M, N, K, e,
+                                                                              out);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int ST, bool WIDE>
+template <int BM, int BN, int ST, bool WIDE, int WGM = 2, int WGN = 2>
 hipError_t pipe_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                        const Epi& e, void* out, hipStream_t st) {
   switch (e.mode) {
-    case MODE_RAW: return pipe_launch_m<BM, BN, ST, WIDE, MODE_RAW>(A, W, Wlo, M, N, K, e, out, st);
-    case MODE_REQ_I8: return pipe_launch_m<BM, BN, ST, WIDE, MODE_REQ_I8>(A, W, Wlo, M, N, K, e, out, st);
-    case MODE_FIX: return pipe_launch_m<BM, BN, ST, WIDE, MODE_FIX>(A, W, Wlo, M, N, K, e, out, st);
-    default: return pipe_launch_m<BM, BN, ST, WIDE, MODE_RES_ADD>(A, W, Wlo, M, N, K, e, out, st);
+    case MODE_RAW:
+      return pipe_launch_m<BM, BN, ST, WIDE, MODE_RAW, WGM, WGN>(A, W, Wlo, M, N, K, e, out, st);
+    case MODE_REQ_I8:
+      return pipe_launch_m<BM, BN, ST, WIDE, MODE_REQ_I8, WGM, WGN>(A, W, Wlo, M, N, K, e, out, st);
+    case MODE_FIX:
+      return pipe_launch_m<BM, BN, ST, WIDE, MODE_FIX, WGM, WGN>(A, W, Wlo, M, N, K, e, out, st);
+    default:
+      return pipe_launch_m<BM, BN, ST, WIDE, MODE_RES_ADD, WGM, WGN>(A, W, Wlo, M, N, K, e, out, st);
   }
 }
 
-// Largest tile that still gives the chip most of a wave of workgroups.
+// Largest tile that still gives the chip most of a wave of workgroups. The
+// 256x256 int8 tiling runs 8 waves (two per SIMD, 128x64 each, accumulators
+// in VGPRs), measured 3-16% faster than 4; with limbs 4 waves are as fast.
 template <bool WIDE>
 hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N,
                          int K, const Epi& e, void* out, hipStream_t st) {
@@ -577,7 +588,7 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
     if (tiles(256, 128) >= FILL) return pipe_launch<256, 128, 2, true>(A, W, Wlo, M, N, K, e, out, st);
     return pipe_launch<128, 128, 3, true>(A, W, Wlo, M, N, K, e, out, st);
   }
-  if (tiles(256, 256) >= FILL) return pipe_launch<256, 256, 2, false>(A, W, Wlo, M, N, K, e, out, st);
+  if (tiles(256, 256) >= FILL) return pipe_launch<256, 256, 2, false, 2, 4>(A, W, Wlo, M, N, K, e, out, st);
   if (tiles(128, 256) >= FILL) return pipe_launch<128, 256, 3, false>(A, W, Wlo, M, N, K, e, out, st);
   return pipe_launch<128, 128, 4, false>(A, W, Wlo, M, N, K, e, out, st);
 }
