@@ -331,16 +331,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   };
   // The MFMAs of one k-step; when kt_load >= 0 the LT loads of that tile go
   // out one after each MFMA, so their issue overlaps matrix work.
-  auto mma = [&](int buf, int kt_load) {
+  // first: MFMAs with index (p TM + a) TN + t below it are issued by an
+  // earlier call (mma_first) for the same step.
+  auto mma = [&](int buf, int kt_load, auto first_c) {
+    constexpr int first = decltype(first_c)::value;
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
+          const int i = (p * TM + a) * TN + t;
+          if (i < first) continue;
           acc[p][a][t] =
               __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][a], fb[buf][p][t], acc[p][a][t], 0, 0, 0);
-          const int i = (p * TM + a) * TN + t;
           if (i < LT && kt_load >= 0) issue_one(kt_load, i);
         }
 #pragma unroll
@@ -350,6 +354,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
       const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
       for (int a = 0; a < TM; ++a) rsum[a] = dot16(fa[buf][a], ones, rsum[a]);
+    }
+  };
+
+  // The first two MFMAs of a step, issued before that step's reads of the
+  // next step's fragments, so no MFMA waits on a read issued in its own step.
+  constexpr int PRE = 2;
+  static_assert(NB * TM * TN >= PRE, "fewer MFMAs per step than the lead-in");
+  auto mma_first = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+      const int p = i / (TM * TN), a = (i / TN) % TM, t = i % TN;
+      acc[p][a][t] =
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][a], fb[buf][p][t], acc[p][a][t], 0, 0, 0);
     }
   };
 
@@ -369,8 +386,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
     for (int s = 0; s < NS; ++s) {
       const int buf = s & 1;
       if (s + 1 < NS) {
+        mma_first(buf);
+        __builtin_amdgcn_sched_barrier(0);
         frag(kt, s + 1, buf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
+        mma(buf, -1, std::integral_constant<int, PRE>{});
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
       } else if (kt + 1 < nk) {
         // Tile kt+1 resident (own loads counted, others' by the barrier) and
         // every wave's reads of tile kt issued and complete, so its stage can
@@ -384,7 +406,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
         frag(kt + 1, 0, buf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      mma(buf, (s + 1 == NS && kt + ST < nk) ? kt + ST : -1);
+      mma(buf, kt + ST < nk ? kt + ST : -1, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
     }
   }
