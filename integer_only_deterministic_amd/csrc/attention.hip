@@ -49,6 +49,29 @@ __device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh)
   return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
 }
 
+// exp_delta in 32-bit arithmetic. v >= 31 * 2^15 (E = 0) exactly when
+// delta * M >= T = 31 * 2^(15 + sh) - 2^(sh - 1) + 1, i.e. delta >= d0 =
+// ceil(T / M); clamping delta to d0 keeps that outcome and bounds the product
+// by T + M < 2^32 when 1 <= sh <= 11 and 2^10 <= M < 2^15 (then d0 < 2^22, so
+// one 24-bit multiply is exact, and v < 32 * 2^15 keeps every shift below
+// 32). Branch-free; same value as exp_delta.
+__device__ __forceinline__ int32_t exp_delta32(uint32_t delta, uint32_t M, int sh, uint32_t d0) {
+  const uint32_t x = __umul24(min(delta, d0), M);
+  const uint32_t v = (x + ((1u << (sh - 1)) - 1u)) >> sh;
+  const uint32_t n = v >> 15;  // <= 31 after the clamp
+  const uint32_t f = 32768u - (((v & 32767u) + 1u) >> 1);
+  const uint32_t E = (f + ((1u << n) >> 1)) >> n;
+  return v >= (31u << 15) ? 0 : (int32_t)E;
+}
+
+// d0 of exp_delta32 for a lane's (M, sh), or 0 when the lane is outside its
+// range (1 <= sh <= 11, 2^10 <= M < 2^15).
+__device__ __forceinline__ uint32_t exp32_limit(int32_t M, int sh) {
+  if (sh < 1 || sh > 11 || M < (1 << 10) || M >= (1 << 15)) return 0;
+  const uint64_t T = (uint64_t(31) << (15 + sh)) - (uint64_t(1) << (sh - 1)) + 1;
+  return (uint32_t)udiv_q<23>(T + (uint64_t)M - 1, (uint64_t)M);  // ceil(T / M) < 2^22
+}
+
 // Transposed partial reduction of N int32 values per lane over the lane
 // offsets O, O/2, ..., OMIN: each step keeps half of the values and adds the
 // partner's copy of them, so N - N / 2^steps exchanges replace
@@ -724,6 +747,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const int sh = Ks - (rvalid ? e_q[(size_t)row * nq + hq] : 0);
   const bool fast = sh >= 1 && sh <= 62 && Ms > 0;
   const bool wfast = __all(fast);  // every lane of the wave on the fast form
+  const uint32_t d0 = exp32_limit(Ms, sh);
+  const bool wfast32 = __all(d0 != 0);  // ... and on its 32-bit form
   // chunks below every query of this wave's tile need no causal mask
   const int pmin = p0 + qb * QP + (wave / G) * 32;
 
@@ -786,7 +811,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       const v16i sacc = scores(c);
       const int lim = pos - c * 32;  // key offsets <= lim are causal
       int32_t part = 0;              // 16 terms of at most 2^15
-      if (wfast) {
+      if (wfast32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t E = exp_delta32((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh, d0);
+          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
+        }
+      } else if (wfast) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int32_t E = exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh);
@@ -855,7 +886,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       ph[r >> 2] |= (P >> 8) << (8 * (r & 3));
       pl[r >> 2] |= ((P & 255u) ^ 128u) << (8 * (r & 3));  // (P & 255) - 128 as a byte
     };
-    if (wfast) {
+    if (wfast32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put(r, exp_delta32((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh, d0));
+    } else if (wfast) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) put(r, exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh));
     } else {
