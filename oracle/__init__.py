@@ -51,6 +51,7 @@ def lib():
 i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
 i16p = np.ctypeslib.ndpointer(np.int16, flags="C_CONTIGUOUS")
 i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+u32p = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
 i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
 vp = C.c_void_p
 i64 = C.c_int64
@@ -121,6 +122,7 @@ def _declare(L):
     L.orc_forward.argtypes = [C.POINTER(OrcModel), i32p, i64, i32p, i32p, i32p, i64,
                               i8p, i8p, i64, i32, i32p, vp]
     L.orc_argmax.argtypes = [i32p, i64, i64, i32p]
+    L.orc_sample.argtypes = [i32p, i64, i64, i64, i32, i32, u32p, i32p]
     L.orc_attention.argtypes = [i8p, i32p, i8p, i8p, i32p, i32p, i64, i64, i64, i64, i64, i64,
                                 i32, i32, i32p]
 
@@ -315,6 +317,19 @@ def argmax(logits):
     R_, V = logits.shape
     out = np.zeros(R_, np.int32)
     lib().orc_argmax(logits, R_, V, out)
+    return out
+
+
+def sample(logits, top_k: int, t_m: int, t_k: int, draws):
+    """Integer temperature / top-k sampling of each row with the caller's
+    uniform 32-bit draws (orc_sample states the reading)."""
+    logits = _c(logits, np.int32)
+    R_, V = logits.shape
+    draws = _c(draws, np.uint32)
+    assert draws.shape == (R_,)
+    out = np.zeros(R_, np.int32)
+    lib().orc_sample(logits, R_, V, int(top_k), int(t_m), int(t_k), draws, out)
+    _check()
     return out
 
 

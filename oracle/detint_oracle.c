@@ -748,6 +748,68 @@ int orc_argmax(const int32_t *logits, int64_t rows, int64_t V, int32_t *out) {
   return 0;
 }
 
+/* Integer sampling with temperature and top-k ([BITEXACT] intro: sampling
+ * rules are part of the integer arithmetic, and deterministic sampling is
+ * named among its unavoidable costs; [BLOG] limits section: integer sampling
+ * left open). The pages give no formula; the reading taken here:
+ *  - order: key(j) ranks a larger logit first and, among equal logits, the
+ *    lower id first (the greedy tie rule, [BLOG] "DetLLM");
+ *  - top-k: the k highest-ranked ids are kept (k <= 0 or k >= V keeps all);
+ *  - weights: E_j = DI-Exp(R((l_j - l_max) * t_m, t_k)) for kept ids, else 0:
+ *    the temperature is the dyadic t_m / 2^t_k applied to the logit gap in
+ *    DI-Exp's base-2 Q15 units (the softmax's own exponential), so the
+ *    maximum gets E = 2^15 and D = sum E >= 2^15;
+ *  - draw: the caller's uniform 32-bit integer r selects t = floor(r D / 2^32),
+ *    in [0, D);
+ *  - token: the smallest id j with E_0 + ... + E_j > t.
+ * Bounds: 1 <= t_m < 2^24, 0 <= t_k <= 62 (the gap times t_m stays < 2^56). */
+static const int32_t *g_sort_row;
+static int key_desc(const void *a, const void *b) {
+  const int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+  const int32_t li = g_sort_row[i], lj = g_sort_row[j];
+  if (li != lj) return li > lj ? -1 : 1;
+  return i < j ? -1 : (i > j ? 1 : 0);
+}
+
+int orc_sample(const int32_t *logits, int64_t rows, int64_t V, int64_t k, int32_t t_m,
+               int32_t t_k, const uint32_t *draws, int32_t *out) {
+  CHECK(V >= 1, "sample: V < 1");
+  CHECK(t_m >= 1 && t_m < (1 << 24) && t_k >= 0 && t_k <= 62, "sample: temperature dyadic");
+  if (g_err) return g_err;
+  const int64_t keep = (k <= 0 || k >= V) ? V : k;
+  int32_t *idx = (int32_t *)malloc((size_t)V * sizeof(int32_t));
+  uint8_t *kept = (uint8_t *)malloc((size_t)V);
+  for (int64_t o = 0; o < rows && !g_err; o++) {
+    const int32_t *l = logits + o * V;
+    int64_t lmax = l[0];
+    for (int64_t j = 1; j < V; j++) if (l[j] > lmax) lmax = l[j];
+    if (keep == V) {
+      memset(kept, 1, (size_t)V);
+    } else {
+      for (int64_t j = 0; j < V; j++) idx[j] = (int32_t)j;
+      g_sort_row = l;
+      qsort(idx, (size_t)V, sizeof(int32_t), key_desc);
+      memset(kept, 0, (size_t)V);
+      for (int64_t i = 0; i < keep; i++) kept[idx[i]] = 1;
+    }
+    int64_t D = 0;
+    for (int64_t j = 0; j < V; j++)
+      if (kept[j]) D += orc_diexp(R(((int64_t)l[j] - lmax) * t_m, t_k));
+    CHECK(D >= 32768, "sample: D < 2^15");
+    const int64_t t = (int64_t)(((unsigned __int128)draws[o] * (uint64_t)D) >> 32);
+    int64_t cum = 0, tok = -1;
+    for (int64_t j = 0; j < V && tok < 0; j++) {
+      if (kept[j]) cum += orc_diexp(R(((int64_t)l[j] - lmax) * t_m, t_k));
+      if (cum > t) tok = j;
+    }
+    CHECK(tok >= 0, "sample: no token");
+    out[o] = (int32_t)tok;
+  }
+  free(idx);
+  free(kept);
+  return g_err;
+}
+
 /* Whole forward: ids -> embedding -> layers -> final RMSNorm -> tied lm_head
  * -> int32 logits ([README] intro: ids to int32 logits with no float), for the
  * last row of every sequence (all rows when all_rows != 0), and the greedy
