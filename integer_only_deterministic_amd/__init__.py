@@ -77,6 +77,7 @@ _SIGS = {
     "detint_lm_head_parts": (i64, [i64]),
     "detint_lm_head": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp]),
     "detint_argmax_parts": (i32, [vp, i64, i64, vp, vp]),
+    "detint_sample": (i32, [vp, i64, i64, i64, i32, i32, vp, vp, vp]),
     "detint_final_head_workspace": (i64, [i64, i64, i64]),
     "detint_final_head": (i32, [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, vp]),
     "detint_layer_forward": (i32, [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, vp, i64,
@@ -279,6 +280,20 @@ def detint_argmax_parts(part):
     S_, npart = part.shape
     out = torch.empty(S_, dtype=torch.int32, device=part.device)
     _call("detint_argmax_parts", _p(part, torch.int64), S_, npart, _p(out), _stream())
+    return out
+
+
+def detint_sample(logits, top_k: int, t_m: int, t_k: int, draws, out=None):
+    """Integer temperature / top-k sampling of each row with the caller's
+    uniform uint32 draws (see detint.h)."""
+    torch = _torch()
+    R_, V = logits.shape
+    if out is None:
+        out = torch.empty(R_, dtype=torch.int32, device=logits.device)
+    if draws.dtype not in (torch.int32, torch.uint32) or draws.shape != (R_,):
+        raise TypeError("draws: one 32-bit integer per row (uint32, or int32 holding the bits)")
+    _call("detint_sample", _p(logits, torch.int32), R_, V, int(top_k), int(t_m), int(t_k),
+          _p(draws), _p(out), _stream())
     return out
 
 

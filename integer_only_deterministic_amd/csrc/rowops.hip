@@ -755,4 +755,128 @@ hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- sampling
+
+// Integer temperature / top-k sampling, one 1024-thread workgroup per row
+// (BitExact blog intro: sampling rules in integer arithmetic; DetLLM blog,
+// limits: integer sampling left open). Same function as detint.h states:
+// keep the k highest-ranked ids (larger logit first, lower id on ties),
+// weight each by E = DI-Exp(R((l - l_max) t_m, t_k)), draw t = floor(r D /
+// 2^32) from the caller's uniform 32-bit r, and return the smallest id whose
+// running weight exceeds t. Every reduction is an integer max, count or sum,
+// so the thread layout changes no result.
+constexpr int SMT = 1024, SMW = SMT / 64;
+
+// Inclusive prefix sum over the workgroup (thread order); *total gets the sum.
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wsum, int64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  __syncthreads();  // wsum free (an earlier scan may still read it)
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < SMW; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  *total = all;
+  return before + v;
+}
+
+__global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
+                                               int32_t t_m, int32_t t_k,
+                                               const uint32_t* __restrict__ draws,
+                                               int32_t* __restrict__ out) {
+  __shared__ int32_t hist[256];
+  __shared__ int64_t red[16], wsum[SMW];
+  __shared__ int32_t s_sel[3];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int32_t* l = logits + (size_t)r * V;
+  int32_t mx = INT32_MIN;
+  for (int j = tid; j < V; j += SMT) mx = max(mx, l[j]);
+  mx = (int32_t)block_max(mx, red);
+  // contiguous chunk of this thread (id order for the scans)
+  const int C = (V + SMT - 1) / SMT, lo = min(V, tid * C), hi = min(V, lo + C);
+  // kept(j): l_j > Lk, or l_j == Lk and j <= idk
+  int32_t Lk = INT32_MIN;
+  int idk = V - 1;
+  if (keep < V) {
+    // radix select of the keep-th largest value on the order-preserving key
+    uint32_t prefix = 0, pmask = 0;
+    int rem = keep;  // rank (from the top, 1-based) inside the current bucket
+    for (int sh = 24; sh >= 0; sh -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int j = tid; j < V; j += SMT) {
+        const uint32_t u = (uint32_t)l[j] ^ 0x80000000u;
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int c = 0, d = 255;
+        for (; d > 0; --d) {
+          if (c + hist[d] >= rem) break;
+          c += hist[d];
+        }
+        s_sel[0] = d;
+        s_sel[1] = rem - c;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_sel[0] << sh;
+      pmask |= 255u << sh;
+      rem = s_sel[1];
+    }
+    Lk = (int32_t)(prefix ^ 0x80000000u);
+    // the rem-th lowest id among the values equal to Lk
+    int cnt = 0;
+    for (int j = lo; j < hi; ++j) cnt += l[j] == Lk;
+    int64_t tot;
+    const int64_t incl = block_scan(cnt, wsum, &tot);
+    const int64_t excl = incl - cnt;
+    if (excl < rem && incl >= rem) {
+      int need = rem - (int)excl;
+      for (int j = lo; j < hi; ++j)
+        if (l[j] == Lk && --need == 0) {
+          s_sel[2] = j;
+          break;
+        }
+    }
+    __syncthreads();
+    idk = s_sel[2];
+  }
+  auto weight = [&](int j) -> int64_t {
+    const int32_t v = l[j];
+    const bool kept = v > Lk || (v == Lk && j <= idk);
+    return kept ? (int64_t)diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k)) : 0;
+  };
+  int64_t sum = 0;
+  for (int j = lo; j < hi; ++j) sum += weight(j);
+  int64_t D;
+  const int64_t incl = block_scan(sum, wsum, &D);
+  const int64_t excl = incl - sum;
+  const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
+  if (excl <= t && t < incl) {
+    int64_t cum = excl;
+    for (int j = lo; j < hi; ++j) {
+      cum += weight(j);
+      if (cum > t) {
+        out[r] = j;
+        break;
+      }
+    }
+  }
+}
+
+hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t t_m,
+                         int32_t t_k, const uint32_t* draws, int32_t* out, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, t_m, t_k, draws, out);
+  return hipGetLastError();
+}
+
 }  // namespace detint

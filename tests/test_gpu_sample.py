@@ -1,0 +1,66 @@
+"""GPU parity of detint_sample (integer temperature / top-k sampling) with the
+oracle, token for token."""
+import numpy as np
+import pytest
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+T1 = (23637, 15)          # temperature 1 for logits with 16 fractional bits
+HOT = (23637, 17)         # temperature 4
+COLD = (1 << 23, 0)       # any gap of one unit already has weight 0
+
+
+@pytest.fixture(scope="module")
+def D():
+    import torch
+    import integer_only_deterministic_amd as D
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    D.library()
+    return D
+
+
+def _run(D, logits, k, tm, draws):
+    import torch
+    lg = torch.from_numpy(logits).cuda()
+    dr = torch.from_numpy(draws.view(np.int32)).cuda()
+    return D.detint_sample(lg, k, tm[0], tm[1], dr).cpu().numpy()
+
+
+def _logits(kind, R, V, rng):
+    if kind == "spread":   # gaps of a few units at 16 fractional bits
+        return rng.normal(0, 3 * 65536, (R, V)).astype(np.int32)
+    if kind == "ties":     # few distinct values: ties at the top-k boundary
+        return (rng.integers(-4, 4, (R, V)) * 65536).astype(np.int32)
+    x = rng.integers(-(1 << 31), 1 << 31, (R, V), dtype=np.int64).astype(np.int32)
+    x[:, 0] = np.iinfo(np.int32).min
+    x[:, -1] = np.iinfo(np.int32).max
+    return x               # "extreme": the whole int32 range
+
+
+@pytest.mark.parametrize("V", [1, 7, 1000, 4099, 151936])
+@pytest.mark.parametrize("kind", ["spread", "ties", "extreme"])
+def test_sample_matches_oracle(D, V, kind):
+    rng = np.random.default_rng(V + len(kind))
+    R = 6
+    logits = _logits(kind, R, V, rng)
+    draws = rng.integers(0, 1 << 32, R, dtype=np.uint64).astype(np.uint32)
+    draws[:2] = [0, (1 << 32) - 1]
+    for k in sorted({0, 1, 5, 50, max(V - 1, 1), V}):
+        for tm in (T1, HOT, COLD):
+            want = O.sample(logits, k, tm[0], tm[1], draws)
+            got = _run(D, logits, k, tm, draws)
+            np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm}")
+
+
+def test_sample_many_draws_one_row(D):
+    """One row, 4096 draws across [0, 2^32): every boundary of the inverse
+    CDF the draws land on matches the oracle."""
+    rng = np.random.default_rng(11)
+    row = rng.normal(0, 2 * 65536, 3000).astype(np.int32)
+    draws = np.sort(rng.integers(0, 1 << 32, 4096, dtype=np.uint64).astype(np.uint32))
+    logits = np.tile(row, (4096, 1))
+    for k in (0, 40):
+        np.testing.assert_array_equal(_run(D, logits, k, T1, draws),
+                                      O.sample(logits, k, T1[0], T1[1], draws))
