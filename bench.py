@@ -9,8 +9,9 @@ into a HIP graph and replayed. The headline value is decode tokens/s at
 batch 1 after a 64-token prompt. The same line reports batch-8 decode and
 prefill on that model, the Llama-3.2-1B-shaped 16-bit-limb model (prefill
 of 4 x 2048 tokens per call, batch-32 decode to a 4096-token context), the
-25-shape int8 GEMM sweep, the roofline of the decode step's fused final
-RMSNorm + lm_head kernel, and the CPU oracle on this host. The Qwen runs'
+25-shape int8 GEMM sweep, integer temperature / top-k sampling over the
+vocabulary, the roofline of the decode step's fused final RMSNorm + lm_head
+kernel, and the CPU oracle on this host. The Qwen runs'
 logits are hashed and compared with the oracle-written golden chains
 (tests/golden), so the timed runs are also verified runs.
 
@@ -263,6 +264,40 @@ def llama_case(D, S, torch, dec_steps: int):
     }
 
 
+def sampling_case(D, torch, with_cpu: bool):
+    """detint_sample (integer temperature / top-k sampling) on rows of the
+    Qwen3-shaped vocabulary (151936 seeded int32 logits, gaps of a few units
+    at 16 fractional bits), temperature 1, batch 1 and 8, all tokens and
+    top-50. Algorithmic bytes per call: one read of the logits plus the draw
+    and the token per row. The oracle's tokens for the same rows and draws
+    are compared, and its time per row is reported beside it."""
+    import numpy as np
+    V, tm, tk = 151936, 23637, 15
+    rng = np.random.default_rng(2026)
+    lg_h = rng.normal(0, 3 * 65536, (8, V)).astype(np.int32)
+    dr_h = rng.integers(0, 1 << 32, 8, dtype=np.uint64).astype(np.uint32)
+    lg, dr = torch.from_numpy(lg_h).cuda(), torch.from_numpy(dr_h.view(np.int32)).cuda()
+    res = {"workload": "detint_sample over %d int32 logits per row, temperature 1" % V}
+    for R in (1, 8):
+        for k in (0, 50):
+            out = torch.empty(R, dtype=torch.int32, device="cuda")
+            f = lambda: D.detint_sample(lg[:R], k, tm, tk, dr[:R], out)
+            for _ in range(3):
+                f()
+            t = timed(f, 50, torch)
+            nbytes = R * (4 * V + 8)
+            key = "b%d_%s" % (R, "all" if k == 0 else "top%d" % k)
+            res[key] = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
+                        "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            if with_cpu and R == 8:
+                import oracle as O
+                t0 = time.perf_counter()
+                want = O.sample(lg_h, k, tm, tk, dr_h)
+                res[key]["oracle_ms_per_row"] = round((time.perf_counter() - t0) * 1e3 / R, 2)
+                res[key]["tokens_equal_oracle"] = bool(np.array_equal(out.cpu().numpy(), want))
+    return res
+
+
 def cpu_baseline(m, p0, seconds: float, gpu_tokens):
     import numpy as np
     import oracle as O
@@ -379,6 +414,8 @@ def main():
         log("Llama-3.2-1B-shaped model: prefill 4 x 2048 per call, batch-32 decode to 4096")
         llama = llama_case(D, S, torch, args.llama_steps)
 
+    log("integer sampling")
+    sampling = sampling_case(D, torch, not args.no_cpu)
     cpu = None if args.no_cpu else cpu_baseline(m, p0, args.cpu_seconds, gpu_tokens)
 
     weights = sum(L.wqkv.size + L.wo.size + L.wgu.size + L.wd.size for L in m.layers) + m.emb.size
@@ -410,6 +447,7 @@ def main():
                           "prompt_64": round(PROMPT_LEN / t_64, 1)},
         "decode_b1_hbm_frac": round(step_bytes * tps1 / 1e9 / HBM_PEAK_GBS, 4),
         "llama3.2_1b_limbs": llama,
+        "sampling": sampling,
         "gemm_sweep_req_i8": gemm,
         "gemm_best_frac_i8_mfma": round(max(big), 4),
         "roofline": {"bound": "hbm",

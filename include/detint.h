@@ -294,7 +294,7 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  * E_0 + ... + E_j > t. top_k = 1 gives the greedy token for every draw.
  *   logits int32 [R, V], device; draws uint32 [R], device (the randomness is
  *   the caller's: any generator, so a stream of draws replays exactly);
- *   tokens int32 [R], device. 1 <= V < 2^31, 1 <= t_m < 2^24, 0 <= t_k <= 62.
+ *   tokens int32 [R], device. 1 <= V <= 262144, 1 <= t_m < 2^24, 0 <= t_k <= 62.
  * One workgroup per row; no workspace. */
 detint_status detint_sample(const int32_t *logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t t_m, int32_t t_k, const uint32_t *draws, int32_t *tokens,

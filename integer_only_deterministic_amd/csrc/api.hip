@@ -291,7 +291,7 @@ detint_status detint_argmax_parts(const int64_t* part, int64_t S, int64_t nparts
 detint_status detint_sample(const int32_t* logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* tokens,
                             void* stream) {
-  REQUIRE(R >= 0 && V >= 1 && V < (int64_t(1) << 31), "sample: bad sizes");
+  REQUIRE(R >= 0 && V >= 1 && V <= 262144, "sample: V must be in [1, 262144]");
   REQUIRE(t_m >= 1 && t_m < (1 << 24) && t_k >= 0 && t_k <= 62, "sample: t_m or t_k out of range");
   if (R == 0) return ok();
   REQUIRE(logits && draws && tokens, "sample: null pointer");

@@ -36,19 +36,6 @@ __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
   return c;
 }
 
-// E = DI-Exp(R((s - mx) M, sh)) for s <= mx, written for x = (mx - s) M >= 0:
-// R(-x, sh) = -((x + 2^(sh-1) - 1) >> sh) for sh >= 1, so DI-Exp's
-// magnitude is v = (x + 2^(sh-1) - 1) >> sh and E = R(2^15 - R(v mod 2^15, 1),
-// v >> 15), zero once v >> 15 > 30. Needs 1 <= sh <= 62 and M > 0; other
-// rows take diexp(R(...)) as written.
-__device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh) {
-  const uint64_t x = (uint64_t)delta * M;
-  const uint64_t v = (x + (uint64_t(1) << (sh - 1)) - 1) >> sh;
-  const uint32_t vv = (uint32_t)v, n = min(vv >> 15, 31u);
-  const uint32_t f = 32768u - (((vv & 32767u) + 1u) >> 1);
-  return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
-}
-
 // exp_delta in 32-bit arithmetic. v >= 31 * 2^15 (E = 0) exactly when
 // delta * M >= T = 31 * 2^(15 + sh) - 2^(sh - 1) + 1, i.e. delta >= d0 =
 // ceil(T / M); clamping delta to d0 keeps that outcome and bounds the product

@@ -200,6 +200,19 @@ __device__ __forceinline__ int32_t diexp(int64_t u) {
   return (int32_t)R(f, (int)n);
 }
 
+// E = DI-Exp(R((s - mx) M, sh)) for s <= mx, written for x = (mx - s) M >= 0:
+// R(-x, sh) = -((x + 2^(sh-1) - 1) >> sh) for sh >= 1, so DI-Exp's
+// magnitude is v = (x + 2^(sh-1) - 1) >> sh and E = R(2^15 - R(v mod 2^15, 1),
+// v >> 15), zero once v >> 15 > 30. Needs 1 <= sh <= 62 and M > 0; other
+// rows take diexp(R(...)) as written.
+__device__ __forceinline__ int32_t exp_delta(uint32_t delta, uint32_t M, int sh) {
+  const uint64_t x = (uint64_t)delta * M;
+  const uint64_t v = (x + (uint64_t(1) << (sh - 1)) - 1) >> sh;
+  const uint32_t vv = (uint32_t)v, n = min(vv >> 15, 31u);
+  const uint32_t f = 32768u - (((vv & 32767u) + 1u) >> 1);
+  return v >= (uint64_t(31) << 15) ? 0 : (int32_t)((f + ((1u << n) >> 1)) >> n);
+}
+
 // Integer sigmoid in Q15 of a gate g with f_a fractional bits, given the
 // exponent multiplier (Mg, Kg): E = DI-Exp(-R(|g| Mg, Kg)),
 // s+ = RD(2^30, 2^15 + E) = floor((2^31 + b) / 2b) with b = 2^15 + E, a

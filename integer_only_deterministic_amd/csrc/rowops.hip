@@ -765,110 +765,226 @@ hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_
 // 2^32) from the caller's uniform 32-bit r, and return the smallest id whose
 // running weight exceeds t. Every reduction is an integer max, count or sum,
 // so the thread layout changes no result.
-constexpr int SMT = 1024, SMW = SMT / 64;
+//
+// Layout: wave w owns ids [w Cw, (w + 1) Cw) in steps of 256 ids, lane i
+// taking ids 4i .. 4i + 3 of a step, and issues the loads of UB steps before
+// using any (one workgroup per row needs many loads in flight). Each step's
+// sum (weights, or ties at the top-k boundary) goes to LDS, where the wave
+// holding a running-sum crossing finds its step with one ballot and reloads
+// only that step. The k-th largest logit comes from a radix select on
+// key - key_min (key the order-preserving unsigned form), starting at the
+// top bit of the row's span, with per-wave LDS histograms.
+constexpr int SMT = 1024, SMW = SMT / 64, SPS = 256, SMS = 64, UB = 4;  // V <= SMW * SPS * SMS
 
-// Inclusive prefix sum over the workgroup (thread order); *total gets the sum.
-__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* wsum, int64_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ uint32_t okey(int32_t v) { return (uint32_t)v ^ 0x80000000u; }
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int64_t t = __shfl_up(v, o);
     if (lane >= o) v += t;
   }
-  __syncthreads();  // wsum free (an earlier scan may still read it)
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int64_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < SMW; ++w) {
-    before += w < wave ? wsum[w] : 0;
-    all += wsum[w];
+  return v;
+}
+
+// The step q of a wave's range (n steps with sums s[0..n)) where the running
+// sum first exceeds x (0 <= x < sum of all), and x minus the sum of the steps
+// before q. Lane i scans steps i, i + 64, ... in rounds of 64.
+__device__ __forceinline__ void step_of(const int64_t* s, int n, int64_t x, int lane, int& q,
+                                        int64_t& rest) {
+  int64_t run = 0;
+  for (int b = 0; b < n; b += 64) {
+    const int64_t inc = wave_incl_scan(b + lane < n ? s[b + lane] : 0, lane);
+    const uint64_t m = __ballot(run + inc > x);
+    if (m) {
+      const int i = __builtin_ctzll(m);
+      q = b + i;
+      rest = x - run - (__shfl(inc, i) - s[b + i]);
+      return;
+    }
+    run += __shfl(inc, 63);
   }
-  *total = all;
-  return before + v;
+  q = n - 1;  // not reached for x below the total
+  rest = 0;
+}
+
+// The id, inside one step of 4 ids per lane with values c[4] (counts or
+// weights), where the running sum over the step first exceeds x.
+__device__ __forceinline__ int crossing_in_step(const int64_t (&c)[4], int64_t x, int lane) {
+  const int64_t mine = c[0] + c[1] + c[2] + c[3];
+  const int64_t inc = wave_incl_scan(mine, lane);
+  const int i = __builtin_ctzll(__ballot(inc > x));  // the lane holding the crossing
+  int found = 0;
+  if (lane == i) {  // it walks its own four values
+    int64_t run = inc - mine;
+    found = 3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      run += c[k];
+      if (run > x) {
+        found = k;
+        break;
+      }
+    }
+  }
+  return 4 * i + __shfl(found, i);
 }
 
 __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
                                                int32_t t_m, int32_t t_k,
                                                const uint32_t* __restrict__ draws,
                                                int32_t* __restrict__ out) {
+  __shared__ int32_t hw[SMW][256];  // per-wave histograms
   __shared__ int32_t hist[256];
   __shared__ int64_t red[16], wsum[SMW];
+  __shared__ int64_t ssum[SMW][SMS];  // per-step sums of each wave's range
   __shared__ int32_t s_sel[3];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* l = logits + (size_t)r * V;
-  int32_t mx = INT32_MIN;
-  for (int j = tid; j < V; j += SMT) mx = max(mx, l[j]);
+  const int Cw = ((V + SMW - 1) / SMW + SPS - 1) / SPS * SPS;
+  const int wlo = min(V, wave * Cw), whi = min(V, wlo + Cw);
+  const int nst = (whi - wlo + SPS - 1) / SPS;
+  // f(step, values[4], valid[4]) over this wave's steps, UB steps of loads in
+  // flight at a time (addresses clamped into the row; invalid ids flagged)
+  auto sweep = [&](auto f) {
+    for (int s0 = 0; s0 < nst; s0 += UB) {
+      int32_t x[UB][4];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[u][e] = l[min(wlo + (s0 + u) * SPS + 4 * lane + e, V - 1)];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        if (s0 + u >= nst) break;
+        bool ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ok[e] = wlo + (s0 + u) * SPS + 4 * lane + e < whi;
+        f(s0 + u, x[u], ok);
+      }
+    }
+  };
+  int32_t mx = INT32_MIN, mn = INT32_MAX;
+  sweep([&](int, const int32_t(&x)[4], const bool(&ok)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (ok[e]) {
+        mx = max(mx, x[e]);
+        mn = min(mn, x[e]);
+      }
+  });
   mx = (int32_t)block_max(mx, red);
-  // contiguous chunk of this thread (id order for the scans)
-  const int C = (V + SMT - 1) / SMT, lo = min(V, tid * C), hi = min(V, lo + C);
+  mn = (int32_t)(-block_max(-(int64_t)mn, red));
   // kept(j): l_j > Lk, or l_j == Lk and j <= idk
   int32_t Lk = INT32_MIN;
   int idk = V - 1;
   if (keep < V) {
-    // radix select of the keep-th largest value on the order-preserving key
+    const uint32_t kmin = okey(mn), span = okey(mx) - kmin;
     uint32_t prefix = 0, pmask = 0;
     int rem = keep;  // rank (from the top, 1-based) inside the current bucket
-    for (int sh = 24; sh >= 0; sh -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int j = tid; j < V; j += SMT) {
-        const uint32_t u = (uint32_t)l[j] ^ 0x80000000u;
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & 255], 1);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int c = 0, d = 255;
-        for (; d > 0; --d) {
-          if (c + hist[d] >= rem) break;
-          c += hist[d];
+    if (span != 0) {
+      const int B = 32 - __builtin_clz(span);
+      for (int sh = ((B - 1) / 8) * 8; sh >= 0; sh -= 8) {
+        for (int i = lane; i < 256; i += 64) hw[wave][i] = 0;
+        __syncthreads();
+        sweep([&](int, const int32_t(&x)[4], const bool(&ok)[4]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t d = okey(x[e]) - kmin;
+            if (ok[e] && (d & pmask) == prefix) atomicAdd(&hw[wave][(d >> sh) & 255], 1);
+          }
+        });
+        __syncthreads();
+        if (tid < 256) {
+          int c = 0;
+#pragma unroll
+          for (int w = 0; w < SMW; ++w) c += hw[w][tid];
+          hist[tid] = c;
         }
-        s_sel[0] = d;
-        s_sel[1] = rem - c;
+        __syncthreads();
+        if (tid == 0) {
+          int c = 0, d = 255;
+          for (; d > 0; --d) {
+            if (c + hist[d] >= rem) break;
+            c += hist[d];
+          }
+          s_sel[0] = d;
+          s_sel[1] = rem - c;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_sel[0] << sh;
+        pmask |= 255u << sh;
+        rem = s_sel[1];
       }
-      __syncthreads();
-      prefix |= (uint32_t)s_sel[0] << sh;
-      pmask |= 255u << sh;
-      rem = s_sel[1];
     }
-    Lk = (int32_t)(prefix ^ 0x80000000u);
+    Lk = (int32_t)((prefix + kmin) ^ 0x80000000u);
     // the rem-th lowest id among the values equal to Lk
-    int cnt = 0;
-    for (int j = lo; j < hi; ++j) cnt += l[j] == Lk;
-    int64_t tot;
-    const int64_t incl = block_scan(cnt, wsum, &tot);
-    const int64_t excl = incl - cnt;
-    if (excl < rem && incl >= rem) {
-      int need = rem - (int)excl;
-      for (int j = lo; j < hi; ++j)
-        if (l[j] == Lk && --need == 0) {
-          s_sel[2] = j;
-          break;
-        }
+    int64_t wc = 0;
+    sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += ok[e] && x[e] == Lk;
+      const int64_t st = wave_sum(c);
+      if (lane == 0) ssum[wave][q] = st;
+      wc += st;
+    });
+    __syncthreads();  // hist / s_sel reads of the last select round done
+    if (lane == 0) wsum[wave] = wc;
+    __syncthreads();
+    int64_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (before < rem && before + wsum[wave] >= rem) {
+      int q;
+      int64_t rest;
+      step_of(ssum[wave], nst, rem - before - 1, lane, q, rest);
+      const int base = wlo + q * SPS + 4 * lane;
+      int64_t c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = base + e < whi && l[min(base + e, V - 1)] == Lk;
+      const int at = crossing_in_step(c, rest, lane);
+      if (lane == 0) s_sel[2] = wlo + q * SPS + at;
     }
     __syncthreads();
     idk = s_sel[2];
   }
-  auto weight = [&](int j) -> int64_t {
-    const int32_t v = l[j];
+  // DI-Exp of the scaled gap: the branch-free exp_delta whenever t_k >= 1
+  // (the same value), else as written
+  auto weight = [&](int j, int32_t v) -> int64_t {
     const bool kept = v > Lk || (v == Lk && j <= idk);
-    return kept ? (int64_t)diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k)) : 0;
+    const int32_t E = t_k >= 1 ? exp_delta((uint32_t)((int64_t)mx - v), (uint32_t)t_m, t_k)
+                               : diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k));
+    return kept ? (int64_t)E : 0;
   };
-  int64_t sum = 0;
-  for (int j = lo; j < hi; ++j) sum += weight(j);
-  int64_t D;
-  const int64_t incl = block_scan(sum, wsum, &D);
-  const int64_t excl = incl - sum;
+  int64_t ws = 0;
+  sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
+    const int base = wlo + q * SPS + 4 * lane;
+    int64_t sm = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm += ok[e] ? weight(base + e, x[e]) : 0;
+    const int64_t st = wave_sum(sm);
+    if (lane == 0) ssum[wave][q] = st;
+    ws += st;
+  });
+  __syncthreads();  // every step sum written; wsum free
+  if (lane == 0) wsum[wave] = ws;
+  __syncthreads();
+  int64_t before = 0, D = 0;
+#pragma unroll
+  for (int w = 0; w < SMW; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    D += wsum[w];
+  }
   const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
-  if (excl <= t && t < incl) {
-    int64_t cum = excl;
-    for (int j = lo; j < hi; ++j) {
-      cum += weight(j);
-      if (cum > t) {
-        out[r] = j;
-        break;
-      }
-    }
+  if (before <= t && t < before + wsum[wave]) {
+    int q;
+    int64_t rest;
+    step_of(ssum[wave], nst, t - before, lane, q, rest);
+    const int base = wlo + q * SPS + 4 * lane;
+    int64_t c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c[e] = base + e < whi ? weight(base + e, l[min(base + e, V - 1)]) : 0;
+    const int at = crossing_in_step(c, rest, lane);
+    if (lane == 0) out[r] = wlo + q * SPS + at;
   }
 }
 
