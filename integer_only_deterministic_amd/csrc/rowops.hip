@@ -901,14 +901,23 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
           hist[tid] = c;
         }
         __syncthreads();
-        if (tid == 0) {
-          int c = 0, d = 255;
-          for (; d > 0; --d) {
-            if (c + hist[d] >= rem) break;
-            c += hist[d];
+        if (wave == 0) {
+          // bins from the top: lane i holds bins 255 - 4i .. 252 - 4i; the
+          // bucket is the first (from the top) whose running count reaches rem
+          int h[4], mine = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mine += h[e] = hist[255 - 4 * lane - e];
+          const int64_t inc = wave_incl_scan(mine, lane);
+          const int i = __builtin_ctzll(__ballot(inc >= rem));  // total count >= rem
+          if (lane == i) {
+            int c = (int)inc - mine, e = 0;
+            for (; e < 3; ++e) {
+              if (c + h[e] >= rem) break;
+              c += h[e];
+            }
+            s_sel[0] = 255 - 4 * i - e;
+            s_sel[1] = rem - c;
           }
-          s_sel[0] = d;
-          s_sel[1] = rem - c;
         }
         __syncthreads();
         prefix |= (uint32_t)s_sel[0] << sh;
