@@ -767,8 +767,9 @@ hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_
 // so the thread layout changes no result.
 //
 // Layout: wave w owns ids [w Cw, (w + 1) Cw) in steps of 256 ids, lane i
-// taking ids 4i .. 4i + 3 of a step, and issues the loads of UB steps before
-// using any (one workgroup per row needs many loads in flight). Each step's
+// taking ids i, 64 + i, 128 + i, 192 + i of a step (each load reads 256
+// contiguous bytes), and issues the loads of UB steps before using any (one
+// workgroup per row needs many loads in flight). Each step's
 // sum (weights, or ties at the top-k boundary) goes to LDS, where the wave
 // holding a running-sum crossing finds its step with one ballot and reloads
 // only that step. The k-th largest logit comes from a radix select on
@@ -808,26 +809,24 @@ __device__ __forceinline__ void step_of(const int64_t* s, int n, int64_t x, int 
   rest = 0;
 }
 
-// The id, inside one step of 4 ids per lane with values c[4] (counts or
+// The offset, inside one step (value c[e] at offset 64 e + lane: counts or
 // weights), where the running sum over the step first exceeds x.
 __device__ __forceinline__ int crossing_in_step(const int64_t (&c)[4], int64_t x, int lane) {
-  const int64_t mine = c[0] + c[1] + c[2] + c[3];
-  const int64_t inc = wave_incl_scan(mine, lane);
-  const int i = __builtin_ctzll(__ballot(inc > x));  // the lane holding the crossing
-  int found = 0;
-  if (lane == i) {  // it walks its own four values
-    int64_t run = inc - mine;
-    found = 3;
+  int64_t run = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      run += c[k];
-      if (run > x) {
-        found = k;
-        break;
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int64_t inc = run + wave_incl_scan(c[e], lane);
+    const uint64_t m = __ballot(inc > x);
+    if (m) return 64 * e + __builtin_ctzll(m);
+    run = __shfl(inc, 63);
   }
-  return 4 * i + __shfl(found, i);
+  return 255;  // not reached for x below the step's sum
+}
+
+__device__ __forceinline__ int32_t wave_sum32(int32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
@@ -852,13 +851,13 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
 #pragma unroll
       for (int u = 0; u < UB; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[u][e] = l[min(wlo + (s0 + u) * SPS + 4 * lane + e, V - 1)];
+        for (int e = 0; e < 4; ++e) x[u][e] = l[min(wlo + (s0 + u) * SPS + 64 * e + lane, V - 1)];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         if (s0 + u >= nst) break;
         bool ok[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ok[e] = wlo + (s0 + u) * SPS + 4 * lane + e < whi;
+        for (int e = 0; e < 4; ++e) ok[e] = wlo + (s0 + u) * SPS + 64 * e + lane < whi;
         f(s0 + u, x[u], ok);
       }
     }
@@ -932,7 +931,7 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
       int c = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) c += ok[e] && x[e] == Lk;
-      const int64_t st = wave_sum(c);
+      const int32_t st = wave_sum32(c);
       if (lane == 0) ssum[wave][q] = st;
       wc += st;
     });
@@ -945,10 +944,10 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
       int q;
       int64_t rest;
       step_of(ssum[wave], nst, rem - before - 1, lane, q, rest);
-      const int base = wlo + q * SPS + 4 * lane;
+      const int base = wlo + q * SPS + lane;
       int64_t c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = base + e < whi && l[min(base + e, V - 1)] == Lk;
+      for (int e = 0; e < 4; ++e) c[e] = base + 64 * e < whi && l[min(base + 64 * e, V - 1)] == Lk;
       const int at = crossing_in_step(c, rest, lane);
       if (lane == 0) s_sel[2] = wlo + q * SPS + at;
     }
@@ -965,11 +964,11 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
   };
   int64_t ws = 0;
   sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
-    const int base = wlo + q * SPS + 4 * lane;
-    int64_t sm = 0;
+    const int base = wlo + q * SPS + lane;
+    int32_t sm = 0;  // at most 4 * 2^15 per lane, 2^23 per step
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm += ok[e] ? weight(base + e, x[e]) : 0;
-    const int64_t st = wave_sum(sm);
+    for (int e = 0; e < 4; ++e) sm += ok[e] ? (int32_t)weight(base + 64 * e, x[e]) : 0;
+    const int32_t st = wave_sum32(sm);
     if (lane == 0) ssum[wave][q] = st;
     ws += st;
   });
@@ -987,11 +986,11 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
     int q;
     int64_t rest;
     step_of(ssum[wave], nst, t - before, lane, q, rest);
-    const int base = wlo + q * SPS + 4 * lane;
+    const int base = wlo + q * SPS + lane;
     int64_t c[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      c[e] = base + e < whi ? weight(base + e, l[min(base + e, V - 1)]) : 0;
+      c[e] = base + 64 * e < whi ? weight(base + 64 * e, l[min(base + 64 * e, V - 1)]) : 0;
     const int at = crossing_in_step(c, rest, lane);
     if (lane == 0) out[r] = wlo + q * SPS + at;
   }
