@@ -122,7 +122,7 @@ def _declare(L):
     L.orc_forward.argtypes = [C.POINTER(OrcModel), i32p, i64, i32p, i32p, i32p, i64,
                               i8p, i8p, i64, i32, i32p, vp]
     L.orc_argmax.argtypes = [i32p, i64, i64, i32p]
-    L.orc_sample.argtypes = [i32p, i64, i64, i64, i32, i32, u32p, i32p]
+    L.orc_sample.argtypes = [i32p, i64, i64, i64, i32, i32, i32, u32p, i32p]
     L.orc_attention.argtypes = [i8p, i32p, i8p, i8p, i32p, i32p, i64, i64, i64, i64, i64, i64,
                                 i32, i32, i32p]
 
@@ -320,15 +320,16 @@ def argmax(logits):
     return out
 
 
-def sample(logits, top_k: int, t_m: int, t_k: int, draws):
-    """Integer temperature / top-k sampling of each row with the caller's
-    uniform 32-bit draws (orc_sample states the reading)."""
+def sample(logits, top_k: int, t_m: int, t_k: int, draws, top_p: int = 65536):
+    """Integer temperature / top-k / top-p sampling of each row with the
+    caller's uniform 32-bit draws; top_p is p in units of 2^-16 (65536: off).
+    orc_sample states the reading."""
     logits = _c(logits, np.int32)
     R_, V = logits.shape
     draws = _c(draws, np.uint32)
     assert draws.shape == (R_,)
     out = np.zeros(R_, np.int32)
-    lib().orc_sample(logits, R_, V, int(top_k), int(t_m), int(t_k), draws, out)
+    lib().orc_sample(logits, R_, V, int(top_k), int(top_p), int(t_m), int(t_k), draws, out)
     _check()
     return out
 

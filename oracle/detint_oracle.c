@@ -759,9 +759,13 @@ int orc_argmax(const int32_t *logits, int64_t rows, int64_t V, int32_t *out) {
  *    the temperature is the dyadic t_m / 2^t_k applied to the logit gap in
  *    DI-Exp's base-2 Q15 units (the softmax's own exponential), so the
  *    maximum gets E = 2^15 and D = sum E >= 2^15;
+ *  - top-p (nucleus), p = top_p / 2^16 with 1 <= top_p <= 2^16 (2^16: off):
+ *    with D_k = sum of E over the top-k ids and P = ceil(top_p D_k / 2^16),
+ *    keep the shortest prefix of the ranking whose weight sum reaches P
+ *    (equal logits have equal weights, so ties again go to the lower id);
  *  - draw: the caller's uniform 32-bit integer r selects t = floor(r D / 2^32),
- *    in [0, D);
- *  - token: the smallest id j with E_0 + ... + E_j > t.
+ *    in [0, D), D the weight sum of the kept ids;
+ *  - token: the smallest id j with E_0 + ... + E_j > t (kept ids only).
  * Bounds: 1 <= t_m < 2^24, 0 <= t_k <= 62 (the gap times t_m stays < 2^56). */
 static const int32_t *g_sort_row;
 static int key_desc(const void *a, const void *b) {
@@ -771,10 +775,11 @@ static int key_desc(const void *a, const void *b) {
   return i < j ? -1 : (i > j ? 1 : 0);
 }
 
-int orc_sample(const int32_t *logits, int64_t rows, int64_t V, int64_t k, int32_t t_m,
-               int32_t t_k, const uint32_t *draws, int32_t *out) {
+int orc_sample(const int32_t *logits, int64_t rows, int64_t V, int64_t k, int32_t top_p,
+               int32_t t_m, int32_t t_k, const uint32_t *draws, int32_t *out) {
   CHECK(V >= 1, "sample: V < 1");
   CHECK(t_m >= 1 && t_m < (1 << 24) && t_k >= 0 && t_k <= 62, "sample: temperature dyadic");
+  CHECK(top_p >= 1 && top_p <= 65536, "sample: top_p outside [1, 2^16]");
   if (g_err) return g_err;
   const int64_t keep = (k <= 0 || k >= V) ? V : k;
   int32_t *idx = (int32_t *)malloc((size_t)V * sizeof(int32_t));
@@ -783,14 +788,22 @@ int orc_sample(const int32_t *logits, int64_t rows, int64_t V, int64_t k, int32_
     const int32_t *l = logits + o * V;
     int64_t lmax = l[0];
     for (int64_t j = 1; j < V; j++) if (l[j] > lmax) lmax = l[j];
-    if (keep == V) {
+    if (keep == V && top_p == 65536) {
       memset(kept, 1, (size_t)V);
     } else {
       for (int64_t j = 0; j < V; j++) idx[j] = (int32_t)j;
       g_sort_row = l;
       qsort(idx, (size_t)V, sizeof(int32_t), key_desc);
+      int64_t m = keep;
+      if (top_p < 65536) {
+        int64_t Dk = 0;
+        for (int64_t i = 0; i < keep; i++) Dk += orc_diexp(R(((int64_t)l[idx[i]] - lmax) * t_m, t_k));
+        const int64_t P = ((int64_t)top_p * Dk + 65535) >> 16;
+        int64_t cum = 0;
+        for (m = 0; m < keep && cum < P; m++) cum += orc_diexp(R(((int64_t)l[idx[m]] - lmax) * t_m, t_k));
+      }
       memset(kept, 0, (size_t)V);
-      for (int64_t i = 0; i < keep; i++) kept[idx[i]] = 1;
+      for (int64_t i = 0; i < m; i++) kept[idx[i]] = 1;
     }
     int64_t D = 0;
     for (int64_t j = 0; j < V; j++)

@@ -90,3 +90,58 @@ def test_distribution_matches_softmax():
     ratio = freq[big] / p[big]
     assert np.all(ratio > 1 / 1.07 - 2 / (N * p[big])) and np.all(ratio < 1.07 + 2 / (N * p[big]))
     assert math.isclose(freq.sum(), 1.0)
+
+
+# ------------------------------------------------------------------ top-p
+
+def test_top_p_smallest_is_greedy():
+    rng = np.random.default_rng(21)
+    logits = rng.integers(-5, 5, (64, 50)).astype(np.int32) * 65536
+    got = O.sample(logits, 0, T1_M, T1_K, _draws(rng, 64), top_p=1)
+    np.testing.assert_array_equal(got, np.argmax(logits, axis=1))
+
+
+@pytest.mark.parametrize("top_p,kept", [(32768, 5), (32769, 6), (65535, 10), (6553, 1), (6554, 2)])
+def test_top_p_equal_logits(top_p, kept):
+    """Ten equal logits weigh 2^15 each: P = ceil(top_p * 10 * 2^15 / 2^16)
+    keeps ceil(P / 2^15) of them, the lowest ids."""
+    rng = np.random.default_rng(top_p)
+    r = _draws(rng, 64)
+    logits = np.full((64, 10), 99, np.int32)
+    want = ((r.astype(object) * kept) >> 32).astype(np.int32)
+    np.testing.assert_array_equal(O.sample(logits, 0, T1_M, T1_K, r, top_p=top_p), want)
+
+
+def test_top_p_after_top_k():
+    rng = np.random.default_rng(22)
+    r = _draws(rng, 64)
+    logits = np.full((64, 40), 5, np.int32)
+    # top-3 first: D_k = 3 * 2^15; p just below 1 still needs all three
+    want = ((r.astype(object) * 3) >> 32).astype(np.int32)
+    np.testing.assert_array_equal(O.sample(logits, 3, T1_M, T1_K, r, top_p=65535), want)
+    # P = ceil(21845 * 3 * 2^15 / 2^16) = 2^15: exactly one; one more unit of p needs two
+    np.testing.assert_array_equal(O.sample(logits, 3, T1_M, T1_K, r, top_p=21845), np.zeros(64, np.int32))
+    want2 = ((r.astype(object) * 2) >> 32).astype(np.int32)
+    np.testing.assert_array_equal(O.sample(logits, 3, T1_M, T1_K, r, top_p=21846), want2)
+
+
+def test_top_p_nucleus_is_a_rank_prefix_of_the_right_mass():
+    rng = np.random.default_rng(23)
+    V, N = 200, 1 << 14
+    row = rng.normal(0, 2 * 65536, V).astype(np.int32)
+    r = ((np.arange(N, dtype=np.uint64) * (1 << 32) + (1 << 31)) // N).astype(np.uint32)
+    got = O.sample(np.tile(row, (N, 1)), 0, T1_M, T1_K, r, top_p=int(0.9 * 65536))
+    order = np.lexsort((np.arange(V), -row.astype(np.int64)))  # rank order
+    rank = np.empty(V, np.int64)
+    rank[order] = np.arange(V)
+    reached = np.unique(got)
+    m = rank[reached].max() + 1
+    assert set(rank[reached].tolist()) <= set(range(m))
+    x = row.astype(np.float64) / 65536.0
+    p = np.exp(x - x.max())
+    p /= p.sum()
+    mass = p[order[:m]].sum()
+    # the kept prefix reaches 0.9 of the (integer) mass; DI-Exp's weights are
+    # within 7% of the real ones, so the real mass of that prefix is near 0.9
+    assert 0.8 < mass < 0.97
+    assert p[order[m - 1]] > 0  # the last kept id carries weight
