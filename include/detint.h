@@ -282,14 +282,17 @@ detint_status detint_lm_head(const int8_t *x8, const int8_t *emb, const int8_t *
 detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts,
                                   int32_t *next_tok, void *stream);
 
-/* Integer temperature / top-k sampling of R rows of int32 logits [R, V]
+/* Integer temperature / top-k / top-p sampling of R rows of int32 logits [R, V]
  * (BitExact blog intro: sampling rules in integer arithmetic; DetLLM blog,
  * limits: integer sampling left open; the pages give no formula). Per row:
  * keep the top_k highest-ranked ids, ranked by larger logit first and, among
  * equal logits, lower id first (top_k <= 0 or >= V keeps all); weight kept id
  * j by E_j = DI-Exp(R((l_j - l_max) * t_m, t_k)) (the softmax's exponential:
  * t_m / 2^t_k is log2(e) / (2^(f_l - 15) T) for temperature T and logits with
- * f_l fractional bits), D = sum E_j; with the caller's uniform draw r,
+ * f_l fractional bits); top-p then keeps the shortest prefix of the ranking
+ * whose weight reaches P = ceil(top_p * D_k / 2^16), D_k the weight of the
+ * top-k ids (top_p = p in units of 2^-16, 1..65536; 65536 keeps all); D = sum
+ * of the kept E_j; with the caller's uniform draw r,
  * t = floor(r * D / 2^32); tokens[row] = the smallest id j with
  * E_0 + ... + E_j > t. top_k = 1 gives the greedy token for every draw.
  *   logits int32 [R, V], device; draws uint32 [R], device (the randomness is
@@ -297,8 +300,8 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  *   tokens int32 [R], device. 1 <= V <= 262144, 1 <= t_m < 2^24, 0 <= t_k <= 62.
  * One workgroup per row; no workspace. */
 detint_status detint_sample(const int32_t *logits, int64_t R, int64_t V, int64_t top_k,
-                            int32_t t_m, int32_t t_k, const uint32_t *draws, int32_t *tokens,
-                            void *stream);
+                            int32_t top_p, int32_t t_m, int32_t t_k, const uint32_t *draws,
+                            int32_t *tokens, void *stream);
 
 /* The model's last step for S rows of the int32 residual h [S, H]: final
  * RMSNorm with gain int16 [H] (scale 2^-12), tied lm_head logits int32

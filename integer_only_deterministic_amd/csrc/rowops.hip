@@ -830,21 +830,24 @@ __device__ __forceinline__ int32_t wave_sum32(int32_t v) {
 }
 
 __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
-                                               int32_t t_m, int32_t t_k,
+                                               int32_t top_p, int32_t t_m, int32_t t_k,
                                                const uint32_t* __restrict__ draws,
                                                int32_t* __restrict__ out) {
-  __shared__ int32_t hw[SMW][256];  // per-wave histograms
+  __shared__ int32_t hw[SMW][256];                // per-wave histograms (counts)
+  __shared__ unsigned long long hm[SMW][256];     // per-wave histograms (weights, top-p)
   __shared__ int32_t hist[256];
+  __shared__ int64_t histm[256];
   __shared__ int64_t red[16], wsum[SMW];
   __shared__ int64_t ssum[SMW][SMS];  // per-step sums of each wave's range
-  __shared__ int32_t s_sel[3];
+  __shared__ int64_t s_sel[3];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* l = logits + (size_t)r * V;
   const int Cw = ((V + SMW - 1) / SMW + SPS - 1) / SPS * SPS;
   const int wlo = min(V, wave * Cw), whi = min(V, wlo + Cw);
   const int nst = (whi - wlo + SPS - 1) / SPS;
   // f(step, values[4], valid[4]) over this wave's steps, UB steps of loads in
-  // flight at a time (addresses clamped into the row; invalid ids flagged)
+  // flight at a time (addresses clamped into the row; invalid ids flagged);
+  // value e of a step is id wlo + step SPS + 64 e + lane
   auto sweep = [&](auto f) {
     for (int s0 = 0; s0 < nst; s0 += UB) {
       int32_t x[UB][4];
@@ -873,69 +876,30 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
   });
   mx = (int32_t)block_max(mx, red);
   mn = (int32_t)(-block_max(-(int64_t)mn, red));
+  const uint32_t kmin = okey(mn), span = okey(mx) - kmin;
+  const int B = span ? 32 - __builtin_clz(span) : 0;
+  // DI-Exp of the scaled gap: the branch-free exp_delta whenever t_k >= 1
+  // (the same value), else as written
+  auto expw = [&](int32_t v) -> int32_t {
+    return t_k >= 1 ? exp_delta((uint32_t)((int64_t)mx - v), (uint32_t)t_m, t_k)
+                    : diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k));
+  };
   // kept(j): l_j > Lk, or l_j == Lk and j <= idk
   int32_t Lk = INT32_MIN;
   int idk = V - 1;
-  if (keep < V) {
-    const uint32_t kmin = okey(mn), span = okey(mx) - kmin;
-    uint32_t prefix = 0, pmask = 0;
-    int rem = keep;  // rank (from the top, 1-based) inside the current bucket
-    if (span != 0) {
-      const int B = 32 - __builtin_clz(span);
-      for (int sh = ((B - 1) / 8) * 8; sh >= 0; sh -= 8) {
-        for (int i = lane; i < 256; i += 64) hw[wave][i] = 0;
-        __syncthreads();
-        sweep([&](int, const int32_t(&x)[4], const bool(&ok)[4]) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t d = okey(x[e]) - kmin;
-            if (ok[e] && (d & pmask) == prefix) atomicAdd(&hw[wave][(d >> sh) & 255], 1);
-          }
-        });
-        __syncthreads();
-        if (tid < 256) {
-          int c = 0;
-#pragma unroll
-          for (int w = 0; w < SMW; ++w) c += hw[w][tid];
-          hist[tid] = c;
-        }
-        __syncthreads();
-        if (wave == 0) {
-          // bins from the top: lane i holds bins 255 - 4i .. 252 - 4i; the
-          // bucket is the first (from the top) whose running count reaches rem
-          int h[4], mine = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mine += h[e] = hist[255 - 4 * lane - e];
-          const int64_t inc = wave_incl_scan(mine, lane);
-          const int i = __builtin_ctzll(__ballot(inc >= rem));  // total count >= rem
-          if (lane == i) {
-            int c = (int)inc - mine, e = 0;
-            for (; e < 3; ++e) {
-              if (c + h[e] >= rem) break;
-              c += h[e];
-            }
-            s_sel[0] = 255 - 4 * i - e;
-            s_sel[1] = rem - c;
-          }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)s_sel[0] << sh;
-        pmask |= 255u << sh;
-        rem = s_sel[1];
-      }
-    }
-    Lk = (int32_t)((prefix + kmin) ^ 0x80000000u);
-    // the rem-th lowest id among the values equal to Lk
+  auto kept = [&](int j, int32_t v) { return v > Lk || (v == Lk && j <= idk); };
+  // the rem-th lowest id (rem >= 1) among the values equal to L
+  auto nth_tie = [&](int32_t L, int64_t rem) -> int {
     int64_t wc = 0;
+    __syncthreads();  // ssum / wsum / s_sel free
     sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
       int c = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c += ok[e] && x[e] == Lk;
+      for (int e = 0; e < 4; ++e) c += ok[e] && x[e] == L;
       const int32_t st = wave_sum32(c);
       if (lane == 0) ssum[wave][q] = st;
       wc += st;
     });
-    __syncthreads();  // hist / s_sel reads of the last select round done
     if (lane == 0) wsum[wave] = wc;
     __syncthreads();
     int64_t before = 0;
@@ -947,32 +911,124 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
       const int base = wlo + q * SPS + lane;
       int64_t c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = base + 64 * e < whi && l[min(base + 64 * e, V - 1)] == Lk;
+      for (int e = 0; e < 4; ++e) c[e] = base + 64 * e < whi && l[min(base + 64 * e, V - 1)] == L;
       const int at = crossing_in_step(c, rest, lane);
       if (lane == 0) s_sel[2] = wlo + q * SPS + at;
     }
     __syncthreads();
-    idk = s_sel[2];
-  }
-  // DI-Exp of the scaled gap: the branch-free exp_delta whenever t_k >= 1
-  // (the same value), else as written
-  auto weight = [&](int j, int32_t v) -> int64_t {
-    const bool kept = v > Lk || (v == Lk && j <= idk);
-    const int32_t E = t_k >= 1 ? exp_delta((uint32_t)((int64_t)mx - v), (uint32_t)t_m, t_k)
-                               : diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k));
-    return kept ? (int64_t)E : 0;
+    return (int)s_sel[2];
   };
+  // bucket from the top (lane i: bins 255 - 4i .. 252 - 4i) whose running
+  // total first reaches rem; s_sel = (bucket, rem minus the bins above it)
+  auto pick_bucket = [&](auto bins, int64_t rem) {
+    if (wave == 0) {
+      int64_t h[4], mine = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine += h[e] = bins(255 - 4 * lane - e);
+      const int64_t inc = wave_incl_scan(mine, lane);
+      const int i = __builtin_ctzll(__ballot(inc >= rem));  // the total reaches rem
+      if (lane == i) {
+        int64_t c = inc - mine;
+        int e = 0;
+        for (; e < 3; ++e) {
+          if (c + h[e] >= rem) break;
+          c += h[e];
+        }
+        s_sel[0] = 255 - 4 * i - e;
+        s_sel[1] = rem - c;
+      }
+    }
+    __syncthreads();
+  };
+  if (keep < V) {
+    // radix select of the keep-th largest value on the order-preserving key
+    uint32_t prefix = 0, pmask = 0;
+    int64_t rem = keep;  // rank (from the top, 1-based) inside the current bucket
+    for (int sh = B ? ((B - 1) / 8) * 8 : -8; sh >= 0; sh -= 8) {
+      for (int i = lane; i < 256; i += 64) hw[wave][i] = 0;
+      __syncthreads();
+      sweep([&](int, const int32_t(&x)[4], const bool(&ok)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t d = okey(x[e]) - kmin;
+          if (ok[e] && (d & pmask) == prefix) atomicAdd(&hw[wave][(d >> sh) & 255], 1);
+        }
+      });
+      __syncthreads();
+      if (tid < 256) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < SMW; ++w) c += hw[w][tid];
+        hist[tid] = c;
+      }
+      __syncthreads();
+      pick_bucket([&](int d) { return (int64_t)hist[d]; }, rem);
+      prefix |= (uint32_t)s_sel[0] << sh;
+      pmask |= 255u << sh;
+      rem = s_sel[1];
+    }
+    Lk = (int32_t)((prefix + kmin) ^ 0x80000000u);
+    idk = nth_tie(Lk, rem);
+  }
+  if (top_p < 65536) {
+    // D_k, then the shortest prefix of the ranking whose weight reaches
+    // P = ceil(top_p D_k / 2^16): a radix select on weight sums
+    int64_t mine = 0;
+    sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = wlo + q * SPS + 64 * e + lane;
+        if (ok[e] && kept(j, x[e])) mine += expw(x[e]);
+      }
+    });
+    const int64_t Dk = block_sum(mine, red);
+    uint32_t prefix = 0, pmask = 0;
+    int64_t rem = ((int64_t)top_p * Dk + 65535) >> 16;  // weight still to reach
+    for (int sh = B ? ((B - 1) / 8) * 8 : -8; sh >= 0; sh -= 8) {
+      for (int i = lane; i < 256; i += 64) hm[wave][i] = 0;
+      __syncthreads();
+      sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = wlo + q * SPS + 64 * e + lane;
+          const uint32_t d = okey(x[e]) - kmin;
+          if (ok[e] && (d & pmask) == prefix && kept(j, x[e]))
+            atomicAdd(&hm[wave][(d >> sh) & 255], (unsigned long long)expw(x[e]));
+        }
+      });
+      __syncthreads();
+      if (tid < 256) {
+        unsigned long long c = 0;
+#pragma unroll
+        for (int w = 0; w < SMW; ++w) c += hm[w][tid];
+        histm[tid] = (int64_t)c;
+      }
+      __syncthreads();
+      pick_bucket([&](int d) { return histm[d]; }, rem);
+      prefix |= (uint32_t)s_sel[0] << sh;
+      pmask |= 255u << sh;
+      rem = s_sel[1];
+    }
+    const int32_t Lp = (int32_t)((prefix + kmin) ^ 0x80000000u);
+    // every id at Lp weighs expw(Lp) > 0: ceil(rem / weight) of them, lowest ids first
+    const uint64_t wp = (uint64_t)expw(Lp);
+    const int64_t need = (int64_t)udiv64((uint64_t)rem + wp - 1, wp);
+    idk = nth_tie(Lp, need);
+    Lk = Lp;
+  }
   int64_t ws = 0;
+  __syncthreads();  // ssum / wsum free
   sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
-    const int base = wlo + q * SPS + lane;
     int32_t sm = 0;  // at most 4 * 2^15 per lane, 2^23 per step
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm += ok[e] ? (int32_t)weight(base + 64 * e, x[e]) : 0;
+    for (int e = 0; e < 4; ++e) {
+      const int j = wlo + q * SPS + 64 * e + lane;
+      sm += ok[e] && kept(j, x[e]) ? expw(x[e]) : 0;
+    }
     const int32_t st = wave_sum32(sm);
     if (lane == 0) ssum[wave][q] = st;
     ws += st;
   });
-  __syncthreads();  // every step sum written; wsum free
   if (lane == 0) wsum[wave] = ws;
   __syncthreads();
   int64_t before = 0, D = 0;
@@ -989,17 +1045,21 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
     const int base = wlo + q * SPS + lane;
     int64_t c[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      c[e] = base + 64 * e < whi ? weight(base + 64 * e, l[min(base + 64 * e, V - 1)]) : 0;
+    for (int e = 0; e < 4; ++e) {
+      const int j = base + 64 * e;
+      const int32_t v = l[min(j, V - 1)];
+      c[e] = j < whi && kept(j, v) ? expw(v) : 0;
+    }
     const int at = crossing_in_step(c, rest, lane);
     if (lane == 0) out[r] = wlo + q * SPS + at;
   }
 }
 
-hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t t_m,
-                         int32_t t_k, const uint32_t* draws, int32_t* out, hipStream_t st) {
+hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
+                         int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out,
+                         hipStream_t st) {
   if (R == 0) return hipSuccess;
-  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, t_m, t_k, draws, out);
+  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);
   return hipGetLastError();
 }
 

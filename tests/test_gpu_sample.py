@@ -21,11 +21,11 @@ def D():
     return D
 
 
-def _run(D, logits, k, tm, draws):
+def _run(D, logits, k, tm, draws, top_p=65536):
     import torch
     lg = torch.from_numpy(logits).cuda()
     dr = torch.from_numpy(draws.view(np.int32)).cuda()
-    return D.detint_sample(lg, k, tm[0], tm[1], dr).cpu().numpy()
+    return D.detint_sample(lg, k, tm[0], tm[1], dr, top_p=top_p).cpu().numpy()
 
 
 def _logits(kind, R, V, rng):
@@ -54,6 +54,22 @@ def test_sample_matches_oracle(D, V, kind):
             np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm}")
 
 
+@pytest.mark.parametrize("V", [7, 1000, 151936])
+@pytest.mark.parametrize("kind", ["spread", "ties", "extreme"])
+def test_sample_top_p_matches_oracle(D, V, kind):
+    rng = np.random.default_rng(3 * V + len(kind))
+    R = 6
+    logits = _logits(kind, R, V, rng)
+    draws = rng.integers(0, 1 << 32, R, dtype=np.uint64).astype(np.uint32)
+    draws[:2] = [0, (1 << 32) - 1]
+    for k in sorted({0, 1, 50, V}):
+        for p in (1, 6553, 32768, 58982, 65535):
+            for tm in (T1, HOT):
+                want = O.sample(logits, k, tm[0], tm[1], draws, top_p=p)
+                got = _run(D, logits, k, tm, draws, top_p=p)
+                np.testing.assert_array_equal(got, want, err_msg=f"k={k} p={p} t={tm}")
+
+
 def test_sample_many_draws_one_row(D):
     """One row, 4096 draws across [0, 2^32): every boundary of the inverse
     CDF the draws land on matches the oracle."""
@@ -61,6 +77,6 @@ def test_sample_many_draws_one_row(D):
     row = rng.normal(0, 2 * 65536, 3000).astype(np.int32)
     draws = np.sort(rng.integers(0, 1 << 32, 4096, dtype=np.uint64).astype(np.uint32))
     logits = np.tile(row, (4096, 1))
-    for k in (0, 40):
-        np.testing.assert_array_equal(_run(D, logits, k, T1, draws),
-                                      O.sample(logits, k, T1[0], T1[1], draws))
+    for k, p in ((0, 65536), (40, 65536), (0, 58982), (40, 32768)):
+        np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p),
+                                      O.sample(logits, k, T1[0], T1[1], draws, top_p=p))
