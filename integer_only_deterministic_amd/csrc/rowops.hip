@@ -773,8 +773,9 @@ hipError_t launch_advance(int32_t* ids, const int32_t* next_tok, int32_t* start_
 // sum (weights, or ties at the top-k boundary) goes to LDS, where the wave
 // holding a running-sum crossing finds its step with one ballot and reloads
 // only that step. The k-th largest logit comes from a radix select on
-// key - key_min (key the order-preserving unsigned form), starting at the
-// top bit of the row's span, with per-wave LDS histograms.
+// key - key_min (key the order-preserving unsigned form) in 8-bit digits
+// aligned to the top bit of the row's span (so the first histogram spreads
+// over 256 bins), with per-wave LDS histograms.
 constexpr int SMT = 1024, SMW = SMT / 64, SPS = 256, SMS = 64, UB = 4;  // V <= SMW * SPS * SMS
 
 __device__ __forceinline__ uint32_t okey(int32_t v) { return (uint32_t)v ^ 0x80000000u; }
@@ -944,14 +945,16 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
     // radix select of the keep-th largest value on the order-preserving key
     uint32_t prefix = 0, pmask = 0;
     int64_t rem = keep;  // rank (from the top, 1-based) inside the current bucket
-    for (int sh = B ? ((B - 1) / 8) * 8 : -8; sh >= 0; sh -= 8) {
+    for (int hi = B; hi > 0; hi -= 8) {  // digit = bits [lo, hi) of key - key_min
+      const int lo = hi > 8 ? hi - 8 : 0;
+      const uint32_t dm = (1u << (hi - lo)) - 1;
       for (int i = lane; i < 256; i += 64) hw[wave][i] = 0;
       __syncthreads();
       sweep([&](int, const int32_t(&x)[4], const bool(&ok)[4]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t d = okey(x[e]) - kmin;
-          if (ok[e] && (d & pmask) == prefix) atomicAdd(&hw[wave][(d >> sh) & 255], 1);
+          if (ok[e] && (d & pmask) == prefix) atomicAdd(&hw[wave][(d >> lo) & dm], 1);
         }
       });
       __syncthreads();
@@ -963,8 +966,8 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
       }
       __syncthreads();
       pick_bucket([&](int d) { return (int64_t)hist[d]; }, rem);
-      prefix |= (uint32_t)s_sel[0] << sh;
-      pmask |= 255u << sh;
+      prefix |= (uint32_t)s_sel[0] << lo;
+      pmask |= dm << lo;
       rem = s_sel[1];
     }
     Lk = (int32_t)((prefix + kmin) ^ 0x80000000u);
@@ -984,7 +987,9 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
     const int64_t Dk = block_sum(mine, red);
     uint32_t prefix = 0, pmask = 0;
     int64_t rem = ((int64_t)top_p * Dk + 65535) >> 16;  // weight still to reach
-    for (int sh = B ? ((B - 1) / 8) * 8 : -8; sh >= 0; sh -= 8) {
+    for (int hi = B; hi > 0; hi -= 8) {  // digit = bits [lo, hi) of key - key_min
+      const int lo = hi > 8 ? hi - 8 : 0;
+      const uint32_t dm = (1u << (hi - lo)) - 1;
       for (int i = lane; i < 256; i += 64) hm[wave][i] = 0;
       __syncthreads();
       sweep([&](int q, const int32_t(&x)[4], const bool(&ok)[4]) {
@@ -993,7 +998,7 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
           const int j = wlo + q * SPS + 64 * e + lane;
           const uint32_t d = okey(x[e]) - kmin;
           if (ok[e] && (d & pmask) == prefix && kept(j, x[e]))
-            atomicAdd(&hm[wave][(d >> sh) & 255], (unsigned long long)expw(x[e]));
+            atomicAdd(&hm[wave][(d >> lo) & dm], (unsigned long long)expw(x[e]));
         }
       });
       __syncthreads();
@@ -1005,8 +1010,8 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
       }
       __syncthreads();
       pick_bucket([&](int d) { return histm[d]; }, rem);
-      prefix |= (uint32_t)s_sel[0] << sh;
-      pmask |= 255u << sh;
+      prefix |= (uint32_t)s_sel[0] << lo;
+      pmask |= dm << lo;
       rem = s_sel[1];
     }
     const int32_t Lp = (int32_t)((prefix + kmin) ^ 0x80000000u);
