@@ -71,7 +71,8 @@ const char *detint_last_error(void);
  *   frac   fractional bits of FIX / RES_ADD outputs.
  *   out    [M, N] int32 (RAW, FIX, RES_ADD; read-modify-write for RES_ADD) or
  *          int8 (REQ_I8).
- * Bounds: K <= 131072 (|acc| < 2^31); scaled modes |acc * m_r * m_c| < 2^62,
+ * Bounds: K <= 131056 (K * 2^14 < 2^31, so |acc| < 2^31 even when every
+ * operand is -128); scaled modes |acc * m_r * m_c| < 2^62,
  * and FIX / RES_ADD results within int32. M, N >= 0; M = 0 or N = 0 is a
  * no-op. */
 detint_status detint_gemm_i8(const int8_t *A, const int8_t *W, int64_t M, int64_t N, int64_t K,

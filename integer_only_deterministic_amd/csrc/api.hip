@@ -75,7 +75,8 @@ const char* detint_last_error(void) { return g_err.c_str(); }
 detint_status detint_gemm_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
                              const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
                              int32_t col_k, int32_t frac, int32_t mode, void* out, void* stream) {
-  detint_status s = check_gemm(A, W, M, N, K, row_m, row_k, col_m, mode, out, 131072);
+  // K * 2^14 < 2^31 even when every operand is -128
+  detint_status s = check_gemm(A, W, M, N, K, row_m, row_k, col_m, mode, out, 131056);
   if (s != DETINT_OK || M == 0 || N == 0) return s;
   Epi e{row_m, row_k, col_m, col_k, frac, mode, nullptr};
   return hip_status(launch_gemm(A, W, nullptr, M, N, K, e, out, S_(stream)), "gemm_i8 launch");
@@ -216,7 +217,7 @@ detint_status detint_lm_head(const int8_t* x8, const int8_t* emb, const int8_t* 
                              const int32_t* emb_m, int32_t w_k, int32_t f_l, int32_t* logits,
                              int64_t* part, void* stream) {
   detint_status s = check_gemm(x8, emb, S, V, H, row_m, row_k, emb_m, DETINT_GEMM_FIX, logits,
-                               emb_lo ? 65536 : 131072);
+                               emb_lo ? 65536 : 131056);
   if (s != DETINT_OK || S == 0 || V == 0) return s;
   REQUIRE(S <= 16, "lm_head: at most 16 rows (S=%lld)", (long long)S);
   REQUIRE(part, "lm_head: null partials");
@@ -249,7 +250,7 @@ detint_status detint_final_head(const int32_t* h, int64_t S, int64_t H, const in
   REQUIRE(h && gain && emb && emb_m && logits && ws, "final_head: null pointer");
   REQUIRE(H % 16 == 0 && aligned16(emb) && (!emb_lo || aligned16(emb_lo)),
           "final_head: hidden must be a multiple of 16 with 16-byte aligned tables");
-  REQUIRE(H <= (emb_lo ? 65536 : 131072), "final_head: hidden too large");
+  REQUIRE(H <= (emb_lo ? 65536 : 131056), "final_head: hidden too large");
   REQUIRE(ws_bytes >= detint_final_head_workspace(S, V, H), "final_head: workspace too small");
   hipStream_t st = S_(stream);
   int64_t* part = (int64_t*)ws;

@@ -86,6 +86,10 @@ def test_validation_rejects_before_device_work(D):
     assert rc == D.DETINT_EINVAL
     # empty GEMM is a no-op
     assert lib.detint_gemm_i8(None, None, 0, 4, 16, None, None, None, 0, 0, D.RAW, None, None) == 0
+    # the int32 accumulator bound: 131072 * (-128)^2 = 2^31 does not fit, 131056 does
+    assert lib.detint_gemm_i8(None, None, 0, 4, 131056, None, None, None, 0, 0, D.RAW, None, None) == 0
+    assert lib.detint_gemm_i8(None, None, 0, 4, 131072, None, None, None, 0, 0, D.RAW, None,
+                              None) == D.DETINT_EINVAL
     # unsupported attention head_dim
     rc = lib.detint_attn_decode(fake, fake, fake, fake, 1, fake, fake, 1, 4, 2, 96, 64, 1 << 14, 10,
                                 fake, None)
