@@ -277,11 +277,12 @@ def sampling_case(D, torch, with_cpu: bool):
     lg_h = rng.normal(0, 3 * 65536, (8, V)).astype(np.int32)
     dr_h = rng.integers(0, 1 << 32, 8, dtype=np.uint64).astype(np.uint32)
     lg, dr = torch.from_numpy(lg_h).cuda(), torch.from_numpy(dr_h.view(np.int32)).cuda()
+    ws = torch.empty(D.detint_sample_workspace(8, V), dtype=torch.uint8, device="cuda")
     res = {"workload": "detint_sample over %d int32 logits per row, temperature 1" % V}
     for R in (1, 8):
         for k, p in ((0, 65536), (50, 65536), (0, 58982)):
             out = torch.empty(R, dtype=torch.int32, device="cuda")
-            f = lambda: D.detint_sample(lg[:R], k, tm, tk, dr[:R], out, top_p=p)
+            f = lambda: D.detint_sample(lg[:R], k, tm, tk, dr[:R], out, top_p=p, ws=ws)
             for _ in range(3):
                 f()
             t = timed(f, 50, torch)

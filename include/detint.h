@@ -299,10 +299,15 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  *   logits int32 [R, V], device; draws uint32 [R], device (the randomness is
  *   the caller's: any generator, so a stream of draws replays exactly);
  *   tokens int32 [R], device. 1 <= V <= 262144, 1 <= t_m < 2^24, 0 <= t_k <= 62.
- * One workgroup per row; no workspace. */
+ *   ws: optional device workspace (16-byte aligned) of ws_bytes >=
+ *   detint_sample_workspace(R, V), owned by the caller, contents need not be
+ *   initialised. With it, rows that keep every id (no top-k, no top-p) are
+ *   spread over 1024-id slices across the GPU; otherwise, or with ws = NULL,
+ *   one workgroup per row. Same tokens either way. */
+int64_t detint_sample_workspace(int64_t R, int64_t V);
 detint_status detint_sample(const int32_t *logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t top_p, int32_t t_m, int32_t t_k, const uint32_t *draws,
-                            int32_t *tokens, void *stream);
+                            int32_t *tokens, void *ws, int64_t ws_bytes, void *stream);
 
 /* The model's last step for S rows of the int32 residual h [S, H]: final
  * RMSNorm with gain int16 [H] (scale 2^-12), tied lm_head logits int32

@@ -77,7 +77,8 @@ _SIGS = {
     "detint_lm_head_parts": (i64, [i64]),
     "detint_lm_head": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp]),
     "detint_argmax_parts": (i32, [vp, i64, i64, vp, vp]),
-    "detint_sample": (i32, [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp]),
+    "detint_sample": (i32, [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, i64, vp]),
+    "detint_sample_workspace": (i64, [i64, i64]),
     "detint_final_head_workspace": (i64, [i64, i64, i64]),
     "detint_final_head": (i32, [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, vp]),
     "detint_layer_forward": (i32, [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, vp, i64,
@@ -283,10 +284,16 @@ def detint_argmax_parts(part):
     return out
 
 
-def detint_sample(logits, top_k: int, t_m: int, t_k: int, draws, out=None, top_p: int = 65536):
+def detint_sample_workspace(R: int, V: int) -> int:
+    return library().detint_sample_workspace(int(R), int(V))
+
+
+def detint_sample(logits, top_k: int, t_m: int, t_k: int, draws, out=None, top_p: int = 65536,
+                  ws=None):
     """Integer temperature / top-k / top-p sampling of each row with the
-    caller's uniform uint32 draws; top_p is p in units of 2^-16 (65536: off).
-    See detint.h."""
+    caller's uniform uint32 draws; top_p is p in units of 2^-16 (65536: off);
+    ws an optional uint8 device workspace of detint_sample_workspace(R, V)
+    bytes. See detint.h."""
     torch = _torch()
     R_, V = logits.shape
     if out is None:
@@ -294,7 +301,8 @@ def detint_sample(logits, top_k: int, t_m: int, t_k: int, draws, out=None, top_p
     if draws.dtype not in (torch.int32, torch.uint32) or draws.shape != (R_,):
         raise TypeError("draws: one 32-bit integer per row (uint32, or int32 holding the bits)")
     _call("detint_sample", _p(logits, torch.int32), R_, V, int(top_k), int(top_p), int(t_m),
-          int(t_k), _p(draws), _p(out), _stream())
+          int(t_k), _p(draws), _p(out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+          _stream())
     return out
 
 

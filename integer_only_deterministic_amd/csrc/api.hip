@@ -289,16 +289,23 @@ detint_status detint_argmax_parts(const int64_t* part, int64_t S, int64_t nparts
                     "argmax_parts launch");
 }
 
+int64_t detint_sample_workspace(int64_t R, int64_t V) {
+  if (R < 0 || V < 1 || V > 262144) return -1;
+  return sample_workspace_bytes(R, V);
+}
+
 detint_status detint_sample(const int32_t* logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t top_p, int32_t t_m, int32_t t_k, const uint32_t* draws,
-                            int32_t* tokens, void* stream) {
+                            int32_t* tokens, void* ws, int64_t ws_bytes, void* stream) {
   REQUIRE(R >= 0 && V >= 1 && V <= 262144, "sample: V must be in [1, 262144]");
   REQUIRE(t_m >= 1 && t_m < (1 << 24) && t_k >= 0 && t_k <= 62, "sample: t_m or t_k out of range");
   REQUIRE(top_p >= 1 && top_p <= 65536, "sample: top_p must be in [1, 65536]");
   if (R == 0) return ok();
   REQUIRE(logits && draws && tokens, "sample: null pointer");
   const int64_t keep = (top_k <= 0 || top_k >= V) ? V : top_k;
-  return hip_status(launch_sample(logits, R, V, keep, top_p, t_m, t_k, draws, tokens, S_(stream)),
+  REQUIRE(ws_bytes >= 0 && (!ws || aligned16(ws)), "sample: workspace misaligned");
+  return hip_status(launch_sample(logits, R, V, keep, top_p, t_m, t_k, draws, tokens, ws, ws_bytes,
+                                  S_(stream)),
                     "sample launch");
 }
 

@@ -70,9 +70,12 @@ hipError_t launch_softmax(const int32_t* s, const int32_t* valid, const int32_t*
                           hipStream_t st);
 // Temperature / top-k / top-p sampling of R rows of V logits (keep in [1, V],
 // top_p in [1, 2^16], 2^16 = off).
+// With a workspace of sample_workspace_bytes(R, V) and every id kept, plain
+// temperature sampling runs over 1024-id slices in three kernels.
 hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
-                         int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out,
-                         hipStream_t st);
+                         int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out, void* ws,
+                         int64_t ws_bytes, hipStream_t st);
+int64_t sample_workspace_bytes(int64_t R, int64_t V);
 hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, int32_t Mg,
                          int32_t Kg, int8_t* a8, int32_t* row_m, int32_t* row_k, hipStream_t st);
 // DQ of int64 SwiGLU products [R, n] -> int8, row scale (2^14, 2 f_a - e + 14)

@@ -1060,10 +1060,137 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
   }
 }
 
+// Plain temperature sampling (every id kept) spread over the chip: slices of
+// 1024 ids, one 256-thread workgroup each, wave w of a slice owning its
+// w-th 256-id step (ids 64 e + lane within it, as in sample_k).
+//   1. slice maxima;  2. each slice reduces the maxima and writes its
+//   per-step DI-Exp weight sums;  3. one workgroup per row scans the step
+//   sums in id order, places the draw and reloads that step.
+// The same integer function as sample_k with all ids kept.
+constexpr int SLC = 1024, SLT = 256;
+
+__global__ __launch_bounds__(SLT) void sample_max_k(const int32_t* __restrict__ logits, int V,
+                                                    int P, int32_t* __restrict__ smax) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.y, p = blockIdx.x;
+  const int32_t* l = logits + (size_t)r * V;
+  int32_t m = INT32_MIN;
+#pragma unroll
+  for (int i = 0; i < SLC / SLT; ++i) {
+    const int j = p * SLC + i * SLT + threadIdx.x;
+    m = max(m, l[min(j, V - 1)]);  // clamped ids repeat a real value
+  }
+  m = (int32_t)block_max(m, red);
+  if (threadIdx.x == 0) smax[(size_t)r * P + p] = m;
+}
+
+__device__ __forceinline__ int32_t row_max_of(const int32_t* smax, int P, int64_t* red) {
+  int32_t m = INT32_MIN;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) m = max(m, smax[i]);
+  return (int32_t)block_max(m, red);
+}
+
+__device__ __forceinline__ int32_t expw_of(int32_t v, int32_t mx, int32_t t_m, int32_t t_k) {
+  return t_k >= 1 ? exp_delta((uint32_t)((int64_t)mx - v), (uint32_t)t_m, t_k)
+                  : diexp(R((int64_t)(v - (int64_t)mx) * t_m, t_k));
+}
+
+__global__ __launch_bounds__(SLT) void sample_wsum_k(const int32_t* __restrict__ logits, int V,
+                                                     int P, int32_t t_m, int32_t t_k,
+                                                     const int32_t* __restrict__ smax,
+                                                     int32_t* __restrict__ ssum) {
+  __shared__ int64_t red[16];
+  const int r = blockIdx.y, p = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int32_t* l = logits + (size_t)r * V;
+  const int32_t mx = row_max_of(smax + (size_t)r * P, P, red);
+  const int base = p * SLC + w * 256 + lane;
+  int32_t sm = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = base + 64 * e;
+    const int32_t v = l[min(j, V - 1)];
+    sm += j < V ? expw_of(v, mx, t_m, t_k) : 0;
+  }
+  sm = wave_sum32(sm);
+  if (lane == 0) ssum[((size_t)r * P + p) * 4 + w] = sm;
+}
+
+__global__ __launch_bounds__(SLT) void sample_pick_k(const int32_t* __restrict__ logits, int V,
+                                                     int P, int32_t t_m, int32_t t_k,
+                                                     const int32_t* __restrict__ smax,
+                                                     const int32_t* __restrict__ ssum,
+                                                     const uint32_t* __restrict__ draws,
+                                                     int32_t* __restrict__ out) {
+  __shared__ int64_t red[16], wtot[SLT / 64];
+  __shared__ int s_step;
+  __shared__ int64_t s_rest;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* l = logits + (size_t)r * V;
+  const int32_t mx = row_max_of(smax + (size_t)r * P, P, red);
+  const int32_t* sr = ssum + (size_t)r * P * 4;
+  const int n = 4 * P;  // steps of 256 ids, in id order
+  // thread t holds steps 4t .. 4t + 3 (n <= 1024)
+  int64_t c[4], mine = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c[e] = 4 * tid + e < n ? sr[4 * tid + e] : 0;
+    mine += c[e];
+  }
+  const int64_t inc = wave_incl_scan(mine, lane);
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  int64_t before = 0, D = 0;
+#pragma unroll
+  for (int w = 0; w < SLT / 64; ++w) {
+    before += w < wave ? wtot[w] : 0;
+    D += wtot[w];
+  }
+  const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
+  const int64_t lo = before + inc - mine;  // weight before this thread's steps
+  if (lo <= t && t < lo + mine) {
+    int64_t run = lo;
+    int e = 0;
+    for (; e < 3; ++e) {
+      if (run + c[e] > t) break;
+      run += c[e];
+    }
+    s_step = 4 * tid + e;
+    s_rest = t - run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int base = s_step * 256 + lane;
+    int64_t cw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = base + 64 * e;
+      cw[e] = j < V ? expw_of(l[min(j, V - 1)], mx, t_m, t_k) : 0;
+    }
+    const int at = crossing_in_step(cw, s_rest, lane);
+    if (lane == 0) out[r] = s_step * 256 + at;
+  }
+}
+
+int64_t sample_workspace_bytes(int64_t R, int64_t V) {
+  const int64_t P = (V + SLC - 1) / SLC;
+  return R * P * 4 * (1 + 4);
+}
+
 hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
-                         int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out,
-                         hipStream_t st) {
+                         int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out, void* ws,
+                         int64_t ws_bytes, hipStream_t st) {
   if (R == 0) return hipSuccess;
+  if (ws && keep >= V && top_p >= 65536 && ws_bytes >= sample_workspace_bytes(R, V) &&
+      R <= 65535) {
+    const int P = (int)((V + SLC - 1) / SLC);
+    int32_t* smax = (int32_t*)ws;
+    int32_t* ssum = smax + R * P;
+    sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, P, smax);
+    sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax,
+                                                                  ssum);
+    sample_pick_k<<<(unsigned)R, SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax, ssum, draws, out);
+    return hipGetLastError();
+  }
   sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);
   return hipGetLastError();
 }

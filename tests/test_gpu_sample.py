@@ -21,11 +21,14 @@ def D():
     return D
 
 
-def _run(D, logits, k, tm, draws, top_p=65536):
+def _run(D, logits, k, tm, draws, top_p=65536, ws=False):
     import torch
     lg = torch.from_numpy(logits).cuda()
     dr = torch.from_numpy(draws.view(np.int32)).cuda()
-    return D.detint_sample(lg, k, tm[0], tm[1], dr, top_p=top_p).cpu().numpy()
+    w = None
+    if ws:
+        w = torch.empty(D.detint_sample_workspace(*logits.shape), dtype=torch.uint8, device="cuda")
+    return D.detint_sample(lg, k, tm[0], tm[1], dr, top_p=top_p, ws=w).cpu().numpy()
 
 
 def _logits(kind, R, V, rng):
@@ -52,6 +55,9 @@ def test_sample_matches_oracle(D, V, kind):
             want = O.sample(logits, k, tm[0], tm[1], draws)
             got = _run(D, logits, k, tm, draws)
             np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm}")
+            # with a workspace: the sliced path where every id is kept
+            got = _run(D, logits, k, tm, draws, ws=True)
+            np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm} (workspace)")
 
 
 @pytest.mark.parametrize("V", [7, 1000, 151936])
@@ -78,5 +84,6 @@ def test_sample_many_draws_one_row(D):
     draws = np.sort(rng.integers(0, 1 << 32, 4096, dtype=np.uint64).astype(np.uint32))
     logits = np.tile(row, (4096, 1))
     for k, p in ((0, 65536), (40, 65536), (0, 58982), (40, 32768)):
-        np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p),
-                                      O.sample(logits, k, T1[0], T1[1], draws, top_p=p))
+        want = O.sample(logits, k, T1[0], T1[1], draws, top_p=p)
+        np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p), want)
+        np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p, ws=True), want)

@@ -101,15 +101,21 @@ def test_validation_rejects_before_device_work(D):
     assert lib.detint_workspace_size(None, 1, 1) == -1
     # sampling: vocabulary, temperature and top-p ranges; empty batch is a no-op
     T = (23637, 15)
-    rc = lib.detint_sample(fake, 1, 262145, 0, 65536, *T, fake, fake, None)
+    rc = lib.detint_sample(fake, 1, 262145, 0, 65536, *T, fake, fake, None, 0, None)
     assert rc == D.DETINT_EINVAL and b"262144" in lib.detint_last_error()
-    assert lib.detint_sample(fake, 1, 100, 0, 0, *T, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(fake, 1, 100, 0, 65537, *T, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(fake, 1, 100, 0, 65536, 0, 15, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(fake, 1, 100, 0, 65536, 1 << 24, 15, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(fake, 1, 100, 0, 65536, 23637, 63, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(None, 1, 100, 0, 65536, *T, fake, fake, None) == D.DETINT_EINVAL
-    assert lib.detint_sample(None, 0, 100, 0, 65536, *T, None, None, None) == D.DETINT_OK
+    assert lib.detint_sample(fake, 1, 100, 0, 0, *T, fake, fake, None, 0, None) == D.DETINT_EINVAL
+    assert lib.detint_sample(fake, 1, 100, 0, 65537, *T, fake, fake, None, 0, None) == D.DETINT_EINVAL
+    assert lib.detint_sample(fake, 1, 100, 0, 65536, 0, 15, fake, fake, None, 0, None) == D.DETINT_EINVAL
+    assert lib.detint_sample(fake, 1, 100, 0, 65536, 1 << 24, 15, fake, fake, None, 0,
+                             None) == D.DETINT_EINVAL
+    assert lib.detint_sample(fake, 1, 100, 0, 65536, 23637, 63, fake, fake, None, 0,
+                             None) == D.DETINT_EINVAL
+    assert lib.detint_sample(None, 1, 100, 0, 65536, *T, fake, fake, None, 0, None) == D.DETINT_EINVAL
+    assert lib.detint_sample(fake, 1, 100, 0, 65536, *T, fake, fake, C.c_void_p(4097), 64,
+                             None) == D.DETINT_EINVAL  # misaligned workspace
+    assert lib.detint_sample(None, 0, 100, 0, 65536, *T, None, None, None, 0, None) == D.DETINT_OK
+    assert lib.detint_sample_workspace(8, 151936) == 8 * 149 * 20
+    assert lib.detint_sample_workspace(1, 262145) == -1
 
 
 def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
