@@ -1171,9 +1171,167 @@ __global__ __launch_bounds__(SLT) void sample_pick_k(const int32_t* __restrict__
   }
 }
 
+// Top-k sampling spread over the chip (top-p off). A global top-k id is
+// among the top min(k, n) of its own slice, so:
+//   1. each 2048-id slice selects its top min(k, slice) ids (radix select on
+//      the order key, ties to the lowest ids) and writes them, in id order,
+//      as (key << 32 | ~id) into a row-private candidate list (kc entries per
+//      slice, padded with 0, which no id's entry equals);
+//   2. one workgroup per row selects the top k among the candidates, weighs
+//      them against the row maximum and places the draw in id order.
+// The same integer function as sample_k.
+constexpr int TKS = 2048, TKT = 512, TKN = TKS / TKT;  // ids per slice, threads, ids per thread
+constexpr int TKC = 16384, TPT = 1024, TPN = TKC / TPT;  // candidates per row, pick threads
+
+// Inclusive prefix sum over the workgroup in thread order; also the total.
+template <int NT>
+__device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t inc = wave_incl_scan(v, lane);
+  __syncthreads();  // wt free from its previous use
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int64_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wave ? wt[w] : 0;
+    tot += wt[w];
+  }
+  total = tot;
+  return before + inc;
+}
+
+// The n-th largest (1 <= n <= number of valid keys) of the valid keys held
+// by the workgroup, 8 bits a pass from the top: its value T and how many of
+// the keys equal to T lie within the top n (tneed >= 1).
+template <int NT, int N>
+__device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (&ok)[N], int n,
+                                          int32_t* hist, int64_t* wt, int* sel, uint32_t& T,
+                                          int& tneed) {
+  uint32_t prefix = 0, pmask = 0;
+  int rem = n;
+  for (int sh = 24; sh >= 0; sh -= 8) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (ok[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> sh) & 255], 1);
+    __syncthreads();
+    // bins from the top down: thread i holds bin 255 - i
+    const int64_t c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0;
+    int64_t tot;
+    const int64_t inc = block_incl_scan<NT>(c, wt, tot);
+    if (inc - c < rem && rem <= inc) {
+      sel[0] = 255 - (int)threadIdx.x;
+      sel[1] = rem - (int)(inc - c);
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << sh;
+    pmask |= 0xFFu << sh;
+    rem = sel[1];
+  }
+  T = prefix;
+  tneed = rem;
+}
+
+// take[e]: key above T, or equal to T and among the first tneed such keys in
+// thread-major order (which is id order); returns how many this thread takes.
+template <int NT, int N>
+__device__ __forceinline__ int take_top(const uint32_t (&key)[N], const bool (&ok)[N], uint32_t T,
+                                        int tneed, int64_t* wt, bool (&take)[N]) {
+  int ties = 0;
+#pragma unroll
+  for (int e = 0; e < N; ++e) ties += ok[e] && key[e] == T;
+  int64_t tt;
+  int tb = (int)(block_incl_scan<NT>(ties, wt, tt) - ties);
+  int nt = 0;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const bool eq = ok[e] && key[e] == T;
+    take[e] = ok[e] && (key[e] > T || (eq && tb < tneed));
+    tb += eq;
+    nt += take[e];
+  }
+  return nt;
+}
+
+__global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ logits, int V,
+                                                    int kc, uint64_t* __restrict__ cand) {
+  __shared__ int32_t hist[256];
+  __shared__ int64_t wt[TKT / 64];
+  __shared__ int sel[2];
+  const int r = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
+  const int32_t* l = logits + (size_t)r * V;
+  const int j0 = p * TKS + TKN * tid;
+  uint32_t key[TKN];
+  bool ok[TKN], take[TKN];
+#pragma unroll
+  for (int e = 0; e < TKN; ++e) {
+    ok[e] = j0 + e < V;
+    key[e] = okey(l[min(j0 + e, V - 1)]);
+  }
+  const int kk = min(kc, V - p * TKS);  // ids kept from this slice
+  uint32_t T;
+  int tneed;
+  radix_nth<TKT, TKN>(key, ok, kk, hist, wt, sel, T, tneed);
+  const int nt = take_top<TKT, TKN>(key, ok, T, tneed, wt, take);
+  int64_t tot;
+  int at = (int)(block_incl_scan<TKT>(nt, wt, tot) - nt);
+  uint64_t* dst = cand + (size_t)r * TKC + (size_t)p * kc;
+#pragma unroll
+  for (int e = 0; e < TKN; ++e)
+    if (take[e] && at < kk) dst[at++] = (uint64_t)key[e] << 32 | (uint32_t)~(uint32_t)(j0 + e);
+  for (int i = kk + tid; i < kc; i += TKT) dst[i] = 0;
+}
+
+__global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
+                                                   int keep, int32_t t_m, int32_t t_k,
+                                                   const uint32_t* __restrict__ draws,
+                                                   int32_t* __restrict__ out) {
+  __shared__ int32_t hist[256];
+  __shared__ int64_t wt[TPT / 64], red[16];
+  __shared__ int sel[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* c = cand + (size_t)r * TKC;
+  uint64_t cv[TPN];
+  uint32_t key[TPN], km = 0;
+  bool ok[TPN], take[TPN];
+#pragma unroll
+  for (int e = 0; e < TPN; ++e) {
+    const int i = TPN * tid + e;
+    cv[e] = i < nc ? c[i] : 0;
+    ok[e] = cv[e] != 0;
+    key[e] = (uint32_t)(cv[e] >> 32);
+    km = ok[e] && key[e] > km ? key[e] : km;
+  }
+  const int32_t mx = (int32_t)((uint32_t)block_max((int64_t)km, red) ^ 0x80000000u);
+  uint32_t T;
+  int tneed;
+  radix_nth<TPT, TPN>(key, ok, keep, hist, wt, sel, T, tneed);
+  take_top<TPT, TPN>(key, ok, T, tneed, wt, take);
+  int64_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < TPN; ++e)
+    mine += take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
+  int64_t D;
+  int64_t run = block_incl_scan<TPT>(mine, wt, D) - mine;  // weight of earlier ids
+  const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
+  if (run <= t && t < run + mine) {
+#pragma unroll
+    for (int e = 0; e < TPN; ++e) {
+      const int64_t w = take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
+      if (run + w > t) {
+        out[r] = (int32_t)~(uint32_t)cv[e];
+        break;
+      }
+      run += w;
+    }
+  }
+}
+
 int64_t sample_workspace_bytes(int64_t R, int64_t V) {
   const int64_t P = (V + SLC - 1) / SLC;
-  return R * P * 4 * (1 + 4);
+  return R * std::max<int64_t>(P * 4 * (1 + 4), TKC * 8);
 }
 
 hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
@@ -1189,6 +1347,14 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
     sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax,
                                                                   ssum);
     sample_pick_k<<<(unsigned)R, SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax, ssum, draws, out);
+    return hipGetLastError();
+  }
+  const int64_t P2 = (V + TKS - 1) / TKS, kc = std::min<int64_t>(keep, TKS);
+  if (ws && keep < V && top_p >= 65536 && P2 * kc <= TKC &&
+      ws_bytes >= sample_workspace_bytes(R, V) && R <= 65535) {
+    uint64_t* cand = (uint64_t*)ws;
+    topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kc, cand);
+    topk_pick_k<<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, t_m, t_k, draws, out);
     return hipGetLastError();
   }
   sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);
