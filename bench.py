@@ -267,8 +267,8 @@ def llama_case(D, S, torch, dec_steps: int):
 def sampling_case(D, torch, with_cpu: bool):
     """detint_sample (integer temperature / top-k sampling) on rows of the
     Qwen3-shaped vocabulary (151936 seeded int32 logits, gaps of a few units
-    at 16 fractional bits), temperature 1, batch 1 and 8: all tokens, top-50
-    and top-p 0.9. Algorithmic bytes per call: one read of the logits plus the draw
+    at 16 fractional bits), temperature 1, batch 1 and 8: all tokens, top-50,
+    top-p 0.9 and both. Algorithmic bytes per call: one read of the logits plus the draw
     and the token per row. The oracle's tokens for the same rows and draws
     are compared, and its time per row is reported beside it."""
     import numpy as np
@@ -280,14 +280,15 @@ def sampling_case(D, torch, with_cpu: bool):
     ws = torch.empty(D.detint_sample_workspace(8, V), dtype=torch.uint8, device="cuda")
     res = {"workload": "detint_sample over %d int32 logits per row, temperature 1" % V}
     for R in (1, 8):
-        for k, p in ((0, 65536), (50, 65536), (0, 58982)):
+        for k, p in ((0, 65536), (50, 65536), (0, 58982), (50, 58982)):
             out = torch.empty(R, dtype=torch.int32, device="cuda")
             f = lambda: D.detint_sample(lg[:R], k, tm, tk, dr[:R], out, top_p=p, ws=ws)
             for _ in range(3):
                 f()
             t = timed(f, 50, torch)
             nbytes = R * (4 * V + 8)
-            key = "b%d_%s" % (R, "top%d" % k if k else ("all" if p == 65536 else "top_p0.9"))
+            key = "b%d_%s%s" % (R, "top%d" % k if k else ("" if p < 65536 else "all"),
+                                ("_" if k else "") + "top_p0.9" if p < 65536 else "")
             res[key] = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
                         "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
             if with_cpu and R == 8:

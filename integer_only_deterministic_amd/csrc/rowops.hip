@@ -1171,14 +1171,15 @@ __global__ __launch_bounds__(SLT) void sample_pick_k(const int32_t* __restrict__
   }
 }
 
-// Top-k sampling spread over the chip (top-p off). A global top-k id is
+// Top-k (and top-p after it) sampling spread over the chip. A global top-k id is
 // among the top min(k, n) of its own slice, so:
 //   1. each 2048-id slice selects its top min(k, slice) ids (radix select on
 //      the order key, ties to the lowest ids) and writes them, in id order,
 //      as (key << 32 | ~id) into a row-private candidate list (kc entries per
 //      slice, padded with 0, which no id's entry equals);
 //   2. one workgroup per row selects the top k among the candidates, weighs
-//      them against the row maximum and places the draw in id order.
+//      them against the row maximum, keeps the top-p nucleus of those and
+//      places the draw in id order.
 // The same integer function as sample_k.
 constexpr int TKS = 2048, TKT = 512, TKN = TKS / TKT;  // ids per slice, threads, ids per thread
 constexpr int TKC = 16384, TPT = 1024, TPN = TKC / TPT;  // candidates per row, pick threads
@@ -1201,13 +1202,15 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
   return before + inc;
 }
 
-// The n-th largest (1 <= n <= number of valid keys) of the valid keys held
-// by the workgroup, 8 bits a pass from the top: its value T and how many of
-// the keys equal to T lie within the top n (tneed >= 1).
+// Radix select over the valid keys held by the workgroup, 8 bits a pass
+// from the top, each key weighing wv (all 1: the n-th largest key). Finds
+// the largest T such that the keys at or above T weigh at least n
+// (1 <= n <= total weight, total below 2^31), and returns in tneed the
+// weight still needed from the keys equal to T (>= 1) beyond those above it.
 template <int NT, int N>
-__device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (&ok)[N], int n,
-                                          int32_t* hist, int64_t* wt, int* sel, uint32_t& T,
-                                          int& tneed) {
+__device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (&ok)[N],
+                                          const int32_t (&wv)[N], int n, int32_t* hist,
+                                          int64_t* wt, int* sel, uint32_t& T, int& tneed) {
   uint32_t prefix = 0, pmask = 0;
   int rem = n;
   for (int sh = 24; sh >= 0; sh -= 8) {
@@ -1215,7 +1218,7 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < N; ++e)
-      if (ok[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> sh) & 255], 1);
+      if (ok[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> sh) & 255], wv[e]);
     __syncthreads();
     // bins from the top down: thread i holds bin 255 - i
     const int64_t c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0;
@@ -1271,9 +1274,10 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
     key[e] = okey(l[min(j0 + e, V - 1)]);
   }
   const int kk = min(kc, V - p * TKS);  // ids kept from this slice
+  const int32_t one[TKN] = {1, 1, 1, 1};
   uint32_t T;
   int tneed;
-  radix_nth<TKT, TKN>(key, ok, kk, hist, wt, sel, T, tneed);
+  radix_nth<TKT, TKN>(key, ok, one, kk, hist, wt, sel, T, tneed);
   const int nt = take_top<TKT, TKN>(key, ok, T, tneed, wt, take);
   int64_t tot;
   int at = (int)(block_incl_scan<TKT>(nt, wt, tot) - nt);
@@ -1285,7 +1289,7 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
 }
 
 __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
-                                                   int keep, int32_t t_m, int32_t t_k,
+                                                   int keep, int32_t top_p, int32_t t_m, int32_t t_k,
                                                    const uint32_t* __restrict__ draws,
                                                    int32_t* __restrict__ out) {
   __shared__ int32_t hist[256];
@@ -1305,26 +1309,50 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     km = ok[e] && key[e] > km ? key[e] : km;
   }
   const int32_t mx = (int32_t)((uint32_t)block_max((int64_t)km, red) ^ 0x80000000u);
+  int32_t w[TPN];
+#pragma unroll
+  for (int e = 0; e < TPN; ++e) w[e] = 1;
   uint32_t T;
   int tneed;
-  radix_nth<TPT, TPN>(key, ok, keep, hist, wt, sel, T, tneed);
+  radix_nth<TPT, TPN>(key, ok, w, keep, hist, wt, sel, T, tneed);
   take_top<TPT, TPN>(key, ok, T, tneed, wt, take);
   int64_t mine = 0;
 #pragma unroll
-  for (int e = 0; e < TPN; ++e)
-    mine += take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
+  for (int e = 0; e < TPN; ++e) {
+    w[e] = take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
+    mine += w[e];
+  }
+  if (top_p < 65536) {
+    // the shortest prefix of the ranking among the kept ids whose weight
+    // reaches ceil(top_p D_k / 2^16): a weighted select (D_k < 2^30), then
+    // ceil(rest / weight of that key) of its ties, lowest ids first
+    int64_t Dk;
+    block_incl_scan<TPT>(mine, wt, Dk);
+    uint32_t Lp;
+    int rest;
+    radix_nth<TPT, TPN>(key, take, w, (int)(((int64_t)top_p * Dk + 65535) >> 16), hist, wt, sel,
+                        Lp, rest);
+    const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
+    bool nuc[TPN];
+    take_top<TPT, TPN>(key, take, Lp, (rest + wp - 1) / wp, wt, nuc);
+    mine = 0;
+#pragma unroll
+    for (int e = 0; e < TPN; ++e) {
+      w[e] = nuc[e] ? w[e] : 0;
+      mine += w[e];
+    }
+  }
   int64_t D;
   int64_t run = block_incl_scan<TPT>(mine, wt, D) - mine;  // weight of earlier ids
   const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
   if (run <= t && t < run + mine) {
 #pragma unroll
     for (int e = 0; e < TPN; ++e) {
-      const int64_t w = take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
-      if (run + w > t) {
+      if (run + w[e] > t) {
         out[r] = (int32_t)~(uint32_t)cv[e];
         break;
       }
-      run += w;
+      run += w[e];
     }
   }
 }
@@ -1350,11 +1378,12 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
     return hipGetLastError();
   }
   const int64_t P2 = (V + TKS - 1) / TKS, kc = std::min<int64_t>(keep, TKS);
-  if (ws && keep < V && top_p >= 65536 && P2 * kc <= TKC &&
+  if (ws && keep < V && P2 * kc <= TKC &&
       ws_bytes >= sample_workspace_bytes(R, V) && R <= 65535) {
     uint64_t* cand = (uint64_t*)ws;
     topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kc, cand);
-    topk_pick_k<<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, t_m, t_k, draws, out);
+    topk_pick_k<<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p, t_m, t_k,
+                                             draws, out);
     return hipGetLastError();
   }
   sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);

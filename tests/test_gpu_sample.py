@@ -75,6 +75,8 @@ def test_sample_top_p_matches_oracle(D, V, kind):
                 want = O.sample(logits, k, tm[0], tm[1], draws, top_p=p)
                 got = _run(D, logits, k, tm, draws, top_p=p)
                 np.testing.assert_array_equal(got, want, err_msg=f"k={k} p={p} t={tm}")
+                got = _run(D, logits, k, tm, draws, top_p=p, ws=True)
+                np.testing.assert_array_equal(got, want, err_msg=f"k={k} p={p} t={tm} (ws)")
 
 
 def test_sample_many_draws_one_row(D):
