@@ -1202,23 +1202,39 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
   return before + inc;
 }
 
-// Radix select over the valid keys held by the workgroup, 8 bits a pass
-// from the top, each key weighing wv (all 1: the n-th largest key). Finds
+// Radix select over the valid keys held by the workgroup, each key weighing
+// wv (all 1: the n-th largest key), on digits of key - (smallest key) taken 8
+// bits a pass from the top of that span (so the first pass already spreads
+// keys that share their high bits over the bins). Finds
 // the largest T such that the keys at or above T weigh at least n
 // (1 <= n <= total weight, total below 2^31), and returns in tneed the
 // weight still needed from the keys equal to T (>= 1) beyond those above it.
 template <int NT, int N>
 __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (&ok)[N],
                                           const int32_t (&wv)[N], int n, int32_t* hist,
-                                          int64_t* wt, int* sel, uint32_t& T, int& tneed) {
+                                          int64_t* wt, int64_t* red, int* sel, uint32_t& T,
+                                          int& tneed) {
+  uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    kmx = ok[e] && key[e] > kmx ? key[e] : kmx;
+    kmn = ok[e] && key[e] < kmn ? key[e] : kmn;
+  }
+  kmx = (uint32_t)block_max((int64_t)kmx, red);
+  kmn = ~(uint32_t)block_max((int64_t)(~kmn), red);
+  const int B = 32 - __clz(kmx - kmn);  // span bits (0: one distinct key)
   uint32_t prefix = 0, pmask = 0;
   int rem = n;
-  for (int sh = 24; sh >= 0; sh -= 8) {
+  for (int hi = B; hi > 0; hi -= 8) {  // digit = bits [lo, hi) of key - kmn
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint32_t dm = (1u << (hi - lo)) - 1;
     for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-      if (ok[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> sh) & 255], wv[e]);
+    for (int e = 0; e < N; ++e) {
+      const uint32_t d = key[e] - kmn;
+      if (ok[e] && (d & pmask) == prefix) atomicAdd(&hist[(d >> lo) & dm], wv[e]);
+    }
     __syncthreads();
     // bins from the top down: thread i holds bin 255 - i
     const int64_t c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0;
@@ -1229,11 +1245,11 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (
       sel[1] = rem - (int)(inc - c);
     }
     __syncthreads();
-    prefix |= (uint32_t)sel[0] << sh;
-    pmask |= 0xFFu << sh;
+    prefix |= (uint32_t)sel[0] << lo;
+    pmask |= dm << lo;
     rem = sel[1];
   }
-  T = prefix;
+  T = prefix + kmn;
   tneed = rem;
 }
 
@@ -1261,7 +1277,7 @@ __device__ __forceinline__ int take_top(const uint32_t (&key)[N], const bool (&o
 __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ logits, int V,
                                                     int kc, uint64_t* __restrict__ cand) {
   __shared__ int32_t hist[256];
-  __shared__ int64_t wt[TKT / 64];
+  __shared__ int64_t wt[TKT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
   const int32_t* l = logits + (size_t)r * V;
@@ -1277,7 +1293,7 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
   const int32_t one[TKN] = {1, 1, 1, 1};
   uint32_t T;
   int tneed;
-  radix_nth<TKT, TKN>(key, ok, one, kk, hist, wt, sel, T, tneed);
+  radix_nth<TKT, TKN>(key, ok, one, kk, hist, wt, red, sel, T, tneed);
   const int nt = take_top<TKT, TKN>(key, ok, T, tneed, wt, take);
   int64_t tot;
   int at = (int)(block_incl_scan<TKT>(nt, wt, tot) - nt);
@@ -1314,7 +1330,7 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
   for (int e = 0; e < TPN; ++e) w[e] = 1;
   uint32_t T;
   int tneed;
-  radix_nth<TPT, TPN>(key, ok, w, keep, hist, wt, sel, T, tneed);
+  radix_nth<TPT, TPN>(key, ok, w, keep, hist, wt, red, sel, T, tneed);
   take_top<TPT, TPN>(key, ok, T, tneed, wt, take);
   int64_t mine = 0;
 #pragma unroll
@@ -1330,8 +1346,8 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     block_incl_scan<TPT>(mine, wt, Dk);
     uint32_t Lp;
     int rest;
-    radix_nth<TPT, TPN>(key, take, w, (int)(((int64_t)top_p * Dk + 65535) >> 16), hist, wt, sel,
-                        Lp, rest);
+    radix_nth<TPT, TPN>(key, take, w, (int)(((int64_t)top_p * Dk + 65535) >> 16), hist, wt, red,
+                        sel, Lp, rest);
     const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
     bool nuc[TPN];
     take_top<TPT, TPN>(key, take, Lp, (rest + wp - 1) / wp, wt, nuc);
