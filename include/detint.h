@@ -301,11 +301,17 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  *   tokens int32 [R], device. 1 <= V <= 262144, 1 <= t_m < 2^24, 0 <= t_k <= 62.
  *   ws: optional device workspace (16-byte aligned) of ws_bytes >=
  *   detint_sample_workspace(R, V), owned by the caller, contents need not be
- *   initialised (R * 128 KiB for V <= 262144). With it and top-p off, rows
- *   that keep every id are spread over 1024-id slices across the GPU, and
- *   top-k rows whose 2048-id slices give at most 16384 candidates
- *   (ceil(V / 2048) * min(k, 2048) <= 16384) select per slice first; other
- *   calls, or ws = NULL, take one workgroup per row. Same tokens either way. */
+ *   initialised (under R * 136 KiB for V <= 262144). With it, work spreads
+ *   over slices of the row across the GPU:
+ *   - every id kept, top-p off: 1024-id slices;
+ *   - top-k (with or without top-p) where the 2048-id slices give at most
+ *     8192 candidates, ceil(V / 2048) * min(k, 2048) <= 8192: each slice
+ *     selects its top ids first;
+ *   - top-p alone: each 2048-id slice offers its top min(2048, 16384 /
+ *     ceil(V / 2048)) ids; a row whose nucleus reaches below what a slice
+ *     offered is redone by the one-workgroup kernel in the same call.
+ *   Other calls, or ws = NULL, take one workgroup per row. Same tokens
+ *   either way. */
 int64_t detint_sample_workspace(int64_t R, int64_t V);
 detint_status detint_sample(const int32_t *logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t top_p, int32_t t_m, int32_t t_k, const uint32_t *draws,

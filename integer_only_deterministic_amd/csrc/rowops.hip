@@ -833,7 +833,9 @@ __device__ __forceinline__ int32_t wave_sum32(int32_t v) {
 __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
                                                int32_t top_p, int32_t t_m, int32_t t_k,
                                                const uint32_t* __restrict__ draws,
-                                               int32_t* __restrict__ out) {
+                                               int32_t* __restrict__ out,
+                                               const int32_t* __restrict__ done) {
+  if (done && done[blockIdx.x]) return;  // row already sampled
   __shared__ int32_t hw[SMW][256];                // per-wave histograms (counts)
   __shared__ unsigned long long hm[SMW][256];     // per-wave histograms (weights, top-p)
   __shared__ int32_t hist[256];
@@ -1182,7 +1184,9 @@ __global__ __launch_bounds__(SLT) void sample_pick_k(const int32_t* __restrict__
 //      places the draw in id order.
 // The same integer function as sample_k.
 constexpr int TKS = 2048, TKT = 512, TKN = TKS / TKT;  // ids per slice, threads, ids per thread
-constexpr int TKC = 16384, TPT = 1024, TPN = TKC / TPT;  // candidates per row, pick threads
+constexpr int TPT = 1024;             // pick threads
+constexpr int TKC = 16 * TPT;         // candidate row stride: 16 a thread for top-p alone
+constexpr int TKK = 8 * TPT;          // top-k: 8 a thread
 
 // Inclusive prefix sum over the workgroup in thread order; also the total.
 template <int NT>
@@ -1202,23 +1206,24 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
   return before + inc;
 }
 
-// Radix select over the valid keys held by the workgroup, each key weighing
-// wv (all 1: the n-th largest key), on digits of key - (smallest key) taken 8
+// Radix select over the valid keys held by the workgroup, key e weighing
+// wv(e) (all 1: the n-th largest key), on digits of key - (smallest key) taken 8
 // bits a pass from the top of that span (so the first pass already spreads
 // keys that share their high bits over the bins). Finds
 // the largest T such that the keys at or above T weigh at least n
 // (1 <= n <= total weight, total below 2^31), and returns in tneed the
 // weight still needed from the keys equal to T (>= 1) beyond those above it.
-template <int NT, int N>
-__device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (&ok)[N],
-                                          const int32_t (&wv)[N], int n, int32_t* hist,
+template <int NT, int N, typename WF>
+__device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm, WF wv, int n,
+                                          int32_t* hist,
                                           int64_t* wt, int64_t* red, int* sel, uint32_t& T,
                                           int& tneed) {
   uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    kmx = ok[e] && key[e] > kmx ? key[e] : kmx;
-    kmn = ok[e] && key[e] < kmn ? key[e] : kmn;
+    const bool ok = okm >> e & 1;
+    kmx = ok && key[e] > kmx ? key[e] : kmx;
+    kmn = ok && key[e] < kmn ? key[e] : kmn;
   }
   kmx = (uint32_t)block_max((int64_t)kmx, red);
   kmn = ~(uint32_t)block_max((int64_t)(~kmn), red);
@@ -1233,7 +1238,7 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (
 #pragma unroll
     for (int e = 0; e < N; ++e) {
       const uint32_t d = key[e] - kmn;
-      if (ok[e] && (d & pmask) == prefix) atomicAdd(&hist[(d >> lo) & dm], wv[e]);
+      if ((okm >> e & 1) && (d & pmask) == prefix) atomicAdd(&hist[(d >> lo) & dm], wv(e));
     }
     __syncthreads();
     // bins from the top down: thread i holds bin 255 - i
@@ -1253,156 +1258,209 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], const bool (
   tneed = rem;
 }
 
-// take[e]: key above T, or equal to T and among the first tneed such keys in
-// thread-major order (which is id order); returns how many this thread takes.
+// Bit e of the result: valid key e above T, or equal to T and among the
+// first tneed such keys in thread-major order (which is id order).
 template <int NT, int N>
-__device__ __forceinline__ int take_top(const uint32_t (&key)[N], const bool (&ok)[N], uint32_t T,
-                                        int tneed, int64_t* wt, bool (&take)[N]) {
+__device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[N], uint32_t okm, uint32_t T,
+                                             int tneed, int64_t* wt) {
   int ties = 0;
 #pragma unroll
-  for (int e = 0; e < N; ++e) ties += ok[e] && key[e] == T;
+  for (int e = 0; e < N; ++e) ties += (okm >> e & 1) && key[e] == T;
   int64_t tt;
   int tb = (int)(block_incl_scan<NT>(ties, wt, tt) - ties);
-  int nt = 0;
+  uint32_t tm = 0;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    const bool eq = ok[e] && key[e] == T;
-    take[e] = ok[e] && (key[e] > T || (eq && tb < tneed));
+    const bool ok = okm >> e & 1, eq = ok && key[e] == T;
+    tm |= (uint32_t)(ok && (key[e] > T || (eq && tb < tneed))) << e;
     tb += eq;
-    nt += take[e];
   }
-  return nt;
+  return tm;
 }
 
 __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ logits, int V,
-                                                    int kc, uint64_t* __restrict__ cand) {
+                                                    int kc, uint64_t* __restrict__ cand,
+                                                    uint32_t* __restrict__ sT) {
   __shared__ int32_t hist[256];
   __shared__ int64_t wt[TKT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
   const int32_t* l = logits + (size_t)r * V;
   const int j0 = p * TKS + TKN * tid;
-  uint32_t key[TKN];
-  bool ok[TKN], take[TKN];
+  uint32_t key[TKN], okm = 0;
 #pragma unroll
   for (int e = 0; e < TKN; ++e) {
-    ok[e] = j0 + e < V;
+    okm |= (uint32_t)(j0 + e < V) << e;
     key[e] = okey(l[min(j0 + e, V - 1)]);
   }
   const int kk = min(kc, V - p * TKS);  // ids kept from this slice
-  const int32_t one[TKN] = {1, 1, 1, 1};
   uint32_t T;
   int tneed;
-  radix_nth<TKT, TKN>(key, ok, one, kk, hist, wt, red, sel, T, tneed);
-  const int nt = take_top<TKT, TKN>(key, ok, T, tneed, wt, take);
+  radix_nth<TKT, TKN>(key, okm, [](int) { return 1; }, kk, hist, wt, red, sel, T, tneed);
+  const uint32_t take = take_top<TKT, TKN>(key, okm, T, tneed, wt);
+  const int nt = __popc(take);
   int64_t tot;
   int at = (int)(block_incl_scan<TKT>(nt, wt, tot) - nt);
   uint64_t* dst = cand + (size_t)r * TKC + (size_t)p * kc;
 #pragma unroll
   for (int e = 0; e < TKN; ++e)
-    if (take[e] && at < kk) dst[at++] = (uint64_t)key[e] << 32 | (uint32_t)~(uint32_t)(j0 + e);
+    if ((take >> e & 1) && at < kk) dst[at++] = (uint64_t)key[e] << 32 | (uint32_t)~(uint32_t)(j0 + e);
   for (int i = kk + tid; i < kc; i += TKT) dst[i] = 0;
+  // the cut key of a slice that had more ids than it kept (0: kept them all)
+  if (sT && tid == 0) sT[(size_t)r * gridDim.x + p] = min(TKS, V - p * TKS) > kc ? T : 0;
 }
 
+// NUC: top-p over the whole row (no top-k). Every candidate is kept, the
+// nucleus target comes from the weight of the whole row (the per-step sums
+// of sample_wsum_k), and the result stands only if the nucleus threshold
+// key lies above every cut key sT of a slice that had more ids than it
+// kept: then the candidates hold every id at or above that key, so the
+// nucleus, its ties and the draw are the whole row's. done[r] says whether
+// it stood; sample_k, launched after, redoes the rows where it did not.
+template <bool NUC>
 __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
                                                    int keep, int32_t top_p, int32_t t_m, int32_t t_k,
                                                    const uint32_t* __restrict__ draws,
-                                                   int32_t* __restrict__ out) {
+                                                   int32_t* __restrict__ out,
+                                                   const int32_t* __restrict__ ssum, int P,
+                                                   const uint32_t* __restrict__ sT, int P2,
+                                                   int32_t* __restrict__ done) {
+  constexpr int N = NUC ? TKC / TPT : TKK / TPT;  // candidates a thread
   __shared__ int32_t hist[256];
   __shared__ int64_t wt[TPT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.x, tid = threadIdx.x;
-  const uint64_t* c = cand + (size_t)r * TKC;
-  uint64_t cv[TPN];
-  uint32_t key[TPN], km = 0;
-  bool ok[TPN], take[TPN];
+  const uint64_t* c = cand + (size_t)r * TKC + N * tid;  // this thread's entries
+  const int nmine = min(N, max(0, nc - N * tid));
+  uint32_t key[N], km = 0, okm = 0;
 #pragma unroll
-  for (int e = 0; e < TPN; ++e) {
-    const int i = TPN * tid + e;
-    cv[e] = i < nc ? c[i] : 0;
-    ok[e] = cv[e] != 0;
-    key[e] = (uint32_t)(cv[e] >> 32);
-    km = ok[e] && key[e] > km ? key[e] : km;
+  for (int e = 0; e < N; ++e) {
+    const uint64_t cv = e < nmine ? c[e] : 0;
+    okm |= (uint32_t)(cv != 0) << e;
+    key[e] = (uint32_t)(cv >> 32);
+    km = cv != 0 && key[e] > km ? key[e] : km;
   }
   const int32_t mx = (int32_t)((uint32_t)block_max((int64_t)km, red) ^ 0x80000000u);
-  int32_t w[TPN];
-#pragma unroll
-  for (int e = 0; e < TPN; ++e) w[e] = 1;
-  uint32_t T;
-  int tneed;
-  radix_nth<TPT, TPN>(key, ok, w, keep, hist, wt, red, sel, T, tneed);
-  take_top<TPT, TPN>(key, ok, T, tneed, wt, take);
-  int64_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < TPN; ++e) {
-    w[e] = take[e] ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
-    mine += w[e];
+  // weights recomputed where needed rather than held (register pressure)
+  auto wgt = [&](int e) -> int32_t {
+    return expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k);
+  };
+  uint32_t take = okm;
+  if constexpr (!NUC) {
+    uint32_t T;
+    int tneed;
+    radix_nth<TPT, N>(key, okm, [](int) { return 1; }, keep, hist, wt, red, sel, T, tneed);
+    take = take_top<TPT, N>(key, okm, T, tneed, wt);
   }
-  if (top_p < 65536) {
-    // the shortest prefix of the ranking among the kept ids whose weight
-    // reaches ceil(top_p D_k / 2^16): a weighted select (D_k < 2^30), then
-    // ceil(rest / weight of that key) of its ties, lowest ids first
-    int64_t Dk;
-    block_incl_scan<TPT>(mine, wt, Dk);
-    uint32_t Lp;
-    int rest;
-    radix_nth<TPT, TPN>(key, take, w, (int)(((int64_t)top_p * Dk + 65535) >> 16), hist, wt, red,
-                        sel, Lp, rest);
-    const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
-    bool nuc[TPN];
-    take_top<TPT, TPN>(key, take, Lp, (rest + wp - 1) / wp, wt, nuc);
-    mine = 0;
+  auto weight_of = [&](uint32_t m) {
+    int64_t s = 0;
 #pragma unroll
-    for (int e = 0; e < TPN; ++e) {
-      w[e] = nuc[e] ? w[e] : 0;
-      mine += w[e];
+    for (int e = 0; e < N; ++e) s += m >> e & 1 ? wgt(e) : 0;
+    return s;
+  };
+  int64_t mine = weight_of(take);
+  if (NUC || top_p < 65536) {
+    // the shortest prefix of the ranking whose weight reaches
+    // ceil(top_p D / 2^16), D the weight of the kept ids (of the whole row
+    // for NUC): a weighted select over the candidates (their weight is below
+    // 2^30), then ceil(rest / weight of that key) of its ties, lowest ids first
+    int64_t Wc, Dk;
+    block_incl_scan<TPT>(mine, wt, Wc);
+    Dk = Wc;
+    uint32_t tc = 0;
+    if constexpr (NUC) {
+      int64_t ds = 0;
+      for (int i = tid; i < 4 * P; i += TPT) ds += ssum[(size_t)r * P * 4 + i];
+      block_incl_scan<TPT>(ds, wt, Dk);
+      for (int i = tid; i < P2; i += TPT) tc = max(tc, sT[(size_t)r * P2 + i]);
+      tc = (uint32_t)block_max((int64_t)tc, red);
     }
+    const int64_t need = ((int64_t)top_p * Dk + 65535) >> 16;
+    uint32_t Lp = 0;
+    int rest = 0;
+    bool good = need <= Wc;  // uniform over the workgroup
+    if (good) {
+      radix_nth<TPT, N>(key, take, wgt, (int)need, hist, wt, red, sel, Lp, rest);
+      good = !NUC || Lp > tc;
+    }
+    if (NUC && !good) {
+      if (tid == 0) done[r] = 0;
+      return;
+    }
+    const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
+    take = take_top<TPT, N>(key, take, Lp, (rest + wp - 1) / wp, wt);
+    mine = weight_of(take);
+    if (NUC && tid == 0) done[r] = 1;
   }
   int64_t D;
   int64_t run = block_incl_scan<TPT>(mine, wt, D) - mine;  // weight of earlier ids
   const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
   if (run <= t && t < run + mine) {
 #pragma unroll
-    for (int e = 0; e < TPN; ++e) {
-      if (run + w[e] > t) {
-        out[r] = (int32_t)~(uint32_t)cv[e];
+    for (int e = 0; e < N; ++e) {
+      const int64_t w = take >> e & 1 ? wgt(e) : 0;
+      if (run + w > t) {
+        out[r] = (int32_t)~(uint32_t)c[e];  // reload the entry for its id
         break;
       }
-      run += w[e];
+      run += w;
     }
   }
 }
 
+// Workspace: candidates [R][TKC] u64 | slice maxima [R][P] | step sums
+// [R][P][4] | slice cut keys [R][P2] | done flags [R]  (P = 1024-id slices,
+// P2 = 2048-id slices); the plain path uses maxima and step sums only.
 int64_t sample_workspace_bytes(int64_t R, int64_t V) {
-  const int64_t P = (V + SLC - 1) / SLC;
-  return R * std::max<int64_t>(P * 4 * (1 + 4), TKC * 8);
+  const int64_t P = (V + SLC - 1) / SLC, P2 = (V + TKS - 1) / TKS;
+  return R * (TKC * 8 + P * 4 * (1 + 4) + P2 * 4 + 4);
 }
 
 hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
                          int32_t t_m, int32_t t_k, const uint32_t* draws, int32_t* out, void* ws,
                          int64_t ws_bytes, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  if (ws && keep >= V && top_p >= 65536 && ws_bytes >= sample_workspace_bytes(R, V) &&
-      R <= 65535) {
-    const int P = (int)((V + SLC - 1) / SLC);
-    int32_t* smax = (int32_t*)ws;
-    int32_t* ssum = smax + R * P;
-    sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, P, smax);
-    sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax,
-                                                                  ssum);
-    sample_pick_k<<<(unsigned)R, SLT, 0, st>>>(logits, (int)V, P, t_m, t_k, smax, ssum, draws, out);
+  const int64_t P = (V + SLC - 1) / SLC, P2 = (V + TKS - 1) / TKS;
+  const bool fits = ws && ws_bytes >= sample_workspace_bytes(R, V) && R <= 65535;
+  uint64_t* cand = (uint64_t*)ws;
+  int32_t* smax = (int32_t*)(cand + R * TKC);
+  int32_t* ssum = smax + R * P;
+  uint32_t* sT = (uint32_t*)(ssum + R * P * 4);
+  int32_t* done = (int32_t*)(sT + R * P2);
+  if (fits && keep >= V && top_p >= 65536) {
+    sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, smax);
+    sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k,
+                                                                  smax, ssum);
+    sample_pick_k<<<(unsigned)R, SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k, smax, ssum, draws,
+                                               out);
     return hipGetLastError();
   }
-  const int64_t P2 = (V + TKS - 1) / TKS, kc = std::min<int64_t>(keep, TKS);
-  if (ws && keep < V && P2 * kc <= TKC &&
-      ws_bytes >= sample_workspace_bytes(R, V) && R <= 65535) {
-    uint64_t* cand = (uint64_t*)ws;
-    topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kc, cand);
-    topk_pick_k<<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p, t_m, t_k,
-                                             draws, out);
+  const int64_t kc = std::min<int64_t>(keep, TKS);
+  if (fits && keep < V && P2 * kc <= TKK) {
+    topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kc, cand,
+                                                                  nullptr);
+    topk_pick_k<false><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p, t_m,
+                                                    t_k, draws, out, nullptr, 0, nullptr, 0,
+                                                    nullptr);
     return hipGetLastError();
   }
-  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);
+  if (fits && keep >= V) {
+    // top-p alone: each slice's top kn ids as candidates, the whole row's
+    // weight from the step sums; rows whose nucleus reaches below a slice's
+    // cut go to sample_k
+    const int64_t kn = std::min<int64_t>(TKS, TKC / P2);
+    sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, smax);
+    sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k,
+                                                                  smax, ssum);
+    topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kn, cand, sT);
+    topk_pick_k<true><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kn), (int)V, top_p, t_m, t_k,
+                                                   draws, out, ssum, (int)P, sT, (int)P2, done);
+    sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out,
+                                          done);
+    return hipGetLastError();
+  }
+  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out,
+                                        nullptr);
   return hipGetLastError();
 }
 

@@ -50,13 +50,13 @@ def test_sample_matches_oracle(D, V, kind):
     logits = _logits(kind, R, V, rng)
     draws = rng.integers(0, 1 << 32, R, dtype=np.uint64).astype(np.uint32)
     draws[:2] = [0, (1 << 32) - 1]
-    for k in sorted({0, 1, 5, 50, 200, max(V - 1, 1), V}):
+    for k in sorted({0, 1, 5, 50, 100, max(V - 1, 1), V}):
         for tm in (T1, HOT, COLD):
             want = O.sample(logits, k, tm[0], tm[1], draws)
             got = _run(D, logits, k, tm, draws)
             np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm}")
             # with a workspace: the sliced paths (every id kept, or top-k
-            # with at most 16384 slice candidates)
+            # with at most 8192 slice candidates)
             got = _run(D, logits, k, tm, draws, ws=True)
             np.testing.assert_array_equal(got, want, err_msg=f"k={k} t={tm} (workspace)")
 
