@@ -1215,7 +1215,7 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
 // weight still needed from the keys equal to T (>= 1) beyond those above it.
 template <int NT, int N, typename WF>
 __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm, WF wv, int n,
-                                          int32_t* hist,
+                                          int32_t (*hw)[256],
                                           int64_t* wt, int64_t* red, int* sel, uint32_t& T,
                                           int& tneed) {
   uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
@@ -1233,16 +1233,20 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm
   for (int hi = B; hi > 0; hi -= 8) {  // digit = bits [lo, hi) of key - kmn
     const int lo = hi > 8 ? hi - 8 : 0;
     const uint32_t dm = (1u << (hi - lo)) - 1;
-    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    for (int i = threadIdx.x; i < NT / 64 * 256; i += NT) hw[i >> 8][i & 255] = 0;
     __syncthreads();
+    int32_t* mh = hw[threadIdx.x >> 6];  // this wave's histogram
 #pragma unroll
     for (int e = 0; e < N; ++e) {
       const uint32_t d = key[e] - kmn;
-      if ((okm >> e & 1) && (d & pmask) == prefix) atomicAdd(&hist[(d >> lo) & dm], wv(e));
+      if ((okm >> e & 1) && (d & pmask) == prefix) atomicAdd(&mh[(d >> lo) & dm], wv(e));
     }
     __syncthreads();
     // bins from the top down: thread i holds bin 255 - i
-    const int64_t c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0;
+    int64_t c = 0;
+    if (threadIdx.x < 256)
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) c += hw[w][255 - threadIdx.x];
     int64_t tot;
     const int64_t inc = block_incl_scan<NT>(c, wt, tot);
     if (inc - c < rem && rem <= inc) {
@@ -1281,7 +1285,7 @@ __device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[N], uint32_t 
 __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ logits, int V,
                                                     int kc, uint64_t* __restrict__ cand,
                                                     uint32_t* __restrict__ sT) {
-  __shared__ int32_t hist[256];
+  __shared__ int32_t hw[TKT / 64][256];
   __shared__ int64_t wt[TKT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
@@ -1296,7 +1300,7 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
   const int kk = min(kc, V - p * TKS);  // ids kept from this slice
   uint32_t T;
   int tneed;
-  radix_nth<TKT, TKN>(key, okm, [](int) { return 1; }, kk, hist, wt, red, sel, T, tneed);
+  radix_nth<TKT, TKN>(key, okm, [](int) { return 1; }, kk, hw, wt, red, sel, T, tneed);
   const uint32_t take = take_top<TKT, TKN>(key, okm, T, tneed, wt);
   const int nt = __popc(take);
   int64_t tot;
@@ -1326,7 +1330,8 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
                                                    const uint32_t* __restrict__ sT, int P2,
                                                    int32_t* __restrict__ done) {
   constexpr int N = NUC ? TKC / TPT : TKK / TPT;  // candidates a thread
-  __shared__ int32_t hist[256];
+  __shared__ int32_t hw[TPT / 64][256];
+  __shared__ int32_t wl[N][TPT];  // candidate weights, element-major
   __shared__ int64_t wt[TPT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -1341,15 +1346,16 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     km = cv != 0 && key[e] > km ? key[e] : km;
   }
   const int32_t mx = (int32_t)((uint32_t)block_max((int64_t)km, red) ^ 0x80000000u);
-  // weights recomputed where needed rather than held (register pressure)
-  auto wgt = [&](int e) -> int32_t {
-    return expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k);
-  };
+  // each weight computed once, kept in LDS (not registers: pressure)
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    wl[e][tid] = okm >> e & 1 ? expw_of((int32_t)(key[e] ^ 0x80000000u), mx, t_m, t_k) : 0;
+  auto wgt = [&](int e) -> int32_t { return wl[e][tid]; };
   uint32_t take = okm;
   if constexpr (!NUC) {
     uint32_t T;
     int tneed;
-    radix_nth<TPT, N>(key, okm, [](int) { return 1; }, keep, hist, wt, red, sel, T, tneed);
+    radix_nth<TPT, N>(key, okm, [](int) { return 1; }, keep, hw, wt, red, sel, T, tneed);
     take = take_top<TPT, N>(key, okm, T, tneed, wt);
   }
   auto weight_of = [&](uint32_t m) {
@@ -1380,7 +1386,7 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     int rest = 0;
     bool good = need <= Wc;  // uniform over the workgroup
     if (good) {
-      radix_nth<TPT, N>(key, take, wgt, (int)need, hist, wt, red, sel, Lp, rest);
+      radix_nth<TPT, N>(key, take, wgt, (int)need, hw, wt, red, sel, Lp, rest);
       good = !NUC || Lp > tc;
     }
     if (NUC && !good) {
