@@ -176,6 +176,7 @@ class Layer:
     kq_k: int
     vq_m: int
     vq_k: int
+    k_gain: np.ndarray | None = None  # [n_kv, d] int8 per-channel key gains, or None
 
 
 @dataclass
@@ -234,7 +235,19 @@ def model_digest(m: Model) -> str:
             if a is not None:
                 h.update(np.ascontiguousarray(a).tobytes())
         h.update(np.array([L.kq_m, L.kq_k, L.vq_m, L.vq_k], np.int64).tobytes())
+        if L.k_gain is not None:
+            h.update(np.ascontiguousarray(L.k_gain).tobytes())
     return h.hexdigest()
+
+
+def with_key_gains(m: Model, seed: int, gmax: int = 3) -> Model:
+    """The same model with seeded per-channel key gains in [0, gmax] on every
+    layer (random stand-ins for calibrated ones)."""
+    rng = np.random.default_rng(seed)
+    sh = m.shape
+    for L in m.layers:
+        L.k_gain = rng.integers(0, gmax + 1, (sh.n_kv, sh.head_dim)).astype(np.int8)
+    return m
 
 
 # --------------------------------------------------------------------------

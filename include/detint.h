@@ -214,6 +214,14 @@ typedef struct detint_layer_desc {
   const int16_t *q_norm, *k_norm;        /* [d] gains (qk_norm models) or NULL */
   int32_t kq_m, kq_k;                    /* K-cache quant scale: k8 = clamp8(R(k * kq_m, kq_k)) */
   int32_t vq_m, vq_k;                    /* V-cache quant scale */
+  /* Per-channel key rescale with the inverse on the query (DetLLM blog
+   * footnote 8): device int8 [n_kv][d], each g in [0, 7], or NULL (all 0).
+   * Key channel j of KV head h is cached as clamp8(R(k_j * kq_m, kq_k - g))
+   * and channel j of every query head sharing h enters its DQ as R(q_j, g),
+   * g = k_gain[h * d + j]: the factors 2^g and 2^-g cancel in q.k, so the
+   * score scale (and the softmax multiplier) stay those of kq_m / 2^kq_k.
+   * Requires kq_k >= 8. */
+  const int8_t *k_gain;
 } detint_layer_desc;
 
 typedef struct detint_model_desc {

@@ -38,7 +38,7 @@ class LayerDesc(C.Structure):
                 ("wgu", vp), ("wgu_lo", vp), ("wgu_m", vp),
                 ("wd", vp), ("wd_lo", vp), ("wd_m", vp),
                 ("attn_norm", vp), ("ffn_norm", vp), ("q_norm", vp), ("k_norm", vp),
-                ("kq_m", i32), ("kq_k", i32), ("vq_m", i32), ("vq_k", i32)]
+                ("kq_m", i32), ("kq_k", i32), ("vq_m", i32), ("vq_k", i32), ("k_gain", vp)]
 
 
 class ModelDesc(C.Structure):
@@ -376,6 +376,8 @@ class DetintModel:
             st.q_norm = _p(up(Lw.q_norm)) if Lw.q_norm is not None else None
             st.k_norm = _p(up(Lw.k_norm)) if Lw.k_norm is not None else None
             st.kq_m, st.kq_k, st.vq_m, st.vq_k = Lw.kq_m, Lw.kq_k, Lw.vq_m, Lw.vq_k
+            kg = getattr(Lw, "k_gain", None)
+            st.k_gain = _p(up(np.ascontiguousarray(kg, np.int8))) if kg is not None else None
         cos_t, sin_t = detint_rope_tables(sh.max_pos, sh.head_dim, sh.rope_base)
         self.rope_cos, self.rope_sin = up(cos_t), up(sin_t)
         d = ModelDesc(n_layers=sh.n_layers, hidden=sh.hidden, n_q=sh.n_q, n_kv=sh.n_kv,

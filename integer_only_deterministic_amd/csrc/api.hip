@@ -464,6 +464,8 @@ detint_status detint_model_create(const detint_model_desc* desc, detint_model** 
             "model_create: layer %lld has a null pointer", (long long)l);
     if (d.qk_norm) REQUIRE(L.q_norm && L.k_norm, "model_create: qk_norm needs q/k gains");
     if (d.wide) REQUIRE(L.wqkv_lo && L.wo_lo && L.wgu_lo && L.wd_lo, "model_create: wide limbs");
+    if (L.k_gain) REQUIRE(L.kq_k >= 8, "model_create: key gains need kq_k >= 8 (layer %lld)",
+                          (long long)l);
   }
   REQUIRE(!(d.wide && d.qk_norm), "model_create: wide weights with q/k-norm not supported");
   detint_model* m = new detint_model();
@@ -530,7 +532,7 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
     LAUNCH(launch_gemm(x8, L.wqkv, d.wide ? L.wqkv_lo : nullptr, R, nqkv, H, ep, qkv, st, sp));
   }
   QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
-             L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
+             L.vq_m, L.vq_k, d.rope_cos, d.rope_sin, L.k_gain};
   if (max_seqlen == 1 && seqs.cu && (int64_t)seqs.S == R) {
     // one row per sequence (decode rows): post-processing fused into the
     // attention kernel, which reads row r's position and slot from
@@ -607,7 +609,7 @@ static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* 
     LAUNCH(launch_fused_qkv(h, L.attn_norm, L.wqkv, L.wqkv_m, wk, d.qk_norm ? 0 : d.f_n,
                             d.qk_norm != 0, R, nqkv, H, qkv, rm, rk, st));
     QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
-               L.vq_m, L.vq_k, d.rope_cos, d.rope_sin};
+               L.vq_m, L.vq_k, d.rope_cos, d.rope_sin, L.k_gain};
     LAUNCH(launch_attention_decode_fused(qkv, qp, start_pos, slot, R, nq, nkv, hd, n_slots,
                                          d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att, st));
     LAUNCH(launch_fused_oproj(att, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, L.wo, L.wo_m, wk, d.f_res,

@@ -411,9 +411,14 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
         x1 = R(a1 * hg1[u] * m, sh + 12 - p.f_n);
       }
     }
-    const int64_t y0 = act ? R(x0 * cs - x1 * sn, 14) : 0;
-    const int64_t y1 = act ? R(x1 * cs + x0 * sn, 14) : 0;
+    int64_t y0 = act ? R(x0 * cs - x1 * sn, 14) : 0;
+    int64_t y1 = act ? R(x1 * cs + x0 * sn, 14) : 0;
+    // per-channel key gains: 2^-g on the query, 2^g on the key
+    const int g0 = p.k_gain && act ? p.k_gain[(size_t)kvh * D + j0] & 7 : 0;
+    const int g1 = p.k_gain && act ? p.k_gain[(size_t)kvh * D + j1] & 7 : 0;
     if (t < G) {
+      y0 = R(y0, g0);
+      y1 = R(y1, g1);
       const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
       const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
       int8_t* qd = (int8_t*)sq + t * D;
@@ -424,7 +429,8 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
       if (lane == 0) seq[t] = e;
     } else if (act) {  // key head
       int8_t* dst = kc + base + (size_t)pos * D;
-      const int8_t k0 = clamp8(R(y0 * p.kq_m, p.kq_k)), k1 = clamp8(R(y1 * p.kq_m, p.kq_k));
+      const int8_t k0 = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
+      const int8_t k1 = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
       dst[j0] = k0;
       dst[j1] = k1;
       snk[j0] = k0;

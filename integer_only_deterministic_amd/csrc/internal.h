@@ -107,6 +107,7 @@ struct QkvPost {
   int32_t kq_m, kq_k, vq_m, vq_k;
   const int16_t* cos_t;
   const int16_t* sin_t;
+  const int8_t* k_gain;       // [nkv][d] per-channel key gains in [0, 7], or null
 };
 hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nkv, int64_t d,
                            const int32_t* pos_of, const int32_t* slot_of, const QkvPost& p,

@@ -70,6 +70,11 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
     y1 = R(x1 * c + x0 * s, 14);
   }
   if (hh < nq) {
+    if (p.k_gain && act) {  // the inverse of the key gain of the shared KV head
+      const int8_t* g = p.k_gain + (size_t)(hh / (nq / nkv)) * d;
+      y0 = R(y0, g[j0] & 7);
+      y1 = R(y1, g[j1] & 7);
+    }
     const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
     const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
     if (act) {
@@ -80,8 +85,9 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
   } else if (act && ok) {
     const int kvh = hh - nq;
     int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
-    dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k));
-    dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k));
+    const int8_t* g = p.k_gain ? p.k_gain + (size_t)kvh * d : nullptr;
+    dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - (g ? g[j0] & 7 : 0)));
+    dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - (g ? g[j1] & 7 : 0)));
   }
 }
 

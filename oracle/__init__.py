@@ -64,7 +64,7 @@ class OrcLayer(C.Structure):
                 ("wgu", vp), ("wgu16", vp), ("wgu_m", vp),
                 ("wd", vp), ("wd16", vp), ("wd_m", vp),
                 ("attn_norm", vp), ("ffn_norm", vp), ("q_norm", vp), ("k_norm", vp),
-                ("kq_m", i32), ("kq_k", i32), ("vq_m", i32), ("vq_k", i32)]
+                ("kq_m", i32), ("kq_k", i32), ("vq_m", i32), ("vq_k", i32), ("k_gain", vp)]
 
 
 class OrcModel(C.Structure):
@@ -365,6 +365,8 @@ class OracleModel:
             st.q_norm = self._ptr(Lw.q_norm) if Lw.q_norm is not None else None
             st.k_norm = self._ptr(Lw.k_norm) if Lw.k_norm is not None else None
             st.kq_m, st.kq_k, st.vq_m, st.vq_k = Lw.kq_m, Lw.kq_k, Lw.vq_m, Lw.vq_k
+            kg = getattr(Lw, "k_gain", None)
+            st.k_gain = self._ptr(np.ascontiguousarray(kg, np.int8)) if kg is not None else None
         self._layers = layers
         md = OrcModel(n_layers=sh.n_layers, hidden=sh.hidden, n_q=sh.n_q, n_kv=sh.n_kv,
                       head_dim=sh.head_dim, ffn=sh.ffn, vocab=sh.vocab, max_pos=sh.max_pos,

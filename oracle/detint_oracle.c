@@ -497,6 +497,7 @@ typedef struct {
   const int8_t *wd;   const int16_t *wd16;   const int32_t *wd_m;
   const int16_t *attn_norm, *ffn_norm, *q_norm, *k_norm;
   int32_t kq_m, kq_k, vq_m, vq_k;
+  const int8_t *k_gain; /* [n_kv][d] per-channel key gains in [0, 7], or NULL */
 } orc_layer;
 
 typedef struct {
@@ -664,12 +665,23 @@ int orc_layer_forward(const orc_model *md, int64_t l, int32_t *h, int64_t R_,
       rope_vec(v, d, cr, sr);
       for (int64_t j = 0; j < d; j++)
         CHECK(v[j] < ((int64_t)1 << 31) && v[j] > -((int64_t)1 << 31), "rotated q/k exceeds int32");
+      /* per-channel key rescale (DetLLM blog footnote 8): key channel j
+       * of KV head h scaled by 2^g, query channel j of the heads sharing h
+       * by 2^-g before their quantisation, g = k_gain[h][j] */
+      const int64_t kvh = is_q ? hh / (nq / nkv) : hh - nq;
+      const int8_t *g = L->k_gain ? L->k_gain + kvh * d : NULL;
+      if (g) {
+        CHECK(L->kq_k >= 8, "key gains need kq_k >= 8");
+        for (int64_t j = 0; j < d; j++) CHECK(g[j] >= 0 && g[j] <= 7, "key gain outside [0, 7]");
+      }
       if (is_q) {
+        if (g)
+          for (int64_t j = 0; j < d; j++) v[j] = R(v[j], g[j]);
         orc_dq(v, d, q8 + (r * nq + hh) * d, eq + r * nq + hh);
       } else {
-        int64_t kvh = hh - nq;
         int8_t *dst = kv_at(kc, md, slots, l, slot[seq_of[r]], kvh, p);
-        for (int64_t j = 0; j < d; j++) dst[j] = clamp8(R(v[j] * L->kq_m, L->kq_k));
+        for (int64_t j = 0; j < d; j++)
+          dst[j] = clamp8(R(v[j] * L->kq_m, L->kq_k - (g ? g[j] : 0)));
       }
     }
   }

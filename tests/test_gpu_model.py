@@ -59,6 +59,37 @@ def test_tiny_kv_cache_matches_oracle(D):
     np.testing.assert_array_equal(host(dm.vc), om.vc)
 
 
+# ------------------------------- per-channel key gains (DetLLM blog footnote 8)
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wide"])
+@pytest.mark.parametrize("use_graph", [True, False])
+def test_tiny_key_gains_match_oracle(D, name, use_graph):
+    """Seeded key gains on every layer: prefill (QKV post-processing kernel)
+    and decode (fused attention, one query head per workgroup) logits, and
+    the cached keys, equal the oracle's."""
+    m = S.with_key_gains(S.make_model(name, seed=23), seed=24, gmax=2)
+    V = m.shape.vocab
+    prompts = [S.make_prompt(V, 7, 1), S.make_prompt(V, 30, 2), S.make_prompt(V, 19, 3)]
+    rows = []
+    om = O.OracleModel(m, slots=3)
+    om.generate(prompts, 12, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=3)
+    hist = host(dm.generate(prompts, 12, use_graph=use_graph))
+    np.testing.assert_array_equal(hist, np.stack(rows))
+    np.testing.assert_array_equal(host(dm.kc), om.kc)
+
+
+def test_tiny_key_gains_batch32_match_oracle(D):
+    """32 decode rows: the fused attention takes every query head of a KV
+    head per workgroup."""
+    m = S.with_key_gains(S.make_model("tiny", seed=25), seed=26, gmax=2)
+    prompts = [S.make_prompt(1000, 3 + (i * 7) % 20, 30 + i) for i in range(32)]
+    rows = []
+    O.OracleModel(m, slots=32).generate(prompts, 4, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=32)
+    np.testing.assert_array_equal(host(dm.generate(prompts, 4, use_graph=True)), np.stack(rows))
+
+
 # ----------------------------------------------------- Qwen3-0.6B shape
 
 @pytest.fixture(scope="module")

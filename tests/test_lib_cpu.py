@@ -99,6 +99,15 @@ def test_validation_rejects_before_device_work(D):
     h = C.c_void_p()
     assert lib.detint_model_create(C.byref(desc), C.byref(h)) == D.DETINT_EINVAL
     assert lib.detint_workspace_size(None, 1, 1) == -1
+    # key gains need kq_k >= 8 (the key shift kq_k - g stays >= 1)
+    L = D.LayerDesc(wqkv=fake, wqkv_m=fake, wo=fake, wo_m=fake, wgu=fake, wgu_m=fake, wd=fake,
+                    wd_m=fake, attn_norm=fake, ffn_norm=fake, kq_m=1 << 14, kq_k=7,
+                    vq_m=1 << 14, vq_k=20, k_gain=fake)
+    layers = (D.LayerDesc * 1)(L)
+    desc.layers = C.cast(layers, C.POINTER(D.LayerDesc))
+    desc.rope_cos = desc.rope_sin = fake
+    assert lib.detint_model_create(C.byref(desc), C.byref(h)) == D.DETINT_EINVAL
+    assert b"kq_k >= 8" in lib.detint_last_error()
     # sampling: vocabulary, temperature and top-p ranges; empty batch is a no-op
     T = (23637, 15)
     rc = lib.detint_sample(fake, 1, 262145, 0, 65536, *T, fake, fake, None, 0, None)

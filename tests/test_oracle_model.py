@@ -164,3 +164,95 @@ def test_forward_invariances(name):
     # repeated runs are identical
     again = O.OracleModel(m, slots=4).generate([p0] + others, n_new)
     np.testing.assert_array_equal(again, batch)
+
+
+# ------------------------------------------ per-channel key rescale (footnote 8)
+
+def _gained_layer(seed, gains=None, k_norm=None):
+    m = S.make_model("layer256", seed=1)
+    if k_norm is not None:
+        m.layers[0].k_norm = k_norm
+    if gains is not None:
+        m.layers[0].k_gain = gains
+    h0 = S.make_residual(64, 256, seed=2)
+    om = O.OracleModel(m, slots=1)
+    h1, dmp = om.layer(0, h0, [64], [0], [0], dump=True)
+    return m, h0, h1, dmp, om
+
+
+def test_key_gains_zero_is_the_plain_layer(layer256):
+    _, _, h1, _, om = layer256
+    z = np.zeros((2, 64), np.int8)
+    _, _, h1z, _, omz = _gained_layer(1, gains=z)
+    np.testing.assert_array_equal(h1z, h1)
+    np.testing.assert_array_equal(omz.kc, om.kc)
+
+
+def _calibrated_gains(kc):
+    """Largest power of two that keeps each channel's cached keys in range,
+    from a run without gains: g = floor(log2(126 / max |k8|)), in [0, 7]."""
+    mx = np.abs(kc.astype(np.int64)).max(axis=1)                        # [nkv, d]
+    return np.clip(np.floor(np.log2(126.0 / np.maximum(mx, 1))), 0, 7).astype(np.int8)
+
+
+def test_key_gains_cancel_in_the_float_shadow(layer256):
+    """2^g on key channel j and 2^-g on query channel j cancel in q.k, so the
+    float model (which has no gains) is still what the integer layer tracks:
+    the cached keys decode at 2^(kq_k - g) / kq_m (closer than without
+    gains), the queries at 2^(e_q + g), the attention output matches a float
+    softmax on them with the unchanged score multiplier, and the layer
+    output keeps its cosine."""
+    g = _calibrated_gains(layer256[4].kc[0, 0, :, :64])
+    assert g.max() >= 1
+    m, h0, h1, dmp, om = _gained_layer(1, gains=g)
+    sh, L = m.shape, m.layers[0]
+    d, nq, nkv = sh.head_dim, sh.n_q, sh.n_kv
+    qkv = dmp["x1"].astype(float) @ FS.wreal(L.wqkv, L.wqkv_m, sh.w_k).T
+    q = qkv[:, :nq * d].reshape(64, nq, d).transpose(1, 0, 2)
+    q = FS.rope(FS.rmsnorm(q, L.q_norm), np.arange(64), sh.rope_base)
+    gq = g[np.arange(nq) * nkv // nq]                                   # [nq, d]
+    q_int = (dmp["q8"] * 2.0 ** dmp["eq"][:, :, None]).transpose(1, 0, 2) * 2.0 ** gq[:, None, :]
+    assert _rel(q_int / 2.0 ** sh.f_n, q) < 0.05
+    k = qkv[:, nq * d:(nq + nkv) * d].reshape(64, nkv, d).transpose(1, 0, 2)
+    k = FS.rope(FS.rmsnorm(k, L.k_norm), np.arange(64), sh.rope_base)
+    kc, vc = om.kc[0, 0, :, :64], om.vc[0, 0, :, :64]
+    k_int = kc.astype(float) * 2.0 ** (L.kq_k - g[:, None, :].astype(float)) / L.kq_m
+    k_plain = layer256[4].kc[0, 0, :, :64].astype(float) * 2.0 ** L.kq_k / L.kq_m
+    assert _rel(k_int / 2.0 ** sh.f_n, k) < 0.8 * _rel(k_plain / 2.0 ** sh.f_n, k)
+    Ms, Ks = O.softmax_mult(L.kq_m, L.kq_k, d, sh.f_n)
+    att = dmp["attn"].reshape(64, nq, d)
+    for hh in range(nq):
+        kv = hh * nkv // nq
+        s = dmp["q8"][:, hh].astype(float) @ kc[kv].astype(float).T
+        x = s * 2.0 ** dmp["eq"][:, hh][:, None] * Ms * 2.0 ** -Ks / 2.0 ** 15
+        x = np.where(np.tril(np.ones((64, 64), bool)), x, -np.inf)
+        p = 2.0 ** (x - x.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        assert _rel(att[:, hh], p @ vc[kv].astype(float) * 2 ** 15) < 0.04
+    f0 = h0 / 2.0 ** sh.f_res
+    d_flt = FS.layer(sh, L, f0, np.arange(64)) - f0
+    d_int = (h1 - h0) / 2.0 ** sh.f_res
+    assert _cos(d_int, d_flt) > 0.99 and _rel(d_int, d_flt) < 0.12
+
+
+def test_key_gains_recover_levels_of_narrow_channels():
+    """The pages' case: key channels whose range is far below the widest one
+    get few int8 levels at one scale. Half the key-norm gains 64x smaller:
+    without gains those channels' cached keys carry a large relative error;
+    with g = 5 on them it falls several-fold."""
+    kn = S.make_model("layer256", seed=1).layers[0].k_norm.copy()
+    kn[::2] = np.maximum(kn[::2] // 64, 1)
+    g = np.zeros((2, 64), np.int8)
+    g[:, ::2] = 5
+    errs = []
+    for gains in (None, g):
+        m, _, _, dmp, om = _gained_layer(1, gains=gains, k_norm=kn)
+        sh, L = m.shape, m.layers[0]
+        d, nq, nkv = sh.head_dim, sh.n_q, sh.n_kv
+        qkv = dmp["x1"].astype(float) @ FS.wreal(L.wqkv, L.wqkv_m, sh.w_k).T
+        k = qkv[:, nq * d:(nq + nkv) * d].reshape(64, nkv, d).transpose(1, 0, 2)
+        k = FS.rope(FS.rmsnorm(k, L.k_norm), np.arange(64), sh.rope_base)
+        gg = np.zeros((2, 64)) if gains is None else gains.astype(float)
+        k_int = om.kc[0, 0, :, :64].astype(float) * 2.0 ** (L.kq_k - gg[:, None, :]) / L.kq_m
+        errs.append(_rel(k_int[..., ::2] / 2.0 ** sh.f_n, k[..., ::2]))
+    assert errs[0] > 0.3 and errs[1] < errs[0] / 4, errs
