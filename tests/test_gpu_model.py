@@ -79,14 +79,14 @@ def test_tiny_key_gains_match_oracle(D, name, use_graph):
     np.testing.assert_array_equal(host(dm.kc), om.kc)
 
 
-def test_tiny_key_gains_batch32_match_oracle(D):
-    """32 decode rows: the fused attention takes every query head of a KV
+def test_tiny_key_gains_batch64_match_oracle(D):
+    """64 decode rows: the fused attention takes every query head of a KV
     head per workgroup."""
     m = S.with_key_gains(S.make_model("tiny", seed=25), seed=26, gmax=2)
-    prompts = [S.make_prompt(1000, 3 + (i * 7) % 20, 30 + i) for i in range(32)]
+    prompts = [S.make_prompt(1000, 3 + (i * 7) % 20, 30 + i) for i in range(64)]
     rows = []
-    O.OracleModel(m, slots=32).generate(prompts, 4, on_step=lambda s, lg: rows.append(lg.copy()))
-    dm = D.DetintModel(m, n_slots=32)
+    O.OracleModel(m, slots=64).generate(prompts, 4, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=64)
     np.testing.assert_array_equal(host(dm.generate(prompts, 4, use_graph=True)), np.stack(rows))
 
 
@@ -259,7 +259,7 @@ def test_llama_limbs_batch24_split_k_rows_match(D, llama):
 def test_decode_attention_long_context_matches_prefill(D, nq, nkv, d, qkn):
     """Decode rows whose context runs past the cached rows the fused decode
     attention loads up front (512-768), so its double-buffered streaming
-    loops run, in its launch shapes: 32 rows (a workgroup per KV head; 512
+    loops run, in its launch shapes: 64 rows (a workgroup per KV head; 512
     threads for four 64-wide heads) and one row (a workgroup per query head).
     Each decode step's logits must equal the last-position logits of
     prefilling the prompt plus the decoded token in one call (the MFMA
@@ -268,7 +268,7 @@ def test_decode_attention_long_context_matches_prefill(D, nq, nkv, d, qkn):
     shape = S.ModelShape("long_ctx", 1, 256, nq, nkv, d, 512, 1000, qkn, False,
                          1_000_000, 2048, 22)
     m = S.make_model(shape, seed=5)
-    V, B = shape.vocab, 32
+    V, B = shape.vocab, 64
     prompts = S.make_prompts(V, B, 900, 1700, 31)
     dm = D.DetintModel(m, n_slots=B)
     first = torch.zeros((B, V), dtype=torch.int32, device="cuda")
@@ -285,8 +285,8 @@ def test_decode_attention_long_context_matches_prefill(D, nq, nkv, d, qkn):
         dm1.prefill([np.append(prompts[r], toks[r]).astype(np.int32)], [0], [0], ref, 0)
         return host(ref)[0]
 
-    for r in (0, 13, 31):
-        np.testing.assert_array_equal(got[r], reference(r), err_msg=f"batch-32 row {r}")
+    for r in (0, 13, 63):
+        np.testing.assert_array_equal(got[r], reference(r), err_msg=f"batch-64 row {r}")
     # one row alone
     r = 7
     dm1 = D.DetintModel(m, n_slots=1)
