@@ -989,15 +989,17 @@ hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* s
 // query head): a small batch has few workgroups' worth of work and is
 // latency-bound, so halving or quartering each workgroup's arithmetic
 // matters more than reading the cache rows once (batch 8 with 8 KV heads:
-// 4.7% faster decode steps with a workgroup per query head).
+// 4.7% faster decode steps with a workgroup per query head). A single
+// 128-wide head takes 512 threads: its passes are latency chains, and twice
+// the waves halve each one (batch 1: 4.9% faster steps, batch 8: 2.8%).
 template <int D, int G>
 hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
                           const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
                           hipStream_t st) {
   if (G > 1 && B * nkv < 128)
-    return launch_fused_g<D, 1, 256>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc,
-                                     M, K, out, st);
+    return launch_fused_g<D, 1, D == 128 ? 512 : 256>(qkv, p, start_pos, slot, B, nq, nkv, n_slots,
+                                                      max_pos, kc, vc, M, K, out, st);
   // four heads per workgroup with 64-wide heads: the passes are
   // VALU-bound, so two waves per SIMD instead of one
   constexpr int NT = D == 64 && G == 4 ? 512 : 256;
