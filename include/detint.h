@@ -318,8 +318,9 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  *   - top-p alone: each 2048-id slice offers its top min(2048, 16384 /
  *     ceil(V / 2048)) ids; a row whose nucleus reaches below what a slice
  *     offered is redone by the one-workgroup kernel in the same call.
- *   Other calls, or ws = NULL, take one workgroup per row. Same tokens
- *   either way. */
+ *   Other calls, ws = NULL, or ws_bytes below the size above, take one
+ *   workgroup per row. Same tokens either way. Calls that may run at the
+ *   same time (other streams) need workspaces of their own. */
 int64_t detint_sample_workspace(int64_t R, int64_t V);
 detint_status detint_sample(const int32_t *logits, int64_t R, int64_t V, int64_t top_k,
                             int32_t top_p, int32_t t_m, int32_t t_k, const uint32_t *draws,
