@@ -90,6 +90,22 @@ def test_tiny_key_gains_batch64_match_oracle(D):
     np.testing.assert_array_equal(host(dm.generate(prompts, 4, use_graph=True)), np.stack(rows))
 
 
+@pytest.mark.parametrize("nq,nkv,d,qkn,B", [(8, 2, 64, False, 64), (4, 2, 128, True, 3)])
+def test_key_gains_512_thread_decode_match_oracle(D, nq, nkv, d, qkn, B):
+    """Key gains through the 512-thread decode workgroups: four 64-wide
+    query heads per KV head (64 rows), and one 128-wide query head (3 rows)."""
+    shape = S.ModelShape("gains_%d_%d" % (d, B), 1, 256, nq, nkv, d, 512, 1000, qkn, False,
+                         1_000_000, 256, 22)
+    m = S.with_key_gains(S.make_model(shape, seed=27), seed=28, gmax=2)
+    prompts = [S.make_prompt(1000, 5 + (i * 11) % 40, 60 + i) for i in range(B)]
+    rows = []
+    om = O.OracleModel(m, slots=B)
+    om.generate(prompts, 4, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=B)
+    np.testing.assert_array_equal(host(dm.generate(prompts, 4, use_graph=True)), np.stack(rows))
+    np.testing.assert_array_equal(host(dm.kc), om.kc)
+
+
 # ----------------------------------------------------- Qwen3-0.6B shape
 
 @pytest.fixture(scope="module")
