@@ -22,6 +22,7 @@ logits are hashed and compared with the oracle-written golden chains
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
 import os
@@ -387,6 +388,18 @@ def main():
     tps8 = 8 * K / wall8
     del hist8, h8
 
+    # ---- decode, batch 1, with per-channel key gains on every layer (the
+    # same weights, seeded gains in [0, 2]): the cost of the rescale path ----
+    log("decode b1 with key gains")
+    mg = copy.copy(m)
+    mg.layers = [copy.copy(L) for L in m.layers]
+    S.with_key_gains(mg, seed=gold["model_seed"] + 1, gmax=2)
+    dmg = D.DetintModel(mg, n_slots=1)
+    _, wallg, _ = decode_run(D, dmg, [p0], W, K, torch)
+    tps_gain = K / wallg
+    del dmg, mg
+    torch.cuda.empty_cache()
+
     # ---- prefill: the batch-8 ragged prompts in one call, and the 64-token prompt ----
     log("prefill")
     scratch = torch.empty((8, sh.vocab), dtype=torch.int32, device="cuda")
@@ -444,6 +457,7 @@ def main():
         "bit_exact": {"decode_b1_vs_oracle_chain": bool(exact_b1),
                       "decode_b8_vs_oracle_chain": bool(exact_b8),
                       "b1_logits_hash": chain1[-1][:12]},
+        "decode_b1_key_gains_tok_s": round(tps_gain, 2),
         "decode_b8_tok_s": round(tps8, 1),
         "prefill_tok_s": {"ragged_8_prompts_%d_tokens" % ntok: round(ntok / t_rag, 1),
                           "prompt_64": round(PROMPT_LEN / t_64, 1)},

@@ -316,6 +316,12 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     }
   }
   const int32_t rm = QKN ? p.row_m[r] : 0, rk = QKN ? p.row_k[r] : 0;
+  // per-channel key gains of this KV head (2^-g on the query, 2^g on the key)
+  int gk0 = 0, gk1 = 0;
+  if (p.k_gain) {
+    gk0 = p.k_gain[(size_t)kvh * D + jl] & 7;
+    gk1 = p.k_gain[(size_t)kvh * D + jl + half] & 7;
+  }
   asm volatile("" ::: "memory");  // keep these loads ahead of the ones below
   const int pos = start_pos[r], slot = slot_arr[r];
   int32_t* orow = out + ((size_t)r * nq + h0) * D;
@@ -413,9 +419,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     }
     int64_t y0 = act ? R(x0 * cs - x1 * sn, 14) : 0;
     int64_t y1 = act ? R(x1 * cs + x0 * sn, 14) : 0;
-    // per-channel key gains: 2^-g on the query, 2^g on the key
-    const int g0 = p.k_gain && act ? p.k_gain[(size_t)kvh * D + j0] & 7 : 0;
-    const int g1 = p.k_gain && act ? p.k_gain[(size_t)kvh * D + j1] & 7 : 0;
+    const int g0 = act ? gk0 : 0, g1 = act ? gk1 : 0;
     if (t < G) {
       y0 = R(y0, g0);
       y1 = R(y1, g1);
