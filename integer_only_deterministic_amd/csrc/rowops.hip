@@ -1206,6 +1206,33 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
   return before + inc;
 }
 
+// The same in 32 bits (half the lane exchanges), for sums below 2^31.
+__device__ __forceinline__ int32_t wave_incl_scan32(int32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+template <int NT>
+__device__ __forceinline__ int32_t block_incl_scan32(int32_t v, int32_t* wt, int32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t inc = wave_incl_scan32(v, lane);
+  __syncthreads();  // wt free from its previous use
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wave ? wt[w] : 0;
+    tot += wt[w];
+  }
+  total = tot;
+  return before + inc;
+}
+
 // Radix select over the valid keys held by the workgroup, key e weighing
 // wv(e) (all 1: the n-th largest key), on digits of key - (smallest key) taken 8
 // bits a pass from the top of that span (so the first pass already spreads
@@ -1216,7 +1243,7 @@ __device__ __forceinline__ int64_t block_incl_scan(int64_t v, int64_t* wt, int64
 template <int NT, int N, typename WF>
 __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm, WF wv, int n,
                                           int32_t (*hw)[256],
-                                          int64_t* wt, int64_t* red, int* sel, uint32_t& T,
+                                          int32_t* wt, int64_t* red, int* sel, uint32_t& T,
                                           int& tneed) {
   uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
 #pragma unroll
@@ -1243,15 +1270,15 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm
     }
     __syncthreads();
     // bins from the top down: thread i holds bin 255 - i
-    int64_t c = 0;
+    int32_t c = 0;  // at most the total weight, below 2^31
     if (threadIdx.x < 256)
 #pragma unroll
       for (int w = 0; w < NT / 64; ++w) c += hw[w][255 - threadIdx.x];
-    int64_t tot;
-    const int64_t inc = block_incl_scan<NT>(c, wt, tot);
+    int32_t tot;
+    const int32_t inc = block_incl_scan32<NT>(c, wt, tot);
     if (inc - c < rem && rem <= inc) {
       sel[0] = 255 - (int)threadIdx.x;
-      sel[1] = rem - (int)(inc - c);
+      sel[1] = rem - (inc - c);
     }
     __syncthreads();
     prefix |= (uint32_t)sel[0] << lo;
@@ -1266,12 +1293,12 @@ __device__ __forceinline__ void radix_nth(const uint32_t (&key)[N], uint32_t okm
 // first tneed such keys in thread-major order (which is id order).
 template <int NT, int N>
 __device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[N], uint32_t okm, uint32_t T,
-                                             int tneed, int64_t* wt) {
+                                             int tneed, int32_t* wt) {
   int ties = 0;
 #pragma unroll
   for (int e = 0; e < N; ++e) ties += (okm >> e & 1) && key[e] == T;
-  int64_t tt;
-  int tb = (int)(block_incl_scan<NT>(ties, wt, tt) - ties);
+  int32_t tt;
+  int tb = block_incl_scan32<NT>(ties, wt, tt) - ties;
   uint32_t tm = 0;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
@@ -1286,7 +1313,8 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
                                                     int kc, uint64_t* __restrict__ cand,
                                                     uint32_t* __restrict__ sT) {
   __shared__ int32_t hw[TKT / 64][256];
-  __shared__ int64_t wt[TKT / 64], red[16];
+  __shared__ int32_t wt[TKT / 64];
+  __shared__ int64_t red[16];
   __shared__ int sel[2];
   const int r = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
   const int32_t* l = logits + (size_t)r * V;
@@ -1303,8 +1331,8 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
   radix_nth<TKT, TKN>(key, okm, [](int) { return 1; }, kk, hw, wt, red, sel, T, tneed);
   const uint32_t take = take_top<TKT, TKN>(key, okm, T, tneed, wt);
   const int nt = __popc(take);
-  int64_t tot;
-  int at = (int)(block_incl_scan<TKT>(nt, wt, tot) - nt);
+  int32_t tot;
+  int at = block_incl_scan32<TKT>(nt, wt, tot) - nt;
   uint64_t* dst = cand + (size_t)r * TKC + (size_t)p * kc;
 #pragma unroll
   for (int e = 0; e < TKN; ++e)
@@ -1332,7 +1360,8 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
   constexpr int N = NUC ? TKC / TPT : TKK / TPT;  // candidates a thread
   __shared__ int32_t hw[TPT / 64][256];
   __shared__ int32_t wl[N][TPT];  // candidate weights, element-major
-  __shared__ int64_t wt[TPT / 64], red[16];
+  __shared__ int32_t wt[TPT / 64];
+  __shared__ int64_t wt64[TPT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.x, tid = threadIdx.x;
   const uint64_t* c = cand + (size_t)r * TKC + N * tid;  // this thread's entries
@@ -1358,26 +1387,26 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     radix_nth<TPT, N>(key, okm, [](int) { return 1; }, keep, hw, wt, red, sel, T, tneed);
     take = take_top<TPT, N>(key, okm, T, tneed, wt);
   }
-  auto weight_of = [&](uint32_t m) {
-    int64_t s = 0;
+  auto weight_of = [&](uint32_t m) {  // candidate weights total below 2^30
+    int32_t s = 0;
 #pragma unroll
     for (int e = 0; e < N; ++e) s += m >> e & 1 ? wgt(e) : 0;
     return s;
   };
-  int64_t mine = weight_of(take);
+  int32_t mine = weight_of(take);
   if (NUC || top_p < 65536) {
     // the shortest prefix of the ranking whose weight reaches
     // ceil(top_p D / 2^16), D the weight of the kept ids (of the whole row
     // for NUC): a weighted select over the candidates (their weight is below
     // 2^30), then ceil(rest / weight of that key) of its ties, lowest ids first
-    int64_t Wc, Dk;
-    block_incl_scan<TPT>(mine, wt, Wc);
-    Dk = Wc;
+    int32_t Wc;
+    block_incl_scan32<TPT>(mine, wt, Wc);
+    int64_t Dk = Wc;
     uint32_t tc = 0;
     if constexpr (NUC) {
       int64_t ds = 0;
       for (int i = tid; i < 4 * P; i += TPT) ds += ssum[(size_t)r * P * 4 + i];
-      block_incl_scan<TPT>(ds, wt, Dk);
+      block_incl_scan<TPT>(ds, wt64, Dk);
       for (int i = tid; i < P2; i += TPT) tc = max(tc, sT[(size_t)r * P2 + i]);
       tc = (uint32_t)block_max((int64_t)tc, red);
     }
@@ -1398,13 +1427,13 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     mine = weight_of(take);
     if (NUC && tid == 0) done[r] = 1;
   }
-  int64_t D;
-  int64_t run = block_incl_scan<TPT>(mine, wt, D) - mine;  // weight of earlier ids
-  const int64_t t = (int64_t)(((unsigned __int128)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
+  int32_t D;
+  int32_t run = block_incl_scan32<TPT>(mine, wt, D) - mine;  // weight of earlier ids
+  const int32_t t = (int32_t)(((uint64_t)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
   if (run <= t && t < run + mine) {
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-      const int64_t w = take >> e & 1 ? wgt(e) : 0;
+      const int32_t w = take >> e & 1 ? wgt(e) : 0;
       if (run + w > t) {
         out[r] = (int32_t)~(uint32_t)c[e];  // reload the entry for its id
         break;
