@@ -338,8 +338,9 @@ def main():
     ap.add_argument("--llama-steps", type=int, default=2047)
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py: this build runs on one GPU only (the integer forward pass is "
-            "data-parallel by sequence; see DESIGN.md for how it would shard). Use --gpus 1.")
+        log("bench.py: runs on one GPU only (the integer forward pass is data-parallel by "
+            "sequence: more GPUs would each hold the weights and their own KV-cache slots, "
+            "with no collective in the step). Use --gpus 1.")
         sys.exit(2)
     if args.warmup + args.steps > 511:
         log("bench.py: warmup + steps must be <= 511 (64-token prompt + 512 steps fit the cache)")
