@@ -106,6 +106,36 @@ def test_key_gains_512_thread_decode_match_oracle(D, nq, nkv, d, qkn, B):
     np.testing.assert_array_equal(host(dm.kc), om.kc)
 
 
+def test_tiny_preemption_recompute_matches_uninterrupted(D):
+    """Row 1 loses its cache after k decode steps and is rebuilt by one
+    prefill of its prompt plus the tokens it produced, in another slot; both
+    rows then decode on (graph replays). Every logits row equals the
+    uninterrupted run's and the oracle's."""
+    import torch
+    m = S.make_model("tiny", seed=31)
+    V = m.shape.vocab
+    p = [S.make_prompt(V, 20, 41), S.make_prompt(V, 13, 42)]
+    n, k = 9, 4
+    rows = []
+    O.OracleModel(m, slots=3).generate(p, n, on_step=lambda s, lg: rows.append(lg.copy()))
+    want = np.stack(rows)
+    ref = host(D.DetintModel(m, n_slots=3).generate(p, n))
+    np.testing.assert_array_equal(ref, want)
+    dm = D.DetintModel(m, n_slots=3)
+    h1 = torch.zeros((k, 2, V), dtype=torch.int32, device="cuda")
+    tok = dm.prefill(p, [0, 0], [0, 1], h1, 0)
+    dm.decode(tok, [20, 13], [0, 1], k - 1, h1, 2, use_graph=True)
+    a = host(h1)
+    gen1 = a[:k - 1, 1].argmax(-1).astype(np.int32)
+    re = torch.zeros((1, V), dtype=torch.int32, device="cuda")
+    t1 = dm.prefill([np.concatenate([p[1], gen1])], [0], [2], re, 0)
+    np.testing.assert_array_equal(host(re)[0], a[k - 1, 1])
+    tok2 = torch.stack([tok[0], t1[0]]).contiguous()
+    h2 = torch.zeros((n - k, 2, V), dtype=torch.int32, device="cuda")
+    dm.decode(tok2, [20 + k - 1, 13 + k - 1], [0, 2], n - k, h2, 0, use_graph=True)
+    np.testing.assert_array_equal(np.concatenate([a, host(h2)]), want)
+
+
 # ----------------------------------------------------- Qwen3-0.6B shape
 
 @pytest.fixture(scope="module")

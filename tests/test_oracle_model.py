@@ -256,3 +256,37 @@ def test_key_gains_recover_levels_of_narrow_channels():
         k_int = om.kc[0, 0, :, :64].astype(float) * 2.0 ** (L.kq_k - gg[:, None, :]) / L.kq_m
         errs.append(_rel(k_int[..., ::2] / 2.0 ** sh.f_n, k[..., ::2]))
     assert errs[0] > 0.3 and errs[1] < errs[0] / 4, errs
+
+
+# ------------------------------------- preemption by recompute (BitExact page)
+
+def test_preempted_sequence_recomputed_in_another_slot_is_invariant():
+    """A sequence whose cache is dropped mid-decode and rebuilt by prefilling
+    its prompt plus the tokens it had produced, into another slot, continues
+    with the same logits as if it had never been preempted; its neighbour in
+    the batch is unaffected."""
+    m = S.make_model("tiny", seed=31)
+    p = [S.make_prompt(1000, 20, 41), S.make_prompt(1000, 13, 42)]
+    n, k = 9, 4
+    ref = []
+    O.OracleModel(m, slots=3).generate(p, n, on_step=lambda s, lg: ref.append(lg.copy()))
+    ref = np.stack(ref)                                        # [n, 2, V]
+    om = O.OracleModel(m, slots=3)
+    lg, tok = om.forward(np.concatenate(p), [20, 13], [0, 0], [0, 1])
+    got, gen1 = [lg], []
+    pos = [20, 13]
+    for _ in range(k - 1):                                     # steps 1 .. k-1 in slots 0, 1
+        gen1.append(int(tok[1]))
+        lg, tok = om.forward(tok.astype(np.int32), [1, 1], pos, [0, 1])
+        got.append(lg)
+        pos = [pos[0] + 1, pos[1] + 1]
+    # row 1 preempted: its cache is gone; recompute prompt + generated tokens in slot 2
+    re_ids = np.concatenate([p[1], np.array(gen1, np.int32)])
+    lg1, t1 = om.forward(re_ids, [len(re_ids)], [0], [2])
+    np.testing.assert_array_equal(lg1[0], got[-1][1])
+    tok = np.array([tok[0], t1[0]], np.int32)
+    for _ in range(n - k):
+        lg, tok = om.forward(tok, [1, 1], pos, [0, 2])
+        got.append(lg)
+        pos = [pos[0] + 1, pos[1] + 1]
+    np.testing.assert_array_equal(np.stack(got), ref)
