@@ -136,6 +136,31 @@ def test_tiny_preemption_recompute_matches_uninterrupted(D):
     np.testing.assert_array_equal(np.concatenate([a, host(h2)]), want)
 
 
+def test_tiny_shared_prefix_copied_cache_matches_full_prefill(D):
+    """The second of two sequences that share a 24-token prefix takes the
+    first's cached prefix rows (device copy into its slot) and prefills only
+    its suffix from position 24; its logits and both rows' decode steps
+    (graph replays) equal the oracle's run that prefilled both in full."""
+    import torch
+    m = S.make_model("tiny", seed=32)
+    V = m.shape.vocab
+    pre = S.make_prompt(V, 24, 43)
+    a = np.concatenate([pre, S.make_prompt(V, 9, 44)])
+    b = np.concatenate([pre, S.make_prompt(V, 6, 45)])
+    n = 6
+    rows = []
+    O.OracleModel(m, slots=2).generate([a, b], n, on_step=lambda s, lg: rows.append(lg.copy()))
+    dm = D.DetintModel(m, n_slots=2)
+    h = torch.zeros((n, 2, V), dtype=torch.int32, device="cuda")
+    ta = dm.prefill([a], [0], [0], h, 0)
+    dm.kc[:, 1, :, :24] = dm.kc[:, 0, :, :24]
+    dm.vc[:, 1, :, :24] = dm.vc[:, 0, :, :24]
+    tb = dm.prefill([b[24:]], [24], [1], h, 1)
+    tok = torch.stack([ta[0], tb[0]]).contiguous()
+    dm.decode(tok, [len(a), len(b)], [0, 1], n - 1, h, 2, use_graph=True)
+    np.testing.assert_array_equal(host(h), np.stack(rows))
+
+
 # ----------------------------------------------------- Qwen3-0.6B shape
 
 @pytest.fixture(scope="module")

@@ -290,3 +290,29 @@ def test_preempted_sequence_recomputed_in_another_slot_is_invariant():
         got.append(lg)
         pos = [pos[0] + 1, pos[1] + 1]
     np.testing.assert_array_equal(np.stack(got), ref)
+
+
+def test_shared_prefix_copied_cache_is_invariant():
+    """Two sequences share a 24-token prefix: the second reuses the first's
+    cached prefix rows (copied into its slot) and prefills only its own
+    suffix from position 24. Its logits, then both rows' decode steps, equal
+    a run that prefilled both sequences in full."""
+    m = S.make_model("tiny", seed=32)
+    pre = S.make_prompt(1000, 24, 43)
+    a = np.concatenate([pre, S.make_prompt(1000, 9, 44)])
+    b = np.concatenate([pre, S.make_prompt(1000, 6, 45)])
+    n = 6
+    ref = []
+    O.OracleModel(m, slots=2).generate([a, b], n, on_step=lambda s, lg: ref.append(lg.copy()))
+    om = O.OracleModel(m, slots=2)
+    la, ta = om.forward(a, [len(a)], [0], [0])
+    om.kc[:, 1, :, :24] = om.kc[:, 0, :, :24]
+    om.vc[:, 1, :, :24] = om.vc[:, 0, :, :24]
+    lb, tb = om.forward(b[24:], [len(b) - 24], [24], [1])
+    got = [np.stack([la[0], lb[0]])]
+    tok, pos = np.array([ta[0], tb[0]], np.int32), [len(a), len(b)]
+    for _ in range(n - 1):
+        lg, tok = om.forward(tok, [1, 1], pos, [0, 1])
+        got.append(lg)
+        pos = [pos[0] + 1, pos[1] + 1]
+    np.testing.assert_array_equal(np.stack(got), np.stack(ref))
