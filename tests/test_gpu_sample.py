@@ -90,3 +90,20 @@ def test_sample_many_draws_one_row(D):
         want = O.sample(logits, k, T1[0], T1[1], draws, top_p=p)
         np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p), want)
         np.testing.assert_array_equal(_run(D, logits, k, T1, draws, top_p=p, ws=True), want)
+
+
+@pytest.mark.parametrize("V", [2048, 2049, 262144])
+def test_sample_slice_edges_and_largest_vocabulary(D, V):
+    """Exactly one 2048-id slice, one id past it, and the largest accepted
+    vocabulary (128 slices of 2048, 256 of 1024): every path, with and
+    without a workspace, token for token."""
+    rng = np.random.default_rng(V)
+    R = 4
+    logits = _logits("spread", R, V, rng)
+    draws = rng.integers(0, 1 << 32, R, dtype=np.uint64).astype(np.uint32)
+    draws[:2] = [0, (1 << 32) - 1]
+    for k, p in ((0, 65536), (1, 65536), (64, 65536), (0, 58982), (64, 58982)):
+        want = O.sample(logits, k, T1[0], T1[1], draws, top_p=p)
+        for ws in (False, True):
+            got = _run(D, logits, k, T1, draws, top_p=p, ws=ws)
+            np.testing.assert_array_equal(got, want, err_msg=f"V={V} k={k} p={p} ws={ws}")
