@@ -1349,19 +1349,19 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
 // kept: then the candidates hold every id at or above that key, so the
 // nucleus, its ties and the draw are the whole row's. done[r] says whether
 // it stood; sample_k, launched after, redoes the rows where it did not.
-template <bool NUC>
-__global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
+template <bool NUC, int PT>
+__global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
                                                    int keep, int32_t top_p, int32_t t_m, int32_t t_k,
                                                    const uint32_t* __restrict__ draws,
                                                    int32_t* __restrict__ out,
                                                    const int32_t* __restrict__ ssum, int P,
                                                    const uint32_t* __restrict__ sT, int P2,
                                                    int32_t* __restrict__ done) {
-  constexpr int N = NUC ? TKC / TPT : TKK / TPT;  // candidates a thread
-  __shared__ int32_t hw[TPT / 64][256];
-  __shared__ int32_t wl[N][TPT];  // candidate weights, element-major
-  __shared__ int32_t wt[TPT / 64];
-  __shared__ int64_t wt64[TPT / 64], red[16];
+  constexpr int N = NUC ? TKC / PT : TKK / TPT;  // candidates a thread
+  __shared__ int32_t hw[PT / 64][256];
+  __shared__ int32_t wl[N][PT];  // candidate weights, element-major
+  __shared__ int32_t wt[PT / 64];
+  __shared__ int64_t wt64[PT / 64], red[16];
   __shared__ int sel[2];
   const int r = blockIdx.x, tid = threadIdx.x;
   const uint64_t* c = cand + (size_t)r * TKC + N * tid;  // this thread's entries
@@ -1384,8 +1384,8 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
   if constexpr (!NUC) {
     uint32_t T;
     int tneed;
-    radix_nth<TPT, N>(key, okm, [](int) { return 1; }, keep, hw, wt, red, sel, T, tneed);
-    take = take_top<TPT, N>(key, okm, T, tneed, wt);
+    radix_nth<PT, N>(key, okm, [](int) { return 1; }, keep, hw, wt, red, sel, T, tneed);
+    take = take_top<PT, N>(key, okm, T, tneed, wt);
   }
   auto weight_of = [&](uint32_t m) {  // candidate weights total below 2^30
     int32_t s = 0;
@@ -1400,14 +1400,14 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     // for NUC): a weighted select over the candidates (their weight is below
     // 2^30), then ceil(rest / weight of that key) of its ties, lowest ids first
     int32_t Wc;
-    block_incl_scan32<TPT>(mine, wt, Wc);
+    block_incl_scan32<PT>(mine, wt, Wc);
     int64_t Dk = Wc;
     uint32_t tc = 0;
     if constexpr (NUC) {
       int64_t ds = 0;
-      for (int i = tid; i < 4 * P; i += TPT) ds += ssum[(size_t)r * P * 4 + i];
-      block_incl_scan<TPT>(ds, wt64, Dk);
-      for (int i = tid; i < P2; i += TPT) tc = max(tc, sT[(size_t)r * P2 + i]);
+      for (int i = tid; i < 4 * P; i += PT) ds += ssum[(size_t)r * P * 4 + i];
+      block_incl_scan<PT>(ds, wt64, Dk);
+      for (int i = tid; i < P2; i += PT) tc = max(tc, sT[(size_t)r * P2 + i]);
       tc = (uint32_t)block_max((int64_t)tc, red);
     }
     const int64_t need = ((int64_t)top_p * Dk + 65535) >> 16;
@@ -1415,7 +1415,7 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
     int rest = 0;
     bool good = need <= Wc;  // uniform over the workgroup
     if (good) {
-      radix_nth<TPT, N>(key, take, wgt, (int)need, hw, wt, red, sel, Lp, rest);
+      radix_nth<PT, N>(key, take, wgt, (int)need, hw, wt, red, sel, Lp, rest);
       good = !NUC || Lp > tc;
     }
     if (NUC && !good) {
@@ -1423,12 +1423,12 @@ __global__ __launch_bounds__(TPT) void topk_pick_k(const uint64_t* __restrict__ 
       return;
     }
     const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
-    take = take_top<TPT, N>(key, take, Lp, (rest + wp - 1) / wp, wt);
+    take = take_top<PT, N>(key, take, Lp, (rest + wp - 1) / wp, wt);
     mine = weight_of(take);
     if (NUC && tid == 0) done[r] = 1;
   }
   int32_t D;
-  int32_t run = block_incl_scan32<TPT>(mine, wt, D) - mine;  // weight of earlier ids
+  int32_t run = block_incl_scan32<PT>(mine, wt, D) - mine;  // weight of earlier ids
   const int32_t t = (int32_t)(((uint64_t)draws[r] * (uint64_t)D) >> 32);  // in [0, D)
   if (run <= t && t < run + mine) {
 #pragma unroll
@@ -1474,9 +1474,16 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
   if (fits && keep < V && P2 * kc <= TKK) {
     topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kc, cand,
                                                                   nullptr);
-    topk_pick_k<false><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p, t_m,
-                                                    t_k, draws, out, nullptr, 0, nullptr, 0,
-                                                    nullptr);
+    // up to 4096 candidates: 512 threads (the pick is a chain of workgroup
+    // scans and barriers, each cheaper with half the waves)
+    if (P2 * kc <= 4096)
+      topk_pick_k<false, 512><<<(unsigned)R, 512, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p,
+                                                          t_m, t_k, draws, out, nullptr, 0, nullptr,
+                                                          0, nullptr);
+    else
+      topk_pick_k<false, TPT><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kc), (int)keep, top_p,
+                                                          t_m, t_k, draws, out, nullptr, 0, nullptr,
+                                                          0, nullptr);
     return hipGetLastError();
   }
   if (fits && keep >= V) {
@@ -1488,7 +1495,7 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
     sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k,
                                                                   smax, ssum);
     topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kn, cand, sT);
-    topk_pick_k<true><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kn), (int)V, top_p, t_m, t_k,
+    topk_pick_k<true, TPT><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kn), (int)V, top_p, t_m, t_k,
                                                    draws, out, ssum, (int)P, sT, (int)P2, done);
     sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out,
                                           done);
