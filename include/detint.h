@@ -317,7 +317,7 @@ detint_status detint_argmax_parts(const int64_t *part, int64_t S, int64_t nparts
  *     selects its top ids first;
  *   - top-p alone: each 2048-id slice offers its top min(2048, 16384 /
  *     ceil(V / 2048)) ids; a row whose nucleus reaches below what a slice
- *     offered is redone by the one-workgroup kernel in the same call.
+ *     offered is sampled by the one-workgroup algorithm in the same kernel.
  *   Other calls, ws = NULL, or ws_bytes below the size above, take one
  *   workgroup per row. Same tokens either way. Calls that may run at the
  *   same time (other streams) need workspaces of their own. */

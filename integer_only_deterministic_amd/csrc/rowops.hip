@@ -830,12 +830,12 @@ __device__ __forceinline__ int32_t wave_sum32(int32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
-                                               int32_t top_p, int32_t t_m, int32_t t_k,
-                                               const uint32_t* __restrict__ draws,
-                                               int32_t* __restrict__ out,
-                                               const int32_t* __restrict__ done) {
-  if (done && done[blockIdx.x]) return;  // row already sampled
+// One row (blockIdx.x) by one SMT-thread workgroup; also the in-kernel
+// fallback of the sliced top-p pick.
+__device__ __forceinline__ void sample_row(const int32_t* __restrict__ logits, int V, int keep,
+                                           int32_t top_p, int32_t t_m, int32_t t_k,
+                                           const uint32_t* __restrict__ draws,
+                                           int32_t* __restrict__ out) {
   __shared__ int32_t hw[SMW][256];                // per-wave histograms (counts)
   __shared__ unsigned long long hm[SMW][256];     // per-wave histograms (weights, top-p)
   __shared__ int32_t hist[256];
@@ -1060,6 +1060,13 @@ __global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logi
     const int at = crossing_in_step(c, rest, lane);
     if (lane == 0) out[r] = wlo + q * SPS + at;
   }
+}
+
+__global__ __launch_bounds__(SMT) void sample_k(const int32_t* __restrict__ logits, int V, int keep,
+                                               int32_t top_p, int32_t t_m, int32_t t_k,
+                                               const uint32_t* __restrict__ draws,
+                                               int32_t* __restrict__ out) {
+  sample_row(logits, V, keep, top_p, t_m, t_k, draws, out);
 }
 
 // Plain temperature sampling (every id kept) spread over the chip: slices of
@@ -1347,8 +1354,8 @@ __global__ __launch_bounds__(TKT) void topk_slice_k(const int32_t* __restrict__ 
 // of sample_wsum_k), and the result stands only if the nucleus threshold
 // key lies above every cut key sT of a slice that had more ids than it
 // kept: then the candidates hold every id at or above that key, so the
-// nucleus, its ties and the draw are the whole row's. done[r] says whether
-// it stood; sample_k, launched after, redoes the rows where it did not.
+// nucleus, its ties and the draw are the whole row's. Otherwise the
+// workgroup samples the row from its logits as sample_k does.
 template <bool NUC, int PT>
 __global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ cand, int nc,
                                                    int keep, int32_t top_p, int32_t t_m, int32_t t_k,
@@ -1356,7 +1363,7 @@ __global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ c
                                                    int32_t* __restrict__ out,
                                                    const int32_t* __restrict__ ssum, int P,
                                                    const uint32_t* __restrict__ sT, int P2,
-                                                   int32_t* __restrict__ done) {
+                                                   const int32_t* __restrict__ logits) {
   constexpr int N = NUC ? TKC / PT : TKK / TPT;  // candidates a thread
   __shared__ int32_t hw[PT / 64][256];
   __shared__ int32_t wl[N][PT];  // candidate weights, element-major
@@ -1418,14 +1425,15 @@ __global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ c
       radix_nth<PT, N>(key, take, wgt, (int)need, hw, wt, red, sel, Lp, rest);
       good = !NUC || Lp > tc;
     }
-    if (NUC && !good) {
-      if (tid == 0) done[r] = 0;
-      return;
+    if constexpr (NUC) {
+      if (!good) {  // uniform: the whole row, one workgroup
+        sample_row(logits, keep, keep, top_p, t_m, t_k, draws, out);
+        return;
+      }
     }
     const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
     take = take_top<PT, N>(key, take, Lp, (rest + wp - 1) / wp, wt);
     mine = weight_of(take);
-    if (NUC && tid == 0) done[r] = 1;
   }
   int32_t D;
   int32_t run = block_incl_scan32<PT>(mine, wt, D) - mine;  // weight of earlier ids
@@ -1444,11 +1452,11 @@ __global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ c
 }
 
 // Workspace: candidates [R][TKC] u64 | slice maxima [R][P] | step sums
-// [R][P][4] | slice cut keys [R][P2] | done flags [R]  (P = 1024-id slices,
-// P2 = 2048-id slices); the plain path uses maxima and step sums only.
+// [R][P][4] | slice cut keys [R][P2]  (P = 1024-id slices, P2 = 2048-id
+// slices); the plain path uses maxima and step sums only.
 int64_t sample_workspace_bytes(int64_t R, int64_t V) {
   const int64_t P = (V + SLC - 1) / SLC, P2 = (V + TKS - 1) / TKS;
-  return R * (TKC * 8 + P * 4 * (1 + 4) + P2 * 4 + 4);
+  return R * (TKC * 8 + P * 4 * (1 + 4) + P2 * 4);
 }
 
 hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t keep, int32_t top_p,
@@ -1461,7 +1469,6 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
   int32_t* smax = (int32_t*)(cand + R * TKC);
   int32_t* ssum = smax + R * P;
   uint32_t* sT = (uint32_t*)(ssum + R * P * 4);
-  int32_t* done = (int32_t*)(sT + R * P2);
   if (fits && keep >= V && top_p >= 65536) {
     sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, smax);
     sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k,
@@ -1488,21 +1495,18 @@ hipError_t launch_sample(const int32_t* logits, int64_t R, int64_t V, int64_t ke
   }
   if (fits && keep >= V) {
     // top-p alone: each slice's top kn ids as candidates, the whole row's
-    // weight from the step sums; rows whose nucleus reaches below a slice's
-    // cut go to sample_k
+    // weight from the step sums; a row whose nucleus reaches below a slice's
+    // cut is sampled from its logits by its pick workgroup
     const int64_t kn = std::min<int64_t>(TKS, TKC / P2);
     sample_max_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, smax);
     sample_wsum_k<<<dim3((unsigned)P, (unsigned)R), SLT, 0, st>>>(logits, (int)V, (int)P, t_m, t_k,
                                                                   smax, ssum);
     topk_slice_k<<<dim3((unsigned)P2, (unsigned)R), TKT, 0, st>>>(logits, (int)V, (int)kn, cand, sT);
     topk_pick_k<true, TPT><<<(unsigned)R, TPT, 0, st>>>(cand, (int)(P2 * kn), (int)V, top_p, t_m, t_k,
-                                                   draws, out, ssum, (int)P, sT, (int)P2, done);
-    sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out,
-                                          done);
+                                                   draws, out, ssum, (int)P, sT, (int)P2, logits);
     return hipGetLastError();
   }
-  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out,
-                                        nullptr);
+  sample_k<<<(unsigned)R, SMT, 0, st>>>(logits, (int)V, (int)keep, top_p, t_m, t_k, draws, out);
   return hipGetLastError();
 }
 

@@ -123,8 +123,8 @@ def test_validation_rejects_before_device_work(D):
     assert lib.detint_sample(fake, 1, 100, 0, 65536, *T, fake, fake, C.c_void_p(4097), 64,
                              None) == D.DETINT_EINVAL  # misaligned workspace
     assert lib.detint_sample(None, 0, 100, 0, 65536, *T, None, None, None, 0, None) == D.DETINT_OK
-    # candidates (16384 x 8 B), 149 slice maxima and 596 step sums, 75 cut keys, a flag
-    assert lib.detint_sample_workspace(8, 151936) == 8 * (16384 * 8 + 149 * 20 + 75 * 4 + 4)
+    # candidates (16384 x 8 B), 149 slice maxima and 596 step sums, 75 cut keys
+    assert lib.detint_sample_workspace(8, 151936) == 8 * (16384 * 8 + 149 * 20 + 75 * 4)
     assert lib.detint_sample_workspace(1, 262145) == -1
 
 
