@@ -107,3 +107,35 @@ def test_sample_slice_edges_and_largest_vocabulary(D, V):
         for ws in (False, True):
             got = _run(D, logits, k, T1, draws, top_p=p, ws=ws)
             np.testing.assert_array_equal(got, want, err_msg=f"V={V} k={k} p={p} ws={ws}")
+
+
+def test_sample_graph_replays_match_oracle(D):
+    """detint_sample with a workspace captured once into a HIP graph per
+    path (all ids, top-50, top-50 then top-p, top-p alone), then replayed
+    with new logits and draws copied in eagerly between replays: every
+    replay's tokens equal the oracle's."""
+    import torch
+    V, R = 151936, 4
+    lg = torch.zeros((R, V), dtype=torch.int32, device="cuda")
+    dr = torch.zeros(R, dtype=torch.int32, device="cuda")
+    out = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ws = torch.empty(D.detint_sample_workspace(R, V), dtype=torch.uint8, device="cuda")
+    for k, p in ((0, 65536), (50, 65536), (50, 58982), (0, 58982)):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            D.detint_sample(lg, k, T1[0], T1[1], dr, out, top_p=p, ws=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(3):
+            rng = np.random.default_rng(1000 * k + p + rep)
+            logits = rng.normal(0, 3 * 65536, (R, V)).astype(np.int32)
+            draws = rng.integers(0, 1 << 32, R, dtype=np.uint64).astype(np.uint32)
+            lg.copy_(torch.from_numpy(logits))
+            dr.copy_(torch.from_numpy(draws.view(np.int32)))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(out.cpu().numpy(),
+                                          O.sample(logits, k, T1[0], T1[1], draws, top_p=p),
+                                          err_msg=f"k={k} p={p} replay {rep}")
