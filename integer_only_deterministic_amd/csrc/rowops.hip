@@ -495,6 +495,68 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
            kc, vc, max_pos);
 }
 
+// Without q/k-norm and with 64-wide heads a head needs only 32 lanes (lane i
+// owns the RoPE pair (i, i + 32)), so a wave takes two: the 32-lane half h
+// handles head 2 w + h. The same integer steps as qkv_head without q/k-norm;
+// the query's DQ maximum is reduced over its half only (xor offsets below
+// 32 stay within a half). Every lane takes part in the reduction; a half
+// past the last head stores nothing.
+__global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict__ qkv, int nq,
+                                                       int nkv, const int32_t* __restrict__ pos_of,
+                                                       const int32_t* __restrict__ slot_of,
+                                                       QkvPost p, int8_t* __restrict__ q8,
+                                                       int32_t* __restrict__ e_q,
+                                                       int8_t* __restrict__ kc,
+                                                       int8_t* __restrict__ vc, int n_slots,
+                                                       int max_pos) {
+  constexpr int d = 64, half = 32;
+  const int r = blockIdx.x, li = threadIdx.x & 31;
+  const int nh = nq + 2 * nkv;
+  const int hh = (blockIdx.y * (TPB / 64) + (threadIdx.x >> 6)) * 2 + ((threadIdx.x >> 5) & 1);
+  const bool live = hh < nh;
+  const int hc = live ? hh : nh - 1;
+  const bool isq = hc < nq, isv = hc >= nq + nkv;
+  const int pos = pos_of[r], slot = slot_of[r];
+  const bool ok = pos >= 0 && pos < max_pos && slot >= 0 && slot < n_slots;
+  const int32_t* row = qkv + (size_t)r * nh * d + (size_t)hc * d;
+  const int j0 = li, j1 = li + half;
+  const int64_t x0 = row[j0], x1 = row[j1];  // f_n fixed point from the GEMM epilogue
+  if (isv && live && ok) {
+    int8_t* dst = vc + (((size_t)slot * nkv + (hc - nq - nkv)) * max_pos + pos) * d;
+    dst[j0] = clamp8(R(x0 * p.vq_m, p.vq_k));
+    dst[j1] = clamp8(R(x1 * p.vq_m, p.vq_k));
+  }
+  const int pc = ok ? pos : 0;
+  const int64_t c = p.cos_t[(size_t)pc * half + li], sn = p.sin_t[(size_t)pc * half + li];
+  int64_t y0 = ok ? R(x0 * c - x1 * sn, 14) : 0;
+  int64_t y1 = ok ? R(x1 * c + x0 * sn, 14) : 0;
+  const int kvh = isq ? hc / (nq / nkv) : (isv ? 0 : hc - nq);
+  const int g0 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j0] & 7 : 0;
+  const int g1 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j1] & 7 : 0;
+  if (isq) {  // the inverse of the key gain
+    y0 = R(y0, g0);
+    y1 = R(y1, g1);
+  }
+  uint64_t u = uabs64(y0) > uabs64(y1) ? uabs64(y0) : uabs64(y1);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) {
+    const uint64_t w = (uint64_t)__shfl_xor((long long)u, o);
+    u = w > u ? w : u;
+  }
+  if (!live || isv) return;
+  if (isq) {
+    const int e = dq_exp(u);
+    int8_t* qd = q8 + ((size_t)r * nq + hc) * d;
+    qd[j0] = clamp8(R(y0, e));
+    qd[j1] = clamp8(R(y1, e));
+    if (li == 0) e_q[(size_t)r * nq + hc] = e;
+  } else if (ok) {
+    int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+    dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
+    dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
+  }
+}
+
 // Greedy argmax with the lowest index among maxima (DetLLM blog "DetLLM").
 // Key = value << 32 | (2^32 - 1 - index): the largest key is the largest
 // value at the smallest index, and max is order-free.
@@ -716,6 +778,13 @@ hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nk
                            int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
                            int64_t max_pos, hipStream_t st) {
   if (R == 0) return hipSuccess;
+  if (!p.qk_norm && d == 64) {  // two heads per wave
+    const unsigned hp = (unsigned)((nq + 2 * nkv + 2 * (TPB / 64) - 1) / (2 * (TPB / 64)));
+    qkv_post_pair_k<<<dim3((unsigned)R, hp), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, pos_of, slot_of,
+                                                           p, q8, e_q, kc, vc, (int)n_slots,
+                                                           (int)max_pos);
+    return hipGetLastError();
+  }
   const unsigned hb = (unsigned)((nq + 2 * nkv + 3) / 4);  // 4 heads (waves) per workgroup
   qkv_post_k<<<dim3((unsigned)R, hb), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, (int)d, pos_of, slot_of,
                                                      p, q8, e_q, kc, vc, (int)n_slots, (int)max_pos);
