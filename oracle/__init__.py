@@ -426,6 +426,14 @@ class OracleModel:
         _check()
         return h, d_arrays
 
+    def embed(self, ids):
+        """Residual rows h0 [R, H] of the token ids (orc_embed)."""
+        ids = _c(ids, np.int32)
+        h = np.zeros((ids.size, self.shape.hidden), np.int32)
+        lib().orc_embed(C.byref(self.md), ids, ids.size, h)
+        _check()
+        return h
+
     def forward(self, ids, lens, starts, slots, all_rows: bool = False):
         """ids packed over sequences -> (logits [S or R, V] int32, next tokens)."""
         sh = self.shape

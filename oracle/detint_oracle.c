@@ -730,9 +730,11 @@ int orc_layer_forward(const orc_model *md, int64_t l, int32_t *h, int64_t R_,
   return g_err;
 }
 
-/* Embedding rounded once onto the residual grid ([BITEXACT] "Three execution
- * paths": the input embedding is rounded once to the residual stream's fixed
- * point): h0 = R(E[id] * m_v[id], w_k - f_res). */
+/* Embedding lookup onto the residual stream ([BITEXACT] "Three execution
+ * paths": the embedding enters the integer residual once, by one rounding to
+ * its fixed-point grid). The table entry's real value is E[id] * m_v[id] *
+ * 2^-w_k; in units of 2^-f_res that is E * m_v * 2^(f_res - w_k), rounded
+ * by the one rule: h0 = R(E[id] * m_v[id], w_k - f_res). */
 int orc_embed(const orc_model *md, const int32_t *ids, int64_t R_, int32_t *h) {
   const int64_t H = md->hidden;
   for (int64_t r = 0; r < R_; r++) {
