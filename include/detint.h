@@ -106,8 +106,10 @@ detint_status detint_split_w16(const int16_t *W16, int64_t n, int8_t *W_hi, int8
  * RD(a, b) = floor((2a + b) / 2b); (x8, e) = DQ(h_i * gain_i);
  * row_m = m, row_k = T - c + 12 - e. So x8 * row_m * 2^-row_k approximates
  * h * (gain * 2^-12) / rms(h). A zero row gives x8 = 0, scale (2^14, 26).
- *   h int32 [R, n] with |h| < 2^25; gain int16 [n]; x8 int8 [R, n];
- *   row_m, row_k int32 [R]. n <= 16384. */
+ *   h int32 [R, n]; gain int16 [n]; x8 int8 [R, n]; row_m, row_k int32 [R].
+ *   n <= 16384. Domain: every row's S = sum h_i^2 < 2^62 and |h| < 2^31,
+ *   e.g. |h| < 2^25 (the residual stream's bound) for n <= 4096, or
+ *   |h| < 2^24 for n <= 16384. Outside it the row's outputs are undefined. */
 detint_status detint_rmsnorm(const int32_t *h, const int16_t *gain, int64_t R, int64_t n,
                              int8_t *x8, int32_t *row_m, int32_t *row_k, void *stream);
 

@@ -5,13 +5,35 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "detint.h"
 #include "internal.h"
 
 using namespace detint;
+
+namespace detint {
+
+hipError_t set_max_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, hipError_t> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = done.find(key);
+  if (it != done.end()) return it->second;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done[key] = e;
+  return e;
+}
+
+}  // namespace detint
 
 namespace {
 
@@ -447,8 +469,10 @@ detint_status detint_model_create(const detint_model_desc* desc, detint_model** 
   REQUIRE(d.n_q % d.n_kv == 0, "model_create: n_q must be a multiple of n_kv");
   REQUIRE(d.hidden % 16 == 0 && d.ffn % 16 == 0 && (d.n_q * d.head_dim) % 16 == 0,
           "model_create: hidden, ffn and n_q*d must be multiples of 16");
-  REQUIRE(d.head_dim <= 128 && d.hidden <= 16384 && d.ffn <= 8192,
-          "model_create: head_dim/hidden/ffn too large");
+  // the residual bound |h| < 2^25 keeps RMSNorm's sum of squares below 2^62
+  // only while hidden <= 4096
+  REQUIRE(d.head_dim <= 128 && d.hidden <= 4096 && d.ffn <= 8192,
+          "model_create: head_dim/hidden/ffn too large (hidden <= 4096, ffn <= 8192)");
   if (!attention_supported(d.head_dim, d.n_q / d.n_kv, d.max_pos))
     return fail(DETINT_EUNSUPPORTED, "model_create: attention does not support d=%lld group=%lld max_pos=%lld",
                 (long long)d.head_dim, (long long)(d.n_q / d.n_kv), (long long)d.max_pos);

@@ -932,13 +932,8 @@ hipError_t launch_pf(const int8_t* q8, const int32_t* e_q, const int8_t* kc, con
                      int64_t n_slots, int64_t max_pos, int32_t M, int32_t K, int32_t* out,
                      hipStream_t st) {
   constexpr int lds = PfLds<D, G>::bytes;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t err = hipFuncSetAttribute((const void*)attn_prefill_mfma<D, G>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (err != hipSuccess) return err;
-    attr = true;
-  }
+  const hipError_t err = set_max_lds((const void*)attn_prefill_mfma<D, G>, lds);
+  if (err != hipSuccess) return err;
   const int nblk = (int)((max_seqlen + PfCfg<G>::QP - 1) / PfCfg<G>::QP);
   attn_prefill_mfma<D, G><<<dim3((unsigned)nblk, (unsigned)seqs.S, (unsigned)nkv), 256, lds, st>>>(
       q8, e_q, kc, vc, seqs.cu, seqs.start, seqs.seq_slot, (int)nq, (int)nkv, (int)n_slots,
@@ -951,12 +946,8 @@ hipError_t launch_t(const int8_t* q8, const int32_t* e_q, const int8_t* kc, cons
                     const RowMap& rows, int64_t R, int64_t nq, int64_t nkv, int64_t n_slots,
                     int64_t max_pos, int32_t M, int32_t K, int32_t* out, hipStream_t st) {
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_rows<D, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        96 * 1024);
-    attr_set = true;
-  }
+  const hipError_t err = set_max_lds((const void*)attn_rows<D, G>, 96 * 1024);
+  if (err != hipSuccess) return err;
   attn_rows<D, G><<<dim3((unsigned)R, (unsigned)nkv), TPB, lds, st>>>(
       q8, e_q, kc, vc, rows, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, M, K, out);
   return hipGetLastError();
@@ -968,14 +959,9 @@ hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* s
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
                           hipStream_t st) {
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, true, NT>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    hipFuncSetAttribute((const void*)attn_decode_fused<D, G, false, NT>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    attr_set = true;
-  }
+  hipError_t err = set_max_lds((const void*)attn_decode_fused<D, G, true, NT>, 96 * 1024);
+  if (err == hipSuccess) err = set_max_lds((const void*)attn_decode_fused<D, G, false, NT>, 96 * 1024);
+  if (err != hipSuccess) return err;
   const dim3 grid((unsigned)B, (unsigned)(nq / G));
   const int gq = (int)(nq / nkv);
   if (p.qk_norm)

@@ -569,14 +569,8 @@ hipError_t pipe_launch_m(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
                          const Epi& e, void* out, hipStream_t st) {
   constexpr int lds = ST * (BM + (WIDE ? 2 : 1) * BN) * PBK;
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the workgroup limit");
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t err =
-        hipFuncSetAttribute((const void*)gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (err != hipSuccess) return err;
-    attr = true;
-  }
+  const hipError_t err = set_max_lds((const void*)gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN>, lds);
+  if (err != hipSuccess) return err;
   const int nb = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN><<<nb, 64 * WGM * WGN, lds, st>>>(A, W, Wlo, M, N, K, e,
                                                                               out);
@@ -746,10 +740,13 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     }
   }
   if (ks > 1) {
-    // Partials go out as agent-scope stores (coherent across the XCDs' L2
-    // caches without a full L2 write-back), complete before the barrier; the
-    // arrival count is a device-scope atomic; the last split reads them back
-    // with agent-scope loads.
+    // Partials go out as agent-scope atomic stores (coherent across the
+    // XCDs' L2 caches). Ordering: every thread's stores happen before the
+    // workgroup barrier; thread 0's arrival is an acquire-release RMW at
+    // agent scope, so it publishes them (release) and, in the last split,
+    // makes every earlier split's partials visible (acquire); the second
+    // barrier carries that to the other threads, which read the partials
+    // back with agent-scope atomic loads.
     auto put = [](int32_t* p, int32_t v) {
       __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
@@ -765,7 +762,9 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&sp.cnt[blockIdx.x], 1) == ks - 1;
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&sp.cnt[blockIdx.x], 1, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
     __syncthreads();
     if (!s_last) return;
     const int32_t* all = sp.part + (size_t)blockIdx.x * ks * TE;
@@ -837,13 +836,8 @@ hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
                          const Epi& e, void* out, const SplitWs* sp, hipStream_t st) {
   constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
   static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t err = hipFuncSetAttribute((const void*)gemm_skinny<WIDE, MR>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (err != hipSuccess) return err;
-    attr = true;
-  }
+  const hipError_t err = set_max_lds((const void*)gemm_skinny<WIDE, MR>, lds);
+  if (err != hipSuccess) return err;
   const int ks = skinny_splits(N, K, sp);
   const SplitWs none{};
   gemm_skinny<WIDE, MR><<<dim3((unsigned)((N + 31) / 32), (unsigned)ks), 1024, lds, st>>>(

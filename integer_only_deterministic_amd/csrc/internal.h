@@ -7,6 +7,12 @@ namespace detint {
 
 enum { MODE_RAW = 0, MODE_REQ_I8 = 1, MODE_FIX = 2, MODE_RES_ADD = 3, MODE_SWIGLU = 4 };
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device,
+// once per (device, kernel): thread-safe (a mutex-guarded registry), and the
+// attribute call is not a stream operation, so a first launch inside a graph
+// capture records only the kernel. Returns the attribute call's status.
+hipError_t set_max_lds(const void* kernel, int bytes);
+
 // Dyadic epilogue parameters of a GEMM (see detint.h, detint_gemm_i8).
 struct Epi {
   const int32_t* row_m;

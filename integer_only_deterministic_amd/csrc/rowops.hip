@@ -703,16 +703,9 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
   if (n % 4 == 0 && n >= 4 && aligned_to(gu, 16) && aligned_to(a8, 4)) {
     if (R > 64) {
       // persistent, two workgroups per CU (the table takes 64 KiB of LDS)
-      static bool attr = false;
-      if (!attr) {
-        hipError_t err = hipFuncSetAttribute((const void*)swiglu_tab_rk<1>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kSigLds);
-        if (err == hipSuccess)
-          err = hipFuncSetAttribute((const void*)swiglu_tab_rk<2>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kSigLds);
-        if (err != hipSuccess) return err;
-        attr = true;
-      }
+      hipError_t err = set_max_lds((const void*)swiglu_tab_rk<1>, kSigLds);
+      if (err == hipSuccess) err = set_max_lds((const void*)swiglu_tab_rk<2>, kSigLds);
+      if (err != hipSuccess) return err;
       const unsigned grid = (unsigned)(R < 512 ? R : 512);
       if (n <= 4 * SWT)
         swiglu_tab_rk<1><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, a8, row_m, row_k);

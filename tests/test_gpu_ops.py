@@ -1,7 +1,7 @@
 """GPU parity of every libdetint op against the CPU oracle, bit for bit
 (tolerance 0: every result is an integer). Inputs are seeded synthetic data;
 sizes span several tiles plus ragged tails; the full-size GEMM sweep is
-checked on sampled rows the oracle computes one by one."""
+checked on every output element."""
 import numpy as np
 import pytest
 
@@ -36,23 +36,19 @@ def host(t):
 @pytest.mark.parametrize("K,N", S.GEMM_SWEEP_KN)
 def test_gemm_sweep(D, K, N):
     """The standalone sweep: M in {1, 8, 64, 512, 2048} x the five projection
-    shapes, RAW int32 and per-row x per-column requant to int8."""
+    shapes, RAW int32 and per-row x per-column requant to int8, every output
+    element against the oracle's int64 brute force."""
     for M in S.GEMM_SWEEP_M:
         g = S.make_gemm_operands(M, N, K, seed=7)
         A, W = dev(g["A"]), dev(g["W"])
         rm, rk, cm = dev(g["row_m"]), dev(g["row_k"]), dev(g["col_m"])
         raw = host(D.detint_gemm_i8(A, W))
         q = host(D.detint_gemm_i8(A, W, rm, rk, cm, g["col_k"], 0, D.REQ_I8))
-        if M <= 64:
-            rows = np.arange(M)
-        else:
-            rng = np.random.default_rng(M + N + K)
-            rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], rng.integers(0, M, 12)]))
-        acc = O.gemm(g["A"][rows], g["W"])
-        np.testing.assert_array_equal(raw[rows], acc, err_msg=f"RAW M={M} N={N} K={K}")
-        want = O.epilogue(acc, g["row_m"][rows], g["row_k"][rows], g["col_m"], g["col_k"], 0, O.REQ_I8)
-        np.testing.assert_array_equal(q[rows], want, err_msg=f"REQ_I8 M={M} N={N} K={K}")
-        del A, W
+        acc = O.gemm(g["A"], g["W"])                 # every row, int64 brute force
+        np.testing.assert_array_equal(raw, acc, err_msg=f"RAW M={M} N={N} K={K}")
+        want = O.epilogue(acc, g["row_m"], g["row_k"], g["col_m"], g["col_k"], 0, O.REQ_I8)
+        np.testing.assert_array_equal(q, want, err_msg=f"REQ_I8 M={M} N={N} K={K}")
+        del A, W, acc, want, raw, q
 
 
 # K % 128 == 0 shapes take the pipelined kernel; (200, 300, 256),
@@ -177,7 +173,24 @@ def test_rmsnorm(D, R, n):
     np.testing.assert_array_equal(host(k), ok)
 
 
-@pytest.mark.parametrize("n", [64, 128, 768, 1024, 2048])
+def test_rmsnorm_largest_rows(D):
+    """The largest rows the stated domain admits: n = 16384 at |h| = 2^24 - 1
+    (sum of squares just under 2^62), and n = 4096 at the +-(2^25 - 1)
+    residual bound, with mixed signs and one all-maximum row."""
+    rng = np.random.default_rng(16384)
+    for n, lim in ((16384, (1 << 24) - 1), (4096, (1 << 25) - 1)):
+        h = rng.choice([-lim, lim], (3, n)).astype(np.int32)
+        h[1] = lim
+        h[2, ::2] = rng.integers(-lim, lim + 1, n // 2)
+        g = rng.integers(1 << 12, (1 << 13) + 1, n).astype(np.int16)
+        x8, m, k = D.detint_rmsnorm(dev(h), dev(g))
+        ox, om, ok = O.rmsnorm(h, g)
+        np.testing.assert_array_equal(host(m), om, err_msg=f"n={n}")
+        np.testing.assert_array_equal(host(k), ok, err_msg=f"n={n}")
+        np.testing.assert_array_equal(host(x8), ox, err_msg=f"n={n}")
+
+
+@pytest.mark.parametrize("n", [64, 128, 768, 1024, 2048, 4096])
 def test_rmsnorm_magnitudes(D, n):
     """The integer square root and divisions of irms over the whole range of
     row magnitudes: row i is scaled to about 2^(i % 26), some rows hold a

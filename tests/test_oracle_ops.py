@@ -136,6 +136,24 @@ def test_rmsnorm_zero_row_and_bound():
         O.rmsnorm(bad, g)
 
 
+def test_rmsnorm_sum_of_squares_domain():
+    """The stated domain is a sum of squares below 2^62: the largest rows it
+    admits (n = 16384 at |h| = 2^24 - 1, n = 4096 at the 2^25 residual
+    bound) normalise to within the real-value bound; one step past it
+    (n = 16384 at |h| = 2^24, S = 2^62) is reported as an error."""
+    g = np.full(16384, 4096, np.int16)           # gain 1.0
+    for n, lim in ((16384, (1 << 24) - 1), (4096, (1 << 25) - 1)):
+        h = np.full((2, n), lim, np.int32)
+        h[1, ::2] = -lim
+        x8, m, k = O.rmsnorm(h, g[:n])
+        # every |h| equals the RMS, so each value normalises to +-1
+        got = x8 * (m * 2.0 ** -k.astype(np.float64))[:, None]
+        assert np.all(np.abs(np.abs(got) - 1.0) <= 2.0 ** -6)
+        assert np.array_equal(np.sign(x8), np.sign(h))
+    with pytest.raises(O.OracleError):
+        O.rmsnorm(np.full((1, 16384), 1 << 24, np.int32), g)
+
+
 def test_requant_rows():
     rng = np.random.default_rng(18)
     y = rng.integers(-(1 << 22), 1 << 22, (20, 2048)).astype(np.int32)
