@@ -50,6 +50,7 @@ typedef int32_t detint_status;
 #define DETINT_EINVAL 1        /* bad shape, null pointer, misalignment */
 #define DETINT_EUNSUPPORTED 2  /* shape or configuration this build does not handle */
 #define DETINT_EHIP 3          /* a HIP launch/runtime call failed */
+#define DETINT_EBOUND 4        /* detint_check: an intermediate left its bound */
 
 /* GEMM epilogue modes (DetLLM README "Layout": dyadic requant in dyadic.py). */
 #define DETINT_GEMM_RAW 0      /* out int32 = acc                                   */
@@ -58,6 +59,32 @@ typedef int32_t detint_status;
 #define DETINT_GEMM_RES_ADD 3  /* out int32 += R(acc*m_r*m_c, k_r + k_c - frac)     */
 
 const char *detint_version(void);
+
+/* Device bound checks (BitExact LLM blog, "Reproducibility has a cost":
+ * range checks before residual additions, on the final logits and on the
+ * linear epilogues). Kernels test their intermediates against the bounds
+ * this header states and, on a violation, set a bit in a flag word of the
+ * device and finish normally (the affected results are undefined, memory
+ * stays safe). Bits:
+ *   RESIDUAL  the residual stream left |h| < 2^25 (embedding, O-proj or
+ *             down-projection residual add of a model);
+ *   INT32     a FIX / logits / standalone RES_ADD result, a q/k/v fixed-point
+ *             value or a rotated q/k left int32;
+ *   NORM      an RMSNorm row's sum of squares reached 2^62;
+ *   SWIGLU    a SwiGLU gate or up value left |x| < 2^24;
+ *   ID        a token id outside [0, vocab) (its row is embedded as zeros).
+ * detint_check waits for `stream` (everything enqueued on it so far), then
+ * reads and clears the current device's flags (set by any call on any
+ * stream of that device since the last check): *flags (nullable) receives
+ * them; returns DETINT_EBOUND when any is set, else DETINT_OK (DETINT_EHIP
+ * if the device could not be read). It synchronises, so it is not for use
+ * inside a graph capture. */
+#define DETINT_BOUND_RESIDUAL 1u
+#define DETINT_BOUND_INT32 2u
+#define DETINT_BOUND_NORM 4u
+#define DETINT_BOUND_SWIGLU 8u
+#define DETINT_BOUND_ID 16u
+detint_status detint_check(void *stream, uint32_t *flags);
 /* Message of the last error returned on the calling thread ("" if none). */
 const char *detint_last_error(void);
 

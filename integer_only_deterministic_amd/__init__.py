@@ -16,7 +16,8 @@ import numpy as np
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libdetint.so"
 
-DETINT_OK, DETINT_EINVAL, DETINT_EUNSUPPORTED, DETINT_EHIP = 0, 1, 2, 3
+DETINT_OK, DETINT_EINVAL, DETINT_EUNSUPPORTED, DETINT_EHIP, DETINT_EBOUND = 0, 1, 2, 3, 4
+BOUND_RESIDUAL, BOUND_INT32, BOUND_NORM, BOUND_SWIGLU, BOUND_ID = 1, 2, 4, 8, 16
 RAW, REQ_I8, FIX, RES_ADD = 0, 1, 2, 3
 FWD_ADVANCE = 1
 
@@ -53,6 +54,7 @@ class ModelDesc(C.Structure):
 _SIGS = {
     "detint_version": (C.c_char_p, []),
     "detint_last_error": (C.c_char_p, []),
+    "detint_check": (i32, [vp, C.POINTER(C.c_uint32)]),
     "detint_gemm_i8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
     "detint_gemm_w16": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
     "detint_split_w16": (i32, [vp, i64, vp, vp, vp]),
@@ -133,6 +135,17 @@ def _p(t, dtype=None):
 
 
 # ------------------------------------------------------------------ ops
+
+def detint_check() -> int:
+    """Wait for the current stream, then read and clear the device's bound
+    flags (BOUND_* bits; 0 when every intermediate stayed in its bound)."""
+    lib = library()
+    f = C.c_uint32(0)
+    rc = lib.detint_check(_stream(), C.byref(f))
+    if rc not in (DETINT_OK, DETINT_EBOUND):
+        raise DetintError(rc, lib.detint_last_error().decode())
+    return int(f.value)
+
 
 def detint_gemm_i8(A, W, row_m=None, row_k=None, col_m=None, col_k=0, frac=0, mode=RAW, out=None):
     torch = _torch()

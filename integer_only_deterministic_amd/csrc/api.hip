@@ -92,6 +92,21 @@ extern "C" {
 const char* detint_version(void) { return "libdetint 0.1 gfx950"; }
 const char* detint_last_error(void) { return g_err.c_str(); }
 
+detint_status detint_check(void* stream, uint32_t* flags) {
+  uint32_t f = 0;
+  hipError_t e = bound_flags_gemm(&f, S_(stream));
+  if (e == hipSuccess) e = bound_flags_decode(&f, S_(stream));
+  if (e == hipSuccess) e = bound_flags_rowops(&f, S_(stream));
+  if (e == hipSuccess) e = bound_flags_attention(&f, S_(stream));
+  if (flags) *flags = f;
+  if (e != hipSuccess) return hip_status(e, "check: reading the bound flags");
+  if (f)
+    return fail(DETINT_EBOUND, "check: bound flags 0x%x (residual %d, int32 %d, norm %d, "
+                "swiglu %d, id %d)", f, !!(f & DETINT_BOUND_RESIDUAL), !!(f & DETINT_BOUND_INT32),
+                !!(f & DETINT_BOUND_NORM), !!(f & DETINT_BOUND_SWIGLU), !!(f & DETINT_BOUND_ID));
+  return ok();
+}
+
 // ------------------------------------------------------------------- GEMMs
 
 detint_status detint_gemm_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
@@ -572,7 +587,7 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   }
   LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
   {
-    Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr};
+    Epi ep{rm, rk, L.wo_m, wk, d.f_res, MODE_RES_ADD, nullptr, 0, 0, 25};
     LAUNCH(launch_gemm(x8, L.wo, d.wide ? L.wo_lo : nullptr, R, H, nqd, ep, h, st, sp));
   }
   // FFN block: RMSNorm -> gate/up -> DI-SwiGLU -> down + residual
@@ -590,7 +605,7 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
     LAUNCH(launch_swiglu(gu, R, F, d.f_a, m->mg, m->kg, x8, rm, rk, st));
   }
   {
-    Epi ep{rm, rk, L.wd_m, wk, d.f_res, MODE_RES_ADD, nullptr};
+    Epi ep{rm, rk, L.wd_m, wk, d.f_res, MODE_RES_ADD, nullptr, 0, 0, 25};
     LAUNCH(launch_gemm(x8, L.wd, d.wide ? L.wd_lo : nullptr, R, H, F, ep, h, st, sp));
   }
 #undef LAUNCH

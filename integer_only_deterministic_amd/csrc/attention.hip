@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   __shared__ int64_t rmax[NW][G], rsum[NW][G], rnv[G];
   __shared__ int32_t sred[NW][G * D];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h0 = blockIdx.y * G, kvh = h0 / gq;
+  const int h0 = blockIdx.y * G, kvh = h0 >> (__builtin_ctz(gq));  // gq: a power of two
 
   // 1. loads of the post-processing, which do not depend on the row's
   //    position: per head this wave handles, lane i < d/2 holds elements i
@@ -378,6 +378,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   //    k, v -> int8 at the cache scales, into the cache and LDS
   int8_t* snk = (int8_t*)snew;
   int8_t* snv = (int8_t*)snew + D;
+  uint32_t bad = 0;
 #pragma unroll
   for (int u = 0; u < HR; ++u) {
     const int t = wave + NW * u;
@@ -390,6 +391,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
       for (int e2 = 0; e2 < 2; ++e2) {
         int64_t vf = e2 ? hx1[u] : hx0[u];
         if (QKN) vf = R(vf * rm * (e2 ? hm1[u] : hm0[u]), rk + p.col_k - p.f_n);
+        if (act) bad |= i32_check(vf);
         const int8_t v8 = clamp8(R(vf * p.vq_m, p.vq_k));
         if (act) {
           dst[e2 ? j1 : j0] = v8;
@@ -419,6 +421,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     }
     int64_t y0 = act ? R(x0 * cs - x1 * sn, 14) : 0;
     int64_t y1 = act ? R(x1 * cs + x0 * sn, 14) : 0;
+    bad |= i32_check(y0) | i32_check(y1);  // rotated q / k within int32
     const int g0 = act ? gk0 : 0, g1 = act ? gk1 : 0;
     if (t < G) {
       y0 = R(y0, g0);
@@ -441,6 +444,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
       snk[j1] = k1;
     }
   }
+  bound_raise(bad);
   lds_barrier();
 
   // 4. pass 1: scores into LDS, per-head maxima
@@ -998,6 +1002,8 @@ hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* s
 }
 
 }  // namespace
+
+DETINT_BOUND_READER(bound_flags_attention)
 
 hipError_t launch_attention_decode_fused(const int32_t* qkv, const QkvPost& p,
                                          const int32_t* start_pos, const int32_t* slot, int64_t B,

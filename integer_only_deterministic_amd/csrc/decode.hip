@@ -127,6 +127,7 @@ struct FG {
   int64_t* part;
   int32_t* rm_out;           // nullable: row scales written by workgroup 0
   int32_t* rk_out;
+  int32_t res_bits;          // EPI_RES bound 2^res_bits (0: int32 range only)
 };
 
 template <int MT, int CPW, int KC, int PRO, int EPI>
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
   const int M = p.M, N = p.N, K = p.K;
   const int ngroups = EPI == EPI_SWIGLU ? N : (N + CPW - 1) / CPW;
   const int64_t obase = EPI == EPI_LOGITS && p.out_row_base ? *p.out_row_base : 0;
+  uint32_t bad = 0;  // bound flags seen by this thread
 
   // 1. Loads. Every load below uses a clamped, always-valid address and
   //    its register is left untouched until all of them are in flight:
@@ -306,6 +308,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
       }
       const int e = dq_exp((uint64_t)At);
       int32_t sm, sk;
+      if (PRO == PRO_NORM && (uint64_t)St >> 62) bad |= kBoundNorm;
       if (PRO == PRO_NORM) {
         if (St == 0) {
           sm = 1 << 14;
@@ -401,6 +404,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         const int64_t gv = R((int64_t)gt * s_m[0] * cm[0], sh);
         const int64_t uv = R((int64_t)ut * s_m[0] * cm[1], sh);
         const int64_t res = R(gv * sigmoid_q15_wave(gv, p.Mg, p.Kg), 15) * uv;
+        bad |= out_of(gv, 24) | out_of(uv, 24) ? kBoundSwiglu : 0u;
         if (lane == 0) ((int64_t*)p.out)[g] = res;
       }
     } else if (EPI == EPI_SWIGLU) {
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         const int sh = s_k[mm] + p.col_k - p.f_a;
         const int64_t gv = R((int64_t)tot * s_m[mm] * cm[0], sh);
         const int64_t uv = R((int64_t)up * s_m[mm] * cm[1], sh);
+        bad |= out_of(gv, 24) | out_of(uv, 24) ? kBoundSwiglu : 0u;
         ((int64_t*)p.out)[(size_t)mm * N + j] = R(gv * sigmoid_q15(gv, p.Mg, p.Kg), 15) * uv;
       }
     } else if (leader && mm < M) {
@@ -420,12 +425,16 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         } else {
           const int64_t y = R((int64_t)tot * s_m[mm] * cm[cc], s_k[mm] + p.col_k - p.frac);
           if (EPI == EPI_FIX) {
+            bad |= i32_check(y);
             ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)y;
           } else if (EPI == EPI_REQ) {
             ((int8_t*)p.out)[(size_t)mm * N + col] = clamp8(y);
           } else if (EPI == EPI_RES) {
-            ((int32_t*)p.out)[(size_t)mm * N + col] = old + (int32_t)y;
+            const int64_t t = (int64_t)old + y;
+            bad |= res_check(t, p.res_bits);
+            ((int32_t*)p.out)[(size_t)mm * N + col] = (int32_t)t;
           } else {
+            bad |= i32_check(y);
             ((int32_t*)p.out)[(size_t)(obase + mm) * N + col] = (int32_t)y;
             const int64_t key = amax_key(y, col);
             bestk = key > bestk ? key : bestk;
@@ -448,6 +457,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
     }
     if (leader && cc == 0 && mm < M) p.part[(size_t)mm * nw + gw] = bestk;
   }
+  bound_raise(bad);
 }
 
 // Workgroups of a launch: one group per wave where that fits, else a cap -
@@ -489,6 +499,8 @@ hipError_t launch_mt(const FG& p, hipStream_t st) {
 
 }  // namespace
 
+DETINT_BOUND_READER(bound_flags_decode)
+
 int fused_decode_parts(int64_t V, int64_t M) {
   return cap_blocks((V + 1) / 2, M <= 1 ? 1 : (M <= 4 ? 4 : 8)) * 4;
 }
@@ -510,7 +522,7 @@ hipError_t launch_fused_oproj(const int32_t* att, int32_t fold_m, int32_t fold_k
                               int64_t N, int64_t K, int32_t* h, hipStream_t st) {
   FG p{};
   p.in32 = att; p.fold_m = fold_m; p.fold_k = fold_k; p.W = W; p.col_m = col_m; p.col_k = col_k;
-  p.frac = frac; p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h;
+  p.frac = frac; p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h; p.res_bits = 25;
   return launch_mt<1, PRO_DQ32, EPI_RES>(p, st);
 }
 
@@ -529,7 +541,7 @@ hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, 
                              int32_t* h, hipStream_t st) {
   FG p{};
   p.in64 = prod; p.f_a = f_a; p.W = W; p.col_m = col_m; p.col_k = col_k; p.frac = frac;
-  p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = h; p.res_bits = 25;
   return launch_mt<1, PRO_DQ64, EPI_RES>(p, st);
 }
 

@@ -36,6 +36,41 @@ __device__ __forceinline__ int64_t R128(__int128 x, int s) {
 
 __device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __builtin_clzll(x) : 0; }
 
+// ------------------------------------------------------------------------
+// Device bound flags (BitExact LLM blog, "Reproducibility has a cost": range
+// checks before residual additions, on the final logits and on the linear
+// epilogues). A kernel that sees an intermediate outside its written bound
+// ORs a bit into a flag word and carries on (memory-safe, result undefined);
+// detint_check reads and clears the words. The bits are the DETINT_BOUND_*
+// values of detint.h. One word per translation unit: static device storage
+// on each GPU, no allocation.
+enum : uint32_t {
+  kBoundResidual = 1u,  // residual stream |h| >= 2^25 (adds, embedding)
+  kBoundInt32 = 2u,     // a FIX / logits / RES_ADD result outside int32
+  kBoundNorm = 4u,      // RMSNorm row with sum of squares >= 2^62
+  kBoundSwiglu = 8u,    // SwiGLU gate or up outside (-2^24, 2^24)
+  kBoundId = 16u,       // token id outside [0, vocab)
+};
+static __device__ uint32_t g_bound_flags;
+
+// OR `bits` into the flag word when nonzero (rare: only on a violation).
+__device__ __forceinline__ void bound_raise(uint32_t bits) {
+  if (bits) atomicOr(&g_bound_flags, bits);
+}
+// 1 when |t| >= 2^b (0 < b <= 62)
+__device__ __forceinline__ uint32_t out_of(int64_t t, int b) {
+  return (uint64_t)(t + (int64_t(1) << b) - 1) >= (uint64_t(1) << (b + 1)) - 1 ? 1u : 0u;
+}
+// flag bit of a residual-add result t with bound 2^res_bits (0: int32)
+__device__ __forceinline__ uint32_t res_check(int64_t t, int res_bits) {
+  return res_bits > 0 ? (out_of(t, res_bits) ? kBoundResidual : 0u)
+                      : ((uint64_t)(t + 2147483648LL) >> 32 ? kBoundInt32 : 0u);
+}
+// flag bit of a FIX result outside int32
+__device__ __forceinline__ uint32_t i32_check(int64_t y) {
+  return (uint64_t)(y + 2147483648LL) >> 32 ? kBoundInt32 : 0u;
+}
+
 // R(x, e) for a shift e >= 0 known to be the same across the wave (a DQ
 // exponent): branch-free, the rounding half is 2^e >> 1 (0 for e = 0).
 __device__ __forceinline__ int64_t R_nn(int64_t x, int e) {
@@ -59,6 +94,21 @@ __device__ __forceinline__ uint64_t udiv64(uint64_t n, uint64_t d) {
     if (r >= d) {
       r -= d;
       q |= uint64_t(1) << i;
+    }
+  }
+  return q;
+}
+
+// floor(n / d) for 32-bit n and d >= 1, restoring division from the top bit
+// of n: index arithmetic (tile numbers, head groups, tie counts) without the
+// compiler's `/`, whose expansion goes through a float reciprocal.
+__device__ __forceinline__ uint32_t udiv32(uint32_t n, uint32_t d) {
+  uint32_t q = 0, r = 0;
+  for (int i = 31 - __builtin_clz(n | 1); i >= 0; --i) {
+    r = (r << 1) | ((n >> i) & 1u);
+    if (r >= d) {
+      r -= d;
+      q |= 1u << i;
     }
   }
   return q;
@@ -317,5 +367,23 @@ __device__ __forceinline__ int dq_exp(uint64_t A) {
   const int b = bitlen64(A);
   return b > 7 ? b - 7 : 0;
 }
+
+// Host side: defines `hipError_t NAME(uint32_t* acc, hipStream_t st)`, which
+// waits for the stream, ORs this translation unit's flag word into *acc and
+// clears it (copies, no memset, outside any graph capture).
+#define DETINT_BOUND_READER(NAME)                                                         \
+  hipError_t NAME(uint32_t* acc, hipStream_t st) {                                        \
+    uint32_t v = 0;                                                                        \
+    static const uint32_t zero = 0;                                                        \
+    hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_bound_flags), sizeof v, 0,    \
+                                            hipMemcpyDeviceToHost, st);                    \
+    if (e == hipSuccess) e = hipStreamSynchronize(st);                                     \
+    if (e == hipSuccess && v)                                                              \
+      e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_bound_flags), &zero, sizeof zero, 0,         \
+                                 hipMemcpyHostToDevice, st);                               \
+    if (e == hipSuccess && v) e = hipStreamSynchronize(st);                                \
+    *acc |= v;                                                                             \
+    return e;                                                                              \
+  }
 
 }  // namespace detint

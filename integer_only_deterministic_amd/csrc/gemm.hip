@@ -52,39 +52,16 @@ __device__ __forceinline__ void epi_store(int64_t acc, int64_t i, int64_t j, int
     y = R128((__int128)(acc * e.row_m[i]) * e.col_m[j], s);
   else
     y = R(acc * e.row_m[i] * e.col_m[j], s);
-  if (e.mode == MODE_REQ_I8)
+  if (e.mode == MODE_REQ_I8) {
     ((int8_t*)out)[o] = clamp8(y);
-  else if (e.mode == MODE_FIX)
+  } else if (e.mode == MODE_FIX) {
+    bound_raise(i32_check(y));
     ((int32_t*)out)[o] = (int32_t)y;
-  else
-    ((int32_t*)out)[o] += (int32_t)y;
-}
-
-// epi_store with the row and column scales already loaded and the flat
-// output index o. Without limbs |m_r * m_c| < 2^30, so acc * (m_r * m_c) is
-// one 32 x 32 -> 64-bit product; the value equals acc * m_r * m_c exactly.
-template <bool WIDE>
-__device__ __forceinline__ void epi_put(int64_t acc, int64_t o, int32_t rm, int32_t rk, int32_t cm,
-                                        const Epi& e, void* out) {
-  if (e.mode == MODE_RAW) {
-    if (WIDE)
-      ((int64_t*)out)[o] = acc;
-    else
-      ((int32_t*)out)[o] = (int32_t)acc;
-    return;
+  } else {
+    const int64_t t = (int64_t)((int32_t*)out)[o] + y;
+    bound_raise(res_check(t, e.res_bits));
+    ((int32_t*)out)[o] = (int32_t)t;
   }
-  const int s = rk + e.col_k - (e.mode == MODE_REQ_I8 ? 0 : e.frac);
-  int64_t y;
-  if (WIDE)
-    y = R128((__int128)(acc * rm) * cm, s);
-  else
-    y = R((int64_t)(int32_t)acc * (int64_t)(rm * cm), s);
-  if (e.mode == MODE_REQ_I8)
-    ((int8_t*)out)[o] = clamp8(y);
-  else if (e.mode == MODE_FIX)
-    ((int32_t*)out)[o] = (int32_t)y;
-  else
-    ((int32_t*)out)[o] += (int32_t)y;
 }
 
 __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
@@ -268,8 +245,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   const int q8 = nb >> 3;
   if (b < 8 * q8) b = (b & 7) * q8 + (b >> 3);
   constexpr int G = 8;
-  const int grp = b / (G * nbn), first = grp * G, gm = min(nbm - first, G);
-  const int tm = first + (b % (G * nbn)) % gm, tn = (b % (G * nbn)) / gm;
+  const int grp = (int)udiv32((uint32_t)b, (uint32_t)(G * nbn)), first = grp * G,
+            gm = min(nbm - first, G);
+  const int inr = b - grp * G * nbn, tn = (int)udiv32((uint32_t)inr, (uint32_t)gm);
+  const int tm = first + inr - tn * gm;
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = K / PBK;
 
@@ -459,6 +438,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
     // exactly, for 32 <= s <= 94.
     auto tiles = [&](auto hi) {  // hi: every shift >= 33 (compile-time flag)
       constexpr bool HI = decltype(hi)::value;
+      uint32_t bad = 0;
 #pragma clang loop unroll(full)
       for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
@@ -496,15 +476,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
               const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)__mul24(s_rm[li], cm);
               y = (pr + (int64_t(1) << (sh - 1))) >> sh;
             }
-            if (MODE == MODE_REQ_I8)
+            if (MODE == MODE_REQ_I8) {
               ((int8_t*)out)[o] = clamp8(y);
-            else if (MODE == MODE_FIX)
+            } else if (MODE == MODE_FIX) {
+              if (!HI) bad |= i32_check(y);  // a mul_hi result is within int32
               ((int32_t*)out)[o] = (int32_t)y;
-            else
-              ((int32_t*)out)[o] = old[r] + (int32_t)y;
+            } else {
+              const int64_t tsum = (int64_t)old[r] + y;
+              bad |= res_check(tsum, e.res_bits);
+              ((int32_t*)out)[o] = (int32_t)tsum;
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      bound_raise(bad);
     };
     // one copy of the unrolled tile loop per case (a per-element branch
     // would interleave both and double the code the loop runs through)
@@ -517,6 +502,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
     tiles(std::false_type{});
     return;
   }
+  uint32_t bad = 0;
 #pragma clang loop unroll(full)
   for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
@@ -552,16 +538,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
         const int64_t y = WIDE ? R128((__int128)(v * s_rm[li]) * cm, sh)
                                : R((int64_t)(int32_t)v * s_rm[li] * cm, sh);
         if (i < M && j < N) {
-          if (MODE == MODE_REQ_I8)
+          if (MODE == MODE_REQ_I8) {
             ((int8_t*)out)[o] = clamp8(y);
-          else if (MODE == MODE_FIX)
+          } else if (MODE == MODE_FIX) {
+            bad |= i32_check(y);
             ((int32_t*)out)[o] = (int32_t)y;
-          else
-            ((int32_t*)out)[o] = old[r] + (int32_t)y;
+          } else {
+            const int64_t tsum = (int64_t)old[r] + y;
+            bad |= res_check(tsum, e.res_bits);
+            ((int32_t*)out)[o] = (int32_t)tsum;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // keep tiles' live ranges apart
     }
+  bound_raise(bad);
 }
 
 template <int BM, int BN, int ST, bool WIDE, int MODE, int WGM, int WGN>
@@ -643,8 +634,9 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 32, ks = gridDim.y, split = blockIdx.y;
-  const int kc = K / ks / SK_W, nst = kc / 32;
-  const int kb = split * (K / ks) + wave * kc + (lane >> 5) * 16;
+  const int kspl = (int)udiv32((uint32_t)K, (uint32_t)ks);  // K range of one split
+  const int kc = kspl / SK_W, nst = kc / 32;
+  const int kb = split * kspl + wave * kc + (lane >> 5) * 16;
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
@@ -796,8 +788,10 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
                              : R(v * e.row_m[ic] * e.col_m[wrc], s);
       const int64_t u = __shfl_xor(y, 16);
       const int j = (n0 >> 1) + c;
-      if (c < 16 && i < M && j < (N >> 1))
+      if (c < 16 && i < M && j < (N >> 1)) {
+        bound_raise(out_of(y, 24) | out_of(u, 24) ? kBoundSwiglu : 0u);
         ((int64_t*)out)[(size_t)i * (N >> 1) + j] = R(y * sigmoid_q15(y, e.sw_mg, e.sw_kg), 15) * u;
+      }
     }
     return;
   }
@@ -915,14 +909,17 @@ __global__ __launch_bounds__(256) void gemv(const int8_t* __restrict__ A,
                                   : R(s0 * e.row_m[m] * e.col_m[j0], sh);
           int64_t k0 = amax_key(y0, j0);
           const int64_t base = (e.out_row_base ? *e.out_row_base : 0) + m;
+          uint32_t bad = i32_check(y0);
           if (lane == 0) ((int32_t*)out)[base * N + j0] = (int32_t)y0;
           if (two) {
             const int64_t y1 = WIDE ? R128((__int128)(s1 * e.row_m[m]) * e.col_m[j0 + 1], sh)
                                     : R(s1 * e.row_m[m] * e.col_m[j0 + 1], sh);
+            bad |= i32_check(y1);
             if (lane == 0) ((int32_t*)out)[base * N + j0 + 1] = (int32_t)y1;
             const int64_t k1 = amax_key(y1, j0 + 1);
             k0 = k1 > k0 ? k1 : k0;
           }
+          if (lane == 0) bound_raise(bad);
           best[m] = k0 > best[m] ? k0 : best[m];
         } else if (lane == 0) {
           epi_store<WIDE>(s0, m, j0, N, e, out);
@@ -974,8 +971,8 @@ hipError_t gemv_dispatch(const int8_t* A, const int8_t* W, const int8_t* W_lo, i
 
 __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __restrict__ hi,
                           int8_t* __restrict__ lo) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // one element a thread
+  if (i < n) {
     const int v = w[i];
     hi[i] = (int8_t)(v >> 8);
     lo[i] = (int8_t)((v & 255) - 128);
@@ -988,6 +985,8 @@ bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs) {
   const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
   return M > 16 && off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !limbs));
 }
+
+DETINT_BOUND_READER(bound_flags_gemm)
 
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
@@ -1031,8 +1030,8 @@ hipError_t launch_logits_argmax(const int8_t* A, const int8_t* W, const int8_t* 
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
                             hipStream_t st) {
   if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   split_w16<<<(unsigned)blocks, 256, 0, st>>>(W16, n, hi, lo);
   return hipGetLastError();
 }

@@ -27,7 +27,17 @@ struct Epi {
   // f_a) and the int64 DI-SwiGLU product R(g sigmoid(g), 15) u is stored to
   // out [M, F]. Sigmoid multiplier (sw_mg, sw_kg).
   int32_t sw_mg, sw_kg;
+  // RES_ADD bound: a result with |h| >= 2^res_bits raises the residual bound
+  // flag (the model's residual stream: 25); 0 checks only the int32 range.
+  int32_t res_bits;
 };
+
+// Bound flags of each translation unit (see detint_check): wait for the
+// stream, OR the unit's flag word into *acc and clear it.
+hipError_t bound_flags_gemm(uint32_t* acc, hipStream_t st);
+hipError_t bound_flags_decode(uint32_t* acc, hipStream_t st);
+hipError_t bound_flags_rowops(uint32_t* acc, hipStream_t st);
+hipError_t bound_flags_attention(uint32_t* acc, hipStream_t st);
 
 // C = A[M,K] . W[N,K]^T with epilogue; W_lo != nullptr selects 16-bit limbs.
 // Workspace for split-K skinny GEMMs: int32 partials for up to

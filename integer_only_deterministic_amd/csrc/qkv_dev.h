@@ -34,6 +34,7 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
       const int j = t ? j1 : j0;
       int64_t vf = row[c0 + j];
       if (p.qk_norm) vf = R(vf * rm * p.col_m[c0 + j], rk + p.col_k - p.f_n);
+      bound_raise(i32_check(vf));
       dst[j] = clamp8(R(vf * p.vq_m, p.vq_k));
     }
     return;
@@ -68,10 +69,12 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
     const int64_t c = p.cos_t[(size_t)pos * half + lane], s = p.sin_t[(size_t)pos * half + lane];
     y0 = R(x0 * c - x1 * s, 14);
     y1 = R(x1 * c + x0 * s, 14);
+    bound_raise(i32_check(y0) | i32_check(y1));  // rotated q / k within int32
   }
   if (hh < nq) {
     if (p.k_gain && act) {  // the inverse of the key gain of the shared KV head
-      const int8_t* g = p.k_gain + (size_t)(hh / (nq / nkv)) * d;
+      // query heads per KV head is a power of two: hh / (nq / nkv) as a shift
+      const int8_t* g = p.k_gain + (size_t)(hh >> (__builtin_ctz(nq) - __builtin_ctz(nkv))) * d;
       y0 = R(y0, g[j0] & 7);
       y1 = R(y1, g[j1] & 7);
     }

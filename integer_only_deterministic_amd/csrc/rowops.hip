@@ -33,6 +33,7 @@ __global__ __launch_bounds__(TPB) void rmsnorm_k(const int32_t* __restrict__ h,
   }
   S = block_sum(S, red);
   A = block_max(A, red);
+  if (threadIdx.x == 0) bound_raise((uint64_t)S >> 62 ? kBoundNorm : 0u);
   int8_t* xr = x8 + (size_t)r * n;
   if (S == 0) {
     for (int i = threadIdx.x; i < n; i += TPB) xr[i] = 0;
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(TPB) void rmsnorm_rk(const int32_t* __restrict__ h,
   }
   S = block_sum(S, red);
   A = block_max(A, red);
+  if (threadIdx.x == 0) bound_raise((uint64_t)S >> 62 ? kBoundNorm : 0u);
   int8_t* xr = x8 + (size_t)r * n;
   int32_t m = 1 << 14, sh = 26;
   int e = 0;
@@ -247,13 +249,16 @@ __global__ __launch_bounds__(SWT) void swiglu_k(const int32_t* __restrict__ gu, 
   const int32_t* u = g + n;
   int64_t p[SWPER];
   int64_t A = 0;
+  uint32_t bad = 0;
 #pragma unroll
   for (int i = 0; i < SWPER; ++i) {
     const int j = threadIdx.x + i * SWT;
     p[i] = j < n ? swiglu_p(g[j], u[j], Mg, Kg) : 0;
+    if (j < n) bad |= out_of(g[j], 24) | out_of(u[j], 24);
     const int64_t a = (int64_t)uabs64(p[i]);
     A = a > A ? a : A;
   }
+  bound_raise(bad ? kBoundSwiglu : 0u);
   A = block_max(A, red);
   const int e = dq_exp((uint64_t)A);
 #pragma unroll
@@ -283,16 +288,19 @@ __global__ __launch_bounds__(SWT) void swiglu_rk(const int32_t* __restrict__ gu,
     uv[u] = *(const v4i*)(up + RR::at(u, n));
   }
   int64_t p[U][4], A = 0;
+  uint32_t bad = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool ok = RR::first(u) < n;
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       p[u][e4] = ok ? swiglu_p(gv[u][e4], uv[u][e4], Mg, Kg) : 0;
+      if (ok) bad |= out_of(gv[u][e4], 24) | out_of(uv[u][e4], 24);
       const int64_t a = (int64_t)uabs64(p[u][e4]);
       A = a > A ? a : A;
     }
   }
+  bound_raise(bad ? kBoundSwiglu : 0u);
   A = block_max(A, red);
   const int e = dq_exp((uint64_t)A);
 #pragma unroll
@@ -358,12 +366,14 @@ __global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__
     v4i gn[U], un[U];
     load(min(r + G, rows - 1), gn, un);  // next row (clamped: the last row reloads itself)
     int64_t p[U][4], A = 0;
+    uint32_t bad = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = RR::first(u) < n;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int64_t g = gv[u][e4];
+        if (ok) bad |= out_of(g, 24) | out_of(uv[u][e4], 24);
         const int64_t ag = g < 0 ? -g : g;
         const int E = min(diexp(-R(ag * Mg, Kg)), kSigEntries - 1);
         const int32_t q = tab[E];
@@ -373,6 +383,7 @@ __global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__
         A = a > A ? a : A;
       }
     }
+    bound_raise(bad ? kBoundSwiglu : 0u);
     A = block_max(A, red);
     const int e = dq_exp((uint64_t)A);
 #pragma unroll
@@ -440,16 +451,21 @@ __global__ __launch_bounds__(TPB) void embed_k(const int32_t* __restrict__ ids,
                                                int shift, int32_t* __restrict__ h) {
   const int r = blockIdx.x;
   const int64_t id = ids[r];
-  if (id < 0 || id >= V) {  // out-of-vocabulary id: zero row
+  if (id < 0 || id >= V) {  // out-of-vocabulary id: zero row, flagged
+    if (threadIdx.x == 0) bound_raise(kBoundId);
     for (int i = threadIdx.x; i < H; i += TPB) h[(size_t)r * H + i] = 0;
     return;
   }
   const int64_t m = emb_m[id];
+  uint32_t bad = 0;
   for (int i = threadIdx.x; i < H; i += TPB) {
     int64_t e = emb[id * H + i];
     if (emb_lo) e = 256 * e + (int64_t)emb_lo[id * H + i] + 128;
-    h[(size_t)r * H + i] = (int32_t)R(e * m, shift);
+    const int64_t v = R(e * m, shift);
+    bad |= out_of(v, 25);
+    h[(size_t)r * H + i] = (int32_t)v;
   }
+  bound_raise(bad ? kBoundResidual : 0u);
 }
 
 __global__ void rows_meta_k(const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
@@ -530,7 +546,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
   const int64_t c = p.cos_t[(size_t)pc * half + li], sn = p.sin_t[(size_t)pc * half + li];
   int64_t y0 = ok ? R(x0 * c - x1 * sn, 14) : 0;
   int64_t y1 = ok ? R(x1 * c + x0 * sn, 14) : 0;
-  const int kvh = isq ? hc / (nq / nkv) : (isv ? 0 : hc - nq);
+  const int kvh = isq ? hc >> (__builtin_ctz(nq) - __builtin_ctz(nkv)) : (isv ? 0 : hc - nq);
   const int g0 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j0] & 7 : 0;
   const int g1 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j1] & 7 : 0;
   if (isq) {  // the inverse of the key gain
@@ -633,6 +649,8 @@ __global__ void advance_k(int32_t* ids, const int32_t* next_tok, int32_t* start_
 bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 }  // namespace
+
+DETINT_BOUND_READER(bound_flags_rowops)
 
 hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int16_t* gain,
                           int64_t R, int64_t n, int8_t* x8, int32_t* row_m, int32_t* row_k,
@@ -1494,7 +1512,7 @@ __global__ __launch_bounds__(PT) void topk_pick_k(const uint64_t* __restrict__ c
       }
     }
     const int wp = expw_of((int32_t)(Lp ^ 0x80000000u), mx, t_m, t_k);  // > 0
-    take = take_top<PT, N>(key, take, Lp, (rest + wp - 1) / wp, wt);
+    take = take_top<PT, N>(key, take, Lp, (int)udiv32((uint32_t)(rest + wp - 1), (uint32_t)wp), wt);
     mine = weight_of(take);
   }
   int32_t D;
