@@ -547,9 +547,11 @@ hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, 
 
 hipError_t launch_fgemv_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
                            const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
-                           int32_t col_k, int32_t frac, int mode, void* out, hipStream_t st) {
+                           int32_t col_k, int32_t frac, int mode, void* out, hipStream_t st,
+                           int32_t res_bits) {
   FG p{};
   p.a8 = A; p.rm_in = row_m; p.rk_in = row_k; p.W = W; p.col_m = col_m; p.col_k = col_k;
+  p.res_bits = res_bits;
   p.frac = mode == MODE_REQ_I8 ? 0 : frac;
   p.M = (int)M; p.N = (int)N; p.K = (int)K; p.out = out;
   switch (mode) {

@@ -997,7 +997,7 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
   if (M <= 8 && K >= 16 && !W_lo && !e.out_row_base && fused_decode_supported(M, K) &&
       N * K < (int64_t(1) << 31) && ((uintptr_t)A & 3) == 0)
     return launch_fgemv_i8(A, W, M, N, K, e.row_m, e.row_k, e.col_m, e.col_k, e.frac, e.mode, out,
-                           st);
+                           st, e.res_bits);
   if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
   // buffer offsets are 32-bit
   const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);

@@ -200,7 +200,8 @@ hipError_t launch_fused_down(const int64_t* prod, int32_t f_a, const int8_t* W, 
 // no out_row_base).
 hipError_t launch_fgemv_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
                            const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
-                           int32_t col_k, int32_t frac, int mode, void* out, hipStream_t st);
+                           int32_t col_k, int32_t frac, int mode, void* out, hipStream_t st,
+                           int32_t res_bits = 0);
 hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, const int16_t* gain,
                                 const int8_t* E, const int32_t* emb_m, int32_t w_k, int32_t f_l,
                                 int64_t M, int64_t V, int64_t K, int32_t* logits,

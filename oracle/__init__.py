@@ -17,7 +17,9 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "detint_oracle.c"
-_LIB = _HERE / "liboracle.so"
+# DETINT_ORACLE_LIB selects another build of the same source (the test that
+# runs the oracle under UndefinedBehaviorSanitizer)
+_LIB = Path(os.environ.get("DETINT_ORACLE_LIB", str(_HERE / "liboracle.so")))
 
 # 16 bits of the cache layout etc. are fixed by the C code; these are the
 # epilogue modes it understands.
