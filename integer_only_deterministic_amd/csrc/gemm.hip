@@ -734,9 +734,11 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
   if (ks > 1) {
     // Partials go out as agent-scope atomic stores (coherent across the
     // XCDs' L2 caches). Ordering: every thread's stores happen before the
-    // workgroup barrier; thread 0's arrival is an acquire-release RMW at
-    // agent scope, so it publishes them (release) and, in the last split,
-    // makes every earlier split's partials visible (acquire); the second
+    // workgroup barrier; thread 0's arrival is a release RMW at agent scope,
+    // which publishes them. RMWs continue release sequences, so the split
+    // whose RMW reads ks - 1 has read every earlier split's release; its
+    // agent-scope acquire fence then synchronises with all of them (only
+    // the last split pays for the acquire's cache invalidation). The second
     // barrier carries that to the other threads, which read the partials
     // back with agent-scope atomic loads.
     auto put = [](int32_t* p, int32_t v) {
@@ -754,9 +756,12 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&sp.cnt[blockIdx.x], 1, __ATOMIC_ACQ_REL,
-                                      __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
+    if (tid == 0) {
+      const bool last = __hip_atomic_fetch_add(&sp.cnt[blockIdx.x], 1, __ATOMIC_RELEASE,
+                                               __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      s_last = last;
+    }
     __syncthreads();
     if (!s_last) return;
     const int32_t* all = sp.part + (size_t)blockIdx.x * ks * TE;
