@@ -373,6 +373,23 @@ detint_status detint_final_head(const int32_t *h, int64_t S, int64_t H, const in
                                 int64_t V, int32_t w_k, int32_t f_l, int32_t *logits,
                                 int32_t *next_tok, void *ws, int64_t ws_bytes, void *stream);
 
+/* detint_final_head for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments, without a workspace. Its
+ * scratch is a fixed DETINT_NOALLOC_SCRATCH_BYTES array in the library's
+ * device storage, one per GPU, held until the process ends; the call
+ * allocates nothing. It returns DETINT_EINVAL when
+ * detint_final_head_workspace(S, V, H) exceeds that size (e.g. up to 16 rows
+ * fit for V <= 262144, H <= 8192). Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+#define DETINT_NOALLOC_SCRATCH_BYTES (4 << 20)
+detint_status detint_final_head_noalloc(const int32_t *h, int64_t S, int64_t H,
+                                        const int16_t *gain, const int8_t *emb,
+                                        const int8_t *emb_lo, const int32_t *emb_m, int64_t V,
+                                        int32_t w_k, int32_t f_l, int32_t *logits,
+                                        int32_t *next_tok, void *stream);
+
 /* One decoder layer in place on the int32 residual h [R, hidden] (|h| <
  * 2^25), same sequence/cache arguments and workspace as detint_forward:
  * RMSNorm -> QKV -> (q/k-norm) -> RoPE -> q DQ, K/V into the cache ->

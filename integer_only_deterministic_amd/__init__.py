@@ -83,6 +83,7 @@ _SIGS = {
     "detint_sample_workspace": (i64, [i64, i64]),
     "detint_final_head_workspace": (i64, [i64, i64, i64]),
     "detint_final_head": (i32, [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, vp]),
+    "detint_final_head_noalloc": (i32, [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp, vp]),
     "detint_layer_forward": (i32, [vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64, i64, vp, i64,
                                    vp]),
 }
@@ -286,6 +287,24 @@ def detint_final_head(h, gain, emb, emb_lo, emb_m, w_k, f_l, logits=None, next_t
           int(w_k), int(f_l), _p(logits, torch.int32), _p(next_tok, torch.int32) if with_token else None,
           _p(ws),
           ws.numel() * ws.element_size(), _stream())
+    return logits, next_tok
+
+
+def detint_final_head_noalloc(h, gain, emb, emb_lo, emb_m, w_k, f_l, logits=None, next_tok=None,
+                              with_token=True):
+    """detint_final_head without a workspace (the library's per-device
+    scratch; see detint.h)."""
+    torch = _torch()
+    S_, H = h.shape
+    V = emb.shape[0]
+    if logits is None:
+        logits = torch.empty((S_, V), dtype=torch.int32, device=h.device)
+    if next_tok is None and with_token:
+        next_tok = torch.empty(S_, dtype=torch.int32, device=h.device)
+    _call("detint_final_head_noalloc", _p(h, torch.int32), S_, H, _p(gain, torch.int16),
+          _p(emb, torch.int8), _p(emb_lo, torch.int8) if emb_lo is not None else None,
+          _p(emb_m, torch.int32), V, int(w_k), int(f_l), _p(logits, torch.int32),
+          _p(next_tok, torch.int32) if with_token else None, _stream())
     return logits, next_tok
 
 

@@ -317,6 +317,64 @@ detint_status detint_final_head(const int32_t* h, int64_t S, int64_t H, const in
                     "final_head argmax");
 }
 
+// ------------------------------------------------ allocation-free final head
+
+// Scratch of detint_final_head_noalloc: file-scope device storage, one copy
+// on every GPU the library runs on, held until the process ends. Host code
+// never uses this name as an address: each device's address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[DETINT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// This device's address of `scratch` (looked up on the first call per device).
+detint_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "final_head_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DETINT_EUNSUPPORTED, "final_head_noalloc: device %d beyond %d", dev, kMaxDevices);
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess || !s.ptr)
+    return hip_status(s.err != hipSuccess ? s.err : hipErrorInvalidSymbol,
+                      "final_head_noalloc: hipGetSymbolAddress(scratch)");
+  *ptr = s.ptr;
+  return ok();
+}
+}  // namespace
+
+detint_status detint_final_head_noalloc(const int32_t* h, int64_t S, int64_t H,
+                                        const int16_t* gain, const int8_t* emb,
+                                        const int8_t* emb_lo, const int32_t* emb_m, int64_t V,
+                                        int32_t w_k, int32_t f_l, int32_t* logits,
+                                        int32_t* next_tok, void* stream) {
+  REQUIRE(S >= 0 && H > 0 && V >= 0, "final_head_noalloc: bad sizes");
+  if (S == 0 || V == 0) return ok();
+  const int64_t need = detint_final_head_workspace(S, V, H);
+  if (need < 0 || need > DETINT_NOALLOC_SCRATCH_BYTES)
+    return fail(DETINT_EINVAL,
+                "final_head_noalloc: S=%lld V=%lld H=%lld needs %lld scratch bytes, more than "
+                "the %lld held per device (use detint_final_head with a workspace)",
+                (long long)S, (long long)V, (long long)H, (long long)need,
+                (long long)DETINT_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const detint_status st = scratch_of_current_device(&ws);
+  if (st != DETINT_OK) return st;
+  // every kernel of the final head writes the scratch it later reads (argmax
+  // partials for all parts, the normalised rows and their scales), so
+  // nothing needs clearing between calls
+  return detint_final_head(h, S, H, gain, emb, emb_lo, emb_m, V, w_k, f_l, logits, next_tok, ws,
+                           DETINT_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 detint_status detint_argmax_parts(const int64_t* part, int64_t S, int64_t nparts,
                                   int32_t* next_tok, void* stream) {
   REQUIRE(S >= 0 && nparts > 0, "argmax_parts: bad sizes");
