@@ -33,6 +33,7 @@ import numpy as np
 __all__ = [
     "ModelShape", "SHAPES", "make_model", "make_prompt", "make_prompts",
     "make_residual", "make_gemm_operands", "GEMM_SWEEP_M", "GEMM_SWEEP_KN",
+    "make_bf16_weights", "bf16_to_float64",
     "model_digest",
 ]
 
@@ -269,6 +270,29 @@ def make_residual(rows: int, hidden: int, seed: int) -> np.ndarray:
     """int32 residual rows uniform in [-2^15, 2^15)."""
     return _rng(seed, 9003).integers(-(1 << 15), 1 << 15, (rows, hidden),
                                      dtype=np.int64).astype(np.int32)
+
+
+def make_bf16_weights(N: int, K: int, seed: int, sigma: float = 0.02,
+                      max_span: int = 23) -> np.ndarray:
+    """bf16 bit patterns [N, K] (uint16) of N(0, sigma) draws, rounded to the
+    nearest bf16 (ties to even) with integer operations on the float32 bit
+    patterns. Entries more than max_span binary orders below their row's
+    largest exponent are set to +0: the stand-in for trained bf16 weights
+    keeps every row within the exponent span that the exact-mode integers
+    hold (the arithmetic itself is exact for whatever bf16 values it gets)."""
+    x = _rng(seed, N, K, 16).standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    E = ((b >> 7) & 255).astype(np.int32)
+    emax = E.max(axis=1, keepdims=True)
+    b[E < emax - max_span] = 0
+    return b
+
+
+def bf16_to_float64(bits: np.ndarray) -> np.ndarray:
+    """Exact real values of bf16 bit patterns (a bf16 is the top half of a
+    float32)."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def make_gemm_operands(M: int, N: int, K: int, seed: int) -> dict:

@@ -125,6 +125,10 @@ def _declare(L):
                               i8p, i8p, i64, i32, i32p, vp]
     L.orc_argmax.argtypes = [i32p, i64, i64, i32p]
     L.orc_sample.argtypes = [i32p, i64, i64, i64, i32, i32, i32, u32p, i32p]
+    u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+    L.orc_exact_weights.argtypes = [u16p, i64, i64, i32p, i32p]
+    L.orc_gemm_exact.argtypes = [i8p, i32p, i64, i64, i64, i64p]
+    L.orc_exact_epilogue.argtypes = [i64p, i64, i64, i32p, i32p, i32p, i32, i32, vp]
     L.orc_attention.argtypes = [i8p, i32p, i8p, i8p, i32p, i32p, i64, i64, i64, i64, i64, i64,
                                 i32, i32, i32p]
 
@@ -251,6 +255,37 @@ def gemm_i8(A, W, row_m=None, row_k=None, col_m=None, col_k=0, frac=0, mode=RAW,
     if mode == RAW:
         return epilogue(acc, np.zeros(M), np.zeros(M), np.zeros(N), 0, 0, RAW)
     return epilogue(acc, row_m, row_k, col_m, col_k, frac, mode, out)
+
+
+def exact_weights(Wbits):
+    """bf16 bit patterns [N, K] (uint16) -> (W_int int32 [N, K], row_exp int32
+    [N]) with w = W_int * 2^row_exp exactly (orc_exact_weights)."""
+    Wbits = _c(Wbits, np.uint16)
+    N, K = Wbits.shape
+    W_int = np.zeros((N, K), np.int32)
+    row_exp = np.zeros(N, np.int32)
+    lib().orc_exact_weights(Wbits, N, K, W_int, row_exp); _check()
+    return W_int, row_exp
+
+
+def gemm_exact(A, W_int) -> np.ndarray:
+    A = _c(A, np.int8)
+    W_int = _c(W_int, np.int32)
+    M, K = A.shape
+    N = W_int.shape[0]
+    acc = np.zeros((M, N), np.int64)
+    lib().orc_gemm_exact(A, W_int, M, N, K, acc); _check()
+    return acc
+
+
+def exact_epilogue(acc, row_m, row_k, row_exp, frac: int, mode: int):
+    acc = _c(acc, np.int64)
+    M, N = acc.shape
+    out = np.zeros((M, N), {RAW: np.int64, REQ_I8: np.int8, FIX: np.int32}[mode])
+    lib().orc_exact_epilogue(acc, M, N, _c(row_m, np.int32), _c(row_k, np.int32),
+                             _c(row_exp, np.int32), int(frac), int(mode), out.ctypes.data)
+    _check()
+    return out
 
 
 def rmsnorm(h, g):

@@ -290,6 +290,99 @@ int orc_epilogue(const int64_t *acc, int64_t M, int64_t N,
 }
 
 /* ------------------------------------------------------------------ */
+/* exact mode: bf16 weights as fixed point                             */
+
+/* Exact-mode weights ([BITEXACT] "Three execution paths": exact mode keeps
+ * the original bf16 weights of the linear layers and multiplies them with
+ * fixed-point activations; "Fix the arithmetic": products split into integer
+ * limbs and combined in wide accumulators). A bf16 pattern (sign s, 8-bit
+ * exponent field E, 7-bit fraction f) is the real number (-1)^s * M *
+ * 2^(E' - 134), with M = 128 + f and E' = E for E >= 1 (normal numbers), M = f
+ * and E' = 1 for E = 0 (zero and subnormals); E = 255 (infinity, NaN) has no
+ * integer form and is an error. Reading taken (the pages state no format):
+ * each output channel (row j of W [N, K]) gets a power-of-two scale, the
+ * smallest E' among its nonzero entries (emin_j; 1 for an all-zero row), and
+ * its integers W_int[j][k] = (-1)^s * M * 2^(E'_k - emin_j), so that
+ * w[j][k] = W_int[j][k] * 2^row_exp[j] exactly with row_exp[j] = emin_j - 134.
+ * Bound: |W_int| < 2^31, i.e. exponents within a row span at most 23. */
+int orc_exact_weights(const uint16_t *W, int64_t N, int64_t K, int32_t *W_int, int32_t *row_exp) {
+  for (int64_t j = 0; j < N; j++) {
+    const uint16_t *w = W + j * K;
+    int emin = 255;
+    for (int64_t k = 0; k < K; k++) {
+      const int E = (w[k] >> 7) & 255, f = w[k] & 127;
+      CHECK(E != 255, "exact weights: infinity or NaN");
+      const int Ep = E ? E : 1, M = E ? 128 + f : f;
+      if (M != 0 && Ep < emin) emin = Ep;
+    }
+    if (emin == 255) emin = 1;   /* all zeros */
+    for (int64_t k = 0; k < K; k++) {
+      const int E = (w[k] >> 7) & 255, f = w[k] & 127;
+      const int Ep = E ? E : 1, M = E ? 128 + f : f;
+      int64_t v = 0;
+      if (M != 0 && E != 255) {
+        CHECK(Ep - emin <= 23, "exact weights: exponents of a row span more than 23");
+        v = (Ep - emin <= 23) ? (int64_t)M << (Ep - emin) : 0;
+      }
+      W_int[j * K + k] = (int32_t)((w[k] & 0x8000) ? -v : v);
+    }
+    row_exp[j] = emin - 134;
+  }
+  return g_err;
+}
+
+/* acc[i][j] = sum_k A[i][k] * W_int[j][k], exactly (int8 activations times
+ * the exact-mode integers; |acc| < 2^7 * 2^31 * K must fit int64). */
+int orc_gemm_exact(const int8_t *A, const int32_t *W_int, int64_t M, int64_t N, int64_t K,
+                   int64_t *acc) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < N; j++)
+    for (int64_t i = 0; i < M; i++) {
+      i128 s = 0;
+      for (int64_t k = 0; k < K; k++) s += (i128)A[i * K + k] * W_int[j * K + k];
+      CHECK(s <= INT64_MAX && s >= INT64_MIN, "exact acc exceeds int64");
+      acc[i * N + j] = (int64_t)s;
+    }
+  return g_err;
+}
+
+/* Dyadic epilogue of an exact-mode product. Row i of the activations stands
+ * for x8 * m_r * 2^-k_r and column j's weights for W_int * 2^row_exp[j], so
+ * the real output is acc * m_r * 2^(row_exp[j] - k_r):
+ *   RAW     out_i64 = acc
+ *   REQ_I8  out_i8  = clamp8(R(acc * m_r, k_r - row_exp[j]))
+ *   FIX     out_i32 = R(acc * m_r, k_r - row_exp[j] - frac) (must fit int32) */
+int orc_exact_epilogue(const int64_t *acc, int64_t M, int64_t N, const int32_t *row_m,
+                       const int32_t *row_k, const int32_t *row_exp, int32_t frac, int32_t mode,
+                       void *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; i++)
+    for (int64_t j = 0; j < N; j++) {
+      const int64_t a = acc[i * N + j];
+      if (mode == ORC_RAW) {
+        ((int64_t *)out)[i * N + j] = a;
+        continue;
+      }
+      const int sh = row_k[i] - row_exp[j] - (mode == ORC_REQ_I8 ? 0 : frac);
+      const i128 p = (i128)a * row_m[i];
+      int64_t y;
+      if (sh > 120) {
+        y = 0;
+      } else {
+        CHECK(sh > -62, "exact epilogue left shift");
+        y = R128(p, sh);
+      }
+      if (mode == ORC_REQ_I8) {
+        ((int8_t *)out)[i * N + j] = clamp8(y);
+      } else {
+        CHECK(y <= INT32_MAX && y >= INT32_MIN, "exact fix output exceeds int32");
+        ((int32_t *)out)[i * N + j] = (int32_t)y;
+      }
+    }
+  return g_err;
+}
+
+/* ------------------------------------------------------------------ */
 /* row ops                                                             */
 
 /* DI-RMSNorm of one row ([README] "Layout": ops/ DI-RMSNorm). The output

@@ -366,3 +366,36 @@ def test_decode_attention_long_context_matches_prefill(D, nq, nkv, d, qkn):
     assert int(host(t1)[0]) == int(toks[r])
     dm1.decode(t1, [len(prompts[r])], [0], 1, one, 0, use_graph=False)
     np.testing.assert_array_equal(host(one)[0], reference(r), err_msg="batch-1 row")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wide"])
+def test_mixed_prefill_and_decode_rows_in_one_call(D, name):
+    """BitExact LLM blog, "What the checks actually compare": mixed requests.
+    One detint_forward call carries a decode row of sequence A (one token at
+    its next position), the first prefill chunk of a new sequence B and the
+    second chunk of sequence C, each in its own cache slot. Every row's
+    logits equal the oracle's for that sequence run alone, and the caches
+    equal the oracle's."""
+    import torch
+    m = S.make_model(name, seed=61)
+    V = m.shape.vocab
+    a, b, c = S.make_prompt(V, 30, 71), S.make_prompt(V, 23, 72), S.make_prompt(V, 41, 73)
+    # oracle: each sequence alone in its slot
+    om = O.OracleModel(m, slots=3)
+    _, ta = om.forward(a, [30], [0], [0])
+    want_a, _ = om.forward(ta, [1], [30], [0])
+    want_b, _ = om.forward(b, [23], [0], [1])
+    om.forward(c[:20], [20], [0], [2])
+    want_c, _ = om.forward(c[20:], [21], [20], [2])
+    # GPU: A prefilled and C's first chunk beforehand, then one mixed call
+    dm = D.DetintModel(m, n_slots=3)
+    scratch = torch.zeros((2, V), dtype=torch.int32, device="cuda")
+    tok_a = host(dm.prefill([a, c[:20]], [0, 0], [0, 2], scratch, 0))[0]
+    assert tok_a == int(ta[0])
+    logits, _ = dm.forward(np.concatenate([[tok_a], b, c[20:]]).astype(np.int32), [1, 23, 21],
+                           [30, 0, 20], [0, 1, 2])
+    np.testing.assert_array_equal(logits[0], want_a[0], err_msg="decode row")
+    np.testing.assert_array_equal(logits[1], want_b[0], err_msg="new prefill")
+    np.testing.assert_array_equal(logits[2], want_c[0], err_msg="second chunk")
+    np.testing.assert_array_equal(host(dm.kc), om.kc)
+    np.testing.assert_array_equal(host(dm.vc), om.vc)
