@@ -72,7 +72,8 @@ const char *detint_version(void);
  *             value or a rotated q/k left int32;
  *   NORM      an RMSNorm row's sum of squares reached 2^62;
  *   SWIGLU    a SwiGLU gate or up value left |x| < 2^24;
- *   ID        a token id outside [0, vocab) (its row is embedded as zeros).
+ *   ID        a token id outside [0, vocab) (its row is embedded as zeros);
+ *   WEIGHT    a bf16 weight exact mode cannot hold (detint_exact_prepare).
  * detint_check waits for `stream` (everything enqueued on it so far), then
  * reads and clears the current device's flags (set by any call on any
  * stream of that device since the last check): *flags (nullable) receives
@@ -84,6 +85,7 @@ const char *detint_version(void);
 #define DETINT_BOUND_NORM 4u
 #define DETINT_BOUND_SWIGLU 8u
 #define DETINT_BOUND_ID 16u
+#define DETINT_BOUND_WEIGHT 32u  /* a bf16 weight exact mode cannot hold */
 detint_status detint_check(void *stream, uint32_t *flags);
 /* Message of the last error returned on the calling thread ("" if none). */
 const char *detint_last_error(void);
@@ -119,6 +121,41 @@ detint_status detint_gemm_w16(const int8_t *A, const int8_t *W_hi, const int8_t 
                               const int32_t *row_m, const int32_t *row_k,
                               const int32_t *col_m, int32_t col_k, int32_t frac,
                               int32_t mode, void *out, void *stream);
+
+/* Exact mode (BitExact LLM blog, "Three execution paths": the linear layers
+ * keep their bf16 weights, multiplied with fixed-point activations; "Fix the
+ * arithmetic": integer limbs, wide accumulators). A bf16 pattern (sign s,
+ * exponent field E, fraction f) is (-1)^s M 2^(E' - 134) with M = 128 + f,
+ * E' = E (E >= 1), or M = f, E' = 1 (E = 0). Row j of W [N, K] becomes the
+ * integers W_int = (-1)^s M 2^(E' - emin_j), emin_j the smallest E' among the
+ * row's nonzero entries (1 for an all-zero row), and the row scale
+ * 2^row_exp[j] with row_exp[j] = emin_j - 134: w = W_int 2^row_exp exactly.
+ * |W_int| < 2^31: a row may span at most 23 binary orders.
+ *
+ * detint_exact_prepare: W uint16 [N, K] bf16 bit patterns (device) ->
+ *   planes int8 [4][N][K] (P0 = W_int >> 24, P1..P3 = its next bytes minus
+ *   128; W_int = 2^24 P0 + 2^16 P1 + 2^8 P2 + P3 + 128 (2^16 + 2^8 + 1)) and
+ *   row_exp int32 [N]. A weight the integers cannot hold (infinity, NaN, a
+ *   wider span) sets the DETINT_BOUND_WEIGHT flag (see detint_check) and is
+ *   written as 0.
+ * detint_gemm_exact: acc[i][j] = sum_k A[i][k] W_int[j][k] (int64, exact;
+ *   computed as 2^16 (A.H16) + A.L16 + 2^15 rowsum(A) with the two 16-bit
+ *   halves on the limb GEMM), then with the activation row scale
+ *   x8 m_r 2^-k_r the real output acc m_r 2^(row_exp[j] - k_r):
+ *     RAW     out int64 [M, N] = acc
+ *     REQ_I8  out int8  = clamp8(R(acc m_r, k_r - row_exp[j]))
+ *     FIX     out int32 = R(acc m_r, k_r - row_exp[j] - frac)  (DETINT_BOUND_INT32
+ *             when outside int32)
+ *   A int8 [M, K] (16-byte aligned, K % 16 == 0, K <= 65536); row_m, row_k
+ *   int32 [M] (ignored by RAW); ws: device workspace of
+ *   detint_gemm_exact_workspace(M, N) bytes, 16-byte aligned. */
+detint_status detint_exact_prepare(const uint16_t *W, int64_t N, int64_t K, int8_t *planes,
+                                   int32_t *row_exp, void *stream);
+int64_t detint_gemm_exact_workspace(int64_t M, int64_t N);
+detint_status detint_gemm_exact(const int8_t *A, const int8_t *planes, const int32_t *row_exp,
+                                int64_t M, int64_t N, int64_t K, const int32_t *row_m,
+                                const int32_t *row_k, int32_t frac, int32_t mode, void *out,
+                                void *ws, int64_t ws_bytes, void *stream);
 
 /* Split int16 weights [n] into the two limb planes used by detint_gemm_w16. */
 detint_status detint_split_w16(const int16_t *W16, int64_t n, int8_t *W_hi, int8_t *W_lo,

@@ -17,7 +17,7 @@ _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libdetint.so"
 
 DETINT_OK, DETINT_EINVAL, DETINT_EUNSUPPORTED, DETINT_EHIP, DETINT_EBOUND = 0, 1, 2, 3, 4
-BOUND_RESIDUAL, BOUND_INT32, BOUND_NORM, BOUND_SWIGLU, BOUND_ID = 1, 2, 4, 8, 16
+BOUND_RESIDUAL, BOUND_INT32, BOUND_NORM, BOUND_SWIGLU, BOUND_ID, BOUND_WEIGHT = 1, 2, 4, 8, 16, 32
 RAW, REQ_I8, FIX, RES_ADD = 0, 1, 2, 3
 FWD_ADVANCE = 1
 
@@ -58,6 +58,9 @@ _SIGS = {
     "detint_gemm_i8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
     "detint_gemm_w16": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
     "detint_split_w16": (i32, [vp, i64, vp, vp, vp]),
+    "detint_exact_prepare": (i32, [vp, i64, i64, vp, vp, vp]),
+    "detint_gemm_exact_workspace": (i64, [i64, i64]),
+    "detint_gemm_exact": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp]),
     "detint_rmsnorm": (i32, [vp, vp, i64, i64, vp, vp, vp, vp]),
     "detint_requant": (i32, [vp, i64, i64, vp, vp, vp]),
     "detint_rope": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, vp]),
@@ -178,6 +181,34 @@ def detint_split_w16(W16):
     lo = torch.empty(W16.shape, dtype=torch.int8, device=W16.device)
     _call("detint_split_w16", _p(W16, torch.int16), W16.numel(), _p(hi), _p(lo), _stream())
     return hi, lo
+
+
+def detint_exact_prepare(W_bits):
+    """bf16 bit patterns [N, K] (a 16-bit device tensor) -> (planes int8
+    [4, N, K], row_exp int32 [N]): exact-mode weights (see detint.h)."""
+    torch = _torch()
+    N, K = W_bits.shape
+    if W_bits.element_size() != 2:
+        raise TypeError("expected 16-bit bf16 bit patterns")
+    planes = torch.empty((4, N, K), dtype=torch.int8, device=W_bits.device)
+    row_exp = torch.empty(N, dtype=torch.int32, device=W_bits.device)
+    _call("detint_exact_prepare", _p(W_bits), N, K, _p(planes), _p(row_exp), _stream())
+    return planes, row_exp
+
+
+def detint_gemm_exact(A, planes, row_exp, row_m=None, row_k=None, frac=0, mode=RAW, out=None, ws=None):
+    torch = _torch()
+    M, K = A.shape
+    N = planes.shape[1]
+    if out is None:
+        dt = {RAW: torch.int64, REQ_I8: torch.int8}.get(mode, torch.int32)
+        out = torch.empty((M, N), dtype=dt, device=A.device)
+    need = library().detint_gemm_exact_workspace(M, N)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A.device)
+    _call("detint_gemm_exact", _p(A, torch.int8), _p(planes, torch.int8), _p(row_exp, torch.int32), M, N,
+          K, _p(row_m), _p(row_k), int(frac), int(mode), _p(out), _p(ws), ws.numel(), _stream())
+    return out
 
 
 def detint_rmsnorm(h, gain):

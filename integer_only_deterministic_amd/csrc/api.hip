@@ -130,6 +130,39 @@ detint_status detint_gemm_w16(const int8_t* A, const int8_t* W_hi, const int8_t*
   return hip_status(launch_gemm(A, W_hi, W_lo, M, N, K, e, out, S_(stream)), "gemm_w16 launch");
 }
 
+detint_status detint_exact_prepare(const uint16_t* W, int64_t N, int64_t K, int8_t* planes,
+                                   int32_t* row_exp, void* stream) {
+  REQUIRE(N >= 0 && K > 0 && N * K < ((int64_t)1 << 40), "exact_prepare: bad shape");
+  if (N == 0) return ok();
+  REQUIRE(W && planes && row_exp, "exact_prepare: null pointer");
+  return hip_status(launch_exact_prepare(W, N, K, planes, row_exp, S_(stream)),
+                    "exact_prepare launch");
+}
+
+int64_t detint_gemm_exact_workspace(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return -1;
+  return 8 * (2 * M * N + M) + 256;
+}
+
+detint_status detint_gemm_exact(const int8_t* A, const int8_t* planes, const int32_t* row_exp,
+                                int64_t M, int64_t N, int64_t K, const int32_t* row_m,
+                                const int32_t* row_k, int32_t frac, int32_t mode, void* out,
+                                void* ws, int64_t ws_bytes, void* stream) {
+  REQUIRE(mode == DETINT_GEMM_RAW || mode == DETINT_GEMM_REQ_I8 || mode == DETINT_GEMM_FIX,
+          "gemm_exact: mode must be RAW, REQ_I8 or FIX");
+  detint_status s = check_gemm(A, planes, M, N, K, row_m, row_k, row_exp, mode, out, 65536);
+  if (s != DETINT_OK || M == 0 || N == 0) return s;
+  REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && M * N < ((int64_t)1 << 40),
+          "gemm_exact: M or N too large");
+  REQUIRE(row_exp, "gemm_exact: null row_exp");
+  REQUIRE(ws && aligned16(ws) && ws_bytes >= detint_gemm_exact_workspace(M, N),
+          "gemm_exact: workspace of %lld bytes needed", (long long)detint_gemm_exact_workspace(M, N));
+  REQUIRE(aligned16(planes + N * K), "gemm_exact: N * K must keep the planes 16-byte aligned");
+  return hip_status(launch_gemm_exact(A, planes, row_exp, M, N, K, row_m, row_k, frac, mode, out,
+                                      (int64_t*)ws, S_(stream)),
+                    "gemm_exact launch");
+}
+
 detint_status detint_split_w16(const int16_t* W16, int64_t n, int8_t* W_hi, int8_t* W_lo,
                                void* stream) {
   REQUIRE(n >= 0, "split_w16: n < 0");

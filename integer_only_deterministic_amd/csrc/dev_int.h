@@ -50,6 +50,7 @@ enum : uint32_t {
   kBoundNorm = 4u,      // RMSNorm row with sum of squares >= 2^62
   kBoundSwiglu = 8u,    // SwiGLU gate or up outside (-2^24, 2^24)
   kBoundId = 16u,       // token id outside [0, vocab)
+  kBoundWeight = 32u,   // a bf16 weight the exact-mode integers cannot hold
 };
 static __device__ uint32_t g_bound_flags;
 

@@ -984,6 +984,123 @@ __global__ void split_w16(const int16_t* __restrict__ w, int64_t n, int8_t* __re
   }
 }
 
+// ------------------------------------------------------------- exact mode
+//
+// bf16 weights as integers (BitExact blog, "Three execution paths": exact
+// mode keeps the bf16 weights and multiplies them with fixed-point
+// activations). Row j's values are W_int = +-M * 2^(E' - emin_j) with M the
+// 8-bit significand (implicit one for normal numbers), E' the exponent field
+// (1 for subnormals) and emin_j the row's smallest E' among nonzero entries;
+// the row scale is 2^(emin_j - 134). |W_int| < 2^31 (a row spans at most 23
+// binary orders), held as four int8 planes: P0 = W_int >> 24 (signed) and
+// P1..P3 = the next bytes minus 128, so that
+//   W_int = 2^24 P0 + 2^16 P1 + 2^8 P2 + P3 + 128 (2^16 + 2^8 + 1).
+// (P0, P1) and (P2, P3) are the limb planes of the 16-bit GEMM for
+// H16 = W_int >> 16 and L16 = (W_int & 65535) - 32768; the product is
+// acc = 2^16 (A.H16) + A.L16 + 2^15 rowsum(A), exact in int64.
+
+__device__ __forceinline__ int block_min_int(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int w = __shfl_xor(v, o);
+    v = w < v ? w : v;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = red[w] < v ? red[w] : v;
+    red[0] = v;
+  }
+  __syncthreads();
+  v = red[0];
+  __syncthreads();
+  return v;
+}
+
+// one 256-thread workgroup per weight row
+__global__ __launch_bounds__(256) void exact_prepare_k(const uint16_t* __restrict__ W, int K,
+                                                       int8_t* __restrict__ planes, int64_t plane,
+                                                       int32_t* __restrict__ row_exp) {
+  __shared__ int red[4];
+  const int64_t j = blockIdx.x;
+  const uint16_t* w = W + j * K;
+  int emin = 255;
+  uint32_t bad = 0;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const int b = w[k], E = (b >> 7) & 255, f = b & 127;
+    const int Ep = E ? E : 1, M = E ? 128 + f : f;
+    if (E == 255) bad = kBoundWeight;
+    if (M != 0 && Ep < emin) emin = Ep;
+  }
+  emin = block_min_int(emin, red);
+  if (emin == 255) emin = 1;  // an all-zero row
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const int b = w[k], E = (b >> 7) & 255, f = b & 127;
+    const int Ep = E ? E : 1, M = E ? 128 + f : f;
+    int32_t v = 0;
+    if (M != 0 && E != 255) {
+      if (Ep - emin > 23) bad = kBoundWeight;
+      else v = M << (Ep - emin);
+    }
+    if (b & 0x8000) v = -v;
+    const int64_t o = j * K + k;
+    planes[o] = (int8_t)(v >> 24);
+    planes[plane + o] = (int8_t)(((v >> 16) & 255) - 128);
+    planes[2 * plane + o] = (int8_t)(((v >> 8) & 255) - 128);
+    planes[3 * plane + o] = (int8_t)((v & 255) - 128);
+  }
+  bound_raise(bad);
+  if (threadIdx.x == 0) row_exp[j] = emin - 134;
+}
+
+// rowsum(A) for M rows of K int8 (one workgroup per row)
+__global__ __launch_bounds__(256) void exact_rowsum_k(const int8_t* __restrict__ A, int K,
+                                                      int64_t* __restrict__ rs) {
+  __shared__ int64_t red[16];
+  const int8_t* a = A + (int64_t)blockIdx.x * K;
+  int64_t s = 0;
+  for (int k = threadIdx.x; k < K; k += 256) s += a[k];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) rs[blockIdx.x] = s;
+}
+
+// acc = 2^16 hi + lo + 2^15 rowsum, then the exact-mode epilogue: the real
+// output is acc * m_r * 2^(row_exp[j] - k_r)
+__global__ __launch_bounds__(256) void exact_combine_k(const int64_t* __restrict__ hi,
+                                                       const int64_t* __restrict__ lo,
+                                                       const int64_t* __restrict__ rs, int M, int N,
+                                                       const int32_t* __restrict__ row_m,
+                                                       const int32_t* __restrict__ row_k,
+                                                       const int32_t* __restrict__ row_exp,
+                                                       int32_t frac, int mode, void* out) {
+  const int j = blockIdx.x * 256 + threadIdx.x;  // column; rows i = y, y + gridDim.y, ...
+  if (j >= N) return;
+  uint32_t bad = 0;
+  for (int i = blockIdx.y; i < M; i += gridDim.y) {
+    const int64_t t = (int64_t)i * N + j;
+    const int64_t acc = 65536 * hi[t] + lo[t] + 32768 * rs[i];
+    if (mode == MODE_RAW) {
+      ((int64_t*)out)[t] = acc;
+      continue;
+    }
+    const int s = row_k[i] - row_exp[j] - (mode == MODE_REQ_I8 ? 0 : frac);
+    const __int128 p = (__int128)acc * row_m[i];
+    int64_t y = 0;
+    if (s <= 120) {
+      if (s <= -62) bad |= kBoundInt32;
+      else y = R128(p, s);
+    }
+    if (mode == MODE_REQ_I8) {
+      ((int8_t*)out)[t] = clamp8(y);
+    } else {
+      bad |= i32_check(y);
+      ((int32_t*)out)[t] = (int32_t)y;
+    }
+  }
+  bound_raise(bad);
+}
+
 }  // namespace
 
 bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs) {
@@ -1030,6 +1147,33 @@ hipError_t launch_logits_argmax(const int8_t* A, const int8_t* W, const int8_t* 
                                 int64_t* part, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   return gemv_dispatch(A, W, W_lo, M, N, K, e, logits, part, st);
+}
+
+hipError_t launch_exact_prepare(const uint16_t* W, int64_t N, int64_t K, int8_t* planes,
+                                int32_t* row_exp, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  exact_prepare_k<<<(unsigned)N, 256, 0, st>>>(W, (int)K, planes, N * K, row_exp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_exact(const int8_t* A, const int8_t* planes, const int32_t* row_exp,
+                             int64_t M, int64_t N, int64_t K, const int32_t* row_m,
+                             const int32_t* row_k, int32_t frac, int32_t mode, void* out,
+                             int64_t* ws, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  int64_t* hi = ws;
+  int64_t* lo = ws + M * N;
+  int64_t* rs = ws + 2 * M * N;
+  const int64_t plane = N * K;
+  const Epi raw{nullptr, nullptr, nullptr, 0, 0, MODE_RAW, nullptr};
+  hipError_t e = launch_gemm(A, planes, planes + plane, M, N, K, raw, hi, st);
+  if (e == hipSuccess) e = launch_gemm(A, planes + 2 * plane, planes + 3 * plane, M, N, K, raw, lo, st);
+  if (e != hipSuccess) return e;
+  exact_rowsum_k<<<(unsigned)M, 256, 0, st>>>(A, (int)K, rs);
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
+  exact_combine_k<<<grid, 256, 0, st>>>(hi, lo, rs, (int)M, (int)N, row_m, row_k, row_exp, frac,
+                                        mode, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,

@@ -60,6 +60,14 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
 bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs);
 hipError_t launch_split_w16(const int16_t* W16, int64_t n, int8_t* hi, int8_t* lo,
                             hipStream_t st);
+// Exact mode (bf16 weights as integers): planes int8 [4][N][K], row_exp [N];
+// the GEMM's workspace holds 2 M N + M int64 (two limb products, row sums).
+hipError_t launch_exact_prepare(const uint16_t* W, int64_t N, int64_t K, int8_t* planes,
+                                int32_t* row_exp, hipStream_t st);
+hipError_t launch_gemm_exact(const int8_t* A, const int8_t* planes, const int32_t* row_exp,
+                             int64_t M, int64_t N, int64_t K, const int32_t* row_m,
+                             const int32_t* row_k, int32_t frac, int32_t mode, void* out,
+                             int64_t* ws, hipStream_t st);
 // lm_head for M <= 16 rows: FIX-mode logits plus per-wave greedy-argmax
 // partials part[M][logits_argmax_parts(N)] (reduce with launch_argmax_final).
 int64_t logits_argmax_parts(int64_t N);
