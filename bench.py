@@ -206,9 +206,10 @@ def decode_run(D, dm, prompts, warmup, steps, torch):
 
 
 def gemm_sweep(D, S, torch):
-    """The 25-shape int8 GEMM sweep, per-row x per-column requant to int8.
-    M >= 512: TOP/s against the i8 MFMA peak (back-to-back launches);
-    M <= 64: GB/s against HBM, each launch cache-cold."""
+    """The 25-shape int8 GEMM sweep, per-row x per-column requant to int8,
+    each call with the workspace detint_gemm_workspace asks for (split-K on
+    few-tile shapes). M >= 512: TOP/s against the i8 MFMA peak (back-to-back
+    launches); M <= 64: GB/s against HBM, each launch cache-cold."""
     res = {}
     for Kd, Nd in S.GEMM_SWEEP_KN:
         g = S.make_gemm_operands(max(S.GEMM_SWEEP_M), Nd, Kd, seed=7)
@@ -218,7 +219,9 @@ def gemm_sweep(D, S, torch):
         for M in S.GEMM_SWEEP_M:
             out = torch.empty((M, Nd), dtype=torch.int8, device="cuda")
             Am, rmm, rkm = A[:M], rm[:M], rk[:M]
-            f = lambda: D.detint_gemm_i8(Am, Wt, rmm, rkm, cm, g["col_k"], 0, D.REQ_I8, out)
+            need = D.detint_gemm_workspace(M, Nd, Kd)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+            f = lambda: D.detint_gemm_i8(Am, Wt, rmm, rkm, cm, g["col_k"], 0, D.REQ_I8, out, ws=ws)
             for _ in range(3):
                 f()
             key = f"M{M}_K{Kd}_N{Nd}"

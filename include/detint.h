@@ -73,7 +73,8 @@ const char *detint_version(void);
  *   NORM      an RMSNorm row's sum of squares reached 2^62;
  *   SWIGLU    a SwiGLU gate or up value left |x| < 2^24;
  *   ID        a token id outside [0, vocab) (its row is embedded as zeros);
- *   WEIGHT    a bf16 weight exact mode cannot hold (detint_exact_prepare).
+ *   WEIGHT    a bf16 weight exact mode cannot hold (detint_exact_prepare);
+ *   PAGE      a KV block-table entry outside the page pool (detint_forward_kv).
  * detint_check waits for `stream` (everything enqueued on it so far), then
  * reads and clears the current device's flags (set by any call on any
  * stream of that device since the last check): *flags (nullable) receives
@@ -86,6 +87,7 @@ const char *detint_version(void);
 #define DETINT_BOUND_SWIGLU 8u
 #define DETINT_BOUND_ID 16u
 #define DETINT_BOUND_WEIGHT 32u  /* a bf16 weight exact mode cannot hold */
+#define DETINT_BOUND_PAGE 64u    /* a KV block-table entry outside the page pool */
 detint_status detint_check(void *stream, uint32_t *flags);
 /* Message of the last error returned on the calling thread ("" if none). */
 const char *detint_last_error(void);
@@ -103,11 +105,20 @@ const char *detint_last_error(void);
  * Bounds: K <= 131056 (K * 2^14 < 2^31, so |acc| < 2^31 even when every
  * operand is -128); scaled modes |acc * m_r * m_c| < 2^62,
  * and FIX / RES_ADD results within int32. M, N >= 0; M = 0 or N = 0 is a
- * no-op. */
+ * no-op.
+ *   ws, ws_bytes: optional device workspace (16-byte aligned, contents need
+ *   not be initialised) of detint_gemm_workspace(M, N, K, limbs) bytes; with
+ *   it, shapes that give few output tiles split K over more workgroups (17-64
+ *   rows: the last split to arrive sums the partials; int8 weights with more
+ *   rows and fewer than 192 tiles of 128 x 64: int32 partials per split, then
+ *   one summing epilogue kernel). Integer sums are order-free and stay below
+ *   2^31, so the split changes no bit (DetLLM blog, "DetLLM"). NULL, 0 or a
+ *   smaller size: no split. Concurrent calls need workspaces of their own. */
+int64_t detint_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t limbs);
 detint_status detint_gemm_i8(const int8_t *A, const int8_t *W, int64_t M, int64_t N, int64_t K,
                              const int32_t *row_m, const int32_t *row_k,
                              const int32_t *col_m, int32_t col_k, int32_t frac,
-                             int32_t mode, void *out, void *stream);
+                             int32_t mode, void *out, void *ws, int64_t ws_bytes, void *stream);
 
 /* GEMM with 16-bit fixed-point weights W16 = 256 * hi + lo held as two int8
  * planes: W_hi = W16 >> 8 (signed) and W_lo = (W16 & 255) - 128 (biased so
@@ -115,12 +126,12 @@ detint_status detint_gemm_i8(const int8_t *A, const int8_t *W, int64_t M, int64_
  * 256 * (A.hi) + (A.lo') + 128 * rowsum(A) = A.W16 exactly (BitExact blog,
  * "Fix the arithmetic": limb partial products combined in wide accumulators).
  * Epilogue modes as above with a 128-bit product; RAW writes int64 [M, N].
- * Bound: K <= 65536. */
+ * Bound: K <= 65536. ws, ws_bytes as for detint_gemm_i8 (limbs = 1). */
 detint_status detint_gemm_w16(const int8_t *A, const int8_t *W_hi, const int8_t *W_lo,
                               int64_t M, int64_t N, int64_t K,
                               const int32_t *row_m, const int32_t *row_k,
                               const int32_t *col_m, int32_t col_k, int32_t frac,
-                              int32_t mode, void *out, void *stream);
+                              int32_t mode, void *out, void *ws, int64_t ws_bytes, void *stream);
 
 /* Exact mode (BitExact LLM blog, "Three execution paths": the linear layers
  * keep their bf16 weights, multiplied with fixed-point activations; "Fix the
@@ -181,6 +192,13 @@ detint_status detint_rmsnorm(const int32_t *h, const int16_t *gain, int64_t R, i
  *   y int32 [R, n] -> q int8 [R, n], row_e int32 [R] with y ~ q * 2^row_e. */
 detint_status detint_requant(const int32_t *y, int64_t R, int64_t n, int8_t *q, int32_t *row_e,
                              void *stream);
+
+/* Requantisation at a fixed dyadic scale, the kind the K/V cache uses (DetLLM
+ * blog "DetLLM": K and V are quantised once at fixed offline scales):
+ *   q[i] = clamp(R(y[i] * m, k), -127, 127) for n elements of y int32 (16-byte
+ *   aligned; q 4-byte aligned), 0 <= k <= 62, |m| < 2^31. */
+detint_status detint_requant_fixed(const int32_t *y, int64_t n, int32_t m, int32_t k, int8_t *q,
+                                   void *stream);
 
 /* Integer RoPE in place on x int32 [R, heads, d] with Q1.14 tables
  * cos_t/sin_t int16 [max_pos, d/2] (DetLLM blog "DetLLM": precomputed int16
@@ -339,6 +357,45 @@ detint_status detint_forward(const detint_model *m, int8_t *k_cache, int8_t *v_c
                              const int32_t *slot, int64_t S, int64_t max_seqlen,
                              int32_t *logits, int32_t *logit_row_base, int32_t *next_tok,
                              int32_t flags, void *ws, int64_t ws_bytes, void *stream);
+
+/* A KV cache described for detint_forward_kv: either the contiguous layout
+ * of detint_forward or pages through a block table (BitExact LLM blog, "What
+ * the checks actually compare": KV-cache reuse, shared prefixes, preemption
+ * and chunked prefill must not change a bit; the cached int8 rows are the
+ * same, only their addresses differ).
+ *   k, v: device int8, 16-byte aligned, caller-owned.
+ *   block_table == NULL: k, v are [n_layers][n_slots][n_kv][max_pos][d]
+ *     (page_size, n_pages, max_blocks ignored).
+ *   block_table != NULL: device int32 [n_slots][max_blocks]; position p of
+ *     slot s is row p & (page_size - 1) of page block_table[s][p / page_size]
+ *     of the pools k, v = [n_layers][n_pages][n_kv][page_size][d].
+ *     page_size: a power of two in [16, max_pos]; max_blocks * page_size >=
+ *     max_pos; n_pages * n_kv * page_size * d < 2^31. Several slots may name
+ *     the same page (a shared prefix is then stored once); a row is written
+ *     by the call whose sequence reaches its position, so slots that share a
+ *     page must not write it differently. Entries past a sequence's length
+ *     are not read. An entry outside [0, n_pages) raises
+ *     DETINT_BOUND_PAGE (see detint_check) and is read and written as page 0. */
+typedef struct detint_kv_desc {
+  int8_t *k, *v;
+  int64_t n_slots;
+  int64_t n_pages;
+  int64_t page_size;
+  const int32_t *block_table;
+  int64_t max_blocks;
+} detint_kv_desc;
+
+/* Bytes of each of k and v the descriptor addresses (-1 if it is invalid
+ * for the model). */
+int64_t detint_kv_bytes(const detint_model *m, const detint_kv_desc *kv);
+
+/* detint_forward over a described (contiguous or paged) KV cache; every other
+ * argument as in detint_forward. */
+detint_status detint_forward_kv(const detint_model *m, const detint_kv_desc *kv, int32_t *ids,
+                                int64_t R, const int32_t *cu_seqlens, int32_t *start_pos,
+                                const int32_t *slot, int64_t S, int64_t max_seqlen,
+                                int32_t *logits, int32_t *logit_row_base, int32_t *next_tok,
+                                int32_t flags, void *ws, int64_t ws_bytes, void *stream);
 
 /* Tied lm_head for up to 16 rows, as one kernel: logits int32 [S, V] =
  * R(x8 . E^T * row_m * emb_m, row_k + w_k - f_l), plus for every row the

@@ -17,7 +17,8 @@ _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libdetint.so"
 
 DETINT_OK, DETINT_EINVAL, DETINT_EUNSUPPORTED, DETINT_EHIP, DETINT_EBOUND = 0, 1, 2, 3, 4
-BOUND_RESIDUAL, BOUND_INT32, BOUND_NORM, BOUND_SWIGLU, BOUND_ID, BOUND_WEIGHT = 1, 2, 4, 8, 16, 32
+BOUND_RESIDUAL, BOUND_INT32, BOUND_NORM, BOUND_SWIGLU, BOUND_ID, BOUND_WEIGHT, BOUND_PAGE = (
+    1, 2, 4, 8, 16, 32, 64)
 RAW, REQ_I8, FIX, RES_ADD = 0, 1, 2, 3
 FWD_ADVANCE = 1
 
@@ -51,18 +52,25 @@ class ModelDesc(C.Structure):
                 ("rope_cos", vp), ("rope_sin", vp), ("layers", C.POINTER(LayerDesc))]
 
 
+class KvDesc(C.Structure):
+    _fields_ = [("k", vp), ("v", vp), ("n_slots", i64), ("n_pages", i64), ("page_size", i64),
+                ("block_table", vp), ("max_blocks", i64)]
+
+
 _SIGS = {
     "detint_version": (C.c_char_p, []),
     "detint_last_error": (C.c_char_p, []),
     "detint_check": (i32, [vp, C.POINTER(C.c_uint32)]),
-    "detint_gemm_i8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
-    "detint_gemm_w16": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp]),
+    "detint_gemm_workspace": (i64, [i64, i64, i64, i32]),
+    "detint_gemm_i8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
+    "detint_gemm_w16": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
     "detint_split_w16": (i32, [vp, i64, vp, vp, vp]),
     "detint_exact_prepare": (i32, [vp, i64, i64, vp, vp, vp]),
     "detint_gemm_exact_workspace": (i64, [i64, i64]),
     "detint_gemm_exact": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp]),
     "detint_rmsnorm": (i32, [vp, vp, i64, i64, vp, vp, vp, vp]),
     "detint_requant": (i32, [vp, i64, i64, vp, vp, vp]),
+    "detint_requant_fixed": (i32, [vp, i64, i32, i32, vp, vp]),
     "detint_rope": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, vp]),
     "detint_softmax": (i32, [vp, vp, vp, i64, i64, i32, i32, vp, vp]),
     "detint_swiglu": (i32, [vp, i64, i64, i32, vp, vp, vp, vp]),
@@ -79,6 +87,9 @@ _SIGS = {
     "detint_workspace_size": (i64, [vp, i64, i64]),
     "detint_forward": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i32, vp,
                              i64, vp]),
+    "detint_kv_bytes": (i64, [vp, C.POINTER(KvDesc)]),
+    "detint_forward_kv": (i32, [vp, C.POINTER(KvDesc), vp, i64, vp, vp, vp, i64, i64, vp, vp, vp, i32,
+                                vp, i64, vp]),
     "detint_lm_head_parts": (i64, [i64]),
     "detint_lm_head": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp]),
     "detint_argmax_parts": (i32, [vp, i64, i64, vp, vp]),
@@ -151,19 +162,30 @@ def detint_check() -> int:
     return int(f.value)
 
 
-def detint_gemm_i8(A, W, row_m=None, row_k=None, col_m=None, col_k=0, frac=0, mode=RAW, out=None):
+def detint_gemm_workspace(M: int, N: int, K: int, limbs: bool = False) -> int:
+    return library().detint_gemm_workspace(int(M), int(N), int(K), int(bool(limbs)))
+
+
+def _ws(ws):
+    return (_p(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
+def detint_gemm_i8(A, W, row_m=None, row_k=None, col_m=None, col_k=0, frac=0, mode=RAW, out=None,
+                   ws=None):
+    """ws: optional uint8 device workspace of detint_gemm_workspace(M, N, K)
+    bytes (split-K for few-tile shapes; the same bits either way)."""
     torch = _torch()
     M, K = A.shape
     N = W.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.int8 if mode == REQ_I8 else torch.int32, device=A.device)
     _call("detint_gemm_i8", _p(A, torch.int8), _p(W, torch.int8), M, N, K, _p(row_m), _p(row_k),
-          _p(col_m), int(col_k), int(frac), int(mode), _p(out), _stream())
+          _p(col_m), int(col_k), int(frac), int(mode), _p(out), *_ws(ws), _stream())
     return out
 
 
 def detint_gemm_w16(A, W_hi, W_lo, row_m=None, row_k=None, col_m=None, col_k=0, frac=0, mode=RAW,
-                    out=None):
+                    out=None, ws=None):
     torch = _torch()
     M, K = A.shape
     N = W_hi.shape[0]
@@ -171,7 +193,8 @@ def detint_gemm_w16(A, W_hi, W_lo, row_m=None, row_k=None, col_m=None, col_k=0, 
         dt = {RAW: torch.int64, REQ_I8: torch.int8}.get(mode, torch.int32)
         out = torch.empty((M, N), dtype=dt, device=A.device)
     _call("detint_gemm_w16", _p(A, torch.int8), _p(W_hi, torch.int8), _p(W_lo, torch.int8), M, N, K,
-          _p(row_m), _p(row_k), _p(col_m), int(col_k), int(frac), int(mode), _p(out), _stream())
+          _p(row_m), _p(row_k), _p(col_m), int(col_k), int(frac), int(mode), _p(out), *_ws(ws),
+          _stream())
     return out
 
 
@@ -229,6 +252,14 @@ def detint_requant(y):
     e = torch.empty(R_, dtype=torch.int32, device=y.device)
     _call("detint_requant", _p(y, torch.int32), R_, n, _p(q), _p(e), _stream())
     return q, e
+
+
+def detint_requant_fixed(y, m, k):
+    """clamp8(R(y * m, k)) elementwise (int32 device tensor -> int8)."""
+    torch = _torch()
+    q = torch.empty(y.shape, dtype=torch.int8, device=y.device)
+    _call("detint_requant_fixed", _p(y, torch.int32), y.numel(), int(m), int(k), _p(q), _stream())
+    return q
 
 
 def detint_rope(x, pos, cos_t, sin_t):
@@ -404,7 +435,11 @@ class DetintModel:
     detint_forward. Weights are uploaded once; 16-bit weights are split into
     limb planes on the device with detint_split_w16."""
 
-    def __init__(self, model, n_slots: int = 1, device: str = "cuda"):
+    def __init__(self, model, n_slots: int = 1, device: str = "cuda", page_size: int = 0,
+                 n_pages: int = 0):
+        """page_size > 0: the KV cache is a pool of n_pages pages of page_size
+        positions per layer, addressed through self.block_table (device int32
+        [n_slots, max_blocks], filled by the caller; detint_forward_kv)."""
         torch = _torch()
         self.torch = torch
         sh = model.shape
@@ -459,9 +494,20 @@ class DetintModel:
         h = vp()
         _call("detint_model_create", C.byref(d), C.byref(h))
         self.handle = h
-        cache_shape = (sh.n_layers, n_slots, sh.n_kv, sh.max_pos, sh.head_dim)
+        self.page_size = page_size
+        if page_size:
+            self.max_blocks = (sh.max_pos + page_size - 1) // page_size
+            cache_shape = (sh.n_layers, n_pages, sh.n_kv, page_size, sh.head_dim)
+            self.block_table = torch.zeros((n_slots, self.max_blocks), dtype=torch.int32, device=device)
+        else:
+            cache_shape = (sh.n_layers, n_slots, sh.n_kv, sh.max_pos, sh.head_dim)
+            self.block_table = None
         self.kc = torch.zeros(cache_shape, dtype=torch.int8, device=device)
         self.vc = torch.zeros(cache_shape, dtype=torch.int8, device=device)
+        self.kv = KvDesc(k=_p(self.kc), v=_p(self.vc), n_slots=n_slots, n_pages=n_pages,
+                         page_size=page_size,
+                         block_table=_p(self.block_table) if page_size else None,
+                         max_blocks=self.max_blocks if page_size else 0)
         self._ws = None
         torch.cuda.synchronize()
 
@@ -476,6 +522,23 @@ class DetintModel:
         self.kc.zero_()
         self.vc.zero_()
 
+    def contiguous_cache(self):
+        """Paged pools gathered into the contiguous layout [layers, slots,
+        n_kv, max_pos, d] through the block table (host arrays)."""
+        sh = self.shape
+        if not self.page_size:
+            return self.kc.cpu().numpy(), self.vc.cpu().numpy()
+        bt = self.block_table.cpu().numpy()
+        out = []
+        for pool in (self.kc.cpu().numpy(), self.vc.cpu().numpy()):
+            c = np.zeros((sh.n_layers, self.n_slots, sh.n_kv, self.max_blocks * self.page_size,
+                          sh.head_dim), np.int8)
+            for s_ in range(self.n_slots):
+                for b in range(self.max_blocks):
+                    c[:, s_, :, b * self.page_size:(b + 1) * self.page_size] = pool[:, bt[s_, b]]
+            out.append(c[:, :, :, : sh.max_pos])
+        return out[0], out[1]
+
     def workspace(self, R: int, S: int):
         need = library().detint_workspace_size(self.handle, R, S)
         if self._ws is None or self._ws.numel() < need:
@@ -485,6 +548,11 @@ class DetintModel:
     def forward_raw(self, ids, R, cu, start, slot, S, max_seqlen, logits, row_base, next_tok, flags=0):
         """Direct detint_forward on device tensors (all int32)."""
         ws = self.workspace(R, S)
+        if self.page_size:
+            _call("detint_forward_kv", self.handle, C.byref(self.kv), _p(ids), R, _p(cu), _p(start),
+                  _p(slot), S, max_seqlen, _p(logits), _p(row_base), _p(next_tok), int(flags), _p(ws),
+                  ws.numel(), _stream())
+            return
         _call("detint_forward", self.handle, _p(self.kc), _p(self.vc), self.n_slots, _p(ids), R, _p(cu),
               _p(start), _p(slot), S, max_seqlen, _p(logits), _p(row_base), _p(next_tok), int(flags),
               _p(ws), ws.numel(), _stream())

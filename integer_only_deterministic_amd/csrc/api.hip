@@ -109,25 +109,51 @@ detint_status detint_check(void* stream, uint32_t* flags) {
 
 // ------------------------------------------------------------------- GEMMs
 
+int64_t detint_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t limbs) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  return gemm_workspace_bytes(M, N, K, limbs != 0);
+}
+
+// Split-K workspace of a standalone GEMM: the skinny kernel's arrival
+// counters (cleared by a kernel first), then the partials.
+static detint_status gemm_with_ws(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
+                                  int64_t N, int64_t K, const Epi& e, void* out, void* ws,
+                                  int64_t ws_bytes, hipStream_t st, const char* what) {
+  const int64_t need = gemm_workspace_bytes(M, N, K, W_lo != nullptr);
+  if (!ws || need == 0 || ws_bytes < need)
+    return hip_status(launch_gemm(A, W, W_lo, M, N, K, e, out, st), what);
+  REQUIRE(aligned16(ws), "%s: workspace must be 16-byte aligned", what);
+  const int64_t tiles = (N + 31) / 32;
+  const int64_t cnt_bytes = ((4 * tiles + 255) / 256) * 256;
+  SplitWs sp{(int32_t*)((char*)ws + cnt_bytes), (int32_t*)ws, kSplitPairsStandalone, tiles,
+             (ws_bytes - cnt_bytes) / 4};
+  if (gemm_takes_skinny(M, N, K, W_lo != nullptr)) {
+    const hipError_t z = launch_zero_i32(sp.cnt, tiles, st);
+    if (z != hipSuccess) return hip_status(z, what);
+  }
+  return hip_status(launch_gemm(A, W, W_lo, M, N, K, e, out, st, &sp), what);
+}
+
 detint_status detint_gemm_i8(const int8_t* A, const int8_t* W, int64_t M, int64_t N, int64_t K,
                              const int32_t* row_m, const int32_t* row_k, const int32_t* col_m,
-                             int32_t col_k, int32_t frac, int32_t mode, void* out, void* stream) {
+                             int32_t col_k, int32_t frac, int32_t mode, void* out, void* ws,
+                             int64_t ws_bytes, void* stream) {
   // K * 2^14 < 2^31 even when every operand is -128
   detint_status s = check_gemm(A, W, M, N, K, row_m, row_k, col_m, mode, out, 131056);
   if (s != DETINT_OK || M == 0 || N == 0) return s;
   Epi e{row_m, row_k, col_m, col_k, frac, mode, nullptr};
-  return hip_status(launch_gemm(A, W, nullptr, M, N, K, e, out, S_(stream)), "gemm_i8 launch");
+  return gemm_with_ws(A, W, nullptr, M, N, K, e, out, ws, ws_bytes, S_(stream), "gemm_i8 launch");
 }
 
 detint_status detint_gemm_w16(const int8_t* A, const int8_t* W_hi, const int8_t* W_lo, int64_t M,
                               int64_t N, int64_t K, const int32_t* row_m, const int32_t* row_k,
                               const int32_t* col_m, int32_t col_k, int32_t frac, int32_t mode,
-                              void* out, void* stream) {
+                              void* out, void* ws, int64_t ws_bytes, void* stream) {
   detint_status s = check_gemm(A, W_hi, M, N, K, row_m, row_k, col_m, mode, out, 65536);
   if (s != DETINT_OK || M == 0 || N == 0) return s;
   REQUIRE(W_lo && aligned16(W_lo), "gemm_w16: W_lo null or misaligned");
   Epi e{row_m, row_k, col_m, col_k, frac, mode, nullptr};
-  return hip_status(launch_gemm(A, W_hi, W_lo, M, N, K, e, out, S_(stream)), "gemm_w16 launch");
+  return gemm_with_ws(A, W_hi, W_lo, M, N, K, e, out, ws, ws_bytes, S_(stream), "gemm_w16 launch");
 }
 
 detint_status detint_exact_prepare(const uint16_t* W, int64_t N, int64_t K, int8_t* planes,
@@ -190,6 +216,14 @@ detint_status detint_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, 
   REQUIRE(y && q && row_e, "requant: null pointer");
   return hip_status(launch_requant(y, R, n, q, row_e, nullptr, nullptr, 0, 0, S_(stream)),
                     "requant launch");
+}
+
+detint_status detint_requant_fixed(const int32_t* y, int64_t n, int32_t m, int32_t k, int8_t* q,
+                                   void* stream) {
+  REQUIRE(n >= 0 && k >= 0 && k <= 62, "requant_fixed: bad n or shift");
+  if (n == 0) return ok();
+  REQUIRE(y && q && aligned16(y) && ((uintptr_t)q & 3) == 0, "requant_fixed: null or misaligned");
+  return hip_status(launch_requant_fixed(y, n, m, k, q, S_(stream)), "requant_fixed launch");
 }
 
 detint_status detint_rope(int32_t* x, const int32_t* pos, const int16_t* cos_t,
@@ -624,8 +658,22 @@ int64_t detint_workspace_size(const detint_model* m, int64_t max_rows, int64_t m
 }
 
 // One decoder layer in place on h [R, H] (workspace buffers from w).
-static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int8_t* k_cache,
-                               int8_t* v_cache, int64_t n_slots, int64_t R, const RowMap& seqs,
+// A KV cache as the kernels see it: per-layer bases at k / v + l layer_stride,
+// contiguous or paged (see KvPages).
+struct Kv {
+  int8_t* k;
+  int8_t* v;
+  int64_t n_slots;
+  int64_t layer_stride;
+  KvPages pages;
+};
+
+Kv contiguous_kv(const detint_model_desc& d, int8_t* k, int8_t* v, int64_t n_slots) {
+  return Kv{k, v, n_slots, n_slots * d.n_kv * d.max_pos * d.head_dim, KvPages{nullptr, 0, 0, 0}};
+}
+
+static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, const Kv& kv,
+                               int64_t R, const RowMap& seqs,
                                int64_t max_seqlen, char* base, const WsLayout& w, hipStream_t st) {
   const detint_model_desc& d = m->d;
   const detint_layer_desc& L = m->layers[l];
@@ -641,13 +689,13 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
   int32_t* gu = (int32_t*)(base + w.gu);
   const int64_t H = d.hidden, nq = d.n_q, nkv = d.n_kv, hd = d.head_dim, F = d.ffn;
   const int64_t nqd = nq * hd, nqkv = (nq + 2 * nkv) * hd;
-  const size_t layer_stride = (size_t)n_slots * nkv * d.max_pos * hd;
+  const int64_t n_slots = kv.n_slots;
   const int32_t wk = d.w_k;
   const SplitWs spw{w.sk_tiles ? (int32_t*)(base + w.sk_part) : nullptr,
                     w.sk_tiles ? (int32_t*)(base + w.sk_cnt) : nullptr, kSplitPairs, w.sk_tiles};
   const SplitWs* sp = w.sk_tiles ? &spw : nullptr;
-  int8_t* kc = k_cache + l * layer_stride;
-  int8_t* vc = v_cache + l * layer_stride;
+  int8_t* kc = kv.k + l * kv.layer_stride;
+  int8_t* vc = kv.v + l * kv.layer_stride;
   hipError_t e;
 #define LAUNCH(x)                                  \
   do {                                             \
@@ -669,12 +717,12 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
     // start[r] and seq_slot[r]
     LAUNCH(launch_attention_decode_fused(qkv, qp, seqs.start, seqs.seq_slot, R, nq, nkv, hd,
                                          n_slots, d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att,
-                                         st));
+                                         st, kv.pages));
   } else {
     LAUNCH(launch_qkv_post(qkv, R, nq, nkv, hd, pos_of, slot_of, qp, q8, eq, kc, vc, n_slots,
-                           d.max_pos, st));
+                           d.max_pos, st, kv.pages));
     LAUNCH(launch_attention_seqs(q8, eq, kc, vc, seqs, R, max_seqlen, nq, nkv, hd, n_slots,
-                                 d.max_pos, m->sm_m[l], m->sm_k[l], att, st));
+                                 d.max_pos, m->sm_m[l], m->sm_k[l], att, st, kv.pages));
   }
   LAUNCH(launch_requant(att, R, nqd, x8, nullptr, rm, rk, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, st));
   {
@@ -708,8 +756,8 @@ static detint_status run_layer(const detint_model* m, int64_t l, int32_t* h, int
 // [q/k-norm + RoPE + KV write + attention], [DQ + O-proj + residual],
 // [RMSNorm + gate/up + SwiGLU product], [DQ + down + residual]; then
 // [RMSNorm + lm_head + argmax partials] and [greedy token + advance].
-static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
-                                int64_t n_slots, int32_t* ids, int64_t R, int32_t* start_pos,
+static detint_status run_decode(const detint_model* m, const Kv& kv, int32_t* ids, int64_t R,
+                                int32_t* start_pos,
                                 const int32_t* slot, int32_t* logits, int32_t* row_base,
                                 int32_t* next_tok, bool advance, char* base, const WsLayout& w,
                                 hipStream_t st) {
@@ -723,7 +771,7 @@ static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* 
   int64_t* part = (int64_t*)(base + w.part);
   const int64_t H = d.hidden, nq = d.n_q, nkv = d.n_kv, hd = d.head_dim, F = d.ffn;
   const int64_t nqd = nq * hd, nqkv = (nq + 2 * nkv) * hd;
-  const size_t layer_stride = (size_t)n_slots * nkv * d.max_pos * hd;
+  const int64_t n_slots = kv.n_slots;
   const int32_t wk = d.w_k;
   hipError_t e;
 #define LAUNCH(x)                                  \
@@ -734,14 +782,15 @@ static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* 
   LAUNCH(launch_embed(ids, R, d.emb, nullptr, d.emb_m, H, d.vocab, wk - d.f_res, h, st));
   for (int64_t l = 0; l < d.n_layers; ++l) {
     const detint_layer_desc& L = m->layers[l];
-    int8_t* kc = k_cache + l * layer_stride;
-    int8_t* vc = v_cache + l * layer_stride;
+    int8_t* kc = kv.k + l * kv.layer_stride;
+    int8_t* vc = kv.v + l * kv.layer_stride;
     LAUNCH(launch_fused_qkv(h, L.attn_norm, L.wqkv, L.wqkv_m, wk, d.qk_norm ? 0 : d.f_n,
                             d.qk_norm != 0, R, nqkv, H, qkv, rm, rk, st));
     QkvPost qp{d.qk_norm, rm, rk, L.wqkv_m, wk, L.q_norm, L.k_norm, d.f_n, L.kq_m, L.kq_k,
                L.vq_m, L.vq_k, d.rope_cos, d.rope_sin, L.k_gain};
     LAUNCH(launch_attention_decode_fused(qkv, qp, start_pos, slot, R, nq, nkv, hd, n_slots,
-                                         d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att, st));
+                                         d.max_pos, kc, vc, m->sm_m[l], m->sm_k[l], att, st,
+                                         kv.pages));
     LAUNCH(launch_fused_oproj(att, m->vd_m[l], m->vd_k[l] + 15 + d.f_n, L.wo, L.wo_m, wk, d.f_res,
                               R, H, nqd, h, st));
     LAUNCH(launch_fused_gateup(h, L.ffn_norm, L.wgu, L.wgu_m, wk, d.f_a, m->mg, m->kg, R, F, H, p64,
@@ -756,15 +805,15 @@ static detint_status run_decode(const detint_model* m, int8_t* k_cache, int8_t* 
   return ok();
 }
 
-static detint_status check_run(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
-                               int64_t n_slots, int64_t R, const int32_t* cu_seqlens,
-                               const int32_t* start_pos, const int32_t* slot, int64_t S,
-                               int64_t max_seqlen, void* ws, int64_t ws_bytes) {
+static detint_status check_run(const detint_model* m, const Kv& kv, int64_t R,
+                               const int32_t* cu_seqlens, const int32_t* start_pos,
+                               const int32_t* slot, int64_t S, int64_t max_seqlen, void* ws,
+                               int64_t ws_bytes) {
   REQUIRE(m, "forward: null model");
-  REQUIRE(R >= 0 && S >= 0 && n_slots > 0, "forward: bad sizes");
+  REQUIRE(R >= 0 && S >= 0 && kv.n_slots > 0, "forward: bad sizes");
   REQUIRE(S > 0 && R >= S, "forward: need 1 <= S <= R (every sequence has a row)");
-  REQUIRE(k_cache && v_cache && cu_seqlens && start_pos && slot && ws, "forward: null pointer");
-  REQUIRE(aligned16(k_cache) && aligned16(v_cache) && aligned16(ws), "forward: misaligned buffer");
+  REQUIRE(kv.k && kv.v && cu_seqlens && start_pos && slot && ws, "forward: null pointer");
+  REQUIRE(aligned16(kv.k) && aligned16(kv.v) && aligned16(ws), "forward: misaligned buffer");
   REQUIRE(max_seqlen >= 1 && max_seqlen <= R, "forward: bad max_seqlen");
   const WsLayout w = ws_layout(m->d, R, S);
   REQUIRE(ws_bytes >= w.total, "forward: workspace %lld < %lld bytes", (long long)ws_bytes,
@@ -772,14 +821,42 @@ static detint_status check_run(const detint_model* m, int8_t* k_cache, int8_t* v
   return ok();
 }
 
-detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t* h,
-                                   int8_t* k_cache, int8_t* v_cache, int64_t n_slots, int64_t R,
-                                   const int32_t* cu_seqlens, const int32_t* start_pos,
-                                   const int32_t* slot, int64_t S, int64_t max_seqlen, void* ws,
-                                   int64_t ws_bytes, void* stream) {
+// A caller's descriptor as the kernels' view (validated).
+static detint_status kv_from_desc(const detint_model* m, const detint_kv_desc* kd, Kv* out) {
+  REQUIRE(m && kd, "kv: null model or descriptor");
+  const detint_model_desc& d = m->d;
+  REQUIRE(kd->n_slots > 0 && kd->n_slots < ((int64_t)1 << 31), "kv: n_slots out of range");
+  if (!kd->block_table) {
+    *out = contiguous_kv(d, kd->k, kd->v, kd->n_slots);
+    return ok();
+  }
+  const int64_t P = kd->page_size;
+  REQUIRE(P >= 16 && P <= d.max_pos && (P & (P - 1)) == 0,
+          "kv: page_size must be a power of two in [16, max_pos]");
+  REQUIRE(kd->max_blocks * P >= d.max_pos && kd->max_blocks < ((int64_t)1 << 24),
+          "kv: max_blocks * page_size must cover max_pos");
+  REQUIRE(kd->n_pages > 0 && kd->n_pages * d.n_kv * P * d.head_dim < ((int64_t)1 << 31),
+          "kv: a layer's pool must hold under 2^31 bytes");
+  int shift = 0;
+  while ((int64_t(1) << shift) < P) ++shift;
+  *out = Kv{kd->k, kd->v, kd->n_slots, kd->n_pages * d.n_kv * P * d.head_dim,
+            KvPages{kd->block_table, (int32_t)kd->max_blocks, shift, (int32_t)kd->n_pages}};
+  return ok();
+}
+
+int64_t detint_kv_bytes(const detint_model* m, const detint_kv_desc* kv) {
+  Kv v;
+  if (kv_from_desc(m, kv, &v) != DETINT_OK) return -1;
+  return v.layer_stride * m->d.n_layers;
+}
+
+static detint_status layer_forward_impl(const detint_model* m, int64_t layer, int32_t* h,
+                                        const Kv& kv, int64_t R, const int32_t* cu_seqlens,
+                                        const int32_t* start_pos, const int32_t* slot, int64_t S,
+                                        int64_t max_seqlen, void* ws, int64_t ws_bytes,
+                                        void* stream) {
   if (R == 0 && S == 0) return ok();
-  detint_status s = check_run(m, k_cache, v_cache, n_slots, R, cu_seqlens, start_pos, slot, S,
-                              max_seqlen, ws, ws_bytes);
+  detint_status s = check_run(m, kv, R, cu_seqlens, start_pos, slot, S, max_seqlen, ws, ws_bytes);
   if (s != DETINT_OK) return s;
   REQUIRE(h && layer >= 0 && layer < m->d.n_layers, "layer_forward: bad layer or null h");
   const WsLayout w = ws_layout(m->d, R, S);
@@ -790,18 +867,26 @@ detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t
                                   w.sk_tiles ? (int32_t*)(base + w.sk_cnt) : nullptr, w.sk_tiles);
   if (e != hipSuccess) return hip_status(e, "rows_meta");
   const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
-  return run_layer(m, layer, h, k_cache, v_cache, n_slots, R, seqs, max_seqlen, base, w, st);
+  return run_layer(m, layer, h, kv, R, seqs, max_seqlen, base, w, st);
 }
 
-detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
-                             int64_t n_slots, int32_t* ids, int64_t R, const int32_t* cu_seqlens,
-                             int32_t* start_pos, const int32_t* slot, int64_t S,
-                             int64_t max_seqlen, int32_t* logits, int32_t* logit_row_base,
-                             int32_t* next_tok, int32_t flags, void* ws, int64_t ws_bytes,
-                             void* stream) {
+detint_status detint_layer_forward(const detint_model* m, int64_t layer, int32_t* h,
+                                   int8_t* k_cache, int8_t* v_cache, int64_t n_slots, int64_t R,
+                                   const int32_t* cu_seqlens, const int32_t* start_pos,
+                                   const int32_t* slot, int64_t S, int64_t max_seqlen, void* ws,
+                                   int64_t ws_bytes, void* stream) {
+  REQUIRE(m, "layer_forward: null model");
+  return layer_forward_impl(m, layer, h, contiguous_kv(m->d, k_cache, v_cache, n_slots), R,
+                            cu_seqlens, start_pos, slot, S, max_seqlen, ws, ws_bytes, stream);
+}
+
+static detint_status forward_impl(const detint_model* m, const Kv& kv, int32_t* ids, int64_t R,
+                                  const int32_t* cu_seqlens, int32_t* start_pos,
+                                  const int32_t* slot, int64_t S, int64_t max_seqlen,
+                                  int32_t* logits, int32_t* logit_row_base, int32_t* next_tok,
+                                  int32_t flags, void* ws, int64_t ws_bytes, void* stream) {
   if (R == 0 && S == 0) return ok();
-  detint_status s = check_run(m, k_cache, v_cache, n_slots, R, cu_seqlens, start_pos, slot, S,
-                              max_seqlen, ws, ws_bytes);
+  detint_status s = check_run(m, kv, R, cu_seqlens, start_pos, slot, S, max_seqlen, ws, ws_bytes);
   if (s != DETINT_OK) return s;
   REQUIRE(ids && logits && next_tok, "forward: null ids/logits/next_tok");
   REQUIRE(m->d.vocab > 0 && m->d.emb, "forward: model has no vocabulary");
@@ -827,9 +912,8 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
   if (d.n_q * d.head_dim > kmax) kmax = d.n_q * d.head_dim;
   if (R == S && !d.wide && fused_decode_supported(R, kmax)) {
     // decode-shaped call (one row per sequence): 5 fused kernels per layer
-    s = run_decode(m, k_cache, v_cache, n_slots, ids, R, start_pos, slot, logits, logit_row_base,
-                   next_tok, (flags & DETINT_FWD_ADVANCE) != 0, base, w, st);
-    return s;
+    return run_decode(m, kv, ids, R, start_pos, slot, logits, logit_row_base, next_tok,
+                      (flags & DETINT_FWD_ADVANCE) != 0, base, w, st);
   }
   LAUNCH(launch_rows_meta(cu_seqlens, start_pos, slot, S, (int32_t*)(base + w.pos_of),
                           (int32_t*)(base + w.slot_of), last_row, st,
@@ -838,7 +922,7 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
                       d.w_k - d.f_res, h, st));
   const RowMap seqs{cu_seqlens, start_pos, slot, (int32_t)S, nullptr, 0, nullptr};
   for (int64_t l = 0; l < d.n_layers; ++l) {
-    s = run_layer(m, l, h, k_cache, v_cache, n_slots, R, seqs, max_seqlen, base, w, st);
+    s = run_layer(m, l, h, kv, R, seqs, max_seqlen, base, w, st);
     if (s != DETINT_OK) return s;
   }
   // final norm on each sequence's last row, tied lm_head, greedy token
@@ -858,6 +942,30 @@ detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_c
     LAUNCH(launch_advance(ids, next_tok, start_pos, logit_row_base, S, st));
 #undef LAUNCH
   return ok();
+}
+
+detint_status detint_forward(const detint_model* m, int8_t* k_cache, int8_t* v_cache,
+                             int64_t n_slots, int32_t* ids, int64_t R, const int32_t* cu_seqlens,
+                             int32_t* start_pos, const int32_t* slot, int64_t S,
+                             int64_t max_seqlen, int32_t* logits, int32_t* logit_row_base,
+                             int32_t* next_tok, int32_t flags, void* ws, int64_t ws_bytes,
+                             void* stream) {
+  REQUIRE(m, "forward: null model");
+  return forward_impl(m, contiguous_kv(m->d, k_cache, v_cache, n_slots), ids, R, cu_seqlens,
+                      start_pos, slot, S, max_seqlen, logits, logit_row_base, next_tok, flags, ws,
+                      ws_bytes, stream);
+}
+
+detint_status detint_forward_kv(const detint_model* m, const detint_kv_desc* kv, int32_t* ids,
+                                int64_t R, const int32_t* cu_seqlens, int32_t* start_pos,
+                                const int32_t* slot, int64_t S, int64_t max_seqlen,
+                                int32_t* logits, int32_t* logit_row_base, int32_t* next_tok,
+                                int32_t flags, void* ws, int64_t ws_bytes, void* stream) {
+  Kv v;
+  detint_status s = kv_from_desc(m, kv, &v);
+  if (s != DETINT_OK) return s;
+  return forward_impl(m, v, ids, R, cu_seqlens, start_pos, slot, S, max_seqlen, logits,
+                      logit_row_base, next_tok, flags, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -103,11 +103,12 @@ __device__ __forceinline__ void row_info(const RowMap& m, int r, int& pos, int& 
 // sq: the G q8 vectors (LDS, 16-byte chunks); eqv: their DQ exponents;
 // K, V: the (slot, KV head) cache block; keys 0..ctx-1; sc: LDS [G][ld].
 // KU key rows and VU value rows are in flight per thread in passes 1 and 4.
-template <int D, int G, int NT = TPB, int KU = 4, int VU = 8>
+// off(j): byte offset of cached position j from K and V (the same for both).
+template <int D, int G, int NT = TPB, int KU = 4, int VU = 8, class Off>
 __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const int8_t* __restrict__ K,
                                        const int8_t* __restrict__ V, int ctx, int ld, int32_t Ms,
                                        int32_t Ks, int32_t* __restrict__ orow, int32_t* sc,
-                                       int64_t* red, int32_t (*sred)[G * D]) {
+                                       int64_t* red, int32_t (*sred)[G * D], Off off) {
   constexpr int CH = D / 16;        // 16-byte chunks per row
   constexpr int RG = NT / CH;       // V rows in flight per pass-4 step
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -137,14 +138,14 @@ __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const 
 #pragma unroll
     for (int u = 0; u < KU; ++u)
 #pragma unroll
-      for (int cc = 0; cc < CH; ++cc) kk[u][cc] = ((const v4i*)(K + (size_t)(j1 + u * NT) * D))[cc];
+      for (int cc = 0; cc < CH; ++cc) kk[u][cc] = ((const v4i*)(K + off(j1 + u * NT)))[cc];
 #pragma unroll
     for (int u = 0; u < KU; ++u) score(kk[u], j1 + u * NT);
   }
   for (; j1 < ctx; j1 += NT) {
     v4i ka[CH];
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc) ka[cc] = ((const v4i*)(K + (size_t)j1 * D))[cc];
+    for (int cc = 0; cc < CH; ++cc) ka[cc] = ((const v4i*)(K + off(j1)))[cc];
     score(ka, j1);
   }
 #pragma unroll
@@ -197,11 +198,11 @@ __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const 
   for (; j + (VU - 1) * RG < ctx; j += VU * RG) {  // VU independent row loads in flight
     v4i vv[VU];
 #pragma unroll
-    for (int u = 0; u < VU; ++u) vv[u] = *(const v4i*)(V + (size_t)(j + u * RG) * D + c * 16);
+    for (int u = 0; u < VU; ++u) vv[u] = *(const v4i*)(V + off(j + u * RG) + c * 16);
 #pragma unroll
     for (int u = 0; u < VU; ++u) pv(vv[u], j + u * RG);
   }
-  for (; j < ctx; j += RG) pv(*(const v4i*)(V + (size_t)j * D + c * 16), j);
+  for (; j < ctx; j += RG) pv(*(const v4i*)(V + off(j) + c * 16), j);
   // reduce over the lanes of a wave that share chunk c
 #pragma unroll
   for (int off = CH; off < 64; off <<= 1)
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
                                                  const int8_t* __restrict__ vc, RowMap rows,
                                                  int nq, int nkv, int n_slots, int max_pos,
                                                  int32_t Ms, int32_t Ks,
-                                                 int32_t* __restrict__ out) {
+                                                 int32_t* __restrict__ out, KvPages kp) {
   constexpr int CH = D / 16;
   extern __shared__ int32_t sc[];   // [G][max_pos]: scores -> E
   __shared__ v4i sq[G * CH];
@@ -251,7 +252,15 @@ __global__ __launch_bounds__(TPB) void attn_rows(const int8_t* __restrict__ q8,
   if (tid < G * CH) sq[tid] = *(const v4i*)(q8 + ((size_t)r * nq + h0) * D + tid * 16);
   if (tid < G) seq[tid] = e_q[(size_t)r * nq + h0 + tid];
   __syncthreads();
-  attend<D, G>(sq, seq, kc + base, vc + base, pos + 1, max_pos, Ms, Ks, orow, sc, red, sred);
+  if (!kp.bt) {
+    attend<D, G>(sq, seq, kc + base, vc + base, pos + 1, max_pos, Ms, Ks, orow, sc, red, sred,
+                 [](int j) { return (int64_t)j * D; });
+  } else {
+    uint32_t bad = 0;
+    attend<D, G>(sq, seq, kc, vc, pos + 1, max_pos, Ms, Ks, orow, sc, red, sred,
+                 [&](int j) { return page_row_off(kp, slot, kvh, nkv, D, j, bad); });
+    bound_raise(bad);
+  }
 }
 
 // Decode: one row per sequence. The workgroup of (row, KV head) does the QKV
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     const int32_t* qkv, QkvPost p, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ slot_arr, int nq, int nkv, int n_slots, int max_pos,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, int32_t Ms, int32_t Ks,
-    int32_t* __restrict__ out, int gq) {
+    int32_t* __restrict__ out, int gq, KvPages kp) {
   constexpr int CH = D / 16;              // 16-byte chunks per row
   constexpr int NW = NT / 64;
   constexpr int PRE = G <= 2 && NT == 256 ? 768 : 512;  // cached rows loaded up front
@@ -335,8 +344,15 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
 
   // 2. cached keys and values 0..min(pos, PRE)-1 into registers; rows past
   //    them read zeros without touching memory (out-of-range offsets)
-  const size_t base = ((size_t)slot * nkv + kvh) * max_pos * D;
-  const int cbytes = max_pos * D;
+  // contiguous: a buffer over this (slot, KV head) block, row j at j D;
+  // paged: a buffer over the layer's pool, row j where the block table puts it
+  const bool paged = kp.bt != nullptr;
+  const size_t base = paged ? 0 : ((size_t)slot * nkv + kvh) * max_pos * D;
+  const int cbytes = paged ? (kp.n_pages * nkv * D) << kp.shift : max_pos * D;
+  uint32_t pbad = 0;
+  auto roff = [&](int j) -> int {
+    return paged ? (int)page_row_off(kp, slot, kvh, nkv, D, j, pbad) : j * D;
+  };
   const __amdgpu_buffer_rsrc_t rsk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, cbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsv =
@@ -346,7 +362,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int j = tid + u * NT;
-    const int off = j < nold ? j * D : cbytes;
+    const int off = j < nold ? roff(j) : cbytes;
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc)
       kpre[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   for (int u = 0; u < VU; ++u) {
     const int j = rg + u * RG;
     vpre[u] = __builtin_bit_cast(
-        v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? roff(j) + c * 16 : cbytes, 0, 0));
   }
   // the first batch of later cached keys too (long contexts; out-of-range
   // rows read zeros without touching memory)
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
 #pragma unroll
     for (int u = 0; u < SK; ++u) {
       const int j = b0 + tid + u * NT;
-      const int off = j < nold ? j * D : cbytes;
+      const int off = j < nold ? roff(j) : cbytes;
 #pragma unroll
       for (int cc = 0; cc < CH; ++cc)
         kr[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     const int j0 = lane, j1 = lane + half;
     if (t == G + 1) {  // value head
       const int c0 = (nq + nkv + kvh) * D;
-      int8_t* dst = vc + base + (size_t)pos * D;
+      int8_t* dst = vc + base + roff(pos);
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         int64_t vf = e2 ? hx1[u] : hx0[u];
@@ -435,7 +451,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
       }
       if (lane == 0) seq[t] = e;
     } else if (act) {  // key head
-      int8_t* dst = kc + base + (size_t)pos * D;
+      int8_t* dst = kc + base + roff(pos);
       const int8_t k0 = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
       const int8_t k1 = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
       dst[j0] = k0;
@@ -444,7 +460,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
       snk[j1] = k1;
     }
   }
-  bound_raise(bad);
+  bound_raise(bad | pbad);
   lds_barrier();
 
   // 4. pass 1: scores into LDS, per-head maxima
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     for (int u = 0; u < SU; ++u) {
       const int j = b0 + rg + u * RG;
       vr[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? j * D + c * 16 : cbytes, 0, 0));
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? roff(j) + c * 16 : cbytes, 0, 0));
     }
   };
   if (PRE < nold) vload(va, PRE);
@@ -634,6 +650,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     for (int w = 0; w < NW; ++w) s2 += sred[w][t];
     orow[t] = s2;
   }
+  bound_raise(pbad);  // pages of the later cached rows
 }
 
 // ------------------------------------------------------ prefill on MFMA
@@ -688,7 +705,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     const int8_t* __restrict__ q8, const int32_t* __restrict__ e_q, const int8_t* __restrict__ kc,
     const int8_t* __restrict__ vc, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
     const int32_t* __restrict__ seq_slot, int nq, int nkv, int n_slots, int max_pos, int nblk,
-    int32_t Ms, int32_t Ks, int32_t* __restrict__ out) {
+    int32_t Ms, int32_t Ks, int32_t* __restrict__ out, KvPages kp) {
   constexpr int QP = PfCfg<G>::QP, KS = D / 32, CPR = D / 16;
   using L = PfLds<D, G>;
   constexpr int BK = L::BK, KB = L::KB, VST = L::VST;
@@ -716,11 +733,16 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const bool live = rvalid && pos >= 0 && pos < max_pos;
   const int kend = min(p0 + qb * QP + nrow, max_pos);
   const int nch = (kend + 31) >> 5, nbt = (kend + BK - 1) / BK;
-  const size_t base = ((size_t)slot * nkv + kvh) * max_pos * D;
+  // contiguous: a buffer over this (slot, KV head) block; paged: over the
+  // layer's pool, each key row where the block table puts it
+  const bool paged = kp.bt != nullptr;
+  const size_t base = paged ? 0 : ((size_t)slot * nkv + kvh) * max_pos * D;
+  const int cbytes = paged ? (kp.n_pages * nkv * D) << kp.shift : max_pos * D;
+  uint32_t pbad = 0;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0,
-                                                                      max_pos * D, 0x00020000);
+                                                                      cbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0,
-                                                                      max_pos * D, 0x00020000);
+                                                                      cbytes, 0x00020000);
   // batch bt of K (swizzled) and, for pass 3, V (natural) into buffer bt & 1:
   // load q of thread t moves chunk g = 256 q + t, LDS bytes [16 g, 16 g + 16)
   auto issue = [&](int bt, bool withv) {
@@ -728,7 +750,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
     for (int q = 0; q < LPB; ++q) {
       const int g = q * 256 + tid, r = g / CPR, ph = g % CPR;
-      const int goff = (bt * BK + r) * D;
+      const int key = bt * BK + r;
+      const int goff = !paged ? key * D
+                              : (key < kend ? (int)page_row_off(kp, slot, kvh, nkv, D, key, pbad) : cbytes);
       // a template call written straight into the builtin's argument list
       // leaves the kernel uninstantiated on the host side (no host stub)
       const int koff = goff + ((ph ^ kswz<D>(r)) << 4);
@@ -912,6 +936,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   sweep_end();
   if (tid < D) s_cs[tid] = cs;
   __syncthreads();
+  bound_raise(pbad);
   if (!rvalid) return;
   // O^T layout: lane l holds query l % 32; register r of d-tile t is
   // d = 32 t + 8 (r / 4) + 4 (l / 32) + r % 4
@@ -934,26 +959,27 @@ template <int D, int G>
 hipError_t launch_pf(const int8_t* q8, const int32_t* e_q, const int8_t* kc, const int8_t* vc,
                      const RowMap& seqs, int64_t max_seqlen, int64_t nq, int64_t nkv,
                      int64_t n_slots, int64_t max_pos, int32_t M, int32_t K, int32_t* out,
-                     hipStream_t st) {
+                     hipStream_t st, KvPages kp) {
   constexpr int lds = PfLds<D, G>::bytes;
   const hipError_t err = set_max_lds((const void*)attn_prefill_mfma<D, G>, lds);
   if (err != hipSuccess) return err;
   const int nblk = (int)((max_seqlen + PfCfg<G>::QP - 1) / PfCfg<G>::QP);
   attn_prefill_mfma<D, G><<<dim3((unsigned)nblk, (unsigned)seqs.S, (unsigned)nkv), 256, lds, st>>>(
       q8, e_q, kc, vc, seqs.cu, seqs.start, seqs.seq_slot, (int)nq, (int)nkv, (int)n_slots,
-      (int)max_pos, nblk, M, K, out);
+      (int)max_pos, nblk, M, K, out, kp);
   return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_t(const int8_t* q8, const int32_t* e_q, const int8_t* kc, const int8_t* vc,
                     const RowMap& rows, int64_t R, int64_t nq, int64_t nkv, int64_t n_slots,
-                    int64_t max_pos, int32_t M, int32_t K, int32_t* out, hipStream_t st) {
+                    int64_t max_pos, int32_t M, int32_t K, int32_t* out, hipStream_t st,
+                    KvPages kp) {
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
   const hipError_t err = set_max_lds((const void*)attn_rows<D, G>, 96 * 1024);
   if (err != hipSuccess) return err;
   attn_rows<D, G><<<dim3((unsigned)R, (unsigned)nkv), TPB, lds, st>>>(
-      q8, e_q, kc, vc, rows, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, M, K, out);
+      q8, e_q, kc, vc, rows, (int)nq, (int)nkv, (int)n_slots, (int)max_pos, M, K, out, kp);
   return hipGetLastError();
 }
 
@@ -961,7 +987,7 @@ template <int D, int G, int NT>
 hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
                           const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
-                          hipStream_t st) {
+                          hipStream_t st, KvPages kp) {
   const size_t lds = (size_t)G * max_pos * sizeof(int32_t);
   hipError_t err = set_max_lds((const void*)attn_decode_fused<D, G, true, NT>, 96 * 1024);
   if (err == hipSuccess) err = set_max_lds((const void*)attn_decode_fused<D, G, false, NT>, 96 * 1024);
@@ -971,11 +997,11 @@ hipError_t launch_fused_g(const int32_t* qkv, const QkvPost& p, const int32_t* s
   if (p.qk_norm)
     attn_decode_fused<D, G, true, NT><<<grid, NT, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
                                                          (int)n_slots, (int)max_pos, kc, vc, M, K,
-                                                         out, gq);
+                                                         out, gq, kp);
   else
     attn_decode_fused<D, G, false, NT><<<grid, NT, lds, st>>>(qkv, p, start_pos, slot, (int)nq, (int)nkv,
                                                           (int)n_slots, (int)max_pos, kc, vc, M, K,
-                                                          out, gq);
+                                                          out, gq, kp);
   return hipGetLastError();
 }
 
@@ -990,15 +1016,15 @@ template <int D, int G>
 hipError_t launch_fused_t(const int32_t* qkv, const QkvPost& p, const int32_t* start_pos,
                           const int32_t* slot, int64_t B, int64_t nq, int64_t nkv, int64_t n_slots,
                           int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M, int32_t K, int32_t* out,
-                          hipStream_t st) {
+                          hipStream_t st, KvPages kp) {
   if (G > 1 && B * nkv < 128)
     return launch_fused_g<D, 1, D == 128 ? 512 : 256>(qkv, p, start_pos, slot, B, nq, nkv, n_slots,
-                                                      max_pos, kc, vc, M, K, out, st);
+                                                      max_pos, kc, vc, M, K, out, st, kp);
   // four heads per workgroup with 64-wide heads: the passes are
   // VALU-bound, so two waves per SIMD instead of one
   constexpr int NT = D == 64 && G == 4 ? 512 : 256;
   return launch_fused_g<D, G, NT>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, M,
-                                  K, out, st);
+                                  K, out, st, kp);
 }
 
 }  // namespace
@@ -1009,13 +1035,13 @@ hipError_t launch_attention_decode_fused(const int32_t* qkv, const QkvPost& p,
                                          const int32_t* start_pos, const int32_t* slot, int64_t B,
                                          int64_t nq, int64_t nkv, int64_t d, int64_t n_slots,
                                          int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M,
-                                         int32_t K, int32_t* out, hipStream_t st) {
+                                         int32_t K, int32_t* out, hipStream_t st, KvPages kp) {
   if (B == 0) return hipSuccess;
   const int64_t G = nq / nkv;
 #define DETINT_ATTF(DD, GG)                                                                      \
   if (d == DD && G == GG)                                                                        \
     return launch_fused_t<DD, GG>(qkv, p, start_pos, slot, B, nq, nkv, n_slots, max_pos, kc, vc, \
-                                  M, K, out, st);
+                                  M, K, out, st, kp);
   DETINT_ATTF(64, 1) DETINT_ATTF(64, 2) DETINT_ATTF(64, 4) DETINT_ATTF(64, 8)
   DETINT_ATTF(128, 1) DETINT_ATTF(128, 2) DETINT_ATTF(128, 4) DETINT_ATTF(128, 8)
 #undef DETINT_ATTF
@@ -1026,19 +1052,19 @@ hipError_t launch_attention_seqs(const int8_t* q8, const int32_t* e_q, const int
                                  const int8_t* vc, const RowMap& seqs, int64_t R,
                                  int64_t max_seqlen, int64_t nq, int64_t nkv, int64_t d,
                                  int64_t n_slots, int64_t max_pos, int32_t M, int32_t K,
-                                 int32_t* out, hipStream_t st) {
+                                 int32_t* out, hipStream_t st, KvPages kp) {
   if (R == 0) return hipSuccess;
   const int64_t G = nq / nkv;
   if (max_seqlen >= 16) {
 #define DETINT_PF(DD, GG)                                                                     \
     if (d == DD && G == GG)                                                                   \
       return launch_pf<DD, GG>(q8, e_q, kc, vc, seqs, max_seqlen, nq, nkv, n_slots, max_pos, M, \
-                               K, out, st);
+                               K, out, st, kp);
     DETINT_PF(64, 1) DETINT_PF(64, 2) DETINT_PF(64, 4)
     DETINT_PF(128, 1) DETINT_PF(128, 2) DETINT_PF(128, 4)
 #undef DETINT_PF
   }
-  return launch_attention(q8, e_q, kc, vc, seqs, R, nq, nkv, d, n_slots, max_pos, M, K, out, st);
+  return launch_attention(q8, e_q, kc, vc, seqs, R, nq, nkv, d, n_slots, max_pos, M, K, out, st, kp);
 }
 
 bool attention_supported(int64_t d, int64_t group, int64_t max_pos) {
@@ -1050,13 +1076,13 @@ bool attention_supported(int64_t d, int64_t group, int64_t max_pos) {
 hipError_t launch_attention(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
                             const int8_t* vc, const RowMap& rows, int64_t R, int64_t nq,
                             int64_t nkv, int64_t d, int64_t n_slots, int64_t max_pos, int32_t M,
-                            int32_t K, int32_t* out, hipStream_t st) {
+                            int32_t K, int32_t* out, hipStream_t st, KvPages kp) {
   if (R == 0) return hipSuccess;
   const int64_t G = nq / nkv;
 #define DETINT_ATT(DD, GG)                                                                   \
   if (d == DD && G == GG)                                                                    \
     return launch_t<DD, GG>(q8, e_q, kc, vc, rows, R, nq, nkv, n_slots, max_pos, M, K, out, \
-                            st);
+                            st, kp);
   DETINT_ATT(64, 1) DETINT_ATT(64, 2) DETINT_ATT(64, 4) DETINT_ATT(64, 8)
   DETINT_ATT(128, 1) DETINT_ATT(128, 2) DETINT_ATT(128, 4) DETINT_ATT(128, 8)
 #undef DETINT_ATT

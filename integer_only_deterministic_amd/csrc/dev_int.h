@@ -51,6 +51,7 @@ enum : uint32_t {
   kBoundSwiglu = 8u,    // SwiGLU gate or up outside (-2^24, 2^24)
   kBoundId = 16u,       // token id outside [0, vocab)
   kBoundWeight = 32u,   // a bf16 weight the exact-mode integers cannot hold
+  kBoundPage = 64u,     // a KV block-table entry outside the page pool
 };
 static __device__ uint32_t g_bound_flags;
 
@@ -61,6 +62,10 @@ __device__ __forceinline__ void bound_raise(uint32_t bits) {
 // 1 when |t| >= 2^b (0 < b <= 62)
 __device__ __forceinline__ uint32_t out_of(int64_t t, int b) {
   return (uint64_t)(t + (int64_t(1) << b) - 1) >= (uint64_t(1) << (b + 1)) - 1 ? 1u : 0u;
+}
+// 1 when |t| >= 2^b for an int32 t (0 < b <= 30), in 32-bit arithmetic
+__device__ __forceinline__ uint32_t out_of32(int32_t t, int b) {
+  return (uint32_t)t + ((1u << b) - 1u) >= (2u << b) - 1u ? 1u : 0u;
 }
 // flag bit of a residual-add result t with bound 2^res_bits (0: int32)
 __device__ __forceinline__ uint32_t res_check(int64_t t, int res_bits) {

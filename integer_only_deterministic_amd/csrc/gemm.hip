@@ -219,7 +219,10 @@ template <int BM, int BN, int ST, bool WIDE, int MODE, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __restrict__ A,
                                                  const int8_t* __restrict__ W,
                                                  const int8_t* __restrict__ Wlo, int M, int N,
-                                                 int K, Epi e, void* out) {
+                                                 int K, Epi e, void* out, int kspan) {
+  // Split-K (RAW only): workgroup row blockIdx.y covers K range
+  // [blockIdx.y kspan, (blockIdx.y + 1) kspan) and writes its partial sums to
+  // the int32 slice blockIdx.y of out ([gridDim.y][M][N]); kspan = K otherwise.
   constexpr int NB = WIDE ? 2 : 1;             // weight planes
   constexpr int CPR = PBK / 16;                // chunks per row
   constexpr int SA = BM * PBK, SB = BN * PBK;  // bytes per stage and operand
@@ -250,7 +253,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   const int inr = b - grp * G * nbn, tn = (int)udiv32((uint32_t)inr, (uint32_t)gm);
   const int tm = first + inr - tn * gm;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = K / PBK;
+  const int nk = kspan / PBK, kbase = blockIdx.y * kspan;
+  if (MODE == MODE_RAW && gridDim.y > 1) out = (int32_t*)out + (int64_t)blockIdx.y * M * N;
 
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   // the stage: LDS bytes [16g, 16g + 16) = row g / 8, physical chunk g % 8.
   // Loads 0 .. LA-1 fill A, the rest the weight plane(s).
   auto issue_one = [&](int kt, int i) {
-    const int st = kt % ST, k0 = kt * PBK;
+    const int st = kt % ST, k0 = kbase + kt * PBK;
     if (i < LA) {
       const int g = i * NT + tid, r = g / CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -564,7 +568,37 @@ hipError_t pipe_launch_m(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
   if (err != hipSuccess) return err;
   const int nb = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   gemm_pipe<BM, BN, ST, WIDE, MODE, WGM, WGN><<<nb, 64 * WGM * WGN, lds, st>>>(A, W, Wlo, M, N, K, e,
-                                                                              out);
+                                                                              out, K);
+  return hipGetLastError();
+}
+
+// Split-K over ks workgroup rows (int8 weights, RAW partials into part
+// [ks][M][N]), then one kernel sums the ks partials (exact: |sum| < 2^31 by
+// the K bound) and applies the epilogue.
+__global__ __launch_bounds__(256) void splitk_reduce_k(const int32_t* __restrict__ part, int ks,
+                                                       int M, int N, Epi e, void* out) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= N) return;
+  const int64_t plane = (int64_t)M * N;
+  for (int i = blockIdx.y; i < M; i += gridDim.y) {
+    int64_t v = 0;
+    for (int s = 0; s < ks; ++s) v += part[s * plane + (int64_t)i * N + j];
+    epi_store<false>(v, i, j, N, e, out);
+  }
+}
+
+hipError_t pipe_splitk(const int8_t* A, const int8_t* W, int M, int N, int K, int ks,
+                       const Epi& e, void* out, int32_t* part, hipStream_t st) {
+  constexpr int BMs = 128, BNs = 64, STs = 4;
+  constexpr int lds = STs * (BMs + BNs) * PBK;
+  const hipError_t err = set_max_lds((const void*)gemm_pipe<BMs, BNs, STs, false, MODE_RAW, 2, 2>, lds);
+  if (err != hipSuccess) return err;
+  const int nb = ((M + BMs - 1) / BMs) * ((N + BNs - 1) / BNs);
+  const Epi raw{nullptr, nullptr, nullptr, 0, 0, MODE_RAW, nullptr};
+  gemm_pipe<BMs, BNs, STs, false, MODE_RAW, 2, 2><<<dim3((unsigned)nb, (unsigned)ks), 256, lds, st>>>(
+      A, W, nullptr, M, N, K, raw, part, K / ks);
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
+  splitk_reduce_k<<<grid, 256, 0, st>>>(part, ks, M, N, e, out);
   return hipGetLastError();
 }
 
@@ -1101,6 +1135,26 @@ __global__ __launch_bounds__(256) void exact_combine_k(const int64_t* __restrict
   bound_raise(bad);
 }
 
+__global__ void zero_i32_k(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// workgroup rows of the pipelined split-K for a few-tile int8 shape: the
+// fewest of 2, 4, 8 that reach 192 workgroups (3/4 of the CUs) with every
+// split at least two 128-byte K steps and the partials within part_ints; 1
+// when the shape fills the chip or no split fits
+int pipe_split_count(int64_t M, int64_t N, int64_t K, int64_t part_ints) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 63) / 64);
+  if (tiles >= 192) return 1;
+  for (int ks = 2; ks <= 8; ks *= 2)
+    if ((K / PBK) % ks == 0 && K / ks >= 2 * PBK && ks * M * N <= part_ints && tiles * ks >= 192)
+      return ks;
+  for (int ks = 8; ks >= 2; ks /= 2)
+    if ((K / PBK) % ks == 0 && K / ks >= 2 * PBK && ks * M * N <= part_ints) return ks;
+  return 1;
+}
+
 }  // namespace
 
 bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs) {
@@ -1129,6 +1183,10 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
     return skinny_launch<false, 2>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
   }
   if (K % PBK == 0 && off32) {
+    if (!W_lo && sp && sp->part_ints > 0) {
+      const int ks = pipe_split_count(M, N, K, sp->part_ints);
+      if (ks > 1) return pipe_splitk(A, W, (int)M, (int)N, (int)K, ks, e, out, sp->part, st);
+    }
     if (W_lo) return pipe_dispatch<true>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
     return pipe_dispatch<false>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, st);
   }
@@ -1147,6 +1205,28 @@ hipError_t launch_logits_argmax(const int8_t* A, const int8_t* W, const int8_t* 
                                 int64_t* part, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   return gemv_dispatch(A, W, W_lo, M, N, K, e, logits, part, st);
+}
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  zero_i32_k<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+// Split-K pays for a standalone call only on long K: measured on MI355X
+// (REQ_I8), 512 x 1024 rows x columns: K = 2048 11.2 -> 14.0 us (a loss),
+// K = 4096 17.1 -> 15.8, K = 8192 29.5 -> 17.8; 256 x 1024 x 16384 52.7 ->
+// 18.3 us; skinny 32 x 1024 x 8192 17.5 -> 13.1 us but 64 x 1024 x 3072
+// 12.3 -> 13.4. So a workspace is asked for only from K = 4096 up.
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool limbs) {
+  if (M <= 0 || N <= 0 || K < 4096) return 0;
+  int64_t b = 0;
+  if (gemm_takes_skinny(M, N, K, limbs)) {
+    b = 4 * ((N + 31) / 32) + 256 + 4 * kSplitPairsStandalone * kSplitTileInts;
+  } else if (!limbs && K % PBK == 0 && ((M + 127) / 128) * ((N + 63) / 64) < 192) {
+    b = 4 * 8 * M * N + 256 + 4 * ((N + 31) / 32);
+  }
+  return b;
 }
 
 hipError_t launch_exact_prepare(const uint16_t* W, int64_t N, int64_t K, int8_t* planes,

@@ -44,13 +44,21 @@ hipError_t bound_flags_attention(uint32_t* acc, hipStream_t st);
 // max_tile_splits (tile, split) pairs of up to 2 x 64 x 32 values each plus
 // row sums, and one arrival counter per 32-column tile (max_tiles), which must
 // be zero before the first use (every use leaves them zero).
+// part_ints > 0 also lets the pipelined int8 GEMM split K over workgroup
+// rows for shapes with few tiles: part then holds ks M N int32 partials.
 struct SplitWs {
   int32_t* part;
   int32_t* cnt;
   int64_t max_tile_splits;
   int64_t max_tiles;
+  int64_t part_ints;
 };
 constexpr int64_t kSplitTileInts = 2 * 2 * 1024 + 2 * 32;
+constexpr int64_t kSplitPairsStandalone = 1024;
+// Workspace bytes a standalone GEMM uses for split-K (0: none), and the
+// kernel that clears int32 counters.
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool limbs);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t st);
 
 hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int64_t M,
                        int64_t N, int64_t K, const Epi& e, void* out, hipStream_t st,
@@ -86,6 +94,9 @@ hipError_t launch_rmsnorm(const int32_t* h, const int32_t* row_index, const int1
 hipError_t launch_requant(const int32_t* y, int64_t R, int64_t n, int8_t* q, int32_t* row_e,
                           int32_t* row_m, int32_t* row_k, int32_t fold_m, int32_t fold_k,
                           hipStream_t st);
+// q = clamp8(R(y m, k)) elementwise (16-byte aligned y, 4-byte aligned q)
+hipError_t launch_requant_fixed(const int32_t* y, int64_t n, int32_t m, int32_t k, int8_t* q,
+                                hipStream_t st);
 hipError_t launch_rope(int32_t* x, const int32_t* pos, const int16_t* cos_t,
                        const int16_t* sin_t, int64_t R, int64_t heads, int64_t d, int64_t max_pos,
                        hipStream_t st);
@@ -117,6 +128,17 @@ hipError_t launch_rows_meta(const int32_t* cu, const int32_t* start, const int32
 hipError_t launch_decode_meta(const int32_t* ctx_len, const int32_t* slot, int64_t B,
                               int32_t* pos_of, int32_t* slot_of, hipStream_t st);
 
+// Where the cached rows of a (slot, KV head) live. bt == nullptr: the
+// contiguous layout [n_slots][n_kv][max_pos][d] per layer. Otherwise a paged
+// pool [n_pages][n_kv][2^shift][d] per layer: position j of slot s is row
+// j & (2^shift - 1) of page bt[s * max_blocks + (j >> shift)]. A page index
+// outside [0, n_pages) raises the PAGE bound flag and is read and written as
+// page 0 (memory-safe, results undefined).
+struct KvPages {
+  const int32_t* bt;
+  int32_t max_blocks, shift, n_pages;
+};
+
 // QKV post-processing: q/k-norm (or fixed-point input), RoPE, q DQ, K/V cache
 // writes. qkv int32 [R, (nq + 2 nkv) d].
 struct QkvPost {
@@ -136,7 +158,7 @@ struct QkvPost {
 hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nkv, int64_t d,
                            const int32_t* pos_of, const int32_t* slot_of, const QkvPost& p,
                            int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
-                           int64_t max_pos, hipStream_t st);
+                           int64_t max_pos, hipStream_t st, KvPages kp = KvPages{});
 
 // Where a row sits: either packed sequences (cu != nullptr: row r belongs to
 // the sequence s with cu[s] <= r < cu[s+1], position start[s] + r - cu[s],
@@ -158,20 +180,21 @@ hipError_t launch_attention_seqs(const int8_t* q8, const int32_t* e_q, const int
                                  const int8_t* vc, const RowMap& seqs, int64_t R,
                                  int64_t max_seqlen, int64_t nq, int64_t nkv, int64_t d,
                                  int64_t n_slots, int64_t max_pos, int32_t M, int32_t K,
-                                 int32_t* out, hipStream_t st);
+                                 int32_t* out, hipStream_t st, KvPages kp = KvPages{});
 
 // Attention over the cache for R rows.
 hipError_t launch_attention(const int8_t* q8, const int32_t* e_q, const int8_t* kc,
                             const int8_t* vc, const RowMap& rows, int64_t R, int64_t nq,
                             int64_t nkv, int64_t d, int64_t n_slots, int64_t max_pos, int32_t M,
-                            int32_t K, int32_t* out, hipStream_t st);
+                            int32_t K, int32_t* out, hipStream_t st, KvPages kp = KvPages{});
 // Decode (one row per sequence at position start_pos[b] of slot slot[b]):
 // QKV post-processing of each (row, KV head)'s own heads fused with attention.
 hipError_t launch_attention_decode_fused(const int32_t* qkv, const QkvPost& p,
                                          const int32_t* start_pos, const int32_t* slot, int64_t B,
                                          int64_t nq, int64_t nkv, int64_t d, int64_t n_slots,
                                          int64_t max_pos, int8_t* kc, int8_t* vc, int32_t M,
-                                         int32_t K, int32_t* out, hipStream_t st);
+                                         int32_t K, int32_t* out, hipStream_t st,
+                                         KvPages kp = KvPages{});
 // true when the attention kernel supports (d, n_q / n_kv, max_pos)
 bool attention_supported(int64_t d, int64_t group, int64_t max_pos);
 

@@ -15,11 +15,31 @@
 
 namespace detint {
 
+// Byte offset, within one layer's paged pool, of position j of (slot, KV
+// head kvh); see KvPages. A page index outside the pool sets kBoundPage in
+// `bad` and addresses page 0.
+__device__ __forceinline__ int64_t page_row_off(const KvPages& kp, int slot, int kvh, int nkv, int d,
+                                                int j, uint32_t& bad) {
+  int page = kp.bt[(int64_t)slot * kp.max_blocks + (j >> kp.shift)];
+  if ((unsigned)page >= (unsigned)kp.n_pages) {
+    bad |= kBoundPage;
+    page = 0;
+  }
+  return ((((int64_t)page * nkv + kvh) << kp.shift) + (j & ((1 << kp.shift) - 1))) * d;
+}
+
+// The same offset for either layout, from the layer's cache base.
+__device__ __forceinline__ int64_t kv_row_off(const KvPages& kp, int slot, int kvh, int nkv,
+                                              int max_pos, int d, int j, uint32_t& bad) {
+  if (!kp.bt) return (((int64_t)slot * nkv + kvh) * max_pos + j) * d;
+  return page_row_off(kp, slot, kvh, nkv, d, j, bad);
+}
+
 __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh, int nq, int nkv,
                                          int d, int pos, int slot, bool ok, int32_t rm, int32_t rk,
                                          const QkvPost& p, int8_t* q_dst, int32_t* e_dst,
                                          int8_t* __restrict__ kc, int8_t* __restrict__ vc,
-                                         int max_pos) {
+                                         int max_pos, const KvPages& kp) {
   const int lane = threadIdx.x & 63;
   const int half = d >> 1;
   const bool act = lane < half;
@@ -28,7 +48,9 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
   if (hh >= nq + nkv) {  // V
     if (!act || !ok) return;
     const int kvh = hh - nq - nkv;
-    int8_t* dst = vc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+    uint32_t bad = 0;
+    int8_t* dst = vc + kv_row_off(kp, slot, kvh, nkv, max_pos, d, pos, bad);
+    bound_raise(bad);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int j = t ? j1 : j0;
@@ -87,7 +109,9 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
     if (lane == 0) *e_dst = e;
   } else if (act && ok) {
     const int kvh = hh - nq;
-    int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+    uint32_t bad = 0;
+    int8_t* dst = kc + kv_row_off(kp, slot, kvh, nkv, max_pos, d, pos, bad);
+    bound_raise(bad);
     const int8_t* g = p.k_gain ? p.k_gain + (size_t)kvh * d : nullptr;
     dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - (g ? g[j0] & 7 : 0)));
     dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - (g ? g[j1] & 7 : 0)));

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(SWT) void swiglu_k(const int32_t* __restrict__ gu, 
   for (int i = 0; i < SWPER; ++i) {
     const int j = threadIdx.x + i * SWT;
     p[i] = j < n ? swiglu_p(g[j], u[j], Mg, Kg) : 0;
-    if (j < n) bad |= out_of(g[j], 24) | out_of(u[j], 24);
+    if (j < n) bad |= out_of32(g[j], 24) | out_of32(u[j], 24);
     const int64_t a = (int64_t)uabs64(p[i]);
     A = a > A ? a : A;
   }
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(SWT) void swiglu_rk(const int32_t* __restrict__ gu,
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       p[u][e4] = ok ? swiglu_p(gv[u][e4], uv[u][e4], Mg, Kg) : 0;
-      if (ok) bad |= out_of(gv[u][e4], 24) | out_of(uv[u][e4], 24);
+      if (ok) bad |= out_of32(gv[u][e4], 24) | out_of32(uv[u][e4], 24);
       const int64_t a = (int64_t)uabs64(p[u][e4]);
       A = a > A ? a : A;
     }
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int64_t g = gv[u][e4];
-        if (ok) bad |= out_of(g, 24) | out_of(uv[u][e4], 24);
+        if (ok) bad |= out_of32((int32_t)g, 24) | out_of32(uv[u][e4], 24);
         const int64_t ag = g < 0 ? -g : g;
         const int E = min(diexp(-R(ag * Mg, Kg)), kSigEntries - 1);
         const int32_t q = tab[E];
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
                                                   const int32_t* __restrict__ slot_of, QkvPost p,
                                                   int8_t* __restrict__ q8, int32_t* __restrict__ e_q,
                                                   int8_t* __restrict__ kc, int8_t* __restrict__ vc,
-                                                  int n_slots, int max_pos) {
+                                                  int n_slots, int max_pos, KvPages kp) {
   const int r = blockIdx.x;
   const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int nh = nq + 2 * nkv;
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
   const int32_t rm = p.qk_norm ? p.row_m[r] : 0, rk = p.qk_norm ? p.row_k[r] : 0;
   qkv_head(qkv + (size_t)r * nh * d, hh, nq, nkv, d, pos, slot, ok, rm, rk, p,
            q8 + ((size_t)r * nq + (hh < nq ? hh : 0)) * d, e_q + (size_t)r * nq + (hh < nq ? hh : 0),
-           kc, vc, max_pos);
+           kc, vc, max_pos, kp);
 }
 
 // Without q/k-norm and with 64-wide heads a head needs only 32 lanes (lane i
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
                                                        int32_t* __restrict__ e_q,
                                                        int8_t* __restrict__ kc,
                                                        int8_t* __restrict__ vc, int n_slots,
-                                                       int max_pos) {
+                                                       int max_pos, KvPages kp) {
   constexpr int d = 64, half = 32;
   const int r = blockIdx.x, li = threadIdx.x & 31;
   const int nh = nq + 2 * nkv;
@@ -537,8 +537,9 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
   const int32_t* row = qkv + (size_t)r * nh * d + (size_t)hc * d;
   const int j0 = li, j1 = li + half;
   const int64_t x0 = row[j0], x1 = row[j1];  // f_n fixed point from the GEMM epilogue
+  uint32_t bad = 0;
   if (isv && live && ok) {
-    int8_t* dst = vc + (((size_t)slot * nkv + (hc - nq - nkv)) * max_pos + pos) * d;
+    int8_t* dst = vc + kv_row_off(kp, slot, hc - nq - nkv, nkv, max_pos, d, pos, bad);
     dst[j0] = clamp8(R(x0 * p.vq_m, p.vq_k));
     dst[j1] = clamp8(R(x1 * p.vq_m, p.vq_k));
   }
@@ -546,6 +547,8 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
   const int64_t c = p.cos_t[(size_t)pc * half + li], sn = p.sin_t[(size_t)pc * half + li];
   int64_t y0 = ok ? R(x0 * c - x1 * sn, 14) : 0;
   int64_t y1 = ok ? R(x1 * c + x0 * sn, 14) : 0;
+  if (live && !isv) bad |= i32_check(y0) | i32_check(y1);  // rotated q / k within int32
+  bound_raise(bad);
   const int kvh = isq ? hc >> (__builtin_ctz(nq) - __builtin_ctz(nkv)) : (isv ? 0 : hc - nq);
   const int g0 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j0] & 7 : 0;
   const int g1 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j1] & 7 : 0;
@@ -567,7 +570,9 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
     qd[j1] = clamp8(R(y1, e));
     if (li == 0) e_q[(size_t)r * nq + hc] = e;
   } else if (ok) {
-    int8_t* dst = kc + (((size_t)slot * nkv + kvh) * max_pos + pos) * d;
+    uint32_t badk = 0;
+    int8_t* dst = kc + kv_row_off(kp, slot, kvh, nkv, max_pos, d, pos, badk);
+    bound_raise(badk);
     dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
     dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
   }
@@ -649,6 +654,31 @@ __global__ void advance_k(int32_t* ids, const int32_t* next_tok, int32_t* start_
 bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 }  // namespace
+
+namespace {
+// q = clamp8(R(y m, k)), four elements per thread (n % 4 == 0 handled by
+// the tail loop of the last thread block)
+__global__ __launch_bounds__(256) void requant_fixed_k(const int32_t* __restrict__ y, int64_t n,
+                                                       int32_t m, int32_t k, int8_t* __restrict__ q) {
+  const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (i + 4 <= n) {
+    const v4i v = *(const v4i*)(y + i);
+    *(uint32_t*)(q + i) = pack4(R((int64_t)v.x * m, k), R((int64_t)v.y * m, k),
+                                R((int64_t)v.z * m, k), R((int64_t)v.w * m, k));
+  } else {
+    for (int64_t t = i; t < n; ++t) q[t] = clamp8(R((int64_t)y[t] * m, k));
+  }
+}
+}  // namespace
+
+hipError_t launch_requant_fixed(const int32_t* y, int64_t n, int32_t m, int32_t k, int8_t* q,
+                                hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 1023) / 1024;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  requant_fixed_k<<<(unsigned)blocks, 256, 0, st>>>(y, n, m, k, q);
+  return hipGetLastError();
+}
 
 DETINT_BOUND_READER(bound_flags_rowops)
 
@@ -787,18 +817,19 @@ hipError_t launch_decode_meta(const int32_t* ctx_len, const int32_t* slot, int64
 hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nkv, int64_t d,
                            const int32_t* pos_of, const int32_t* slot_of, const QkvPost& p,
                            int8_t* q8, int32_t* e_q, int8_t* kc, int8_t* vc, int64_t n_slots,
-                           int64_t max_pos, hipStream_t st) {
+                           int64_t max_pos, hipStream_t st, KvPages kp) {
   if (R == 0) return hipSuccess;
   if (!p.qk_norm && d == 64) {  // two heads per wave
     const unsigned hp = (unsigned)((nq + 2 * nkv + 2 * (TPB / 64) - 1) / (2 * (TPB / 64)));
     qkv_post_pair_k<<<dim3((unsigned)R, hp), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, pos_of, slot_of,
                                                            p, q8, e_q, kc, vc, (int)n_slots,
-                                                           (int)max_pos);
+                                                           (int)max_pos, kp);
     return hipGetLastError();
   }
   const unsigned hb = (unsigned)((nq + 2 * nkv + 3) / 4);  // 4 heads (waves) per workgroup
   qkv_post_k<<<dim3((unsigned)R, hb), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, (int)d, pos_of, slot_of,
-                                                     p, q8, e_q, kc, vc, (int)n_slots, (int)max_pos);
+                                                     p, q8, e_q, kc, vc, (int)n_slots, (int)max_pos,
+                                                     kp);
   return hipGetLastError();
 }
 

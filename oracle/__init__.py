@@ -115,6 +115,7 @@ def _declare(L):
     L.orc_epilogue.argtypes = [i64p, i64, i64, i32p, i32p, i32p, i32, i32, i32, vp]
     L.orc_rmsnorm.argtypes = [i32p, i16p, i64, i64, i8p, i32p, i32p]
     L.orc_requant_rows.argtypes = [i32p, i64, i64, i8p, i32p]
+    L.orc_requant_fixed.argtypes = [i32p, i64, i32, i32, i8p]
     L.orc_rope.argtypes = [i32p, i32p, i16p, i16p, i64, i64, i64, i64]
     L.orc_softmax.argtypes = [i32p, i32p, i32p, i64, i64, i32, i32, i16p]
     L.orc_swiglu.argtypes = [i32p, i64, i64, i32, i8p, i32p, i32p]
@@ -305,6 +306,14 @@ def requant_rows(y):
     e = np.zeros(R_, np.int32)
     lib().orc_requant_rows(y, R_, n, q, e); _check()
     return q, e
+
+
+def requant_fixed(y, m: int, k: int):
+    """clamp8(R(y * m, k)) elementwise (the K/V cache quantisation)."""
+    y = _c(y, np.int32)
+    q = np.zeros(y.shape, np.int8)
+    lib().orc_requant_fixed(y.ravel(), y.size, int(m), int(k), q.ravel()); _check()
+    return q
 
 
 def rope(x, pos, cos_t, sin_t):

@@ -438,6 +438,13 @@ int orc_requant_rows(const int32_t *y, int64_t rows, int64_t n, int8_t *q, int32
   return g_err;
 }
 
+/* Requantisation at a fixed dyadic scale ([BLOG] "DetLLM": K and V are
+ * quantised once at fixed offline scales): q = clamp8(R(y * m, k)). */
+int orc_requant_fixed(const int32_t *y, int64_t n, int32_t m, int32_t k, int8_t *q) {
+  for (int64_t i = 0; i < n; i++) q[i] = clamp8(R((int64_t)y[i] * m, k));
+  return g_err;
+}
+
 /* Per-head RMSNorm of q or k (Qwen3 q/k-norm, which [BLOG] footnote 8 places
  * before RoPE). Input a_j = acc_j * m_c_j (the per-tensor column shift and the
  * row scale cancel in a normalisation). Pre-shift p = max(0, bl(max|a|) - 24),

@@ -35,6 +35,7 @@ def host(t):
 
 @pytest.mark.parametrize("K,N", S.GEMM_SWEEP_KN)
 def test_gemm_sweep(D, K, N):
+    import torch
     """The standalone sweep: M in {1, 8, 64, 512, 2048} x the five projection
     shapes, RAW int32 and per-row x per-column requant to int8, every output
     element against the oracle's int64 brute force."""
@@ -42,12 +43,17 @@ def test_gemm_sweep(D, K, N):
         g = S.make_gemm_operands(M, N, K, seed=7)
         A, W = dev(g["A"]), dev(g["W"])
         rm, rk, cm = dev(g["row_m"]), dev(g["row_k"]), dev(g["col_m"])
-        raw = host(D.detint_gemm_i8(A, W))
-        q = host(D.detint_gemm_i8(A, W, rm, rk, cm, g["col_k"], 0, D.REQ_I8))
         acc = O.gemm(g["A"], g["W"])                 # every row, int64 brute force
-        np.testing.assert_array_equal(raw, acc, err_msg=f"RAW M={M} N={N} K={K}")
         want = O.epilogue(acc, g["row_m"], g["row_k"], g["col_m"], g["col_k"], 0, O.REQ_I8)
-        np.testing.assert_array_equal(q, want, err_msg=f"REQ_I8 M={M} N={N} K={K}")
+        need = D.detint_gemm_workspace(M, N, K)
+        for ws in (None, torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None):
+            raw = host(D.detint_gemm_i8(A, W, ws=ws))
+            q = host(D.detint_gemm_i8(A, W, rm, rk, cm, g["col_k"], 0, D.REQ_I8, ws=ws))
+            tag = f"M={M} N={N} K={K} ws={ws is not None}"
+            np.testing.assert_array_equal(raw, acc, err_msg=f"RAW {tag}")
+            np.testing.assert_array_equal(q, want, err_msg=f"REQ_I8 {tag}")
+            if need == 0:
+                break
         del A, W, acc, want, raw, q
 
 
@@ -62,8 +68,10 @@ def test_gemm_sweep(D, K, N):
                                    (200, 300, 256), (1000, 3000, 256), (1000, 6100, 256),
                                    (2000, 6000, 128),
                                    (32, 1000, 2048), (20, 100, 512), (50, 77, 1024),
-                                   (5, 300, 1040), (8, 333, 2064)])
+                                   (5, 300, 1040), (8, 333, 2064),
+                                   (300, 1000, 8192), (40, 700, 4096), (512, 1024, 16384)])
 def test_gemm_ragged_all_modes(D, M, N, K):
+    import torch
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
     W = rng.integers(-128, 128, (N, K)).astype(np.int8)
@@ -75,14 +83,20 @@ def test_gemm_ragged_all_modes(D, M, N, K):
     acc = O.gemm(A, W)
     base = rng.integers(-(1 << 20), 1 << 20, (M, N)).astype(np.int32)
     dA, dW, drm, drk, dcm = dev(A), dev(W), dev(rm), dev(rk), dev(cm)
-    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW)), acc)
-    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 0, D.REQ_I8)),
-                                  O.epilogue(acc, rm, rk, cm, 22, 0, O.REQ_I8))
-    np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.FIX)),
-                                  O.epilogue(acc, rm, rk, cm, 22, 8, O.FIX))
-    out = dev(base)
-    D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.RES_ADD, out=out)
-    np.testing.assert_array_equal(host(out), O.epilogue(acc, rm, rk, cm, 22, 8, O.RES_ADD, out=base))
+    need = D.detint_gemm_workspace(M, N, K)
+    # with a workspace, few-tile shapes split K (skinny last-arriver sums or
+    # pipelined partials plus a summing epilogue); same bits
+    for ws in (None, torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None):
+        np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, ws=ws)), acc)
+        np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 0, D.REQ_I8, ws=ws)),
+                                      O.epilogue(acc, rm, rk, cm, 22, 0, O.REQ_I8))
+        np.testing.assert_array_equal(host(D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.FIX, ws=ws)),
+                                      O.epilogue(acc, rm, rk, cm, 22, 8, O.FIX))
+        out = dev(base)
+        D.detint_gemm_i8(dA, dW, drm, drk, dcm, 22, 8, D.RES_ADD, out=out, ws=ws)
+        np.testing.assert_array_equal(host(out), O.epilogue(acc, rm, rk, cm, 22, 8, O.RES_ADD, out=base))
+        if need == 0:
+            break
 
 
 @pytest.mark.parametrize("mode", ["REQ_I8", "FIX", "RES_ADD"])
@@ -143,6 +157,13 @@ def test_gemm_w16_limbs(D, M, N, K):
     np.testing.assert_array_equal(host(lo), ((w & 255) - 128).astype(np.int8))
     acc = O.gemm(A, W16)
     dA, drm, drk, dcm = dev(A), dev(rm), dev(rk), dev(cm)
+    need = D.detint_gemm_workspace(M, N, K, limbs=True)
+    if need:                  # skinny limb shapes: split K with a workspace, same bits
+        import torch
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, ws=ws)), acc)
+        np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 12, D.FIX, ws=ws)),
+                                      O.epilogue(acc, rm, rk, cm, 30, 12, O.FIX))
     np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo)), acc)
     np.testing.assert_array_equal(host(D.detint_gemm_w16(dA, hi, lo, drm, drk, dcm, 30, 12, D.FIX)),
                                   O.epilogue(acc, rm, rk, cm, 30, 12, O.FIX))
@@ -221,6 +242,14 @@ def test_requant(D, R, n):
     oq, oe = O.requant_rows(y)
     np.testing.assert_array_equal(host(q), oq)
     np.testing.assert_array_equal(host(e), oe)
+
+
+@pytest.mark.parametrize("n", [1, 7, 4096, 100003])
+def test_requant_fixed(D, n):
+    rng = np.random.default_rng(n)
+    y = rng.integers(-(1 << 24), 1 << 24, n).astype(np.int32)
+    for m, k in ((3 << 13, 15), (20000, 30), (1, 0)):
+        np.testing.assert_array_equal(host(D.detint_requant_fixed(dev(y), m, k)), O.requant_fixed(y, m, k))
 
 
 @pytest.mark.parametrize("d,base", [(64, 1_000_000), (128, 1_000_000), (64, 500_000)])

@@ -73,23 +73,29 @@ def test_validation_rejects_before_device_work(D):
     lib = D.library()
     fake = C.c_void_p(4096)
     # K not a multiple of 16
-    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 15, None, None, None, 0, 0, D.RAW, fake, None)
+    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 15, None, None, None, 0, 0, D.RAW, fake, None, 0, None)
     assert rc == D.DETINT_EINVAL and b"multiple of 16" in lib.detint_last_error()
     # misaligned operand
-    rc = lib.detint_gemm_i8(C.c_void_p(4097), fake, 4, 4, 16, None, None, None, 0, 0, D.RAW, fake, None)
+    rc = lib.detint_gemm_i8(C.c_void_p(4097), fake, 4, 4, 16, None, None, None, 0, 0, D.RAW, fake, None, 0, None)
     assert rc == D.DETINT_EINVAL
     # K beyond the int32 accumulator bound
-    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 1 << 20, None, None, None, 0, 0, D.RAW, fake, None)
+    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 1 << 20, None, None, None, 0, 0, D.RAW, fake, None, 0, None)
     assert rc == D.DETINT_EINVAL
     # scaled modes need scales
-    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 16, None, None, None, 0, 0, D.REQ_I8, fake, None)
+    rc = lib.detint_gemm_i8(fake, fake, 4, 4, 16, None, None, None, 0, 0, D.REQ_I8, fake, None, 0, None)
     assert rc == D.DETINT_EINVAL
     # empty GEMM is a no-op
-    assert lib.detint_gemm_i8(None, None, 0, 4, 16, None, None, None, 0, 0, D.RAW, None, None) == 0
+    assert lib.detint_gemm_i8(None, None, 0, 4, 16, None, None, None, 0, 0, D.RAW, None, None, 0, None) == 0
     # the int32 accumulator bound: 131072 * (-128)^2 = 2^31 does not fit, 131056 does
-    assert lib.detint_gemm_i8(None, None, 0, 4, 131056, None, None, None, 0, 0, D.RAW, None, None) == 0
+    assert lib.detint_gemm_i8(None, None, 0, 4, 131056, None, None, None, 0, 0, D.RAW, None, None, 0, None) == 0
     assert lib.detint_gemm_i8(None, None, 0, 4, 131072, None, None, None, 0, 0, D.RAW, None,
-                              None) == D.DETINT_EINVAL
+                              None, 0, None) == D.DETINT_EINVAL
+    # workspace sizes: split-K only where the shape gives few tiles
+    assert lib.detint_gemm_workspace(32, 1024, 8192, 0) > 0          # skinny rows, long K
+    assert lib.detint_gemm_workspace(512, 1024, 8192, 0) >= 4 * 8 * 512 * 1024
+    assert lib.detint_gemm_workspace(512, 1024, 2048, 0) == 0        # short K: no split
+    assert lib.detint_gemm_workspace(2048, 151936, 1024, 0) == 0     # fills the chip
+    assert lib.detint_gemm_workspace(-1, 4, 16, 0) == -1
     # unsupported attention head_dim
     rc = lib.detint_attn_decode(fake, fake, fake, fake, 1, fake, fake, 1, 4, 2, 96, 64, 1 << 14, 10,
                                 fake, None)

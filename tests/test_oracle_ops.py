@@ -154,6 +154,19 @@ def test_rmsnorm_sum_of_squares_domain():
         O.rmsnorm(np.full((1, 16384), 1 << 24, np.int32), g)
 
 
+def test_requant_fixed_is_the_rounded_real_product():
+    """clamp8 of y * m / 2^k rounded half up, by exact rationals, over values
+    that hit both clamps, exact halves and negative halves."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    y = np.concatenate([rng.integers(-(1 << 24), 1 << 24, 500), [0, 1, -1, 3, -3, 5, -5]]).astype(np.int32)
+    for m, k in ((3 << 13, 15), (20000, 30), (1, 0), (16384, 14)):
+        q = O.requant_fixed(y, m, k)
+        for v, got in zip(y, q):
+            want = (Fraction(int(v) * m, 2 ** k) + Fraction(1, 2)).__floor__()
+            assert got == max(-127, min(127, want)), (int(v), m, k)
+
+
 def test_requant_rows():
     rng = np.random.default_rng(18)
     y = rng.integers(-(1 << 22), 1 << 22, (20, 2048)).astype(np.int32)
