@@ -488,6 +488,34 @@ def cpu_baseline(m, p0, seconds: float, gpu_tokens):
                        f"tokens {'equal' if agree else 'DIFFER from'} the GPU run's")
 
 
+def barrier_probe(D, torch):
+    """Cost of one device-wide barrier between 256 resident workgroups (the
+    step a persistent decode kernel would take between phases), per mode of
+    detint_probe_barrier, against one node of a HIP graph of tiny kernels
+    (what each phase costs as its own launch)."""
+    names = {0: "flags_release_acquire", 1: "counter_release_acquire",
+             2: "two_level_flags_release_acquire", 3: "flags_relaxed_no_fences_lower_bound"}
+    out = {}
+    for mode, name in names.items():
+        fails = D.detint_probe_barrier(mode, 20) | D.detint_probe_barrier(mode, 2020)
+        t20 = timed(lambda: D.detint_probe_barrier(mode, 20, wait=False), 5, torch)
+        t2020 = timed(lambda: D.detint_probe_barrier(mode, 2020, wait=False), 5, torch)
+        out[name] = {"us_per_barrier": round((t2020 - t20) / 2000 * 1e6, 3), "failures": fails}
+    x = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        x.add_(1)
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(140):
+                x.add_(1)
+    torch.cuda.current_stream().wait_stream(st)
+    out["graph_node_us"] = round(timed(g.replay, 20, torch) / 140 * 1e6, 3)
+    out["workgroups"] = 256
+    return out
+
+
 def decode_only(D, S, torch, steps: int, warmup: int):
     """Batch-1 decode of the Qwen3-0.6B shape for counter runs: prefill, a
     few graph replays, then the copy calibration."""
@@ -516,6 +544,7 @@ def main():
     ap.add_argument("--no-llama", action="store_true")
     ap.add_argument("--llama-only", action="store_true")
     ap.add_argument("--llama-steps", type=int, default=2048)
+    ap.add_argument("--barrier-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py: runs on one GPU only (the integer forward pass is data-parallel by "
@@ -542,6 +571,9 @@ def main():
         return
     if args.llama_only:
         print(json.dumps(llama_case(D, S, torch, args.llama_steps)), flush=True)
+        return
+    if args.barrier_probe:
+        print(json.dumps({"grid_barrier_probe": barrier_probe(D, torch)}), flush=True)
         return
 
     gold = json.loads((ROOT / "tests" / "golden" / "qwen3_b1.json").read_text())
@@ -628,6 +660,8 @@ def main():
 
     log("integer sampling")
     sampling = sampling_case(D, torch, not args.no_cpu)
+    log("grid barrier probe")
+    barrier = barrier_probe(D, torch)
     cpu = None
     c1_cpu = None
     if not args.no_cpu:
@@ -686,6 +720,7 @@ def main():
         "gemm_sweep_req_i8": gemm,
         "gemm_best_frac_i8_mfma": round(max(big), 4),
         "gemm_sweep_oracle_gops": c1_cpu,
+        "grid_barrier_probe": barrier,
         "final_head_kernel_roofline": {
             "bound": "hbm",
             "kernel": "fused final RMSNorm + tied lm_head GEMV, 1 row (fgemv<1,2,1,1,4>), cache-cold launches",

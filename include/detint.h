@@ -496,6 +496,20 @@ detint_status detint_layer_forward(const detint_model *m, int64_t layer, int32_t
                                    const int32_t *slot, int64_t S, int64_t max_seqlen, void *ws,
                                    int64_t ws_bytes, void *stream);
 
+/* Measurement, not part of the forward pass: runs `rounds` device-wide
+ * barriers between 256 resident workgroups (one per CU) on `stream`, each
+ * round exchanging a 64-int row per workgroup, so that the barrier's cost
+ * (kernel time / rounds) can be set against a graph node per decode phase.
+ * mode 0: per-workgroup generation flags, release store and acquire fence;
+ * 1: one arrival counter (release RMW); 2: two levels of flags (8 groups,
+ * then their leaders); 3: mode 0's flags with relaxed stores and no fences
+ * (a hardware lower bound, not a barrier the memory model guarantees).
+ * Every wait is bounded: when one runs out of polls its workgroup returns.
+ * When `result` is non-null the call waits for the stream and writes the
+ * run's failure bits (1: a wait ran out, 2: a row read back wrong).
+ * DETINT_EUNSUPPORTED on a device with fewer than 256 CUs. */
+detint_status detint_probe_barrier(int32_t mode, int32_t rounds, uint32_t *result, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

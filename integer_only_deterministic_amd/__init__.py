@@ -61,6 +61,7 @@ _SIGS = {
     "detint_version": (C.c_char_p, []),
     "detint_last_error": (C.c_char_p, []),
     "detint_check": (i32, [vp, C.POINTER(C.c_uint32)]),
+    "detint_probe_barrier": (i32, [i32, i32, C.POINTER(C.c_uint32), vp]),
     "detint_gemm_workspace": (i64, [i64, i64, i64, i32]),
     "detint_gemm_i8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
     "detint_gemm_w16": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, i32, i32, i32, vp, vp, i64, vp]),
@@ -160,6 +161,14 @@ def detint_check() -> int:
     if rc not in (DETINT_OK, DETINT_EBOUND):
         raise DetintError(rc, lib.detint_last_error().decode())
     return int(f.value)
+
+
+def detint_probe_barrier(mode: int, rounds: int, wait: bool = True):
+    """Enqueue `rounds` device-wide barriers of the given mode (a measurement,
+    see detint.h); with wait, synchronise and return the failure bits."""
+    f = C.c_uint32(0)
+    _call("detint_probe_barrier", int(mode), int(rounds), C.byref(f) if wait else None, _stream())
+    return int(f.value) if wait else None
 
 
 def detint_gemm_workspace(M: int, N: int, K: int, limbs: bool = False) -> int:

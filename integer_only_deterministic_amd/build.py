@@ -11,7 +11,7 @@ HERE = Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 OUT = HERE / "libdetint.so"
 BUILD = HERE / "_build"
-SOURCES = ["gemm.hip", "decode.hip", "rowops.hip", "attention.hip", "api.hip"]
+SOURCES = ["gemm.hip", "decode.hip", "rowops.hip", "attention.hip", "probe.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

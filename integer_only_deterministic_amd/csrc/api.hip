@@ -969,3 +969,16 @@ detint_status detint_forward_kv(const detint_model* m, const detint_kv_desc* kv,
 }
 
 }  // extern "C"
+
+extern "C" detint_status detint_probe_barrier(int32_t mode, int32_t rounds, uint32_t* result,
+                                              void* stream) {
+  REQUIRE(mode >= 0 && mode <= 3 && rounds >= 0 && rounds <= (1 << 20),
+          "probe_barrier: mode in 0..3 and rounds in 0..2^20");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e, "probe_barrier");
+  if (cus < 256)
+    return fail(DETINT_EUNSUPPORTED, "probe_barrier: needs 256 CUs (one resident workgroup each), found %d", cus);
+  return hip_status(launch_probe_barrier(mode, rounds, result, S_(stream)), "probe_barrier");
+}

@@ -238,4 +238,8 @@ hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, cons
                                 int64_t M, int64_t V, int64_t K, int32_t* logits,
                                 const int32_t* row_base, int64_t* part, hipStream_t st);
 
+// Device-wide barrier measurement (256 resident workgroups; mode 0..3; the
+// failure bits of the last run into *result after a stream sync, if given).
+hipError_t launch_probe_barrier(int mode, int rounds, uint32_t* result, hipStream_t st);
+
 }  // namespace detint

@@ -132,6 +132,9 @@ def test_validation_rejects_before_device_work(D):
     # candidates (16384 x 8 B), 149 slice maxima and 596 step sums, 75 cut keys
     assert lib.detint_sample_workspace(8, 151936) == 8 * (16384 * 8 + 149 * 20 + 75 * 4)
     assert lib.detint_sample_workspace(1, 262145) == -1
+    # barrier probe: mode and round ranges
+    assert lib.detint_probe_barrier(4, 10, None, None) == D.DETINT_EINVAL
+    assert lib.detint_probe_barrier(0, -1, None, None) == D.DETINT_EINVAL
 
 
 def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
