@@ -668,53 +668,58 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
 // Computing S^T rather than S leaves each lane with 16 keys of one query in
 // its accumulator registers (lane l: query l % 32; register r: key
 // 8 (r / 4) + 4 (l / 32) + r % 4), which is exactly a 16-byte MFMA operand of
-// P^T once the contraction runs over keys in that order; V^T is staged in
-// LDS with its keys permuted the same way. Row statistics become per-lane
-// values plus one exchange between the two half-waves. Masked keys (past the
-// query's position, or past the chunk's end) get P = 0, i.e. Ph = 0,
-// Pl = -128, which the colsum term cancels exactly.
+// P^T once the contraction runs over keys in that order; the V^T operand is
+// read from the row-major V tile with LDS transpose reads in the same key
+// order. Row statistics become per-lane values plus one exchange between the
+// two half-waves. Masked keys (past the query's position, or past the
+// chunk's end) get P = 0, i.e. Ph = 0, Pl = -128, which the colsum term
+// cancels exactly; the column sums are taken over the chunks each wave
+// actually multiplies.
 template <int G>
 struct PfCfg {
   static constexpr int PT = 4 / G;       // 32-position tiles per workgroup
   static constexpr int QP = 32 * PT;     // query positions per workgroup
 };
 
-// position k' = 16 h + b of key 8 (b / 4) + 4 h + b % 4 in the P.V contraction
-__device__ __forceinline__ int key_slot(int key) {
-  return 16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3);
-}
-
 template <int D, int G>
 struct PfLds {
   static constexpr int BK = 256;           // keys per staged batch (8 chunks)
   static constexpr int KB = BK * D;        // bytes of K (or V) per batch
-  static constexpr int VST = 48;           // V^T row stride (bytes; 16-byte aligned)
-  static constexpr int bytes = 4 * KB + 2 * D * VST + D * 4;
+  static constexpr int bytes = 4 * KB;     // K and V, each double-buffered
 };
 
-// K rows in LDS: 16-byte chunk c of key row r sits at chunk c ^ swz(r), so the
-// 16 rows one MFMA operand read touches per LDS cycle hit 16 distinct slots
-// of the 256-byte bank window.
+// K and V rows in LDS: 16-byte chunk c of key row r sits at chunk c ^ swz(r).
+// The 16 rows one MFMA operand read of K touches per LDS cycle then hit 16
+// distinct slots of the 256-byte bank window, and the transposed reads of V
+// below spread their 128 dwords evenly over the banks (two per bank).
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
   return D == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane j receives byte
+// j % 8 of the 8 bytes read by lanes 2 m + j / 8 (m = 0..7), as byte m.
+__device__ __forceinline__ v2i_t lds_read_tr8(const int8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t*)(p));
+}
+
+// d = 64 fits two workgroups per CU in LDS (64 KiB each): keep the registers
+// within 256 so that both are resident
 template <int D, int G>
-__global__ __launch_bounds__(256) void attn_prefill_mfma(
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
     const int8_t* __restrict__ q8, const int32_t* __restrict__ e_q, const int8_t* __restrict__ kc,
     const int8_t* __restrict__ vc, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
     const int32_t* __restrict__ seq_slot, int nq, int nkv, int n_slots, int max_pos, int nblk,
     int32_t Ms, int32_t Ks, int32_t* __restrict__ out, KvPages kp) {
   constexpr int QP = PfCfg<G>::QP, KS = D / 32, CPR = D / 16;
   using L = PfLds<D, G>;
-  constexpr int BK = L::BK, KB = L::KB, VST = L::VST;
+  constexpr int BK = L::BK, KB = L::KB;
   constexpr int LPB = KB / 4096;  // DMA loads per thread per batch and operand
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
   int8_t* sK = smem;                 // [2][KB]
   int8_t* sV = smem + 2 * KB;        // [2][KB]
-  int8_t* vt = smem + 4 * KB;        // [2][D * VST]
-  int32_t* s_cs = (int32_t*)(vt + 2 * D * VST);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ql = lane & 31;
   const int qb = nblk - 1 - (int)blockIdx.x, sq = blockIdx.y, kvh = blockIdx.z;
   const int r0 = cu[sq], len = cu[sq + 1] - r0;
@@ -743,7 +748,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
                                                                       cbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0,
                                                                       cbytes, 0x00020000);
-  // batch bt of K (swizzled) and, for pass 3, V (natural) into buffer bt & 1:
+  // batch bt of K and, for pass 3, V (both swizzled) into buffer bt & 1:
   // load q of thread t moves chunk g = 256 q + t, LDS bytes [16 g, 16 g + 16)
   auto issue = [&](int bt, bool withv) {
     const int buf = bt & 1;
@@ -755,12 +760,12 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
                               : (key < kend ? (int)page_row_off(kp, slot, kvh, nkv, D, key, pbad) : cbytes);
       // a template call written straight into the builtin's argument list
       // leaves the kernel uninstantiated on the host side (no host stub)
-      const int koff = goff + ((ph ^ kswz<D>(r)) << 4);
+      const int soff = goff + ((ph ^ kswz<D>(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, DETINT_LDS(sK + buf * KB + (q * 256 + wave * 64) * 16),
-                                               16, koff, 0, 0, 0);
+                                               16, soff, 0, 0, 0);
       if (withv)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, DETINT_LDS(sV + buf * KB + (q * 256 + wave * 64) * 16),
-                                                 16, goff + (ph << 4), 0, 0, 0);
+                                                 16, soff, 0, 0, 0);
     }
   };
 
@@ -771,9 +776,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     qf[ks] = rvalid ? *(const v4i*)(q8 + ((size_t)row * nq + hq) * D + 32 * ks + 16 * hh) : z4;
   const int sh = Ks - (rvalid ? e_q[(size_t)row * nq + hq] : 0);
   const bool fast = sh >= 1 && sh <= 62 && Ms > 0;
-  const bool wfast = __all(fast);  // every lane of the wave on the fast form
   const uint32_t d0 = exp32_limit(Ms, sh);
-  const bool wfast32 = __all(d0 != 0);  // ... and on its 32-bit form
+  const bool wfast32 = __all(d0 != 0);  // every lane of the wave on the 32-bit form
   // chunks below every query of this wave's tile need no causal mask
   const int pmin = p0 + qb * QP + (wave / G) * 32;
 
@@ -791,7 +795,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     }
     return acc;
   };
-  auto key_of = [&](int c, int r) { return c * 32 + 8 * (r >> 2) + 4 * hh + (r & 3); };
+  // key offset within its chunk of accumulator register r
+  auto koff = [&](int r) { return 8 * (r >> 2) + 4 * hh + (r & 3); };
   // Each pass walks the chunks with batches staged one ahead: at a batch's
   // start, wait for it, then a barrier (which also retires every wave's
   // reads of the buffer the next issue overwrites), then issue the next.
@@ -819,7 +824,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key_of(c, r) <= pos) mx = max(mx, sacc[r]);
+          if (c * 32 + koff(r) <= pos) mx = max(mx, sacc[r]);
       }
     }
   }
@@ -827,114 +832,152 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   mx = max(mx, __shfl_xor(mx, 32));
   if (!live) mx = 0;  // its values are never used; keep the arithmetic tame
 
+  // E(s) = DI-Exp(R((s - mx) Ms, sh)) for s <= mx. The 32-bit form is
+  // exp_delta32 of mx - s with the clamp at d0 moved onto the score: v =
+  // (mx - max(s, mx - d0)) Ms + 2^(sh-1) - 1, shifted by sh, evaluated as
+  // C - max(s, slo) Ms mod 2^32 (its value is below 2^31); then n = v >> 15
+  // <= 31, f = (2^16 - v mod 2^15) >> 1 = 2^15 - R(v mod 2^15, 1), and
+  // E = R(f, n), which is 0 from n = 17 on. Other waves take the 64-bit
+  // forms.
+  const int32_t slo = mx - (int32_t)d0;
+  const uint32_t c32 = (uint32_t)mx * (uint32_t)Ms + ((1u << ((sh - 1) & 31)) - 1u);
+  auto e32 = [&](int32_t s) -> uint32_t {
+    const uint32_t v = (c32 - (uint32_t)__mul24(max(s, slo), Ms)) >> sh;
+    const uint32_t n = v >> 15, f = (65536u - (v & 32767u)) >> 1;
+    return (f + ((1u << n) >> 1)) >> n;
+  };
+  auto e64 = [&](int32_t s) -> uint32_t {
+    return (uint32_t)(fast ? exp_delta((uint32_t)(mx - s), (uint32_t)Ms, sh)
+                           : diexp(R(((int64_t)s - mx) * Ms, sh)));
+  };
+  // A chunk's 32 x 32 tile is dead when every exponential in it is 0. E
+  // does not increase as the score falls (Ms > 0), so E at the lane's
+  // largest score of the chunk being 0 (masked keys included, and that
+  // score no larger than the row maximum) clears the lane's 16 keys; lanes
+  // without a live query are dead. A wave skips a dead tile in passes 2
+  // and 3: it adds nothing to D, to P.V or to the column sums below.
+  auto dead = [&](const v16i& sacc, auto ef) {
+    int32_t cm = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) cm = max(cm, sacc[r]);
+    return __all(!live || (Ms > 0 && cm <= mx && ef(cm) == 0u));
+  };
+
   // pass 2: sum of exponentials
   int64_t den = 0;
+  auto sum_chunk = [&](int c, const v16i& sacc, auto ef) {
+    uint32_t part = 0;  // 16 terms of at most 2^15
+    if (c * 32 + 31 <= pmin) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += ef(sacc[r]);
+    } else {
+      const int lim = pos - c * 32;  // key offsets <= lim are causal
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += koff(r) <= lim ? ef(sacc[r]) : 0u;
+    }
+    den += part;
+  };
   issue(0, false);
   for (int bt = 0; bt < nbt; ++bt) {
     batch_begin(bt, false);
     for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
       const v16i sacc = scores(c);
-      const int lim = pos - c * 32;  // key offsets <= lim are causal
-      int32_t part = 0;              // 16 terms of at most 2^15
       if (wfast32) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t E = exp_delta32((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh, d0);
-          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
-        }
-      } else if (wfast) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t E = exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh);
-          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t E = fast ? exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh)
-                                 : diexp(R(((int64_t)sacc[r] - mx) * Ms, sh));
-          part += (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? E : 0;
-        }
+        if (!dead(sacc, e32)) sum_chunk(c, sacc, e32);
+      } else if (!dead(sacc, e64)) {
+        sum_chunk(c, sacc, e64);
       }
-      den += part;
     }
   }
   sweep_end();
   den += __shfl_xor(den, 32);
   if (!live) den = 0;
-  const int64_t rn = den > 0 ? (int64_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den) : 0;  // D >= 2^15
+  const uint32_t rn = den > 0 ? (uint32_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den) : 0u;  // D >= 2^15
+  // P = min(R(E rn, 31), 2^15 - 1) from 24-bit products: with rn = 2^16 rh
+  // + rl, E rn + 2^30 = 2^16 (E rh + (t >> 16)) + (t mod 2^16) for t = E rl
+  // + 2^30 < 2^32 (E <= 2^15, rl < 2^16), so R(E rn, 31) = (E rh + (t >>
+  // 16)) >> 15. Rows without a live query have rn = 0, hence P = 0.
+  const uint32_t rh = rn >> 16, rl = rn & 0xFFFFu;
+  auto pr = [&](uint32_t E) -> uint32_t {
+    const uint32_t t = __umul24(E, rl) + (1u << 30);
+    return min((__umul24(E, rh) + (t >> 16)) >> 15, 32767u);
+  };
 
-  // pass 3: probabilities and P.V
-  v16i oh[KS], ol[KS];
+  // pass 3: probabilities and P.V, O^T += V^T . P^T. The V^T operand of
+  // d-tile t comes from two transposed reads of the staged V rows: in the
+  // group of 16 lanes g = lane / 16 (query columns 16 (g % 2) .., keys of
+  // half-wave g / 2), lanes 2 m and 2 m + 1 read the two 8-byte halves of
+  // d = 32 t + 16 (g % 2) .. + 15 in the row of key 8 (m / 4) + 4 (g / 2) +
+  // m % 4 (+ 16 for the second read), so lane j of the group receives d =
+  // 32 t + 16 (g % 2) + j at the 16 keys its P^T operand bytes stand for.
+  // The same bytes give this wave's column sums of V over the chunks it
+  // processes, for d = 32 t + lane % 32 (half of the keys in each half-wave).
+  int voff[2][KS];
+  {
+    const int g = lane >> 4, i = lane & 15, m = i >> 1;
+    const int key = 8 * (m >> 2) + 4 * hh + (m & 3);
 #pragma unroll
-  for (int t = 0; t < KS; ++t)
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int l2 = 0; l2 < 2; ++l2)
+        voff[l2][t] = (key + 16 * l2) * D + (((2 * t + (g & 1)) ^ kswz<D>(key)) << 4) + 8 * (i & 1);
+  }
+  v16i oh[KS], ol[KS];
+  int cs[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    cs[t] = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) oh[t][r] = ol[t][r] = 0;
-  int cs = 0;  // thread d < D: colsum of V over the staged keys
+  }
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  // V^T of a chunk: thread t moves D/8 bytes of key t/8 (keys permuted)
-  const int vj = tid >> 3, vd = (tid & 7) * (D / 8), vslot = key_slot(vj);
-  issue(0, true);
-  for (int bt = 0; bt < nbt; ++bt) {
-   batch_begin(bt, true);
-   for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
-    int8_t* vb = vt + (c & 1) * D * VST;
-    {
-      const int8_t* src = sV + ((c / (BK / 32)) & 1) * KB + ((c * 32) % BK + vj) * D + vd;
-      uint32_t w[D / 32];
-      if constexpr (D == 64) {
-        const uint2 x = *(const uint2*)src;
-        w[0] = x.x;
-        w[1] = x.y;
-      } else {
-        const v4i x = *(const v4i*)src;
+  auto pv_chunk = [&](int c, const v16i& sacc, auto ef) {
+    uint32_t P[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)x[i];
-      }
+    for (int r = 0; r < 16; ++r) P[r] = pr(ef(sacc[r]));
+    if (c * 32 + 31 > pmin) {
+      const int lim = pos - c * 32;
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) vb[(vd + i) * VST + vslot] = (int8_t)(w[i >> 2] >> (8 * (i & 3)));
+      for (int r = 0; r < 16; ++r) P[r] = koff(r) <= lim ? P[r] : 0u;
     }
-    __syncthreads();  // V^T of chunk c staged; the other V^T buffer is free
-    if (tid < D) {
-      cs = dot16(*(const v4i*)(vb + tid * VST), ones, cs);
-      cs = dot16(*(const v4i*)(vb + tid * VST + 16), ones, cs);
+    // limbs, byte r of a fragment = register r: Ph = P >> 8, Pl = (P & 255) - 128
+    v4i fph, fpl;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t p01 = P[4 * r4] | (P[4 * r4 + 1] << 16), p23 = P[4 * r4 + 2] | (P[4 * r4 + 3] << 16);
+      fph[r4] = (int)__builtin_amdgcn_perm(p23, p01, 0x07050301u);
+      fpl[r4] = (int)(__builtin_amdgcn_perm(p23, p01, 0x06040200u) ^ 0x80808080u);
     }
-    const v16i sacc = scores(c);
-    const int lim = live ? pos - c * 32 : -1;  // key offsets <= lim get P > 0
-    // P limbs, byte r of the fragment = register r. P = R(E rn, 31) capped
-    // at 2^15 - 1; E rn < 2^47.
-    uint32_t ph[4] = {0, 0, 0, 0}, pl[4] = {0, 0, 0, 0};
-    auto put = [&](int r, int32_t E) {
-      const uint32_t pp = (uint32_t)(((uint64_t)(uint32_t)E * (uint64_t)rn + (uint64_t(1) << 30)) >> 31);
-      uint32_t P = pp > 32767u ? 32767u : pp;
-      P = (8 * (r >> 2) + 4 * hh + (r & 3) <= lim) ? P : 0u;
-      ph[r >> 2] |= (P >> 8) << (8 * (r & 3));
-      pl[r >> 2] |= ((P & 255u) ^ 128u) << (8 * (r & 3));  // (P & 255) - 128 as a byte
-    };
-    if (wfast32) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) put(r, exp_delta32((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh, d0));
-    } else if (wfast) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) put(r, exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        put(r, fast ? exp_delta((uint32_t)(mx - sacc[r]), (uint32_t)Ms, sh)
-                    : diexp(R(((int64_t)sacc[r] - mx) * Ms, sh)));
-    }
-    const v4i fph = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3]};
-    const v4i fpl = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
+    const int8_t* vb = sV + ((c / CPB) & 1) * KB + ((c * 32) % BK) * D;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      const v4i fv = *(const v4i*)(vb + (32 * t + ql) * VST + 16 * hh);
+      const v2i_t lo = lds_read_tr8(vb + voff[0][t]), hi = lds_read_tr8(vb + voff[1][t]);
+      const v4i fv = {lo.x, lo.y, hi.x, hi.y};
       oh[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fph, oh[t], 0, 0, 0);
       ol[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fpl, ol[t], 0, 0, 0);
+      cs[t] = dot16(fv, ones, cs[t]);
     }
-   }
+  };
+  issue(0, true);
+  for (int bt = 0; bt < nbt; ++bt) {
+    batch_begin(bt, true);
+    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
+      const v16i sacc = scores(c);
+      if (wfast32) {
+        if (!dead(sacc, e32)) pv_chunk(c, sacc, e32);
+      } else if (!dead(sacc, e64)) {
+        pv_chunk(c, sacc, e64);
+      }
+    }
   }
   sweep_end();
-  if (tid < D) s_cs[tid] = cs;
+  // the wave's column sums into LDS (the K/V buffers are free now), d-major
+  int32_t* s_cs = (int32_t*)smem + wave * D;
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    const int tot = cs[t] + __shfl_xor(cs[t], 32);
+    if (hh == 0) s_cs[32 * t + ql] = tot;
+  }
   __syncthreads();
   bound_raise(pbad);
   if (!rvalid) return;
@@ -944,14 +987,14 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   for (int t = 0; t < KS; ++t)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * t + 8 * r4 + 4 * hh;
+      const int db = 32 * t + 8 * r4 + 4 * hh;
       v4i o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * r4 + i;
-        o[i] = live ? (int)(256 * (int64_t)oh[t][r] + ol[t][r] + 128 * (int64_t)s_cs[d0 + i]) : 0;
+        o[i] = live ? (int)(256 * (int64_t)oh[t][r] + ol[t][r] + 128 * (int64_t)s_cs[db + i]) : 0;
       }
-      *(v4i*)(orow + d0) = o;
+      *(v4i*)(orow + db) = o;
     }
 }
 
