@@ -401,28 +401,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   // + r % 4, column l % 32.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();  // every wave done with the LDS ring
-  int32_t* srow = (int32_t*)smem;  // WIDE: row sums of the tile's A rows
-  int32_t* s_rm = srow + BM;       // row scales of the tile's rows
-  int32_t* s_rk = s_rm + BM;
+  // per row r of the tile, ints 4 r .. 4 r + 3: {WIDE: row sum of A, row
+  // scale, total shift, shift - 33}, stored one int at a time (a store to one
+  // lane of a 16-byte vector would rewrite all four) and read as one vector
+  int32_t* s_row = (int32_t*)smem;
   if (WIDE && wn == 0) {
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
       const int v = rsum[a] + __shfl_xor(rsum[a], 32);
-      if (lane < 32) srow[wm * WM + a * 32 + lane] = v;
+      if (lane < 32) s_row[4 * (wm * WM + a * 32 + lane)] = v;  // |v| <= 128 K
     }
   }
-  // s_rk holds each row's total shift. The fast path needs every scale in
-  // [0, 2^15) and every shift in [1, 62] (int8 weights) or [32, 94] (limbs);
-  // anything else takes the general per-element path below.
+  // The fast path needs every scale in [0, 2^15) and every shift in [1, 62]
+  // (int8 weights) or [33, 94] with K < 2^16 (limbs); anything else takes
+  // the general per-element path below.
   const int csh = e.col_k - (MODE == MODE_REQ_I8 ? 0 : e.frac);
   int slow = 0, narrow = 0;
   if (MODE != MODE_RAW) {
     for (int t = tid; t < BM; t += NT) {
       const int i = min(m0 + t, M - 1);
       const int rm = e.row_m[i], sh = e.row_k[i] + csh;
-      s_rm[t] = rm;
-      s_rk[t] = sh;
-      slow |= (unsigned)rm >= 32768u || (WIDE ? sh < 32 || sh > 94 : sh < 1 || sh > 62);
+      s_row[4 * t + 1] = rm;
+      s_row[4 * t + 2] = sh;
+      s_row[4 * t + 3] = sh - 33;
+      slow |= (unsigned)rm >= 32768u || (WIDE ? sh < 33 || sh > 94 || K >= 65536 : sh < 1 || sh > 62);
       narrow |= sh < 33;
     }
     for (int t = tid; t < BN; t += NT) slow |= (unsigned)e.col_m[min(n0 + t, N - 1)] >= 32768u;
@@ -433,67 +435,84 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
   // exactly, hi(p) the upper 32 bits of the 64-bit product p (the low word
   // cannot carry into the floor), so the product needs one mul_hi
   const bool hi_only = !WIDE && !__syncthreads_or(narrow);
-  if (MODE != MODE_RAW && !slow && m0 + BM <= M && n0 + BN <= N) {
+  if (MODE != MODE_RAW && !slow && m0 + BM <= M && n0 + BN <= N &&
+      (int64_t)BM * N * (MODE == MODE_REQ_I8 ? 1 : 4) < (int64_t(1) << 31)) {
     // Interior tile, in-range scales: no bounds checks, branch-free rounding.
     // int8 weights: |m_r * m_c| < 2^30, so acc * m_r * m_c is one 32 x 32 ->
-    // 64-bit product. Limbs: t = v * m_r fits int64; with t = th * 2^32 + tl
-    // (0 <= tl < 2^32) and the rounding term 2^(s-1) = ch * 2^32 + cl,
-    // R(t * m_c, s) = (th * m_c + ch + ((tl * m_c + cl) >> 32)) >> (s - 32)
-    // exactly, for 32 <= s <= 94.
+    // 64-bit product. For a shift s >= 33, R(p, s) = (floor(p / 2^32) +
+    // 2^(s-33)) >> (s-32) exactly (p's low word cannot carry into the floor).
+    // Limbs: v = 256 hi + w with w = lo + 128 rowsum = sum A (W & 255), |w| <
+    // 2^15 K < 2^31; M = m_r m_c < 2^30; with v = vh 2^32 + vl (0 <= vl <
+    // 2^32), floor(v M / 2^32) = vh M + mulhi(vl, M).
     auto tiles = [&](auto hi) {  // hi: every shift >= 33 (compile-time flag)
       constexpr bool HI = decltype(hi)::value;
-      uint32_t bad = 0;
+      constexpr int EB = MODE == MODE_REQ_I8 ? 1 : 4;  // output element bytes
+      // the tile's output block through a buffer resource (it spans fewer
+      // than 2^31 bytes): a lane offset per 32x32 sub-tile in a VGPR, the
+      // offsets of its 16 rows as scalars
+      const __amdgpu_buffer_rsrc_t ro =
+          brsrc((const int8_t*)out + ((m0 + obase) * N + n0) * EB, (int64_t)BM * N * EB);
+      // bound checks as OR-accumulated words (no per-element compares):
+      // nonzero when a result left int32 / when a residual sum t had
+      // |t| >= 2^res_bits (t + 2^b - 1 < 0 or t - 2^b >= 0)
+      uint32_t ovf = 0, ovr = 0;
+      const int rb = e.res_bits;
+      const int64_t rlo = rb > 0 ? (int64_t(1) << rb) - 1 : 0, rhi = rb > 0 ? int64_t(1) << rb : 0;
 #pragma clang loop unroll(full)
       for (int a = 0; a < TM; ++a)
 #pragma clang loop unroll(full)
         for (int t = 0; t < TN; ++t) {
           if constexpr (WIDE) pin_acc<NB>(acc, a, t);
-          const int j = n0 + wn * WN + t * 32 + (lane & 31);
-          const int32_t cm = e.col_m[j];
+          const int jj = wn * WN + t * 32 + (lane & 31);
+          const int32_t cm = e.col_m[n0 + jj];
           const int lb = wm * WM + a * 32 + 4 * (lane >> 5);
+          const int vo = (lb * N + jj) * EB;
           int32_t old[16];
           if (MODE == MODE_RES_ADD) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              old[r] = ((const int32_t*)out)[(m0 + lb + 8 * (r >> 2) + (r & 3) + obase) * N + j];
+              old[r] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ro, vo, (8 * (r >> 2) + (r & 3)) * N * EB, 0);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int li = lb + 8 * (r >> 2) + (r & 3);
-            const int64_t o = (m0 + li + obase) * N + j;
-            const int sh = s_rk[li];
+            const int so = (8 * (r >> 2) + (r & 3)) * N * EB;
+            const v4i rw = *(const v4i*)(s_row + 4 * li);
+            const uint32_t Mrc = (uint32_t)__mul24(rw[1], cm);
+            // R(x, s) = ((x >> (s - 1)) + 1) >> 1 for s >= 1, and the
+            // floor(p / 2^32) form above: R(p, s) = ((floor(p / 2^32) >> (s -
+            // 33)) + 1) >> 1 for s >= 33 (rw[3] = s - 33)
             int64_t y;
             if (WIDE) {
-              const int64_t v = 256 * (int64_t)acc[0][a][t][r] + (int64_t)acc[NB - 1][a][t][r] +
-                                128 * (int64_t)srow[li];
-              const int64_t tt = v * s_rm[li];
-              const int64_t th = tt >> 32;
-              const uint64_t tl = (uint32_t)tt;
-              const int64_t ch = sh >= 33 ? int64_t(1) << (sh - 33) : 0;
-              const uint64_t cl = sh == 32 ? uint64_t(1) << 31 : 0;
-              const uint64_t lo = tl * (uint64_t)(uint32_t)cm + cl;
-              y = (th * cm + ch + (int64_t)(lo >> 32)) >> (sh - 32);
+              const int32_t w = acc[NB - 1][a][t][r] + rw[0] * 128;
+              const int64_t v = (int64_t)acc[0][a][t][r] * 256 + w;
+              const int64_t q = (int64_t)(int32_t)(v >> 32) * (int64_t)(int32_t)Mrc +
+                                (int64_t)__umulhi((uint32_t)v, Mrc);
+              y = ((q >> rw[3]) + 1) >> 1;
             } else if (HI) {
-              const int32_t ph = __mulhi(acc[0][a][t][r], __mul24(s_rm[li], cm));
-              y = (ph + (1 << (sh - 33))) >> (sh - 32);
+              const int32_t ph = __mulhi(acc[0][a][t][r], (int32_t)Mrc);
+              y = ((ph >> rw[3]) + 1) >> 1;
             } else {
-              const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)__mul24(s_rm[li], cm);
-              y = (pr + (int64_t(1) << (sh - 1))) >> sh;
+              const int64_t pr = (int64_t)acc[0][a][t][r] * (int64_t)Mrc;
+              y = ((pr >> (rw[2] - 1)) + 1) >> 1;
             }
             if (MODE == MODE_REQ_I8) {
-              ((int8_t*)out)[o] = clamp8(y);
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)clamp8(y), ro, vo, so, 0);
             } else if (MODE == MODE_FIX) {
-              if (!HI) bad |= i32_check(y);  // a mul_hi result is within int32
-              ((int32_t*)out)[o] = (int32_t)y;
+              if (!HI) ovf |= (uint32_t)((uint64_t)(y + 2147483648LL) >> 32);  // mul_hi results fit
+              __builtin_amdgcn_raw_buffer_store_b32((uint32_t)y, ro, vo, so, 0);
             } else {
               const int64_t tsum = (int64_t)old[r] + y;
-              bad |= res_check(tsum, e.res_bits);
-              ((int32_t*)out)[o] = (int32_t)tsum;
+              if (rb > 0)
+                ovr |= (uint32_t)((uint64_t)(tsum + rlo) >> 63) | (uint32_t)(~(uint64_t)(tsum - rhi) >> 63);
+              else
+                ovf |= (uint32_t)((uint64_t)(tsum + 2147483648LL) >> 32);
+              __builtin_amdgcn_raw_buffer_store_b32((uint32_t)tsum, ro, vo, so, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-      bound_raise(bad);
+      bound_raise((ovf ? (uint32_t)kBoundInt32 : 0u) | (ovr ? (uint32_t)kBoundResidual : 0u));
     };
     // one copy of the unrolled tile loop per case (a per-element branch
     // would interleave both and double the code the loop runs through)
@@ -527,7 +546,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
       for (int r = 0; r < 16; ++r) {
         const int li = lb + 8 * (r >> 2) + (r & 3), i = m0 + li;
         int64_t v = acc[0][a][t][r];
-        if (WIDE) v = 256 * v + (int64_t)acc[NB - 1][a][t][r] + 128 * (int64_t)srow[li];
+        if (WIDE) v = 256 * v + (int64_t)acc[NB - 1][a][t][r] + 128 * (int64_t)s_row[4 * li];
         const int64_t o = (i + obase) * N + j;
         if (MODE == MODE_RAW) {
           if (i < M && j < N) {
@@ -538,9 +557,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe(const int8_t* __rest
           }
           continue;
         }
-        const int sh = s_rk[li];
-        const int64_t y = WIDE ? R128((__int128)(v * s_rm[li]) * cm, sh)
-                               : R((int64_t)(int32_t)v * s_rm[li] * cm, sh);
+        const int sh = s_row[4 * li + 2];
+        const int64_t y = WIDE ? R128((__int128)(v * s_row[4 * li + 1]) * cm, sh)
+                               : R((int64_t)(int32_t)v * s_row[4 * li + 1] * cm, sh);
         if (i < M && j < N) {
           if (MODE == MODE_REQ_I8) {
             ((int8_t*)out)[o] = clamp8(y);
