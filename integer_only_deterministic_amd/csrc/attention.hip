@@ -36,23 +36,13 @@ __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
   return c;
 }
 
-// exp_delta in 32-bit arithmetic. v >= 31 * 2^15 (E = 0) exactly when
+// exp_delta in 32-bit arithmetic: v >= 31 * 2^15 (E = 0) exactly when
 // delta * M >= T = 31 * 2^(15 + sh) - 2^(sh - 1) + 1, i.e. delta >= d0 =
 // ceil(T / M); clamping delta to d0 keeps that outcome and bounds the product
 // by T + M < 2^32 when 1 <= sh <= 11 and 2^10 <= M < 2^15 (then d0 < 2^22, so
 // one 24-bit multiply is exact, and v < 32 * 2^15 keeps every shift below
-// 32). Branch-free; same value as exp_delta.
-__device__ __forceinline__ int32_t exp_delta32(uint32_t delta, uint32_t M, int sh, uint32_t d0) {
-  const uint32_t x = __umul24(min(delta, d0), M);
-  const uint32_t v = (x + ((1u << (sh - 1)) - 1u)) >> sh;
-  const uint32_t n = v >> 15;  // <= 31 after the clamp
-  const uint32_t f = 32768u - (((v & 32767u) + 1u) >> 1);
-  const uint32_t E = (f + ((1u << n) >> 1)) >> n;
-  return v >= (31u << 15) ? 0 : (int32_t)E;
-}
-
-// d0 of exp_delta32 for a lane's (M, sh), or 0 when the lane is outside its
-// range (1 <= sh <= 11, 2^10 <= M < 2^15).
+// 32). exp32_limit gives d0 for a lane's (M, sh), or 0 when the lane is
+// outside that range.
 __device__ __forceinline__ uint32_t exp32_limit(int32_t M, int sh) {
   if (sh < 1 || sh > 11 || M < (1 << 10) || M >= (1 << 15)) return 0;
   const uint64_t T = (uint64_t(31) << (15 + sh)) - (uint64_t(1) << (sh - 1)) + 1;
@@ -811,13 +801,27 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   };
   constexpr int CPB = BK / 32;  // chunks per batch
 
+  // Every pass takes a batch's chunks with their scores one chunk ahead:
+  // the MFMAs of chunk c + 1 are issued before chunk c's integer work, which
+  // then runs under them (the batch's last chunk recomputes its own).
+  auto sweep = [&](bool withv, auto body) {
+    issue(0, withv);
+    for (int bt = 0; bt < nbt; ++bt) {
+      batch_begin(bt, withv);
+      const int c0 = bt * CPB, c1 = min(nch, (bt + 1) * CPB);
+      v16i sacc = scores(c0);
+      for (int c = c0; c < c1; ++c) {
+        const v16i snext = scores(min(c + 1, c1 - 1));
+        body(c, sacc);
+        sacc = snext;
+      }
+    }
+    sweep_end();
+  };
+
   // pass 1: maxima
   int mx = INT32_MIN;
-  issue(0, false);
-  for (int bt = 0; bt < nbt; ++bt) {
-    batch_begin(bt, false);
-    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
-      const v16i sacc = scores(c);
+  sweep(false, [&](int c, const v16i& sacc) {
       if (c * 32 + 31 <= pmin) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = max(mx, sacc[r]);
@@ -826,14 +830,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
         for (int r = 0; r < 16; ++r)
           if (c * 32 + koff(r) <= pos) mx = max(mx, sacc[r]);
       }
-    }
-  }
-  sweep_end();
+  });
   mx = max(mx, __shfl_xor(mx, 32));
   if (!live) mx = 0;  // its values are never used; keep the arithmetic tame
 
   // E(s) = DI-Exp(R((s - mx) Ms, sh)) for s <= mx. The 32-bit form is
-  // exp_delta32 of mx - s with the clamp at d0 moved onto the score: v =
+  // exp_delta of mx - s with the clamp at d0 moved onto the score: v =
   // (mx - max(s, mx - d0)) Ms + 2^(sh-1) - 1, shifted by sh, evaluated as
   // C - max(s, slo) Ms mod 2^32 (its value is below 2^31); then n = v >> 15
   // <= 31, f = (2^16 - v mod 2^15) >> 1 = 2^15 - R(v mod 2^15, 1), and
@@ -877,19 +879,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
     }
     den += part;
   };
-  issue(0, false);
-  for (int bt = 0; bt < nbt; ++bt) {
-    batch_begin(bt, false);
-    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
-      const v16i sacc = scores(c);
-      if (wfast32) {
-        if (!dead(sacc, e32)) sum_chunk(c, sacc, e32);
-      } else if (!dead(sacc, e64)) {
-        sum_chunk(c, sacc, e64);
-      }
+  sweep(false, [&](int c, const v16i& sacc) {
+    if (wfast32) {
+      if (!dead(sacc, e32)) sum_chunk(c, sacc, e32);
+    } else if (!dead(sacc, e64)) {
+      sum_chunk(c, sacc, e64);
     }
-  }
-  sweep_end();
+  });
   den += __shfl_xor(den, 32);
   if (!live) den = 0;
   const uint32_t rn = den > 0 ? (uint32_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den) : 0u;  // D >= 2^15
@@ -958,19 +954,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
       cs[t] = dot16(fv, ones, cs[t]);
     }
   };
-  issue(0, true);
-  for (int bt = 0; bt < nbt; ++bt) {
-    batch_begin(bt, true);
-    for (int c = bt * CPB; c < min(nch, (bt + 1) * CPB); ++c) {
-      const v16i sacc = scores(c);
-      if (wfast32) {
-        if (!dead(sacc, e32)) pv_chunk(c, sacc, e32);
-      } else if (!dead(sacc, e64)) {
-        pv_chunk(c, sacc, e64);
-      }
+  sweep(true, [&](int c, const v16i& sacc) {
+    if (wfast32) {
+      if (!dead(sacc, e32)) pv_chunk(c, sacc, e32);
+    } else if (!dead(sacc, e64)) {
+      pv_chunk(c, sacc, e64);
     }
-  }
-  sweep_end();
+  });
   // the wave's column sums into LDS (the K/V buffers are free now), d-major
   int32_t* s_cs = (int32_t*)smem + wave * D;
 #pragma unroll
