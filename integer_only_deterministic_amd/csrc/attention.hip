@@ -771,18 +771,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   // chunks below every query of this wave's tile need no causal mask
   const int pmin = p0 + qb * QP + (wave / G) * 32;
 
-  // S^T of chunk c (keys 32 c ..) from the staged batch
-  auto scores = [&](int c) {
+  // S^T of chunk c (keys 32 c ..) from the staged batch: its K fragments,
+  // then the MFMAs on them
+  auto kfrag = [&](int c, v4i (&kf)[KS]) {
     const int8_t* kb = sK + ((c / (BK / 32)) & 1) * KB;
     const int r = (c * 32) % BK + ql;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v4i*)(kb + r * D + (((2 * ks + hh) ^ kswz<D>(r)) << 4));
+  };
+  auto smma = [&](const v4i (&kf)[KS]) {
     v16i acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const v4i kf = *(const v4i*)(kb + r * D + (((2 * ks + hh) ^ kswz<D>(r)) << 4));
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ks], acc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[ks], qf[ks], acc, 0, 0, 0);
     return acc;
   };
   // key offset within its chunk of accumulator register r
@@ -801,17 +803,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   };
   constexpr int CPB = BK / 32;  // chunks per batch
 
-  // Every pass takes a batch's chunks with their scores one chunk ahead:
-  // the MFMAs of chunk c + 1 are issued before chunk c's integer work, which
-  // then runs under them (the batch's last chunk recomputes its own).
+  // Every pass takes a batch's chunks with their scores one chunk ahead and
+  // their K fragments two ahead: the MFMAs of chunk c + 1 and the LDS reads
+  // of chunk c + 2 are issued before chunk c's integer work, which then runs
+  // under them (near the batch's end the last chunk is taken again).
   auto sweep = [&](bool withv, auto body) {
     issue(0, withv);
     for (int bt = 0; bt < nbt; ++bt) {
       batch_begin(bt, withv);
       const int c0 = bt * CPB, c1 = min(nch, (bt + 1) * CPB);
-      v16i sacc = scores(c0);
+      v4i kn[KS];
+      kfrag(c0, kn);
+      v16i sacc = smma(kn);
+      kfrag(min(c0 + 1, c1 - 1), kn);
       for (int c = c0; c < c1; ++c) {
-        const v16i snext = scores(min(c + 1, c1 - 1));
+        const v16i snext = smma(kn);
+        kfrag(min(c + 2, c1 - 1), kn);
         body(c, sacc);
         sacc = snext;
       }
@@ -928,6 +935,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   }
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   auto pv_chunk = [&](int c, const v16i& sacc, auto ef) {
+    // V^T fragments first: the LDS reads complete under the P arithmetic
+    const int8_t* vb = sV + ((c / CPB) & 1) * KB + ((c * 32) % BK) * D;
+    v2i_t vlo[KS], vhi[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      vlo[t] = lds_read_tr8(vb + voff[0][t]);
+      vhi[t] = lds_read_tr8(vb + voff[1][t]);
+    }
     uint32_t P[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) P[r] = pr(ef(sacc[r]));
@@ -944,11 +959,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
       fph[r4] = (int)__builtin_amdgcn_perm(p23, p01, 0x07050301u);
       fpl[r4] = (int)(__builtin_amdgcn_perm(p23, p01, 0x06040200u) ^ 0x80808080u);
     }
-    const int8_t* vb = sV + ((c / CPB) & 1) * KB + ((c * 32) % BK) * D;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      const v2i_t lo = lds_read_tr8(vb + voff[0][t]), hi = lds_read_tr8(vb + voff[1][t]);
-      const v4i fv = {lo.x, lo.y, hi.x, hi.y};
+      const v4i fv = {vlo[t].x, vlo[t].y, vhi[t].x, vhi[t].y};
       oh[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fph, oh[t], 0, 0, 0);
       ol[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fv, fpl, ol[t], 0, 0, 0);
       cs[t] = dot16(fv, ones, cs[t]);
