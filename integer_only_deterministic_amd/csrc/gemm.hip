@@ -638,21 +638,25 @@ hipError_t pipe_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int 
 
 // Largest tile that still gives the chip most of a wave of workgroups (int8
 // weights fall back to 128x64, which fills the chip where 128x128 leaves
-// half of it idle, e.g. M = 2048, N = 1024: 20% faster). The
-// 256x256 int8 tiling runs 8 waves (two per SIMD, 128x64 each, accumulators
-// in VGPRs), measured 3-16% faster than 4; with limbs 4 waves are as fast.
+// half of it idle, e.g. M = 2048, N = 1024: 20% faster). Every tiling that
+// fills the LDS runs 8 waves, two per SIMD, so one wave's barrier and load
+// waits run under the other's MFMAs: the 256x256 int8 tiling (2 x 4 waves of
+// 128x64) measured 3-16% faster than 4 waves, the 256x128 limb tiling (4 x 2
+// waves of 64x64, both planes, 128 accumulators each) 9-13% faster, the
+// 128x256 int8 tiling 14% at M = 2048, N = 4096. The 128x64 fallback keeps
+// 4 waves (8 would leave each a single 32x32 tile).
 template <bool WIDE>
 hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N,
                          int K, const Epi& e, void* out, hipStream_t st) {
   auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   constexpr int64_t FILL = 192;  // 3/4 of the 256 CUs
   if (WIDE) {
-    if (tiles(256, 128) >= FILL) return pipe_launch<256, 128, 2, true>(A, W, Wlo, M, N, K, e, out, st);
-    return pipe_launch<128, 128, 3, true>(A, W, Wlo, M, N, K, e, out, st);
+    if (tiles(256, 128) >= FILL) return pipe_launch<256, 128, 2, true, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
+    return pipe_launch<128, 128, 3, true, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
   }
   if (tiles(256, 256) >= FILL) return pipe_launch<256, 256, 2, false, 2, 4>(A, W, Wlo, M, N, K, e, out, st);
-  if (tiles(128, 256) >= FILL) return pipe_launch<128, 256, 3, false>(A, W, Wlo, M, N, K, e, out, st);
-  if (tiles(128, 128) >= FILL) return pipe_launch<128, 128, 4, false>(A, W, Wlo, M, N, K, e, out, st);
+  if (tiles(128, 256) >= FILL) return pipe_launch<128, 256, 3, false, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
+  if (tiles(128, 128) >= FILL) return pipe_launch<128, 128, 4, false, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
   return pipe_launch<128, 64, 4, false>(A, W, Wlo, M, N, K, e, out, st);
 }
 
