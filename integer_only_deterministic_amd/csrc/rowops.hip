@@ -335,12 +335,12 @@ constexpr size_t kSigLds = sizeof(SigTable);  // 65552 bytes
 
 // DI-SwiGLU for many rows (prefill): a persistent grid whose workgroups copy
 // the sigmoid quotients into LDS once and then take rows w, w + G, ...; the
-// sigmoid's division becomes one LDS lookup. Each row's inputs for the next
-// row are loaded while the current one is computed. Same integer function
-// as swiglu_rk, row for row.
+// sigmoid's division becomes one LDS lookup. Two 1024-thread workgroups run
+// per CU (the table allows two), 8 waves per SIMD, so at most 64 VGPRs. Same
+// integer function as swiglu_rk, row for row.
 template <int U>
-__global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__ gu, int rows, int n,
-                                                     int32_t f_a, int32_t Mg, int32_t Kg,
+__global__ __launch_bounds__(SWT, 8) void swiglu_tab_rk(const int32_t* __restrict__ gu, int rows, int n,
+                                                     int32_t f_a, int32_t Mg, int32_t Kg, uint32_t g0,
                                                      int8_t* __restrict__ a8,
                                                      int32_t* __restrict__ rm,
                                                      int32_t* __restrict__ rk) {
@@ -360,11 +360,65 @@ __global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__
       uu[u] = *(const v4i*)(g + n + RR::at(u, n));
     }
   };
-  load(r, gv, uv);
   __syncthreads();  // table resident
+  // no register prefetch of the next row: 64 VGPRs leave no room for it, and
+  // with two 1024-thread workgroups per CU one workgroup's loads run under
+  // the other's arithmetic
   for (; r < rows; r += G) {
-    v4i gn[U], un[U];
-    load(min(r + G, rows - 1), gn, un);  // next row (clamped: the last row reloads itself)
+    load(r, gv, uv);
+    if (g0) {
+      // 32-bit form (g0 > 0: 1 <= Kg <= 12, 2^10 <= Mg < 2^15). The sigmoid's
+      // DI-Exp input v = R(|g| Mg, Kg) reaches 31 * 2^15 (E = 0) exactly from
+      // |g| = g0 on, so |g| is clamped there: the product then stays below
+      // 31 * 2^(15 + Kg) + Mg < 2^32 and v >> 15 <= 31. With v = 2^15 n + r,
+      // DI-Exp's fraction 2^15 - R(r, 1) is (2^16 - r) >> 1. In range |g|,
+      // |u| < 2^24 (checked), so the magnitudes enter unsigned 24-bit
+      // products: with a = |g| sig (sig >= 0), |R(g sig, 15)| is
+      // (a + 2^14) >> 15 for g >= 0 and (a + 2^14 - 1) >> 15 for g < 0
+      // (round half up on a negative value), and the row's DQ exponent comes
+      // from the OR of the exact |silu| |u| (the bit length of the OR is that
+      // of the maximum).
+      // silu and the 24-bit u replace g and u in the row's own registers
+      uint32_t amax = 0, lo_or = 0, hi_or = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = RR::first(u) < n;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int32_t g = ok ? gv[u][e4] : 0, uv0 = ok ? uv[u][e4] : 0;
+          const uint32_t ag = (uint32_t)max(g, -g), au = (uint32_t)max(uv0, -uv0);
+          amax = max(amax, max(ag, au));
+          const uint32_t v = (__umul24(min(ag, g0), (uint32_t)Mg) + (1u << (Kg - 1))) >> Kg;
+          const uint32_t nn = v >> 15, f = (65536u - (v & 32767u)) >> 1;
+          const uint32_t E = (f + ((1u << nn) >> 1)) >> nn;
+          const int32_t q = tab[E];
+          const int32_t sig = g >= 0 ? q : 32768 - q;
+          const uint64_t a = (uint64_t)(ag & 0xFFFFFFu) * ((uint32_t)sig & 0xFFFFu);
+          const uint32_t as = (uint32_t)((a + (1u << 14) - (g < 0 ? 1u : 0u)) >> 15);
+          const uint32_t au24 = au & 0xFFFFFFu;
+          lo_or |= __umul24(as, au24);
+          hi_or |= __umulhi(as, au24);
+          gv[u][e4] = g < 0 ? -(int32_t)as : (int32_t)as;  // silu
+          uv[u][e4] = uv0;
+        }
+      }
+      bound_raise(amax >= (1u << 24) ? kBoundSwiglu : 0u);
+      const int64_t A = block_max((int64_t)(((uint64_t)hi_or << 32) | lo_or), red);
+      const int e = dq_exp((uint64_t)A);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (RR::first(u) < n) {
+          int64_t pq[4];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) pq[e4] = R_nn((int64_t)gv[u][e4] * uv[u][e4], e);
+          *(uint32_t*)(a8 + (size_t)r * n + RR::first(u)) = pack4(pq[0], pq[1], pq[2], pq[3]);
+        }
+      if (threadIdx.x == 0) {
+        rm[r] = 1 << 14;
+        rk[r] = 2 * f_a - e + 14;
+      }
+      continue;
+    }
     int64_t p[U][4], A = 0;
     uint32_t bad = 0;
 #pragma unroll
@@ -394,11 +448,6 @@ __global__ __launch_bounds__(SWT) void swiglu_tab_rk(const int32_t* __restrict__
     if (threadIdx.x == 0) {
       rm[r] = 1 << 14;
       rk[r] = 2 * f_a - e + 14;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      gv[u] = gn[u];
-      uv[u] = un[u];
     }
   }
 }
@@ -755,10 +804,18 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
       if (err == hipSuccess) err = set_max_lds((const void*)swiglu_tab_rk<2>, kSigLds);
       if (err != hipSuccess) return err;
       const unsigned grid = (unsigned)(R < 512 ? R : 512);
+      // clamp of the 32-bit form: the least |g| with R(|g| Mg, Kg) >= 31 2^15,
+      // ceil((31 2^(15 + Kg) - 2^(Kg - 1)) / Mg); 0 (the 64-bit form) outside
+      // 1 <= Kg <= 12, 2^10 <= Mg < 2^15
+      uint32_t g0 = 0;
+      if (Kg >= 1 && Kg <= 12 && Mg >= (1 << 10) && Mg < (1 << 15)) {
+        const uint64_t T = (uint64_t(31) << (15 + Kg)) - (uint64_t(1) << (Kg - 1));
+        g0 = (uint32_t)((T + (uint64_t)Mg - 1) / (uint64_t)Mg);
+      }
       if (n <= 4 * SWT)
-        swiglu_tab_rk<1><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+        swiglu_tab_rk<1><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, g0, a8, row_m, row_k);
       else
-        swiglu_tab_rk<2><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, a8, row_m, row_k);
+        swiglu_tab_rk<2><<<grid, SWT, kSigLds, st>>>(gu, (int)R, (int)n, f_a, Mg, Kg, g0, a8, row_m, row_k);
       return hipGetLastError();
     }
     if (n <= 4 * SWT)

@@ -295,6 +295,23 @@ def test_swiglu(D, R, n):
     np.testing.assert_array_equal(host(k), ok)
 
 
+@pytest.mark.parametrize("f_a", [14, 15])
+def test_swiglu_64_bit_form(D, f_a):
+    """The table kernel's 64-bit form: f_a = 14, 15 give the sigmoid shift
+    K = f_a - 1 > 12, where the 32-bit form's product bound does not hold
+    (f_a = 12, every other test, takes the 32-bit form)."""
+    rng = np.random.default_rng(f_a)
+    R, n = 130, 4100
+    gu = rng.normal(0, 8 * 4096, (R, 2 * n)).astype(np.int32)
+    gu[1, 7] = (1 << 24) - 1
+    gu[1, 8] = -(1 << 24) + 1
+    a8, m, k = D.detint_swiglu(dev(gu), f_a)
+    oa, om, ok = O.swiglu(gu, f_a)
+    np.testing.assert_array_equal(host(a8), oa)
+    np.testing.assert_array_equal(host(m), om)
+    np.testing.assert_array_equal(host(k), ok)
+
+
 def test_swiglu_every_gate(D):
     """Every gate value in [-2^17, 2^17) exactly once (256 shuffled rows of
     1024, so the table-driven kernel runs): with f_a = 12 larger gates all give
