@@ -663,26 +663,34 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
 // ------------------------------------------------------------- skinny GEMM
 
 // M <= 64 rows (batched decode, short prompts): weight streaming. A
-// 1024-thread workgroup owns 32 output columns for all rows; its 16 waves
-// split K into 16 chunks, each streaming its chunk of the weight rows from
-// HBM straight into MFMA fragments (buffer loads, two k-steps in flight per
-// wave) against A fragments that stay L2-resident. Per-wave partial sums
-// meet in LDS; integer sums are order-free, so the split changes no bit.
-// Limb planes are reduced separately in int32 (|sum| <= 2^14 K < 2^31) and
-// combined in int64 at the end.
-constexpr int SK_W = 16;   // waves per workgroup = K chunks
-constexpr int SK_G = 2;    // k-steps per load group
+// workgroup of SK_W waves owns 32 output columns for all rows; its waves
+// split K into SK_W chunks, each streaming its chunk of the weight rows from
+// HBM straight into MFMA fragments (buffer loads, one group of SK_G k-steps
+// in flight while the previous group is multiplied) against A fragments that
+// stay L2-resident. Per-wave partial sums meet in LDS; integer sums are
+// order-free, so the split changes no bit. Limb planes are reduced
+// separately in int32 (|sum| <= 2^14 K < 2^31) and combined in int64 at the
+// end. SK_W = 4 waves where the column tiles alone fill the chip (each wave
+// streams a quarter of K and several workgroups share a CU: lm_head 235 ->
+// 163 us at batch 32), 16 where few tiles need K split over waves and
+// workgroups to fill it (4 waves there left a CU a quarter of the loads).
+constexpr int SK_KQ = 512;  // K granularity of the skinny path (and of its splits)
 
 // Split-K across workgroups (grid.y = ks > 1, given a workspace): split s
 // covers K range [s K / ks, (s + 1) K / ks); each split writes its partial
 // sums for the tile to sp.part, and the last split to arrive (counted in
 // sp.cnt[tile], which it resets to 0) adds the ks partials - an exact integer
 // sum, so the split changes no bit - and runs the epilogue.
-template <bool WIDE, int MR>
-__global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A,
-                                                    const int8_t* __restrict__ W,
-                                                    const int8_t* __restrict__ Wlo, int M, int N,
-                                                    int K, Epi e, void* out, SplitWs sp) {
+template <bool WIDE, int MR, int SK_W>
+__global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restrict__ A,
+                                                         const int8_t* __restrict__ W,
+                                                         const int8_t* __restrict__ Wlo, int M, int N,
+                                                         int K, Epi e, void* out, SplitWs sp) {
+  constexpr int SK_T = 64 * SK_W;
+  constexpr int SK_O = 1024 / SK_T;  // outputs of a 32 x 32 tile per thread
+  // k-steps per load group: 16 waves keep 2 (128 registers each), 4 waves
+  // stream four times the K range and take 4
+  constexpr int SK_G = SK_W == 16 ? 2 : 4;
   constexpr int NB = WIDE ? 2 : 1;
   constexpr int TE = NB * MR * 1024 + MR * 32;       // partial ints per (tile, split)
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
@@ -774,20 +782,24 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     }
   }
   __syncthreads();
-  int32_t hs[MR], ls[MR], rss[MR];
+  // thread t finishes outputs o = t + SK_T q of each 32 x 32 block m: row
+  // m * 32 + o / 32, column o % 32
+  int32_t hs[MR][SK_O], ls[MR][SK_O], rss[MR][SK_O];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const int row = m * 32 + (tid >> 5);
-    hs[m] = ls[m] = rss[m] = 0;
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int w = 0; w < SK_W; ++w) {
-      hs[m] += part[((w * NB + 0) * MR + m) * 1024 + tid];
-      if (WIDE) {
-        ls[m] += part[((w * NB + NB - 1) * MR + m) * 1024 + tid];
-        rss[m] += prs[w * MR * 32 + row];
+    for (int q = 0; q < SK_O; ++q) {
+      const int o = tid + SK_T * q, row = m * 32 + (o >> 5);
+      hs[m][q] = ls[m][q] = rss[m][q] = 0;
+#pragma unroll
+      for (int w = 0; w < SK_W; ++w) {
+        hs[m][q] += part[((w * NB + 0) * MR + m) * 1024 + o];
+        if (WIDE) {
+          ls[m][q] += part[((w * NB + NB - 1) * MR + m) * 1024 + o];
+          rss[m][q] += prs[w * MR * 32 + row];
+        }
       }
     }
-  }
   if (ks > 1) {
     // Partials go out as agent-scope atomic stores (coherent across the
     // XCDs' L2 caches). Ordering: every thread's stores happen before the
@@ -806,11 +818,14 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     };
     int32_t* mine = sp.part + ((size_t)blockIdx.x * ks + split) * TE;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      put(&mine[m * 1024 + tid], hs[m]);
-      if (WIDE) put(&mine[(MR + m) * 1024 + tid], ls[m]);
-      if (WIDE && (tid & 31) == 0) put(&mine[NB * MR * 1024 + m * 32 + (tid >> 5)], rss[m]);
-    }
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < SK_O; ++q) {
+        const int o = tid + SK_T * q;
+        put(&mine[m * 1024 + o], hs[m][q]);
+        if (WIDE) put(&mine[(MR + m) * 1024 + o], ls[m][q]);
+        if (WIDE && (o & 31) == 0) put(&mine[NB * MR * 1024 + m * 32 + (o >> 5)], rss[m][q]);
+      }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
@@ -823,54 +838,62 @@ __global__ __launch_bounds__(1024) void gemm_skinny(const int8_t* __restrict__ A
     if (!s_last) return;
     const int32_t* all = sp.part + (size_t)blockIdx.x * ks * TE;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      hs[m] = ls[m] = rss[m] = 0;
-      for (int t = 0; t < ks; ++t) {
-        hs[m] += get(&all[t * TE + m * 1024 + tid]);
-        if (WIDE) {
-          ls[m] += get(&all[t * TE + (MR + m) * 1024 + tid]);
-          rss[m] += get(&all[t * TE + NB * MR * 1024 + m * 32 + (tid >> 5)]);
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < SK_O; ++q) {
+        const int o = tid + SK_T * q;
+        hs[m][q] = ls[m][q] = rss[m][q] = 0;
+        for (int t = 0; t < ks; ++t) {
+          hs[m][q] += get(&all[t * TE + m * 1024 + o]);
+          if (WIDE) {
+            ls[m][q] += get(&all[t * TE + (MR + m) * 1024 + o]);
+            rss[m][q] += get(&all[t * TE + NB * MR * 1024 + m * 32 + (o >> 5)]);
+          }
         }
       }
-    }
     if (tid == 0) put(&sp.cnt[blockIdx.x], 0);  // ready for the next call
   }
   if (swg) {
     // FIX value of this thread's gate or up column, then the gate thread
     // (column c < 16) takes its up partner's from the lane 16 apart
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int i = m * 32 + (tid >> 5), ic = i < M ? i : M - 1, c = tid & 31;
-      const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
-      const int wrc = wr < N ? wr : N - 1;
-      int64_t v = hs[m];
-      if (WIDE) v = 256 * v + (int64_t)ls[m] + 128 * (int64_t)rss[m];
-      const int s = e.row_k[ic] + e.col_k - e.frac;
-      const int64_t y = WIDE ? R128((__int128)(v * e.row_m[ic]) * e.col_m[wrc], s)
-                             : R(v * e.row_m[ic] * e.col_m[wrc], s);
-      const int64_t u = __shfl_xor(y, 16);
-      const int j = (n0 >> 1) + c;
-      if (c < 16 && i < M && j < (N >> 1)) {
-        bound_raise(out_of(y, 24) | out_of(u, 24) ? kBoundSwiglu : 0u);
-        ((int64_t*)out)[(size_t)i * (N >> 1) + j] = R(y * sigmoid_q15(y, e.sw_mg, e.sw_kg), 15) * u;
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < SK_O; ++q) {
+        const int o = tid + SK_T * q;
+        const int i = m * 32 + (o >> 5), ic = i < M ? i : M - 1, c = o & 31;
+        const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
+        const int wrc = wr < N ? wr : N - 1;
+        int64_t v = hs[m][q];
+        if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
+        const int s = e.row_k[ic] + e.col_k - e.frac;
+        const int64_t y = WIDE ? R128((__int128)(v * e.row_m[ic]) * e.col_m[wrc], s)
+                               : R(v * e.row_m[ic] * e.col_m[wrc], s);
+        const int64_t u = __shfl_xor(y, 16);
+        const int j = (n0 >> 1) + c;
+        if (c < 16 && i < M && j < (N >> 1)) {
+          bound_raise(out_of(y, 24) | out_of(u, 24) ? kBoundSwiglu : 0u);
+          ((int64_t*)out)[(size_t)i * (N >> 1) + j] = R(y * sigmoid_q15(y, e.sw_mg, e.sw_kg), 15) * u;
+        }
       }
-    }
     return;
   }
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const int row = m * 32 + (tid >> 5), i = row, j = n0 + (tid & 31);
-    const int32_t hi = hs[m], lo = ls[m], rs = rss[m];
-    if (i < M && j < N) {
-      int64_t v = hi;
-      if (WIDE) v = 256 * v + (int64_t)lo + 128 * (int64_t)rs;
-      epi_store<WIDE>(v, i, j, N, e, out);
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < SK_O; ++q) {
+      const int o = tid + SK_T * q;
+      const int i = m * 32 + (o >> 5), j = n0 + (o & 31);
+      if (i < M && j < N) {
+        int64_t v = hs[m][q];
+        if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
+        epi_store<WIDE>(v, i, j, N, e, out);
+      }
     }
-  }
 }
 
 // K splits for a skinny GEMM: the most workgroups that still run as one
-// round (one 1024-thread workgroup per CU, 256 CUs: a second round would
+// round (one workgroup per CU, 256 CUs: a second round would
 // repeat the whole load / reduce / epilogue latency), each split a multiple
 // of 512 bytes of K, within the workspace.
 int skinny_splits(int64_t N, int64_t K, const SplitWs* sp) {
@@ -880,25 +903,31 @@ int skinny_splits(int64_t N, int64_t K, const SplitWs* sp) {
   int ks = 1;
   for (int c = 2; c <= 16; ++c) {
     if (tiles * c > 256) break;
-    if (K % (c * 512) != 0) continue;
+    if (K % (c * SK_KQ) != 0) continue;
     if (tiles * c > sp->max_tile_splits || tiles > sp->max_tiles) break;
     ks = c;
   }
   return ks;
 }
 
+template <bool WIDE, int MR, int SK_W>
+hipError_t skinny_launch_w(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
+                           const Epi& e, void* out, const SplitWs* sp, int ks, hipStream_t st) {
+  constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
+  static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
+  const hipError_t err = set_max_lds((const void*)gemm_skinny<WIDE, MR, SK_W>, lds);
+  if (err != hipSuccess) return err;
+  const SplitWs none{};
+  gemm_skinny<WIDE, MR, SK_W><<<dim3((unsigned)((N + 31) / 32), (unsigned)ks), 64 * SK_W, lds, st>>>(
+      A, W, Wlo, M, N, K, e, out, ks > 1 ? *sp : none);
+  return hipGetLastError();
+}
+
 template <bool WIDE, int MR>
 hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                          const Epi& e, void* out, const SplitWs* sp, hipStream_t st) {
-  constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
-  static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
-  const hipError_t err = set_max_lds((const void*)gemm_skinny<WIDE, MR>, lds);
-  if (err != hipSuccess) return err;
-  const int ks = skinny_splits(N, K, sp);
-  const SplitWs none{};
-  gemm_skinny<WIDE, MR><<<dim3((unsigned)((N + 31) / 32), (unsigned)ks), 1024, lds, st>>>(
-      A, W, Wlo, M, N, K, e, out, ks > 1 ? *sp : none);
-  return hipGetLastError();
+  if ((N + 31) / 32 >= 256) return skinny_launch_w<WIDE, MR, 4>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
+  return skinny_launch_w<WIDE, MR, 16>(A, W, Wlo, M, N, K, e, out, sp, skinny_splits(N, K, sp), st);
 }
 
 // ---------------------------------------------------------------- GEMV
@@ -1182,7 +1211,7 @@ int pipe_split_count(int64_t M, int64_t N, int64_t K, int64_t part_ints) {
 
 bool gemm_takes_skinny(int64_t M, int64_t N, int64_t K, bool limbs) {
   const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
-  return M > 16 && off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !limbs));
+  return M > 16 && off32 && K % SK_KQ == 0 && (M <= 32 || (M <= 64 && !limbs));
 }
 
 DETINT_BOUND_READER(bound_flags_gemm)
@@ -1200,7 +1229,7 @@ hipError_t launch_gemm(const int8_t* A, const int8_t* W, const int8_t* W_lo, int
   if (M <= 16) return gemv_dispatch(A, W, W_lo, M, N, K, e, out, nullptr, st);
   // buffer offsets are 32-bit
   const bool off32 = M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
-  if (off32 && K % (SK_W * 32) == 0 && (M <= 32 || (M <= 64 && !W_lo))) {
+  if (off32 && K % SK_KQ == 0 && (M <= 32 || (M <= 64 && !W_lo))) {
     if (W_lo) return skinny_launch<true, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
     if (M <= 32) return skinny_launch<false, 1>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
     return skinny_launch<false, 2>(A, W, W_lo, (int)M, (int)N, (int)K, e, out, sp, st);
