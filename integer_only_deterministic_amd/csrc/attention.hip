@@ -64,7 +64,7 @@ struct HalveTo {
       for (int i = 0; i < N / 2; ++i) {
         const int keep = upper ? v[i + N / 2] : v[i];
         const int give = upper ? v[i] : v[i + N / 2];
-        v[i] = keep + __shfl_xor(give, O);
+        v[i] = keep + lane_xor<O>(give);
       }
       HalveTo<N / 2, O / 2, OMIN>::run(v, lane);
     }
@@ -195,11 +195,9 @@ __device__ __forceinline__ void attend(const v4i* sq, const int32_t* eqv, const 
   for (; j < ctx; j += RG) pv(*(const v4i*)(V + off(j) + c * 16), j);
   // reduce over the lanes of a wave that share chunk c
 #pragma unroll
-  for (int off = CH; off < 64; off <<= 1)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int b = 0; b < 16; ++b) acc[g][b] += __shfl_xor(acc[g][b], off);
+    for (int b = 0; b < 16; ++b) acc[g][b] = xor_sum_from<CH>(acc[g][b]);
   if (lane < CH) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -838,7 +836,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
           if (c * 32 + koff(r) <= pos) mx = max(mx, sacc[r]);
       }
   });
-  mx = max(mx, __shfl_xor(mx, 32));
+  mx = max(mx, lane_xor<32>(mx));
   if (!live) mx = 0;  // its values are never used; keep the arithmetic tame
 
   // E(s) = DI-Exp(R((s - mx) Ms, sh)) for s <= mx. The 32-bit form is
@@ -893,7 +891,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
       sum_chunk(c, sacc, e64);
     }
   });
-  den += __shfl_xor(den, 32);
+  den += lane_xor<32>(den);
   if (!live) den = 0;
   const uint32_t rn = den > 0 ? (uint32_t)udiv_q<32>(uint64_t(1) << 46, (uint64_t)den) : 0u;  // D >= 2^15
   // P = min(R(E rn, 31), 2^15 - 1) from 24-bit products: with rn = 2^16 rh
@@ -978,7 +976,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   int32_t* s_cs = (int32_t*)smem + wave * D;
 #pragma unroll
   for (int t = 0; t < KS; ++t) {
-    const int tot = cs[t] + __shfl_xor(cs[t], 32);
+    const int tot = cs[t] + lane_xor<32>(cs[t]);
     if (hh == 0) s_cs[32 * t + ql] = tot;
   }
   __syncthreads();

@@ -47,7 +47,7 @@ struct Halve {
     for (int i = 0; i < N / 2; ++i) {
       const int keep = upper ? v[i + N / 2] : v[i];
       const int give = upper ? v[i] : v[i + N / 2];
-      v[i] = keep + __shfl_xor(give, O);
+      v[i] = keep + lane_xor<O>(give);
     }
     return Halve<N / 2, O / 2>::run(v, lane);
   }
@@ -55,10 +55,7 @@ struct Halve {
 template <int O>
 struct Halve<1, O> {
   __device__ __forceinline__ static int run(int* v, int) {
-    int t = v[0];
-#pragma unroll
-    for (int o = O; o > 0; o >>= 1) t += __shfl_xor(t, o);
-    return t;
+    return xor_sum_to<O>(v[0]);
   }
 };
 
@@ -76,7 +73,7 @@ struct Halve64 {
     for (int i = 0; i < N / 2; ++i) {
       const int64_t keep = upper ? v[i + N / 2] : v[i];
       const int64_t give = upper ? v[i] : v[i + N / 2];
-      const int64_t got = __shfl_xor(give, O);
+      const int64_t got = lane_xor<O>(give);
       v[i] = MAX ? (got > keep ? got : keep) : keep + got;
     }
     return Halve64<N / 2, O / 2, MAX>::run(v, lane);
@@ -85,13 +82,7 @@ struct Halve64 {
 template <int O, bool MAX>
 struct Halve64<1, O, MAX> {
   __device__ __forceinline__ static int64_t run(int64_t* v, int) {
-    int64_t t = v[0];
-#pragma unroll
-    for (int o = O; o > 0; o >>= 1) {
-      const int64_t got = __shfl_xor(t, o);
-      t = MAX ? (got > t ? got : t) : t + got;
-    }
-    return t;
+    return xor_fold_to<O, MAX>(v[0]);
   }
 };
 
@@ -408,7 +399,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         if (lane == 0) ((int64_t*)p.out)[g] = res;
       }
     } else if (EPI == EPI_SWIGLU) {
-      const int up = __shfl_xor(tot, 32);  // column 1 (up) sits in the lane 32 apart
+      const int up = lane_xor<32>(tot);  // column 1 (up) sits in the lane 32 apart
       if (leader && cc == 0 && mm < M && g < ngroups) {
         const int j = g;
         const int sh = s_k[mm] + p.col_k - p.f_a;
@@ -452,7 +443,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
   }
   if (EPI == EPI_LOGITS) {
     if (CPW == 2) {
-      const int64_t o2 = __shfl_xor(bestk, 32);
+      const int64_t o2 = lane_xor<32>(bestk);
       bestk = o2 > bestk ? o2 : bestk;
     }
     if (leader && cc == 0 && mm < M) p.part[(size_t)mm * nw + gw] = bestk;

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace detint {
 
 constexpr int kWave = 64;
@@ -311,27 +313,138 @@ __device__ __forceinline__ int32_t sigmoid_q15_wave(int64_t g, int32_t Mg, int32
 }
 
 // ---------------------------------------------------------------- reductions
+//
+// Lane exchanges on the VALU rather than through the LDS crossbar
+// (ds_bpermute, which __shfl_xor compiles to): DPP quad permutes and row
+// mirrors / rotates inside 16-lane rows, and gfx950's permlane16 / permlane32
+// swaps across rows. Each step costs a few cycles instead of an LDS round
+// trip, which matters on the latency chains of the batch-1 decode kernels.
+// Workgroups are one-dimensional with a multiple of 64 threads, and every
+// lane of the wave must be active (uniform control flow).
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppRev4 = 0x1B,        // quad_perm [3,2,1,0]: lane i ^ 3
+  kDppHalfMirror = 0x141, // lane i ^ 7 within 8
+  kDppMirror = 0x140,     // lane i ^ 15 within 16
+  kDppRor8 = 0x128,       // lane i ^ 8 within 16
+};
+
+// (a, b) with a = v of the even and b = v of the odd 16-lane rows (O = 16),
+// or of the lower and upper 32 lanes (O = 32), in every lane of the pair
+template <int O>
+__device__ __forceinline__ void row_pair(uint32_t v, uint32_t& a, uint32_t& b) {
+  static_assert(O == 16 || O == 32, "row_pair: 16 or 32");
+  if constexpr (O == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = s[0];
+    b = s[1];
+  } else {
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = s[0];
+    b = s[1];
+  }
+}
+
+// v of lane (lane ^ O), O a power of two below 64
+template <int O>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (O == 1) {
+    return dpp_u32<kDppXor1>(v);
+  } else if constexpr (O == 2) {
+    return dpp_u32<kDppXor2>(v);
+  } else if constexpr (O == 4) {
+    return dpp_u32<kDppHalfMirror>(dpp_u32<kDppRev4>(v));  // i ^ 4 = (i ^ 3) ^ 7
+  } else if constexpr (O == 8) {
+    return dpp_u32<kDppRor8>(v);
+  } else {
+    uint32_t a, b;
+    row_pair<O>(v, a, b);
+    return (threadIdx.x & O) ? a : b;
+  }
+}
+template <int O>
+__device__ __forceinline__ int lane_xor(int v) {
+  return (int)lane_xor<O>((uint32_t)v);
+}
+template <int O>
+__device__ __forceinline__ int64_t lane_xor(int64_t v) {
+  const uint32_t lo = lane_xor<O>((uint32_t)(uint64_t)v);
+  const uint32_t hi = lane_xor<O>((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <int O>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
+  return (uint64_t)lane_xor<O>((int64_t)v);
+}
+
+// Whole-wave reduction of 64-bit values by an associative, commutative op;
+// every lane receives the result. After the two quad steps a quad holds one
+// value, so the half-row and row mirrors pair it with the other quad / half
+// row; the permlane swaps then pair rows.
+template <class Op>
+__device__ __forceinline__ uint64_t wave_reduce64(uint64_t v, Op op) {
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const uint64_t w = ((uint64_t)dpp_u32<C>((uint32_t)(v >> 32)) << 32) | dpp_u32<C>((uint32_t)v);
+    v = op(v, w);
+  };
+  step(std::integral_constant<int, kDppXor1>{});
+  step(std::integral_constant<int, kDppXor2>{});
+  step(std::integral_constant<int, kDppHalfMirror>{});
+  step(std::integral_constant<int, kDppMirror>{});
+  uint32_t al, bl, ah, bh;
+  row_pair<16>((uint32_t)v, al, bl);
+  row_pair<16>((uint32_t)(v >> 32), ah, bh);
+  v = op(((uint64_t)ah << 32) | al, ((uint64_t)bh << 32) | bl);
+  row_pair<32>((uint32_t)v, al, bl);
+  row_pair<32>((uint32_t)(v >> 32), ah, bh);
+  return op(((uint64_t)ah << 32) | al, ((uint64_t)bh << 32) | bl);
+}
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return (int64_t)wave_reduce64((uint64_t)v, [](uint64_t a, uint64_t b) { return a + b; });
 }
 __device__ __forceinline__ int64_t wave_max(int64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    int64_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
+  return (int64_t)wave_reduce64(
+      (uint64_t)v, [](uint64_t a, uint64_t b) { return (int64_t)a > (int64_t)b ? a : b; });
 }
 __device__ __forceinline__ uint64_t wave_max_u(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = (uint64_t)__shfl_xor((long long)v, o);
-    v = w > v ? w : v;
+  return wave_reduce64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
+
+// Sum over the lanes that differ from this one in bits O, O / 2, ..., 1
+template <int O>
+__device__ __forceinline__ int xor_sum_to(int v) {
+  if constexpr (O == 0) {
+    return v;
+  } else {
+    return xor_sum_to<O / 2>(v + lane_xor<O>(v));
   }
-  return v;
+}
+// Sum (or maximum) of 64-bit values over the lanes that differ in bits O .. 1
+template <int O, bool MAX>
+__device__ __forceinline__ int64_t xor_fold_to(int64_t v) {
+  if constexpr (O == 0) {
+    return v;
+  } else {
+    const int64_t w = lane_xor<O>(v);
+    return xor_fold_to<O / 2, MAX>(MAX ? (w > v ? w : v) : v + w);
+  }
+}
+// Sum over the lanes that differ from this one in bits O, 2 O, ..., 32
+template <int O>
+__device__ __forceinline__ int xor_sum_from(int v) {
+  if constexpr (O >= 64) {
+    return v;
+  } else {
+    return xor_sum_from<2 * O>(v + lane_xor<O>(v));
+  }
 }
 
 // Block-wide reductions for blockDim.x a multiple of 64 (<= 1024); `red` is

@@ -606,11 +606,12 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
     y1 = R(y1, g1);
   }
   uint64_t u = uabs64(y0) > uabs64(y1) ? uabs64(y0) : uabs64(y1);
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) {
-    const uint64_t w = (uint64_t)__shfl_xor((long long)u, o);
-    u = w > u ? w : u;
-  }
+  auto umax = [](uint64_t x, uint64_t y) { return x > y ? x : y; };
+  u = umax(u, lane_xor<16>(u));
+  u = umax(u, lane_xor<8>(u));
+  u = umax(u, lane_xor<4>(u));
+  u = umax(u, lane_xor<2>(u));
+  u = umax(u, lane_xor<1>(u));
   if (!live || isv) return;
   if (isq) {
     const int e = dq_exp(u);
@@ -993,9 +994,7 @@ __device__ __forceinline__ int crossing_in_step(const int64_t (&c)[4], int64_t x
 }
 
 __device__ __forceinline__ int32_t wave_sum32(int32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return xor_sum_to<32>(v);
 }
 
 // One row (blockIdx.x) by one SMT-thread workgroup; also the in-kernel
