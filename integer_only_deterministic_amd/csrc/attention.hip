@@ -330,8 +330,23 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   const int64_t cs = p.cos_t[(size_t)pos * half + jl], sn = p.sin_t[(size_t)pos * half + jl];
   asm volatile("" ::: "memory");
 
-  // 2. cached keys and values 0..min(pos, PRE)-1 into registers; rows past
-  //    them read zeros without touching memory (out-of-range offsets)
+  // 2. cached keys and values 0..min(pos, PRE)-1 into registers. Loads are
+  //    issued only where a row lies below pos - per wave for keys, per step
+  //    for values and for the first later batch (a uniform test each): a row
+  //    past the end would read zeros without touching memory but still cost
+  //    the texture unit 16 cycles per load, which on a short context is most
+  //    of the preload. Their number thus varies with pos, so the
+  //    post-processing inputs are waited for before them (a wait after them
+  //    could not count only the older loads); their latency then overlaps
+  //    the post-processing arithmetic. Lanes whose row is past the end read
+  //    zeros through an out-of-range offset.
+#pragma unroll
+  for (int u = 0; u < HR; ++u) asm volatile("" ::"v"(hx0[u]), "v"(hx1[u]));
+  if (QKN) {
+#pragma unroll
+    for (int u = 0; u < HR; ++u) asm volatile("" ::"v"(hm0[u]), "v"(hm1[u]), "v"(hg0[u]), "v"(hg1[u]));
+  }
+  asm volatile("" ::"v"(gk0), "v"(gk1), "v"(cs), "v"(sn));
   // contiguous: a buffer over this (slot, KV head) block, row j at j D;
   // paged: a buffer over the layer's pool, row j where the block table puts it
   const bool paged = kp.bt != nullptr;
@@ -346,23 +361,31 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   const __amdgpu_buffer_rsrc_t rsv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, cbytes, 0x00020000);
   const int c = tid % CH, rg = tid / CH;
+  const int wave_row0 = __builtin_amdgcn_readfirstlane(wave * 64);
+  const v4i zero4 = {0, 0, 0, 0};
   v4i kpre[KU][CH], vpre[VU];
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int j = tid + u * NT;
-    const int off = j < nold ? roff(j) : cbytes;
+    if (wave_row0 + u * NT < nold) {
+      const int off = j < nold ? roff(j) : cbytes;
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc)
-      kpre[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
+      for (int cc = 0; cc < CH; ++cc)
+        kpre[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) kpre[u][cc] = zero4;
+    }
   }
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
     const int j = rg + u * RG;
-    vpre[u] = __builtin_bit_cast(
-        v4i, __builtin_amdgcn_raw_buffer_load_b128(rsv, j < nold ? roff(j) + c * 16 : cbytes, 0, 0));
+    vpre[u] = u * RG < nold ? __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rsv, j < nold ? roff(j) + c * 16 : cbytes, 0, 0))
+                            : zero4;
   }
-  // the first batch of later cached keys too (long contexts; out-of-range
-  // rows read zeros without touching memory)
+  // the first batch of later cached keys too (long contexts; rows past the
+  // end read zeros without touching memory)
   constexpr int SK = D == 64 && NT == 256 ? 4 : 2;
   v4i ka[SK][CH], kb[SK][CH];
   auto kload = [&](v4i (&kr)[SK][CH], int b0) {
@@ -375,7 +398,14 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
         kr[u][cc] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsk, off + cc * 16, 0, 0));
     }
   };
-  kload(ka, PRE);
+  if (PRE < nold) {
+    kload(ka, PRE);
+  } else {
+#pragma unroll
+    for (int u = 0; u < SK; ++u)
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) ka[u][cc] = zero4;
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. post-processing (the integer steps of qkv_head): q -> q8, e_q (LDS);
@@ -560,30 +590,33 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     if (lane == 0) rsum[wave][g] = d;
   }
   lds_barrier();
-  for (int g = wave; g < G; g += NW) {  // one head per wave, in parallel
-    int64_t d = 0;
+  // rn = floor(2^46 / D) per head (D >= 2^15): with one or two heads every
+  // wave divides for itself, else one head per wave, in parallel, through LDS
+  uint32_t rn[G];
+  if constexpr (G <= 2) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) d += rsum[w][g];
-    const int64_t q = (int64_t)udiv_wave<32>(uint64_t(1) << 46, (uint64_t)d);  // D >= 2^15
-    if (lane == 0) rnv[g] = q;
-  }
-  lds_barrier();
-  {
-    // 6a. P = min(R(E rn, 31), 2^15 - 1) in place, once per (head, key)
-    int64_t rn[G];
+    for (int g = 0; g < G; ++g) {
+      int64_t d = 0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) rn[g] = rnv[g];
-    for (int j = tid; j < ctx; j += NT) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int64_t pp = R((int64_t)sc[g * ld + j] * rn[g], 31);
-        sc[g * ld + j] = (int32_t)(pp > 32767 ? 32767 : pp);
-      }
+      for (int w = 0; w < NW; ++w) d += rsum[w][g];
+      rn[g] = (uint32_t)udiv_wave<32>(uint64_t(1) << 46, (uint64_t)d);
     }
+  } else {
+    for (int g = wave; g < G; g += NW) {
+      int64_t d = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) d += rsum[w][g];
+      const int64_t q = (int64_t)udiv_wave<32>(uint64_t(1) << 46, (uint64_t)d);
+      if (lane == 0) rnv[g] = q;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < G; ++g) rn[g] = (uint32_t)rnv[g];
   }
-  lds_barrier();
 
-  // 6b. P.V; a lane owns a 16-byte chunk c of value rows rg, rg + RG, ...
+  // 6. P.V with P = min(R(E rn, 31), 2^15 - 1) formed as each value row is
+  //    used (the lanes sharing a row repeat it); a lane owns a 16-byte
+  //    chunk c of value rows rg, rg + RG, ...
   int acc[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -592,7 +625,8 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   auto pv = [&](const v4i& v, int j) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int P = sc[g * ld + j];
+      const uint64_t pp = ((((uint64_t)(uint32_t)sc[g * ld + j] * rn[g]) >> 30) + 1) >> 1;
+      const int P = (int)(pp > 32767 ? 32767 : pp);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         acc[g][b] += P * sbyte(v.x, b);

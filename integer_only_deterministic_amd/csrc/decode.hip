@@ -178,6 +178,11 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
     }
   };
   int g = gw;
+  // every wave streams at most one group (the decode shapes): the refills
+  // two groups ahead would all fall past the end, and a load past the end,
+  // though it reads zeros without touching memory, still costs the texture
+  // unit 16 cycles per instruction - issue none of them
+  const bool one = nw >= ngroups;
 
   if constexpr (PRO == PRO_I8) {
     // int8 rows given (a standalone GEMM): rows and their scales into LDS
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         ar[m][kc] = *(const uint32_t*)(p.a8 + (size_t)(m < M ? m : M - 1) * K + i);
     }
     load_w(g, 0);
-    load_w(g + nw, 1);
+    if (!one) load_w(g + nw, 1);
     __builtin_amdgcn_sched_barrier(0);
     if (tid < MT) {
       const int mc = tid < M ? tid : M - 1;
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
       }
     }
     load_w(g, 0);
-    load_w(g + nw, 1);
+    if (!one) load_w(g + nw, 1);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. prologue: int8 input rows and their scales into LDS. Thread t owns
@@ -289,8 +294,13 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
       }
     }
     lds_barrier();
-    // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole wave)
-    for (int r = wave; r < M; r += TPB / 64) {
+    // row scales: wave w finishes rows w, w + 4, ... (irms needs a whole
+    // wave); a single row is finished by every wave, which then needs no
+    // barrier before quantising its own elements (wave 0 publishes the
+    // scales for the epilogue, read after the barrier below)
+    constexpr bool SOLO = MT == 1;
+    int e_solo = 0;
+    for (int r = SOLO ? 0 : wave; r < M; r += SOLO ? M : TPB / 64) {
       int64_t St = 0, At = 0;
   #pragma unroll
       for (int w2 = 0; w2 < TPB / 64; ++w2) {
@@ -317,19 +327,21 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
         sm = 1 << 14;
         sk = 2 * p.f_a - e + 14;
       }
-      if (lane == 0) {
+      const int eq = (PRO == PRO_NORM && St == 0) ? 0 : e;
+      if (lane == 0 && (!SOLO || wave == 0)) {
         s_m[r] = sm;
         s_k[r] = sk;
-        s_e[r] = (PRO == PRO_NORM && St == 0) ? 0 : e;
+        s_e[r] = eq;
       }
+      e_solo = eq;
     }
-    lds_barrier();
+    if (!SOLO) lds_barrier();
     // quantised rows, zero-padded to KC * 1024 bytes (the weight loads of
     // lanes past K read clamped addresses; their products with the padding
     // are zero)
   #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int e = s_e[m < M ? m : 0];
+      const int e = SOLO ? e_solo : s_e[m < M ? m : 0];
   #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const int i = kc * 1024 + 4 * tid;
@@ -356,7 +368,8 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
   const bool leader = (lane & (64 / NV - 1)) == 0;
   const int cc = idx / MT, mm = idx % MT;  // the (column, row) this lane finishes
   int64_t bestk = INT64_MIN;
-  auto group = [&](int g, int b) {  // b is a constant at each call; g may be past the end
+  // b and refill are constants at each call; g may be past the end
+  auto group = [&](int g, int b, bool refill) {
     int32_t cm[CPW];  // this group's mantissas, before buffer b is refilled
 #pragma unroll
     for (int c = 0; c < CPW; ++c) cm[c] = cmv[b][c];
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
     // dot products so the loads reuse its registers: a copy would have to
     // wait for them)
     __builtin_amdgcn_sched_barrier(0);
-    load_w(g + 2 * nw, b);
+    if (refill) load_w(g + 2 * nw, b);
     __builtin_amdgcn_sched_barrier(0);
     const int tot = wave_reduce_t<NV>(v, lane);
     if (EPI == EPI_SWIGLU && MT == 1) {
@@ -434,12 +447,17 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
       }
     }
   };
-  // both calls unconditional (the second group may be past the end: its
-  // loads read zeros and its results are dropped), so the loop body is
-  // straight-line code and the wait for a buffer counts only older loads
-  for (; g < ngroups; g += 2 * nw) {
-    group(g, 0);
-    group(g + nw, 1);
+  // several groups per wave: both calls unconditional (the second group may
+  // be past the end: its loads read zeros and its results are dropped), so
+  // the loop body is straight-line code and the wait for a buffer counts
+  // only older loads
+  if (one) {
+    if (g < ngroups) group(g, 0, false);
+  } else {
+    for (; g < ngroups; g += 2 * nw) {
+      group(g, 0, true);
+      group(g + nw, 1, true);
+    }
   }
   if (EPI == EPI_LOGITS) {
     if (CPW == 2) {
