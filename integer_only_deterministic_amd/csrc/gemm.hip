@@ -64,6 +64,32 @@ __device__ __forceinline__ void epi_store(int64_t acc, int64_t i, int64_t j, int
   }
 }
 
+// epi_store with the output index, the row and column scales and (RES_ADD)
+// the residual already loaded
+template <bool WIDE>
+__device__ __forceinline__ void epi_store_pre(int64_t acc, int64_t o, int32_t rm, int32_t rk,
+                                              int32_t cm, int32_t res, const Epi& e, void* out) {
+  if (e.mode == MODE_RAW) {
+    if (WIDE)
+      ((int64_t*)out)[o] = acc;
+    else
+      ((int32_t*)out)[o] = (int32_t)acc;
+    return;
+  }
+  const int s = rk + e.col_k - (e.mode == MODE_REQ_I8 ? 0 : e.frac);
+  const int64_t y = WIDE ? R128((__int128)(acc * rm) * cm, s) : R(acc * rm * cm, s);
+  if (e.mode == MODE_REQ_I8) {
+    ((int8_t*)out)[o] = clamp8(y);
+  } else if (e.mode == MODE_FIX) {
+    bound_raise(i32_check(y));
+    ((int32_t*)out)[o] = (int32_t)y;
+  } else {
+    const int64_t t = (int64_t)res + y;
+    bound_raise(res_check(t, e.res_bits));
+    ((int32_t*)out)[o] = (int32_t)t;
+  }
+}
+
 __device__ __forceinline__ int dot16(const v4i& a, const v4i& b, int c) {
   c = __builtin_amdgcn_sdot4(a.x, b.x, c, false);
   c = __builtin_amdgcn_sdot4(a.y, b.y, c, false);
@@ -742,6 +768,37 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
       }
     }
   };
+  // Epilogue operands, loaded before the weights so that their latency
+  // hides under the streaming (loaded inside the epilogue, each output's
+  // scales would wait behind the previous output's store, which may alias
+  // them): per output of this thread, the row and column scales and, for
+  // RES_ADD, the residual it adds to; the output row base once. Thread t
+  // finishes outputs o = t + SK_T q of each 32 x 32 block m: row m 32 +
+  // o / 32, column o % 32 of the tile (in SWIGLU mode the weight row of
+  // that gate or up column).
+  const int64_t orb = e.out_row_base ? *e.out_row_base : 0;
+  int32_t erm[MR][SK_O], erk[MR][SK_O], ecm[MR][SK_O], eres[MR][SK_O];
+  {
+    const bool scaled = e.mode != MODE_RAW;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < SK_O; ++q) {
+        const int o = tid + SK_T * q, c = o & 31;
+        const int i = m * 32 + (o >> 5), ic = i < M ? i : M - 1;
+        int jc;
+        if (swg) {
+          const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
+          jc = wr < N ? wr : N - 1;
+        } else {
+          jc = n0 + c < N ? n0 + c : N - 1;
+        }
+        erm[m][q] = scaled ? e.row_m[ic] : 0;
+        erk[m][q] = scaled ? e.row_k[ic] : 0;
+        ecm[m][q] = scaled ? e.col_m[jc] : 0;
+        eres[m][q] = e.mode == MODE_RES_ADD ? ((const int32_t*)out)[(orb + ic) * N + jc] : 0;
+      }
+  }
   const int ng = (nst + SK_G - 1) / SK_G;
   auto group = [&](int g, int buf) {  // buf is a constant at each call
     if (g + 1 < ng) load(g + 1, buf ^ 1);
@@ -861,15 +918,13 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
 #pragma unroll
       for (int q = 0; q < SK_O; ++q) {
         const int o = tid + SK_T * q;
-        const int i = m * 32 + (o >> 5), ic = i < M ? i : M - 1, c = o & 31;
-        const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
-        const int wrc = wr < N ? wr : N - 1;
+        const int i = m * 32 + (o >> 5), c = o & 31;
         int64_t v = hs[m][q];
         if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
-        const int s = e.row_k[ic] + e.col_k - e.frac;
-        const int64_t y = WIDE ? R128((__int128)(v * e.row_m[ic]) * e.col_m[wrc], s)
-                               : R(v * e.row_m[ic] * e.col_m[wrc], s);
-        const int64_t u = __shfl_xor(y, 16);
+        const int s = erk[m][q] + e.col_k - e.frac;
+        const int64_t y = WIDE ? R128((__int128)(v * erm[m][q]) * ecm[m][q], s)
+                               : R(v * erm[m][q] * ecm[m][q], s);
+        const int64_t u = lane_xor<16>(y);
         const int j = (n0 >> 1) + c;
         if (c < 16 && i < M && j < (N >> 1)) {
           bound_raise(out_of(y, 24) | out_of(u, 24) ? kBoundSwiglu : 0u);
@@ -887,7 +942,7 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
       if (i < M && j < N) {
         int64_t v = hs[m][q];
         if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
-        epi_store<WIDE>(v, i, j, N, e, out);
+        epi_store_pre<WIDE>(v, (orb + i) * N + j, erm[m][q], erk[m][q], ecm[m][q], eres[m][q], e, out);
       }
     }
 }
