@@ -880,13 +880,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
   // <= 31, f = (2^16 - v mod 2^15) >> 1 = 2^15 - R(v mod 2^15, 1), and
   // E = R(f, n), which is 0 from n = 17 on. Other waves take the 64-bit
   // forms.
+  // Per score: one 24-bit multiply-add gives x = C - max(s, slo) Ms, then
+  // n = x >> (sh + 15) and v mod 2^15 = bits sh .. sh + 14 of x.
   const int32_t slo = mx - (int32_t)d0;
   const uint32_t c32 = (uint32_t)mx * (uint32_t)Ms + ((1u << ((sh - 1) & 31)) - 1u);
+  const int32_t nMs = -Ms;
+  const uint32_t sh15 = (uint32_t)(sh + 15) & 31u, shb = (uint32_t)sh & 31u;
   auto e32 = [&](int32_t s) -> uint32_t {
-    const uint32_t v = (c32 - (uint32_t)__mul24(max(s, slo), Ms)) >> sh;
-    const uint32_t n = v >> 15, f = (65536u - (v & 32767u)) >> 1;
+    const uint32_t x = (uint32_t)__mul24(max(s, slo), nMs) + c32;
+    const uint32_t n = x >> sh15, f = (65536u - __builtin_amdgcn_ubfe(x, shb, 15u)) >> 1;
     return (f + ((1u << n) >> 1)) >> n;
   };
+  // E = 0 exactly when v >= 16 2^15 + 1 (n = 16 leaves 1 only for v mod
+  // 2^15 = 0), i.e. when (mx - s) Ms >= T1 = (2^19 + 1) 2^sh - 2^(sh-1) + 1:
+  // for s <= szero = mx - ceil(T1 / Ms). On the 32-bit form (sh <= 11,
+  // 2^10 <= Ms) T1 < 2^31 and the quotient is below 2^21.
+  const int shz = d0 != 0 ? sh : 1;  // keeps the shifts in range on the other lanes
+  const uint64_t Mz = d0 != 0 ? (uint64_t)Ms : 1u << 10;
+  const int32_t szero = d0 != 0 ? mx - (int32_t)udiv_q<21>(((uint64_t)524289 << shz) -
+                                                               (uint64_t(1) << (shz - 1)) + Mz, Mz)
+                                : INT32_MIN;
   auto e64 = [&](int32_t s) -> uint32_t {
     return (uint32_t)(fast ? exp_delta((uint32_t)(mx - s), (uint32_t)Ms, sh)
                            : diexp(R(((int64_t)s - mx) * Ms, sh)));
@@ -901,7 +914,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
     int32_t cm = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) cm = max(cm, sacc[r]);
-    return __all(!live || (Ms > 0 && cm <= mx && ef(cm) == 0u));
+    if constexpr (std::is_same_v<decltype(ef), decltype(e32)>)
+      return __all(!live || cm <= szero);  // the same test through the threshold
+    else
+      return __all(!live || (Ms > 0 && cm <= mx && ef(cm) == 0u));
   };
 
   // pass 2: sum of exponentials
