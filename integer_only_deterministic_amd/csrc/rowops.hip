@@ -335,11 +335,12 @@ constexpr size_t kSigLds = sizeof(SigTable);  // 65552 bytes
 
 // DI-SwiGLU for many rows (prefill): a persistent grid whose workgroups copy
 // the sigmoid quotients into LDS once and then take rows w, w + G, ...; the
-// sigmoid's division becomes one LDS lookup. Two 1024-thread workgroups run
-// per CU (the table allows two), 8 waves per SIMD, so at most 64 VGPRs. Same
-// integer function as swiglu_rk, row for row.
+// sigmoid's division becomes one LDS lookup. One 1024-thread workgroup per
+// CU, 4 waves per SIMD (up to 128 VGPRs), which holds the next row's
+// gate/up values in flight while it computes the current row. Same integer
+// function as swiglu_rk, row for row.
 template <int U>
-__global__ __launch_bounds__(SWT, 8) void swiglu_tab_rk(const int32_t* __restrict__ gu, int rows, int n,
+__global__ __launch_bounds__(SWT, 4) void swiglu_tab_rk(const int32_t* __restrict__ gu, int rows, int n,
                                                      int32_t f_a, int32_t Mg, int32_t Kg, uint32_t g0,
                                                      int8_t* __restrict__ a8,
                                                      int32_t* __restrict__ rm,
@@ -361,11 +362,8 @@ __global__ __launch_bounds__(SWT, 8) void swiglu_tab_rk(const int32_t* __restric
     }
   };
   __syncthreads();  // table resident
-  // no register prefetch of the next row: 64 VGPRs leave no room for it, and
-  // with two 1024-thread workgroups per CU one workgroup's loads run under
-  // the other's arithmetic
-  for (; r < rows; r += G) {
-    load(r, gv, uv);
+  // one row: silu and the DQ'd product, in place in gv / uv
+  auto body = [&](int r, v4i (&gv)[U], v4i (&uv)[U]) {
     if (g0) {
       // 32-bit form (g0 > 0: 1 <= Kg <= 12, 2^10 <= Mg < 2^15). The sigmoid's
       // DI-Exp input v = R(|g| Mg, Kg) reaches 31 * 2^15 (E = 0) exactly from
@@ -417,7 +415,7 @@ __global__ __launch_bounds__(SWT, 8) void swiglu_tab_rk(const int32_t* __restric
         rm[r] = 1 << 14;
         rk[r] = 2 * f_a - e + 14;
       }
-      continue;
+      return;
     }
     int64_t p[U][4], A = 0;
     uint32_t bad = 0;
@@ -449,6 +447,17 @@ __global__ __launch_bounds__(SWT, 8) void swiglu_tab_rk(const int32_t* __restric
       rm[r] = 1 << 14;
       rk[r] = 2 * f_a - e + 14;
     }
+  };
+  // the next row's loads in flight under this row's arithmetic (rows past
+  // the end load the last row again; its values are not used)
+  v4i gb[U], ub[U];
+  if (r < rows) load(r, gv, uv);
+  for (; r < rows; r += 2 * G) {
+    load(min(r + G, rows - 1), gb, ub);
+    body(r, gv, uv);
+    if (r + G >= rows) break;
+    load(min(r + 2 * G, rows - 1), gv, uv);
+    body(r + G, gb, ub);
   }
 }
 
@@ -800,11 +809,14 @@ hipError_t launch_swiglu(const int32_t* gu, int64_t R, int64_t n, int32_t f_a, i
   if (n > SWT * SWPER) return hipErrorInvalidValue;
   if (n % 4 == 0 && n >= 4 && aligned_to(gu, 16) && aligned_to(a8, 4)) {
     if (R > 64) {
-      // persistent, two workgroups per CU (the table takes 64 KiB of LDS)
+      // persistent, one workgroup per CU (the table takes 64 KiB of LDS),
+      // each row's loads issued under the previous row's arithmetic: 150
+      // against 163 us per layer for two workgroups per CU without the
+      // prefetch (their 64 VGPRs leave no room for it)
       hipError_t err = set_max_lds((const void*)swiglu_tab_rk<1>, kSigLds);
       if (err == hipSuccess) err = set_max_lds((const void*)swiglu_tab_rk<2>, kSigLds);
       if (err != hipSuccess) return err;
-      const unsigned grid = (unsigned)(R < 512 ? R : 512);
+      const unsigned grid = (unsigned)(R < 256 ? R : 256);
       // clamp of the 32-bit form: the least |g| with R(|g| Mg, Kg) >= 31 2^15,
       // ceil((31 2^(15 + Kg) - 2^(Kg - 1)) / Mg); 0 (the 64-bit form) outside
       // 1 <= Kg <= 12, 2^10 <= Mg < 2^15
