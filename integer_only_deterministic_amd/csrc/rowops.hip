@@ -574,8 +574,12 @@ __global__ __launch_bounds__(TPB) void qkv_post_k(const int32_t* __restrict__ qk
 // handles head 2 w + h. The same integer steps as qkv_head without q/k-norm;
 // the query's DQ maximum is reduced over its half only (xor offsets below
 // 32 stay within a half). Every lane takes part in the reduction; a half
-// past the last head stores nothing.
-__global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict__ qkv, int nq,
+// past the last head stores nothing. A workgroup takes RPW consecutive rows
+// (their loads all issued before the first wait, then their RoPE table
+// rows), so that the two dependent round trips (position, then table row)
+// are paid once per RPW rows rather than per row.
+template <int RPW>
+__global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict__ qkv, int rows, int nq,
                                                        int nkv, const int32_t* __restrict__ pos_of,
                                                        const int32_t* __restrict__ slot_of,
                                                        QkvPost p, int8_t* __restrict__ q8,
@@ -584,57 +588,75 @@ __global__ __launch_bounds__(TPB) void qkv_post_pair_k(const int32_t* __restrict
                                                        int8_t* __restrict__ vc, int n_slots,
                                                        int max_pos, KvPages kp) {
   constexpr int d = 64, half = 32;
-  const int r = blockIdx.x, li = threadIdx.x & 31;
+  const int li = threadIdx.x & 31;
   const int nh = nq + 2 * nkv;
   const int hh = (blockIdx.y * (TPB / 64) + (threadIdx.x >> 6)) * 2 + ((threadIdx.x >> 5) & 1);
   const bool live = hh < nh;
   const int hc = live ? hh : nh - 1;
   const bool isq = hc < nq, isv = hc >= nq + nkv;
-  const int pos = pos_of[r], slot = slot_of[r];
-  const bool ok = pos >= 0 && pos < max_pos && slot >= 0 && slot < n_slots;
-  const int32_t* row = qkv + (size_t)r * nh * d + (size_t)hc * d;
-  const int j0 = li, j1 = li + half;
-  const int64_t x0 = row[j0], x1 = row[j1];  // f_n fixed point from the GEMM epilogue
-  uint32_t bad = 0;
-  if (isv && live && ok) {
-    int8_t* dst = vc + kv_row_off(kp, slot, hc - nq - nkv, nkv, max_pos, d, pos, bad);
-    dst[j0] = clamp8(R(x0 * p.vq_m, p.vq_k));
-    dst[j1] = clamp8(R(x1 * p.vq_m, p.vq_k));
-  }
-  const int pc = ok ? pos : 0;
-  const int64_t c = p.cos_t[(size_t)pc * half + li], sn = p.sin_t[(size_t)pc * half + li];
-  int64_t y0 = ok ? R(x0 * c - x1 * sn, 14) : 0;
-  int64_t y1 = ok ? R(x1 * c + x0 * sn, 14) : 0;
-  if (live && !isv) bad |= i32_check(y0) | i32_check(y1);  // rotated q / k within int32
-  bound_raise(bad);
   const int kvh = isq ? hc >> (__builtin_ctz(nq) - __builtin_ctz(nkv)) : (isv ? 0 : hc - nq);
+  const int j0 = li, j1 = li + half;
+  // rows past the last repeat it (loads only; nothing is stored for them)
+  int pos[RPW], slot[RPW];
+  int64_t x0[RPW], x1[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int rr = min((int)blockIdx.x * RPW + i, rows - 1);
+    pos[i] = pos_of[rr];
+    slot[i] = slot_of[rr];
+    const int32_t* row = qkv + (size_t)rr * nh * d + (size_t)hc * d;
+    x0[i] = row[j0];  // f_n fixed point from the GEMM epilogue
+    x1[i] = row[j1];
+  }
+  int64_t c[RPW], sn[RPW];
+  bool ok[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    ok[i] = (int)blockIdx.x * RPW + i < rows && pos[i] >= 0 && pos[i] < max_pos && slot[i] >= 0 &&
+            slot[i] < n_slots;
+    const int pc = ok[i] ? pos[i] : 0;
+    c[i] = p.cos_t[(size_t)pc * half + li];
+    sn[i] = p.sin_t[(size_t)pc * half + li];
+  }
   const int g0 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j0] & 7 : 0;
   const int g1 = p.k_gain && !isv ? p.k_gain[(size_t)kvh * d + j1] & 7 : 0;
-  if (isq) {  // the inverse of the key gain
-    y0 = R(y0, g0);
-    y1 = R(y1, g1);
+  uint32_t bad = 0;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = (int)blockIdx.x * RPW + i;
+    if (isv && live && ok[i]) {
+      int8_t* dst = vc + kv_row_off(kp, slot[i], hc - nq - nkv, nkv, max_pos, d, pos[i], bad);
+      dst[j0] = clamp8(R(x0[i] * p.vq_m, p.vq_k));
+      dst[j1] = clamp8(R(x1[i] * p.vq_m, p.vq_k));
+    }
+    int64_t y0 = ok[i] ? R(x0[i] * c[i] - x1[i] * sn[i], 14) : 0;
+    int64_t y1 = ok[i] ? R(x1[i] * c[i] + x0[i] * sn[i], 14) : 0;
+    if (live && !isv) bad |= i32_check(y0) | i32_check(y1);  // rotated q / k within int32
+    if (isq) {  // the inverse of the key gain
+      y0 = R(y0, g0);
+      y1 = R(y1, g1);
+    }
+    uint64_t u = uabs64(y0) > uabs64(y1) ? uabs64(y0) : uabs64(y1);
+    auto umax = [](uint64_t x, uint64_t y) { return x > y ? x : y; };
+    u = umax(u, lane_xor<16>(u));
+    u = umax(u, lane_xor<8>(u));
+    u = umax(u, lane_xor<4>(u));
+    u = umax(u, lane_xor<2>(u));
+    u = umax(u, lane_xor<1>(u));
+    if (!live || isv || r >= rows) continue;
+    if (isq) {
+      const int e = dq_exp(u);
+      int8_t* qd = q8 + ((size_t)r * nq + hc) * d;
+      qd[j0] = clamp8(R(y0, e));
+      qd[j1] = clamp8(R(y1, e));
+      if (li == 0) e_q[(size_t)r * nq + hc] = e;
+    } else if (ok[i]) {
+      int8_t* dst = kc + kv_row_off(kp, slot[i], kvh, nkv, max_pos, d, pos[i], bad);
+      dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
+      dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
+    }
   }
-  uint64_t u = uabs64(y0) > uabs64(y1) ? uabs64(y0) : uabs64(y1);
-  auto umax = [](uint64_t x, uint64_t y) { return x > y ? x : y; };
-  u = umax(u, lane_xor<16>(u));
-  u = umax(u, lane_xor<8>(u));
-  u = umax(u, lane_xor<4>(u));
-  u = umax(u, lane_xor<2>(u));
-  u = umax(u, lane_xor<1>(u));
-  if (!live || isv) return;
-  if (isq) {
-    const int e = dq_exp(u);
-    int8_t* qd = q8 + ((size_t)r * nq + hc) * d;
-    qd[j0] = clamp8(R(y0, e));
-    qd[j1] = clamp8(R(y1, e));
-    if (li == 0) e_q[(size_t)r * nq + hc] = e;
-  } else if (ok) {
-    uint32_t badk = 0;
-    int8_t* dst = kc + kv_row_off(kp, slot, kvh, nkv, max_pos, d, pos, badk);
-    bound_raise(badk);
-    dst[j0] = clamp8(R(y0 * p.kq_m, p.kq_k - g0));
-    dst[j1] = clamp8(R(y1 * p.kq_m, p.kq_k - g1));
-  }
+  bound_raise(bad);
 }
 
 // Greedy argmax with the lowest index among maxima (DetLLM blog "DetLLM").
@@ -891,9 +913,10 @@ hipError_t launch_qkv_post(const int32_t* qkv, int64_t R, int64_t nq, int64_t nk
   if (R == 0) return hipSuccess;
   if (!p.qk_norm && d == 64) {  // two heads per wave
     const unsigned hp = (unsigned)((nq + 2 * nkv + 2 * (TPB / 64) - 1) / (2 * (TPB / 64)));
-    qkv_post_pair_k<<<dim3((unsigned)R, hp), TPB, 0, st>>>(qkv, (int)nq, (int)nkv, pos_of, slot_of,
-                                                           p, q8, e_q, kc, vc, (int)n_slots,
-                                                           (int)max_pos, kp);
+    constexpr int RPW = 4;
+    qkv_post_pair_k<RPW><<<dim3((unsigned)((R + RPW - 1) / RPW), hp), TPB, 0, st>>>(
+        qkv, (int)R, (int)nq, (int)nkv, pos_of, slot_of, p, q8, e_q, kc, vc, (int)n_slots,
+        (int)max_pos, kp);
     return hipGetLastError();
   }
   const unsigned hb = (unsigned)((nq + 2 * nkv + 3) / 4);  // 4 heads (waves) per workgroup
