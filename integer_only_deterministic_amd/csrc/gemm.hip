@@ -776,26 +776,36 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
   // finishes outputs o = t + SK_T q of each 32 x 32 block m: row m 32 +
   // o / 32, column o % 32 of the tile (in SWIGLU mode the weight row of
   // that gate or up column).
+  // The rows' scales come from one load per lane (lane l: row min(l, M - 1),
+  // M <= 64), handed out by lane reads after the stream (a read here would
+  // wait for the load before the weights go out): output o of block m sits
+  // in row m 32 + 2 wave + 2 SK_W q + (lane >= 32), so two wave-uniform lane
+  // reads serve each (m, q) - per-output loads would cost the texture unit
+  // as much as a third of the weight stream. The column's mantissa is the
+  // same for every (m, q) of a thread (column o % 32 = lane % 32).
   const int64_t orb = e.out_row_base ? *e.out_row_base : 0;
-  int32_t erm[MR][SK_O], erk[MR][SK_O], ecm[MR][SK_O], eres[MR][SK_O];
+  int32_t eres[MR][SK_O];
+  int32_t ecm, vrm, vrk;
+  const int w2 = 2 * __builtin_amdgcn_readfirstlane(wave);
   {
     const bool scaled = e.mode != MODE_RAW;
+    const int lr = lane < M ? lane : M - 1;
+    vrm = scaled ? e.row_m[lr] : 0;
+    vrk = scaled ? e.row_k[lr] : 0;
+    const int c = lane & 31;
+    int jc;
+    if (swg) {
+      const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
+      jc = wr < N ? wr : N - 1;
+    } else {
+      jc = n0 + c < N ? n0 + c : N - 1;
+    }
+    ecm = scaled ? e.col_m[jc] : 0;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int q = 0; q < SK_O; ++q) {
-        const int o = tid + SK_T * q, c = o & 31;
-        const int i = m * 32 + (o >> 5), ic = i < M ? i : M - 1;
-        int jc;
-        if (swg) {
-          const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
-          jc = wr < N ? wr : N - 1;
-        } else {
-          jc = n0 + c < N ? n0 + c : N - 1;
-        }
-        erm[m][q] = scaled ? e.row_m[ic] : 0;
-        erk[m][q] = scaled ? e.row_k[ic] : 0;
-        ecm[m][q] = scaled ? e.col_m[jc] : 0;
+        const int i = m * 32 + w2 + 2 * SK_W * q + (lane >> 5), ic = i < M ? i : M - 1;
         eres[m][q] = e.mode == MODE_RES_ADD ? ((const int32_t*)out)[(orb + ic) * N + jc] : 0;
       }
   }
@@ -910,6 +920,17 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
       }
     if (tid == 0) put(&sp.cnt[blockIdx.x], 0);  // ready for the next call
   }
+  int32_t erm[MR][SK_O], erk[MR][SK_O];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < SK_O; ++q) {
+      const int ib = m * 32 + w2 + 2 * SK_W * q;  // <= 62
+      const int32_t m0 = __builtin_amdgcn_readlane(vrm, ib), m1 = __builtin_amdgcn_readlane(vrm, ib + 1);
+      const int32_t k0 = __builtin_amdgcn_readlane(vrk, ib), k1 = __builtin_amdgcn_readlane(vrk, ib + 1);
+      erm[m][q] = lane < 32 ? m0 : m1;
+      erk[m][q] = lane < 32 ? k0 : k1;
+    }
   if (swg) {
     // FIX value of this thread's gate or up column, then the gate thread
     // (column c < 16) takes its up partner's from the lane 16 apart
@@ -922,8 +943,8 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
         int64_t v = hs[m][q];
         if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
         const int s = erk[m][q] + e.col_k - e.frac;
-        const int64_t y = WIDE ? R128((__int128)(v * erm[m][q]) * ecm[m][q], s)
-                               : R(v * erm[m][q] * ecm[m][q], s);
+        const int64_t y = WIDE ? R128((__int128)(v * erm[m][q]) * ecm, s)
+                               : R(v * erm[m][q] * ecm, s);
         const int64_t u = lane_xor<16>(y);
         const int j = (n0 >> 1) + c;
         if (c < 16 && i < M && j < (N >> 1)) {
@@ -942,7 +963,7 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
       if (i < M && j < N) {
         int64_t v = hs[m][q];
         if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
-        epi_store_pre<WIDE>(v, (orb + i) * N + j, erm[m][q], erk[m][q], ecm[m][q], eres[m][q], e, out);
+        epi_store_pre<WIDE>(v, (orb + i) * N + j, erm[m][q], erk[m][q], ecm, eres[m][q], e, out);
       }
     }
 }
