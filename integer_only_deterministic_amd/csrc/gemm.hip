@@ -707,7 +707,7 @@ constexpr int SK_KQ = 512;  // K granularity of the skinny path (and of its spli
 // sums for the tile to sp.part, and the last split to arrive (counted in
 // sp.cnt[tile], which it resets to 0) adds the ks partials - an exact integer
 // sum, so the split changes no bit - and runs the epilogue.
-template <bool WIDE, int MR, int SK_W>
+template <bool WIDE, int MR, int SK_W, int NC>
 __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restrict__ A,
                                                          const int8_t* __restrict__ W,
                                                          const int8_t* __restrict__ Wlo, int M, int N,
@@ -715,52 +715,64 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
   constexpr int SK_T = 64 * SK_W;
   constexpr int SK_O = 1024 / SK_T;  // outputs of a 32 x 32 tile per thread
   // k-steps per load group: 16 waves keep 2 (128 registers each), 4 waves
-  // stream four times the K range and take 4
-  constexpr int SK_G = SK_W == 16 ? 2 : 4;
+  // stream four times the K range and take 4, or 2 with two column tiles
+  constexpr int SK_G = SK_W == 16 || NC == 2 ? 2 : 4;
   constexpr int NB = WIDE ? 2 : 1;
   constexpr int TE = NB * MR * 1024 + MR * 32;       // partial ints per (tile, split)
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  int32_t* part = (int32_t*)smem;                   // [SK_W][NB][MR][32 * 32]
-  int32_t* prs = part + SK_W * NB * MR * 1024;       // [SK_W][MR * 32] row sums
+  int32_t* part = (int32_t*)smem;                   // [SK_W][NC][NB][MR][32 * 32]
+  int32_t* prs = part + SK_W * NC * NB * MR * 1024;  // [SK_W][MR * 32] row sums
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 32, ks = gridDim.y, split = blockIdx.y;
+  const int n0 = blockIdx.x * 32 * NC, ks = gridDim.y, split = blockIdx.y;
   const int kspl = (int)udiv32((uint32_t)K, (uint32_t)ks);  // K range of one split
   const int kc = kspl / SK_W, nst = kc / 32;
   const int kb = split * kspl + wave * kc + (lane >> 5) * 16;
   const __amdgpu_buffer_rsrc_t ra = brsrc(A, (int64_t)M * K);
   const __amdgpu_buffer_rsrc_t rb = brsrc(W, (int64_t)N * K);
   const __amdgpu_buffer_rsrc_t rl = brsrc(WIDE ? Wlo : W, (int64_t)N * K);
-  // weight row of this lane's output column; in SWIGLU mode a tile's 32
-  // columns are gate columns j0 .. j0 + 15 then up columns j0 .. j0 + 15
-  // (j0 = n0 / 2), so each gate/up pair meets in one workgroup
+  // weight row of this lane's output column in column tile t (columns n0 +
+  // 32 t ..); in SWIGLU mode a tile's 32 columns are gate columns j0 .. j0 +
+  // 15 then up columns j0 .. j0 + 15 (j0 = n0t / 2), so each gate/up pair
+  // meets in one workgroup. With NC = 2 tiles every A fragment serves two
+  // tiles' MFMAs, halving the A loads per weight load.
   const bool swg = e.mode == MODE_SWIGLU;
   const int cl = lane & 31;
-  const int wrow = swg ? (cl < 16 ? (n0 >> 1) + cl : (N >> 1) + (n0 >> 1) + cl - 16) : n0 + cl;
-  const int aoff = (lane & 31) * K + kb, woff = wrow * K + kb;
+  const int aoff = (lane & 31) * K + kb;
+  int woff[NC];
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    const int n0t = n0 + 32 * t;
+    const int wrow = swg ? (cl < 16 ? (n0t >> 1) + cl : (N >> 1) + (n0t >> 1) + cl - 16) : n0t + cl;
+    woff[t] = wrow * K + kb;
+  }
 
-  v16i acc[NB][MR];
+  v16i acc[NC][NB][MR];
 #pragma unroll
-  for (int p = 0; p < NB; ++p)
+  for (int t = 0; t < NC; ++t)
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+    for (int p = 0; p < NB; ++p)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[p][m][r] = 0;
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][p][m][r] = 0;
   int rsum[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) rsum[m] = 0;
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-  v4i fa[2][SK_G][MR], fw[2][SK_G][NB];
+  v4i fa[2][SK_G][MR], fw[2][SK_G][NC][NB];
   auto load = [&](int g, int buf) {
 #pragma unroll
     for (int s = 0; s < SK_G; ++s) {
       const int k = (g * SK_G + s) * 32;
       if (g * SK_G + s < nst) {
 #pragma unroll
-        for (int p = 0; p < NB; ++p)
-          fw[buf][s][p] = __builtin_bit_cast(
-              v4i, __builtin_amdgcn_raw_buffer_load_b128(p ? rl : rb, woff + k, 0, 0));
+        for (int t = 0; t < NC; ++t)
+#pragma unroll
+          for (int p = 0; p < NB; ++p)
+            fw[buf][s][t][p] = __builtin_bit_cast(
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(p ? rl : rb, woff[t] + k, 0, 0));
 #pragma unroll
         for (int m = 0; m < MR; ++m)
           fa[buf][s][m] = __builtin_bit_cast(
@@ -784,8 +796,8 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
   // as much as a third of the weight stream. The column's mantissa is the
   // same for every (m, q) of a thread (column o % 32 = lane % 32).
   const int64_t orb = e.out_row_base ? *e.out_row_base : 0;
-  int32_t eres[MR][SK_O];
-  int32_t ecm, vrm, vrk;
+  int32_t eres[NC][MR][SK_O];
+  int32_t ecm[NC], vrm, vrk;
   const int w2 = 2 * __builtin_amdgcn_readfirstlane(wave);
   {
     const bool scaled = e.mode != MODE_RAW;
@@ -793,21 +805,25 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
     vrm = scaled ? e.row_m[lr] : 0;
     vrk = scaled ? e.row_k[lr] : 0;
     const int c = lane & 31;
-    int jc;
-    if (swg) {
-      const int wr = c < 16 ? (n0 >> 1) + c : (N >> 1) + (n0 >> 1) + c - 16;
-      jc = wr < N ? wr : N - 1;
-    } else {
-      jc = n0 + c < N ? n0 + c : N - 1;
-    }
-    ecm = scaled ? e.col_m[jc] : 0;
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int q = 0; q < SK_O; ++q) {
-        const int i = m * 32 + w2 + 2 * SK_W * q + (lane >> 5), ic = i < M ? i : M - 1;
-        eres[m][q] = e.mode == MODE_RES_ADD ? ((const int32_t*)out)[(orb + ic) * N + jc] : 0;
+    for (int t = 0; t < NC; ++t) {
+      const int n0t = n0 + 32 * t;
+      int jc;
+      if (swg) {
+        const int wr = c < 16 ? (n0t >> 1) + c : (N >> 1) + (n0t >> 1) + c - 16;
+        jc = wr < N ? wr : N - 1;
+      } else {
+        jc = n0t + c < N ? n0t + c : N - 1;
       }
+      ecm[t] = scaled ? e.col_m[jc] : 0;
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int q = 0; q < SK_O; ++q) {
+          const int i = m * 32 + w2 + 2 * SK_W * q + (lane >> 5), ic = i < M ? i : M - 1;
+          eres[t][m][q] = e.mode == MODE_RES_ADD ? ((const int32_t*)out)[(orb + ic) * N + jc] : 0;
+        }
+    }
   }
   const int ng = (nst + SK_G - 1) / SK_G;
   auto group = [&](int g, int buf) {  // buf is a constant at each call
@@ -818,9 +834,11 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
 #pragma unroll
-          for (int p = 0; p < NB; ++p)
-            acc[p][m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][s][m], fw[buf][s][p],
-                                                              acc[p][m], 0, 0, 0);
+          for (int t = 0; t < NC; ++t)
+#pragma unroll
+            for (int p = 0; p < NB; ++p)
+              acc[t][p][m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[buf][s][m], fw[buf][s][t][p],
+                                                                   acc[t][p][m], 0, 0, 0);
           if (WIDE) rsum[m] = dot16(fa[buf][s][m], ones, rsum[m]);
         }
       }
@@ -834,13 +852,15 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
   // partials to LDS (accumulator layout: lane l, register r -> row
   // 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32)
 #pragma unroll
-  for (int p = 0; p < NB; ++p)
+  for (int t = 0; t < NC; ++t)
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+    for (int p = 0; p < NB; ++p)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        part[((wave * NB + p) * MR + m) * 1024 + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 +
-             (lane & 31)] = acc[p][m][r];
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part[(((wave * NC + t) * NB + p) * MR + m) * 1024 + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 +
+               (lane & 31)] = acc[t][p][m][r];
   if (WIDE) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -851,23 +871,27 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
   __syncthreads();
   // thread t finishes outputs o = t + SK_T q of each 32 x 32 block m: row
   // m * 32 + o / 32, column o % 32
-  int32_t hs[MR][SK_O], ls[MR][SK_O], rss[MR][SK_O];
+  int32_t hs[NC][MR][SK_O], ls[NC][MR][SK_O], rss[MR][SK_O];
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int q = 0; q < SK_O; ++q) {
       const int o = tid + SK_T * q, row = m * 32 + (o >> 5);
-      hs[m][q] = ls[m][q] = rss[m][q] = 0;
+      rss[m][q] = 0;
+#pragma unroll
+      for (int t = 0; t < NC; ++t) hs[t][m][q] = ls[t][m][q] = 0;
 #pragma unroll
       for (int w = 0; w < SK_W; ++w) {
-        hs[m][q] += part[((w * NB + 0) * MR + m) * 1024 + o];
-        if (WIDE) {
-          ls[m][q] += part[((w * NB + NB - 1) * MR + m) * 1024 + o];
-          rss[m][q] += prs[w * MR * 32 + row];
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+          hs[t][m][q] += part[(((w * NC + t) * NB + 0) * MR + m) * 1024 + o];
+          if (WIDE) ls[t][m][q] += part[(((w * NC + t) * NB + NB - 1) * MR + m) * 1024 + o];
         }
+        if (WIDE) rss[m][q] += prs[w * MR * 32 + row];
       }
     }
-  if (ks > 1) {
+  // (split K runs with one column tile per workgroup: NC = 1)
+  if (NC == 1 && ks > 1) {
     // Partials go out as agent-scope atomic stores (coherent across the
     // XCDs' L2 caches). Ordering: every thread's stores happen before the
     // workgroup barrier; thread 0's arrival is a release RMW at agent scope,
@@ -889,8 +913,8 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
 #pragma unroll
       for (int q = 0; q < SK_O; ++q) {
         const int o = tid + SK_T * q;
-        put(&mine[m * 1024 + o], hs[m][q]);
-        if (WIDE) put(&mine[(MR + m) * 1024 + o], ls[m][q]);
+        put(&mine[m * 1024 + o], hs[0][m][q]);
+        if (WIDE) put(&mine[(MR + m) * 1024 + o], ls[0][m][q]);
         if (WIDE && (o & 31) == 0) put(&mine[NB * MR * 1024 + m * 32 + (o >> 5)], rss[m][q]);
       }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -909,11 +933,11 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
 #pragma unroll
       for (int q = 0; q < SK_O; ++q) {
         const int o = tid + SK_T * q;
-        hs[m][q] = ls[m][q] = rss[m][q] = 0;
+        hs[0][m][q] = ls[0][m][q] = rss[m][q] = 0;
         for (int t = 0; t < ks; ++t) {
-          hs[m][q] += get(&all[t * TE + m * 1024 + o]);
+          hs[0][m][q] += get(&all[t * TE + m * 1024 + o]);
           if (WIDE) {
-            ls[m][q] += get(&all[t * TE + (MR + m) * 1024 + o]);
+            ls[0][m][q] += get(&all[t * TE + (MR + m) * 1024 + o]);
             rss[m][q] += get(&all[t * TE + NB * MR * 1024 + m * 32 + (o >> 5)]);
           }
         }
@@ -935,18 +959,20 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
     // FIX value of this thread's gate or up column, then the gate thread
     // (column c < 16) takes its up partner's from the lane 16 apart
 #pragma unroll
+    for (int t = 0; t < NC; ++t)
+#pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int q = 0; q < SK_O; ++q) {
         const int o = tid + SK_T * q;
         const int i = m * 32 + (o >> 5), c = o & 31;
-        int64_t v = hs[m][q];
-        if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
+        int64_t v = hs[t][m][q];
+        if (WIDE) v = 256 * v + (int64_t)ls[t][m][q] + 128 * (int64_t)rss[m][q];
         const int s = erk[m][q] + e.col_k - e.frac;
-        const int64_t y = WIDE ? R128((__int128)(v * erm[m][q]) * ecm, s)
-                               : R(v * erm[m][q] * ecm, s);
+        const int64_t y = WIDE ? R128((__int128)(v * erm[m][q]) * ecm[t], s)
+                               : R(v * erm[m][q] * ecm[t], s);
         const int64_t u = lane_xor<16>(y);
-        const int j = (n0 >> 1) + c;
+        const int j = ((n0 + 32 * t) >> 1) + c;
         if (c < 16 && i < M && j < (N >> 1)) {
           bound_raise(out_of(y, 24) | out_of(u, 24) ? kBoundSwiglu : 0u);
           ((int64_t*)out)[(size_t)i * (N >> 1) + j] = R(y * sigmoid_q15(y, e.sw_mg, e.sw_kg), 15) * u;
@@ -955,17 +981,19 @@ __global__ __launch_bounds__(64 * SK_W) void gemm_skinny(const int8_t* __restric
     return;
   }
 #pragma unroll
-  for (int m = 0; m < MR; ++m)
+  for (int t = 0; t < NC; ++t)
 #pragma unroll
-    for (int q = 0; q < SK_O; ++q) {
-      const int o = tid + SK_T * q;
-      const int i = m * 32 + (o >> 5), j = n0 + (o & 31);
-      if (i < M && j < N) {
-        int64_t v = hs[m][q];
-        if (WIDE) v = 256 * v + (int64_t)ls[m][q] + 128 * (int64_t)rss[m][q];
-        epi_store_pre<WIDE>(v, (orb + i) * N + j, erm[m][q], erk[m][q], ecm, eres[m][q], e, out);
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < SK_O; ++q) {
+        const int o = tid + SK_T * q;
+        const int i = m * 32 + (o >> 5), j = n0 + 32 * t + (o & 31);
+        if (i < M && j < N) {
+          int64_t v = hs[t][m][q];
+          if (WIDE) v = 256 * v + (int64_t)ls[t][m][q] + 128 * (int64_t)rss[m][q];
+          epi_store_pre<WIDE>(v, (orb + i) * N + j, erm[m][q], erk[m][q], ecm[t], eres[t][m][q], e, out);
+        }
       }
-    }
 }
 
 // K splits for a skinny GEMM: the most workgroups that still run as one
@@ -986,15 +1014,16 @@ int skinny_splits(int64_t N, int64_t K, const SplitWs* sp) {
   return ks;
 }
 
-template <bool WIDE, int MR, int SK_W>
+template <bool WIDE, int MR, int SK_W, int NC = 1>
 hipError_t skinny_launch_w(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                            const Epi& e, void* out, const SplitWs* sp, int ks, hipStream_t st) {
-  constexpr int lds = (SK_W * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
+  constexpr int lds = (SK_W * NC * (WIDE ? 2 : 1) * MR * 1024 + SK_W * MR * 32) * 4;
   static_assert(lds <= 160 * 1024, "skinny partials exceed the workgroup LDS");
-  const hipError_t err = set_max_lds((const void*)gemm_skinny<WIDE, MR, SK_W>, lds);
+  if (NC > 1 && ks > 1) return hipErrorInvalidValue;  // split K takes one column tile
+  const hipError_t err = set_max_lds((const void*)gemm_skinny<WIDE, MR, SK_W, NC>, lds);
   if (err != hipSuccess) return err;
   const SplitWs none{};
-  gemm_skinny<WIDE, MR, SK_W><<<dim3((unsigned)((N + 31) / 32), (unsigned)ks), 64 * SK_W, lds, st>>>(
+  gemm_skinny<WIDE, MR, SK_W, NC><<<dim3((unsigned)((N + 32 * NC - 1) / (32 * NC)), (unsigned)ks), 64 * SK_W, lds, st>>>(
       A, W, Wlo, M, N, K, e, out, ks > 1 ? *sp : none);
   return hipGetLastError();
 }
@@ -1002,6 +1031,7 @@ hipError_t skinny_launch_w(const int8_t* A, const int8_t* W, const int8_t* Wlo, 
 template <bool WIDE, int MR>
 hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                          const Epi& e, void* out, const SplitWs* sp, hipStream_t st) {
+  if ((N + 63) / 64 >= 256) return skinny_launch_w<WIDE, MR, 4, 2>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
   if ((N + 31) / 32 >= 256) return skinny_launch_w<WIDE, MR, 4>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
   return skinny_launch_w<WIDE, MR, 16>(A, W, Wlo, M, N, K, e, out, sp, skinny_splits(N, K, sp), st);
 }
