@@ -700,6 +700,10 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
 // streams a quarter of K and several workgroups share a CU: lm_head 235 ->
 // 163 us at batch 32), 16 where few tiles need K split over waves and
 // workgroups to fill it (4 waves there left a CU a quarter of the loads).
+// Where 64-column tiles still give 256 workgroups, a workgroup takes two
+// adjacent 32-column tiles (NC = 2): each A fragment, reloaded per tile
+// otherwise, feeds both tiles' MFMAs (64 x 1024 x 151936, cache-cold: 107
+// -> 88 us; batch-32 limb gate/up 26.6 -> 25.4 us).
 constexpr int SK_KQ = 512;  // K granularity of the skinny path (and of its splits)
 
 // Split-K across workgroups (grid.y = ks > 1, given a workspace): split s
