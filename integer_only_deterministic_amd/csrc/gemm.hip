@@ -703,7 +703,8 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
 // Where 64-column tiles still give 256 workgroups, a workgroup takes two
 // adjacent 32-column tiles (NC = 2): each A fragment, reloaded per tile
 // otherwise, feeds both tiles' MFMAs (64 x 1024 x 151936, cache-cold: 107
-// -> 88 us; batch-32 limb gate/up 26.6 -> 25.4 us).
+// -> 88 us; batch-32 limb gate/up 26.6 -> 25.4 us; not the limb lm_head,
+// see skinny_launch).
 constexpr int SK_KQ = 512;  // K granularity of the skinny path (and of its splits)
 
 // Split-K across workgroups (grid.y = ks > 1, given a workspace): split s
@@ -1035,7 +1036,12 @@ hipError_t skinny_launch_w(const int8_t* A, const int8_t* W, const int8_t* Wlo, 
 template <bool WIDE, int MR>
 hipError_t skinny_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N, int K,
                          const Epi& e, void* out, const SplitWs* sp, hipStream_t st) {
-  if ((N + 63) / 64 >= 256) return skinny_launch_w<WIDE, MR, 4, 2>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
+  // two tiles per workgroup: limb weights already load two weight
+  // fragments per A fragment, so on a vocabulary-wide limb head (4008
+  // tiles, already many workgroups per CU) the saving does not pay for the
+  // lower occupancy (165.5 against 167.0 us)
+  if ((N + 63) / 64 >= 256 && (!WIDE || (N + 31) / 32 < 2048))
+    return skinny_launch_w<WIDE, MR, 4, 2>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
   if ((N + 31) / 32 >= 256) return skinny_launch_w<WIDE, MR, 4>(A, W, Wlo, M, N, K, e, out, sp, 1, st);
   return skinny_launch_w<WIDE, MR, 16>(A, W, Wlo, M, N, K, e, out, sp, skinny_splits(N, K, sp), st);
 }
