@@ -60,6 +60,29 @@ def timed(fn, n, torch):
     return s.elapsed_time(e) / 1e3 / n
 
 
+def timed_graph(fn, n, torch, reps=5):
+    """Average seconds per call of fn with the host's launch cost taken out:
+    n back-to-back calls captured once into a HIP graph, replayed reps
+    times, HIP events around the replays (a standalone call's argument
+    checks and Python marshalling take longer than a small GEMM runs)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(n):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (n * reps)
+
+
 def timed_cold(fn, n, torch):
     """Average seconds of one fn launch with the caches flushed before it:
     reading a 1 GiB buffer evicts the 256 MB Infinity Cache and the L2s with
@@ -208,8 +231,10 @@ def decode_run(D, dm, prompts, warmup, steps, torch):
 def gemm_sweep(D, S, torch):
     """The 25-shape int8 GEMM sweep, per-row x per-column requant to int8,
     each call with the workspace detint_gemm_workspace asks for (split-K on
-    few-tile shapes). M >= 512: TOP/s against the i8 MFMA peak (back-to-back
-    launches); M <= 64: GB/s against HBM, each launch cache-cold."""
+    few-tile shapes). M >= 512: TOP/s against the i8 MFMA peak (20
+    back-to-back calls replayed from a HIP graph, so the host's per-call
+    cost is not timed); M <= 64: GB/s against HBM, each launch cache-cold
+    (its flush covers the host's launch cost)."""
     res = {}
     for Kd, Nd in S.GEMM_SWEEP_KN:
         g = S.make_gemm_operands(max(S.GEMM_SWEEP_M), Nd, Kd, seed=7)
@@ -226,7 +251,7 @@ def gemm_sweep(D, S, torch):
                 f()
             key = f"M{M}_K{Kd}_N{Nd}"
             if M >= 512:
-                t = timed(f, 20, torch)
+                t = timed_graph(f, 20, torch)
                 tops = 2 * M * Nd * Kd / t / 1e12
                 res[key] = {"tops": round(tops, 1), "frac_i8_mfma": round(tops / I8_PEAK_TOPS, 4)}
             else:
@@ -253,7 +278,8 @@ def c0_case(D, S, torch, with_cpu: bool):
     """One Qwen-style decoder layer (hidden 256, 4/2 heads, d 64, FFN 768),
     prefill of 64 tokens on a seeded residual in [-2^15, 2^15): the output
     residual against the oracle's, the GPU layer latency (HIP events, 50
-    back-to-back calls on fresh copies of the input), the kernels one call
+    back-to-back calls on fresh copies of the input; also replayed from a
+    HIP graph, without the host's launch cost), the kernels one call
     launches, and the oracle's time on one host thread."""
     import numpy as np
     m = S.make_model("layer256", seed=1)
@@ -279,8 +305,27 @@ def c0_case(D, S, torch, with_cpu: bool):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
     kernels = graph_kernel_count(lambda: call(0), torch)
+    # the same n calls replayed from a HIP graph (the layer's kernels
+    # without the host's launch cost), each replay on fresh copies
+    fresh = torch.from_numpy(np.ascontiguousarray(h0)).cuda().repeat(n + 1, 1, 1)
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for i in range(n):
+            call(i)
+    torch.cuda.current_stream().wait_stream(gs)
+    hs.copy_(fresh)
+    g.replay()
+    hs.copy_(fresh)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / n
     res = {"workload": "one Qwen-style layer, hidden 256, 4/2 heads, d 64, FFN 768, 64-token prefill",
-           "gpu_layer_us": round(us, 2), "kernels_per_call": kernels,
+           "gpu_layer_us": round(us, 2), "gpu_layer_us_graph": round(us_graph, 2), "kernels_per_call": kernels,
            "weight_bytes": int(sum(a.size for a in (m.layers[0].wqkv, m.layers[0].wo, m.layers[0].wgu,
                                                     m.layers[0].wd)))}
     if with_cpu:

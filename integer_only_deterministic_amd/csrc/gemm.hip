@@ -670,7 +670,11 @@ hipError_t pipe_launch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int 
 // 128x64) measured 3-16% faster than 4 waves, the 256x128 limb tiling (4 x 2
 // waves of 64x64, both planes, 128 accumulators each) 9-13% faster, the
 // 128x256 int8 tiling 14% at M = 2048, N = 4096. The 128x64 fallback keeps
-// 4 waves (8 would leave each a single 32x32 tile).
+// 4 waves (8 would leave each a single 32x32 tile); where even it leaves a
+// quarter of the CUs idle, 64x64 tiles of two waves take twice the
+// workgroups (M = 512, N = 1024: K = 2048 10.9 -> 9.8 us, K = 3072 14.1
+// -> 12.5 us, graph-replayed; a split of K over workgroups was slower
+// there, 14.1 us).
 template <bool WIDE>
 hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, int M, int N,
                          int K, const Epi& e, void* out, hipStream_t st) {
@@ -683,6 +687,7 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
   if (tiles(256, 256) >= FILL) return pipe_launch<256, 256, 2, false, 2, 4>(A, W, Wlo, M, N, K, e, out, st);
   if (tiles(128, 256) >= FILL) return pipe_launch<128, 256, 3, false, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
   if (tiles(128, 128) >= FILL) return pipe_launch<128, 128, 4, false, 4, 2>(A, W, Wlo, M, N, K, e, out, st);
+  if (tiles(128, 64) < FILL) return pipe_launch<64, 64, 4, false, 2, 1>(A, W, Wlo, M, N, K, e, out, st);
   return pipe_launch<128, 64, 4, false>(A, W, Wlo, M, N, K, e, out, st);
 }
 

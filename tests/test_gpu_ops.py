@@ -58,14 +58,14 @@ def test_gemm_sweep(D, K, N):
 
 
 # K % 128 == 0 shapes take the pipelined kernel; (200, 300, 256),
-# (1000, 3000, 256), (1000, 6100, 256) and (2000, 6000, 128) are sized so
-# that its 128x64, 128x128, 128x256 and 256x256 tilings are each chosen,
-# with ragged M and N edges.
+# (1000, 1590, 256), (1000, 3000, 256), (1000, 6100, 256) and (2000, 6000,
+# 128) are sized so that its 64x64, 128x64, 128x128, 128x256 and 256x256
+# tilings are each chosen, with ragged M and N edges.
 # 16 < M <= 64 with K % 512 == 0 takes the skinny kernel (one or two 32-row
 # tiles).
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 77, 32), (17, 130, 64),
                                    (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072),
-                                   (200, 300, 256), (1000, 3000, 256), (1000, 6100, 256),
+                                   (200, 300, 256), (1000, 1590, 256), (1000, 3000, 256), (1000, 6100, 256),
                                    (2000, 6000, 128),
                                    (32, 1000, 2048), (20, 100, 512), (50, 77, 1024),
                                    (5, 300, 1040), (8, 333, 2064),
@@ -103,7 +103,7 @@ def test_gemm_ragged_all_modes(D, M, N, K):
 @pytest.mark.parametrize("M", [512, 6])
 def test_gemm_general_scales(D, mode, M):
     """Mantissas >= 2^15 and (for REQ_I8) shifts from -3 to 70: at M = 512 an
-    all-interior 128x64 tiling takes the pipelined kernel's general
+    all-interior 64x64 tiling takes the pipelined kernel's general
     epilogue, not its in-range fast path; at M = 6 the GEMV's epilogue."""
     N, K = 512, 256
     rng = np.random.default_rng(99)
