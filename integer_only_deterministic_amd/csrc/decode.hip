@@ -122,7 +122,7 @@ struct FG {
 };
 
 template <int MT, int CPW, int KC, int PRO, int EPI>
-__global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 : 1)) void fgemv(FG p) {
+__global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? (CPW == 4 ? 6 : 8) : 1)) void fgemv(FG p) {
   extern __shared__ __attribute__((aligned(16))) int8_t sx[];  // [MT][K] int8 input rows
   __shared__ int64_t sred[TPB / 64][2 * MT];
   __shared__ int32_t s_m[MT], s_k[MT], s_e[MT];
@@ -460,7 +460,13 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? 8 :
     }
   }
   if (EPI == EPI_LOGITS) {
-    if (CPW == 2) {
+    // the column leaders' best keys into lane 0 (leaders 16 apart for four
+    // columns, 32 apart for two)
+    if (CPW == 4) {
+      const int64_t o1 = lane_xor<16>(bestk);
+      bestk = o1 > bestk ? o1 : bestk;
+    }
+    if (CPW >= 2) {
       const int64_t o2 = lane_xor<32>(bestk);
       bestk = o2 > bestk ? o2 : bestk;
     }
@@ -510,8 +516,12 @@ hipError_t launch_mt(const FG& p, hipStream_t st) {
 
 DETINT_BOUND_READER(bound_flags_decode)
 
+// column groups of the vocabulary head: four columns per wave for one row,
+// two otherwise
+constexpr int head_cpw(int64_t M) { return M <= 1 ? 4 : 2; }
+
 int fused_decode_parts(int64_t V, int64_t M) {
-  return cap_blocks((V + 1) / 2, M <= 1 ? 1 : (M <= 4 ? 4 : 8)) * 4;
+  return cap_blocks((V + head_cpw(M) - 1) / head_cpw(M), M <= 1 ? 1 : (M <= 4 ? 4 : 8)) * 4;
 }
 
 bool fused_decode_supported(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K <= 8192 && K % 16 == 0; }
@@ -579,6 +589,9 @@ hipError_t launch_fused_lm_head(const int32_t* h, const int32_t* row_index, cons
   p.h = h; p.row_index = row_index; p.gain = gain; p.W = E; p.col_m = emb_m; p.col_k = w_k;
   p.frac = f_l; p.M = (int)M; p.N = (int)V; p.K = (int)K; p.out = logits;
   p.out_row_base = row_base; p.part = part;
+  // one row: four columns per wave, twice the weight bytes in flight per
+  // wave with the same workgroups
+  if (head_cpw(M) == 4) return launch_kc<1, 4, PRO_NORM, EPI_LOGITS>(p, st);
   return launch_mt<2, PRO_NORM, EPI_LOGITS>(p, st);
 }
 
