@@ -768,7 +768,7 @@ def main():
         "grid_barrier_probe": barrier,
         "final_head_kernel_roofline": {
             "bound": "hbm",
-            "kernel": "fused final RMSNorm + tied lm_head GEMV, 1 row (fgemv<1,2,1,1,4>), cache-cold launches",
+            "kernel": "fused final RMSNorm + tied lm_head GEMV, 1 row (fgemv<1,4,1,1,4>), cache-cold launches",
             "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(head_gbs / HBM_PEAK_GBS, 4),
             "traffic": profile_value("final_head_hbm_traffic.txt", "hbm_bytes_per_launch",
