@@ -858,18 +858,36 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_prefill_mfma(
     sweep_end();
   };
 
-  // pass 1: maxima
+  // pass 1: maxima. Its per-chunk work (16 maxima) is too short to cover a
+  // chunk's two chained MFMAs, so chunks go in pairs: both pairs' MFMA
+  // chains issued together, the next pair's K fragments read under them.
   int mx = INT32_MIN;
-  sweep(false, [&](int c, const v16i& sacc) {
-      if (c * 32 + 31 <= pmin) {
+  auto max_chunk = [&](int c, const v16i& sacc) {
+    if (c * 32 + 31 <= pmin) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = max(mx, sacc[r]);
-      } else {
+      for (int r = 0; r < 16; ++r) mx = max(mx, sacc[r]);
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (c * 32 + koff(r) <= pos) mx = max(mx, sacc[r]);
-      }
-  });
+      for (int r = 0; r < 16; ++r)
+        if (c * 32 + koff(r) <= pos) mx = max(mx, sacc[r]);
+    }
+  };
+  issue(0, false);
+  for (int bt = 0; bt < nbt; ++bt) {
+    batch_begin(bt, false);
+    const int c0 = bt * CPB, c1 = min(nch, (bt + 1) * CPB);
+    v4i ka[KS], kb[KS];
+    kfrag(c0, ka);
+    kfrag(min(c0 + 1, c1 - 1), kb);
+    for (int c = c0; c < c1; c += 2) {
+      const v16i sa = smma(ka), sb = smma(kb);
+      kfrag(min(c + 2, c1 - 1), ka);
+      kfrag(min(c + 3, c1 - 1), kb);
+      max_chunk(c, sa);
+      if (c + 1 < c1) max_chunk(c + 1, sb);
+    }
+  }
+  sweep_end();
   mx = max(mx, lane_xor<32>(mx));
   if (!live) mx = 0;  // its values are never used; keep the arithmetic tame
 
