@@ -62,14 +62,16 @@ def test_gemm_sweep(D, K, N):
 # 128) are sized so that its 64x64, 128x64, 128x128, 128x256 and 256x256
 # tilings are each chosen, with ragged M and N edges.
 # 16 < M <= 64 with K % 512 == 0 takes the skinny kernel (one or two 32-row
-# tiles).
+# tiles; (40, 16400, 512) two 32-column tiles per workgroup, the last one
+# ragged).
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 77, 32), (17, 130, 64),
                                    (37, 300, 112), (129, 257, 80), (200, 64, 1024), (300, 1000, 3072),
                                    (200, 300, 256), (1000, 1590, 256), (1000, 3000, 256), (1000, 6100, 256),
                                    (2000, 6000, 128),
                                    (32, 1000, 2048), (20, 100, 512), (50, 77, 1024),
                                    (5, 300, 1040), (8, 333, 2064),
-                                   (300, 1000, 8192), (40, 700, 4096), (512, 1024, 16384)])
+                                   (300, 1000, 8192), (40, 700, 4096), (512, 1024, 16384),
+                                   (40, 16400, 512)])
 def test_gemm_ragged_all_modes(D, M, N, K):
     import torch
     rng = np.random.default_rng(M * 7 + N + K)
@@ -139,9 +141,11 @@ def test_gemm_empty(D):
 
 # (33, 130, 512) and (300, 200, 1024) take the pipelined kernel's 128x128
 # limb tiling, (1000, 6100, 128) its 256x128 one; (32, 130, 2048) and
-# (17, 300, 512) the skinny kernel.
+# (17, 300, 512) the skinny kernel, (29, 16400, 512) its two-tile
+# workgroups with a ragged last tile.
 @pytest.mark.parametrize("M,N,K", [(1, 100, 2048), (7, 300, 256), (16, 64, 8192), (33, 130, 512),
-                                   (300, 200, 1024), (1000, 6100, 128), (32, 130, 2048), (17, 300, 512)])
+                                   (300, 200, 1024), (1000, 6100, 128), (32, 130, 2048), (17, 300, 512),
+                                   (29, 16400, 512)])
 def test_gemm_w16_limbs(D, M, N, K):
     rng = np.random.default_rng(M + N + K)
     A = rng.integers(-128, 128, (M, K)).astype(np.int8)
