@@ -694,7 +694,7 @@ hipError_t pipe_dispatch(const int8_t* A, const int8_t* W, const int8_t* Wlo, in
 // ------------------------------------------------------------- skinny GEMM
 
 // M <= 64 rows (batched decode, short prompts): weight streaming. A
-// workgroup of SK_W waves owns 32 output columns for all rows; its waves
+// workgroup of SK_W waves owns 32 NC output columns for all rows; its waves
 // split K into SK_W chunks, each streaming its chunk of the weight rows from
 // HBM straight into MFMA fragments (buffer loads, one group of SK_G k-steps
 // in flight while the previous group is multiplied) against A fragments that
