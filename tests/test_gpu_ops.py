@@ -425,9 +425,10 @@ def test_layer256_split_and_token_by_token(D, layer_case):
 
 # -------------------------------------------------------------- lm_head
 
-# S <= 8 int8 rows take the fused decode kernel; wide tables and S > 8 take
+# S <= 8 int8 rows take the fused decode kernel (four columns per wave for
+# one row: V = 4099 leaves a ragged last group); wide tables and S > 8 take
 # RMSNorm + lm_head (GEMV up to 16 rows, MFMA GEMM beyond) + argmax.
-@pytest.mark.parametrize("S_,V,H,wide", [(1, 151936, 1024, False), (8, 5000, 256, False),
+@pytest.mark.parametrize("S_,V,H,wide", [(1, 151936, 1024, False), (1, 4099, 1024, False), (8, 5000, 256, False),
                                          (5, 4099, 2048, False), (12, 3000, 512, False),
                                          (40, 2000, 256, False), (3, 4099, 512, True)])
 def test_final_head(D, S_, V, H, wide):
