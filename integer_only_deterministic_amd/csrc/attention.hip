@@ -438,8 +438,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     int64_t x0 = act ? hx0[u] : 0, x1 = act ? hx1[u] : 0;
     if (QKN) {
       int64_t a0 = act ? x0 * hm0[u] : 0, a1 = act ? x1 * hm1[u] : 0;
-      const uint64_t u0 = uabs64(a0), u1 = uabs64(a1);
-      const int b = bitlen64(wave_max_u(u0 > u1 ? u0 : u1));
+      const int b = wave_bitlen_max(uabs64(a0), uabs64(a1));
       const int sh0 = b > 24 ? b - 24 : 0;
       a0 = R(a0, sh0);
       a1 = R(a1, sh0);
@@ -460,8 +459,8 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     if (t < G) {
       y0 = R(y0, g0);
       y1 = R(y1, g1);
-      const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
-      const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
+      const int bl = wave_bitlen_max(uabs64(y0), uabs64(y1));
+      const int e = bl > 7 ? bl - 7 : 0;  // dq_exp of the maximum
       int8_t* qd = (int8_t*)sq + t * D;
       if (act) {
         qd[j0] = clamp8(R(y0, e));

@@ -418,6 +418,26 @@ __device__ __forceinline__ uint64_t wave_max_u(uint64_t v) {
   return wave_reduce64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
+// Maximum over the wave of a 32-bit value (one exchange per step).
+__device__ __forceinline__ int wave_max32(int v) {
+  v = max(v, (int)dpp_u32<kDppXor1>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppXor2>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppHalfMirror>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppMirror>((uint32_t)v));
+  uint32_t a, b;
+  row_pair<16>((uint32_t)v, a, b);
+  v = max((int)a, (int)b);
+  row_pair<32>((uint32_t)v, a, b);
+  return max((int)a, (int)b);
+}
+
+// Bit length of the wave's largest magnitude among 64-bit u0, u1: the bit
+// length of a maximum is the maximum of the bit lengths, so the exchange
+// carries 32-bit lengths instead of 64-bit values.
+__device__ __forceinline__ int wave_bitlen_max(uint64_t u0, uint64_t u1) {
+  return wave_max32(bitlen64(u0 | u1));
+}
+
 // Sum over the lanes that differ from this one in bits O, O / 2, ..., 1
 template <int O>
 __device__ __forceinline__ int xor_sum_to(int v) {
