@@ -64,6 +64,35 @@ __device__ __forceinline__ int wave_reduce_t(int (&v)[NV], int lane) {
   return Halve<NV, 32>::run(v, lane);
 }
 
+// The same transposed reduction with a maximum (bit lengths).
+template <int O>
+__device__ __forceinline__ int xor_max_to(int v) {
+  if constexpr (O == 0) {
+    return v;
+  } else {
+    return xor_max_to<O / 2>(max(v, lane_xor<O>(v)));
+  }
+}
+template <int N, int O>
+struct HalveMax {
+  __device__ __forceinline__ static int run(int* v, int lane) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const int keep = upper ? v[i + N / 2] : v[i];
+      const int give = upper ? v[i] : v[i + N / 2];
+      v[i] = max(keep, lane_xor<O>(give));
+    }
+    return HalveMax<N / 2, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct HalveMax<1, O> {
+  __device__ __forceinline__ static int run(int* v, int) {
+    return xor_max_to<O>(v[0]);
+  }
+};
+
 // The same transposed reduction for int64 values with a sum or a max.
 template <int N, int O, bool MAX>
 struct Halve64 {
@@ -267,25 +296,29 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? (CP
         }
       }
     }
-    int64_t Sv[MT], Av[MT];
+    // per row: the sum of squares and the bit length of the largest
+    // magnitude (all the DQ exponent needs; the bit length of the OR of the
+    // magnitudes is that of their maximum), so the maxima travel as 32 bits
+    int64_t Sv[MT];
+    int Bv[MT];
   #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      int64_t S = 0, A = 0;
+      int64_t S = 0;
+      uint64_t A = 0;
   #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
   #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int64_t v = xv[m][kc][e4];
           if (PRO == PRO_NORM) S += v * v;
-          const int64_t a = (int64_t)uabs64(PRO == PRO_NORM ? v * gv[kc][e4] : v);
-          A = a > A ? a : A;
+          A |= uabs64(PRO == PRO_NORM ? v * gv[kc][e4] : v);
         }
       Sv[m] = S;
-      Av[m] = A;
+      Bv[m] = bitlen64(A);
     }
     {
       // wave totals of every row at once: lane l ends with row idx(l)'s totals
-      const int64_t At = Halve64<MT, 32, true>::run(Av, lane);
+      const int At = HalveMax<MT, 32>::run(Bv, lane);
       const int64_t St = PRO == PRO_NORM ? Halve64<MT, 32, false>::run(Sv, lane) : 0;
       const int r = reduce_index<MT>(lane);
       if ((lane & (64 / MT - 1)) == 0) {
@@ -307,7 +340,7 @@ __global__ __launch_bounds__(TPB, (EPI == EPI_LOGITS && MT == 1 && KC == 1 ? (CP
         St += sred[w2][2 * r];
         At = sred[w2][2 * r + 1] > At ? sred[w2][2 * r + 1] : At;
       }
-      const int e = dq_exp((uint64_t)At);
+      const int e = At > 7 ? (int)At - 7 : 0;  // dq_exp of the rows' largest magnitude
       int32_t sm, sk;
       if (PRO == PRO_NORM && (uint64_t)St >> 62) bad |= kBoundNorm;
       if (PRO == PRO_NORM) {

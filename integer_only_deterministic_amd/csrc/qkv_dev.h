@@ -69,8 +69,7 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
   if (p.qk_norm) {
     const int16_t* gn = hh < nq ? p.q_norm : p.k_norm;
     int64_t a0 = act ? x0 * p.col_m[c0 + j0] : 0, a1 = act ? x1 * p.col_m[c0 + j1] : 0;
-    const uint64_t u0 = uabs64(a0), u1 = uabs64(a1);
-    const int b = bitlen64(wave_max_u(u0 > u1 ? u0 : u1));
+    const int b = wave_bitlen_max(uabs64(a0), uabs64(a1));
     const int sh0 = b > 24 ? b - 24 : 0;
     a0 = R(a0, sh0);
     a1 = R(a1, sh0);
@@ -100,8 +99,8 @@ __device__ __forceinline__ void qkv_head(const int32_t* __restrict__ row, int hh
       y0 = R(y0, g[j0] & 7);
       y1 = R(y1, g[j1] & 7);
     }
-    const uint64_t u0 = uabs64(y0), u1 = uabs64(y1);
-    const int e = dq_exp(wave_max_u(u0 > u1 ? u0 : u1));
+    const int bl = wave_bitlen_max(uabs64(y0), uabs64(y1));
+    const int e = bl > 7 ? bl - 7 : 0;  // dq_exp of the maximum
     if (act) {
       q_dst[j0] = clamp8(R(y0, e));
       q_dst[j1] = clamp8(R(y1, e));
