@@ -481,9 +481,11 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   lds_barrier();
 
   // 4. pass 1: scores into LDS, per-head maxima
-  int64_t mx[G];
+  // scores are int32 (|q . k| <= 2^14 d), and so are the maxima and, below
+  // max_pos <= 16384 keys of E <= 2^15, the sums: reductions in 32 bits
+  int32_t mx[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = INT64_MIN;
+  for (int g = 0; g < G; ++g) mx[g] = INT32_MIN;
   auto score = [&](const v4i (&kv)[CH], int j) {
     int s[G];
 #pragma unroll
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int64_t m = wave_max(mx[g]);
+    const int m = wave_max32(mx[g]);
     if (lane == 0) rmax[wave][g] = m;
   }
   lds_barrier();
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
     int64_t m = rmax[0][g];
 #pragma unroll
     for (int w = 1; w < NW; ++w) m = rmax[w][g] > m ? rmax[w][g] : m;
-    mx[g] = m;
+    mx[g] = (int32_t)m;
   }
 
   // the first batch of later cached values, in flight during passes 2-3
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   if (PRE < nold) vload(va, PRE);
 
   // 5. pass 2: exponentials in place and their sums; 2^46 / D per head
-  int64_t den[G];
+  int32_t den[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) den[g] = 0;
   {
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(NT) void attn_decode_fused(
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int64_t d = wave_sum(den[g]);
+    const int d = wave_sum32(den[g]);
     if (lane == 0) rsum[wave][g] = d;
   }
   lds_barrier();

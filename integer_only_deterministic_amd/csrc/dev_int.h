@@ -418,17 +418,24 @@ __device__ __forceinline__ uint64_t wave_max_u(uint64_t v) {
   return wave_reduce64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
-// Maximum over the wave of a 32-bit value (one exchange per step).
-__device__ __forceinline__ int wave_max32(int v) {
-  v = max(v, (int)dpp_u32<kDppXor1>((uint32_t)v));
-  v = max(v, (int)dpp_u32<kDppXor2>((uint32_t)v));
-  v = max(v, (int)dpp_u32<kDppHalfMirror>((uint32_t)v));
-  v = max(v, (int)dpp_u32<kDppMirror>((uint32_t)v));
+// Maximum / sum over the wave of a 32-bit value (one exchange per step).
+template <class Op>
+__device__ __forceinline__ int wave_reduce32(int v, Op op) {
+  v = op(v, (int)dpp_u32<kDppXor1>((uint32_t)v));
+  v = op(v, (int)dpp_u32<kDppXor2>((uint32_t)v));
+  v = op(v, (int)dpp_u32<kDppHalfMirror>((uint32_t)v));
+  v = op(v, (int)dpp_u32<kDppMirror>((uint32_t)v));
   uint32_t a, b;
   row_pair<16>((uint32_t)v, a, b);
-  v = max((int)a, (int)b);
+  v = op((int)a, (int)b);
   row_pair<32>((uint32_t)v, a, b);
-  return max((int)a, (int)b);
+  return op((int)a, (int)b);
+}
+__device__ __forceinline__ int wave_max32(int v) {
+  return wave_reduce32(v, [](int a, int b) { return max(a, b); });
+}
+__device__ __forceinline__ int wave_sum32(int v) {
+  return wave_reduce32(v, [](int a, int b) { return a + b; });
 }
 
 // Bit length of the wave's largest magnitude among 64-bit u0, u1: the bit

@@ -1028,10 +1028,6 @@ __device__ __forceinline__ int crossing_in_step(const int64_t (&c)[4], int64_t x
   return 255;  // not reached for x below the step's sum
 }
 
-__device__ __forceinline__ int32_t wave_sum32(int32_t v) {
-  return xor_sum_to<32>(v);
-}
-
 // One row (blockIdx.x) by one SMT-thread workgroup; also the in-kernel
 // fallback of the sliced top-p pick.
 __device__ __forceinline__ void sample_row(const int32_t* __restrict__ logits, int V, int keep,
