@@ -486,6 +486,28 @@ __device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red) {
   for (int i = 0; i < nw; ++i) t += red[i];
   return t;
 }
+// A row's sum of squares and the bit length of its largest magnitude in
+// one exchange through LDS (`red` >= 32 entries): the sum in 64 bits, the
+// bit length as a 32-bit maximum. All threads receive both.
+__device__ __forceinline__ void block_sum_maxbits(int64_t& s, int& b, int64_t* red) {
+  s = wave_sum(s);
+  b = wave_max32(b);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red[w] = s;
+    red[16 + w] = b;
+  }
+  __syncthreads();
+  int64_t ts = 0;
+  int tb = 0;
+  for (int i = 0; i < nw; ++i) {
+    ts += red[i];
+    tb = max(tb, (int)red[16 + i]);
+  }
+  s = ts;
+  b = tb;
+}
 __device__ __forceinline__ int64_t block_max(int64_t v, int64_t* red) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(TPB) void rmsnorm_rk(const int32_t* __restrict__ h,
                                                   int32_t* __restrict__ rm,
                                                   int32_t* __restrict__ rk) {
   using RR = RowRegs<TPB, U>;
-  __shared__ int64_t red[16];
+  __shared__ int64_t red[32];
   const int r = blockIdx.x;
   const int src = row_index ? row_index[r] : r;
   const int32_t* hr = h + (size_t)src * n;
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(TPB) void rmsnorm_rk(const int32_t* __restrict__ h,
     hv[u] = *(const v4i*)(hr + RR::at(u, n));
     gw[u] = *(const int2*)(g + RR::at(u, n));
   }
-  int64_t v[U][4], gv[U][4], S = 0, A = 0;
+  int64_t v[U][4], gv[U][4], S = 0;
+  uint64_t A = 0;  // OR of the magnitudes: the bit length of their maximum
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool ok = RR::first(u) < n;
@@ -100,19 +101,18 @@ __global__ __launch_bounds__(TPB) void rmsnorm_rk(const int32_t* __restrict__ h,
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       S += v[u][e4] * v[u][e4];
-      const int64_t a = (int64_t)uabs64(v[u][e4] * gv[u][e4]);
-      A = a > A ? a : A;
+      A |= uabs64(v[u][e4] * gv[u][e4]);
     }
   }
-  S = block_sum(S, red);
-  A = block_max(A, red);
+  int B = bitlen64(A);
+  block_sum_maxbits(S, B, red);
   if (threadIdx.x == 0) bound_raise((uint64_t)S >> 62 ? kBoundNorm : 0u);
   int8_t* xr = x8 + (size_t)r * n;
   int32_t m = 1 << 14, sh = 26;
   int e = 0;
   if (S != 0) {
     irms_wave(S, n, m, sh);
-    e = dq_exp((uint64_t)A);
+    e = B > 7 ? B - 7 : 0;  // dq_exp of the largest magnitude
     sh = sh + 12 - e;
   }
 #pragma unroll
